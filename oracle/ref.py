@@ -1,0 +1,259 @@
+"""Plain fp64 CPU oracle for the linear-recurrence scans.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module.  The product path
+(the HIP library and its Python binding) never imports it and shares no code
+with it; both sides only consume the same seeded inputs from ``lrgen``.
+
+Every function is sequential in time and vectorised only across independent
+channels (batch, channel, head, state index).  Nothing is blocked, chunked,
+fused or reordered.  Inputs are taken as given (bf16 values arrive as exact
+float32 values) and promoted to float64.
+
+Sources (cited by page title and section):
+  [KS]  IBM Research blog "K-Search for MLX" (repost), section
+        "A 20x faster prefill: the Mamba SSM kernel": the recurrence
+        h_t = a_t h_{t-1} + b_t and the associative combine of (a, b) pairs.
+  [MR]  "mlx-recurrence" post, Apple Developer Forums thread 840535: the
+        kernel list (ssd_scan, gla_scan, rglru_scan) with state shapes, and
+        the segment checkpoint-and-recompute training path.
+  [LX]  "lrnnx: A library for Linear RNNs" (paper summary), Key Contributions
+        2-3: ZOH as a discretisation of the time-varying selective scan, and
+        the fused scan + output projection.
+
+Readings where the pages are silent (each is listed in the design doc):
+  * ZOH: e = exp(dt*A), phi = expm1(dt*A)/A (phi = dt when A == 0), i.e. the
+    textbook exact zero-order hold for a diagonal A.  "euler" gives phi = dt.
+  * The readout is inclusive: y_t reads h_t after token t has been written.
+  * h_{-1} = h0 (zero when not given).
+  * SSD: A and Dskip are per head; B, C are shared by the H/G heads of a group.
+  * GLA: S_t = g_t S_{t-1} + k_t v_t^T, o_t = S_t^T q_t, no extra scaling.
+  * The backward differentiates loss = sum(dy * y) + <dh_last, h_last>.
+
+Parity pins: every function here is checked in ``tests/test_oracle_*.py``
+against closed forms, brute-force unrolls, library routines (numpy matmul,
+torch.autograd) or finite differences.  No function is "parity unpinned".
+"""
+from __future__ import annotations
+
+import numpy as np
+
+F64 = np.float64
+
+
+def _f(x):
+    return None if x is None else np.asarray(x, dtype=F64)
+
+
+# ---------------------------------------------------------------------------
+# The associative combine  [KS, combine equation]
+# ---------------------------------------------------------------------------
+def combine(later, earlier):
+    """(a2, b2) o (a1, b1) = (a2*a1, a2*b1 + b2): apply ``earlier`` first,
+    then ``later``.  The operator is associative but not commutative."""
+    a2, b2 = later
+    a1, b1 = earlier
+    return (a2 * a1, a2 * b1 + b2)
+
+
+# ---------------------------------------------------------------------------
+# Diagonal recurrence  [KS, recurrence equation; MR, rglru_scan state [B, D]]
+# ---------------------------------------------------------------------------
+def diag_scan(a, b, h0=None):
+    """h[:, t] = a[:, t] * h[:, t-1] + b[:, t]; a, b: [B, L, D].
+
+    Returns (h [B, L, D], h_last [B, D]) in float64."""
+    a, b = _f(a), _f(b)
+    Bn, L, D = a.shape
+    h = np.zeros((Bn, D), F64) if h0 is None else _f(h0).copy()
+    out = np.empty((Bn, L, D), F64)
+    for t in range(L):
+        h = a[:, t] * h + b[:, t]
+        out[:, t] = h
+    return out, h
+
+
+# ---------------------------------------------------------------------------
+# Discretisation  [LX, Key Contributions 2-3: ZOH]
+# ---------------------------------------------------------------------------
+def discretize(dt, A, disc="zoh"):
+    """Return (e, phi) with e = exp(dt*A) and
+    zoh:   phi = expm1(dt*A) / A   (phi = dt where A == 0)
+    euler: phi = dt
+    ``dt`` and ``A`` broadcast against each other."""
+    dt, A = np.broadcast_arrays(_f(dt), _f(A))
+    lam = dt * A
+    e = np.exp(lam)
+    if disc == "zoh":
+        safe = np.where(A == 0.0, 1.0, A)
+        phi = np.where(A == 0.0, dt, np.expm1(lam) / safe)
+    elif disc == "euler":
+        phi = dt.copy()
+    else:
+        raise ValueError(disc)
+    return e, phi
+
+
+def discretize_grads(dt, A, e, phi, disc="zoh"):
+    """Partial derivatives (de/ddt, de/dA, dphi/ddt, dphi/dA).
+
+    zoh: dphi/dA = (dt*e - phi)/A, evaluated as dt^2 (1/2 + l/3 + l^2/8 +
+    l^3/30) for |l| = |dt*A| < 1e-3 to avoid cancellation."""
+    dt, A = np.broadcast_arrays(_f(dt), _f(A))
+    de_ddt = A * e
+    de_dA = dt * e
+    if disc == "zoh":
+        lam = dt * A
+        small = np.abs(lam) < 1e-3
+        safe = np.where(A == 0.0, 1.0, A)
+        direct = (dt * e - phi) / safe
+        series = dt * dt * (0.5 + lam / 3.0 + lam * lam / 8.0 + lam ** 3 / 30.0)
+        dphi_ddt = e
+        dphi_dA = np.where(small, series, direct)
+    else:
+        dphi_ddt = np.ones_like(dt)
+        dphi_dA = np.zeros_like(dt)
+    return de_ddt, de_dA, dphi_ddt, dphi_dA
+
+
+# ---------------------------------------------------------------------------
+# Mamba-1 selective scan with fused readout  [LX, Key Contributions 3]
+# ---------------------------------------------------------------------------
+def selective_scan(x, dt, A, Bm, Cm, Dskip=None, h0=None, disc="zoh"):
+    """x, dt: [B, L, D]; A: [D, N]; Bm, Cm: [B, L, N]; Dskip: [D]; h0: [B, D, N].
+
+    h[b, d, n] <- e*h + phi*Bm[b, t, n]*x[b, t, d],  e, phi from dt[b,t,d]*A[d,n]
+    y[b, t, d]  = sum_n Cm[b, t, n]*h[b, d, n] + Dskip[d]*x[b, t, d]
+    Returns (y [B, L, D], h_last [B, D, N])."""
+    x, dt, A, Bm, Cm = map(_f, (x, dt, A, Bm, Cm))
+    Bn, L, D = x.shape
+    N = A.shape[1]
+    h = np.zeros((Bn, D, N), F64) if h0 is None else _f(h0).copy()
+    Dv = np.zeros(D, F64) if Dskip is None else _f(Dskip)
+    y = np.empty((Bn, L, D), F64)
+    for t in range(L):
+        e, phi = discretize(dt[:, t, :, None], A[None], disc)
+        h = e * h + phi * Bm[:, t, None, :] * x[:, t, :, None]
+        y[:, t] = np.einsum("bdn,bn->bd", h, Cm[:, t]) + Dv * x[:, t]
+    return y, h
+
+
+# ---------------------------------------------------------------------------
+# Mamba-2 head-wise SSD scan  [MR, ssd_scan: state [B, H, Dh, N]]
+# ---------------------------------------------------------------------------
+def _expand_groups(M, H):
+    """[B, L, G, N] -> [B, L, H, N]: head h reads group h // (H // G)."""
+    G = M.shape[2]
+    return np.repeat(M, H // G, axis=2)
+
+
+def ssd_scan(x, dt, A, Bm, Cm, Dskip=None, h0=None, disc="zoh", seg=0):
+    """x: [B, L, H, P]; dt: [B, L, H]; A, Dskip: [H]; Bm, Cm: [B, L, G, N];
+    h0: [B, H, P, N].
+
+    h[b,h,p,n] <- e*h + phi*x[b,t,h,p]*Bm[b,t,g,n],  e, phi from dt[b,t,h]*A[h]
+    y[b,t,h,p]  = sum_n Cm[b,t,g,n]*h[b,h,p,n] + Dskip[h]*x[b,t,h,p]
+    With seg > 0 also returns ckpt[s] = the state entering token s*seg
+    ([ceil(L/seg), B, H, P, N]); ckpt[0] = h0 (or 0).
+    Returns (y, h_last, ckpt or None)."""
+    x, dt, A, Bm, Cm = map(_f, (x, dt, A, Bm, Cm))
+    Bn, L, H, P = x.shape
+    N = Bm.shape[3]
+    Bh, Ch = _expand_groups(Bm, H), _expand_groups(Cm, H)
+    h = np.zeros((Bn, H, P, N), F64) if h0 is None else _f(h0).copy()
+    Dv = np.zeros(H, F64) if Dskip is None else _f(Dskip)
+    y = np.empty((Bn, L, H, P), F64)
+    ckpt = None
+    if seg:
+        ckpt = np.empty(((L + seg - 1) // seg, Bn, H, P, N), F64)
+    for t in range(L):
+        if seg and t % seg == 0:
+            ckpt[t // seg] = h
+        e, phi = discretize(dt[:, t], A[None], disc)          # [B, H]
+        h = (e[:, :, None, None] * h
+             + phi[:, :, None, None] * x[:, t, :, :, None] * Bh[:, t, :, None, :])
+        y[:, t] = np.einsum("bhpn,bhn->bhp", h, Ch[:, t]) + Dv[None, :, None] * x[:, t]
+    return y, h, ckpt
+
+
+def ssd_scan_bwd(x, dt, A, Bm, Cm, Dskip, h0, dy, dh_last=None, disc="zoh"):
+    """Gradients of loss = sum(dy*y) + <dh_last, h_last> for ``ssd_scan``.
+
+    Reverse-time adjoint of the recurrence, written out directly: with
+    G_t = dloss/dh_t (P x N per head),
+        G_{L-1} = dh_last + dy_{L-1} (x) C_{L-1},
+        G_t     = e_{t+1} G_{t+1} + dy_t (x) C_t,
+    the input gradients are
+        dx_t  = phi_t G_t B_t + Dskip dy_t,        dB_t += phi_t G_t^T x_t,
+        dC_t += h_t^T dy_t,                        dphi_t = x_t^T G_t B_t,
+        de_t  = <G_t, h_{t-1}>_F,                  dh0 = e_0 G_0,
+        dD   += <dy_t, x_t>,
+    and dt, A follow by the chain rule through (e, phi).  dB and dC sum over
+    the heads of a group.  The full forward state history is kept (no
+    checkpointing).  Returns a dict of float64 arrays."""
+    x, dt, A, Bm, Cm, dy = map(_f, (x, dt, A, Bm, Cm, dy))
+    Bn, L, H, P = x.shape
+    G = Bm.shape[2]
+    N = Bm.shape[3]
+    hpg = H // G
+    Bh, Ch = _expand_groups(Bm, H), _expand_groups(Cm, H)
+    Dv = np.zeros(H, F64) if Dskip is None else _f(Dskip)
+    h_init = np.zeros((Bn, H, P, N), F64) if h0 is None else _f(h0)
+
+    # forward, keeping h_{t} for t = -1 .. L-1
+    hist = np.empty((L + 1, Bn, H, P, N), F64)
+    hist[0] = h_init
+    E = np.empty((Bn, L, H), F64)
+    PHI = np.empty((Bn, L, H), F64)
+    for t in range(L):
+        e, phi = discretize(dt[:, t], A[None], disc)
+        E[:, t], PHI[:, t] = e, phi
+        hist[t + 1] = (e[:, :, None, None] * hist[t]
+                       + phi[:, :, None, None] * x[:, t, :, :, None] * Bh[:, t, :, None, :])
+
+    dx = np.empty_like(x)
+    ddt = np.empty_like(dt)
+    dBh = np.empty((Bn, L, H, N), F64)
+    dCh = np.empty((Bn, L, H, N), F64)
+    dA = np.zeros(H, F64)
+    Gt = np.zeros((Bn, H, P, N), F64) if dh_last is None else _f(dh_last).copy()
+    for t in range(L - 1, -1, -1):
+        Gt = Gt + dy[:, t, :, :, None] * Ch[:, t, :, None, :]
+        h_t, h_prev = hist[t + 1], hist[t]
+        e, phi = E[:, t], PHI[:, t]
+        dCh[:, t] = np.einsum("bhpn,bhp->bhn", h_t, dy[:, t])
+        gB = np.einsum("bhpn,bhn->bhp", Gt, Bh[:, t])
+        dx[:, t] = phi[:, :, None] * gB + Dv[None, :, None] * dy[:, t]
+        dBh[:, t] = phi[:, :, None] * np.einsum("bhpn,bhp->bhn", Gt, x[:, t])
+        dphi = np.einsum("bhp,bhp->bh", x[:, t], gB)
+        de = np.einsum("bhpn,bhpn->bh", Gt, h_prev)
+        de_ddt, de_dA, dphi_ddt, dphi_dA = discretize_grads(dt[:, t], A[None], e, phi, disc)
+        ddt[:, t] = de * de_ddt + dphi * dphi_ddt
+        dA += (de * de_dA + dphi * dphi_dA).sum(axis=0)
+        Gt = e[:, :, None, None] * Gt
+    dh0 = Gt
+    dD = np.einsum("blhp,blhp->h", dy, x)
+    dB = dBh.reshape(Bn, L, G, hpg, N).sum(axis=3)
+    dC = dCh.reshape(Bn, L, G, hpg, N).sum(axis=3)
+    return dict(dx=dx, ddt=ddt, dA=dA, dB=dB, dC=dC, dD=dD, dh0=dh0)
+
+
+# ---------------------------------------------------------------------------
+# Gated linear attention  [MR, gla_scan: scalar forget gate, outer-product
+# write, state [B, H, Dh, Dh]]
+# ---------------------------------------------------------------------------
+def gla_scan(q, k, v, g, S0=None):
+    """q, k: [B, L, H, K]; v: [B, L, H, V]; g: [B, L, H]; S0: [B, H, K, V].
+
+    S[b,h] <- g[b,t,h]*S[b,h] + k[b,t,h] v[b,t,h]^T
+    o[b,t,h] = S[b,h]^T q[b,t,h]
+    Returns (o [B, L, H, V], S_last [B, H, K, V])."""
+    q, k, v, g = map(_f, (q, k, v, g))
+    Bn, L, H, K = q.shape
+    V = v.shape[3]
+    S = np.zeros((Bn, H, K, V), F64) if S0 is None else _f(S0).copy()
+    o = np.empty((Bn, L, H, V), F64)
+    for t in range(L):
+        S = g[:, t, :, None, None] * S + k[:, t, :, :, None] * v[:, t, :, None, :]
+        o[:, t] = np.einsum("bhkv,bhk->bhv", S, q[:, t])
+    return o, S
