@@ -1,0 +1,185 @@
+/*
+ * lr.h — C ABI of liblr, fused linear-recurrence scans for AMD MI355X (gfx950).
+ *
+ * Every scan evaluates the first-order linear recurrence
+ *     h_t = a_t (.) h_{t-1} + b_t
+ * whose steps compose under the associative (not commutative) combine
+ *     (a2, b2) o (a1, b1) = (a2 a1, a2 b1 + b2)
+ * (IBM Research blog "K-Search for MLX", section "A 20x faster prefill: the
+ * Mamba SSM kernel", recurrence and combine equations).  Each forward scan is
+ * one kernel launch over the whole sequence ("mlx-recurrence" post, Apple
+ * Developer Forums thread 840535, opening paragraphs).
+ *
+ * Conventions for every entry point
+ *   - All calls are asynchronous on `stream` (a hipStream_t passed as void*;
+ *     NULL means the default stream).  The library never synchronises.
+ *   - Tensor pointers are DEVICE pointers, dense, contiguous and row-major in
+ *     exactly the shapes given in the comments (token-major [B, L, ...]).
+ *     They must be 16-byte aligned.  No strides.
+ *   - `io` is the element type of every per-token tensor and per-token
+ *     gradient.  A, Dskip, states (h0, h_last, ckpt, S0, S_last) and the
+ *     parameter gradients (dA, dD, dh0) are always float32.
+ *   - Ownership: the caller owns every buffer.  The library allocates no
+ *     memory and keeps no per-call state; scratch memory of the backward is a
+ *     caller-provided workspace whose size comes from a query function.
+ *   - Sizes: B and L may be 0 (empty input: nothing is computed; outputs that
+ *     carry a state receive the initial state).  Feature sizes must be > 0.
+ *   - Errors: each call validates all arguments BEFORE touching the device.
+ *     On failure it returns a non-zero lr_status and writes nothing.  Launch
+ *     failures map to LR_E_HIP.  Faults inside a kernel surface at the
+ *     caller's next synchronisation.  No C++ exception crosses the ABI.  The
+ *     library is thread-safe (it has no mutable global state).
+ *   - Determinism: results are bitwise identical across runs for a fixed
+ *     build, shape and input (no floating-point atomics anywhere).
+ */
+#ifndef LR_H_
+#define LR_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of per-token tensors. */
+typedef enum { LR_F32 = 0, LR_BF16 = 1 } lr_dtype;
+
+/* Discretisation of a continuous-time decay A over a step dt ("lrnnx: A
+ * library for Linear RNNs", Key Contributions 2, which names ZOH among the
+ * supported schemes; the pages give no formula).  Reading used here:
+ *   LR_DISC_ZOH:   abar = exp(dt*A), bbar = expm1(dt*A)/A * B   (= dt*B at A=0)
+ *   LR_DISC_EULER: abar = exp(dt*A), bbar = dt * B                            */
+typedef enum { LR_DISC_ZOH = 0, LR_DISC_EULER = 1 } lr_disc;
+
+typedef enum {
+  LR_OK = 0,
+  LR_E_NULLPTR = 1,     /* a required pointer is NULL                        */
+  LR_E_SHAPE = 2,       /* a size is negative/zero where it must be > 0, or
+                           sizes are inconsistent (e.g. H % G != 0)          */
+  LR_E_DTYPE = 3,       /* unknown lr_dtype or lr_disc value                  */
+  LR_E_ALIGN = 4,       /* a pointer is not 16-byte aligned                   */
+  LR_E_UNSUPPORTED = 5, /* a size or dtype outside the compiled set           */
+  LR_E_WORKSPACE = 6,   /* workspace missing or smaller than required         */
+  LR_E_OVERFLOW = 7,    /* a size product overflows int64 / exceeds limits    */
+  LR_E_HIP = 8          /* the HIP runtime reported an error at launch        */
+} lr_status;
+
+/* Static, NUL-terminated description of a status code. */
+const char* lr_status_string(int status);
+/* Library version string, e.g. "liblr 0.1.0 gfx950". */
+const char* lr_version(void);
+
+/* ---------------------------------------------------------------------------
+ * Diagonal recurrence (RG-LRU-style; "mlx-recurrence" post, rglru_scan,
+ * state [B, D]).  The decay a and input b are given directly.
+ *     h[b,t,d] = a[b,t,d] * h[b,t-1,d] + b[b,t,d],   h[b,-1,:] = h0 (or 0)
+ *   io:     LR_F32 or LR_BF16 (a, b, h); state arithmetic is fp32.
+ *   a, b:   [B, L, D] io          h: [B, L, D] io (every step is written)
+ *   h0:     [B, D] fp32 or NULL   h_last: [B, D] fp32 or NULL
+ * Supported: any B >= 0, L >= 0, D >= 1.
+ * ------------------------------------------------------------------------- */
+lr_status lr_diag_scan(lr_dtype io, int64_t B, int64_t L, int64_t D,
+                       const void* a, const void* b, const float* h0,
+                       void* h, float* h_last, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Mamba-1 selective scan with ZOH (or Euler) discretisation and a fused
+ * readout ("lrnnx: A library for Linear RNNs", Key Contributions 3: fused
+ * scan + output projection; the hidden state never reaches memory).
+ *     e = exp(dt[b,t,d] A[d,n]),  phi = expm1(dt A)/A (ZOH) or dt (Euler)
+ *     h[b,d,n] <- e h[b,d,n] + phi Bm[b,t,n] x[b,t,d]
+ *     y[b,t,d]  = sum_n Cm[b,t,n] h[b,d,n] + Dskip[d] x[b,t,d]
+ *   x, dt:  [B, L, D] io     Bm, Cm: [B, L, N] io     y: [B, L, D] io
+ *   A:      [D, N] fp32      Dskip:  [D] fp32 or NULL (treated as 0)
+ *   h0:     [B, D, N] fp32 or NULL    h_last: [B, D, N] fp32 or NULL
+ * dt is the step itself (> 0 expected; no bias or softplus is applied).
+ * Supported: 1 <= N <= 64, any D >= 1.
+ * ------------------------------------------------------------------------- */
+lr_status lr_selective_scan(lr_dtype io, lr_disc disc, int64_t B, int64_t L,
+                            int64_t D, int64_t N, const void* x,
+                            const void* dt, const float* A, const void* Bm,
+                            const void* Cm, const float* Dskip,
+                            const float* h0, void* y, float* h_last,
+                            void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Mamba-2 head-wise SSD scan ("mlx-recurrence" post, ssd_scan, state
+ * [B, H, Dh, N]; Dh is called P here).  G groups share B/C: head h reads
+ * group h / (H/G).  A and Dskip are per head, dt per (b, t, h).
+ *     e = exp(dt[b,t,h] A[h]),  phi as in lr_selective_scan
+ *     h[b,h,p,n] <- e h + phi x[b,t,h,p] Bm[b,t,g,n]
+ *     y[b,t,h,p]  = sum_n Cm[b,t,g,n] h[b,h,p,n] + Dskip[h] x[b,t,h,p]
+ *   x, y: [B, L, H, P] io    dt: [B, L, H] io    Bm, Cm: [B, L, G, N] io
+ *   A: [H] fp32    Dskip: [H] fp32 or NULL    h0, h_last: [B, H, P, N] fp32
+ *   chunk: the caller's chunk length; any multiple of 64.  The kernel always
+ *          evaluates the intra-chunk quadratic form on 64-token blocks and
+ *          carries the exact state between blocks, so the result does not
+ *          depend on chunk beyond rounding.
+ *   seg:   0, or a multiple of 64: then ckpt[s] receives the state ENTERING
+ *          token s*seg (ckpt[0] = h0 or 0) for s = 0 .. ceil(L/seg)-1 —
+ *          the segment checkpoints consumed by lr_ssd_scan_bwd.
+ *   ckpt:  [ceil(L/seg), B, H, P, N] fp32; required iff seg > 0.
+ * Supported: io = LR_BF16; P % 64 == 0; N in {64, 128}; H % G == 0.
+ * ------------------------------------------------------------------------- */
+lr_status lr_ssd_scan(lr_dtype io, lr_disc disc, int64_t B, int64_t L,
+                      int64_t H, int64_t P, int64_t G, int64_t N,
+                      int64_t chunk, int64_t seg, const void* x,
+                      const void* dt, const float* A, const void* Bm,
+                      const void* Cm, const float* Dskip, const float* h0,
+                      void* y, float* h_last, float* ckpt, void* stream);
+
+/* Workspace bytes needed by lr_ssd_scan_bwd for these sizes (0 on invalid
+ * sizes).  The workspace holds fp32 per-head partial sums of dB and dC, the
+ * adjoint state at segment boundaries and per-segment partials of dA, dD. */
+size_t lr_ssd_scan_bwd_workspace_bytes(int64_t B, int64_t L, int64_t H,
+                                       int64_t P, int64_t G, int64_t N,
+                                       int64_t chunk, int64_t seg);
+
+/* ---------------------------------------------------------------------------
+ * Backward of lr_ssd_scan with segment checkpoint-and-recompute
+ * ("mlx-recurrence" post: the training path stores segment checkpoints in
+ * the forward and recomputes inside each segment in the backward).
+ * Gradients of  loss = sum(dy * y) + <dh_last, h_last>  with respect to
+ * x, dt, A, Bm, Cm, Dskip and h0.
+ *   ckpt:    the checkpoints written by lr_ssd_scan with the same seg.
+ *   dy:      [B, L, H, P] io      dh_last: [B, H, P, N] fp32 or NULL (= 0)
+ *   dx:      [B, L, H, P] io      ddt: [B, L, H] io
+ *   dBm, dCm: [B, L, G, N] io (summed over the heads of each group)
+ *   dA: [H] fp32    dD: [H] fp32 or NULL    dh0: [B, H, P, N] fp32 or NULL
+ *   workspace: device memory of at least lr_ssd_scan_bwd_workspace_bytes().
+ * Supported: as lr_ssd_scan, with seg > 0.
+ * ------------------------------------------------------------------------- */
+lr_status lr_ssd_scan_bwd(lr_dtype io, lr_disc disc, int64_t B, int64_t L,
+                          int64_t H, int64_t P, int64_t G, int64_t N,
+                          int64_t chunk, int64_t seg, const void* x,
+                          const void* dt, const float* A, const void* Bm,
+                          const void* Cm, const float* Dskip, const float* h0,
+                          const float* ckpt, const void* dy,
+                          const float* dh_last, void* dx, void* ddt,
+                          float* dA, void* dBm, void* dCm, float* dD,
+                          float* dh0, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Gated linear attention with a scalar forget gate and an outer-product
+ * write ("mlx-recurrence" post, gla_scan, state [B, H, Dh, Dh], read here as
+ * [B, H, K, V]).
+ *     S[b,h] <- g[b,t,h] S[b,h] + k[b,t,h] v[b,t,h]^T
+ *     o[b,t,h] = S[b,h]^T q[b,t,h]
+ *   q, k: [B, L, H, K] io    v, o: [B, L, H, V] io    g: [B, L, H] io, in (0, 1]
+ *   S0, S_last: [B, H, K, V] fp32 or NULL
+ *   chunk: any multiple of 64 (same meaning as in lr_ssd_scan).
+ * No extra scaling of q is applied.
+ * Supported: io = LR_BF16; K in {64, 128}; V % 64 == 0.
+ * ------------------------------------------------------------------------- */
+lr_status lr_gla_scan(lr_dtype io, int64_t B, int64_t L, int64_t H, int64_t K,
+                      int64_t V, int64_t chunk, const void* q, const void* k,
+                      const void* v, const void* g, const float* S0, void* o,
+                      float* S_last, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LR_H_ */

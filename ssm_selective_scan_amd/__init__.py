@@ -1,0 +1,140 @@
+"""Python binding of liblr — fused linear-recurrence scans on MI355X (gfx950).
+
+Argument marshalling only: every function takes torch tensors on the GPU,
+checks dtype/device/contiguity, allocates the outputs the caller did not
+pass, and calls the C entry point of the same name (include/lr.h) on the
+current torch stream.  All arithmetic happens in the HIP kernels of liblr.so;
+there is no CPU or PyTorch fallback.
+"""
+from __future__ import annotations
+
+import torch
+
+from ._lib import (LR_BF16, LR_DISC_EULER, LR_DISC_ZOH, LR_F32, LrError,  # noqa: F401
+                   check, lib)
+
+__all__ = ["lr_diag_scan", "lr_selective_scan", "lr_ssd_scan", "lr_ssd_scan_bwd",
+           "lr_ssd_scan_bwd_workspace_bytes", "lr_gla_scan", "lr_version", "LrError"]
+
+_DISC = {"zoh": LR_DISC_ZOH, "euler": LR_DISC_EULER}
+
+
+def _io(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return LR_F32
+    if t.dtype == torch.bfloat16:
+        return LR_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr() or None
+
+
+def _f32(t, name):
+    if t is not None and t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32")
+    return _ptr(t)
+
+
+def _stream(t):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def lr_version() -> str:
+    return lib().lr_version().decode()
+
+
+def lr_diag_scan(a, b, h0=None, h=None, h_last=None, want_last=False):
+    """h[b,t,d] = a[b,t,d] h[b,t-1,d] + b[b,t,d]; a, b: [B, L, D]."""
+    B, L, D = a.shape
+    if h is None:
+        h = torch.empty_like(a)
+    if want_last and h_last is None:
+        h_last = torch.empty(B, D, device=a.device, dtype=torch.float32)
+    check("lr_diag_scan", lib().lr_diag_scan(
+        _io(a), B, L, D, _ptr(a), _ptr(b), _f32(h0, "h0"), _ptr(h), _f32(h_last, "h_last"),
+        _stream(a)))
+    return h, h_last
+
+
+def lr_selective_scan(x, dt, A, Bm, Cm, Dskip=None, h0=None, disc="zoh", y=None, h_last=None,
+                      want_last=False):
+    """Mamba-1 selective scan with fused readout; x, dt: [B, L, D], A: [D, N],
+    Bm, Cm: [B, L, N]."""
+    B, L, D = x.shape
+    N = A.shape[1]
+    if y is None:
+        y = torch.empty_like(x)
+    if want_last and h_last is None:
+        h_last = torch.empty(B, D, N, device=x.device, dtype=torch.float32)
+    check("lr_selective_scan", lib().lr_selective_scan(
+        _io(x), _DISC[disc], B, L, D, N, _ptr(x), _ptr(dt), _f32(A, "A"), _ptr(Bm), _ptr(Cm),
+        _f32(Dskip, "Dskip"), _f32(h0, "h0"), _ptr(y), _f32(h_last, "h_last"), _stream(x)))
+    return y, h_last
+
+
+def lr_ssd_scan(x, dt, A, Bm, Cm, Dskip=None, h0=None, disc="zoh", chunk=64, seg=0, y=None,
+                h_last=None, ckpt=None, want_last=False):
+    """Mamba-2 SSD scan; x: [B, L, H, P], dt: [B, L, H], A: [H],
+    Bm, Cm: [B, L, G, N].  With seg > 0 also returns the segment checkpoints."""
+    B, L, H, P = x.shape
+    G, N = Bm.shape[2], Bm.shape[3]
+    if y is None:
+        y = torch.empty_like(x)
+    if want_last and h_last is None:
+        h_last = torch.empty(B, H, P, N, device=x.device, dtype=torch.float32)
+    if seg and ckpt is None:
+        ckpt = torch.empty((L + seg - 1) // seg, B, H, P, N, device=x.device, dtype=torch.float32)
+    check("lr_ssd_scan", lib().lr_ssd_scan(
+        _io(x), _DISC[disc], B, L, H, P, G, N, chunk, seg, _ptr(x), _ptr(dt), _f32(A, "A"),
+        _ptr(Bm), _ptr(Cm), _f32(Dskip, "Dskip"), _f32(h0, "h0"), _ptr(y),
+        _f32(h_last, "h_last"), _f32(ckpt, "ckpt"), _stream(x)))
+    return y, h_last, ckpt
+
+
+def lr_ssd_scan_bwd_workspace_bytes(B, L, H, P, G, N, chunk, seg) -> int:
+    return int(lib().lr_ssd_scan_bwd_workspace_bytes(B, L, H, P, G, N, chunk, seg))
+
+
+def lr_ssd_scan_bwd(x, dt, A, Bm, Cm, Dskip, h0, ckpt, dy, dh_last=None, disc="zoh", chunk=64,
+                    seg=64, workspace=None, want_dh0=False):
+    """Gradients of sum(dy*y) + <dh_last, h_last> of lr_ssd_scan.  Returns a
+    dict with dx, ddt, dA, dB, dC, dD (None without Dskip) and dh0."""
+    B, L, H, P = x.shape
+    G, N = Bm.shape[2], Bm.shape[3]
+    dev = x.device
+    dx, ddt = torch.empty_like(x), torch.empty_like(dt)
+    dB, dC = torch.empty_like(Bm), torch.empty_like(Cm)
+    dA = torch.empty(H, device=dev, dtype=torch.float32)
+    dD = torch.empty(H, device=dev, dtype=torch.float32) if Dskip is not None else None
+    dh0 = torch.empty(B, H, P, N, device=dev, dtype=torch.float32) if want_dh0 else None
+    need = lr_ssd_scan_bwd_workspace_bytes(B, L, H, P, G, N, chunk, seg)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), device=dev, dtype=torch.uint8)
+    check("lr_ssd_scan_bwd", lib().lr_ssd_scan_bwd(
+        _io(x), _DISC[disc], B, L, H, P, G, N, chunk, seg, _ptr(x), _ptr(dt), _f32(A, "A"),
+        _ptr(Bm), _ptr(Cm), _f32(Dskip, "Dskip"), _f32(h0, "h0"), _f32(ckpt, "ckpt"), _ptr(dy),
+        _f32(dh_last, "dh_last"), _ptr(dx), _ptr(ddt), _f32(dA, "dA"), _ptr(dB), _ptr(dC),
+        _f32(dD, "dD"), _f32(dh0, "dh0"), _ptr(workspace), workspace.numel(), _stream(x)))
+    return dict(dx=dx, ddt=ddt, dA=dA, dB=dB, dC=dC, dD=dD, dh0=dh0)
+
+
+def lr_gla_scan(q, k, v, g, S0=None, chunk=64, o=None, S_last=None, want_last=False):
+    """GLA; q, k: [B, L, H, K], v: [B, L, H, V], g: [B, L, H]."""
+    B, L, H, K = q.shape
+    V = v.shape[3]
+    if o is None:
+        o = torch.empty_like(v)
+    if want_last and S_last is None:
+        S_last = torch.empty(B, H, K, V, device=q.device, dtype=torch.float32)
+    check("lr_gla_scan", lib().lr_gla_scan(
+        _io(q), B, L, H, K, V, chunk, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _f32(S0, "S0"),
+        _ptr(o), _f32(S_last, "S_last"), _stream(q)))
+    return o, S_last

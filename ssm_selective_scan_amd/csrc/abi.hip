@@ -1,0 +1,225 @@
+// abi.hip — the extern "C" boundary of liblr (declared in include/lr.h).
+//
+// Each entry point validates every argument without touching the device
+// (the shape and argument checks of the "mlx-recurrence" post's shared
+// chassis), then launches its kernel(s) on the caller's stream and maps a
+// launch failure to LR_E_HIP.  No allocation, no synchronisation, no global
+// mutable state.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <limits>
+
+#include "lr.h"
+
+namespace lr {
+template <typename T>
+hipError_t launch_diag_scan(const void* a, const void* b, const float* h0, void* h,
+                            float* h_last, int64_t B, int64_t L, int64_t D, hipStream_t stream);
+template <typename T>
+hipError_t launch_selective_scan(int disc, const void* x, const void* dt, const float* A,
+                                 const void* Bm, const void* Cm, const float* Dskip,
+                                 const float* h0, void* y, float* h_last, int64_t B, int64_t L,
+                                 int64_t D, int N, hipStream_t stream);
+hipError_t launch_ssd_fwd(int disc, const void* x, const void* dt, const float* A, const void* Bm,
+                          const void* Cm, const float* Dskip, const float* h0, void* y,
+                          float* h_last, float* ckpt, int64_t B, int64_t L, int64_t H, int64_t P,
+                          int64_t G, int64_t N, int64_t seg, hipStream_t stream);
+hipError_t launch_gla_fwd(const void* q, const void* k, const void* v, const void* gate,
+                          const float* S0, void* o, float* S_last, int64_t B, int64_t L,
+                          int64_t H, int64_t K, int64_t V, hipStream_t stream);
+size_t ssd_bwd_workspace(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N,
+                         int64_t seg);
+hipError_t launch_ssd_bwd(int disc, const void* x, const void* dt, const float* A, const void* Bm,
+                          const void* Cm, const float* Dskip, const float* ckpt, const void* dy,
+                          const float* dh_last, void* dx, void* ddt, float* dA, void* dBm,
+                          void* dCm, float* dD, float* dh0, void* ws, int64_t B, int64_t L,
+                          int64_t H, int64_t P, int64_t G, int64_t N, int64_t seg,
+                          hipStream_t stream);
+}  // namespace lr
+
+namespace {
+
+constexpr int64_t kMaxElems = int64_t(1) << 46;   // per tensor; keeps every index in int64
+constexpr int64_t kMaxGrid = std::numeric_limits<int32_t>::max();
+
+// Checked product of non-negative sizes; false on overflow.
+bool mul_ok(int64_t& acc, int64_t v) {
+  if (v < 0) return false;
+  if (v != 0 && acc > std::numeric_limits<int64_t>::max() / v) return false;
+  acc *= v;
+  return true;
+}
+
+bool elems_ok(std::initializer_list<int64_t> dims) {
+  int64_t n = 1;
+  for (int64_t d : dims)
+    if (!mul_ok(n, d)) return false;
+  return n <= kMaxElems;
+}
+
+bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool all_aligned(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (p != nullptr && !aligned(p)) return false;
+  return true;
+}
+
+bool any_null(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (p == nullptr) return true;
+  return false;
+}
+
+lr_status hip_status(hipError_t e) { return e == hipSuccess ? LR_OK : LR_E_HIP; }
+
+bool valid_io(int io) { return io == LR_F32 || io == LR_BF16; }
+bool valid_disc(int d) { return d == LR_DISC_ZOH || d == LR_DISC_EULER; }
+
+// Checks shared by the SSD forward and backward.
+lr_status check_ssd_sizes(int io, int disc, int64_t B, int64_t L, int64_t H, int64_t P, int64_t G,
+                          int64_t N, int64_t chunk, int64_t seg) {
+  if (!valid_io(io) || !valid_disc(disc)) return LR_E_DTYPE;
+  if (B < 0 || L < 0 || H < 1 || P < 1 || G < 1 || N < 1 || chunk < 1 || seg < 0) return LR_E_SHAPE;
+  if (H % G != 0) return LR_E_SHAPE;
+  if (io != LR_BF16) return LR_E_UNSUPPORTED;
+  if (P % 64 != 0 || (N != 64 && N != 128) || chunk % 64 != 0 || seg % 64 != 0)
+    return LR_E_UNSUPPORTED;
+  if (!elems_ok({B, L, H, P}) || !elems_ok({B, L, G, N}) || !elems_ok({B, H, P, N}))
+    return LR_E_OVERFLOW;
+  int64_t nwg = 1;
+  if (!mul_ok(nwg, B) || !mul_ok(nwg, H) || !mul_ok(nwg, P / 64) || nwg > kMaxGrid)
+    return LR_E_OVERFLOW;
+  if (seg > 0) {
+    const int64_t nseg = (L + seg - 1) / seg;
+    if (!elems_ok({nseg, B, H, P, N})) return LR_E_OVERFLOW;
+  }
+  return LR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lr_status_string(int s) {
+  switch (s) {
+    case LR_OK: return "LR_OK: success";
+    case LR_E_NULLPTR: return "LR_E_NULLPTR: a required pointer is NULL";
+    case LR_E_SHAPE: return "LR_E_SHAPE: invalid or inconsistent sizes";
+    case LR_E_DTYPE: return "LR_E_DTYPE: unknown dtype or discretisation";
+    case LR_E_ALIGN: return "LR_E_ALIGN: a pointer is not 16-byte aligned";
+    case LR_E_UNSUPPORTED: return "LR_E_UNSUPPORTED: size or dtype outside the compiled set";
+    case LR_E_WORKSPACE: return "LR_E_WORKSPACE: workspace missing or too small";
+    case LR_E_OVERFLOW: return "LR_E_OVERFLOW: sizes overflow the supported index range";
+    case LR_E_HIP: return "LR_E_HIP: the HIP runtime reported an error";
+    default: return "unknown lr_status";
+  }
+}
+
+const char* lr_version(void) { return "liblr 0.1.0 gfx950"; }
+
+lr_status lr_diag_scan(lr_dtype io, int64_t B, int64_t L, int64_t D, const void* a, const void* b,
+                       const float* h0, void* h, float* h_last, void* stream) {
+  if (!valid_io(io)) return LR_E_DTYPE;
+  if (B < 0 || L < 0 || D < 1) return LR_E_SHAPE;
+  if (!elems_ok({B, L, D})) return LR_E_OVERFLOW;
+  int64_t nwg = 1;
+  if (!mul_ok(nwg, B) || !mul_ok(nwg, (D + 15) / 16) || nwg > kMaxGrid) return LR_E_OVERFLOW;
+  if (B * L > 0 && any_null({a, b, h})) return LR_E_NULLPTR;
+  if (!all_aligned({a, b, h, h0, h_last})) return LR_E_ALIGN;
+  if (B == 0) return LR_OK;
+  auto s = static_cast<hipStream_t>(stream);
+  return hip_status(io == LR_F32 ? lr::launch_diag_scan<float>(a, b, h0, h, h_last, B, L, D, s)
+                                 : lr::launch_diag_scan<uint16_t>(a, b, h0, h, h_last, B, L, D, s));
+}
+
+lr_status lr_selective_scan(lr_dtype io, lr_disc disc, int64_t B, int64_t L, int64_t D, int64_t N,
+                            const void* x, const void* dt, const float* A, const void* Bm,
+                            const void* Cm, const float* Dskip, const float* h0, void* y,
+                            float* h_last, void* stream) {
+  if (!valid_io(io) || !valid_disc(disc)) return LR_E_DTYPE;
+  if (B < 0 || L < 0 || D < 1 || N < 1) return LR_E_SHAPE;
+  if (N > 64) return LR_E_UNSUPPORTED;
+  if (!elems_ok({B, L, D}) || !elems_ok({B, D, N}) || !elems_ok({D, N})) return LR_E_OVERFLOW;
+  int64_t nwg = 1;
+  if (!mul_ok(nwg, B) || !mul_ok(nwg, (D + 63) / 64) || nwg > kMaxGrid) return LR_E_OVERFLOW;
+  if (A == nullptr) return LR_E_NULLPTR;
+  if (B * L > 0 && any_null({x, dt, Bm, Cm, y})) return LR_E_NULLPTR;
+  if (!all_aligned({x, dt, A, Bm, Cm, Dskip, h0, y, h_last})) return LR_E_ALIGN;
+  if (B == 0) return LR_OK;
+  auto s = static_cast<hipStream_t>(stream);
+  const int n = static_cast<int>(N);
+  return hip_status(io == LR_F32
+                        ? lr::launch_selective_scan<float>(disc, x, dt, A, Bm, Cm, Dskip, h0, y,
+                                                           h_last, B, L, D, n, s)
+                        : lr::launch_selective_scan<uint16_t>(disc, x, dt, A, Bm, Cm, Dskip, h0,
+                                                              y, h_last, B, L, D, n, s));
+}
+
+lr_status lr_ssd_scan(lr_dtype io, lr_disc disc, int64_t B, int64_t L, int64_t H, int64_t P,
+                      int64_t G, int64_t N, int64_t chunk, int64_t seg, const void* x,
+                      const void* dt, const float* A, const void* Bm, const void* Cm,
+                      const float* Dskip, const float* h0, void* y, float* h_last, float* ckpt,
+                      void* stream) {
+  lr_status st = check_ssd_sizes(io, disc, B, L, H, P, G, N, chunk, seg);
+  if (st != LR_OK) return st;
+  if (A == nullptr) return LR_E_NULLPTR;
+  if (B * L > 0 && any_null({x, dt, Bm, Cm, y})) return LR_E_NULLPTR;
+  if (seg > 0 && B * L > 0 && ckpt == nullptr) return LR_E_NULLPTR;
+  if (!all_aligned({x, dt, A, Bm, Cm, Dskip, h0, y, h_last, ckpt})) return LR_E_ALIGN;
+  if (B == 0) return LR_OK;
+  return hip_status(lr::launch_ssd_fwd(disc, x, dt, A, Bm, Cm, Dskip, h0, y, h_last, ckpt, B, L,
+                                       H, P, G, N, seg, static_cast<hipStream_t>(stream)));
+}
+
+size_t lr_ssd_scan_bwd_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G,
+                                       int64_t N, int64_t chunk, int64_t seg) {
+  if (check_ssd_sizes(LR_BF16, LR_DISC_ZOH, B, L, H, P, G, N, chunk, seg) != LR_OK || seg < 1)
+    return 0;
+  return lr::ssd_bwd_workspace(B, L, H, P, G, N, seg);
+}
+
+lr_status lr_ssd_scan_bwd(lr_dtype io, lr_disc disc, int64_t B, int64_t L, int64_t H, int64_t P,
+                          int64_t G, int64_t N, int64_t chunk, int64_t seg, const void* x,
+                          const void* dt, const float* A, const void* Bm, const void* Cm,
+                          const float* Dskip, const float* h0, const float* ckpt, const void* dy,
+                          const float* dh_last, void* dx, void* ddt, float* dA, void* dBm,
+                          void* dCm, float* dD, float* dh0, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  lr_status st = check_ssd_sizes(io, disc, B, L, H, P, G, N, chunk, seg);
+  if (st != LR_OK) return st;
+  if (seg < 1) return LR_E_SHAPE;
+  if (A == nullptr || dA == nullptr) return LR_E_NULLPTR;
+  if (B * L > 0 && any_null({x, dt, Bm, Cm, ckpt, dy, dx, ddt, dBm, dCm})) return LR_E_NULLPTR;
+  if (!all_aligned({x, dt, A, Bm, Cm, Dskip, h0, ckpt, dy, dh_last, dx, ddt, dA, dBm, dCm, dD,
+                    dh0, workspace}))
+    return LR_E_ALIGN;
+  const size_t need = lr::ssd_bwd_workspace(B, L, H, P, G, N, seg);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LR_E_WORKSPACE;
+  (void)h0;  // the entering state is ckpt[0]
+  return hip_status(lr::launch_ssd_bwd(disc, x, dt, A, Bm, Cm, Dskip, ckpt, dy, dh_last, dx, ddt,
+                                       dA, dBm, dCm, dD, dh0, workspace, B, L, H, P, G, N, seg,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+lr_status lr_gla_scan(lr_dtype io, int64_t B, int64_t L, int64_t H, int64_t K, int64_t V,
+                      int64_t chunk, const void* q, const void* k, const void* v, const void* g,
+                      const float* S0, void* o, float* S_last, void* stream) {
+  if (!valid_io(io)) return LR_E_DTYPE;
+  if (B < 0 || L < 0 || H < 1 || K < 1 || V < 1 || chunk < 1) return LR_E_SHAPE;
+  if (io != LR_BF16 || (K != 64 && K != 128) || V % 64 != 0 || chunk % 64 != 0)
+    return LR_E_UNSUPPORTED;
+  if (!elems_ok({B, L, H, K}) || !elems_ok({B, L, H, V}) || !elems_ok({B, H, K, V}))
+    return LR_E_OVERFLOW;
+  int64_t nwg = 1;
+  if (!mul_ok(nwg, B) || !mul_ok(nwg, H) || !mul_ok(nwg, V / 64) || nwg > kMaxGrid)
+    return LR_E_OVERFLOW;
+  if (B * L > 0 && any_null({q, k, v, g, o})) return LR_E_NULLPTR;
+  if (!all_aligned({q, k, v, g, S0, o, S_last})) return LR_E_ALIGN;
+  if (B == 0) return LR_OK;
+  return hip_status(lr::launch_gla_fwd(q, k, v, g, S0, o, S_last, B, L, H, K, V,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,107 @@
+"""Boundary tests that run without a GPU: liblr.so loads, exports every
+symbol declared in include/lr.h, and rejects invalid arguments with the
+documented status code before touching the device (fake, never-dereferenced
+pointer values are used; validation happens before any HIP call)."""
+import ctypes as C
+
+import pytest
+
+from ssm_selective_scan_amd import _lib
+
+OK, NULL, SHAPE, DTYPE, ALIGN, UNSUP, WS, OVF = 0, 1, 2, 3, 4, 5, 6, 7
+P = 0x10000      # a fake 16-byte-aligned device address (never dereferenced)
+MIS = 0x10008    # a fake misaligned one
+
+
+@pytest.fixture(scope="module")
+def L():
+    return _lib.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = _lib.header_symbols()
+    assert len(names) == 8, names
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(_lib.SIGNATURES)
+
+
+def test_version_and_status_strings(L):
+    assert L.lr_version().decode().startswith("liblr")
+    for code in range(9):
+        assert L.lr_status_string(code).decode().startswith(_lib.STATUS[code])
+
+
+def diag(L, io=0, B=1, Lq=8, D=4, a=P, b=P, h0=None, h=P, hl=None):
+    return L.lr_diag_scan(io, B, Lq, D, a, b, h0, h, hl, None)
+
+
+def test_diag_validation(L):
+    assert diag(L, io=2) == DTYPE
+    assert diag(L, D=0) == SHAPE
+    assert diag(L, B=-1) == SHAPE
+    assert diag(L, a=None) == NULL
+    assert diag(L, h=None) == NULL
+    assert diag(L, b=MIS) == ALIGN
+    assert diag(L, h0=MIS) == ALIGN
+    assert diag(L, B=1 << 40, Lq=1 << 20, D=1 << 10) == OVF
+    # empty batch: nothing to do, no device access
+    assert diag(L, B=0, a=None, b=None, h=None) == OK
+
+
+def sel(L, io=1, disc=0, B=1, Lq=8, D=4, N=16, x=P, dt=P, A=P, Bm=P, Cm=P, y=P):
+    return L.lr_selective_scan(io, disc, B, Lq, D, N, x, dt, A, Bm, Cm, None, None, y, None, None)
+
+
+def test_selective_validation(L):
+    assert sel(L, disc=7) == DTYPE
+    assert sel(L, N=0) == SHAPE
+    assert sel(L, N=65) == UNSUP
+    assert sel(L, A=None) == NULL
+    assert sel(L, Cm=None) == NULL
+    assert sel(L, dt=MIS) == ALIGN
+    assert sel(L, B=0, x=None, dt=None, Bm=None, Cm=None, y=None) == OK
+
+
+def ssd(L, io=1, disc=0, B=1, Lq=64, H=2, Pp=64, G=1, N=128, chunk=64, seg=0, x=P, ck=None):
+    return L.lr_ssd_scan(io, disc, B, Lq, H, Pp, G, N, chunk, seg, x, P, P, P, P, None, None, P,
+                         None, ck, None)
+
+
+def test_ssd_validation(L):
+    assert ssd(L, io=0) == UNSUP          # fp32 I/O is not compiled for SSD
+    assert ssd(L, H=3, G=2) == SHAPE
+    assert ssd(L, Pp=48) == UNSUP
+    assert ssd(L, N=96) == UNSUP
+    assert ssd(L, chunk=100) == UNSUP
+    assert ssd(L, seg=64) == NULL         # seg > 0 needs ckpt
+    assert ssd(L, seg=96, ck=P) == UNSUP
+    assert ssd(L, x=None) == NULL
+    assert ssd(L, x=MIS) == ALIGN
+    assert ssd(L, B=0, x=None) == OK
+
+
+def test_ssd_bwd_validation(L):
+    ws = L.lr_ssd_scan_bwd_workspace_bytes(1, 64, 2, 64, 1, 128, 64, 64)
+    args = [1, 0, 1, 64, 2, 64, 1, 128, 64, 64, P, P, P, P, P, None, None, P, P, None,
+            P, P, P, P, P, None, None]
+    if ws > 0:
+        assert L.lr_ssd_scan_bwd(*args, None, 0, None) == WS
+        assert L.lr_ssd_scan_bwd(*args, P, ws - 1, None) == WS
+    bad = list(args)
+    bad[9] = 0     # seg = 0
+    assert L.lr_ssd_scan_bwd(*bad, P, ws, None) == SHAPE
+    bad = list(args)
+    bad[17] = None  # ckpt
+    assert L.lr_ssd_scan_bwd(*bad, P, ws, None) == NULL
+
+
+def test_gla_validation(L):
+    def gla(io=1, K=128, V=128, chunk=64, q=P, g=P):
+        return L.lr_gla_scan(io, 1, 64, 2, K, V, chunk, q, P, P, g, None, P, None, None)
+    assert gla(io=3) == DTYPE
+    assert gla(K=32) == UNSUP
+    assert gla(V=96) == UNSUP
+    assert gla(chunk=32) == UNSUP
+    assert gla(q=None) == NULL
+    assert gla(g=MIS) == ALIGN
