@@ -1,0 +1,345 @@
+"""Benchmark of the linear-recurrence scans on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one pass of the headline workload over one batch of synthetic
+input already resident in HBM: the Mamba-1 selective scan with ZOH and fused
+readout at B=8, L=4096, D=2048, N=16, bf16 I/O, fp32 state (the workload the
+prefill tokens/s metric is quoted on).  W untimed warm-up steps, then K timed
+steps bracketed by torch.cuda.synchronize(); the kernel's own duration is
+taken with HIP events recorded on the launch stream.  Input/output buffer
+sets are rotated so that the 256 MB Infinity Cache cannot hold a step's
+working set from the previous step.
+
+The same run also measures the other four workloads (diagonal scan, SSD
+forward, GLA forward, SSD forward + backward with segment checkpoints) and a
+plain device copy for the achievable-bandwidth reference, and times the fp64
+CPU oracle on a bounded sample of the headline workload (cpu_baseline).
+One JSON line is printed.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import lrgen  # noqa: E402
+import ssm_selective_scan_amd as lr  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 MFMA
+# fp32 VALU issue rate without packed math: 256 CU x 4 SIMD x 16 lanes x 2.4 GHz
+VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+METRIC = "SSD/selective-scan prefill tokens/s + achieved HBM GB/s vs MI355X peak"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def dev(t):
+    x = torch.from_numpy(np.ascontiguousarray(t.values)).cuda()
+    return x.to(torch.bfloat16) if t.io == "bf16" else x
+
+
+def rotations(nbytes, floor=3):
+    """Buffer sets needed so consecutive launches never share a cached set."""
+    return max(floor, int(np.ceil(768e6 / max(nbytes, 1))) + 1)
+
+
+def time_launches(fn, sets, warmup, iters):
+    """Average duration (s) of fn(set) measured with events on the launch
+    stream, cycling through the buffer sets."""
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        fn(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(iters)]
+    for i in range(iters):
+        ev[i][0].record(stream)
+        fn(sets[i % len(sets)])
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    return ms.mean() / 1e3, ms
+
+
+# --------------------------------------------------------------------------
+# workloads
+# --------------------------------------------------------------------------
+def selective_setup(g):
+    x, dt, Bm, Cm = dev(g.t("x")), dev(g.t("dt")), dev(g.t("B")), dev(g.t("C"))
+    A, Dk = dev(g.t("A")), dev(g.t("Dskip"))
+    per = sum(t.numel() * t.element_size() for t in (x, dt, Bm, Cm)) * 3 // 2
+    R = rotations(per)
+    sets = [dict(x=x if i == 0 else x.clone(), dt=dt if i == 0 else dt.clone(),
+                 Bm=Bm if i == 0 else Bm.clone(), Cm=Cm if i == 0 else Cm.clone(),
+                 y=torch.empty_like(x)) for i in range(R)]
+
+    def fn(s):
+        lr.lr_selective_scan(s["x"], s["dt"], A, s["Bm"], s["Cm"], Dk, disc="zoh", y=s["y"])
+    return fn, sets
+
+
+def selective_bytes(p):
+    B, L, D, N = p["B"], p["L"], p["D"], p["N"]
+    return 3 * B * L * D * 2 + 2 * B * L * N * 2 + D * N * 4 + D * 4
+
+
+def sel_valu_ops(p):
+    # fused ZOH update per (b, t, d, n): e = 2^(dt A log2e) (1 mul + 1 exp),
+    # v = (B x)/A (2 mul), h = e (h + v) - v (add + fma), y += C h (fma)
+    B, L, D, N = p["B"], p["L"], p["D"], p["N"]
+    return 7 * B * L * D * N
+
+
+def measure_diag(warmup, iters):
+    g = lrgen.make(1)
+    a, b = dev(g.t("a")), dev(g.t("b"))
+    sets = [dict(a=a, b=b, h=torch.empty_like(a))]
+    t, _ = time_launches(lambda s: lr.lr_diag_scan(s["a"], s["b"], h=s["h"]), sets, warmup, iters)
+    p = g.params
+    nb = 3 * p["B"] * p["L"] * p["D"] * 4
+    return dict(workload=lrgen.NAMES[1], kernel="diag_scan_kernel", us=t * 1e6,
+                tokens_per_s=p["B"] * p["L"] / t, elems_per_s=p["B"] * p["L"] * p["D"] / t,
+                alg_bytes=nb, GBs=nb / t / 1e9, hbm_frac=nb / t / 1e9 / HBM_PEAK_GBS,
+                note="3 MB working set: launch/latency bound")
+
+
+def measure_ssd(warmup, iters):
+    g = lrgen.make(3)
+    p = g.params
+    x, dt, Bm, Cm = dev(g.t("x")), dev(g.t("dt")), dev(g.t("B")), dev(g.t("C"))
+    A, Dk = dev(g.t("A")), dev(g.t("Dskip"))
+    per = sum(t.numel() * t.element_size() for t in (x, dt, Bm, Cm)) + x.numel() * 2
+    sets = [dict(x=x if i == 0 else x.clone(), dt=dt if i == 0 else dt.clone(),
+                 Bm=Bm if i == 0 else Bm.clone(), Cm=Cm if i == 0 else Cm.clone(),
+                 y=torch.empty_like(x)) for i in range(rotations(per))]
+    t, _ = time_launches(lambda s: lr.lr_ssd_scan(s["x"], s["dt"], A, s["Bm"], s["Cm"], Dk,
+                                                  chunk=p["chunk"], y=s["y"]),
+                         sets, warmup, iters)
+    B, L, H, P, N = p["B"], p["L"], p["H"], p["P"], p["N"]
+    nb = 2 * B * L * H * P * 2 + B * L * H * 2 + 2 * B * L * N * 2 + 2 * H * 4
+    fl = ssd_mfma_flops(B, L, H, P, N)
+    return dict(workload=lrgen.NAMES[3], kernel="chunk_fwd_kernel<SSD>", us=t * 1e6,
+                tokens_per_s=B * L / t, elems_per_s=B * L * H * P / t, alg_bytes=nb,
+                GBs=nb / t / 1e9, hbm_frac=nb / t / 1e9 / HBM_PEAK_GBS,
+                mfma_tflops=fl / t / 1e12, mfma_frac=fl / t / 1e12 / MFMA_BF16_PEAK_TFLOPS)
+
+
+def ssd_mfma_flops(B, L, H, P, N, Q=64):
+    # MFMA work of the 64-token block form per (b, h, block): C B^T on the
+    # causal 10 of 16 tiles, M X (causal), C h_prev, B_w^T X
+    per_blk = 2 * (10 * 16 * 16 * N + (Q * Q // 2 + Q * 8) * P + Q * N * P + N * Q * P)
+    return B * H * ((L + Q - 1) // Q) * per_blk
+
+
+def measure_gla(warmup, iters):
+    g = lrgen.make(4)
+    p = g.params
+    q, k, v, gg = dev(g.t("q")), dev(g.t("k")), dev(g.t("v")), dev(g.t("g"))
+    per = 4 * q.numel() * 2
+    sets = [dict(q=q if i == 0 else q.clone(), k=k if i == 0 else k.clone(),
+                 v=v if i == 0 else v.clone(), g=gg, o=torch.empty_like(v))
+            for i in range(rotations(per, floor=2))]
+    t, _ = time_launches(lambda s: lr.lr_gla_scan(s["q"], s["k"], s["v"], s["g"],
+                                                  chunk=p["chunk"], o=s["o"]),
+                         sets, warmup, iters)
+    B, L, H, K, V = p["B"], p["L"], p["H"], p["K"], p["V"]
+    nb = 2 * B * L * H * K * 2 + 2 * B * L * H * V * 2 + B * L * H * 2
+    fl = (V // 64) * ssd_mfma_flops(B, L, H, 64, K)
+    return dict(workload=lrgen.NAMES[4], kernel="chunk_fwd_kernel<GLA>", us=t * 1e6,
+                tokens_per_s=B * L / t, elems_per_s=B * L * H * V / t, alg_bytes=nb,
+                GBs=nb / t / 1e9, hbm_frac=nb / t / 1e9 / HBM_PEAK_GBS,
+                mfma_tflops=fl / t / 1e12, mfma_frac=fl / t / 1e12 / MFMA_BF16_PEAK_TFLOPS)
+
+
+def measure_ssd_bwd(warmup, iters):
+    g = lrgen.make(5)
+    p = g.params
+    B, L, H, P, G, N, seg = p["B"], p["L"], p["H"], p["P"], p["G"], p["N"], p["seg"]
+    x, dt, Bm, Cm = dev(g.t("x")), dev(g.t("dt")), dev(g.t("B")), dev(g.t("C"))
+    A, Dk, dy = dev(g.t("A")), dev(g.t("Dskip")), dev(g.t("dy"))
+    y = torch.empty_like(x)
+    nseg = (L + seg - 1) // seg
+    ckpt = torch.empty(nseg, B, H, P, N, device="cuda", dtype=torch.float32)
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    tf, _ = time_launches(lambda s: lr.lr_ssd_scan(x, dt, A, Bm, Cm, Dk, chunk=p["chunk"],
+                                                   seg=seg, y=y, ckpt=ckpt),
+                          [None], warmup, iters)
+    ws_bytes = lr.lr_ssd_scan_bwd_workspace_bytes(B, L, H, P, G, N, p["chunk"], seg)
+    out = dict(workload=lrgen.NAMES[5], fwd_us=tf * 1e6,
+               ckpt_bytes=ckpt.numel() * 4,
+               full_state_bytes=L * B * H * P * N * 4,
+               state_mem_ratio=(L * B * H * P * N * 4) / (ckpt.numel() * 4 + ws_bytes),
+               bwd_workspace_bytes=ws_bytes)
+    fwd_bytes = 2 * B * L * H * P * 2 + B * L * H * 2 + 2 * B * L * N * 2 + ckpt.numel() * 4
+    out["fwd_GBs"] = fwd_bytes / tf / 1e9
+    try:
+        ws = torch.empty(max(ws_bytes, 16), device="cuda", dtype=torch.uint8)
+        tb, _ = time_launches(lambda s: lr.lr_ssd_scan_bwd(x, dt, A, Bm, Cm, Dk, None, ckpt, dy,
+                                                           chunk=p["chunk"], seg=seg,
+                                                           workspace=ws),
+                              [None], warmup, iters)
+        bwd_bytes = (3 * B * L * H * P * 2 + 2 * B * L * H * 2 + 4 * B * L * N * 2
+                     + ckpt.numel() * 4)
+        out.update(bwd_us=tb * 1e6, bwd_GBs=bwd_bytes / tb / 1e9,
+                   fwd_bwd_tokens_per_s=B * L / (tf + tb),
+                   peak_alloc_delta_bytes=torch.cuda.max_memory_allocated() - base)
+    except lr.LrError as e:
+        out["bwd"] = f"unavailable: {e}"
+    return out
+
+
+def copy_bandwidth(nbytes=1 << 30, iters=10):
+    a = torch.empty(nbytes // 4, device="cuda", dtype=torch.float32).fill_(1.0)
+    b = torch.empty_like(a)
+    t, _ = time_launches(lambda s: b.copy_(a), [None], 3, iters)
+    return 2 * nbytes / t / 1e9
+
+
+# --------------------------------------------------------------------------
+# CPU oracle baseline (bounded sample of the headline workload)
+# --------------------------------------------------------------------------
+def cpu_baseline(g, rows):
+    import oracle  # the oracle is test infrastructure; only this leg uses it
+    t0 = time.perf_counter()
+    oracle.selective_scan(g["x"][:rows], g["dt"][:rows], g["A"], g["B"][:rows], g["C"][:rows],
+                          g["Dskip"])
+    dt = time.perf_counter() - t0
+    toks = rows * g.params["L"]
+    return dict(value=toks / dt, unit="tokens/s", cores=1, kind="oracle",
+                sample=f"selective scan, {rows} of {g.params['B']} batch rows x full "
+                       f"L={g.params['L']}, D={g.params['D']}, N={g.params['N']}, fp64 numpy, "
+                       f"one thread, {dt:.1f} s")
+
+
+def load_traffic():
+    """HBM traffic of the selective kernel from the committed rocprofv3 PMC
+    summary, if it was taken on the current kernel source."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "selective_scan_cfg2_traffic.txt")
+    src = os.path.join(ROOT, "ssm_selective_scan_amd", "csrc", "selective_scan.hip")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if kv.get("kernel_src_sha256_16") != sha:
+        return None
+    return float(kv["traffic_bytes_per_launch"])
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--headline-only", action="store_true",
+                    help="time only the headline workload (for profiler runs)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-rows", type=int, default=8)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the scans shard by batch/head with no exchange, see DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU available", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+
+    if args.copy_probe:
+        bw = copy_bandwidth()
+        print(json.dumps({"copy_probe_GBs": bw, "bytes_per_copy": 2 * (1 << 30)}))
+        return
+
+    log(f"[bench] liblr: {lr.lr_version()}")
+    g = lrgen.make(2)
+    p = g.params
+    fn, sets = selective_setup(g)
+    log(f"[bench] headline {lrgen.NAMES[2]}: {len(sets)} rotating buffer sets")
+
+    for i in range(args.warmup):
+        fn(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        fn(sets[i % len(sets)])
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    ms_step = wall * 1e3 / args.steps
+    tokens = p["B"] * p["L"]
+    log(f"[bench] headline: {ms_step:.3f} ms/step wall, kernel {kern_ms.mean() * 1e3:.1f} us "
+        f"(min {kern_ms.min() * 1e3:.1f}, max {kern_ms.max() * 1e3:.1f})")
+
+    kt = kern_ms.mean() / 1e3
+    nbytes = selective_bytes(p)
+    ops = sel_valu_ops(p)
+    traffic = load_traffic()
+    roofline = {"bound": "alu", "achieved": ops / kt / 1e12, "peak": VALU_PEAK_TOPS,
+                "unit": "Tops/s (fp32 VALU lane-ops)",
+                "frac": ops / kt / 1e12 / VALU_PEAK_TOPS, "traffic": traffic,
+                "kernel": "selective_scan_kernel<bf16, ZOH>",
+                "alg_ops_per_launch": ops, "alg_bytes_per_launch": nbytes,
+                "hbm_GBs": nbytes / kt / 1e9, "hbm_frac": nbytes / kt / 1e9 / HBM_PEAK_GBS}
+
+    result = {
+        "metric": METRIC, "value": tokens / (ms_step / 1e3), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": lrgen.NAMES[2], "B": p["B"], "L": p["L"], "D": p["D"],
+                   "N": p["N"], "io": "bf16", "state": "f32", "disc": "zoh"},
+        "kernel_us": kern_ms.mean() * 1e3,
+        "roofline": roofline,
+    }
+    del sets
+    torch.cuda.empty_cache()
+
+    if not args.headline_only:
+        extra = {}
+        for name, f in (("diag", measure_diag), ("ssd", measure_ssd), ("gla", measure_gla),
+                        ("ssd_fwd_bwd", measure_ssd_bwd)):
+            log(f"[bench] measuring {name}")
+            try:
+                extra[name] = f(3, 20)
+            except Exception as e:  # report, keep the headline line
+                extra[name] = {"error": repr(e)}
+            torch.cuda.empty_cache()
+        extra["copy_GBs"] = copy_bandwidth()
+        result["workloads"] = extra
+
+    if not args.no_cpu:
+        log("[bench] cpu_baseline (fp64 oracle)")
+        result["cpu_baseline"] = cpu_baseline(g, args.cpu_rows)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -100,9 +100,46 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkFwdArgs g) {
   }
 
   const int64_t nblk = (g.L + kCQ - 1) / kCQ;
-  for (int64_t blk = 0; blk < nblk; ++blk) {
+
+  // Register staging of one block: C and B rows (NS/32 16-byte chunks of each
+  // per thread), x (2 chunks per thread, lanes walk tokens) and the gate
+  // (wave 0, lane = token).  The next block's loads are issued as soon as
+  // the current block is in LDS, so their latency overlaps the MFMA work.
+  constexpr int kCB = (kCQ * (NS / 8)) / 256;
+  constexpr int kXC = (kCQ * (kCPS / 8)) / 256;
+  u16x8 creg[kCB], breg[kCB], xreg[kXC];
+  uint16_t greg = 0;
+  int nv_next = 0;
+  auto prefetch = [&](int64_t blk) {
     const int64_t t0 = blk * kCQ;
     const int nv = static_cast<int>((g.L - t0) < kCQ ? (g.L - t0) : kCQ);
+    nv_next = nv;
+#pragma unroll
+    for (int k = 0; k < kCB; ++k) {
+      const int idx = tid + 256 * k;
+      const int r = idx / (NS / 8), c = idx % (NS / 8);
+      creg[k] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      breg[k] = creg[k];
+      if (r < nv) {
+        const int64_t off = (b * g.L + t0 + r) * g.bc_row + bcoff + 8 * c;
+        creg[k] = *reinterpret_cast<const u16x8*>(g.Cm + off);
+        breg[k] = *reinterpret_cast<const u16x8*>(g.Bm + off);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kXC; ++k) {
+      const int idx = tid + 256 * k;
+      const int s = idx & 63, c = idx >> 6;
+      xreg[k] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      if (s < nv) xreg[k] = *reinterpret_cast<const u16x8*>(g.x + (b * g.L + t0 + s) * xrow + xoff + 8 * c);
+    }
+    if (w == 0 && lane < nv) greg = g.gate[(b * g.L + t0 + lane) * g.H + h];
+  };
+  if (nblk > 0) prefetch(0);
+
+  for (int64_t blk = 0; blk < nblk; ++blk) {
+    const int64_t t0 = blk * kCQ;
+    const int nv = nv_next;
 
     if (g.ckpt != nullptr && (t0 % g.seg) == 0) {
       float* cp = g.ckpt + ((t0 / g.seg) * g.B * g.H) * g.P * NS + sbase;
@@ -114,14 +151,13 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkFwdArgs g) {
     // ---- per-token decay and input scale (wave 0, lane = token)
     if (w == 0) {
       const bool ok = lane < nv;
-      const int64_t gi = (b * g.L + t0 + lane) * g.H + h;
       float l2, ph;
       if (MODE == kModeGla) {
-        const float gv = ok ? bf2f(g.gate[gi]) : 1.f;
+        const float gv = ok ? bf2f(greg) : 1.f;
         l2 = fast_log2(gv);
         ph = ok ? 1.f : 0.f;
       } else {
-        const float dtv = ok ? bf2f(g.gate[gi]) : 0.f;
+        const float dtv = ok ? bf2f(greg) : 0.f;
         const float lam = dtv * Ah;
         l2 = lam * kLog2e;
         if (MODE == kModeSsdEuler) {
@@ -134,27 +170,23 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkFwdArgs g) {
       sm.cum[lane] = wave_incl_sum(l2);
       sm.phi[lane] = ph;
     }
-    // ---- stage C and B rows (16-byte loads, coalesced along n)
-    for (int idx = tid; idx < kCQ * (NS / 8); idx += 256) {
-      const int r = idx / (NS / 8), c = idx % (NS / 8);
-      u16x8 vc = {0, 0, 0, 0, 0, 0, 0, 0}, vb = vc;
-      if (r < nv) {
-        const int64_t off = (b * g.L + t0 + r) * g.bc_row + bcoff + 8 * c;
-        vc = *reinterpret_cast<const u16x8*>(g.Cm + off);
-        vb = *reinterpret_cast<const u16x8*>(g.Bm + off);
-      }
-      *reinterpret_cast<u16x8*>(sm.Cs + r * kLdN + 8 * c) = vc;
-      *reinterpret_cast<u16x8*>(sm.Bs + r * kLdN + 8 * c) = vb;
-    }
-    // ---- stage x transposed: XT[p][s] (lanes walk tokens -> conflict-free writes)
-    for (int idx = tid; idx < kCQ * (kCPS / 8); idx += 256) {
-      const int s = idx & 63, c = idx >> 6;
-      u16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (s < nv) v = *reinterpret_cast<const u16x8*>(g.x + (b * g.L + t0 + s) * xrow + xoff + 8 * c);
+    // ---- staged registers -> LDS: C, B row-major; x transposed XT[p][s]
 #pragma unroll
-      for (int i = 0; i < 8; ++i) sm.XT[(8 * c + i) * kLdT + s] = v[i];
+    for (int k = 0; k < kCB; ++k) {
+      const int idx = tid + 256 * k;
+      const int r = idx / (NS / 8), c = idx % (NS / 8);
+      *reinterpret_cast<u16x8*>(sm.Cs + r * kLdN + 8 * c) = creg[k];
+      *reinterpret_cast<u16x8*>(sm.Bs + r * kLdN + 8 * c) = breg[k];
+    }
+#pragma unroll
+    for (int k = 0; k < kXC; ++k) {
+      const int idx = tid + 256 * k;
+      const int s = idx & 63, c = idx >> 6;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sm.XT[(8 * c + i) * kLdT + s] = xreg[k][i];
     }
     __syncthreads();
+    if (blk + 1 < nblk) prefetch(blk + 1);
 
     const float cum_end = sm.cum[kCQ - 1];
     // ---- B scaled by 2^(cum_end - cum_s) phi_s, transposed: BwT[n][s]

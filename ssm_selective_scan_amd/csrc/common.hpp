@@ -26,11 +26,9 @@ typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ float bf2f(uint16_t v) {
   return __uint_as_float(static_cast<uint32_t>(v) << 16);
 }
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
 // I/O element types: float (LR_F32) or uint16_t holding bf16 bits (LR_BF16).
@@ -38,10 +36,12 @@ template <typename T> struct Io;
 template <> struct Io<float> {
   __device__ __forceinline__ static float load(const float* p) { return *p; }
   __device__ __forceinline__ static void store(float* p, float v) { *p = v; }
+  __device__ __forceinline__ static float cvt(float v) { return v; }
 };
 template <> struct Io<uint16_t> {
   __device__ __forceinline__ static float load(const uint16_t* p) { return bf2f(*p); }
   __device__ __forceinline__ static void store(uint16_t* p, float v) { *p = f2bf(v); }
+  __device__ __forceinline__ static float cvt(uint16_t v) { return bf2f(v); }
 };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

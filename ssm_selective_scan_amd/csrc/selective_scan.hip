@@ -8,11 +8,12 @@
 //
 // Work split: a workgroup owns one batch row and 64 consecutive channels d
 // (lane = d, so every per-token load and store is a coalesced row segment).
-// Its waves split the state index n: wave w owns n in [4w, 4w+4), so the
-// (d, n) chains it carries stay in registers for the whole sequence and the
-// hidden state never touches memory.  Tokens are staged through LDS in tiles
-// of TT steps; each wave writes its partial readout sum_n C h to LDS and the
-// workgroup adds the partials, D.x, and stores y.
+// Its waves split the state index n: wave w owns n in [NPW w, NPW w + NPW),
+// so the (d, n) chains it carries stay in registers for the whole sequence
+// and the hidden state never touches memory.  Tokens are staged through LDS
+// in tiles of TT steps (the next tile's global loads are in flight while the
+// current one is computed); each wave writes its partial readout
+// sum_n C h to LDS and the workgroup adds the partials and D.x and stores y.
 //
 // Per (t, d, n) the ZOH update costs one v_exp_f32 and six VALU operations:
 //   e = 2^(dt A log2e);  v = (B x)/A;  h = e (h + v) - v;  y += C h
@@ -25,103 +26,253 @@
 
 namespace lr {
 
-constexpr int kSelNPW = 4;     // state indices per wave
 constexpr int kSelCT = 64;     // channels per workgroup (one per lane)
 
 enum { kDiscZoh = 0, kDiscEuler = 1 };
 
-template <typename T, int DISC, bool PRECISE, int TT>
+// Register staging of one tile of TT tokens.  x and dt are moved in 8-channel
+// chunks (16-byte loads for bf16 when VEC, i.e. D % 8 == 0), B and C as the
+// contiguous TT*N block of the tile.  All per-thread offsets are 32-bit and
+// computed once; each tile only moves the (wave-uniform) base pointers.
+template <typename T, int TT, int MK, bool VEC>
+struct SelStage {
+  static constexpr int kMaxE = 2;   // B/C elements per thread (threads >= 16 N)
+  T xr[MK][8], dr[MK][8];           // raw I/O words until they are written to LDS
+  T br[kMaxE], cr[kMaxE];
+  int xoff[MK], xlds[MK], xrow[MK];  // global offset, LDS offset, token of each chunk
+  int ce[kMaxE], clds[kMaxE], crow[kMaxE];
+
+  __device__ __forceinline__ void init(int64_t D, int N) {
+    const int tid = threadIdx.x, nthr = blockDim.x;
+#pragma unroll
+    for (int k = 0; k < MK; ++k) {
+      const int c = tid + k * nthr;
+      xrow[k] = c < TT * 8 ? (c >> 3) : TT;     // TT marks an unused slot
+      xoff[k] = (c >> 3) * static_cast<int>(D) + 8 * (c & 7);
+      xlds[k] = (c >> 3) * 64 + 8 * (c & 7);
+    }
+#pragma unroll
+    for (int k = 0; k < kMaxE; ++k) {
+      const int e = tid + k * nthr;
+      crow[k] = e / N;
+      ce[k] = e;
+      clds[k] = crow[k] * 64 + (e - crow[k] * N);
+    }
+  }
+
+  // x0, dt0: tile base (token t0, channel d0); B0, C0: tile base of Bm, Cm.
+  // nt = tokens of the tile inside the sequence; dcols = channels < D left.
+  __device__ __forceinline__ void load(const T* x0, const T* dt0, const T* B0, const T* C0, int nt,
+                                       int dcols, int N) {
+#pragma unroll
+    for (int k = 0; k < MK; ++k) {
+      const int c8 = (xlds[k] & 63);
+      if (VEC && xrow[k] < nt && c8 + 8 <= dcols) {
+        if constexpr (sizeof(T) == 2) {
+          const u16x8 vx = *reinterpret_cast<const u16x8*>(x0 + xoff[k]);
+          const u16x8 vd = *reinterpret_cast<const u16x8*>(dt0 + xoff[k]);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) { xr[k][i] = vx[i]; dr[k][i] = vd[i]; }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; i += 4) {
+            const float4 vx = *reinterpret_cast<const float4*>(x0 + xoff[k] + i);
+            const float4 vd = *reinterpret_cast<const float4*>(dt0 + xoff[k] + i);
+            xr[k][i] = vx.x; xr[k][i + 1] = vx.y; xr[k][i + 2] = vx.z; xr[k][i + 3] = vx.w;
+            dr[k][i] = vd.x; dr[k][i + 1] = vd.y; dr[k][i + 2] = vd.z; dr[k][i + 3] = vd.w;
+          }
+        }
+      } else if (!VEC) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const bool ok = xrow[k] < nt && c8 + i < dcols;
+          xr[k][i] = ok ? x0[xoff[k] + i] : T(0);
+          dr[k][i] = ok ? dt0[xoff[k] + i] : T(0);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) { xr[k][i] = T(0); dr[k][i] = T(0); }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kMaxE; ++k) {
+      const bool ok = ce[k] < nt * N;
+      br[k] = ok ? B0[ce[k]] : T(0);
+      cr[k] = ok ? C0[ce[k]] : T(0);
+    }
+  }
+
+  __device__ __forceinline__ void store(float* xs, float* dts, float* Bs, float* Cs) const {
+#pragma unroll
+    for (int k = 0; k < MK; ++k) {
+      if (xrow[k] < TT) {
+        float fx[8], fd[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) { fx[i] = Io<T>::cvt(xr[k][i]); fd[i] = Io<T>::cvt(dr[k][i]); }
+        float* px = xs + xlds[k];
+        float* pd = dts + xlds[k];
+        *reinterpret_cast<float4*>(px) = make_float4(fx[0], fx[1], fx[2], fx[3]);
+        *reinterpret_cast<float4*>(px + 4) = make_float4(fx[4], fx[5], fx[6], fx[7]);
+        *reinterpret_cast<float4*>(pd) = make_float4(fd[0], fd[1], fd[2], fd[3]);
+        *reinterpret_cast<float4*>(pd + 4) = make_float4(fd[4], fd[5], fd[6], fd[7]);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kMaxE; ++k) {
+      if (crow[k] < TT) {
+        Bs[clds[k]] = Io<T>::cvt(br[k]);
+        Cs[clds[k]] = Io<T>::cvt(cr[k]);
+      }
+    }
+  }
+};
+
+// One group of GS steps of this wave's NPW chains: the LDS values it needs
+// (x, dt of the lane's channel; B, C of the wave's state indices) and the
+// recurrence over them.
+template <int NPW, int GS>
+struct SelGroup {
+  float xv[GS], dv[GS], bb[GS][NPW], cc[GS][NPW];
+
+  __device__ __forceinline__ void read(const float* xs, const float* dts, const float* Bs,
+                                       const float* Cs, int g0, int lane, int n0) {
+#pragma unroll
+    for (int i = 0; i < GS; ++i) {
+      const int tt = g0 + i;
+      xv[i] = xs[tt * 64 + lane];
+      dv[i] = dts[tt * 64 + lane];
+      if constexpr (NPW == 4) {
+        const float4 b4 = *reinterpret_cast<const float4*>(Bs + tt * 64 + n0);
+        const float4 c4 = *reinterpret_cast<const float4*>(Cs + tt * 64 + n0);
+        bb[i][0] = b4.x; bb[i][1] = b4.y; bb[i][2] = b4.z; bb[i][3] = b4.w;
+        cc[i][0] = c4.x; cc[i][1] = c4.y; cc[i][2] = c4.z; cc[i][3] = c4.w;
+      } else {
+        const float2 b2 = *reinterpret_cast<const float2*>(Bs + tt * 64 + n0);
+        const float2 c2 = *reinterpret_cast<const float2*>(Cs + tt * 64 + n0);
+        bb[i][0] = b2.x; bb[i][1] = b2.y;
+        cc[i][0] = c2.x; cc[i][1] = c2.y;
+      }
+    }
+  }
+
+  // yp_lane: this lane's partial-readout slot of the group's first step
+  template <int DISC, bool PRECISE>
+  __device__ __forceinline__ void step(float (&h)[NPW], const float (&A2)[NPW],
+                                       const float (&iA)[NPW], const float (&An)[NPW],
+                                       float* yp_lane) const {
+    float yv[GS];
+#pragma unroll
+    for (int i = 0; i < GS; ++i) {
+      const float xt = xv[i], dtt = dv[i];
+      const float ux = (DISC == kDiscEuler) ? dtt * xt : 0.f;
+      float yj[NPW];
+#pragma unroll
+      for (int j = 0; j < NPW; ++j) {
+        const float e = fast_exp2(dtt * A2[j]);
+        if (DISC == kDiscEuler) {
+          h[j] = fmaf(e, h[j], bb[i][j] * ux);
+        } else if (!PRECISE) {
+          const float v = (bb[i][j] * xt) * iA[j];
+          h[j] = fmaf(e, h[j] + v, -v);
+        } else {
+          const float l = dtt * An[j];
+          const float ser = dtt * fmaf(l, fmaf(l, fmaf(l, 1.f / 24.f, 1.f / 6.f), 0.5f), 1.f);
+          const float phi = fabsf(l) < 0.1f ? ser : (e - 1.f) * iA[j];
+          h[j] = fmaf(e, h[j], phi * (bb[i][j] * xt));
+        }
+        yj[j] = cc[i][j] * h[j];
+      }
+      yv[i] = (NPW == 4) ? (yj[0] + yj[1 % NPW]) + (yj[2 % NPW] + yj[3 % NPW])
+                         : yj[0] + yj[1 % NPW];
+    }
+#pragma unroll
+    for (int i = 0; i < GS; ++i) yp_lane[i * 64] = yv[i];
+  }
+};
+
+template <typename T, int DISC, bool PRECISE, int TT, int MK, int NPW, int GS, bool VEC>
 __device__ __forceinline__ void selective_body(
     const T* __restrict__ x, const T* __restrict__ dt, const T* __restrict__ Bm,
-    const T* __restrict__ Cm, const float* __restrict__ Dskip, T* __restrict__ y,
-    float* __restrict__ smem, float (&h)[kSelNPW], const float (&A2)[kSelNPW],
-    const float (&iA)[kSelNPW], const float (&An)[kSelNPW], int64_t bi, int64_t d0, int64_t L,
-    int64_t D, int N) {
+    const T* __restrict__ Cm, T* __restrict__ y, float* __restrict__ smem, float (&h)[NPW],
+    const float (&A2)[NPW], const float (&iA)[NPW], const float (&An)[NPW], int64_t bi,
+    int64_t d0, int64_t L, int64_t D, int N) {
   const int tid = threadIdx.x, nthr = blockDim.x;
-  const int w = tid >> 6, lane = tid & 63;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int nw = nthr >> 6;
-  const int n0 = w * kSelNPW;
+  const int n0 = w * NPW;
   float* xs = smem;               // [TT][64]
   float* dts = xs + TT * 64;      // [TT][64]
-  float* Bs = dts + TT * 64;      // [TT][64]  (n < N used)
+  float* Bs = dts + TT * 64;      // [TT][64]  columns n >= N stay zero
   float* Cs = Bs + TT * 64;       // [TT][64]
   float* Dk = Cs + TT * 64;       // [64]
   float* yp = Dk + 64;            // [nw][TT][64]
+  const int dcols = static_cast<int>((D - d0) < 64 ? (D - d0) : 64);
 
+  // per-thread output coordinates of the reduce phase: column dd, rows
+  // r0, r0 + nw, ...  (32-bit offsets from the tile's base pointer)
+  const int dd = tid & 63, r0 = tid >> 6;
+  const int Di = static_cast<int>(D);
+
+  SelStage<T, TT, MK, VEC> st;
+  st.init(D, N);
+  const int64_t row0 = bi * L;
+  if (L > 0) {
+    const int nt = static_cast<int>(L < TT ? L : TT);
+    st.load(x + row0 * D + d0, dt + row0 * D + d0, Bm + row0 * N, Cm + row0 * N, nt, dcols, N);
+  }
   for (int64_t t0 = 0; t0 < L; t0 += TT) {
-    // ---- stage a tile of TT tokens
-    for (int idx = tid; idx < TT * 64; idx += nthr) {
-      const int tt = idx >> 6, dd = idx & 63;
-      const int64_t t = t0 + tt;
-      const bool ok = t < L && d0 + dd < D;
-      const int64_t off = (bi * L + t) * D + d0 + dd;
-      xs[idx] = ok ? Io<T>::load(x + off) : 0.f;
-      dts[idx] = ok ? Io<T>::load(dt + off) : 0.f;
-    }
-    for (int idx = tid; idx < TT * N; idx += nthr) {
-      const int tt = idx / N, n = idx - tt * N;
-      const int64_t t = t0 + tt;
-      const bool ok = t < L;
-      const int64_t off = (bi * L + t) * N + n;
-      Bs[tt * 64 + n] = ok ? Io<T>::load(Bm + off) : 0.f;
-      Cs[tt * 64 + n] = ok ? Io<T>::load(Cm + off) : 0.f;
-    }
+    st.store(xs, dts, Bs, Cs);
     __syncthreads();
+    // next tile's loads are in flight while this tile is computed
+    if (t0 + TT < L) {
+      const int64_t t1 = t0 + TT;
+      const int nt = static_cast<int>((L - t1) < TT ? (L - t1) : TT);
+      st.load(x + (row0 + t1) * D + d0, dt + (row0 + t1) * D + d0, Bm + (row0 + t1) * N,
+              Cm + (row0 + t1) * N, nt, dcols, N);
+    }
 
-    // ---- the recurrence for this wave's (d, n) chains
-    const int tend = static_cast<int>((L - t0) < TT ? (L - t0) : TT);
-    for (int tt = 0; tt < tend; ++tt) {
-      const float xv = xs[tt * 64 + lane];
-      const float dv = dts[tt * 64 + lane];
-      const float4 b4 = *reinterpret_cast<const float4*>(Bs + tt * 64 + n0);
-      const float4 c4 = *reinterpret_cast<const float4*>(Cs + tt * 64 + n0);
-      const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
-      const float cc[4] = {c4.x, c4.y, c4.z, c4.w};
-      const float ux = (DISC == kDiscEuler) ? dv * xv : 0.f;
-      float yacc = 0.f;
-#pragma unroll
-      for (int j = 0; j < kSelNPW; ++j) {
-        if (n0 + j < N) {  // uniform across the wave
-          const float e = fast_exp2(dv * A2[j]);
-          if (DISC == kDiscEuler) {
-            h[j] = fmaf(e, h[j], bb[j] * ux);
-          } else if (!PRECISE) {
-            const float v = (bb[j] * xv) * iA[j];
-            h[j] = fmaf(e, h[j] + v, -v);
-          } else {
-            const float l = dv * An[j];
-            const float ser = dv * fmaf(l, fmaf(l, fmaf(l, 1.f / 24.f, 1.f / 6.f), 0.5f), 1.f);
-            const float phi = fabsf(l) < 0.1f ? ser : (e - 1.f) * iA[j];
-            h[j] = fmaf(e, h[j], phi * (bb[j] * xv));
-          }
-          yacc = fmaf(cc[j], h[j], yacc);
-        }
-      }
-      yp[(w * TT + tt) * 64 + lane] = yacc;
+    // Steps past L carry x = dt = 0 (e = 1, no input): h is unchanged and
+    // their outputs are not stored, so every tile runs all TT steps.  The
+    // tile is walked in groups of GS steps with two register sets: the LDS
+    // reads of the next group are issued before the current group is
+    // computed, and a group's partial readouts are stored after it.
+    SelGroup<NPW, GS> ga, gb;
+    ga.read(xs, dts, Bs, Cs, 0, lane, n0);
+#pragma unroll 1
+    for (int gs = 0; gs < TT; gs += 2 * GS) {
+      gb.read(xs, dts, Bs, Cs, gs + GS, lane, n0);
+      ga.template step<DISC, PRECISE>(h, A2, iA, An, yp + (w * TT + gs) * 64 + lane);
+      if (gs + 2 * GS < TT) ga.read(xs, dts, Bs, Cs, gs + 2 * GS, lane, n0);
+      gb.template step<DISC, PRECISE>(h, A2, iA, An, yp + (w * TT + gs + GS) * 64 + lane);
     }
     __syncthreads();
 
     // ---- sum the per-wave partial readouts, add D x, store y
-    for (int idx = tid; idx < TT * 64; idx += nthr) {
-      const int tt = idx >> 6, dd = idx & 63;
-      const int64_t t = t0 + tt;
-      if (t < L && d0 + dd < D) {
-        float s = Dk[dd] * xs[idx];
-        for (int ww = 0; ww < nw; ++ww) s += yp[(ww * TT + tt) * 64 + dd];
-        Io<T>::store(y + (bi * L + t) * D + d0 + dd, s);
+    {
+      const int nt = static_cast<int>((L - t0) < TT ? (L - t0) : TT);
+      T* y0 = y + (row0 + t0) * D + d0;
+      if (dd < dcols) {
+        const float dk = Dk[dd];
+        for (int tt = r0; tt < nt; tt += nw) {
+          float s = dk * xs[tt * 64 + dd];
+          for (int ww = 0; ww < nw; ++ww) s += yp[(ww * TT + tt) * 64 + dd];
+          Io<T>::store(y0 + tt * Di + dd, s);
+        }
       }
     }
     __syncthreads();
   }
 }
 
-template <typename T, int DISC, int TT>
-__global__ __launch_bounds__(1024) void selective_scan_kernel(
+template <typename T, int DISC, int TT, int MK, int MAXT, int NPW, bool VEC>
+__global__ __launch_bounds__(MAXT) void selective_scan_kernel(
     const T* __restrict__ x, const T* __restrict__ dt, const float* __restrict__ A,
     const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ Dskip,
     const float* __restrict__ h0, T* __restrict__ y, float* __restrict__ h_last, int64_t L,
     int64_t D, int N) {
   extern __shared__ float smem[];
+  constexpr int GS = MAXT >= 1024 ? 2 : ((NPW == 4 || sizeof(T) == 4) ? 4 : 8);
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63;
   const int64_t ndt = (D + kSelCT - 1) / kSelCT;
@@ -129,72 +280,91 @@ __global__ __launch_bounds__(1024) void selective_scan_kernel(
   const int64_t d0 = (blockIdx.x % ndt) * kSelCT;
   const int64_t d = d0 + lane;
   const bool dok = d < D;
-  const int n0 = w * kSelNPW;
+  const int n0 = w * NPW;
 
-  float A2[kSelNPW], iA[kSelNPW], An[kSelNPW], h[kSelNPW];
+  float A2[NPW], iA[NPW], An[NPW], h[NPW];
   bool small = false;
 #pragma unroll
-  for (int j = 0; j < kSelNPW; ++j) {
+  for (int j = 0; j < NPW; ++j) {
     const int n = n0 + j;
     const bool ok = dok && n < N;
-    const float a = ok ? A[d * N + n] : -1.f;
+    // state indices n >= N get A = 0 and 1/A = 0: with B = C = 0 there they
+    // contribute nothing and need no per-index branch in the step loop
+    const float a = ok ? A[d * N + n] : 0.f;
     An[j] = a;
     A2[j] = a * kLog2e;
-    iA[j] = 1.f / a;
+    iA[j] = ok ? 1.f / a : 0.f;
     small |= ok && fabsf(a) < 0.5f;
     h[j] = (ok && h0 != nullptr) ? h0[(bi * D + d) * N + n] : 0.f;
   }
   {
+    float* Bs = smem + 2 * TT * 64;
+    for (int i = tid; i < 2 * TT * 64; i += blockDim.x) Bs[i] = 0.f;   // Bs and Cs
     float* Dk = smem + 4 * TT * 64;
     if (tid < 64) Dk[tid] = (Dskip != nullptr && d0 + tid < D) ? Dskip[d0 + tid] : 0.f;
   }
   const bool precise = __syncthreads_or(small ? 1 : 0) != 0;
 
   if (DISC == kDiscEuler) {
-    selective_body<T, DISC, false, TT>(x, dt, Bm, Cm, Dskip, y, smem, h, A2, iA, An, bi, d0, L, D, N);
+    selective_body<T, DISC, false, TT, MK, NPW, GS, VEC>(x, dt, Bm, Cm, y, smem, h, A2, iA, An,
+                                                        bi, d0, L, D, N);
   } else if (precise) {
-    selective_body<T, DISC, true, TT>(x, dt, Bm, Cm, Dskip, y, smem, h, A2, iA, An, bi, d0, L, D, N);
+    selective_body<T, DISC, true, TT, MK, NPW, GS, VEC>(x, dt, Bm, Cm, y, smem, h, A2, iA, An,
+                                                       bi, d0, L, D, N);
   } else {
-    selective_body<T, DISC, false, TT>(x, dt, Bm, Cm, Dskip, y, smem, h, A2, iA, An, bi, d0, L, D, N);
+    selective_body<T, DISC, false, TT, MK, NPW, GS, VEC>(x, dt, Bm, Cm, y, smem, h, A2, iA, An,
+                                                        bi, d0, L, D, N);
   }
 
   if (h_last != nullptr && dok) {
 #pragma unroll
-    for (int j = 0; j < kSelNPW; ++j)
+    for (int j = 0; j < NPW; ++j)
       if (n0 + j < N) h_last[(bi * D + d) * N + n0 + j] = h[j];
   }
 }
 
-template <typename T, int DISC, int TT>
+template <typename T, int DISC, int TT, int MK, int MAXT, int NPW>
 static hipError_t launch_sel(const void* x, const void* dt, const float* A, const void* Bm,
                              const void* Cm, const float* Dskip, const float* h0, void* y,
                              float* h_last, int64_t B, int64_t L, int64_t D, int N,
                              hipStream_t stream) {
-  const int nw = (N + kSelNPW - 1) / kSelNPW;
+  const int nw = (N + NPW - 1) / NPW;
   const size_t lds = (4 * TT * 64 + 64 + static_cast<size_t>(nw) * TT * 64) * sizeof(float);
   dim3 grid(static_cast<unsigned>(B * ((D + kSelCT - 1) / kSelCT)));
-  hipLaunchKernelGGL((selective_scan_kernel<T, DISC, TT>), grid, dim3(64 * nw), lds, stream,
-                     static_cast<const T*>(x), static_cast<const T*>(dt), A,
-                     static_cast<const T*>(Bm), static_cast<const T*>(Cm), Dskip, h0,
-                     static_cast<T*>(y), h_last, L, D, N);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, dim3(64 * nw), lds, stream, static_cast<const T*>(x),
+                       static_cast<const T*>(dt), A, static_cast<const T*>(Bm),
+                       static_cast<const T*>(Cm), Dskip, h0, static_cast<T*>(y), h_last, L, D, N);
+  };
+  if (D % 8 == 0) go(selective_scan_kernel<T, DISC, TT, MK, MAXT, NPW, true>);
+  else go(selective_scan_kernel<T, DISC, TT, MK, MAXT, NPW, false>);
   return hipGetLastError();
 }
 
-// TT = 32 tokens per LDS tile while the per-wave partial buffers fit
-// (N <= 32); larger N uses TT = 16.
+// Instances by block size:
+//   N <= 16: 2 state indices per wave, <= 512 threads, TT = 32
+//   N <= 32: 4 per wave, <= 512 threads, TT = 32
+//   N <= 64: 4 per wave, <= 1024 threads, TT = 16 (partials must fit in LDS)
+template <typename T, int DISC>
+static hipError_t launch_sel_n(const void* x, const void* dt, const float* A, const void* Bm,
+                               const void* Cm, const float* Dskip, const float* h0, void* y,
+                               float* h_last, int64_t B, int64_t L, int64_t D, int N,
+                               hipStream_t stream) {
+  if (N <= 16)
+    return launch_sel<T, DISC, 32, 4, 512, 2>(x, dt, A, Bm, Cm, Dskip, h0, y, h_last, B, L, D, N, stream);
+  if (N <= 32)
+    return launch_sel<T, DISC, 32, 1, 512, 4>(x, dt, A, Bm, Cm, Dskip, h0, y, h_last, B, L, D, N, stream);
+  return launch_sel<T, DISC, 16, 1, 1024, 4>(x, dt, A, Bm, Cm, Dskip, h0, y, h_last, B, L, D, N, stream);
+}
+
 template <typename T>
 hipError_t launch_selective_scan(int disc, const void* x, const void* dt, const float* A,
                                  const void* Bm, const void* Cm, const float* Dskip,
                                  const float* h0, void* y, float* h_last, int64_t B, int64_t L,
                                  int64_t D, int N, hipStream_t stream) {
-  if (N <= 32) {
-    return disc == kDiscEuler
-               ? launch_sel<T, kDiscEuler, 32>(x, dt, A, Bm, Cm, Dskip, h0, y, h_last, B, L, D, N, stream)
-               : launch_sel<T, kDiscZoh, 32>(x, dt, A, Bm, Cm, Dskip, h0, y, h_last, B, L, D, N, stream);
-  }
   return disc == kDiscEuler
-             ? launch_sel<T, kDiscEuler, 16>(x, dt, A, Bm, Cm, Dskip, h0, y, h_last, B, L, D, N, stream)
-             : launch_sel<T, kDiscZoh, 16>(x, dt, A, Bm, Cm, Dskip, h0, y, h_last, B, L, D, N, stream);
+             ? launch_sel_n<T, kDiscEuler>(x, dt, A, Bm, Cm, Dskip, h0, y, h_last, B, L, D, N, stream)
+             : launch_sel_n<T, kDiscZoh>(x, dt, A, Bm, Cm, Dskip, h0, y, h_last, B, L, D, N, stream);
 }
 
 template hipError_t launch_selective_scan<float>(int, const void*, const void*, const float*,
