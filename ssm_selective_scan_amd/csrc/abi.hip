@@ -30,6 +30,9 @@ hipError_t launch_gla_fwd(const void* q, const void* k, const void* v, const voi
                           int64_t H, int64_t K, int64_t V, hipStream_t stream);
 size_t ssd_bwd_workspace(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N,
                          int64_t seg);
+bool ssd_bwd_supported(int64_t P, int64_t N, int64_t seg);
+hipError_t launch_ssd_bwd_empty(float* dA, float* dD, float* dh0, const float* dh_last, int64_t H,
+                                int64_t nstate, hipStream_t stream);
 hipError_t launch_ssd_bwd(int disc, const void* x, const void* dt, const float* A, const void* Bm,
                           const void* Cm, const float* Dskip, const float* ckpt, const void* dy,
                           const float* dh_last, void* dx, void* ddt, float* dA, void* dBm,
@@ -175,7 +178,8 @@ lr_status lr_ssd_scan(lr_dtype io, lr_disc disc, int64_t B, int64_t L, int64_t H
 
 size_t lr_ssd_scan_bwd_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G,
                                        int64_t N, int64_t chunk, int64_t seg) {
-  if (check_ssd_sizes(LR_BF16, LR_DISC_ZOH, B, L, H, P, G, N, chunk, seg) != LR_OK || seg < 1)
+  if (check_ssd_sizes(LR_BF16, LR_DISC_ZOH, B, L, H, P, G, N, chunk, seg) != LR_OK || seg < 1 ||
+      !lr::ssd_bwd_supported(P, N, seg))
     return 0;
   return lr::ssd_bwd_workspace(B, L, H, P, G, N, seg);
 }
@@ -190,6 +194,7 @@ lr_status lr_ssd_scan_bwd(lr_dtype io, lr_disc disc, int64_t B, int64_t L, int64
   lr_status st = check_ssd_sizes(io, disc, B, L, H, P, G, N, chunk, seg);
   if (st != LR_OK) return st;
   if (seg < 1) return LR_E_SHAPE;
+  if (!lr::ssd_bwd_supported(P, N, seg)) return LR_E_UNSUPPORTED;
   if (A == nullptr || dA == nullptr) return LR_E_NULLPTR;
   if (B * L > 0 && any_null({x, dt, Bm, Cm, ckpt, dy, dx, ddt, dBm, dCm})) return LR_E_NULLPTR;
   if (!all_aligned({x, dt, A, Bm, Cm, Dskip, h0, ckpt, dy, dh_last, dx, ddt, dA, dBm, dCm, dD,
@@ -198,6 +203,9 @@ lr_status lr_ssd_scan_bwd(lr_dtype io, lr_disc disc, int64_t B, int64_t L, int64
   const size_t need = lr::ssd_bwd_workspace(B, L, H, P, G, N, seg);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LR_E_WORKSPACE;
   (void)h0;  // the entering state is ckpt[0]
+  if (B * L == 0)
+    return hip_status(lr::launch_ssd_bwd_empty(dA, dD, dh0, dh_last, H, B * H * P * N,
+                                               static_cast<hipStream_t>(stream)));
   return hip_status(lr::launch_ssd_bwd(disc, x, dt, A, Bm, Cm, Dskip, ckpt, dy, dh_last, dx, ddt,
                                        dA, dBm, dCm, dD, dh0, workspace, B, L, H, P, G, N, seg,
                                        static_cast<hipStream_t>(stream)));

@@ -1,19 +1,759 @@
-// ssd_bwd.hip — SSD backward with segment checkpoint-and-recompute.
+// ssd_bwd.hip — backward of the Mamba-2 SSD scan with segment checkpoints.
+//
+// ("mlx-recurrence" post, Apple Developer Forums thread 840535: the training
+// path keeps the state only at segment boundaries in the forward and
+// recomputes inside each segment in the backward.)
+//
+// Loss l = sum(dy * y) + <dh_last, h_last>.  Per (b, h), with G_t = dl/dh_t:
+//   G_t = e_{t+1} G_{t+1} + dy_t (x) C_t,  dx_t = phi_t G_t B_t + D dy_t,
+//   dB_t += phi_t G_t^T x_t,  dC_t += h_t^T dy_t,  dphi_t = x_t^T G_t B_t,
+//   d(log e_t) = <G_t, h_{t-1}> e_t,  dh0 = e_0 G_0.
+// Evaluated per 64-token block on MFMA.  With c the inclusive cumulative
+// log-decay inside the block, E_t = e^{c_t}, sE_t = e^{c_end - c_t} and the
+// decayed causal masks
+//   Mp[u][t] = (C_u . B_t) e^{c_u - c_t},  W[u][t] = (dy_u . x_t) e^{c_u - c_t}
+// for u >= t, and Gamma the adjoint of the block's last state from later
+// tokens and h_prev the state entering the block:
+//   dx_t  = phi_t (sum_u Mp[u][t] dy_u + sE_t Gamma B_t) + D dy_t
+//   dB_t += phi_t (sum_u W[u][t] C_u + sE_t Gamma^T x_t)
+//   dC_u += sum_t W[u][t] phi_t B_t + E_u h_prev^T dy_u
+//   Gamma_prev = E_end Gamma + sum_u E_u dy_u (x) C_u
+// and the log-decay gradient follows from dl/dc_j (pairs (u, t) contribute
+// T[u][t] = Mp phi_t (dy_u . x_t) with + to c_u and - to c_t; the entering
+// state and Gamma add boundary terms) by a reverse prefix sum over the block.
+//
+// Launches:
+//   gloc:     per (b, h, segment): Gamma_loc = adjoint of the segment's own
+//             outputs w.r.t. its entering state, and the segment decay.
+//   gcombine: per state element, backwards over segments,
+//             Gamma_out(s-1) = Lambda_s Gamma_out(s) + Gamma_loc(s)
+//             (the (a, b) combine again, run in reverse); also gives dh0.
+//   main:     per (b, h, segment): recompute the block-entry states from the
+//             checkpoint (kept in registers), then the blocks in reverse.
+//             Writes dx, ddt and per-head partial sums of dB, dC, dA, dD.
+//   reduce:   fixed-order sums of the partials over heads (and batch and
+//             segments for dA, dD), so results are deterministic.
 #include "common.hpp"
 
 namespace lr {
 
-size_t ssd_bwd_workspace(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N,
-                         int64_t seg) {
-  (void)B; (void)L; (void)H; (void)P; (void)G; (void)N; (void)seg;
-  return 0;
+constexpr int kBQ = 64;          // tokens per block
+constexpr int kBP = 64;          // head dim P (one 64-wide slice)
+constexpr int kBLd = kBQ + 8;    // leading dim of 64-wide LDS tiles
+
+enum { kBwdZoh = 0, kBwdEuler = 1 };
+
+struct BwdArgs {
+  const uint16_t* x; const uint16_t* dt; const float* A; const uint16_t* Bm; const uint16_t* Cm;
+  const float* Dskip; const float* ckpt; const uint16_t* dy; const float* dh_last;
+  uint16_t* dx; uint16_t* ddt; float* dA; uint16_t* dBm; uint16_t* dCm; float* dD; float* dh0;
+  float* dBpart; float* dCpart;   // [H][B][L][N]
+  float* gseg;                    // [nseg][B][H][P][N]: Gamma_loc, then Gamma_out
+  float* lam;                     // [nseg][B][H]
+  float* dApart; float* dDpart;   // [B][H][nseg]
+  int64_t B, L, H, G, N, seg, nseg;
+};
+
+// Per-token scalars of one block (lane = token): log2 cumulative decay,
+// phi, e, dt.  Masked tokens (t >= nv) get dt = 0: no decay, no input.
+template <int DISC>
+__device__ __forceinline__ void block_scalars(float dtv, float Ah, float& l2, float& ph, float& ek) {
+  const float lam = dtv * Ah;
+  l2 = lam * kLog2e;
+  ek = fast_exp2(l2);
+  if (DISC == kBwdEuler) {
+    ph = dtv;
+  } else {
+    const float ser = dtv * fmaf(lam, fmaf(lam, fmaf(lam, 1.f / 24.f, 1.f / 6.f), 0.5f), 1.f);
+    ph = fabsf(lam) < 0.1f ? ser : (ek - 1.f) / Ah;
+  }
 }
 
-hipError_t launch_ssd_bwd(int, const void*, const void*, const float*, const void*, const void*,
-                          const float*, const float*, const void*, const float*, void*, void*,
-                          float*, void*, void*, float*, float*, void*, int64_t, int64_t, int64_t,
-                          int64_t, int64_t, int64_t, int64_t, hipStream_t) {
-  return hipErrorNotSupported;
+// Sum over the 16 lanes of a DPP row (lanes with the same l / 16).
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __shfl_xor(v, 1);
+  v += __shfl_xor(v, 2);
+  v += __shfl_xor(v, 4);
+  v += __shfl_xor(v, 8);
+  return v;
+}
+// Sum over the 4 lanes l % 16 == c (the 4 row groups of a wave).
+__device__ __forceinline__ float col4_sum(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) { return col4_sum(row16_sum(v)); }
+
+// ---------------------------------------------------------------------------
+// gloc: Gamma_loc(s) = sum_u E_u dy_u (x) C_u over the segment (E from the
+// segment start), accumulated block by block backwards; Lambda_s = E_end.
+// ---------------------------------------------------------------------------
+template <int NS>
+struct GlocLds {
+  uint16_t CT[NS * kBLd];      // C[u][n] as [n][u]
+  uint16_t dys[kBQ * kBLd];    // dy[u][p]
+  uint16_t dyET[kBP * kBLd];   // E_u dy[u][p] as [p][u]
+  float cum[kBQ];
+  float E[kBQ];
+};
+
+template <int NS>
+__global__ __launch_bounds__(256) void ssd_bwd_gloc_kernel(BwdArgs a) {
+  constexpr int NT = NS / 16;
+  __shared__ GlocLds<NS> sm;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int g4 = lane >> 4, c16 = lane & 15;
+  const int64_t wid = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t sg = wid % a.nseg;
+  const int64_t bh = wid / a.nseg;
+  const int64_t h = bh % a.H, b = bh / a.H;
+  const int64_t grp = h / (a.H / a.G);
+  const float Ah = a.A[h];
+  const int64_t ts0 = sg * a.seg;
+  const int64_t tse = (ts0 + a.seg < a.L) ? ts0 + a.seg : a.L;
+  const int nb = static_cast<int>((tse - ts0 + kBQ - 1) / kBQ);
+
+  f32x4 gacc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) gacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float lsum = 0.f;   // log2 of the segment decay
+
+  for (int j = nb - 1; j >= 0; --j) {
+    const int64_t t0 = ts0 + static_cast<int64_t>(j) * kBQ;
+    const int nv = static_cast<int>((tse - t0) < kBQ ? (tse - t0) : kBQ);
+    if (w == 0) {
+      const float dtv = lane < nv ? bf2f(a.dt[(b * a.L + t0 + lane) * a.H + h]) : 0.f;
+      const float c = wave_incl_sum(dtv * Ah * kLog2e);
+      sm.cum[lane] = c;
+      sm.E[lane] = fast_exp2(c);
+    }
+    // C transposed: lanes walk tokens
+    for (int idx = tid; idx < kBQ * (NS / 8); idx += 256) {
+      const int u = idx & 63, c = idx >> 6;
+      u16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (u < nv) v = *reinterpret_cast<const u16x8*>(a.Cm + ((b * a.L + t0 + u) * a.G + grp) * NS + 8 * c);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sm.CT[(8 * c + i) * kBLd + u] = v[i];
+    }
+    for (int idx = tid; idx < kBQ * (kBP / 8); idx += 256) {
+      const int u = idx >> 3, c = idx & 7;
+      u16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (u < nv) v = *reinterpret_cast<const u16x8*>(a.dy + ((b * a.L + t0 + u) * a.H + h) * kBP + 8 * c);
+      *reinterpret_cast<u16x8*>(sm.dys + u * kBLd + 8 * c) = v;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < kBQ * (kBP / 8); idx += 256) {
+      const int u = idx & 63, c = idx >> 6;
+      const u16x8 v = *reinterpret_cast<const u16x8*>(sm.dys + u * kBLd + 8 * c);
+      const float e = sm.E[u];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sm.dyET[(8 * c + i) * kBLd + u] = f2bf(bf2f(v[i]) * e);
+    }
+    __syncthreads();
+    const float cend = sm.cum[kBQ - 1];
+    const float dec = fast_exp2(cend);
+    lsum += cend;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      gacc[nt] *= dec;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        gacc[nt] = mfma16x16x32(lds_tile(sm.CT, kBLd, 16 * nt, 32 * ks, lane),
+                                lds_tile(sm.dyET, kBLd, 16 * w, 32 * ks, lane), gacc[nt]);
+    }
+    __syncthreads();
+  }
+  float* out = a.gseg + ((sg * a.B + b) * a.H + h) * kBP * NS;
+  const int p = 16 * w + c16;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+    *reinterpret_cast<f32x4*>(out + p * NS + 16 * nt + 4 * g4) = gacc[nt];
+  if (tid == 0) a.lam[(sg * a.B + b) * a.H + h] = fast_exp2(lsum);
+}
+
+// ---------------------------------------------------------------------------
+// gcombine: one thread per state element; backwards over segments replace
+// Gamma_loc(s) by Gamma_out(s) = adjoint of the state at the end of segment s.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void ssd_bwd_gcombine_kernel(BwdArgs a, int64_t PN) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t BH = a.B * a.H;
+  if (idx >= BH * PN) return;
+  const int64_t bh = idx / PN;
+  float carry = a.dh_last != nullptr ? a.dh_last[idx] : 0.f;
+  for (int64_t s = a.nseg - 1; s >= 0; --s) {
+    float* gp = a.gseg + s * BH * PN + idx;
+    const float gl = *gp;
+    *gp = carry;
+    carry = fmaf(a.lam[s * BH + bh], carry, gl);
+  }
+  if (a.dh0 != nullptr) a.dh0[idx] = carry;
+}
+
+// ---------------------------------------------------------------------------
+// main
+// ---------------------------------------------------------------------------
+template <int NS>
+struct MainLds {
+  static constexpr int kLdN = NS + 8;
+  uint16_t Cs[kBQ * kLdN];     // C[u][n]
+  uint16_t Bs[kBQ * kLdN];     // B[t][n]
+  uint16_t xs[kBQ * kBLd];     // x[t][p]
+  uint16_t dys[kBQ * kBLd];    // dy[u][p]
+  uint16_t dyT[kBP * kBLd];    // dy[u][p] as [p][u]          (recompute: x as [p][s])
+  uint16_t dyET[kBP * kBLd];   // E_u dy[u][p] as [p][u]
+  uint16_t CT[NS * kBLd];      // C[u][n] as [n][u]           (recompute: B_w as [n][s])
+  uint16_t pBT[NS * kBLd];     // phi_t B[t][n] as [n][t]
+  uint16_t Mt[kBQ * kBLd];     // Mp[u][t] as [t][u]
+  uint16_t Wt[kBQ * kBLd];     // W[u][t] as [t][u]
+  uint16_t Wu[kBQ * kBLd];     // W[u][t] as [u][t]
+  uint16_t GT[NS * kBLd];      // Gamma[p][n] as [n][p], then h_prev[p][n] as [n][p]
+  float cum[kBQ], E[kBQ], sE[kBQ], phi[kBQ], dtv[kBQ], ek[kBQ];
+  float rowTp[12][16], colTp[12][16];
+  float toffp[4][kBQ], dphip[4][kBQ], up[4][kBQ];
+  float uprevp[4];
+};
+
+// the 12 (u-tile j, t-tile i) tiles of a block: the 10 causal ones plus (0,1)
+// and (2,3), all-zero, which complete the 32-wide k steps of the consumers
+__constant__ int kTileJ[12] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3, 0, 2};
+__constant__ int kTileI[12] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3, 1, 3};
+
+template <int DISC, int NS, int NBS>
+__global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
+  constexpr int NT = NS / 16, NK = NS / 32;
+  constexpr int kLdN = MainLds<NS>::kLdN;
+  __shared__ MainLds<NS> sm;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int g4 = lane >> 4, c16 = lane & 15;
+  const int64_t wid = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t sg = wid % a.nseg;
+  const int64_t bh = wid / a.nseg;
+  const int64_t h = bh % a.H, b = bh / a.H;
+  const int64_t grp = h / (a.H / a.G);
+  const float Ah = a.A[h];
+  const float Dh = a.Dskip != nullptr ? a.Dskip[h] : 0.f;
+  const int64_t ts0 = sg * a.seg;
+  const int64_t tse = (ts0 + a.seg < a.L) ? ts0 + a.seg : a.L;
+  const int nb = static_cast<int>((tse - ts0 + kBQ - 1) / kBQ);
+  const int64_t xrow = a.H * kBP;              // elements between tokens of x, dy, dx
+  const int64_t xoff = h * kBP;
+  const int64_t bcrow = a.G * NS;
+  const int64_t bcoff = grp * NS;
+  const int p = 16 * w + c16;                  // this lane's p column
+
+  // ---- forward recompute of the block-entry states of this segment; they
+  // are kept in registers as packed bf16 MFMA operands (hsb[j][kk] holds
+  // n-tiles 2kk and 2kk+1 in the operand order of pack_dd)
+  bf16x8 hsb[NBS][NK];
+  f32x4 hacc[NT];
+  {
+    const float* cp = a.ckpt + ((sg * a.B + b) * a.H + h) * kBP * NS;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) hacc[nt] = *reinterpret_cast<const f32x4*>(cp + p * NS + 16 * nt + 4 * g4);
+  }
+#pragma unroll
+  for (int j = 0; j < NBS; ++j) {
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) hsb[j][kk] = pack_dd(hacc[2 * kk], hacc[2 * kk + 1]);
+    if (j + 1 < nb) {
+      const int64_t t0 = ts0 + static_cast<int64_t>(j) * kBQ;
+      const int nv = static_cast<int>((tse - t0) < kBQ ? (tse - t0) : kBQ);
+      if (w == 0) {
+        const float dtv = lane < nv ? bf2f(a.dt[(b * a.L + t0 + lane) * a.H + h]) : 0.f;
+        float l2, ph, ek;
+        block_scalars<DISC>(dtv, Ah, l2, ph, ek);
+        sm.cum[lane] = wave_incl_sum(l2);
+        sm.phi[lane] = lane < nv ? ph : 0.f;
+      }
+      for (int idx = tid; idx < kBQ * (NS / 8); idx += 256) {
+        const int r = idx / (NS / 8), c = idx % (NS / 8);
+        u16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (r < nv) v = *reinterpret_cast<const u16x8*>(a.Bm + (b * a.L + t0 + r) * bcrow + bcoff + 8 * c);
+        *reinterpret_cast<u16x8*>(sm.Bs + r * kLdN + 8 * c) = v;
+      }
+      for (int idx = tid; idx < kBQ * (kBP / 8); idx += 256) {
+        const int s = idx & 63, c = idx >> 6;
+        u16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (s < nv) v = *reinterpret_cast<const u16x8*>(a.x + (b * a.L + t0 + s) * xrow + xoff + 8 * c);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sm.dyT[(8 * c + i) * kBLd + s] = v[i];   // XT
+      }
+      __syncthreads();
+      const float cend = sm.cum[kBQ - 1];
+      for (int idx = tid; idx < kBQ * (NS / 8); idx += 256) {
+        const int s = idx & 63, c = idx >> 6;
+        const float ws = fast_exp2(cend - sm.cum[s]) * sm.phi[s];
+        const u16x8 v = *reinterpret_cast<const u16x8*>(sm.Bs + s * kLdN + 8 * c);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sm.CT[(8 * c + i) * kBLd + s] = f2bf(bf2f(v[i]) * ws);   // BwT
+      }
+      __syncthreads();
+      const float dec = fast_exp2(cend);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        hacc[nt] *= dec;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+          hacc[nt] = mfma16x16x32(lds_tile(sm.CT, kBLd, 16 * nt, 32 * ks, lane),
+                                  lds_tile(sm.dyT, kBLd, 16 * w, 32 * ks, lane), hacc[nt]);
+      }
+      __syncthreads();
+    }
+  }
+
+  // ---- adjoint of the segment's last state from later tokens
+  f32x4 gacc[NT];
+  {
+    const float* gp = a.gseg + ((sg * a.B + b) * a.H + h) * kBP * NS;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) gacc[nt] = *reinterpret_cast<const f32x4*>(gp + p * NS + 16 * nt + 4 * g4);
+  }
+  float dA_acc = 0.f, dD_acc = 0.f;
+
+#pragma unroll 1
+  for (int j = nb - 1; j >= 0; --j) {
+    // the stash entry of this block (uniform switch keeps register indices static)
+    bf16x8 hcur[NK];
+#pragma unroll
+    for (int jj = 0; jj < NBS; ++jj)
+      if (jj == j) {
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) hcur[kk] = hsb[jj][kk];
+      }
+    const int64_t t0 = ts0 + static_cast<int64_t>(j) * kBQ;
+    const int nv = static_cast<int>((tse - t0) < kBQ ? (tse - t0) : kBQ);
+
+    // ---- stage the block
+    if (w == 0) {
+      const float dtv = lane < nv ? bf2f(a.dt[(b * a.L + t0 + lane) * a.H + h]) : 0.f;
+      float l2, ph, ek;
+      block_scalars<DISC>(dtv, Ah, l2, ph, ek);
+      const float c = wave_incl_sum(l2);
+      const float cend = __shfl(c, 63);
+      sm.cum[lane] = c;
+      sm.E[lane] = fast_exp2(c);
+      sm.sE[lane] = fast_exp2(cend - c);
+      sm.phi[lane] = lane < nv ? ph : 0.f;
+      sm.dtv[lane] = dtv;
+      sm.ek[lane] = ek;
+    }
+    for (int idx = tid; idx < kBQ * (NS / 8); idx += 256) {
+      const int r = idx & 63, c = idx >> 6;     // lanes walk tokens (transposed writes)
+      u16x8 vc = {0, 0, 0, 0, 0, 0, 0, 0}, vb = vc;
+      float ph = 0.f;
+      if (r < nv) {
+        const int64_t off = (b * a.L + t0 + r) * bcrow + bcoff + 8 * c;
+        vc = *reinterpret_cast<const u16x8*>(a.Cm + off);
+        vb = *reinterpret_cast<const u16x8*>(a.Bm + off);
+        float l2, ek;
+        block_scalars<DISC>(bf2f(a.dt[(b * a.L + t0 + r) * a.H + h]), Ah, l2, ph, ek);
+      }
+      *reinterpret_cast<u16x8*>(sm.Cs + r * kLdN + 8 * c) = vc;
+      *reinterpret_cast<u16x8*>(sm.Bs + r * kLdN + 8 * c) = vb;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        sm.CT[(8 * c + i) * kBLd + r] = vc[i];
+        sm.pBT[(8 * c + i) * kBLd + r] = f2bf(bf2f(vb[i]) * ph);
+      }
+    }
+    for (int idx = tid; idx < kBQ * (kBP / 8); idx += 256) {
+      const int r = idx & 63, c = idx >> 6;
+      u16x8 vx = {0, 0, 0, 0, 0, 0, 0, 0}, vd = vx;
+      if (r < nv) {
+        const int64_t off = (b * a.L + t0 + r) * xrow + xoff + 8 * c;
+        vx = *reinterpret_cast<const u16x8*>(a.x + off);
+        vd = *reinterpret_cast<const u16x8*>(a.dy + off);
+      }
+      *reinterpret_cast<u16x8*>(sm.xs + r * kBLd + 8 * c) = vx;
+      *reinterpret_cast<u16x8*>(sm.dys + r * kBLd + 8 * c) = vd;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sm.dyT[(8 * c + i) * kBLd + r] = vd[i];
+    }
+    __syncthreads();
+
+    // ---- E-scaled dy transposed; decayed masks and the T sums
+    for (int idx = tid; idx < kBQ * (kBP / 8); idx += 256) {
+      const int u = idx & 63, c = idx >> 6;
+      const u16x8 v = *reinterpret_cast<const u16x8*>(sm.dys + u * kBLd + 8 * c);
+      const float e = sm.E[u];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sm.dyET[(8 * c + i) * kBLd + u] = f2bf(bf2f(v[i]) * e);
+    }
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      const int tile = 3 * w + q;
+      const int tj = kTileJ[tile], ti = kTileI[tile];
+      const int t = 16 * ti + c16;           // this lane's column (source token)
+      const int u0 = 16 * tj + 4 * g4;       // this lane's 4 rows (output tokens)
+      u16x4 om = {0, 0, 0, 0}, ow = om;
+      float rsum[4] = {0.f, 0.f, 0.f, 0.f}, csum = 0.f;
+      if (tj >= ti) {
+        f32x4 s = {0.f, 0.f, 0.f, 0.f}, rr = s;
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk)
+          s = mfma16x16x32(lds_tile(sm.Cs, kLdN, 16 * tj, 32 * kk, lane),
+                           lds_tile(sm.Bs, kLdN, 16 * ti, 32 * kk, lane), s);
+#pragma unroll
+        for (int kp = 0; kp < 2; ++kp)
+          rr = mfma16x16x32(lds_tile(sm.dys, kBLd, 16 * tj, 32 * kp, lane),
+                            lds_tile(sm.xs, kBLd, 16 * ti, 32 * kp, lane), rr);
+        const float ct = sm.cum[t], pt = sm.phi[t];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int u = u0 + r;
+          const float m = (u >= t) ? fast_exp2(sm.cum[u] - ct) : 0.f;
+          const float mp = s[r] * m, wv = rr[r] * m;
+          const float tv = mp * pt * rr[r];
+          om[r] = f2bf(mp);
+          ow[r] = f2bf(wv);
+          rsum[r] = tv;
+          csum += tv;
+        }
+      }
+      *reinterpret_cast<u16x4*>(sm.Mt + t * kBLd + u0) = om;
+      *reinterpret_cast<u16x4*>(sm.Wt + t * kBLd + u0) = ow;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sm.Wu[(u0 + r) * kBLd + t] = ow[r];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float rs = row16_sum(rsum[r]);
+        if (c16 == 0) sm.rowTp[tile][4 * g4 + r] = rs;
+      }
+      const float cs = col4_sum(csum);
+      if (g4 == 0) sm.colTp[tile][c16] = cs;
+    }
+    __syncthreads();
+
+    // ---- recomputed C h_prev (for the c-gradient), dx, dphi, U, dD, U_prev
+    {
+      f32x4 yo[4], dxa[4], dxb[4];
+#pragma unroll
+      for (int ti = 0; ti < 4; ++ti) {
+        yo[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dxa[ti] = yo[ti];
+        dxb[ti] = yo[ti];
+      }
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) {
+        const bf16x8 hb = hcur[kk];
+        const bf16x8 gb = pack_dd(gacc[2 * kk], gacc[2 * kk + 1]);
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti) {
+          yo[ti] = mfma16x16x32(lds_tile_perm(sm.Cs, kLdN, 16 * ti, 32 * kk, lane), hb, yo[ti]);
+          dxb[ti] = mfma16x16x32(lds_tile_perm(sm.Bs, kLdN, 16 * ti, 32 * kk, lane), gb, dxb[ti]);
+        }
+      }
+#pragma unroll
+      for (int ti = 0; ti < 4; ++ti) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          if (ks == 0 && ti >= 2) continue;
+          dxa[ti] = mfma16x16x32(lds_tile(sm.Mt, kBLd, 16 * ti, 32 * ks, lane),
+                                 lds_tile(sm.dyT, kBLd, 16 * w, 32 * ks, lane), dxa[ti]);
+        }
+      }
+      float ddsum = 0.f;
+#pragma unroll
+      for (int ti = 0; ti < 4; ++ti) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = 16 * ti + 4 * g4 + r;
+          const float xv = bf2f(sm.xs[t * kBLd + p]);
+          const float dyv = bf2f(sm.dys[t * kBLd + p]);
+          const float xb = dxb[ti][r] * sm.sE[t];
+          const float gB = dxa[ti][r] + xb;
+          const float ph = sm.phi[t];
+          if (t < nv) a.dx[(b * a.L + t0 + t) * xrow + xoff + p] = f2bf(fmaf(ph, gB, Dh * dyv));
+          const float toff = row16_sum(sm.E[t] * yo[ti][r] * dyv);
+          const float dph = row16_sum(xv * gB);
+          const float uu = row16_sum(ph * xv * xb);
+          if (c16 == 0) {
+            sm.toffp[w][t] = toff;
+            sm.dphip[w][t] = dph;
+            sm.up[w][t] = uu;
+          }
+          ddsum += dyv * xv;
+        }
+      }
+      dD_acc += wave_sum(ddsum);
+      float up = 0.f;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const u16x8 hv = __builtin_bit_cast(u16x8, hcur[nt >> 1]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) up += gacc[nt][r] * bf2f(hv[4 * (nt & 1) + r]);
+      }
+      up = wave_sum(up);
+      if (lane == 0) sm.uprevp[w] = up;
+    }
+
+    // ---- dB: Gamma to LDS, then phi_t (W^T C + sE_t x Gamma)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sm.GT[(16 * nt + 4 * g4 + r) * kBLd + p] = f2bf(gacc[nt][r]);
+    __syncthreads();
+#pragma unroll
+    for (int aa = 0; aa < NT / 4; ++aa) {
+      const int nt = (NT / 4) * w + aa;
+#pragma unroll
+      for (int ti = 0; ti < 4; ++ti) {
+        f32x4 d1 = {0.f, 0.f, 0.f, 0.f}, d2 = d1;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          if (ks == 0 && ti >= 2) continue;
+          d1 = mfma16x16x32(lds_tile(sm.CT, kBLd, 16 * nt, 32 * ks, lane),
+                            lds_tile(sm.Wt, kBLd, 16 * ti, 32 * ks, lane), d1);
+        }
+#pragma unroll
+        for (int kp = 0; kp < 2; ++kp)
+          d2 = mfma16x16x32(lds_tile(sm.GT, kBLd, 16 * nt, 32 * kp, lane),
+                            lds_tile(sm.xs, kBLd, 16 * ti, 32 * kp, lane), d2);
+        const int t = 16 * ti + c16;
+        if (t < nv) {
+          const float ph = sm.phi[t], se = sm.sE[t];
+          f32x4 v;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = ph * fmaf(se, d2[r], d1[r]);
+          *reinterpret_cast<f32x4*>(a.dBpart + ((h * a.B + b) * a.L + t0 + t) * NS + 16 * nt + 4 * g4) = v;
+        }
+      }
+    }
+    // ---- Gamma for the previous block: E_end Gamma + sum_u E_u dy_u (x) C_u
+    {
+      const float dec = fast_exp2(sm.cum[kBQ - 1]);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        gacc[nt] *= dec;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+          gacc[nt] = mfma16x16x32(lds_tile(sm.CT, kBLd, 16 * nt, 32 * ks, lane),
+                                  lds_tile(sm.dyET, kBLd, 16 * w, 32 * ks, lane), gacc[nt]);
+      }
+    }
+    __syncthreads();
+
+    // ---- dC: h_prev to LDS, then W (phi B) + E_u dy h_prev
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const u16x8 hv = __builtin_bit_cast(u16x8, hcur[nt >> 1]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sm.GT[(16 * nt + 4 * g4 + r) * kBLd + p] = hv[4 * (nt & 1) + r];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int aa = 0; aa < NT / 4; ++aa) {
+      const int nt = (NT / 4) * w + aa;
+#pragma unroll
+      for (int tj = 0; tj < 4; ++tj) {
+        f32x4 d1 = {0.f, 0.f, 0.f, 0.f}, d2 = d1;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          if (ks == 1 && tj < 2) continue;
+          d1 = mfma16x16x32(lds_tile(sm.pBT, kBLd, 16 * nt, 32 * ks, lane),
+                            lds_tile(sm.Wu, kBLd, 16 * tj, 32 * ks, lane), d1);
+        }
+#pragma unroll
+        for (int kp = 0; kp < 2; ++kp)
+          d2 = mfma16x16x32(lds_tile(sm.GT, kBLd, 16 * nt, 32 * kp, lane),
+                            lds_tile(sm.dys, kBLd, 16 * tj, 32 * kp, lane), d2);
+        const int u = 16 * tj + c16;
+        if (u < nv) {
+          const float e = sm.E[u];
+          f32x4 v;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = fmaf(e, d2[r], d1[r]);
+          *reinterpret_cast<f32x4*>(a.dCpart + ((h * a.B + b) * a.L + t0 + u) * NS + 16 * nt + 4 * g4) = v;
+        }
+      }
+    }
+
+    // ---- log-decay gradient -> ddt, dA (wave 0, lane = token)
+    if (w == 0) {
+      const int k = lane;
+      float rowT = 0.f, colT = 0.f;
+#pragma unroll
+      for (int tile = 0; tile < 12; ++tile) {
+        if (kTileJ[tile] == (k >> 4)) rowT += sm.rowTp[tile][k & 15];
+        if (kTileI[tile] == (k >> 4)) colT += sm.colTp[tile][k & 15];
+      }
+      const float toff = sm.toffp[0][k] + sm.toffp[1][k] + sm.toffp[2][k] + sm.toffp[3][k];
+      const float dph = sm.dphip[0][k] + sm.dphip[1][k] + sm.dphip[2][k] + sm.dphip[3][k];
+      const float uu = sm.up[0][k] + sm.up[1][k] + sm.up[2][k] + sm.up[3][k];
+      const float uprev = fast_exp2(sm.cum[kBQ - 1]) *
+                          (sm.uprevp[0] + sm.uprevp[1] + sm.uprevp[2] + sm.uprevp[3]);
+      const float usum = wave_sum(uu);
+      float dcum = rowT - colT + toff - uu;
+      if (k == kBQ - 1) dcum += uprev + usum;
+      // reverse inclusive prefix sum: dlam_k = sum_{j >= k} dcum_j
+      const float incl = wave_incl_sum(dcum);
+      const float total = __shfl(incl, 63);
+      const float dlam = total - incl + dcum;
+      const float dtv = sm.dtv[k], ek = sm.ek[k], ph = sm.phi[k];
+      float ddt, dAk;
+      if (DISC == kBwdEuler) {
+        ddt = dlam * Ah + dph;
+        dAk = dlam * dtv;
+      } else {
+        const float lam = dtv * Ah;
+        const float dphidA = fabsf(lam) < 1e-3f
+                                 ? dtv * dtv * fmaf(lam, fmaf(lam, 1.f / 8.f, 1.f / 3.f), 0.5f)
+                                 : (dtv * ek - ph) / Ah;
+        ddt = fmaf(dlam, Ah, dph * ek);
+        dAk = fmaf(dlam, dtv, dph * dphidA);
+      }
+      if (k < nv) a.ddt[(b * a.L + t0 + k) * a.H + h] = f2bf(ddt);
+      dA_acc += wave_sum(k < nv ? dAk : 0.f);
+    }
+    __syncthreads();
+  }
+  if (tid == 0) a.dApart[(b * a.H + h) * a.nseg + sg] = dA_acc;
+  if (lane == 0) sm.uprevp[w] = dD_acc;
+  __syncthreads();
+  if (tid == 0)
+    a.dDpart[(b * a.H + h) * a.nseg + sg] = sm.uprevp[0] + sm.uprevp[1] + sm.uprevp[2] + sm.uprevp[3];
+}
+
+// ---------------------------------------------------------------------------
+// reduce: dB, dC over the heads of each group (fixed order); dA, dD over
+// (batch, segment) per head.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void ssd_bwd_reduce_kernel(BwdArgs a) {
+  const int64_t n4 = a.N / 4;
+  const int64_t total = a.B * a.L * a.G * n4;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t hpg = a.H / a.G;
+  if (idx < total) {
+    const int64_t c4 = idx % n4;
+    const int64_t g = (idx / n4) % a.G;
+    const int64_t bt = idx / (n4 * a.G);     // b * L + t
+    f32x4 sb = {0.f, 0.f, 0.f, 0.f}, sc = sb;
+    for (int64_t hh = g * hpg; hh < (g + 1) * hpg; ++hh) {
+      const int64_t off = (hh * a.B * a.L + bt) * a.N + 4 * c4;
+      sb += *reinterpret_cast<const f32x4*>(a.dBpart + off);
+      sc += *reinterpret_cast<const f32x4*>(a.dCpart + off);
+    }
+    const int64_t o = (bt * a.G + g) * a.N + 4 * c4;
+    u16x4 vb = {f2bf(sb[0]), f2bf(sb[1]), f2bf(sb[2]), f2bf(sb[3])};
+    u16x4 vc = {f2bf(sc[0]), f2bf(sc[1]), f2bf(sc[2]), f2bf(sc[3])};
+    *reinterpret_cast<u16x4*>(a.dBm + o) = vb;
+    *reinterpret_cast<u16x4*>(a.dCm + o) = vc;
+  }
+  if (blockIdx.x == 0) {
+    for (int64_t hh = threadIdx.x; hh < a.H; hh += 256) {
+      float sa = 0.f, sd = 0.f;
+      for (int64_t bb = 0; bb < a.B; ++bb)
+        for (int64_t s = 0; s < a.nseg; ++s) {
+          sa += a.dApart[(bb * a.H + hh) * a.nseg + s];
+          sd += a.dDpart[(bb * a.H + hh) * a.nseg + s];
+        }
+      a.dA[hh] = sa;
+      if (a.dD != nullptr) a.dD[hh] = sd;
+    }
+  }
+}
+
+// Empty input (B * L == 0): dA = dD = 0 and dh0 = dh_last (or 0).
+__global__ __launch_bounds__(256) void ssd_bwd_empty_kernel(float* dA, float* dD, float* dh0,
+                                                            const float* dh_last, int64_t H,
+                                                            int64_t nstate) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i < H) {
+    dA[i] = 0.f;
+    if (dD != nullptr) dD[i] = 0.f;
+  }
+  if (dh0 != nullptr && i < nstate) dh0[i] = dh_last != nullptr ? dh_last[i] : 0.f;
+}
+
+hipError_t launch_ssd_bwd_empty(float* dA, float* dD, float* dh0, const float* dh_last, int64_t H,
+                                int64_t nstate, hipStream_t stream) {
+  const int64_t n = (nstate > H ? nstate : H);
+  hipLaunchKernelGGL(ssd_bwd_empty_kernel, dim3((n + 255) / 256 > 0 ? (n + 255) / 256 : 1), dim3(256),
+                     0, stream, dA, dD, dh0, dh_last, H, nstate);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+static inline int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
+
+struct WsLayout {
+  int64_t dB, dC, g, lam, dA, dD, total;
+};
+
+static WsLayout ws_layout(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t seg) {
+  const int64_t nseg = (L + seg - 1) / seg;
+  WsLayout w;
+  int64_t o = 0;
+  w.dB = o; o = align256(o + H * B * L * N * 4);
+  w.dC = o; o = align256(o + H * B * L * N * 4);
+  w.g = o; o = align256(o + nseg * B * H * P * N * 4);
+  w.lam = o; o = align256(o + nseg * B * H * 4);
+  w.dA = o; o = align256(o + B * H * nseg * 4);
+  w.dD = o; o = align256(o + B * H * nseg * 4);
+  w.total = o;
+  return w;
+}
+
+size_t ssd_bwd_workspace(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N,
+                         int64_t seg) {
+  (void)G;
+  if (P != kBP || seg > 256 || B * L == 0) return 0;
+  return static_cast<size_t>(ws_layout(B, L, H, P, N, seg).total);
+}
+
+bool ssd_bwd_supported(int64_t P, int64_t N, int64_t seg) {
+  return P == kBP && (N == 64 || N == 128) && seg >= 64 && seg <= 256 && seg % 64 == 0;
+}
+
+template <int DISC, int NS>
+static void launch_main(const BwdArgs& a, int64_t nwg, int nbs, hipStream_t s) {
+  if (nbs == 1) hipLaunchKernelGGL((ssd_bwd_main_kernel<DISC, NS, 1>), dim3(nwg), dim3(256), 0, s, a);
+  else if (nbs == 2) hipLaunchKernelGGL((ssd_bwd_main_kernel<DISC, NS, 2>), dim3(nwg), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((ssd_bwd_main_kernel<DISC, NS, 4>), dim3(nwg), dim3(256), 0, s, a);
+}
+
+hipError_t launch_ssd_bwd(int disc, const void* x, const void* dt, const float* A, const void* Bm,
+                          const void* Cm, const float* Dskip, const float* ckpt, const void* dy,
+                          const float* dh_last, void* dx, void* ddt, float* dA, void* dBm,
+                          void* dCm, float* dD, float* dh0, void* ws, int64_t B, int64_t L,
+                          int64_t H, int64_t P, int64_t G, int64_t N, int64_t seg,
+                          hipStream_t stream) {
+  if (B * L == 0) return hipSuccess;
+  const WsLayout lay = ws_layout(B, L, H, P, N, seg);
+  char* base = static_cast<char*>(ws);
+  BwdArgs a;
+  a.x = static_cast<const uint16_t*>(x); a.dt = static_cast<const uint16_t*>(dt); a.A = A;
+  a.Bm = static_cast<const uint16_t*>(Bm); a.Cm = static_cast<const uint16_t*>(Cm);
+  a.Dskip = Dskip; a.ckpt = ckpt; a.dy = static_cast<const uint16_t*>(dy); a.dh_last = dh_last;
+  a.dx = static_cast<uint16_t*>(dx); a.ddt = static_cast<uint16_t*>(ddt); a.dA = dA;
+  a.dBm = static_cast<uint16_t*>(dBm); a.dCm = static_cast<uint16_t*>(dCm); a.dD = dD; a.dh0 = dh0;
+  a.dBpart = reinterpret_cast<float*>(base + lay.dB);
+  a.dCpart = reinterpret_cast<float*>(base + lay.dC);
+  a.gseg = reinterpret_cast<float*>(base + lay.g);
+  a.lam = reinterpret_cast<float*>(base + lay.lam);
+  a.dApart = reinterpret_cast<float*>(base + lay.dA);
+  a.dDpart = reinterpret_cast<float*>(base + lay.dD);
+  a.B = B; a.L = L; a.H = H; a.G = G; a.N = N; a.seg = seg; a.nseg = (L + seg - 1) / seg;
+
+  const int64_t nwg = B * H * a.nseg;
+  if (N == 128) hipLaunchKernelGGL(ssd_bwd_gloc_kernel<128>, dim3(nwg), dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL(ssd_bwd_gloc_kernel<64>, dim3(nwg), dim3(256), 0, stream, a);
+  const int64_t PN = P * N;
+  hipLaunchKernelGGL(ssd_bwd_gcombine_kernel, dim3((B * H * PN + 255) / 256), dim3(256), 0, stream,
+                     a, PN);
+  const int nbs = static_cast<int>(seg / kBQ);
+  if (disc == kBwdEuler) {
+    if (N == 128) launch_main<kBwdEuler, 128>(a, nwg, nbs, stream);
+    else launch_main<kBwdEuler, 64>(a, nwg, nbs, stream);
+  } else {
+    if (N == 128) launch_main<kBwdZoh, 128>(a, nwg, nbs, stream);
+    else launch_main<kBwdZoh, 64>(a, nwg, nbs, stream);
+  }
+  const int64_t red = (B * L * G * (N / 4) + 255) / 256;
+  hipLaunchKernelGGL(ssd_bwd_reduce_kernel, dim3(red > 0 ? red : 1), dim3(256), 0, stream, a);
+  return hipGetLastError();
 }
 
 }  // namespace lr
