@@ -256,6 +256,8 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=8)
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--only", choices=["diag", "ssd", "gla", "ssd_fwd_bwd"],
+                    help="only time one secondary workload (for profiler runs)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -270,6 +272,11 @@ def main():
     if args.copy_probe:
         bw = copy_bandwidth()
         print(json.dumps({"copy_probe_GBs": bw, "bytes_per_copy": 2 * (1 << 30)}))
+        return
+    if args.only:
+        f = {"diag": measure_diag, "ssd": measure_ssd, "gla": measure_gla,
+             "ssd_fwd_bwd": measure_ssd_bwd}[args.only]
+        print(json.dumps({args.only: f(args.warmup, args.steps)}))
         return
 
     log(f"[bench] liblr: {lr.lr_version()}")

@@ -15,21 +15,30 @@
 // scan) and decays always formed as 2^(cum_t - cum_s) of differences:
 //   M[t][s]  = (C_t . B_s) 2^(cum_t - cum_s) phi_s  for s <= t, else 0
 //   y_t      = 2^cum_t (C_t . h_prev) + sum_s M[t][s] x_s + D x_t
-//   h_next   = 2^cum_end h_prev + sum_s 2^(cum_end - cum_s) phi_s x_s B_s^T
-// The four contractions (C B^T, M X, C h, B_w^T X) run on
-// v_mfma_f32_16x16x32_bf16 with fp32 accumulation; the state h stays in
-// MFMA accumulator registers for the whole sequence (wave w owns columns
-// p in [16w, 16w+16) for all n), so it never goes to memory except for the
-// optional checkpoints and the final state.  Inputs are staged through LDS
-// in k-contiguous layouts (B also transposed and pre-scaled for the state
-// update; x transposed), and the decayed mask M goes through LDS so every
-// wave can use it for its p columns.
+//   h_next   = 2^cum_end h_prev + sum_s B_s (2^(cum_end - cum_s) phi_s x_s)^T
+// The contractions run on v_mfma_f32_16x16x32_bf16 with fp32 accumulation.
+// y is computed transposed (rows p, columns t): the state accumulators are
+// then directly the A operand of h_prev C^T, each lane ends with four
+// consecutive p of one token (one 8-byte store), and D x is folded into the
+// diagonal of M (y_t = sum_s (M[t][s] + D delta_ts) x_s + ...).
+// The state h stays in accumulator registers for the whole sequence (wave w
+// owns columns p in [16w, 16w+16) for all n); it goes to memory only for the
+// optional checkpoints and the final state.  The 10 causal C B^T tiles of
+// the decayed mask M are split over the waves and shared through LDS.
+// Inputs live in two LDS buffers: while block k is computed from one, block
+// k+1 (loaded from HBM into registers during block k-1) is written into the
+// other, transposed where a contraction runs over tokens (B as [n][s], x and
+// the decay-weighted x as [p][s]) with two tokens per 4-byte LDS word.  The
+// rows of C and B are stored with the n-order of pack_dd inside each 32-wide
+// block (see perm_pos), so C h_prev reads its A operand as one plain 16-byte
+// read per lane; C B^T sees the same order on both operands.  Two barriers
+// per block.
 #include "common.hpp"
 
 namespace lr {
 
-constexpr int kCQ = 64;    // tokens per block
-constexpr int kCPS = 64;   // p columns per workgroup
+constexpr int kCQ = 64;        // tokens per block
+constexpr int kCPS = 64;       // p columns per workgroup
 constexpr int kLdT = kCQ + 8;  // leading dim of token-contiguous LDS tiles
 
 enum { kModeSsdZoh = 0, kModeSsdEuler = 1, kModeGla = 2 };
@@ -50,24 +59,60 @@ struct ChunkFwdArgs {
   int64_t st_p, st_n;   // state strides of p and n (SSD: N, 1; GLA: 1, V)
 };
 
+// Position of n inside its 32-wide block in the permuted C/B row layout:
+// positions 8g..8g+3 hold n = 4g..4g+3, positions 8g+4..8g+7 hold
+// n = 16+4g..16+4g+3 (g < 4), which is the k order of pack_dd.
+__device__ __forceinline__ int perm_pos(int n) {
+  const int nl = n & 31, base = n & ~31;
+  return base + (nl < 16 ? 8 * (nl >> 2) + (nl & 3) : 8 * ((nl - 16) >> 2) + 4 + (nl & 3));
+}
+
 template <int NS>
-struct ChunkLds {
+struct ChunkBuf {
   static constexpr int kLdN = NS + 8;
-  uint16_t Cs[kCQ * kLdN];     // C[t][n]
-  uint16_t Bs[kCQ * kLdN];     // B[s][n]
-  uint16_t BwT[NS * kLdT];     // B[s][n] 2^(cum_end - cum_s) phi_s, as [n][s]
-  uint16_t XT[kCPS * kLdT];    // x[s][p], as [p][s]
-  uint16_t Ms[kCQ * kLdT];     // M[t][s]
+  uint16_t Cs[kCQ * kLdN];     // C[t][n], n permuted (perm_pos)
+  uint16_t Bs[kCQ * kLdN];     // B[s][n], n permuted (perm_pos)
+  uint16_t BT[NS * kLdT];      // B[s][n] as [n][s]
+  uint16_t XT[kCPS * kLdT];    // x[s][p] as [p][s]
+  uint16_t XwT[kCPS * kLdT];   // 2^(cum_end - cum_s) phi_s x[s][p] as [p][s]
   float cum[kCQ];
   float phi[kCQ];
 };
+
+// Per-token log2-decay and input scale of one token.
+template <int MODE>
+__device__ __forceinline__ void chunk_scalars(uint16_t graw, bool ok, float Ah, float& l2, float& ph) {
+  if (MODE == kModeGla) {
+    const float gv = ok ? bf2f(graw) : 1.f;
+    l2 = fast_log2(gv);
+    ph = ok ? 1.f : 0.f;
+  } else {
+    const float dtv = ok ? bf2f(graw) : 0.f;
+    const float lam = dtv * Ah;
+    l2 = lam * kLog2e;
+    if (MODE == kModeSsdEuler) {
+      ph = dtv;
+    } else {
+      const float ser = dtv * fmaf(lam, fmaf(lam, fmaf(lam, 1.f / 24.f, 1.f / 6.f), 0.5f), 1.f);
+      ph = fabsf(lam) < 0.1f ? ser : (fast_exp2(l2) - 1.f) / Ah;
+    }
+  }
+}
+
+__device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi) {
+  return static_cast<uint32_t>(lo) | (static_cast<uint32_t>(hi) << 16);
+}
 
 template <int MODE, int NS>
 __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkFwdArgs g) {
   constexpr int NT = NS / 16;     // 16-row tiles of n
   constexpr int NK = NS / 32;     // 32-wide k steps over n
-  constexpr int kLdN = ChunkLds<NS>::kLdN;
-  __shared__ ChunkLds<NS> sm;
+  constexpr int kLdN = ChunkBuf<NS>::kLdN;
+  // staged pair-chunks per thread: (token pair, 8-wide column chunk)
+  constexpr int kCB = (kCQ / 2) * (NS / 8) / 256;    // C, B
+  constexpr int kXC = (kCQ / 2) * (kCPS / 8) / 256;  // x
+  __shared__ ChunkBuf<NS> sm[2];
+  __shared__ uint16_t Ms[kCQ * kLdT];   // M[t][s]
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63;
@@ -81,10 +126,14 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkFwdArgs g) {
   const int64_t b = bh / g.H;
   const int64_t grp = (MODE == kModeGla) ? h : h / (g.H / g.G);
   const int64_t xrow = g.H * g.P;               // elements between tokens of x / y
-  const int64_t xoff = h * g.P + ps * kCPS;     // this workgroup's columns
-  const int64_t bcoff = grp * NS;
   const float Ah = (MODE == kModeGla) ? 0.f : g.A[h];
   const float Dh = (MODE == kModeGla || g.Dskip == nullptr) ? 0.f : g.Dskip[h];
+  // per-thread base pointers (token 0 of this batch row, this workgroup's columns)
+  const uint16_t* xb = g.x + b * g.L * xrow + h * g.P + ps * kCPS;
+  uint16_t* yb = g.y + b * g.L * xrow + h * g.P + ps * kCPS;
+  const uint16_t* Cb = g.Cm + b * g.L * g.bc_row + grp * NS;
+  const uint16_t* Bb = g.Bm + b * g.L * g.bc_row + grp * NS;
+  const uint16_t* gb = g.gate + b * g.L * g.H + h;
 
   // state accumulators: hacc[nt] holds h[n = 16 nt + 4 g4 + r][p = 16 w + c16]
   f32x4 hacc[NT];
@@ -101,45 +150,112 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkFwdArgs g) {
 
   const int64_t nblk = (g.L + kCQ - 1) / kCQ;
 
-  // Register staging of one block: C and B rows (NS/32 16-byte chunks of each
-  // per thread), x (2 chunks per thread, lanes walk tokens) and the gate
-  // (wave 0, lane = token).  The next block's loads are issued as soon as
-  // the current block is in LDS, so their latency overlaps the MFMA work.
-  constexpr int kCB = (kCQ * (NS / 8)) / 256;
-  constexpr int kXC = (kCQ * (kCPS / 8)) / 256;
-  u16x8 creg[kCB], breg[kCB], xreg[kXC];
+  // ---- register staging of one block
+  u16x8 creg[kCB][2], breg[kCB][2], xreg[kXC][2];
   uint16_t greg = 0;
-  int nv_next = 0;
+  // per-lane 32-bit offsets inside one block (token pair sp, column chunk c)
+  int cboff[kCB][2], xoffl[kXC][2];
+#pragma unroll
+  for (int k = 0; k < kCB; ++k) {
+    const int q = tid + 256 * k, sp = q & 31, c = q >> 5;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) cboff[k][e] = (2 * sp + e) * static_cast<int>(g.bc_row) + 8 * c;
+  }
+#pragma unroll
+  for (int k = 0; k < kXC; ++k) {
+    const int q = tid + 256 * k, sp = q & 31, c = q >> 5;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) xoffl[k][e] = (2 * sp + e) * static_cast<int>(xrow) + 8 * c;
+  }
   auto prefetch = [&](int64_t blk) {
     const int64_t t0 = blk * kCQ;
     const int nv = static_cast<int>((g.L - t0) < kCQ ? (g.L - t0) : kCQ);
-    nv_next = nv;
+    const uint16_t* cblk = Cb + t0 * g.bc_row;
+    const uint16_t* bblk = Bb + t0 * g.bc_row;
+    const uint16_t* xblk = xb + t0 * xrow;
 #pragma unroll
     for (int k = 0; k < kCB; ++k) {
-      const int idx = tid + 256 * k;
-      const int r = idx / (NS / 8), c = idx % (NS / 8);
-      creg[k] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      breg[k] = creg[k];
-      if (r < nv) {
-        const int64_t off = (b * g.L + t0 + r) * g.bc_row + bcoff + 8 * c;
-        creg[k] = *reinterpret_cast<const u16x8*>(g.Cm + off);
-        breg[k] = *reinterpret_cast<const u16x8*>(g.Bm + off);
+      const int sp = (tid + 256 * k) & 31;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        creg[k][e] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        breg[k][e] = creg[k][e];
+        if (2 * sp + e < nv) {
+          creg[k][e] = *reinterpret_cast<const u16x8*>(cblk + cboff[k][e]);
+          breg[k][e] = *reinterpret_cast<const u16x8*>(bblk + cboff[k][e]);
+        }
       }
     }
 #pragma unroll
     for (int k = 0; k < kXC; ++k) {
-      const int idx = tid + 256 * k;
-      const int s = idx & 63, c = idx >> 6;
-      xreg[k] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      if (s < nv) xreg[k] = *reinterpret_cast<const u16x8*>(g.x + (b * g.L + t0 + s) * xrow + xoff + 8 * c);
+      const int sp = (tid + 256 * k) & 31;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        xreg[k][e] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        if (2 * sp + e < nv) xreg[k][e] = *reinterpret_cast<const u16x8*>(xblk + xoffl[k][e]);
+      }
     }
-    if (w == 0 && lane < nv) greg = g.gate[(b * g.L + t0 + lane) * g.H + h];
+    greg = (lane < nv) ? gb[(t0 + lane) * g.H] : uint16_t(0);
   };
-  if (nblk > 0) prefetch(0);
+
+  // ---- registers -> LDS buffer for block blk (scalars from the gates every
+  // wave holds, scan done redundantly per wave; lane = token)
+  auto stage = [&](int64_t blk, ChunkBuf<NS>& bf) {
+    const int64_t t0 = blk * kCQ;
+    const int nv = static_cast<int>((g.L - t0) < kCQ ? (g.L - t0) : kCQ);
+    float l2, ph;
+    chunk_scalars<MODE>(greg, lane < nv, Ah, l2, ph);
+    const float c = wave_incl_sum(l2);
+    const float cend = __shfl(c, 63);
+    const float wsc = fast_exp2(cend - c) * ph;      // weight of token `lane` in the state update
+    if (w == 0) {
+      bf.cum[lane] = c;
+      bf.phi[lane] = ph;
+    }
+#pragma unroll
+    for (int k = 0; k < kCB; ++k) {
+      const int q = tid + 256 * k;
+      const int sp = q & 31, cc = q >> 5;
+      const int pa = perm_pos(8 * cc), pb = perm_pos(8 * cc + 4);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        uint16_t* cr = bf.Cs + (2 * sp + e) * kLdN;
+        uint16_t* br = bf.Bs + (2 * sp + e) * kLdN;
+        const u16x8 cv = creg[k][e], bv = breg[k][e];
+        *reinterpret_cast<u16x4*>(cr + pa) = u16x4{cv[0], cv[1], cv[2], cv[3]};
+        *reinterpret_cast<u16x4*>(cr + pb) = u16x4{cv[4], cv[5], cv[6], cv[7]};
+        *reinterpret_cast<u16x4*>(br + pa) = u16x4{bv[0], bv[1], bv[2], bv[3]};
+        *reinterpret_cast<u16x4*>(br + pb) = u16x4{bv[4], bv[5], bv[6], bv[7]};
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        *reinterpret_cast<uint32_t*>(bf.BT + (8 * cc + i) * kLdT + 2 * sp) = pack2(breg[k][0][i], breg[k][1][i]);
+    }
+#pragma unroll
+    for (int k = 0; k < kXC; ++k) {
+      const int q = tid + 256 * k;
+      const int sp = q & 31, cc = q >> 5;
+      const float w0 = __shfl(wsc, 2 * sp), w1 = __shfl(wsc, 2 * sp + 1);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        *reinterpret_cast<uint32_t*>(bf.XT + (8 * cc + i) * kLdT + 2 * sp) = pack2(xreg[k][0][i], xreg[k][1][i]);
+        *reinterpret_cast<uint32_t*>(bf.XwT + (8 * cc + i) * kLdT + 2 * sp) =
+            pack2(f2bf(bf2f(xreg[k][0][i]) * w0), f2bf(bf2f(xreg[k][1][i]) * w1));
+      }
+    }
+  };
+
+  if (nblk > 0) {
+    prefetch(0);
+    stage(0, sm[0]);
+    if (nblk > 1) prefetch(1);
+  }
+  __syncthreads();
 
   for (int64_t blk = 0; blk < nblk; ++blk) {
+    ChunkBuf<NS>& cur = sm[blk & 1];
     const int64_t t0 = blk * kCQ;
-    const int nv = nv_next;
+    const int nv = static_cast<int>((g.L - t0) < kCQ ? (g.L - t0) : kCQ);
 
     if (g.ckpt != nullptr && (t0 % g.seg) == 0) {
       float* cp = g.ckpt + ((t0 / g.seg) * g.B * g.H) * g.P * NS + sbase;
@@ -147,62 +263,18 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkFwdArgs g) {
       for (int nt = 0; nt < NT; ++nt)
         *reinterpret_cast<f32x4*>(cp + pcol * NS + 16 * nt + 4 * g4) = hacc[nt];
     }
+    // next block into the other buffer, the one after into registers
+    if (blk + 1 < nblk) {
+      stage(blk + 1, sm[(blk + 1) & 1]);
+      if (blk + 2 < nblk) prefetch(blk + 2);
+    }
 
-    // ---- per-token decay and input scale (wave 0, lane = token)
-    if (w == 0) {
-      const bool ok = lane < nv;
-      float l2, ph;
-      if (MODE == kModeGla) {
-        const float gv = ok ? bf2f(greg) : 1.f;
-        l2 = fast_log2(gv);
-        ph = ok ? 1.f : 0.f;
-      } else {
-        const float dtv = ok ? bf2f(greg) : 0.f;
-        const float lam = dtv * Ah;
-        l2 = lam * kLog2e;
-        if (MODE == kModeSsdEuler) {
-          ph = dtv;
-        } else {
-          const float ser = dtv * fmaf(lam, fmaf(lam, fmaf(lam, 1.f / 24.f, 1.f / 6.f), 0.5f), 1.f);
-          ph = fabsf(lam) < 0.1f ? ser : (fast_exp2(l2) - 1.f) / Ah;
-        }
-      }
-      sm.cum[lane] = wave_incl_sum(l2);
-      sm.phi[lane] = ph;
-    }
-    // ---- staged registers -> LDS: C, B row-major; x transposed XT[p][s]
-#pragma unroll
-    for (int k = 0; k < kCB; ++k) {
-      const int idx = tid + 256 * k;
-      const int r = idx / (NS / 8), c = idx % (NS / 8);
-      *reinterpret_cast<u16x8*>(sm.Cs + r * kLdN + 8 * c) = creg[k];
-      *reinterpret_cast<u16x8*>(sm.Bs + r * kLdN + 8 * c) = breg[k];
-    }
-#pragma unroll
-    for (int k = 0; k < kXC; ++k) {
-      const int idx = tid + 256 * k;
-      const int s = idx & 63, c = idx >> 6;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) sm.XT[(8 * c + i) * kLdT + s] = xreg[k][i];
-    }
-    __syncthreads();
-    if (blk + 1 < nblk) prefetch(blk + 1);
-
-    const float cum_end = sm.cum[kCQ - 1];
-    // ---- B scaled by 2^(cum_end - cum_s) phi_s, transposed: BwT[n][s]
-    for (int idx = tid; idx < kCQ * (NS / 8); idx += 256) {
-      const int s = idx & 63, c = idx >> 6;
-      const float ws = fast_exp2(cum_end - sm.cum[s]) * sm.phi[s];
-      const u16x8 v = *reinterpret_cast<const u16x8*>(sm.Bs + s * kLdN + 8 * c);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) sm.BwT[(8 * c + i) * kLdT + s] = f2bf(bf2f(v[i]) * ws);
-    }
-    // ---- decayed causal mask M[t][s]; 12 tiles of 16x16 (3 per wave):
-    //      (t-tile, s-tile) with s-tile <= t-tile, plus the all-zero tiles
-    //      (0,1) and (2,3) that complete the 32-wide k steps of M X.
+    // ---- decayed causal mask M[t][s]: 12 tiles of 16x16 (3 per wave), the
+    //      10 with s-tile <= t-tile plus the all-zero (0,1) and (2,3) that
+    //      complete the 32-wide k steps of M X
     {
-      const int ti_tab[12] = {0, 0, 1, 1, 2, 2, 2, 2, 3, 3, 3, 3};
-      const int si_tab[12] = {0, 1, 0, 1, 0, 1, 2, 3, 0, 1, 2, 3};
+      const int ti_tab[12] = {3, 3, 3, 2, 2, 2, 1, 1, 3, 0, 0, 2};
+      const int si_tab[12] = {0, 1, 2, 0, 1, 2, 0, 1, 3, 0, 1, 3};
 #pragma unroll
       for (int q = 0; q < 3; ++q) {
         const int ti = ti_tab[3 * w + q], si = si_tab[3 * w + q];
@@ -213,22 +285,24 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkFwdArgs g) {
           f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int kk = 0; kk < NK; ++kk)
-            z = mfma16x16x32(lds_tile(sm.Bs, kLdN, 16 * si, 32 * kk, lane),
-                             lds_tile(sm.Cs, kLdN, 16 * ti, 32 * kk, lane), z);
-          const float ct = sm.cum[t];
+            z = mfma16x16x32(lds_tile(cur.Bs, kLdN, 16 * si, 32 * kk, lane),
+                             lds_tile(cur.Cs, kLdN, 16 * ti, 32 * kk, lane), z);
+          const float ct = cur.cum[t];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int s = s0 + r;
-            const float m = (s <= t) ? z[r] * fast_exp2(ct - sm.cum[s]) * sm.phi[s] : 0.f;
+            const int sr = s0 + r;
+            float m = (sr <= t) ? z[r] * fast_exp2(ct - cur.cum[sr]) * cur.phi[sr] : 0.f;
+            if (sr == t) m += Dh;   // D x_t folded into the diagonal
             out[r] = f2bf(m);
           }
         }
-        *reinterpret_cast<u16x4*>(sm.Ms + t * kLdT + s0) = out;
+        *reinterpret_cast<u16x4*>(Ms + t * kLdT + s0) = out;
       }
     }
     __syncthreads();
 
-    // ---- y = 2^cum_t (C_t . h_prev) + M X + D x
+    // ---- y^T[p][t] = 2^cum_t (h_prev C^T)[p][t] + (X^T M^T)[p][t]
+    //      lane holds p = 16 w + 4 g4 + r, t = 16 ti + c16
     f32x4 yacc[4];
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) yacc[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -237,47 +311,41 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkFwdArgs g) {
       const bf16x8 hb = pack_dd(hacc[2 * kk], hacc[2 * kk + 1]);
 #pragma unroll
       for (int ti = 0; ti < 4; ++ti)
-        yacc[ti] = mfma16x16x32(lds_tile_perm(sm.Cs, kLdN, 16 * ti, 32 * kk, lane), hb, yacc[ti]);
+        yacc[ti] = mfma16x16x32(hb, lds_tile(cur.Cs, kLdN, 16 * ti, 32 * kk, lane), yacc[ti]);
     }
 #pragma unroll
-    for (int ti = 0; ti < 4; ++ti)
+    for (int ti = 0; ti < 4; ++ti) yacc[ti] *= fast_exp2(cur.cum[16 * ti + c16]);
+    {
+      const bf16x8 x0 = lds_tile(cur.XT, kLdT, 16 * w, 0, lane);
+      const bf16x8 x1 = lds_tile(cur.XT, kLdT, 16 * w, 32, lane);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) yacc[ti][r] *= fast_exp2(sm.cum[16 * ti + 4 * g4 + r]);
-#pragma unroll
-    for (int ti = 0; ti < 4; ++ti) {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        if (ks == 1 && ti < 2) continue;
-        yacc[ti] = mfma16x16x32(lds_tile(sm.Ms, kLdT, 16 * ti, 32 * ks, lane),
-                                lds_tile(sm.XT, kLdT, 16 * w, 32 * ks, lane), yacc[ti]);
+      for (int ti = 0; ti < 4; ++ti) {
+        yacc[ti] = mfma16x16x32(x0, lds_tile(Ms, kLdT, 16 * ti, 0, lane), yacc[ti]);
+        if (ti >= 2) yacc[ti] = mfma16x16x32(x1, lds_tile(Ms, kLdT, 16 * ti, 32, lane), yacc[ti]);
       }
     }
     {
-      const int p = 16 * w + c16;
+      uint16_t* yt = yb + t0 * xrow + 16 * w + 4 * g4;
 #pragma unroll
       for (int ti = 0; ti < 4; ++ti) {
-        const int tb = 16 * ti + 4 * g4;
-        const u16x4 xv = *reinterpret_cast<const u16x4*>(sm.XT + p * kLdT + tb);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          if (tb + r < nv) {
-            const float v = yacc[ti][r] + Dh * bf2f(xv[r]);
-            g.y[(b * g.L + t0 + tb + r) * xrow + xoff + p] = f2bf(v);
-          }
+        const int t = 16 * ti + c16;
+        if (t < nv) {
+          const u16x4 v = {f2bf(yacc[ti][0]), f2bf(yacc[ti][1]), f2bf(yacc[ti][2]), f2bf(yacc[ti][3])};
+          *reinterpret_cast<u16x4*>(yt + t * xrow) = v;
         }
       }
     }
 
-    // ---- h_next = 2^cum_end h_prev + Bw^T X
+    // ---- h_next = 2^cum_end h_prev + B^T (decay-weighted x)
     {
-      const float dec = fast_exp2(cum_end);
+      const float dec = fast_exp2(cur.cum[kCQ - 1]);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         hacc[nt] *= dec;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
-          hacc[nt] = mfma16x16x32(lds_tile(sm.BwT, kLdT, 16 * nt, 32 * ks, lane),
-                                  lds_tile(sm.XT, kLdT, 16 * w, 32 * ks, lane), hacc[nt]);
+          hacc[nt] = mfma16x16x32(lds_tile(cur.BT, kLdT, 16 * nt, 32 * ks, lane),
+                                  lds_tile(cur.XwT, kLdT, 16 * w, 32 * ks, lane), hacc[nt]);
       }
     }
     __syncthreads();
