@@ -229,8 +229,8 @@ def load_traffic():
     """HBM traffic of the selective kernel from the committed rocprofv3 PMC
     summary, if it was taken on the current kernel source."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "selective_scan_cfg2_traffic.txt")
-    src = os.path.join(ROOT, "ssm_selective_scan_amd", "csrc", "selective_scan.hip")
+    path = os.path.join(ROOT, "profiles", "selective_scan_mamba1_B8_L4096_D2048_N16_traffic.txt")
+    csrc = os.path.join(ROOT, "ssm_selective_scan_amd", "csrc")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -239,7 +239,9 @@ def load_traffic():
             if "=" in line and not line.startswith("#"):
                 k, v = line.split("=", 1)
                 kv[k.strip()] = v.strip()
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    src = b"".join(open(os.path.join(csrc, f), "rb").read()
+                   for f in ("selective_scan.hip", "common.hpp"))
+    sha = hashlib.sha256(src).hexdigest()[:16]
     if kv.get("kernel_src_sha256_16") != sha:
         return None
     return float(kv["traffic_bytes_per_launch"])
