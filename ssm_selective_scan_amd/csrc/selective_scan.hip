@@ -34,9 +34,9 @@ enum { kDiscZoh = 0, kDiscEuler = 1 };
 // chunks (16-byte loads for bf16 when VEC, i.e. D % 8 == 0), B and C as the
 // contiguous TT*N block of the tile.  All per-thread offsets are 32-bit and
 // computed once; each tile only moves the (wave-uniform) base pointers.
-template <typename T, int TT, int MK, bool VEC>
+template <typename T, int TT, int MK, int ME, bool VEC>
 struct SelStage {
-  static constexpr int kMaxE = 2;   // B/C elements per thread (threads >= 16 N)
+  static constexpr int kMaxE = ME;  // B/C elements per thread
   T xr[MK][8], dr[MK][8];           // raw I/O words until they are written to LDS
   T br[kMaxE], cr[kMaxE];
   int xoff[MK], xlds[MK], xrow[MK];  // global offset, LDS offset, token of each chunk
@@ -190,31 +190,34 @@ struct SelGroup {
   }
 };
 
-template <typename T, int DISC, bool PRECISE, int TT, int MK, int NPW, int GS, bool VEC>
+template <typename T, int DISC, bool PRECISE, int TT, int NPW, int NW, int GS, bool VEC>
 __device__ __forceinline__ void selective_body(
     const T* __restrict__ x, const T* __restrict__ dt, const T* __restrict__ Bm,
     const T* __restrict__ Cm, T* __restrict__ y, float* __restrict__ smem, float (&h)[NPW],
     const float (&A2)[NPW], const float (&iA)[NPW], const float (&An)[NPW], int64_t bi,
     int64_t d0, int64_t L, int64_t D, int N) {
-  const int tid = threadIdx.x, nthr = blockDim.x;
+  constexpr int kThreads = 64 * NW;
+  constexpr int MK = (TT * 8 + kThreads - 1) / kThreads;    // 8-channel x/dt chunks per thread
+  constexpr int ME = (TT * NPW * NW + kThreads - 1) / kThreads;  // B/C values per thread
+  constexpr int kRows = TT / NW;                            // output tokens per thread per tile
+  static_assert(TT % NW == 0, "tile must split evenly over the waves");
+  const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-  const int nw = nthr >> 6;
   const int n0 = w * NPW;
   float* xs = smem;               // [TT][64]
   float* dts = xs + TT * 64;      // [TT][64]
   float* Bs = dts + TT * 64;      // [TT][64]  columns n >= N stay zero
   float* Cs = Bs + TT * 64;       // [TT][64]
   float* Dk = Cs + TT * 64;       // [64]
-  float* yp = Dk + 64;            // [nw][TT][64]
+  float* yp = Dk + 64;            // [NW][TT][64]
   const int dcols = static_cast<int>((D - d0) < 64 ? (D - d0) : 64);
 
-  // per-thread output coordinates of the reduce phase: column dd, rows
-  // r0, r0 + nw, ...  (32-bit offsets from the tile's base pointer)
+  // reduce phase: thread (dd, r0) sums tokens r0, r0 + NW, ... of column dd
   const int dd = tid & 63, r0 = tid >> 6;
   const int Di = static_cast<int>(D);
 
-  SelStage<T, TT, MK, VEC> st;
+  SelStage<T, TT, MK, ME, VEC> st;
   st.init(D, N);
   const int64_t row0 = bi * L;
   if (L > 0) {
@@ -248,16 +251,31 @@ __device__ __forceinline__ void selective_body(
     }
     __syncthreads();
 
-    // ---- sum the per-wave partial readouts, add D x, store y
+    // ---- sum the per-wave partial readouts, add D x, store y.  All NW * kRows
+    // partials of a thread are read before any is added.
     {
       const int nt = static_cast<int>((L - t0) < TT ? (L - t0) : TT);
       T* y0 = y + (row0 + t0) * D + d0;
+      const float dk = Dk[dd];
+      float part[kRows][NW];
+      float s[kRows];
+#pragma unroll
+      for (int k = 0; k < kRows; ++k) {
+        const int tt = r0 + k * NW;
+        s[k] = dk * xs[tt * 64 + dd];
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) part[k][ww] = yp[(ww * TT + tt) * 64 + dd];
+      }
+#pragma unroll
+      for (int k = 0; k < kRows; ++k) {
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) s[k] += part[k][ww];
+      }
       if (dd < dcols) {
-        const float dk = Dk[dd];
-        for (int tt = r0; tt < nt; tt += nw) {
-          float s = dk * xs[tt * 64 + dd];
-          for (int ww = 0; ww < nw; ++ww) s += yp[(ww * TT + tt) * 64 + dd];
-          Io<T>::store(y0 + tt * Di + dd, s);
+#pragma unroll
+        for (int k = 0; k < kRows; ++k) {
+          const int tt = r0 + k * NW;
+          if (tt < nt) Io<T>::store(y0 + tt * Di + dd, s[k]);
         }
       }
     }
@@ -265,14 +283,16 @@ __device__ __forceinline__ void selective_body(
   }
 }
 
-template <typename T, int DISC, int TT, int MK, int MAXT, int NPW, bool VEC>
-__global__ __launch_bounds__(MAXT) void selective_scan_kernel(
+// NW waves of NPW state indices each cover n < NW * NPW; indices n >= N are
+// padding (A = 0, 1/A = 0, B = C = 0) and contribute nothing.
+template <typename T, int DISC, int TT, int NPW, int NW, bool VEC>
+__global__ __launch_bounds__(64 * NW) void selective_scan_kernel(
     const T* __restrict__ x, const T* __restrict__ dt, const float* __restrict__ A,
     const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ Dskip,
     const float* __restrict__ h0, T* __restrict__ y, float* __restrict__ h_last, int64_t L,
     int64_t D, int N) {
   extern __shared__ float smem[];
-  constexpr int GS = MAXT >= 1024 ? 2 : ((NPW == 4 || sizeof(T) == 4) ? 4 : 8);
+  constexpr int GS = NW >= 16 ? 2 : ((NPW == 4 || sizeof(T) == 4) ? 4 : 8);
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63;
   const int64_t ndt = (D + kSelCT - 1) / kSelCT;
@@ -288,8 +308,6 @@ __global__ __launch_bounds__(MAXT) void selective_scan_kernel(
   for (int j = 0; j < NPW; ++j) {
     const int n = n0 + j;
     const bool ok = dok && n < N;
-    // state indices n >= N get A = 0 and 1/A = 0: with B = C = 0 there they
-    // contribute nothing and need no per-index branch in the step loop
     const float a = ok ? A[d * N + n] : 0.f;
     An[j] = a;
     A2[j] = a * kLog2e;
@@ -299,20 +317,20 @@ __global__ __launch_bounds__(MAXT) void selective_scan_kernel(
   }
   {
     float* Bs = smem + 2 * TT * 64;
-    for (int i = tid; i < 2 * TT * 64; i += blockDim.x) Bs[i] = 0.f;   // Bs and Cs
+    for (int i = tid; i < 2 * TT * 64; i += 64 * NW) Bs[i] = 0.f;   // Bs and Cs
     float* Dk = smem + 4 * TT * 64;
     if (tid < 64) Dk[tid] = (Dskip != nullptr && d0 + tid < D) ? Dskip[d0 + tid] : 0.f;
   }
   const bool precise = __syncthreads_or(small ? 1 : 0) != 0;
 
   if (DISC == kDiscEuler) {
-    selective_body<T, DISC, false, TT, MK, NPW, GS, VEC>(x, dt, Bm, Cm, y, smem, h, A2, iA, An,
+    selective_body<T, DISC, false, TT, NPW, NW, GS, VEC>(x, dt, Bm, Cm, y, smem, h, A2, iA, An,
                                                         bi, d0, L, D, N);
   } else if (precise) {
-    selective_body<T, DISC, true, TT, MK, NPW, GS, VEC>(x, dt, Bm, Cm, y, smem, h, A2, iA, An,
+    selective_body<T, DISC, true, TT, NPW, NW, GS, VEC>(x, dt, Bm, Cm, y, smem, h, A2, iA, An,
                                                        bi, d0, L, D, N);
   } else {
-    selective_body<T, DISC, false, TT, MK, NPW, GS, VEC>(x, dt, Bm, Cm, y, smem, h, A2, iA, An,
+    selective_body<T, DISC, false, TT, NPW, NW, GS, VEC>(x, dt, Bm, Cm, y, smem, h, A2, iA, An,
                                                         bi, d0, L, D, N);
   }
 
@@ -323,38 +341,40 @@ __global__ __launch_bounds__(MAXT) void selective_scan_kernel(
   }
 }
 
-template <typename T, int DISC, int TT, int MK, int MAXT, int NPW>
+template <typename T, int DISC, int TT, int NPW, int NW>
 static hipError_t launch_sel(const void* x, const void* dt, const float* A, const void* Bm,
                              const void* Cm, const float* Dskip, const float* h0, void* y,
                              float* h_last, int64_t B, int64_t L, int64_t D, int N,
                              hipStream_t stream) {
-  const int nw = (N + NPW - 1) / NPW;
-  const size_t lds = (4 * TT * 64 + 64 + static_cast<size_t>(nw) * TT * 64) * sizeof(float);
+  const size_t lds = (4 * TT * 64 + 64 + static_cast<size_t>(NW) * TT * 64) * sizeof(float);
   dim3 grid(static_cast<unsigned>(B * ((D + kSelCT - 1) / kSelCT)));
   auto go = [&](auto kern) {
-    hipLaunchKernelGGL(kern, grid, dim3(64 * nw), lds, stream, static_cast<const T*>(x),
+    hipLaunchKernelGGL(kern, grid, dim3(64 * NW), lds, stream, static_cast<const T*>(x),
                        static_cast<const T*>(dt), A, static_cast<const T*>(Bm),
                        static_cast<const T*>(Cm), Dskip, h0, static_cast<T*>(y), h_last, L, D, N);
   };
-  if (D % 8 == 0) go(selective_scan_kernel<T, DISC, TT, MK, MAXT, NPW, true>);
-  else go(selective_scan_kernel<T, DISC, TT, MK, MAXT, NPW, false>);
+  if (D % 8 == 0) go(selective_scan_kernel<T, DISC, TT, NPW, NW, true>);
+  else go(selective_scan_kernel<T, DISC, TT, NPW, NW, false>);
   return hipGetLastError();
 }
 
-// Instances by block size:
-//   N <= 16: 2 state indices per wave, <= 512 threads, TT = 32
-//   N <= 32: 4 per wave, <= 512 threads, TT = 32
-//   N <= 64: 4 per wave, <= 1024 threads, TT = 16 (partials must fit in LDS)
+// Instances by state size (state indices per wave x waves, tile length):
+//   N <=  8: 2 x 4,  TT = 32
+//   N <= 16: 2 x 8,  TT = 32
+//   N <= 32: 4 x 8,  TT = 32
+//   N <= 64: 4 x 16, TT = 16 (the partial readouts must fit in LDS)
 template <typename T, int DISC>
 static hipError_t launch_sel_n(const void* x, const void* dt, const float* A, const void* Bm,
                                const void* Cm, const float* Dskip, const float* h0, void* y,
                                float* h_last, int64_t B, int64_t L, int64_t D, int N,
                                hipStream_t stream) {
+  if (N <= 8)
+    return launch_sel<T, DISC, 32, 2, 4>(x, dt, A, Bm, Cm, Dskip, h0, y, h_last, B, L, D, N, stream);
   if (N <= 16)
-    return launch_sel<T, DISC, 32, 4, 512, 2>(x, dt, A, Bm, Cm, Dskip, h0, y, h_last, B, L, D, N, stream);
+    return launch_sel<T, DISC, 32, 2, 8>(x, dt, A, Bm, Cm, Dskip, h0, y, h_last, B, L, D, N, stream);
   if (N <= 32)
-    return launch_sel<T, DISC, 32, 1, 512, 4>(x, dt, A, Bm, Cm, Dskip, h0, y, h_last, B, L, D, N, stream);
-  return launch_sel<T, DISC, 16, 1, 1024, 4>(x, dt, A, Bm, Cm, Dskip, h0, y, h_last, B, L, D, N, stream);
+    return launch_sel<T, DISC, 32, 4, 8>(x, dt, A, Bm, Cm, Dskip, h0, y, h_last, B, L, D, N, stream);
+  return launch_sel<T, DISC, 16, 4, 16>(x, dt, A, Bm, Cm, Dskip, h0, y, h_last, B, L, D, N, stream);
 }
 
 template <typename T>
