@@ -25,21 +25,20 @@
 // owns columns p in [16w, 16w+16) for all n); it goes to memory only for the
 // optional checkpoints and the final state.  The 10 causal C B^T tiles of
 // the decayed mask M are split over the waves and shared through LDS.
-// Inputs live in two LDS buffers: while block k is computed from one, block
-// k+1 (loaded from HBM into registers during block k-1) is written into the
-// other, transposed where a contraction runs over tokens (B as [n][s], x and
-// the decay-weighted x as [p][s]) with two tokens per 4-byte LDS word.  The
-// rows of C and B are stored with the n-order of pack_dd inside each 32-wide
-// block (see perm_pos), so C h_prev reads its A operand as one plain 16-byte
-// read per lane; C B^T sees the same order on both operands.  Two barriers
-// per block.
+// Every input tile sits in LDS exactly as it lies in memory (token rows):
+// operands whose contraction runs over tokens (x in M X, B and the
+// decay-weighted x in the state update) are read with gfx950's transposing
+// LDS read, so staging is a plain 16-byte copy.  Two LDS buffers: while
+// block k is computed from one, block k+1 (loaded from HBM into registers
+// during block k-1) is written into the other.  Row pitches are chosen per
+// tile for its read pattern (see ChunkBuf).  Two barriers per block.
 #include "common.hpp"
 
 namespace lr {
 
 constexpr int kCQ = 64;        // tokens per block
 constexpr int kCPS = 64;       // p columns per workgroup
-constexpr int kLdT = kCQ + 8;  // leading dim of token-contiguous LDS tiles
+constexpr int kLdM = kCQ + 8;  // pitch of M[t][s] (36 words: conflict-free 16-byte reads)
 
 enum { kModeSsdZoh = 0, kModeSsdEuler = 1, kModeGla = 2 };
 
@@ -59,22 +58,20 @@ struct ChunkFwdArgs {
   int64_t st_p, st_n;   // state strides of p and n (SSD: N, 1; GLA: 1, V)
 };
 
-// Position of n inside its 32-wide block in the permuted C/B row layout:
-// positions 8g..8g+3 hold n = 4g..4g+3, positions 8g+4..8g+7 hold
-// n = 16+4g..16+4g+3 (g < 4), which is the k order of pack_dd.
-__device__ __forceinline__ int perm_pos(int n) {
-  const int nl = n & 31, base = n & ~31;
-  return base + (nl < 16 ? 8 * (nl >> 2) + (nl & 3) : 8 * ((nl - 16) >> 2) + 4 + (nl & 3));
-}
-
+// One block of inputs in LDS, token-major.  Every row starts 16-byte
+// aligned; pitches in 4-byte words are, mod 32:
+//   Cs: 4  -> the 16-byte reads of C B^T are conflict-free
+//   Bs: 8  -> the transposing reads of the state update are conflict-free
+//   Xs, Xw: 8 (transposing reads only)
 template <int NS>
 struct ChunkBuf {
-  static constexpr int kLdN = NS + 8;
-  uint16_t Cs[kCQ * kLdN];     // C[t][n], n permuted (perm_pos)
-  uint16_t Bs[kCQ * kLdN];     // B[s][n], n permuted (perm_pos)
-  uint16_t BT[NS * kLdT];      // B[s][n] as [n][s]
-  uint16_t XT[kCPS * kLdT];    // x[s][p] as [p][s]
-  uint16_t XwT[kCPS * kLdT];   // 2^(cum_end - cum_s) phi_s x[s][p] as [p][s]
+  static constexpr int kLdC = NS + 8;
+  static constexpr int kLdB = NS + 16;
+  static constexpr int kLdX = kCPS + 16;
+  uint16_t Cs[kCQ * kLdC];     // C[t][n]
+  uint16_t Bs[kCQ * kLdB];     // B[s][n]
+  uint16_t Xs[kCQ * kLdX];     // x[s][p]
+  uint16_t Xw[kCQ * kLdX];     // 2^(cum_end - cum_s) phi_s x[s][p]
   float cum[kCQ];
   float phi[kCQ];
 };
@@ -99,20 +96,17 @@ __device__ __forceinline__ void chunk_scalars(uint16_t graw, bool ok, float Ah, 
   }
 }
 
-__device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi) {
-  return static_cast<uint32_t>(lo) | (static_cast<uint32_t>(hi) << 16);
-}
-
 template <int MODE, int NS>
 __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkFwdArgs g) {
   constexpr int NT = NS / 16;     // 16-row tiles of n
   constexpr int NK = NS / 32;     // 32-wide k steps over n
-  constexpr int kLdN = ChunkBuf<NS>::kLdN;
-  // staged pair-chunks per thread: (token pair, 8-wide column chunk)
-  constexpr int kCB = (kCQ / 2) * (NS / 8) / 256;    // C, B
-  constexpr int kXC = (kCQ / 2) * (kCPS / 8) / 256;  // x
+  constexpr int kLdC = ChunkBuf<NS>::kLdC, kLdB = ChunkBuf<NS>::kLdB, kLdX = ChunkBuf<NS>::kLdX;
+  // staged 16-byte chunks per thread: row = token, 8 columns per chunk
+  constexpr int kRowCB = NS / 8, kRowX = kCPS / 8;
+  constexpr int kCB = kCQ * kRowCB / 256;   // C, B
+  constexpr int kXC = kCQ * kRowX / 256;    // x
   __shared__ ChunkBuf<NS> sm[2];
-  __shared__ uint16_t Ms[kCQ * kLdT];   // M[t][s]
+  __shared__ uint16_t Ms[kCQ * kLdM];   // M[t][s]
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63;
@@ -150,22 +144,21 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkFwdArgs g) {
 
   const int64_t nblk = (g.L + kCQ - 1) / kCQ;
 
-  // ---- register staging of one block
-  u16x8 creg[kCB][2], breg[kCB][2], xreg[kXC][2];
+  // ---- register staging of one block: chunk q = tid + 256 k is token
+  // q / kRow, columns 8 (q % kRow) .. + 7 (consecutive lanes read consecutive
+  // 16 bytes of a row; 32-bit offsets inside the block)
+  u16x8 creg[kCB], breg[kCB], xreg[kXC];
   uint16_t greg = 0;
-  // per-lane 32-bit offsets inside one block (token pair sp, column chunk c)
-  int cboff[kCB][2], xoffl[kXC][2];
+  int cboff[kCB], xoffl[kXC];
 #pragma unroll
   for (int k = 0; k < kCB; ++k) {
-    const int q = tid + 256 * k, sp = q & 31, c = q >> 5;
-#pragma unroll
-    for (int e = 0; e < 2; ++e) cboff[k][e] = (2 * sp + e) * static_cast<int>(g.bc_row) + 8 * c;
+    const int q = tid + 256 * k;
+    cboff[k] = (q / kRowCB) * static_cast<int>(g.bc_row) + 8 * (q % kRowCB);
   }
 #pragma unroll
   for (int k = 0; k < kXC; ++k) {
-    const int q = tid + 256 * k, sp = q & 31, c = q >> 5;
-#pragma unroll
-    for (int e = 0; e < 2; ++e) xoffl[k][e] = (2 * sp + e) * static_cast<int>(xrow) + 8 * c;
+    const int q = tid + 256 * k;
+    xoffl[k] = (q / kRowX) * static_cast<int>(xrow) + 8 * (q % kRowX);
   }
   auto prefetch = [&](int64_t blk) {
     const int64_t t0 = blk * kCQ;
@@ -175,25 +168,19 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkFwdArgs g) {
     const uint16_t* xblk = xb + t0 * xrow;
 #pragma unroll
     for (int k = 0; k < kCB; ++k) {
-      const int sp = (tid + 256 * k) & 31;
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        creg[k][e] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-        breg[k][e] = creg[k][e];
-        if (2 * sp + e < nv) {
-          creg[k][e] = *reinterpret_cast<const u16x8*>(cblk + cboff[k][e]);
-          breg[k][e] = *reinterpret_cast<const u16x8*>(bblk + cboff[k][e]);
-        }
+      const int row = (tid + 256 * k) / kRowCB;
+      creg[k] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      breg[k] = creg[k];
+      if (row < nv) {
+        creg[k] = *reinterpret_cast<const u16x8*>(cblk + cboff[k]);
+        breg[k] = *reinterpret_cast<const u16x8*>(bblk + cboff[k]);
       }
     }
 #pragma unroll
     for (int k = 0; k < kXC; ++k) {
-      const int sp = (tid + 256 * k) & 31;
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        xreg[k][e] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-        if (2 * sp + e < nv) xreg[k][e] = *reinterpret_cast<const u16x8*>(xblk + xoffl[k][e]);
-      }
+      const int row = (tid + 256 * k) / kRowX;
+      xreg[k] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      if (row < nv) xreg[k] = *reinterpret_cast<const u16x8*>(xblk + xoffl[k]);
     }
     greg = (lane < nv) ? gb[(t0 + lane) * g.H] : uint16_t(0);
   };
@@ -214,34 +201,19 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkFwdArgs g) {
     }
 #pragma unroll
     for (int k = 0; k < kCB; ++k) {
-      const int q = tid + 256 * k;
-      const int sp = q & 31, cc = q >> 5;
-      const int pa = perm_pos(8 * cc), pb = perm_pos(8 * cc + 4);
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        uint16_t* cr = bf.Cs + (2 * sp + e) * kLdN;
-        uint16_t* br = bf.Bs + (2 * sp + e) * kLdN;
-        const u16x8 cv = creg[k][e], bv = breg[k][e];
-        *reinterpret_cast<u16x4*>(cr + pa) = u16x4{cv[0], cv[1], cv[2], cv[3]};
-        *reinterpret_cast<u16x4*>(cr + pb) = u16x4{cv[4], cv[5], cv[6], cv[7]};
-        *reinterpret_cast<u16x4*>(br + pa) = u16x4{bv[0], bv[1], bv[2], bv[3]};
-        *reinterpret_cast<u16x4*>(br + pb) = u16x4{bv[4], bv[5], bv[6], bv[7]};
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        *reinterpret_cast<uint32_t*>(bf.BT + (8 * cc + i) * kLdT + 2 * sp) = pack2(breg[k][0][i], breg[k][1][i]);
+      const int q = tid + 256 * k, row = q / kRowCB, col = 8 * (q % kRowCB);
+      *reinterpret_cast<u16x8*>(bf.Cs + row * kLdC + col) = creg[k];
+      *reinterpret_cast<u16x8*>(bf.Bs + row * kLdB + col) = breg[k];
     }
 #pragma unroll
     for (int k = 0; k < kXC; ++k) {
-      const int q = tid + 256 * k;
-      const int sp = q & 31, cc = q >> 5;
-      const float w0 = __shfl(wsc, 2 * sp), w1 = __shfl(wsc, 2 * sp + 1);
+      const int q = tid + 256 * k, row = q / kRowX, col = 8 * (q % kRowX);
+      const float ws = __shfl(wsc, row);
+      u16x8 xw;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        *reinterpret_cast<uint32_t*>(bf.XT + (8 * cc + i) * kLdT + 2 * sp) = pack2(xreg[k][0][i], xreg[k][1][i]);
-        *reinterpret_cast<uint32_t*>(bf.XwT + (8 * cc + i) * kLdT + 2 * sp) =
-            pack2(f2bf(bf2f(xreg[k][0][i]) * w0), f2bf(bf2f(xreg[k][1][i]) * w1));
-      }
+      for (int i = 0; i < 8; ++i) xw[i] = f2bf(bf2f(xreg[k][i]) * ws);
+      *reinterpret_cast<u16x8*>(bf.Xs + row * kLdX + col) = xreg[k];
+      *reinterpret_cast<u16x8*>(bf.Xw + row * kLdX + col) = xw;
     }
   };
 
@@ -285,8 +257,8 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkFwdArgs g) {
           f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int kk = 0; kk < NK; ++kk)
-            z = mfma16x16x32(lds_tile(cur.Bs, kLdN, 16 * si, 32 * kk, lane),
-                             lds_tile(cur.Cs, kLdN, 16 * ti, 32 * kk, lane), z);
+            z = mfma16x16x32(lds_tile(cur.Bs, kLdB, 16 * si, 32 * kk, lane),
+                             lds_tile(cur.Cs, kLdC, 16 * ti, 32 * kk, lane), z);
           const float ct = cur.cum[t];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
@@ -296,7 +268,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkFwdArgs g) {
             out[r] = f2bf(m);
           }
         }
-        *reinterpret_cast<u16x4*>(Ms + t * kLdT + s0) = out;
+        *reinterpret_cast<u16x4*>(Ms + t * kLdM + s0) = out;
       }
     }
     __syncthreads();
@@ -311,17 +283,17 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkFwdArgs g) {
       const bf16x8 hb = pack_dd(hacc[2 * kk], hacc[2 * kk + 1]);
 #pragma unroll
       for (int ti = 0; ti < 4; ++ti)
-        yacc[ti] = mfma16x16x32(hb, lds_tile(cur.Cs, kLdN, 16 * ti, 32 * kk, lane), yacc[ti]);
+        yacc[ti] = mfma16x16x32(hb, lds_tile_perm(cur.Cs, kLdC, 16 * ti, 32 * kk, lane), yacc[ti]);
     }
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) yacc[ti] *= fast_exp2(cur.cum[16 * ti + c16]);
     {
-      const bf16x8 x0 = lds_tile(cur.XT, kLdT, 16 * w, 0, lane);
-      const bf16x8 x1 = lds_tile(cur.XT, kLdT, 16 * w, 32, lane);
+      const bf16x8 x0 = lds_tile_tr(cur.Xs, kLdX, 0, 16 * w, lane);
+      const bf16x8 x1 = lds_tile_tr(cur.Xs, kLdX, 32, 16 * w, lane);
 #pragma unroll
       for (int ti = 0; ti < 4; ++ti) {
-        yacc[ti] = mfma16x16x32(x0, lds_tile(Ms, kLdT, 16 * ti, 0, lane), yacc[ti]);
-        if (ti >= 2) yacc[ti] = mfma16x16x32(x1, lds_tile(Ms, kLdT, 16 * ti, 32, lane), yacc[ti]);
+        yacc[ti] = mfma16x16x32(x0, lds_tile(Ms, kLdM, 16 * ti, 0, lane), yacc[ti]);
+        if (ti >= 2) yacc[ti] = mfma16x16x32(x1, lds_tile(Ms, kLdM, 16 * ti, 32, lane), yacc[ti]);
       }
     }
     {
@@ -339,13 +311,13 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkFwdArgs g) {
     // ---- h_next = 2^cum_end h_prev + B^T (decay-weighted x)
     {
       const float dec = fast_exp2(cur.cum[kCQ - 1]);
+      const bf16x8 xw0 = lds_tile_tr(cur.Xw, kLdX, 0, 16 * w, lane);
+      const bf16x8 xw1 = lds_tile_tr(cur.Xw, kLdX, 32, 16 * w, lane);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         hacc[nt] *= dec;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-          hacc[nt] = mfma16x16x32(lds_tile(cur.BT, kLdT, 16 * nt, 32 * ks, lane),
-                                  lds_tile(cur.XwT, kLdT, 16 * w, 32 * ks, lane), hacc[nt]);
+        hacc[nt] = mfma16x16x32(lds_tile_tr(cur.Bs, kLdB, 0, 16 * nt, lane), xw0, hacc[nt]);
+        hacc[nt] = mfma16x16x32(lds_tile_tr(cur.Bs, kLdB, 32, 16 * nt, lane), xw1, hacc[nt]);
       }
     }
     __syncthreads();

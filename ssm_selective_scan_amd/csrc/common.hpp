@@ -125,6 +125,25 @@ __device__ __forceinline__ bf16x8 lds_tile_perm(const uint16_t* base, int ld, in
   return as_bf16x8(v);
 }
 
+// 16x32 operand tile from LDS stored [k][m] (m contiguous, leading dim ld,
+// ld % 4 == 0): operand index m0 + (lane & 15), k-block k0.  Uses gfx950's
+// transposing LDS read ds_read_b64_tr_b16: inside each group of 16 lanes, lane
+// i receives element j of the 8-byte chunk addressed by lane 4 j + i / 4, at
+// position i % 4.  Lane m of group g therefore addresses row k0 + 8 g + m / 4
+// (then + 4 for the second half), columns m0 + 4 (m % 4) .. + 3, and ends up
+// with column m0 + (lane & 15), rows k0 + 8 g + 0..7.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
+__device__ __forceinline__ bf16x8 lds_tile_tr(const uint16_t* base, int ld, int k0, int m0, int lane) {
+  const int g = lane >> 4, m = lane & 15;
+  const uint16_t* p = base + (k0 + 8 * g + (m >> 2)) * ld + m0 + 4 * (m & 3);
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(p));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(p + 4 * ld));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 // Two fp32 D tiles (k rows 0-15 and 16-31 of a 32-k block) -> one bf16
 // operand with the permutation of lds_tile_perm.
 __device__ __forceinline__ bf16x8 pack_dd(f32x4 lo, f32x4 hi) {
