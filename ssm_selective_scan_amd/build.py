@@ -25,6 +25,9 @@ FLAGS = [
     # no packed-fp32 VALU instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-munsafe-fp-atomics", "-ffp-contract=fast",
+    # MFMA accumulators in ordinary VGPRs: no copies between AGPRs and VGPRs
+    # where an accumulator is also an operand or is scaled by VALU code
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
 

@@ -149,38 +149,53 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkFwdArgs g) {
   // 16 bytes of a row; 32-bit offsets inside the block)
   u16x8 creg[kCB], breg[kCB], xreg[kXC];
   uint16_t greg = 0;
-  int cboff[kCB], xoffl[kXC];
+  // byte offsets from the block's first token (unsigned 32-bit: the loads
+  // take the wave-uniform block base as their 64-bit address)
+  uint32_t cboff[kCB], xoffl[kXC];
 #pragma unroll
   for (int k = 0; k < kCB; ++k) {
     const int q = tid + 256 * k;
-    cboff[k] = (q / kRowCB) * static_cast<int>(g.bc_row) + 8 * (q % kRowCB);
+    cboff[k] = 2u * ((q / kRowCB) * static_cast<uint32_t>(g.bc_row) + 8 * (q % kRowCB));
   }
 #pragma unroll
   for (int k = 0; k < kXC; ++k) {
     const int q = tid + 256 * k;
-    xoffl[k] = (q / kRowX) * static_cast<int>(xrow) + 8 * (q % kRowX);
+    xoffl[k] = 2u * ((q / kRowX) * static_cast<uint32_t>(xrow) + 8 * (q % kRowX));
   }
+  auto ld16 = [](const uint16_t* base, uint32_t off) {
+    return *reinterpret_cast<const u16x8*>(reinterpret_cast<const char*>(base) + off);
+  };
   auto prefetch = [&](int64_t blk) {
     const int64_t t0 = blk * kCQ;
     const int nv = static_cast<int>((g.L - t0) < kCQ ? (g.L - t0) : kCQ);
     const uint16_t* cblk = Cb + t0 * g.bc_row;
     const uint16_t* bblk = Bb + t0 * g.bc_row;
     const uint16_t* xblk = xb + t0 * xrow;
+    if (nv == kCQ) {   // full block: no bounds
 #pragma unroll
-    for (int k = 0; k < kCB; ++k) {
-      const int row = (tid + 256 * k) / kRowCB;
-      creg[k] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      breg[k] = creg[k];
-      if (row < nv) {
-        creg[k] = *reinterpret_cast<const u16x8*>(cblk + cboff[k]);
-        breg[k] = *reinterpret_cast<const u16x8*>(bblk + cboff[k]);
+      for (int k = 0; k < kCB; ++k) {
+        creg[k] = ld16(cblk, cboff[k]);
+        breg[k] = ld16(bblk, cboff[k]);
       }
-    }
 #pragma unroll
-    for (int k = 0; k < kXC; ++k) {
-      const int row = (tid + 256 * k) / kRowX;
-      xreg[k] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      if (row < nv) xreg[k] = *reinterpret_cast<const u16x8*>(xblk + xoffl[k]);
+      for (int k = 0; k < kXC; ++k) xreg[k] = ld16(xblk, xoffl[k]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < kCB; ++k) {
+        const int row = (tid + 256 * k) / kRowCB;
+        creg[k] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        breg[k] = creg[k];
+        if (row < nv) {
+          creg[k] = ld16(cblk, cboff[k]);
+          breg[k] = ld16(bblk, cboff[k]);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < kXC; ++k) {
+        const int row = (tid + 256 * k) / kRowX;
+        xreg[k] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        if (row < nv) xreg[k] = ld16(xblk, xoffl[k]);
+      }
     }
     greg = (lane < nv) ? gb[(t0 + lane) * g.H] : uint16_t(0);
   };
@@ -224,16 +239,23 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkFwdArgs g) {
   }
   __syncthreads();
 
+  // checkpoint s (the state entering token s * seg) goes to ckpt + s * ck_step
+  const int64_t ck_step = g.B * g.H * g.P * NS;
+  float* ck_next = g.ckpt != nullptr ? g.ckpt + sbase + pcol * NS + 4 * g4 : nullptr;
+  int64_t ck_t = 0;
+  // per-lane byte offset of this lane's 4 outputs of token c16 in a 16-token tile
+  const uint32_t yoff = 2u * (static_cast<uint32_t>(c16) * static_cast<uint32_t>(xrow) + 16 * w + 4 * g4);
+
   for (int64_t blk = 0; blk < nblk; ++blk) {
     ChunkBuf<NS>& cur = sm[blk & 1];
     const int64_t t0 = blk * kCQ;
     const int nv = static_cast<int>((g.L - t0) < kCQ ? (g.L - t0) : kCQ);
 
-    if (g.ckpt != nullptr && (t0 % g.seg) == 0) {
-      float* cp = g.ckpt + ((t0 / g.seg) * g.B * g.H) * g.P * NS + sbase;
+    if (ck_next != nullptr && t0 == ck_t) {
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        *reinterpret_cast<f32x4*>(cp + pcol * NS + 16 * nt + 4 * g4) = hacc[nt];
+      for (int nt = 0; nt < NT; ++nt) *reinterpret_cast<f32x4*>(ck_next + 16 * nt) = hacc[nt];
+      ck_next += ck_step;
+      ck_t += g.seg;
     }
     // next block into the other buffer, the one after into registers
     if (blk + 1 < nblk) {
@@ -297,13 +319,12 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkFwdArgs g) {
       }
     }
     {
-      uint16_t* yt = yb + t0 * xrow + 16 * w + 4 * g4;
 #pragma unroll
       for (int ti = 0; ti < 4; ++ti) {
-        const int t = 16 * ti + c16;
-        if (t < nv) {
+        char* yt = reinterpret_cast<char*>(yb + (t0 + 16 * ti) * xrow);
+        if (16 * ti + c16 < nv) {
           const u16x4 v = {f2bf(yacc[ti][0]), f2bf(yacc[ti][1]), f2bf(yacc[ti][2]), f2bf(yacc[ti][3])};
-          *reinterpret_cast<u16x4*>(yt + t * xrow) = v;
+          *reinterpret_cast<u16x4*>(yt + yoff) = v;
         }
       }
     }
