@@ -73,6 +73,30 @@ def diag_scan(a, b, h0=None):
     return out, h
 
 
+def diag_scan_bwd(a, h, dh, h0=None, dh_last=None):
+    """Reverse-time adjoint of ``diag_scan`` for the loss
+    sum_t <dh[:, t], h[:, t]> + <dh_last, h[:, L-1]>  (h = forward outputs).
+
+    g_t = dl/dh_t (through every later step):
+        g_{L-1} = dh_{L-1} + dh_last,   g_t = dh_t + a_{t+1} g_{t+1}
+    then db_t = g_t, da_t = g_t h_{t-1} (h_{-1} = h0 or 0), dh0 = a_0 g_0.
+    Returns (da, db, dh0) in float64 (dh0 = dh_last when L = 0)."""
+    a, h, dh = _f(a), _f(h), _f(dh)
+    Bn, L, D = a.shape
+    g = np.zeros((Bn, D), F64) if dh_last is None else _f(dh_last).copy()
+    hm1 = np.zeros((Bn, D), F64) if h0 is None else _f(h0)
+    da = np.empty((Bn, L, D), F64)
+    db = np.empty((Bn, L, D), F64)
+    for t in range(L - 1, -1, -1):
+        if t < L - 1:
+            g = a[:, t + 1] * g
+        g = g + dh[:, t]
+        db[:, t] = g
+        da[:, t] = g * (h[:, t - 1] if t > 0 else hm1)
+    dh0 = a[:, 0] * g if L > 0 else g
+    return da, db, dh0
+
+
 # ---------------------------------------------------------------------------
 # Discretisation  [LX, Key Contributions 2-3: ZOH]
 # ---------------------------------------------------------------------------
