@@ -84,6 +84,22 @@ lr_status lr_diag_scan(lr_dtype io, int64_t B, int64_t L, int64_t D,
                        void* h, float* h_last, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Backward of lr_diag_scan for the loss
+ *     sum_t <dh[b,t,:], h[b,t,:]> + <dh_last[b,:], h[b,L-1,:]>
+ * (reverse-time adjoint of the recurrence above: g_{L-1} = dh_{L-1} + dh_last,
+ * g_t = a_{t+1} g_{t+1} + dh_t; then db_t = g_t, da_t = g_t h_{t-1} with
+ * h_{-1} = h0, and dh0 = a_0 g_0).  The forward already writes every state,
+ * so nothing is recomputed: h is the forward's output.
+ *   a, h, dh: [B, L, D] io    h0, dh_last: [B, D] fp32 or NULL (= 0)
+ *   da, db:   [B, L, D] io    dh0: [B, D] fp32 or NULL; dh0 = dh_last at L = 0
+ * Supported: as lr_diag_scan.
+ * ------------------------------------------------------------------------- */
+lr_status lr_diag_scan_bwd(lr_dtype io, int64_t B, int64_t L, int64_t D,
+                           const void* a, const void* h, const float* h0,
+                           const void* dh, const float* dh_last, void* da,
+                           void* db, float* dh0, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Mamba-1 selective scan with ZOH (or Euler) discretisation and a fused
  * readout ("lrnnx: A library for Linear RNNs", Key Contributions 3: fused
  * scan + output projection; the hidden state never reaches memory).

@@ -149,7 +149,8 @@ def _io_round(x32: np.ndarray, io: str) -> np.ndarray:
 def make(cfg_id: int, seed: int = SEED, **over) -> Inputs:
     """Generate the inputs of workload ``cfg_id``; keyword overrides change
     shapes (e.g. ``L=65``) or the I/O type (``io="f32"``) while keeping the
-    value distributions."""
+    value distributions.  ``grads=True`` adds a seeded upstream gradient of
+    the outputs (dh, dy or do, N(0, 1)) for backward cases."""
     p = dict(CONFIGS[cfg_id])
     p.update(over)
     io = p["io"]
@@ -163,6 +164,8 @@ def make(cfg_id: int, seed: int = SEED, **over) -> Inputs:
         B, L, D = p["B"], p["L"], p["D"]
         put("a", _Stream(seed, cfg_id, 0).uniform((B, L, D), 0.90, 0.999), io)
         put("b", _Stream(seed, cfg_id, 1).normal((B, L, D)), io)
+        if p.get("grads"):
+            put("dh", _Stream(seed, cfg_id, 2).normal((B, L, D)), io)
     elif kind == "selective":
         B, L, D, N = p["B"], p["L"], p["D"], p["N"]
         put("x", _Stream(seed, cfg_id, 0).normal((B, L, D)), io)
@@ -172,6 +175,8 @@ def make(cfg_id: int, seed: int = SEED, **over) -> Inputs:
         put("B", _Stream(seed, cfg_id, 3).normal((B, L, N)), io)
         put("C", _Stream(seed, cfg_id, 4).normal((B, L, N)), io)
         put("Dskip", _Stream(seed, cfg_id, 5).normal((D,)), "f32")
+        if p.get("grads"):
+            put("dy", _Stream(seed, cfg_id, 6).normal((B, L, D)), io)
     elif kind in ("ssd", "ssd_bwd"):
         B, L, H, P, G, N = p["B"], p["L"], p["H"], p["P"], p["G"], p["N"]
         put("x", _Stream(seed, cfg_id, 0).normal((B, L, H, P)), io)
@@ -190,6 +195,8 @@ def make(cfg_id: int, seed: int = SEED, **over) -> Inputs:
         put("k", _Stream(seed, cfg_id, 1).normal((B, L, H, K), 0.0, s), io)
         put("v", _Stream(seed, cfg_id, 2).normal((B, L, H, V)), io)
         put("g", _Stream(seed, cfg_id, 3).sigmoid_normal((B, L, H), 3.0, 1.0), io)
+        if p.get("grads"):
+            put("do", _Stream(seed, cfg_id, 4).normal((B, L, H, V)), io)
     else:
         raise ValueError(kind)
     return out

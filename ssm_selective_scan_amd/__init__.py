@@ -13,7 +13,7 @@ import torch
 from ._lib import (LR_BF16, LR_DISC_EULER, LR_DISC_ZOH, LR_F32, LrError,  # noqa: F401
                    check, lib)
 
-__all__ = ["lr_diag_scan", "lr_selective_scan", "lr_ssd_scan", "lr_ssd_scan_bwd",
+__all__ = ["lr_diag_scan", "lr_diag_scan_bwd", "lr_selective_scan", "lr_ssd_scan", "lr_ssd_scan_bwd",
            "lr_ssd_scan_bwd_workspace_bytes", "lr_gla_scan", "lr_version", "LrError"]
 
 _DISC = {"zoh": LR_DISC_ZOH, "euler": LR_DISC_EULER}
@@ -62,6 +62,19 @@ def lr_diag_scan(a, b, h0=None, h=None, h_last=None, want_last=False):
         _io(a), B, L, D, _ptr(a), _ptr(b), _f32(h0, "h0"), _ptr(h), _f32(h_last, "h_last"),
         _stream(a)))
     return h, h_last
+
+
+def lr_diag_scan_bwd(a, h, dh, h0=None, dh_last=None, want_dh0=False):
+    """Gradients (da, db, dh0) of sum <dh, h> + <dh_last, h_last> through
+    lr_diag_scan; h is the forward's output [B, L, D]."""
+    B, L, D = a.shape
+    da = torch.empty_like(a)
+    db = torch.empty_like(a)
+    dh0 = torch.empty(B, D, device=a.device, dtype=torch.float32) if want_dh0 else None
+    check("lr_diag_scan_bwd", lib().lr_diag_scan_bwd(
+        _io(a), B, L, D, _ptr(a), _ptr(h), _f32(h0, "h0"), _ptr(dh), _f32(dh_last, "dh_last"),
+        _ptr(da), _ptr(db), _f32(dh0, "dh0"), _stream(a)))
+    return da, db, dh0
 
 
 def lr_selective_scan(x, dt, A, Bm, Cm, Dskip=None, h0=None, disc="zoh", y=None, h_last=None,

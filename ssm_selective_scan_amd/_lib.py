@@ -24,6 +24,8 @@ SIGNATURES = {
     "lr_status_string": (C.c_char_p, [_int]),
     "lr_version": (C.c_char_p, []),
     "lr_diag_scan": (_int, [_int, _i64, _i64, _i64, _p, _p, _f32p, _p, _f32p, _p]),
+    "lr_diag_scan_bwd": (_int, [_int, _i64, _i64, _i64, _p, _p, _f32p, _p, _f32p, _p, _p, _f32p,
+                                _p]),
     "lr_selective_scan": (_int, [_int, _int, _i64, _i64, _i64, _i64, _p, _p, _f32p, _p, _p,
                                  _f32p, _f32p, _p, _f32p, _p]),
     "lr_ssd_scan": (_int, [_int, _int, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _p, _p,

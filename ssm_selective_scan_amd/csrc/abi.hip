@@ -17,6 +17,10 @@ template <typename T>
 hipError_t launch_diag_scan(const void* a, const void* b, const float* h0, void* h,
                             float* h_last, int64_t B, int64_t L, int64_t D, hipStream_t stream);
 template <typename T>
+hipError_t launch_diag_scan_bwd(const void* a, const void* h, const float* h0, const void* dh,
+                                const float* dh_last, void* da, void* db, float* dh0, int64_t B,
+                                int64_t L, int64_t D, hipStream_t stream);
+template <typename T>
 hipError_t launch_selective_scan(int disc, const void* x, const void* dt, const float* A,
                                  const void* Bm, const void* Cm, const float* Dskip,
                                  const float* h0, void* y, float* h_last, int64_t B, int64_t L,
@@ -135,6 +139,23 @@ lr_status lr_diag_scan(lr_dtype io, int64_t B, int64_t L, int64_t D, const void*
   auto s = static_cast<hipStream_t>(stream);
   return hip_status(io == LR_F32 ? lr::launch_diag_scan<float>(a, b, h0, h, h_last, B, L, D, s)
                                  : lr::launch_diag_scan<uint16_t>(a, b, h0, h, h_last, B, L, D, s));
+}
+
+lr_status lr_diag_scan_bwd(lr_dtype io, int64_t B, int64_t L, int64_t D, const void* a,
+                           const void* h, const float* h0, const void* dh, const float* dh_last,
+                           void* da, void* db, float* dh0, void* stream) {
+  if (!valid_io(io)) return LR_E_DTYPE;
+  if (B < 0 || L < 0 || D < 1) return LR_E_SHAPE;
+  if (!elems_ok({B, L, D})) return LR_E_OVERFLOW;
+  int64_t nwg = 1;
+  if (!mul_ok(nwg, B) || !mul_ok(nwg, (D + 15) / 16) || nwg > kMaxGrid) return LR_E_OVERFLOW;
+  if (B * L > 0 && any_null({a, h, dh, da, db})) return LR_E_NULLPTR;
+  if (!all_aligned({a, h, h0, dh, dh_last, da, db, dh0})) return LR_E_ALIGN;
+  if (B == 0) return LR_OK;
+  auto s = static_cast<hipStream_t>(stream);
+  return hip_status(io == LR_F32
+                        ? lr::launch_diag_scan_bwd<float>(a, h, h0, dh, dh_last, da, db, dh0, B, L, D, s)
+                        : lr::launch_diag_scan_bwd<uint16_t>(a, h, h0, dh, dh_last, da, db, dh0, B, L, D, s));
 }
 
 lr_status lr_selective_scan(lr_dtype io, lr_disc disc, int64_t B, int64_t L, int64_t D, int64_t N,

@@ -20,7 +20,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = _lib.header_symbols()
-    assert len(names) == 8, names
+    assert len(names) == len(_lib.SIGNATURES), names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -47,6 +47,22 @@ def test_diag_validation(L):
     assert diag(L, B=1 << 40, Lq=1 << 20, D=1 << 10) == OVF
     # empty batch: nothing to do, no device access
     assert diag(L, B=0, a=None, b=None, h=None) == OK
+
+
+def diag_bwd(L, io=0, B=1, Lq=8, D=4, a=P, h=P, h0=None, dh=P, dhl=None, da=P, db=P, dh0=None):
+    return L.lr_diag_scan_bwd(io, B, Lq, D, a, h, h0, dh, dhl, da, db, dh0, None)
+
+
+def test_diag_bwd_validation(L):
+    assert diag_bwd(L, io=5) == DTYPE
+    assert diag_bwd(L, D=0) == SHAPE
+    assert diag_bwd(L, Lq=-1) == SHAPE
+    for k in ("a", "h", "dh", "da", "db"):
+        assert diag_bwd(L, **{k: None}) == NULL, k
+    assert diag_bwd(L, dhl=MIS) == ALIGN
+    assert diag_bwd(L, dh0=MIS) == ALIGN
+    assert diag_bwd(L, B=1 << 40, Lq=1 << 20, D=1 << 10) == OVF
+    assert diag_bwd(L, B=0, a=None, h=None, dh=None, da=None, db=None) == OK
 
 
 def sel(L, io=1, disc=0, B=1, Lq=8, D=4, N=16, x=P, dt=P, A=P, Bm=P, Cm=P, y=P):
