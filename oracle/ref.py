@@ -281,3 +281,37 @@ def gla_scan(q, k, v, g, S0=None):
         S = g[:, t, :, None, None] * S + k[:, t, :, :, None] * v[:, t, :, None, :]
         o[:, t] = np.einsum("bhkv,bhk->bhv", S, q[:, t])
     return o, S
+
+
+def gla_scan_bwd(q, k, v, g, S0, do, dS_last=None):
+    """Gradients of loss = sum(do*o) + <dS_last, S_last> for ``gla_scan``.
+
+    Reverse-time adjoint written out directly: with G_t = dloss/dS_t (K x V),
+        G_{L-1} = dS_last + q_{L-1} do_{L-1}^T,   G_t = g_{t+1} G_{t+1} + q_t do_t^T,
+    the input gradients are
+        dq_t = S_t do_t,   dk_t = G_t v_t,   dv_t = G_t^T k_t,
+        dg_t = <G_t, S_{t-1}>_F,   dS0 = g_0 G_0.
+    The forward state history is kept for every (b, h) (no checkpointing).
+    Returns a dict of float64 arrays dq, dk, dv, dg, dS0."""
+    q, k, v, g, do = map(_f, (q, k, v, g, do))
+    Bn, L, H, K = q.shape
+    V = v.shape[3]
+    S_init = np.zeros((Bn, H, K, V), F64) if S0 is None else _f(S0)
+    hist = np.empty((L + 1, Bn, H, K, V), F64)
+    hist[0] = S_init
+    for t in range(L):
+        hist[t + 1] = (g[:, t, :, None, None] * hist[t]
+                       + k[:, t, :, :, None] * v[:, t, :, None, :])
+    dq = np.empty_like(q)
+    dk = np.empty_like(k)
+    dv = np.empty_like(v)
+    dg = np.empty_like(g)
+    Gt = np.zeros((Bn, H, K, V), F64) if dS_last is None else _f(dS_last).copy()
+    for t in range(L - 1, -1, -1):
+        Gt = Gt + q[:, t, :, :, None] * do[:, t, :, None, :]
+        dq[:, t] = np.einsum("bhkv,bhv->bhk", hist[t + 1], do[:, t])
+        dk[:, t] = np.einsum("bhkv,bhv->bhk", Gt, v[:, t])
+        dv[:, t] = np.einsum("bhkv,bhk->bhv", Gt, k[:, t])
+        dg[:, t] = np.einsum("bhkv,bhkv->bh", Gt, hist[t])
+        Gt = g[:, t, :, None, None] * Gt
+    return dict(dq=dq, dk=dk, dv=dv, dg=dg, dS0=Gt)
