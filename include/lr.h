@@ -186,13 +186,44 @@ lr_status lr_ssd_scan_bwd(lr_dtype io, lr_disc disc, int64_t B, int64_t L,
  *   q, k: [B, L, H, K] io    v, o: [B, L, H, V] io    g: [B, L, H] io, in (0, 1]
  *   S0, S_last: [B, H, K, V] fp32 or NULL
  *   chunk: any multiple of 64 (same meaning as in lr_ssd_scan).
+ *   seg:   0, or a multiple of 64: then ckpt[s] receives the state entering
+ *          token s*seg, TRANSPOSED: ckpt is [ceil(L/seg), B, H, V, K] fp32
+ *          (required iff seg > 0; consumed by lr_gla_scan_bwd).
  * No extra scaling of q is applied.
  * Supported: io = LR_BF16; K in {64, 128}; V % 64 == 0.
  * ------------------------------------------------------------------------- */
 lr_status lr_gla_scan(lr_dtype io, int64_t B, int64_t L, int64_t H, int64_t K,
-                      int64_t V, int64_t chunk, const void* q, const void* k,
-                      const void* v, const void* g, const float* S0, void* o,
-                      float* S_last, void* stream);
+                      int64_t V, int64_t chunk, int64_t seg, const void* q,
+                      const void* k, const void* v, const void* g,
+                      const float* S0, void* o, float* S_last, float* ckpt,
+                      void* stream);
+
+/* Workspace bytes needed by lr_gla_scan_bwd (0 on invalid sizes): fp32
+ * partial sums of dk, dq and of the log-gate gradient per 64 columns of v,
+ * and the adjoint state at segment boundaries. */
+size_t lr_gla_scan_bwd_workspace_bytes(int64_t B, int64_t L, int64_t H,
+                                       int64_t K, int64_t V, int64_t chunk,
+                                       int64_t seg);
+
+/* ---------------------------------------------------------------------------
+ * Backward of lr_gla_scan with segment checkpoint-and-recompute (same
+ * training path as lr_ssd_scan_bwd).  Gradients of
+ *     loss = sum(dout * o) + <dS_last, S_last>
+ * with respect to q, k, v, g and S0.
+ *   ckpt:  written by lr_gla_scan with the same seg.
+ *   dout:  [B, L, H, V] io      dS_last: [B, H, K, V] fp32 or NULL (= 0)
+ *   dq, dk: [B, L, H, K] io     dv: [B, L, H, V] io     dg: [B, L, H] io
+ *   dS0:   [B, H, K, V] fp32 or NULL
+ *   workspace: device memory of at least lr_gla_scan_bwd_workspace_bytes().
+ * Supported: as lr_gla_scan, with seg in {64, 128, 192, 256}.
+ * ------------------------------------------------------------------------- */
+lr_status lr_gla_scan_bwd(lr_dtype io, int64_t B, int64_t L, int64_t H,
+                          int64_t K, int64_t V, int64_t chunk, int64_t seg,
+                          const void* q, const void* k, const void* v,
+                          const void* g, const float* ckpt, const void* dout,
+                          const float* dS_last, void* dq, void* dk, void* dv,
+                          void* dg, float* dS0, void* workspace,
+                          size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -14,7 +14,8 @@ from ._lib import (LR_BF16, LR_DISC_EULER, LR_DISC_ZOH, LR_F32, LrError,  # noqa
                    check, lib)
 
 __all__ = ["lr_diag_scan", "lr_diag_scan_bwd", "lr_selective_scan", "lr_ssd_scan", "lr_ssd_scan_bwd",
-           "lr_ssd_scan_bwd_workspace_bytes", "lr_gla_scan", "lr_version", "LrError"]
+           "lr_ssd_scan_bwd_workspace_bytes", "lr_gla_scan", "lr_gla_scan_bwd",
+           "lr_gla_scan_bwd_workspace_bytes", "lr_version", "LrError"]
 
 _DISC = {"zoh": LR_DISC_ZOH, "euler": LR_DISC_EULER}
 
@@ -139,15 +140,43 @@ def lr_ssd_scan_bwd(x, dt, A, Bm, Cm, Dskip, h0, ckpt, dy, dh_last=None, disc="z
     return dict(dx=dx, ddt=ddt, dA=dA, dB=dB, dC=dC, dD=dD, dh0=dh0)
 
 
-def lr_gla_scan(q, k, v, g, S0=None, chunk=64, o=None, S_last=None, want_last=False):
-    """GLA; q, k: [B, L, H, K], v: [B, L, H, V], g: [B, L, H]."""
+def lr_gla_scan(q, k, v, g, S0=None, chunk=64, seg=0, o=None, S_last=None, ckpt=None,
+                want_last=False):
+    """GLA; q, k: [B, L, H, K], v: [B, L, H, V], g: [B, L, H].  With seg > 0
+    the segment checkpoints ([ceil(L/seg), B, H, V, K], the state transposed)
+    are returned as the third value."""
     B, L, H, K = q.shape
     V = v.shape[3]
     if o is None:
         o = torch.empty_like(v)
     if want_last and S_last is None:
         S_last = torch.empty(B, H, K, V, device=q.device, dtype=torch.float32)
+    if seg > 0 and ckpt is None:
+        ckpt = torch.empty((L + seg - 1) // seg, B, H, V, K, device=q.device, dtype=torch.float32)
     check("lr_gla_scan", lib().lr_gla_scan(
-        _io(q), B, L, H, K, V, chunk, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _f32(S0, "S0"),
-        _ptr(o), _f32(S_last, "S_last"), _stream(q)))
-    return o, S_last
+        _io(q), B, L, H, K, V, chunk, seg, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _f32(S0, "S0"),
+        _ptr(o), _f32(S_last, "S_last"), _f32(ckpt, "ckpt"), _stream(q)))
+    return (o, S_last, ckpt) if seg > 0 else (o, S_last)
+
+
+def lr_gla_scan_bwd_workspace_bytes(B, L, H, K, V, chunk, seg) -> int:
+    return int(lib().lr_gla_scan_bwd_workspace_bytes(B, L, H, K, V, chunk, seg))
+
+
+def lr_gla_scan_bwd(q, k, v, g, ckpt, dout, dS_last=None, chunk=64, seg=64, workspace=None,
+                    want_dS0=False):
+    """Gradients of sum(dout*o) + <dS_last, S_last> of lr_gla_scan.  Returns a
+    dict with dq, dk, dv, dg and dS0."""
+    B, L, H, K = q.shape
+    V = v.shape[3]
+    dev = q.device
+    dq, dk, dv, dg = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), torch.empty_like(g)
+    dS0 = torch.empty(B, H, K, V, device=dev, dtype=torch.float32) if want_dS0 else None
+    need = lr_gla_scan_bwd_workspace_bytes(B, L, H, K, V, chunk, seg)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), device=dev, dtype=torch.uint8)
+    check("lr_gla_scan_bwd", lib().lr_gla_scan_bwd(
+        _io(q), B, L, H, K, V, chunk, seg, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _f32(ckpt, "ckpt"),
+        _ptr(dout), _f32(dS_last, "dS_last"), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg),
+        _f32(dS0, "dS0"), _ptr(workspace), workspace.numel(), _stream(q)))
+    return dict(dq=dq, dk=dk, dv=dv, dg=dg, dS0=dS0)

@@ -30,8 +30,14 @@ hipError_t launch_ssd_fwd(int disc, const void* x, const void* dt, const float* 
                           float* h_last, float* ckpt, int64_t B, int64_t L, int64_t H, int64_t P,
                           int64_t G, int64_t N, int64_t seg, hipStream_t stream);
 hipError_t launch_gla_fwd(const void* q, const void* k, const void* v, const void* gate,
-                          const float* S0, void* o, float* S_last, int64_t B, int64_t L,
-                          int64_t H, int64_t K, int64_t V, hipStream_t stream);
+                          const float* S0, void* o, float* S_last, float* ckpt, int64_t B,
+                          int64_t L, int64_t H, int64_t K, int64_t V, int64_t seg,
+                          hipStream_t stream);
+size_t gla_bwd_workspace(int64_t B, int64_t L, int64_t H, int64_t K, int64_t V, int64_t seg);
+hipError_t launch_gla_bwd(const void* q, const void* k, const void* v, const void* g,
+                          const float* ckpt, const void* dout, const float* dS_last, void* dq,
+                          void* dk, void* dv, void* dg, float* dS0, void* ws, int64_t B, int64_t L,
+                          int64_t H, int64_t K, int64_t V, int64_t seg, hipStream_t stream);
 size_t ssd_bwd_workspace(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N,
                          int64_t seg);
 bool ssd_bwd_supported(int64_t P, int64_t N, int64_t seg);
@@ -232,22 +238,68 @@ lr_status lr_ssd_scan_bwd(lr_dtype io, lr_disc disc, int64_t B, int64_t L, int64
                                        static_cast<hipStream_t>(stream)));
 }
 
-lr_status lr_gla_scan(lr_dtype io, int64_t B, int64_t L, int64_t H, int64_t K, int64_t V,
-                      int64_t chunk, const void* q, const void* k, const void* v, const void* g,
-                      const float* S0, void* o, float* S_last, void* stream) {
+// Checks shared by the GLA forward and backward.
+static lr_status check_gla_sizes(int io, int64_t B, int64_t L, int64_t H, int64_t K, int64_t V,
+                          int64_t chunk, int64_t seg) {
   if (!valid_io(io)) return LR_E_DTYPE;
-  if (B < 0 || L < 0 || H < 1 || K < 1 || V < 1 || chunk < 1) return LR_E_SHAPE;
-  if (io != LR_BF16 || (K != 64 && K != 128) || V % 64 != 0 || chunk % 64 != 0)
+  if (B < 0 || L < 0 || H < 1 || K < 1 || V < 1 || chunk < 1 || seg < 0) return LR_E_SHAPE;
+  if (io != LR_BF16 || (K != 64 && K != 128) || V % 64 != 0 || chunk % 64 != 0 || seg % 64 != 0)
     return LR_E_UNSUPPORTED;
   if (!elems_ok({B, L, H, K}) || !elems_ok({B, L, H, V}) || !elems_ok({B, H, K, V}))
     return LR_E_OVERFLOW;
   int64_t nwg = 1;
   if (!mul_ok(nwg, B) || !mul_ok(nwg, H) || !mul_ok(nwg, V / 64) || nwg > kMaxGrid)
     return LR_E_OVERFLOW;
+  if (seg > 0) {
+    const int64_t nseg = (L + seg - 1) / seg;
+    if (!elems_ok({nseg, B, H, K, V})) return LR_E_OVERFLOW;
+    if (!mul_ok(nwg, nseg) || nwg > kMaxGrid) return LR_E_OVERFLOW;
+  }
+  return LR_OK;
+}
+
+lr_status lr_gla_scan(lr_dtype io, int64_t B, int64_t L, int64_t H, int64_t K, int64_t V,
+                      int64_t chunk, int64_t seg, const void* q, const void* k, const void* v,
+                      const void* g, const float* S0, void* o, float* S_last, float* ckpt,
+                      void* stream) {
+  const lr_status st = check_gla_sizes(io, B, L, H, K, V, chunk, seg);
+  if (st != LR_OK) return st;
   if (B * L > 0 && any_null({q, k, v, g, o})) return LR_E_NULLPTR;
-  if (!all_aligned({q, k, v, g, S0, o, S_last})) return LR_E_ALIGN;
+  if (B * L > 0 && seg > 0 && ckpt == nullptr) return LR_E_NULLPTR;
+  if (!all_aligned({q, k, v, g, S0, o, S_last, ckpt})) return LR_E_ALIGN;
   if (B == 0) return LR_OK;
-  return hip_status(lr::launch_gla_fwd(q, k, v, g, S0, o, S_last, B, L, H, K, V,
+  return hip_status(lr::launch_gla_fwd(q, k, v, g, S0, o, S_last, seg > 0 ? ckpt : nullptr, B, L,
+                                       H, K, V, seg, static_cast<hipStream_t>(stream)));
+}
+
+size_t lr_gla_scan_bwd_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t K, int64_t V,
+                                       int64_t chunk, int64_t seg) {
+  if (check_gla_sizes(LR_BF16, B, L, H, K, V, chunk, seg) != LR_OK || !lr::ssd_bwd_supported(64, K, seg))
+    return 0;
+  return lr::gla_bwd_workspace(B, L, H, K, V, seg);
+}
+
+lr_status lr_gla_scan_bwd(lr_dtype io, int64_t B, int64_t L, int64_t H, int64_t K, int64_t V,
+                          int64_t chunk, int64_t seg, const void* q, const void* k, const void* v,
+                          const void* g, const float* ckpt, const void* dout,
+                          const float* dS_last, void* dq, void* dk, void* dv, void* dg,
+                          float* dS0, void* workspace, size_t workspace_bytes, void* stream) {
+  const lr_status st = check_gla_sizes(io, B, L, H, K, V, chunk, seg);
+  if (st != LR_OK) return st;
+  if (seg < 1) return LR_E_SHAPE;
+  if (!lr::ssd_bwd_supported(64, K, seg)) return LR_E_UNSUPPORTED;
+  if (B * L > 0 && any_null({q, k, v, g, ckpt, dout, dq, dk, dv, dg})) return LR_E_NULLPTR;
+  if (!all_aligned({q, k, v, g, ckpt, dout, dS_last, dq, dk, dv, dg, dS0, workspace}))
+    return LR_E_ALIGN;
+  const size_t need = lr::gla_bwd_workspace(B, L, H, K, V, seg);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LR_E_WORKSPACE;
+  if (B * L == 0) {
+    if (dS0 == nullptr || B == 0) return LR_OK;
+    return hip_status(lr::launch_ssd_bwd_empty(nullptr, nullptr, dS0, dS_last, 0, B * H * K * V,
+                                               static_cast<hipStream_t>(stream)));
+  }
+  return hip_status(lr::launch_gla_bwd(q, k, v, g, ckpt, dout, dS_last, dq, dk, dv, dg, dS0,
+                                       workspace, B, L, H, K, V, seg,
                                        static_cast<hipStream_t>(stream)));
 }
 

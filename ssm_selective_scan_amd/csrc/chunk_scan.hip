@@ -388,8 +388,9 @@ hipError_t launch_ssd_fwd(int disc, const void* x, const void* dt, const float* 
 }
 
 hipError_t launch_gla_fwd(const void* q, const void* k, const void* v, const void* gate,
-                          const float* S0, void* o, float* S_last, int64_t B, int64_t L,
-                          int64_t H, int64_t K, int64_t V, hipStream_t stream) {
+                          const float* S0, void* o, float* S_last, float* ckpt, int64_t B,
+                          int64_t L, int64_t H, int64_t K, int64_t V, int64_t seg,
+                          hipStream_t stream) {
   ChunkFwdArgs a;
   a.x = static_cast<const uint16_t*>(v);
   a.gate = static_cast<const uint16_t*>(gate);
@@ -400,8 +401,8 @@ hipError_t launch_gla_fwd(const void* q, const void* k, const void* v, const voi
   a.h0 = S0;
   a.y = static_cast<uint16_t*>(o);
   a.h_last = S_last;
-  a.ckpt = nullptr;
-  a.B = B; a.L = L; a.H = H; a.P = V; a.G = H; a.seg = 1;
+  a.ckpt = seg > 0 ? ckpt : nullptr;   // [nseg][B][H][V][K]: the state transposed
+  a.B = B; a.L = L; a.H = H; a.P = V; a.G = H; a.seg = seg > 0 ? seg : 1;
   a.bc_row = H * K;
   a.st_p = 1; a.st_n = V;
   if (K == 128) return launch_chunk<kModeGla, 128>(a, stream);

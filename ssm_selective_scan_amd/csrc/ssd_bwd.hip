@@ -41,7 +41,11 @@ constexpr int kBQ = 64;          // tokens per block
 constexpr int kBP = 64;          // head dim P (one 64-wide slice)
 constexpr int kBLd = kBQ + 8;    // leading dim of 64-wide LDS tiles
 
-enum { kBwdZoh = 0, kBwdEuler = 1 };
+// Recurrence kinds: SSD with ZOH or Euler discretisation, and GLA, which is
+// the same recurrence with x <-> v, B <-> k, C <-> q, phi = 1 and the decay
+// given directly as the gate g (log-decay ln g).  A GLA head of V columns is
+// run as V / 64 "heads" of 64 columns that form one group sharing k and q.
+enum { kBwdZoh = 0, kBwdEuler = 1, kBwdGla = 2 };
 
 struct BwdArgs {
   const uint16_t* x; const uint16_t* dt; const float* A; const uint16_t* Bm; const uint16_t* Cm;
@@ -51,13 +55,45 @@ struct BwdArgs {
   float* gseg;                    // [nseg][B][H][P][N]: Gamma_loc, then Gamma_out
   float* lam;                     // [nseg][B][H]
   float* dApart; float* dDpart;   // [B][H][nseg]
+  float* dgpart;                  // GLA: [H][B][L] log-gate gradient per 64-column slice
+  uint16_t* dg;                   // GLA: [B][L][G] gate gradient
   int64_t B, L, H, G, N, seg, nseg;
 };
 
-// Per-token scalars of one block (lane = token): log2 cumulative decay,
-// phi, e, dt.  Masked tokens (t >= nv) get dt = 0: no decay, no input.
+// Gate (SSD dt, GLA g) of token t of head h in group grp.
+template <int MODE>
+__device__ __forceinline__ float gate_at(const BwdArgs& a, int64_t b, int64_t t, int64_t h,
+                                         int64_t grp) {
+  return MODE == kBwdGla ? bf2f(a.dt[(b * a.L + t) * a.G + grp]) : bf2f(a.dt[(b * a.L + t) * a.H + h]);
+}
+
+// Offset of state element idx = ((b H + h) P + p) N + n of the internal
+// [B][H][P][N] order in the caller's dh_last / dh0 layout: the same for SSD,
+// [B][G][N][V] (V = 64 H / G) for GLA.
+template <int MODE>
+__device__ __forceinline__ int64_t state_off(const BwdArgs& a, int64_t idx) {
+  if (MODE != kBwdGla) return idx;
+  const int64_t PN = static_cast<int64_t>(64) * a.N;
+  const int64_t bh = idx / PN, pn = idx % PN;
+  const int64_t p = pn / a.N, n = pn % a.N;
+  const int64_t b = bh / a.H, hh = bh % a.H;
+  const int64_t hpg = a.H / a.G, grp = hh / hpg, vs = hh % hpg;
+  return ((b * a.G + grp) * a.N + n) * (64 * hpg) + 64 * vs + p;
+}
+
+// Per-token scalars of one token: log2 decay, phi, e.  Masked tokens
+// (ok == false) get no decay and no input.  For SSD the gate is dt; for GLA
+// it is g itself.
 template <int DISC>
-__device__ __forceinline__ void block_scalars(float dtv, float Ah, float& l2, float& ph, float& ek) {
+__device__ __forceinline__ void block_scalars(float gate, bool ok, float Ah, float& l2, float& ph,
+                                              float& ek) {
+  if (DISC == kBwdGla) {
+    ek = ok ? gate : 1.f;
+    l2 = fast_log2(ek);
+    ph = ok ? 1.f : 0.f;
+    return;
+  }
+  const float dtv = ok ? gate : 0.f;
   const float lam = dtv * Ah;
   l2 = lam * kLog2e;
   ek = fast_exp2(l2);
@@ -98,7 +134,7 @@ struct GlocLds {
   float E[kBQ];
 };
 
-template <int NS>
+template <int MODE, int NS>
 __global__ __launch_bounds__(256) void ssd_bwd_gloc_kernel(BwdArgs a) {
   constexpr int NT = NS / 16;
   __shared__ GlocLds<NS> sm;
@@ -109,7 +145,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_gloc_kernel(BwdArgs a) {
   const int64_t bh = wid / a.nseg;
   const int64_t h = bh % a.H, b = bh / a.H;
   const int64_t grp = h / (a.H / a.G);
-  const float Ah = a.A[h];
+  const float Ah = MODE == kBwdGla ? 0.f : a.A[h];
   const int64_t ts0 = sg * a.seg;
   const int64_t tse = (ts0 + a.seg < a.L) ? ts0 + a.seg : a.L;
   const int nb = static_cast<int>((tse - ts0 + kBQ - 1) / kBQ);
@@ -123,8 +159,10 @@ __global__ __launch_bounds__(256) void ssd_bwd_gloc_kernel(BwdArgs a) {
     const int64_t t0 = ts0 + static_cast<int64_t>(j) * kBQ;
     const int nv = static_cast<int>((tse - t0) < kBQ ? (tse - t0) : kBQ);
     if (w == 0) {
-      const float dtv = lane < nv ? bf2f(a.dt[(b * a.L + t0 + lane) * a.H + h]) : 0.f;
-      const float c = wave_incl_sum(dtv * Ah * kLog2e);
+      const bool ok = lane < nv;
+      float l2, ph, ek;
+      block_scalars<MODE>(ok ? gate_at<MODE>(a, b, t0 + lane, h, grp) : 0.f, ok, Ah, l2, ph, ek);
+      const float c = wave_incl_sum(l2);
       sm.cum[lane] = c;
       sm.E[lane] = fast_exp2(c);
     }
@@ -176,19 +214,21 @@ __global__ __launch_bounds__(256) void ssd_bwd_gloc_kernel(BwdArgs a) {
 // gcombine: one thread per state element; backwards over segments replace
 // Gamma_loc(s) by Gamma_out(s) = adjoint of the state at the end of segment s.
 // ---------------------------------------------------------------------------
+template <int MODE>
 __global__ __launch_bounds__(256) void ssd_bwd_gcombine_kernel(BwdArgs a, int64_t PN) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   const int64_t BH = a.B * a.H;
   if (idx >= BH * PN) return;
   const int64_t bh = idx / PN;
-  float carry = a.dh_last != nullptr ? a.dh_last[idx] : 0.f;
+  const int64_t so = state_off<MODE>(a, idx);
+  float carry = a.dh_last != nullptr ? a.dh_last[so] : 0.f;
   for (int64_t s = a.nseg - 1; s >= 0; --s) {
     float* gp = a.gseg + s * BH * PN + idx;
     const float gl = *gp;
     *gp = carry;
     carry = fmaf(a.lam[s * BH + bh], carry, gl);
   }
-  if (a.dh0 != nullptr) a.dh0[idx] = carry;
+  if (a.dh0 != nullptr) a.dh0[so] = carry;
 }
 
 // ---------------------------------------------------------------------------
@@ -232,7 +272,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
   const int64_t bh = wid / a.nseg;
   const int64_t h = bh % a.H, b = bh / a.H;
   const int64_t grp = h / (a.H / a.G);
-  const float Ah = a.A[h];
+  const float Ah = DISC == kBwdGla ? 0.f : a.A[h];
   const float Dh = a.Dskip != nullptr ? a.Dskip[h] : 0.f;
   const int64_t ts0 = sg * a.seg;
   const int64_t tse = (ts0 + a.seg < a.L) ? ts0 + a.seg : a.L;
@@ -261,9 +301,9 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
       const int64_t t0 = ts0 + static_cast<int64_t>(j) * kBQ;
       const int nv = static_cast<int>((tse - t0) < kBQ ? (tse - t0) : kBQ);
       if (w == 0) {
-        const float dtv = lane < nv ? bf2f(a.dt[(b * a.L + t0 + lane) * a.H + h]) : 0.f;
+        const bool ok = lane < nv;
         float l2, ph, ek;
-        block_scalars<DISC>(dtv, Ah, l2, ph, ek);
+        block_scalars<DISC>(ok ? gate_at<DISC>(a, b, t0 + lane, h, grp) : 0.f, ok, Ah, l2, ph, ek);
         sm.cum[lane] = wave_incl_sum(l2);
         sm.phi[lane] = lane < nv ? ph : 0.f;
       }
@@ -327,9 +367,10 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
 
     // ---- stage the block
     if (w == 0) {
-      const float dtv = lane < nv ? bf2f(a.dt[(b * a.L + t0 + lane) * a.H + h]) : 0.f;
+      const bool ok = lane < nv;
+      const float dtv = ok ? gate_at<DISC>(a, b, t0 + lane, h, grp) : 0.f;
       float l2, ph, ek;
-      block_scalars<DISC>(dtv, Ah, l2, ph, ek);
+      block_scalars<DISC>(dtv, ok, Ah, l2, ph, ek);
       const float c = wave_incl_sum(l2);
       const float cend = __shfl(c, 63);
       sm.cum[lane] = c;
@@ -348,7 +389,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
         vc = *reinterpret_cast<const u16x8*>(a.Cm + off);
         vb = *reinterpret_cast<const u16x8*>(a.Bm + off);
         float l2, ek;
-        block_scalars<DISC>(bf2f(a.dt[(b * a.L + t0 + r) * a.H + h]), Ah, l2, ph, ek);
+        block_scalars<DISC>(gate_at<DISC>(a, b, t0 + r, h, grp), true, Ah, l2, ph, ek);
       }
       *reinterpret_cast<u16x8*>(sm.Cs + r * kLdN + 8 * c) = vc;
       *reinterpret_cast<u16x8*>(sm.Bs + r * kLdN + 8 * c) = vb;
@@ -592,8 +633,11 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
       const float total = __shfl(incl, 63);
       const float dlam = total - incl + dcum;
       const float dtv = sm.dtv[k], ek = sm.ek[k], ph = sm.phi[k];
-      float ddt, dAk;
-      if (DISC == kBwdEuler) {
+      float ddt = 0.f, dAk = 0.f;
+      if (DISC == kBwdGla) {
+        // phi is constant: the log-gate gradient goes out per 64-column slice
+        if (k < nv) a.dgpart[(h * a.B + b) * a.L + t0 + k] = dlam;
+      } else if (DISC == kBwdEuler) {
         ddt = dlam * Ah + dph;
         dAk = dlam * dtv;
       } else {
@@ -604,8 +648,10 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
         ddt = fmaf(dlam, Ah, dph * ek);
         dAk = fmaf(dlam, dtv, dph * dphidA);
       }
-      if (k < nv) a.ddt[(b * a.L + t0 + k) * a.H + h] = f2bf(ddt);
-      dA_acc += wave_sum(k < nv ? dAk : 0.f);
+      if (DISC != kBwdGla) {
+        if (k < nv) a.ddt[(b * a.L + t0 + k) * a.H + h] = f2bf(ddt);
+        dA_acc += wave_sum(k < nv ? dAk : 0.f);
+      }
     }
     __syncthreads();
   }
@@ -641,7 +687,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_reduce_kernel(BwdArgs a) {
     *reinterpret_cast<u16x4*>(a.dBm + o) = vb;
     *reinterpret_cast<u16x4*>(a.dCm + o) = vc;
   }
-  if (blockIdx.x == 0) {
+  if (blockIdx.x == 0 && a.dA != nullptr) {
     for (int64_t hh = threadIdx.x; hh < a.H; hh += 256) {
       float sa = 0.f, sd = 0.f;
       for (int64_t bb = 0; bb < a.B; ++bb)
@@ -655,13 +701,24 @@ __global__ __launch_bounds__(256) void ssd_bwd_reduce_kernel(BwdArgs a) {
   }
 }
 
+// GLA: dg = (sum of the per-slice log-gate gradients) / g, fixed order.
+__global__ __launch_bounds__(256) void gla_bwd_dg_kernel(BwdArgs a) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;   // (b L + t) G + grp
+  if (idx >= a.B * a.L * a.G) return;
+  const int64_t grp = idx % a.G, bt = idx / a.G;
+  const int64_t hpg = a.H / a.G;
+  float s = 0.f;
+  for (int64_t hh = grp * hpg; hh < (grp + 1) * hpg; ++hh) s += a.dgpart[hh * a.B * a.L + bt];
+  a.dg[idx] = f2bf(s / bf2f(a.dt[idx]));
+}
+
 // Empty input (B * L == 0): dA = dD = 0 and dh0 = dh_last (or 0).
 __global__ __launch_bounds__(256) void ssd_bwd_empty_kernel(float* dA, float* dD, float* dh0,
                                                             const float* dh_last, int64_t H,
                                                             int64_t nstate) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i < H) {
-    dA[i] = 0.f;
+    if (dA != nullptr) dA[i] = 0.f;
     if (dD != nullptr) dD[i] = 0.f;
   }
   if (dh0 != nullptr && i < nstate) dh0[i] = dh_last != nullptr ? dh_last[i] : 0.f;
@@ -679,19 +736,21 @@ hipError_t launch_ssd_bwd_empty(float* dA, float* dD, float* dh0, const float* d
 static inline int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
 
 struct WsLayout {
-  int64_t dB, dC, g, lam, dA, dD, total;
+  int64_t dB, dC, g, lam, dA, dD, dg, total;
 };
 
-static WsLayout ws_layout(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t seg) {
+// H: heads of 64 columns (for GLA, H * V / 64)
+static WsLayout ws_layout(int64_t B, int64_t L, int64_t H, int64_t N, int64_t seg, bool gla) {
   const int64_t nseg = (L + seg - 1) / seg;
   WsLayout w;
   int64_t o = 0;
   w.dB = o; o = align256(o + H * B * L * N * 4);
   w.dC = o; o = align256(o + H * B * L * N * 4);
-  w.g = o; o = align256(o + nseg * B * H * P * N * 4);
+  w.g = o; o = align256(o + nseg * B * H * kBP * N * 4);
   w.lam = o; o = align256(o + nseg * B * H * 4);
   w.dA = o; o = align256(o + B * H * nseg * 4);
   w.dD = o; o = align256(o + B * H * nseg * 4);
+  w.dg = o; o = align256(o + (gla ? H * B * L * 4 : 0));
   w.total = o;
   return w;
 }
@@ -700,18 +759,54 @@ size_t ssd_bwd_workspace(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G, 
                          int64_t seg) {
   (void)G;
   if (P != kBP || seg > 256 || B * L == 0) return 0;
-  return static_cast<size_t>(ws_layout(B, L, H, P, N, seg).total);
+  return static_cast<size_t>(ws_layout(B, L, H, N, seg, false).total);
+}
+
+size_t gla_bwd_workspace(int64_t B, int64_t L, int64_t H, int64_t K, int64_t V, int64_t seg) {
+  if (V % kBP != 0 || seg > 256 || B * L == 0) return 0;
+  return static_cast<size_t>(ws_layout(B, L, H * (V / kBP), K, seg, true).total);
 }
 
 bool ssd_bwd_supported(int64_t P, int64_t N, int64_t seg) {
   return P == kBP && (N == 64 || N == 128) && seg >= 64 && seg <= 256 && seg % 64 == 0;
 }
 
-template <int DISC, int NS>
+template <int MODE, int NS>
 static void launch_main(const BwdArgs& a, int64_t nwg, int nbs, hipStream_t s) {
-  if (nbs == 1) hipLaunchKernelGGL((ssd_bwd_main_kernel<DISC, NS, 1>), dim3(nwg), dim3(256), 0, s, a);
-  else if (nbs == 2) hipLaunchKernelGGL((ssd_bwd_main_kernel<DISC, NS, 2>), dim3(nwg), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((ssd_bwd_main_kernel<DISC, NS, 4>), dim3(nwg), dim3(256), 0, s, a);
+  if (nbs == 1) hipLaunchKernelGGL((ssd_bwd_main_kernel<MODE, NS, 1>), dim3(nwg), dim3(256), 0, s, a);
+  else if (nbs == 2) hipLaunchKernelGGL((ssd_bwd_main_kernel<MODE, NS, 2>), dim3(nwg), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((ssd_bwd_main_kernel<MODE, NS, 4>), dim3(nwg), dim3(256), 0, s, a);
+}
+
+// The four launches (plus the gate reduction for GLA) on filled-in args.
+template <int MODE>
+static hipError_t launch_bwd(BwdArgs a, void* ws, hipStream_t stream) {
+  const WsLayout lay = ws_layout(a.B, a.L, a.H, a.N, a.seg, MODE == kBwdGla);
+  char* base = static_cast<char*>(ws);
+  a.dBpart = reinterpret_cast<float*>(base + lay.dB);
+  a.dCpart = reinterpret_cast<float*>(base + lay.dC);
+  a.gseg = reinterpret_cast<float*>(base + lay.g);
+  a.lam = reinterpret_cast<float*>(base + lay.lam);
+  a.dApart = reinterpret_cast<float*>(base + lay.dA);
+  a.dDpart = reinterpret_cast<float*>(base + lay.dD);
+  a.dgpart = reinterpret_cast<float*>(base + lay.dg);
+  a.nseg = (a.L + a.seg - 1) / a.seg;
+  const int64_t nwg = a.B * a.H * a.nseg;
+  if (a.N == 128) hipLaunchKernelGGL((ssd_bwd_gloc_kernel<MODE, 128>), dim3(nwg), dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL((ssd_bwd_gloc_kernel<MODE, 64>), dim3(nwg), dim3(256), 0, stream, a);
+  const int64_t PN = kBP * a.N;
+  hipLaunchKernelGGL(ssd_bwd_gcombine_kernel<MODE>, dim3((a.B * a.H * PN + 255) / 256), dim3(256), 0,
+                     stream, a, PN);
+  const int nbs = static_cast<int>(a.seg / kBQ);
+  if (a.N == 128) launch_main<MODE, 128>(a, nwg, nbs, stream);
+  else launch_main<MODE, 64>(a, nwg, nbs, stream);
+  const int64_t red = (a.B * a.L * a.G * (a.N / 4) + 255) / 256;
+  hipLaunchKernelGGL(ssd_bwd_reduce_kernel, dim3(red > 0 ? red : 1), dim3(256), 0, stream, a);
+  if (MODE == kBwdGla) {
+    const int64_t nd = (a.B * a.L * a.G + 255) / 256;
+    hipLaunchKernelGGL(gla_bwd_dg_kernel, dim3(nd), dim3(256), 0, stream, a);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_ssd_bwd(int disc, const void* x, const void* dt, const float* A, const void* Bm,
@@ -720,40 +815,32 @@ hipError_t launch_ssd_bwd(int disc, const void* x, const void* dt, const float* 
                           void* dCm, float* dD, float* dh0, void* ws, int64_t B, int64_t L,
                           int64_t H, int64_t P, int64_t G, int64_t N, int64_t seg,
                           hipStream_t stream) {
+  (void)P;
   if (B * L == 0) return hipSuccess;
-  const WsLayout lay = ws_layout(B, L, H, P, N, seg);
-  char* base = static_cast<char*>(ws);
-  BwdArgs a;
+  BwdArgs a = {};
   a.x = static_cast<const uint16_t*>(x); a.dt = static_cast<const uint16_t*>(dt); a.A = A;
   a.Bm = static_cast<const uint16_t*>(Bm); a.Cm = static_cast<const uint16_t*>(Cm);
   a.Dskip = Dskip; a.ckpt = ckpt; a.dy = static_cast<const uint16_t*>(dy); a.dh_last = dh_last;
   a.dx = static_cast<uint16_t*>(dx); a.ddt = static_cast<uint16_t*>(ddt); a.dA = dA;
   a.dBm = static_cast<uint16_t*>(dBm); a.dCm = static_cast<uint16_t*>(dCm); a.dD = dD; a.dh0 = dh0;
-  a.dBpart = reinterpret_cast<float*>(base + lay.dB);
-  a.dCpart = reinterpret_cast<float*>(base + lay.dC);
-  a.gseg = reinterpret_cast<float*>(base + lay.g);
-  a.lam = reinterpret_cast<float*>(base + lay.lam);
-  a.dApart = reinterpret_cast<float*>(base + lay.dA);
-  a.dDpart = reinterpret_cast<float*>(base + lay.dD);
-  a.B = B; a.L = L; a.H = H; a.G = G; a.N = N; a.seg = seg; a.nseg = (L + seg - 1) / seg;
+  a.B = B; a.L = L; a.H = H; a.G = G; a.N = N; a.seg = seg;
+  return disc == kBwdEuler ? launch_bwd<kBwdEuler>(a, ws, stream) : launch_bwd<kBwdZoh>(a, ws, stream);
+}
 
-  const int64_t nwg = B * H * a.nseg;
-  if (N == 128) hipLaunchKernelGGL(ssd_bwd_gloc_kernel<128>, dim3(nwg), dim3(256), 0, stream, a);
-  else hipLaunchKernelGGL(ssd_bwd_gloc_kernel<64>, dim3(nwg), dim3(256), 0, stream, a);
-  const int64_t PN = P * N;
-  hipLaunchKernelGGL(ssd_bwd_gcombine_kernel, dim3((B * H * PN + 255) / 256), dim3(256), 0, stream,
-                     a, PN);
-  const int nbs = static_cast<int>(seg / kBQ);
-  if (disc == kBwdEuler) {
-    if (N == 128) launch_main<kBwdEuler, 128>(a, nwg, nbs, stream);
-    else launch_main<kBwdEuler, 64>(a, nwg, nbs, stream);
-  } else {
-    if (N == 128) launch_main<kBwdZoh, 128>(a, nwg, nbs, stream);
-    else launch_main<kBwdZoh, 64>(a, nwg, nbs, stream);
-  }
-  const int64_t red = (B * L * G * (N / 4) + 255) / 256;
-  hipLaunchKernelGGL(ssd_bwd_reduce_kernel, dim3(red > 0 ? red : 1), dim3(256), 0, stream, a);
-  return hipGetLastError();
+hipError_t launch_gla_bwd(const void* q, const void* k, const void* v, const void* g,
+                          const float* ckpt, const void* dout, const float* dS_last, void* dq,
+                          void* dk, void* dv, void* dg, float* dS0, void* ws, int64_t B, int64_t L,
+                          int64_t H, int64_t K, int64_t V, int64_t seg, hipStream_t stream) {
+  if (B * L == 0) return hipSuccess;
+  BwdArgs a = {};
+  a.x = static_cast<const uint16_t*>(v); a.dt = static_cast<const uint16_t*>(g); a.A = nullptr;
+  a.Bm = static_cast<const uint16_t*>(k); a.Cm = static_cast<const uint16_t*>(q);
+  a.Dskip = nullptr; a.ckpt = ckpt; a.dy = static_cast<const uint16_t*>(dout); a.dh_last = dS_last;
+  a.dx = static_cast<uint16_t*>(dv); a.ddt = nullptr; a.dA = nullptr;
+  a.dBm = static_cast<uint16_t*>(dk); a.dCm = static_cast<uint16_t*>(dq); a.dD = nullptr; a.dh0 = dS0;
+  a.dg = static_cast<uint16_t*>(dg);
+  a.B = B; a.L = L; a.H = H * (V / kBP); a.G = H; a.N = K; a.seg = seg;
+  return launch_bwd<kBwdGla>(a, ws, stream);
 }
 
 }  // namespace lr

@@ -113,11 +113,40 @@ def test_ssd_bwd_validation(L):
 
 
 def test_gla_validation(L):
-    def gla(io=1, K=128, V=128, chunk=64, q=P, g=P):
-        return L.lr_gla_scan(io, 1, 64, 2, K, V, chunk, q, P, P, g, None, P, None, None)
+    def gla(io=1, K=128, V=128, chunk=64, seg=0, q=P, g=P, ck=None):
+        return L.lr_gla_scan(io, 1, 64, 2, K, V, chunk, seg, q, P, P, g, None, P, None, ck, None)
     assert gla(io=3) == DTYPE
     assert gla(K=32) == UNSUP
     assert gla(V=96) == UNSUP
     assert gla(chunk=32) == UNSUP
+    assert gla(seg=32, ck=P) == UNSUP
+    assert gla(seg=-64) == SHAPE
     assert gla(q=None) == NULL
+    assert gla(seg=64) == NULL          # checkpoints requested without a buffer
     assert gla(g=MIS) == ALIGN
+    assert gla(seg=64, ck=MIS) == ALIGN
+
+
+def test_gla_bwd_validation(L):
+    ws = L.lr_gla_scan_bwd_workspace_bytes(1, 64, 2, 128, 128, 64, 64)
+    assert ws > 0
+    assert L.lr_gla_scan_bwd_workspace_bytes(1, 64, 2, 128, 128, 64, 512) == 0
+    #       io  B  L   H  K    V    chunk seg q  k  v  g  ckpt dout dSl  dq dk dv dg dS0
+    args = [1, 1, 64, 2, 128, 128, 64, 64, P, P, P, P, P, P, None, P, P, P, P, None]
+    bad = list(args)
+    bad[0] = 7
+    assert L.lr_gla_scan_bwd(*bad, P, ws, None) == DTYPE
+    bad = list(args)
+    bad[7] = 0      # seg = 0: no checkpoints to recompute from
+    assert L.lr_gla_scan_bwd(*bad, P, ws, None) == SHAPE
+    bad = list(args)
+    bad[7] = 320    # seg beyond the compiled set
+    assert L.lr_gla_scan_bwd(*bad, P, ws, None) == UNSUP
+    bad = list(args)
+    bad[12] = None  # ckpt
+    assert L.lr_gla_scan_bwd(*bad, P, ws, None) == NULL
+    bad = list(args)
+    bad[18] = MIS   # dg
+    assert L.lr_gla_scan_bwd(*bad, P, ws, None) == ALIGN
+    assert L.lr_gla_scan_bwd(*args, P, ws - 256, None) == WS
+    assert L.lr_gla_scan_bwd(*args, None, ws, None) == WS
