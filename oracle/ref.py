@@ -162,6 +162,51 @@ def selective_scan(x, dt, A, Bm, Cm, Dskip=None, h0=None, disc="zoh"):
     return y, h
 
 
+def selective_scan_bwd(x, dt, A, Bm, Cm, Dskip, h0, dy, dh_last=None, disc="zoh"):
+    """Gradients of loss = sum(dy*y) + <dh_last, h_last> for ``selective_scan``.
+
+    Reverse-time adjoint written out directly: with G_t = dloss/dh_t
+    ([B, D, N]),
+        G_{L-1} = dh_last + dy_{L-1} C_{L-1},   G_t = e_{t+1} G_{t+1} + dy_t C_t,
+    the input gradients are
+        dx_t[d] = sum_n G phi B_t[n] + Dskip[d] dy_t[d],
+        dB_t[n] = sum_d G phi x_t[d],     dC_t[n] = sum_d h_t dy_t[d],
+        dphi = G B_t[n] x_t[d],           de = G h_{t-1},
+        dD[d]  = sum_{b,t} dy x,          dh0 = e_0 G_0,
+    and dt, A follow by the chain rule through (e, phi).  The full forward
+    state history is kept.  Returns a dict of float64 arrays."""
+    x, dt, A, Bm, Cm, dy = map(_f, (x, dt, A, Bm, Cm, dy))
+    Bn, L, D = x.shape
+    N = A.shape[1]
+    Dv = np.zeros(D, F64) if Dskip is None else _f(Dskip)
+    hist = np.empty((L + 1, Bn, D, N), F64)
+    hist[0] = np.zeros((Bn, D, N), F64) if h0 is None else _f(h0)
+    for t in range(L):
+        e, phi = discretize(dt[:, t, :, None], A[None], disc)
+        hist[t + 1] = e * hist[t] + phi * Bm[:, t, None, :] * x[:, t, :, None]
+    dx = np.empty_like(x)
+    ddt = np.empty_like(dt)
+    dB = np.empty_like(Bm)
+    dC = np.empty_like(Cm)
+    dA = np.zeros((D, N), F64)
+    Gt = np.zeros((Bn, D, N), F64) if dh_last is None else _f(dh_last).copy()
+    for t in range(L - 1, -1, -1):
+        e, phi = discretize(dt[:, t, :, None], A[None], disc)
+        Gt = Gt + dy[:, t, :, None] * Cm[:, t, None, :]
+        gphi = Gt * phi
+        dx[:, t] = np.einsum("bdn,bn->bd", gphi, Bm[:, t]) + Dv * dy[:, t]
+        dB[:, t] = np.einsum("bdn,bd->bn", gphi, x[:, t])
+        dC[:, t] = np.einsum("bdn,bd->bn", hist[t + 1], dy[:, t])
+        dphi = Gt * Bm[:, t, None, :] * x[:, t, :, None]
+        de = Gt * hist[t]
+        de_ddt, de_dA, dphi_ddt, dphi_dA = discretize_grads(dt[:, t, :, None], A[None], e, phi, disc)
+        ddt[:, t] = (de * de_ddt + dphi * dphi_ddt).sum(axis=2)
+        dA += (de * de_dA + dphi * dphi_dA).sum(axis=0)
+        Gt = e * Gt
+    dD = np.einsum("bld,bld->d", dy, x)
+    return dict(dx=dx, ddt=ddt, dA=dA, dB=dB, dC=dC, dD=dD, dh0=Gt)
+
+
 # ---------------------------------------------------------------------------
 # Mamba-2 head-wise SSD scan  [MR, ssd_scan: state [B, H, Dh, N]]
 # ---------------------------------------------------------------------------
