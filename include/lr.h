@@ -110,14 +110,45 @@ lr_status lr_diag_scan_bwd(lr_dtype io, int64_t B, int64_t L, int64_t D,
  *   A:      [D, N] fp32      Dskip:  [D] fp32 or NULL (treated as 0)
  *   h0:     [B, D, N] fp32 or NULL    h_last: [B, D, N] fp32 or NULL
  * dt is the step itself (> 0 expected; no bias or softplus is applied).
+ *   seg:    0, or a multiple of 32: then ckpt[s] receives the state entering
+ *           token s*seg (ckpt[0] = h0 or 0); ckpt: [ceil(L/seg), B, D, N]
+ *           fp32, required iff seg > 0 (consumed by lr_selective_scan_bwd).
  * Supported: 1 <= N <= 64, any D >= 1.
  * ------------------------------------------------------------------------- */
 lr_status lr_selective_scan(lr_dtype io, lr_disc disc, int64_t B, int64_t L,
-                            int64_t D, int64_t N, const void* x,
+                            int64_t D, int64_t N, int64_t seg, const void* x,
                             const void* dt, const float* A, const void* Bm,
                             const void* Cm, const float* Dskip,
                             const float* h0, void* y, float* h_last,
-                            void* stream);
+                            float* ckpt, void* stream);
+
+/* Workspace bytes needed by lr_selective_scan_bwd (0 on invalid or
+ * unsupported sizes): fp32 partial sums of dB and dC per 64-channel tile and
+ * of dA and dD per batch row. */
+size_t lr_selective_scan_bwd_workspace_bytes(int64_t B, int64_t L, int64_t D,
+                                             int64_t N, int64_t seg);
+
+/* ---------------------------------------------------------------------------
+ * Backward of lr_selective_scan with segment checkpoint-and-recompute
+ * ("mlx-recurrence" post: segment checkpoints in the forward, recompute in
+ * the backward).  Gradients of  loss = sum(dy * y) + <dh_last, h_last>  with
+ * respect to x, dt, A, Bm, Cm, Dskip and h0.
+ *   ckpt:   the checkpoints written by lr_selective_scan with the same seg.
+ *   dy:     [B, L, D] io        dh_last: [B, D, N] fp32 or NULL (= 0)
+ *   dx, ddt: [B, L, D] io       dBm, dCm: [B, L, N] io
+ *   dA: [D, N] fp32    dD: [D] fp32 or NULL    dh0: [B, D, N] fp32 or NULL
+ *   workspace: device memory of at least lr_selective_scan_bwd_workspace_bytes().
+ * Supported: 1 <= N <= 16; seg a multiple of 32 with 32 <= seg <= 256.
+ * ------------------------------------------------------------------------- */
+lr_status lr_selective_scan_bwd(lr_dtype io, lr_disc disc, int64_t B,
+                                int64_t L, int64_t D, int64_t N, int64_t seg,
+                                const void* x, const void* dt, const float* A,
+                                const void* Bm, const void* Cm,
+                                const float* Dskip, const float* ckpt,
+                                const void* dy, const float* dh_last, void* dx,
+                                void* ddt, float* dA, void* dBm, void* dCm,
+                                float* dD, float* dh0, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Mamba-2 head-wise SSD scan ("mlx-recurrence" post, ssd_scan, state

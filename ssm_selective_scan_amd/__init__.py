@@ -13,7 +13,8 @@ import torch
 from ._lib import (LR_BF16, LR_DISC_EULER, LR_DISC_ZOH, LR_F32, LrError,  # noqa: F401
                    check, lib)
 
-__all__ = ["lr_diag_scan", "lr_diag_scan_bwd", "lr_selective_scan", "lr_ssd_scan", "lr_ssd_scan_bwd",
+__all__ = ["lr_diag_scan", "lr_diag_scan_bwd", "lr_selective_scan", "lr_selective_scan_bwd",
+           "lr_selective_scan_bwd_workspace_bytes", "lr_ssd_scan", "lr_ssd_scan_bwd",
            "lr_ssd_scan_bwd_workspace_bytes", "lr_gla_scan", "lr_gla_scan_bwd",
            "lr_gla_scan_bwd_workspace_bytes", "lr_version", "LrError"]
 
@@ -78,20 +79,51 @@ def lr_diag_scan_bwd(a, h, dh, h0=None, dh_last=None, want_dh0=False):
     return da, db, dh0
 
 
-def lr_selective_scan(x, dt, A, Bm, Cm, Dskip=None, h0=None, disc="zoh", y=None, h_last=None,
-                      want_last=False):
+def lr_selective_scan(x, dt, A, Bm, Cm, Dskip=None, h0=None, disc="zoh", seg=0, y=None,
+                      h_last=None, ckpt=None, want_last=False):
     """Mamba-1 selective scan with fused readout; x, dt: [B, L, D], A: [D, N],
-    Bm, Cm: [B, L, N]."""
+    Bm, Cm: [B, L, N].  With seg > 0 the segment checkpoints
+    ([ceil(L/seg), B, D, N]) are returned as the third value."""
     B, L, D = x.shape
     N = A.shape[1]
     if y is None:
         y = torch.empty_like(x)
     if want_last and h_last is None:
         h_last = torch.empty(B, D, N, device=x.device, dtype=torch.float32)
+    if seg > 0 and ckpt is None:
+        ckpt = torch.empty((L + seg - 1) // seg, B, D, N, device=x.device, dtype=torch.float32)
     check("lr_selective_scan", lib().lr_selective_scan(
-        _io(x), _DISC[disc], B, L, D, N, _ptr(x), _ptr(dt), _f32(A, "A"), _ptr(Bm), _ptr(Cm),
-        _f32(Dskip, "Dskip"), _f32(h0, "h0"), _ptr(y), _f32(h_last, "h_last"), _stream(x)))
-    return y, h_last
+        _io(x), _DISC[disc], B, L, D, N, seg, _ptr(x), _ptr(dt), _f32(A, "A"), _ptr(Bm),
+        _ptr(Cm), _f32(Dskip, "Dskip"), _f32(h0, "h0"), _ptr(y), _f32(h_last, "h_last"),
+        _f32(ckpt, "ckpt"), _stream(x)))
+    return (y, h_last, ckpt) if seg > 0 else (y, h_last)
+
+
+def lr_selective_scan_bwd_workspace_bytes(B, L, D, N, seg) -> int:
+    return int(lib().lr_selective_scan_bwd_workspace_bytes(B, L, D, N, seg))
+
+
+def lr_selective_scan_bwd(x, dt, A, Bm, Cm, Dskip, ckpt, dy, dh_last=None, disc="zoh", seg=256,
+                          workspace=None, want_dh0=False):
+    """Gradients of sum(dy*y) + <dh_last, h_last> of lr_selective_scan.
+    Returns a dict with dx, ddt, dA, dB, dC, dD (None without Dskip), dh0."""
+    B, L, D = x.shape
+    N = A.shape[1]
+    dev = x.device
+    dx, ddt = torch.empty_like(x), torch.empty_like(dt)
+    dB, dC = torch.empty_like(Bm), torch.empty_like(Cm)
+    dA = torch.empty(D, N, device=dev, dtype=torch.float32)
+    dD = torch.empty(D, device=dev, dtype=torch.float32) if Dskip is not None else None
+    dh0 = torch.empty(B, D, N, device=dev, dtype=torch.float32) if want_dh0 else None
+    need = lr_selective_scan_bwd_workspace_bytes(B, L, D, N, seg)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), device=dev, dtype=torch.uint8)
+    check("lr_selective_scan_bwd", lib().lr_selective_scan_bwd(
+        _io(x), _DISC[disc], B, L, D, N, seg, _ptr(x), _ptr(dt), _f32(A, "A"), _ptr(Bm),
+        _ptr(Cm), _f32(Dskip, "Dskip"), _f32(ckpt, "ckpt"), _ptr(dy), _f32(dh_last, "dh_last"),
+        _ptr(dx), _ptr(ddt), _f32(dA, "dA"), _ptr(dB), _ptr(dC), _f32(dD, "dD"),
+        _f32(dh0, "dh0"), _ptr(workspace), workspace.numel(), _stream(x)))
+    return dict(dx=dx, ddt=ddt, dA=dA, dB=dB, dC=dC, dD=dD, dh0=dh0)
 
 
 def lr_ssd_scan(x, dt, A, Bm, Cm, Dskip=None, h0=None, disc="zoh", chunk=64, seg=0, y=None,

@@ -26,8 +26,13 @@ SIGNATURES = {
     "lr_diag_scan": (_int, [_int, _i64, _i64, _i64, _p, _p, _f32p, _p, _f32p, _p]),
     "lr_diag_scan_bwd": (_int, [_int, _i64, _i64, _i64, _p, _p, _f32p, _p, _f32p, _p, _p, _f32p,
                                 _p]),
-    "lr_selective_scan": (_int, [_int, _int, _i64, _i64, _i64, _i64, _p, _p, _f32p, _p, _p,
-                                 _f32p, _f32p, _p, _f32p, _p]),
+    "lr_selective_scan": (_int, [_int, _int, _i64, _i64, _i64, _i64, _i64, _p, _p, _f32p, _p,
+                                 _p, _f32p, _f32p, _p, _f32p, _f32p, _p]),
+    "lr_selective_scan_bwd_workspace_bytes": (_sz, [_i64] * 5),
+    "lr_selective_scan_bwd": (_int, [_int, _int] + [_i64] * 5 + [_p, _p, _f32p, _p, _p, _f32p,
+                                                                 _f32p, _p, _f32p, _p, _p, _f32p,
+                                                                 _p, _p, _f32p, _f32p, _p, _sz,
+                                                                 _p]),
     "lr_ssd_scan": (_int, [_int, _int, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _p, _p,
                            _f32p, _p, _p, _f32p, _f32p, _p, _f32p, _f32p, _p]),
     "lr_ssd_scan_bwd_workspace_bytes": (_sz, [_i64] * 8),

@@ -23,8 +23,17 @@ hipError_t launch_diag_scan_bwd(const void* a, const void* h, const float* h0, c
 template <typename T>
 hipError_t launch_selective_scan(int disc, const void* x, const void* dt, const float* A,
                                  const void* Bm, const void* Cm, const float* Dskip,
-                                 const float* h0, void* y, float* h_last, int64_t B, int64_t L,
-                                 int64_t D, int N, hipStream_t stream);
+                                 const float* h0, void* y, float* h_last, float* ckpt, int64_t B,
+                                 int64_t L, int64_t D, int N, int64_t seg, hipStream_t stream);
+bool selective_bwd_supported(int64_t N, int64_t seg);
+size_t selective_bwd_workspace(int64_t B, int64_t L, int64_t D, int64_t N);
+template <typename T>
+hipError_t launch_selective_bwd(int disc, const void* x, const void* dt, const float* A,
+                                const void* Bm, const void* Cm, const float* Dskip,
+                                const float* ckpt, const void* dy, const float* dh_last, void* dx,
+                                void* ddt, float* dA, void* dBm, void* dCm, float* dD, float* dh0,
+                                void* ws, int64_t B, int64_t L, int64_t D, int64_t N, int64_t seg,
+                                hipStream_t stream);
 hipError_t launch_ssd_fwd(int disc, const void* x, const void* dt, const float* A, const void* Bm,
                           const void* Cm, const float* Dskip, const float* h0, void* y,
                           float* h_last, float* ckpt, int64_t B, int64_t L, int64_t H, int64_t P,
@@ -165,26 +174,68 @@ lr_status lr_diag_scan_bwd(lr_dtype io, int64_t B, int64_t L, int64_t D, const v
 }
 
 lr_status lr_selective_scan(lr_dtype io, lr_disc disc, int64_t B, int64_t L, int64_t D, int64_t N,
-                            const void* x, const void* dt, const float* A, const void* Bm,
-                            const void* Cm, const float* Dskip, const float* h0, void* y,
-                            float* h_last, void* stream) {
+                            int64_t seg, const void* x, const void* dt, const float* A,
+                            const void* Bm, const void* Cm, const float* Dskip, const float* h0,
+                            void* y, float* h_last, float* ckpt, void* stream) {
   if (!valid_io(io) || !valid_disc(disc)) return LR_E_DTYPE;
-  if (B < 0 || L < 0 || D < 1 || N < 1) return LR_E_SHAPE;
-  if (N > 64) return LR_E_UNSUPPORTED;
+  if (B < 0 || L < 0 || D < 1 || N < 1 || seg < 0) return LR_E_SHAPE;
+  if (N > 64 || seg % 32 != 0) return LR_E_UNSUPPORTED;
   if (!elems_ok({B, L, D}) || !elems_ok({B, D, N}) || !elems_ok({D, N})) return LR_E_OVERFLOW;
+  if (seg > 0 && !elems_ok({(L + seg - 1) / seg, B, D, N})) return LR_E_OVERFLOW;
   int64_t nwg = 1;
   if (!mul_ok(nwg, B) || !mul_ok(nwg, (D + 63) / 64) || nwg > kMaxGrid) return LR_E_OVERFLOW;
   if (A == nullptr) return LR_E_NULLPTR;
   if (B * L > 0 && any_null({x, dt, Bm, Cm, y})) return LR_E_NULLPTR;
-  if (!all_aligned({x, dt, A, Bm, Cm, Dskip, h0, y, h_last})) return LR_E_ALIGN;
+  if (B * L > 0 && seg > 0 && ckpt == nullptr) return LR_E_NULLPTR;
+  if (!all_aligned({x, dt, A, Bm, Cm, Dskip, h0, y, h_last, ckpt})) return LR_E_ALIGN;
   if (B == 0) return LR_OK;
   auto s = static_cast<hipStream_t>(stream);
   const int n = static_cast<int>(N);
+  float* ck = seg > 0 ? ckpt : nullptr;
   return hip_status(io == LR_F32
                         ? lr::launch_selective_scan<float>(disc, x, dt, A, Bm, Cm, Dskip, h0, y,
-                                                           h_last, B, L, D, n, s)
+                                                           h_last, ck, B, L, D, n, seg, s)
                         : lr::launch_selective_scan<uint16_t>(disc, x, dt, A, Bm, Cm, Dskip, h0,
-                                                              y, h_last, B, L, D, n, s));
+                                                              y, h_last, ck, B, L, D, n, seg, s));
+}
+
+size_t lr_selective_scan_bwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N,
+                                             int64_t seg) {
+  if (B < 0 || L < 0 || D < 1 || N < 1 || !lr::selective_bwd_supported(N, seg)) return 0;
+  if (!elems_ok({B, L, D}) || !elems_ok({B, D, N})) return 0;
+  return lr::selective_bwd_workspace(B, L, D, N);
+}
+
+lr_status lr_selective_scan_bwd(lr_dtype io, lr_disc disc, int64_t B, int64_t L, int64_t D,
+                                int64_t N, int64_t seg, const void* x, const void* dt,
+                                const float* A, const void* Bm, const void* Cm,
+                                const float* Dskip, const float* ckpt, const void* dy,
+                                const float* dh_last, void* dx, void* ddt, float* dA, void* dBm,
+                                void* dCm, float* dD, float* dh0, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (!valid_io(io) || !valid_disc(disc)) return LR_E_DTYPE;
+  if (B < 0 || L < 0 || D < 1 || N < 1 || seg < 1) return LR_E_SHAPE;
+  if (!lr::selective_bwd_supported(N, seg)) return LR_E_UNSUPPORTED;
+  if (!elems_ok({B, L, D}) || !elems_ok({B, D, N}) || !elems_ok({D, N}) ||
+      !elems_ok({(D + 63) / 64, B, L, N}) || !elems_ok({(L + seg - 1) / seg, B, D, N}))
+    return LR_E_OVERFLOW;
+  int64_t nwg = 1;
+  if (!mul_ok(nwg, B) || !mul_ok(nwg, (D + 63) / 64) || nwg > kMaxGrid) return LR_E_OVERFLOW;
+  if (A == nullptr || dA == nullptr) return LR_E_NULLPTR;
+  if (B * L > 0 && any_null({x, dt, Bm, Cm, ckpt, dy, dx, ddt, dBm, dCm})) return LR_E_NULLPTR;
+  if (!all_aligned({x, dt, A, Bm, Cm, Dskip, ckpt, dy, dh_last, dx, ddt, dA, dBm, dCm, dD, dh0,
+                    workspace}))
+    return LR_E_ALIGN;
+  const size_t need = lr::selective_bwd_workspace(B, L, D, N);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LR_E_WORKSPACE;
+  auto s = static_cast<hipStream_t>(stream);
+  return hip_status(io == LR_F32
+                        ? lr::launch_selective_bwd<float>(disc, x, dt, A, Bm, Cm, Dskip, ckpt, dy,
+                                                          dh_last, dx, ddt, dA, dBm, dCm, dD, dh0,
+                                                          workspace, B, L, D, N, seg, s)
+                        : lr::launch_selective_bwd<uint16_t>(disc, x, dt, A, Bm, Cm, Dskip, ckpt,
+                                                             dy, dh_last, dx, ddt, dA, dBm, dCm, dD,
+                                                             dh0, workspace, B, L, D, N, seg, s));
 }
 
 lr_status lr_ssd_scan(lr_dtype io, lr_disc disc, int64_t B, int64_t L, int64_t H, int64_t P,

@@ -1,0 +1,390 @@
+// selective_bwd.hip — backward of the Mamba-1 selective scan with segment
+// checkpoints and recompute.
+//
+// ("lrnnx: A library for Linear RNNs", Key Contributions 2-3: the
+// time-varying selective scan with ZOH discretisation and fused readout;
+// "mlx-recurrence" post, Apple Developer Forums thread 840535: the training
+// path keeps the state at segment boundaries in the forward and recomputes
+// inside each segment in the backward.)
+//
+// Loss l = sum(dy * y) + <dh_last, h_last>.  Per chain (b, d, n), with
+// G_t = dl/dh_t:
+//   G_t = e_{t+1} G_{t+1} + dy_t C_t[n],          dh0 = e_0 G_0
+//   dx_t[d] = sum_n G phi B_t[n] + D[d] dy_t[d]
+//   dB_t[n] = sum_d G phi x_t[d],   dC_t[n] = sum_d h_t dy_t[d]
+//   de = G h_{t-1},  dphi = G B_t[n] x_t[d]  -> ddt (sum over n), dA (sum over b, t)
+//
+// Work split: one workgroup per (batch row, 64 channels), 8 waves, wave w
+// owning state indices n = 2w, 2w + 1 of every channel (lane = channel), as
+// in the forward.  The workgroup walks the segments last to first carrying
+// G in registers.  Per segment it first runs the forward from the segment's
+// checkpoint, keeping the state every 16 tokens in LDS, then walks the
+// 16-token chunks last to first: recompute the chunk's 16 states into
+// registers, then the reverse steps.  Sums over n (dx, ddt) go through LDS
+// across the waves; sums over the 64 channels of a wave (dB, dC) use a
+// butterfly reduction of the four values (dB, dC at n = 2w, 2w + 1); sums
+// over channel tiles (dB, dC) and batch rows (dA, dD) are fixed-order
+// partial sums reduced by a second launch, so results are deterministic.
+#include "common.hpp"
+
+namespace lr {
+
+constexpr int kSbTC = 16;     // tokens per chunk
+constexpr int kSbNW = 8;      // waves (2 state indices each: N <= 16)
+constexpr int kSbSub = 16;    // chunks per segment (seg <= 256)
+constexpr int kSbCT = 64;     // channels per workgroup
+
+enum { kSbZoh = 0, kSbEuler = 1 };
+
+struct SelBwdArgs {
+  const void* x; const void* dt; const float* A; const void* Bm; const void* Cm;
+  const float* Dskip; const float* ckpt; const void* dy; const float* dh_last;
+  void* dx; void* ddt; float* dh0;
+  float* dBpart; float* dCpart;   // [ntile][B][L][N]
+  float* dApart;                  // [B][D][N]
+  float* dDpart;                  // [B][D]
+  void* dBm; void* dCm; float* dA; float* dD;
+  int64_t B, L, D, N, seg, nseg, ntile;
+};
+
+// e, phi and their derivatives for one (dt, A).  ZOH: phi = expm1(dt A) / A
+// through a series near dt A = 0 (A = 0 included); dphi/dA = (dt e - phi)/A,
+// also through its series there.
+template <int DISC>
+__device__ __forceinline__ void sb_disc(float dtv, float Av, float& e, float& phi) {
+  const float lam = dtv * Av;
+  e = fast_exp2(lam * kLog2e);
+  if (DISC == kSbEuler) {
+    phi = dtv;
+  } else {
+    const float ser =
+        dtv * fmaf(lam, fmaf(lam, fmaf(lam, fmaf(lam, 1.f / 120.f, 1.f / 24.f), 1.f / 6.f), 0.5f), 1.f);
+    phi = fabsf(lam) < 0.1f ? ser : (e - 1.f) / Av;
+  }
+}
+
+template <int DISC>
+__device__ __forceinline__ float sb_dphi_dA(float dtv, float Av, float e, float phi) {
+  if (DISC == kSbEuler) return 0.f;
+  const float lam = dtv * Av;
+  const float ser = dtv * dtv *
+                    fmaf(lam, fmaf(lam, fmaf(lam, fmaf(lam, 1.f / 144.f, 1.f / 30.f), 1.f / 8.f), 1.f / 3.f), 0.5f);
+  return fabsf(lam) < 0.1f ? ser : (dtv * e - phi) / Av;
+}
+
+struct SbLds {
+  float xs[kSbTC][kSbCT], dts[kSbTC][kSbCT], dys[kSbTC][kSbCT];
+  float Bs[kSbTC][16], Cs[kSbTC][16];                 // n >= N stay zero
+  float pdx[kSbNW][kSbTC][kSbCT], pddt[kSbNW][kSbTC][kSbCT];
+  float sub[kSbSub][kSbNW][2][kSbCT];                 // state entering each chunk
+  float rbc[kSbTC][2][16];                            // dB, dC of the chunk
+};
+
+template <typename T, int DISC>
+__global__ __launch_bounds__(512) void selective_bwd_kernel(SelBwdArgs a) {
+  __shared__ SbLds sm;
+  const T* x = static_cast<const T*>(a.x);
+  const T* dt = static_cast<const T*>(a.dt);
+  const T* Bm = static_cast<const T*>(a.Bm);
+  const T* Cm = static_cast<const T*>(a.Cm);
+  const T* dy = static_cast<const T*>(a.dy);
+  T* dx = static_cast<T*>(a.dx);
+  T* ddt = static_cast<T*>(a.ddt);
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int64_t tile = blockIdx.x % a.ntile;
+  const int64_t b = blockIdx.x / a.ntile;
+  const int64_t d0 = tile * kSbCT;
+  const int64_t d = d0 + lane;
+  const bool dok = d < a.D;
+  const int N = static_cast<int>(a.N);
+  const int n0 = 2 * w;
+  const int64_t D = a.D, L = a.L;
+
+  float Av[2], G[2], dAacc[2] = {0.f, 0.f};
+  bool okj[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    okj[j] = dok && n0 + j < N;
+    Av[j] = okj[j] ? a.A[d * N + n0 + j] : 0.f;
+    G[j] = (okj[j] && a.dh_last != nullptr) ? a.dh_last[(b * D + d) * N + n0 + j] : 0.f;
+  }
+  const float Dd = (dok && a.Dskip != nullptr) ? a.Dskip[d] : 0.f;
+  float dDacc = 0.f;
+
+  // B and C columns n >= N stay zero for the whole kernel
+  for (int i = tid; i < kSbTC * 16; i += 512) {
+    (&sm.Bs[0][0])[i] = 0.f;
+    (&sm.Cs[0][0])[i] = 0.f;
+  }
+  __syncthreads();
+
+  // stage tokens t0 .. t0 + nv - 1 (missing tokens and channels as zeros:
+  // dt = 0 gives e = 1, phi = 0, so they leave the state unchanged)
+  auto stage = [&](int64_t t0, int nv, bool with_dy) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int i = tid + 512 * k;     // [TC][64]
+      const int r = i >> 6, c = i & 63;
+      const bool ok = r < nv && d0 + c < D;
+      const int64_t off = (b * L + t0 + r) * D + d0 + c;
+      sm.xs[r][c] = ok ? Io<T>::load(x + off) : 0.f;
+      sm.dts[r][c] = ok ? Io<T>::load(dt + off) : 0.f;
+      if (with_dy) sm.dys[r][c] = ok ? Io<T>::load(dy + off) : 0.f;
+    }
+    if (tid < kSbTC * N) {
+      const int r = tid / N, n = tid % N;
+      const bool ok = r < nv;
+      const int64_t off = (b * L + t0 + r) * N + n;
+      sm.Bs[r][n] = ok ? Io<T>::load(Bm + off) : 0.f;
+      sm.Cs[r][n] = ok ? Io<T>::load(Cm + off) : 0.f;
+    }
+  };
+
+  for (int64_t s = a.nseg - 1; s >= 0; --s) {
+    const int64_t ts0 = s * a.seg;
+    const int64_t tse = (ts0 + a.seg < L) ? ts0 + a.seg : L;
+    const int nch = static_cast<int>((tse - ts0 + kSbTC - 1) / kSbTC);
+    float h[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      h[j] = okj[j] ? a.ckpt[((s * a.B + b) * D + d) * N + n0 + j] : 0.f;
+
+    // ---- forward over the segment: the state entering every chunk
+    for (int c = 0; c < nch; ++c) {
+      const int64_t t0 = ts0 + static_cast<int64_t>(c) * kSbTC;
+      const int nv = static_cast<int>((tse - t0) < kSbTC ? (tse - t0) : kSbTC);
+      sm.sub[c][w][0][lane] = h[0];
+      sm.sub[c][w][1][lane] = h[1];
+      stage(t0, nv, false);
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < kSbTC; ++i) {
+        const float xv = sm.xs[i][lane], dtv = sm.dts[i][lane];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          float e, phi;
+          sb_disc<DISC>(dtv, Av[j], e, phi);
+          h[j] = fmaf(e, h[j], phi * sm.Bs[i][n0 + j] * xv);
+        }
+      }
+      __syncthreads();
+    }
+
+    // ---- chunks last to first
+    for (int c = nch - 1; c >= 0; --c) {
+      const int64_t t0 = ts0 + static_cast<int64_t>(c) * kSbTC;
+      const int nv = static_cast<int>((tse - t0) < kSbTC ? (tse - t0) : kSbTC);
+      stage(t0, nv, true);
+      __syncthreads();
+      float hs[kSbTC][2];
+      float hin[2] = {sm.sub[c][w][0][lane], sm.sub[c][w][1][lane]};
+      {
+        float hh[2] = {hin[0], hin[1]};
+#pragma unroll
+        for (int i = 0; i < kSbTC; ++i) {
+          const float xv = sm.xs[i][lane], dtv = sm.dts[i][lane];
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            float e, phi;
+            sb_disc<DISC>(dtv, Av[j], e, phi);
+            hh[j] = fmaf(e, hh[j], phi * sm.Bs[i][n0 + j] * xv);
+            hs[i][j] = hh[j];
+          }
+        }
+      }
+#pragma unroll
+      for (int i = kSbTC - 1; i >= 0; --i) {
+        const float xv = sm.xs[i][lane], dtv = sm.dts[i][lane], dyv = sm.dys[i][lane];
+        float dxp = 0.f, ddtp = 0.f, v[4];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const float Bv = sm.Bs[i][n0 + j], Cv = sm.Cs[i][n0 + j];
+          float e, ph;
+          sb_disc<DISC>(dtv, Av[j], e, ph);
+          G[j] = fmaf(dyv, Cv, G[j]);
+          const float gphi = G[j] * ph;
+          dxp = fmaf(gphi, Bv, dxp);
+          v[j] = gphi * xv;                 // dB partial
+          v[2 + j] = hs[i][j] * dyv;        // dC partial
+          const float hp = i > 0 ? hs[i - 1][j] : hin[j];
+          const float de = G[j] * hp;
+          const float dphi = G[j] * Bv * xv;
+          const float dphidt = DISC == kSbEuler ? 1.f : e;
+          ddtp += fmaf(de * Av[j], e, dphi * dphidt);
+          dAacc[j] += fmaf(de * dtv, e, dphi * sb_dphi_dA<DISC>(dtv, Av[j], e, ph));
+          G[j] *= e;
+        }
+        // butterfly: lanes l, l^16, l^32, l^48 end with one of the four values
+        const bool hi = (lane & 32) != 0, mid = (lane & 16) != 0;
+        float a0 = hi ? v[2] : v[0], a1 = hi ? v[3] : v[1];
+        const float s0 = __shfl_xor(hi ? v[0] : v[2], 32), s1 = __shfl_xor(hi ? v[1] : v[3], 32);
+        a0 += s0;
+        a1 += s1;
+        float r = mid ? a1 : a0;
+        r += __shfl_xor(mid ? a0 : a1, 16);
+        r += __shfl_xor(r, 8);
+        r += __shfl_xor(r, 4);
+        r += __shfl_xor(r, 2);
+        r += __shfl_xor(r, 1);
+        if ((lane & 15) == 0) sm.rbc[i][hi ? 1 : 0][n0 + (mid ? 1 : 0)] = r;
+        sm.pdx[w][i][lane] = dxp;
+        sm.pddt[w][i][lane] = ddtp;
+        if (w == 0) dDacc = fmaf(dyv, xv, dDacc);
+      }
+      __syncthreads();
+      // sums over the waves -> dx, ddt; the chunk's dB, dC partials
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int i = tid + 512 * k;
+        const int r = i >> 6, cc = i & 63;
+        if (r < nv && d0 + cc < D) {
+          float sx = 0.f, st = 0.f;
+#pragma unroll
+          for (int ww = 0; ww < kSbNW; ++ww) {
+            sx += sm.pdx[ww][r][cc];
+            st += sm.pddt[ww][r][cc];
+          }
+          const float Dc = a.Dskip != nullptr ? a.Dskip[d0 + cc] : 0.f;
+          const int64_t off = (b * L + t0 + r) * D + d0 + cc;
+          Io<T>::store(dx + off, fmaf(Dc, sm.dys[r][cc], sx));
+          Io<T>::store(ddt + off, st);
+        }
+      }
+      if (tid < kSbTC * N) {
+        const int r = tid / N, n = tid % N;
+        if (r < nv) {
+          const int64_t off = ((tile * a.B + b) * L + t0 + r) * N + n;
+          a.dBpart[off] = sm.rbc[r][0][n];
+          a.dCpart[off] = sm.rbc[r][1][n];
+        }
+      }
+      __syncthreads();
+    }
+  }
+  (void)Dd;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    if (okj[j]) {
+      const int64_t o = (b * D + d) * N + n0 + j;
+      if (a.dh0 != nullptr) a.dh0[o] = G[j];
+      a.dApart[o] = dAacc[j];
+    }
+  }
+  if (w == 0 && dok) a.dDpart[b * D + d] = dDacc;
+}
+
+// Fixed-order sums: dB, dC over channel tiles; dA, dD over batch rows.
+template <typename T>
+__global__ __launch_bounds__(256) void selective_bwd_reduce_kernel(SelBwdArgs a) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t nbc = a.B * a.L * a.N;
+  if (idx < nbc) {
+    float sb = 0.f, sc = 0.f;
+    for (int64_t t = 0; t < a.ntile; ++t) {
+      sb += a.dBpart[t * nbc + idx];
+      sc += a.dCpart[t * nbc + idx];
+    }
+    Io<T>::store(static_cast<T*>(a.dBm) + idx, sb);
+    Io<T>::store(static_cast<T*>(a.dCm) + idx, sc);
+    return;
+  }
+  const int64_t i2 = idx - nbc;
+  const int64_t DN = a.D * a.N;
+  if (i2 < DN) {
+    float s = 0.f;
+    for (int64_t bb = 0; bb < a.B; ++bb) s += a.dApart[bb * DN + i2];
+    a.dA[i2] = s;
+    return;
+  }
+  const int64_t i3 = i2 - DN;
+  if (i3 < a.D && a.dD != nullptr) {
+    float s = 0.f;
+    for (int64_t bb = 0; bb < a.B; ++bb) s += a.dDpart[bb * a.D + i3];
+    a.dD[i3] = s;
+  }
+}
+
+// Empty sequence (B * L == 0): dA = dD = 0, dh0 = dh_last (or 0).
+__global__ __launch_bounds__(256) void selective_bwd_empty_kernel(float* dA, float* dD, float* dh0,
+                                                                  const float* dh_last, int64_t DN,
+                                                                  int64_t D, int64_t nstate) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i < DN) dA[i] = 0.f;
+  if (dD != nullptr && i < D) dD[i] = 0.f;
+  if (dh0 != nullptr && i < nstate) dh0[i] = dh_last != nullptr ? dh_last[i] : 0.f;
+}
+
+static inline int64_t sb_align(int64_t v) { return (v + 255) & ~int64_t(255); }
+
+struct SbLayout { int64_t dB, dC, dA, dD, total; };
+
+static SbLayout sb_layout(int64_t B, int64_t L, int64_t D, int64_t N) {
+  const int64_t nt = (D + kSbCT - 1) / kSbCT;
+  SbLayout w;
+  int64_t o = 0;
+  w.dB = o; o = sb_align(o + nt * B * L * N * 4);
+  w.dC = o; o = sb_align(o + nt * B * L * N * 4);
+  w.dA = o; o = sb_align(o + B * D * N * 4);
+  w.dD = o; o = sb_align(o + B * D * 4);
+  w.total = o;
+  return w;
+}
+
+bool selective_bwd_supported(int64_t N, int64_t seg) {
+  return N >= 1 && N <= 2 * kSbNW && seg >= 32 && seg <= kSbTC * kSbSub && seg % 32 == 0;
+}
+
+size_t selective_bwd_workspace(int64_t B, int64_t L, int64_t D, int64_t N) {
+  if (B * L == 0) return 0;
+  return static_cast<size_t>(sb_layout(B, L, D, N).total);
+}
+
+template <typename T>
+hipError_t launch_selective_bwd(int disc, const void* x, const void* dt, const float* A,
+                                const void* Bm, const void* Cm, const float* Dskip,
+                                const float* ckpt, const void* dy, const float* dh_last, void* dx,
+                                void* ddt, float* dA, void* dBm, void* dCm, float* dD, float* dh0,
+                                void* ws, int64_t B, int64_t L, int64_t D, int64_t N, int64_t seg,
+                                hipStream_t stream) {
+  if (B * L == 0) {
+    const int64_t n = (B * D * N > D * N) ? B * D * N : D * N;
+    hipLaunchKernelGGL(selective_bwd_empty_kernel, dim3((n + 255) / 256 > 0 ? (n + 255) / 256 : 1),
+                       dim3(256), 0, stream, dA, dD, dh0, dh_last, D * N, D, B * D * N);
+    return hipGetLastError();
+  }
+  const SbLayout lay = sb_layout(B, L, D, N);
+  char* base = static_cast<char*>(ws);
+  SelBwdArgs a;
+  a.x = x; a.dt = dt; a.A = A; a.Bm = Bm; a.Cm = Cm; a.Dskip = Dskip; a.ckpt = ckpt; a.dy = dy;
+  a.dh_last = dh_last; a.dx = dx; a.ddt = ddt; a.dh0 = dh0;
+  a.dBpart = reinterpret_cast<float*>(base + lay.dB);
+  a.dCpart = reinterpret_cast<float*>(base + lay.dC);
+  a.dApart = reinterpret_cast<float*>(base + lay.dA);
+  a.dDpart = reinterpret_cast<float*>(base + lay.dD);
+  a.dBm = dBm; a.dCm = dCm; a.dA = dA; a.dD = dD;
+  a.B = B; a.L = L; a.D = D; a.N = N; a.seg = seg; a.nseg = (L + seg - 1) / seg;
+  a.ntile = (D + kSbCT - 1) / kSbCT;
+  const dim3 grid(static_cast<unsigned>(B * a.ntile));
+  if (disc == kSbEuler) hipLaunchKernelGGL((selective_bwd_kernel<T, kSbEuler>), grid, dim3(512), 0, stream, a);
+  else hipLaunchKernelGGL((selective_bwd_kernel<T, kSbZoh>), grid, dim3(512), 0, stream, a);
+  const int64_t nred = B * L * N + D * N + D;
+  hipLaunchKernelGGL(selective_bwd_reduce_kernel<T>, dim3((nred + 255) / 256), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+template hipError_t launch_selective_bwd<float>(int, const void*, const void*, const float*,
+                                                const void*, const void*, const float*,
+                                                const float*, const void*, const float*, void*,
+                                                void*, float*, void*, void*, float*, float*, void*,
+                                                int64_t, int64_t, int64_t, int64_t, int64_t,
+                                                hipStream_t);
+template hipError_t launch_selective_bwd<uint16_t>(int, const void*, const void*, const float*,
+                                                   const void*, const void*, const float*,
+                                                   const float*, const void*, const float*, void*,
+                                                   void*, float*, void*, void*, float*, float*,
+                                                   void*, int64_t, int64_t, int64_t, int64_t,
+                                                   int64_t, hipStream_t);
+
+}  // namespace lr

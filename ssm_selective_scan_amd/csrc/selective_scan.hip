@@ -195,7 +195,7 @@ __device__ __forceinline__ void selective_body(
     const T* __restrict__ x, const T* __restrict__ dt, const T* __restrict__ Bm,
     const T* __restrict__ Cm, T* __restrict__ y, float* __restrict__ smem, float (&h)[NPW],
     const float (&A2)[NPW], const float (&iA)[NPW], const float (&An)[NPW], int64_t bi,
-    int64_t d0, int64_t L, int64_t D, int N) {
+    int64_t d0, int64_t L, int64_t D, int N, float* ck, int64_t ck_step, int64_t seg) {
   constexpr int kThreads = 64 * NW;
   constexpr int MK = (TT * 8 + kThreads - 1) / kThreads;    // 8-channel x/dt chunks per thread
   constexpr int ME = (TT * NPW * NW + kThreads - 1) / kThreads;  // B/C values per thread
@@ -224,7 +224,15 @@ __device__ __forceinline__ void selective_body(
     const int nt = static_cast<int>(L < TT ? L : TT);
     st.load(x + row0 * D + d0, dt + row0 * D + d0, Bm + row0 * N, Cm + row0 * N, nt, dcols, N);
   }
+  int64_t ck_t = 0;   // token of the next segment checkpoint
   for (int64_t t0 = 0; t0 < L; t0 += TT) {
+    if (ck != nullptr && t0 == ck_t) {   // the state entering token t0 (seg % TT == 0)
+#pragma unroll
+      for (int j = 0; j < NPW; ++j)
+        if (n0 + j < N) ck[j] = h[j];
+      ck += ck_step;
+      ck_t += seg;
+    }
     st.store(xs, dts, Bs, Cs);
     __syncthreads();
     // next tile's loads are in flight while this tile is computed
@@ -289,8 +297,8 @@ template <typename T, int DISC, int TT, int NPW, int NW, bool VEC>
 __global__ __launch_bounds__(64 * NW) void selective_scan_kernel(
     const T* __restrict__ x, const T* __restrict__ dt, const float* __restrict__ A,
     const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ Dskip,
-    const float* __restrict__ h0, T* __restrict__ y, float* __restrict__ h_last, int64_t L,
-    int64_t D, int N) {
+    const float* __restrict__ h0, T* __restrict__ y, float* __restrict__ h_last,
+    float* __restrict__ ckpt, int64_t L, int64_t D, int N, int64_t seg, int64_t ck_step) {
   extern __shared__ float smem[];
   constexpr int GS = NW >= 16 ? 2 : ((NPW == 4 || sizeof(T) == 4) ? 4 : 8);
   const int tid = threadIdx.x;
@@ -322,16 +330,17 @@ __global__ __launch_bounds__(64 * NW) void selective_scan_kernel(
     if (tid < 64) Dk[tid] = (Dskip != nullptr && d0 + tid < D) ? Dskip[d0 + tid] : 0.f;
   }
   const bool precise = __syncthreads_or(small ? 1 : 0) != 0;
+  float* ck = (ckpt != nullptr && dok) ? ckpt + (bi * D + d) * N + n0 : nullptr;
 
   if (DISC == kDiscEuler) {
     selective_body<T, DISC, false, TT, NPW, NW, GS, VEC>(x, dt, Bm, Cm, y, smem, h, A2, iA, An,
-                                                        bi, d0, L, D, N);
+                                                        bi, d0, L, D, N, ck, ck_step, seg);
   } else if (precise) {
     selective_body<T, DISC, true, TT, NPW, NW, GS, VEC>(x, dt, Bm, Cm, y, smem, h, A2, iA, An,
-                                                       bi, d0, L, D, N);
+                                                       bi, d0, L, D, N, ck, ck_step, seg);
   } else {
     selective_body<T, DISC, false, TT, NPW, NW, GS, VEC>(x, dt, Bm, Cm, y, smem, h, A2, iA, An,
-                                                        bi, d0, L, D, N);
+                                                        bi, d0, L, D, N, ck, ck_step, seg);
   }
 
   if (h_last != nullptr && dok) {
@@ -344,14 +353,15 @@ __global__ __launch_bounds__(64 * NW) void selective_scan_kernel(
 template <typename T, int DISC, int TT, int NPW, int NW>
 static hipError_t launch_sel(const void* x, const void* dt, const float* A, const void* Bm,
                              const void* Cm, const float* Dskip, const float* h0, void* y,
-                             float* h_last, int64_t B, int64_t L, int64_t D, int N,
-                             hipStream_t stream) {
+                             float* h_last, float* ckpt, int64_t B, int64_t L, int64_t D, int N,
+                             int64_t seg, hipStream_t stream) {
   const size_t lds = (4 * TT * 64 + 64 + static_cast<size_t>(NW) * TT * 64) * sizeof(float);
   dim3 grid(static_cast<unsigned>(B * ((D + kSelCT - 1) / kSelCT)));
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, grid, dim3(64 * NW), lds, stream, static_cast<const T*>(x),
                        static_cast<const T*>(dt), A, static_cast<const T*>(Bm),
-                       static_cast<const T*>(Cm), Dskip, h0, static_cast<T*>(y), h_last, L, D, N);
+                       static_cast<const T*>(Cm), Dskip, h0, static_cast<T*>(y), h_last, ckpt, L, D,
+                       N, seg, B * D * N);
   };
   if (D % 8 == 0) go(selective_scan_kernel<T, DISC, TT, NPW, NW, true>);
   else go(selective_scan_kernel<T, DISC, TT, NPW, NW, false>);
@@ -366,34 +376,34 @@ static hipError_t launch_sel(const void* x, const void* dt, const float* A, cons
 template <typename T, int DISC>
 static hipError_t launch_sel_n(const void* x, const void* dt, const float* A, const void* Bm,
                                const void* Cm, const float* Dskip, const float* h0, void* y,
-                               float* h_last, int64_t B, int64_t L, int64_t D, int N,
-                               hipStream_t stream) {
+                               float* h_last, float* ckpt, int64_t B, int64_t L, int64_t D,
+                               int N, int64_t seg, hipStream_t stream) {
   if (N <= 8)
-    return launch_sel<T, DISC, 32, 2, 4>(x, dt, A, Bm, Cm, Dskip, h0, y, h_last, B, L, D, N, stream);
+    return launch_sel<T, DISC, 32, 2, 4>(x, dt, A, Bm, Cm, Dskip, h0, y, h_last, ckpt, B, L, D, N, seg, stream);
   if (N <= 16)
-    return launch_sel<T, DISC, 32, 2, 8>(x, dt, A, Bm, Cm, Dskip, h0, y, h_last, B, L, D, N, stream);
+    return launch_sel<T, DISC, 32, 2, 8>(x, dt, A, Bm, Cm, Dskip, h0, y, h_last, ckpt, B, L, D, N, seg, stream);
   if (N <= 32)
-    return launch_sel<T, DISC, 32, 4, 8>(x, dt, A, Bm, Cm, Dskip, h0, y, h_last, B, L, D, N, stream);
-  return launch_sel<T, DISC, 16, 4, 16>(x, dt, A, Bm, Cm, Dskip, h0, y, h_last, B, L, D, N, stream);
+    return launch_sel<T, DISC, 32, 4, 8>(x, dt, A, Bm, Cm, Dskip, h0, y, h_last, ckpt, B, L, D, N, seg, stream);
+  return launch_sel<T, DISC, 16, 4, 16>(x, dt, A, Bm, Cm, Dskip, h0, y, h_last, ckpt, B, L, D, N, seg, stream);
 }
 
 template <typename T>
 hipError_t launch_selective_scan(int disc, const void* x, const void* dt, const float* A,
                                  const void* Bm, const void* Cm, const float* Dskip,
-                                 const float* h0, void* y, float* h_last, int64_t B, int64_t L,
-                                 int64_t D, int N, hipStream_t stream) {
+                                 const float* h0, void* y, float* h_last, float* ckpt, int64_t B,
+                                 int64_t L, int64_t D, int N, int64_t seg, hipStream_t stream) {
   return disc == kDiscEuler
-             ? launch_sel_n<T, kDiscEuler>(x, dt, A, Bm, Cm, Dskip, h0, y, h_last, B, L, D, N, stream)
-             : launch_sel_n<T, kDiscZoh>(x, dt, A, Bm, Cm, Dskip, h0, y, h_last, B, L, D, N, stream);
+             ? launch_sel_n<T, kDiscEuler>(x, dt, A, Bm, Cm, Dskip, h0, y, h_last, ckpt, B, L, D, N, seg, stream)
+             : launch_sel_n<T, kDiscZoh>(x, dt, A, Bm, Cm, Dskip, h0, y, h_last, ckpt, B, L, D, N, seg, stream);
 }
 
 template hipError_t launch_selective_scan<float>(int, const void*, const void*, const float*,
                                                  const void*, const void*, const float*,
-                                                 const float*, void*, float*, int64_t, int64_t,
-                                                 int64_t, int, hipStream_t);
+                                                 const float*, void*, float*, float*, int64_t,
+                                                 int64_t, int64_t, int, int64_t, hipStream_t);
 template hipError_t launch_selective_scan<uint16_t>(int, const void*, const void*, const float*,
                                                     const void*, const void*, const float*,
-                                                    const float*, void*, float*, int64_t,
-                                                    int64_t, int64_t, int, hipStream_t);
+                                                    const float*, void*, float*, float*, int64_t,
+                                                    int64_t, int64_t, int, int64_t, hipStream_t);
 
 }  // namespace lr

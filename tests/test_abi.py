@@ -65,8 +65,41 @@ def test_diag_bwd_validation(L):
     assert diag_bwd(L, B=0, a=None, h=None, dh=None, da=None, db=None) == OK
 
 
-def sel(L, io=1, disc=0, B=1, Lq=8, D=4, N=16, x=P, dt=P, A=P, Bm=P, Cm=P, y=P):
-    return L.lr_selective_scan(io, disc, B, Lq, D, N, x, dt, A, Bm, Cm, None, None, y, None, None)
+def sel(L, io=1, disc=0, B=1, Lq=8, D=4, N=16, x=P, dt=P, A=P, Bm=P, Cm=P, y=P, seg=0, ck=None):
+    return L.lr_selective_scan(io, disc, B, Lq, D, N, seg, x, dt, A, Bm, Cm, None, None, y, None, ck,
+                               None)
+
+
+def test_selective_ckpt_and_bwd_validation(L):
+    assert sel(L, seg=48, ck=P) == UNSUP
+    assert sel(L, seg=-32) == SHAPE
+    assert sel(L, seg=32) == NULL        # checkpoints requested without a buffer
+    assert sel(L, seg=32, ck=MIS) == ALIGN
+    ws = L.lr_selective_scan_bwd_workspace_bytes(2, 100, 70, 16, 64)
+    assert ws > 0
+    assert L.lr_selective_scan_bwd_workspace_bytes(2, 100, 70, 17, 64) == 0
+    assert L.lr_selective_scan_bwd_workspace_bytes(2, 100, 70, 16, 48) == 0
+    #       io disc B  L    D   N   seg x  dt A  Bm Cm Dk    ckpt dy dhl   dx ddt dA dB dC dD    dh0
+    args = [1, 0, 2, 100, 70, 16, 64, P, P, P, P, P, None, P, P, None, P, P, P, P, P, None, None]
+    bad = list(args)
+    bad[1] = 9
+    assert L.lr_selective_scan_bwd(*bad, P, ws, None) == DTYPE
+    bad = list(args)
+    bad[6] = 0
+    assert L.lr_selective_scan_bwd(*bad, P, ws, None) == SHAPE
+    bad = list(args)
+    bad[5] = 32
+    assert L.lr_selective_scan_bwd(*bad, P, ws, None) == UNSUP
+    bad = list(args)
+    bad[13] = None   # ckpt
+    assert L.lr_selective_scan_bwd(*bad, P, ws, None) == NULL
+    bad = list(args)
+    bad[18] = None   # dA
+    assert L.lr_selective_scan_bwd(*bad, P, ws, None) == NULL
+    bad = list(args)
+    bad[16] = MIS    # dx
+    assert L.lr_selective_scan_bwd(*bad, P, ws, None) == ALIGN
+    assert L.lr_selective_scan_bwd(*args, P, ws - 256, None) == WS
 
 
 def test_selective_validation(L):
