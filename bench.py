@@ -202,6 +202,65 @@ def measure_ssd_bwd(warmup, iters):
     return out
 
 
+def measure_diag_bwd(warmup, iters):
+    g = lrgen.make(1, grads=True)
+    a, b, dh = dev(g.t("a")), dev(g.t("b")), dev(g.t("dh"))
+    h, _ = lr.lr_diag_scan(a, b)
+    t, _ = time_launches(lambda s: lr.lr_diag_scan_bwd(a, h, dh), [None], warmup, iters)
+    p = g.params
+    nb = 5 * p["B"] * p["L"] * p["D"] * 4     # read a, h, dh; write da, db
+    return dict(workload=lrgen.NAMES[1] + "_bwd", kernel="diag_scan_bwd_kernel", us=t * 1e6,
+                tokens_per_s=p["B"] * p["L"] / t, alg_bytes=nb, GBs=nb / t / 1e9,
+                hbm_frac=nb / t / 1e9 / HBM_PEAK_GBS, note="5 MB working set: launch/latency bound")
+
+
+def measure_selective_bwd(warmup, iters):
+    """Mamba-1 workload, forward with segment checkpoints (seg 256) then the
+    backward from them."""
+    g = lrgen.make(2, grads=True)
+    p = g.params
+    B, L, D, N, seg = p["B"], p["L"], p["D"], p["N"], 256
+    x, dt, Bm, Cm = dev(g.t("x")), dev(g.t("dt")), dev(g.t("B")), dev(g.t("C"))
+    A, Dk, dy = dev(g.t("A")), dev(g.t("Dskip")), dev(g.t("dy"))
+    y = torch.empty_like(x)
+    ckpt = torch.empty((L + seg - 1) // seg, B, D, N, device="cuda", dtype=torch.float32)
+    tf, _ = time_launches(lambda s: lr.lr_selective_scan(x, dt, A, Bm, Cm, Dk, seg=seg, y=y,
+                                                         ckpt=ckpt), [None], warmup, iters)
+    ws = torch.empty(max(lr.lr_selective_scan_bwd_workspace_bytes(B, L, D, N, seg), 16),
+                     device="cuda", dtype=torch.uint8)
+    tb, _ = time_launches(lambda s: lr.lr_selective_scan_bwd(x, dt, A, Bm, Cm, Dk, ckpt, dy,
+                                                             seg=seg, workspace=ws),
+                          [None], warmup, iters)
+    bwd_bytes = 5 * B * L * D * 2 + 4 * B * L * N * 2 + ckpt.numel() * 4
+    return dict(workload=lrgen.NAMES[2] + "_fwd_bwd_seg256", fwd_us=tf * 1e6, bwd_us=tb * 1e6,
+                fwd_bwd_tokens_per_s=B * L / (tf + tb), bwd_GBs=bwd_bytes / tb / 1e9,
+                ckpt_bytes=ckpt.numel() * 4, full_state_bytes=L * B * D * N * 4,
+                bwd_workspace_bytes=ws.numel())
+
+
+def measure_gla_bwd(warmup, iters):
+    """GLA workload, forward with segment checkpoints (seg 256) then the
+    backward from them."""
+    g = lrgen.make(4, grads=True)
+    p = g.params
+    B, L, H, K, V, seg = p["B"], p["L"], p["H"], p["K"], p["V"], 256
+    q, k, v, gg, do = (dev(g.t(n)) for n in ("q", "k", "v", "g", "do"))
+    o = torch.empty_like(v)
+    ckpt = torch.empty((L + seg - 1) // seg, B, H, V, K, device="cuda", dtype=torch.float32)
+    tf, _ = time_launches(lambda s: lr.lr_gla_scan(q, k, v, gg, chunk=p["chunk"], seg=seg, o=o,
+                                                   ckpt=ckpt), [None], warmup, iters)
+    ws = torch.empty(max(lr.lr_gla_scan_bwd_workspace_bytes(B, L, H, K, V, p["chunk"], seg), 16),
+                     device="cuda", dtype=torch.uint8)
+    tb, _ = time_launches(lambda s: lr.lr_gla_scan_bwd(q, k, v, gg, ckpt, do, chunk=p["chunk"],
+                                                       seg=seg, workspace=ws),
+                          [None], warmup, iters)
+    bwd_bytes = 4 * B * L * H * K * 2 + 3 * B * L * H * V * 2 + 2 * B * L * H * 2 + ckpt.numel() * 4
+    return dict(workload=lrgen.NAMES[4] + "_fwd_bwd_seg256", fwd_us=tf * 1e6, bwd_us=tb * 1e6,
+                fwd_bwd_tokens_per_s=B * L / (tf + tb), bwd_GBs=bwd_bytes / tb / 1e9,
+                ckpt_bytes=ckpt.numel() * 4, full_state_bytes=L * B * H * K * V * 4,
+                bwd_workspace_bytes=ws.numel())
+
+
 def copy_bandwidth(nbytes=1 << 30, iters=10):
     a = torch.empty(nbytes // 4, device="cuda", dtype=torch.float32).fill_(1.0)
     b = torch.empty_like(a)
@@ -247,6 +306,11 @@ def load_traffic():
     return float(kv["traffic_bytes_per_launch"])
 
 
+SECONDARY = {"diag": measure_diag, "ssd": measure_ssd, "gla": measure_gla,
+             "ssd_fwd_bwd": measure_ssd_bwd, "diag_bwd": measure_diag_bwd,
+             "selective_fwd_bwd": measure_selective_bwd, "gla_fwd_bwd": measure_gla_bwd}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -258,7 +322,7 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=8)
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
-    ap.add_argument("--only", choices=["diag", "ssd", "gla", "ssd_fwd_bwd"],
+    ap.add_argument("--only", choices=sorted(SECONDARY),
                     help="only time one secondary workload (for profiler runs)")
     args = ap.parse_args()
 
@@ -276,9 +340,7 @@ def main():
         print(json.dumps({"copy_probe_GBs": bw, "bytes_per_copy": 2 * (1 << 30)}))
         return
     if args.only:
-        f = {"diag": measure_diag, "ssd": measure_ssd, "gla": measure_gla,
-             "ssd_fwd_bwd": measure_ssd_bwd}[args.only]
-        print(json.dumps({args.only: f(args.warmup, args.steps)}))
+        print(json.dumps({args.only: SECONDARY[args.only](args.warmup, args.steps)}))
         return
 
     log(f"[bench] liblr: {lr.lr_version()}")
@@ -333,8 +395,7 @@ def main():
 
     if not args.headline_only:
         extra = {}
-        for name, f in (("diag", measure_diag), ("ssd", measure_ssd), ("gla", measure_gla),
-                        ("ssd_fwd_bwd", measure_ssd_bwd)):
+        for name, f in SECONDARY.items():
             log(f"[bench] measuring {name}")
             try:
                 extra[name] = f(3, 20)
