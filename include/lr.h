@@ -256,6 +256,48 @@ lr_status lr_gla_scan_bwd(lr_dtype io, int64_t B, int64_t L, int64_t H,
                           void* dg, float* dS0, void* workspace,
                           size_t workspace_bytes, void* stream);
 
+/* ===========================================================================
+ * Single-token steps (decode).  "lrnnx: A library for Linear RNNs" gives
+ * every layer a step method for autoregressive generation, checked against
+ * the parallel and recurrent modes, and runs the decode loop under graph
+ * capture.  Each call advances the caller's fp32 state h (or S) by one token
+ * IN PLACE and writes the token's output; T calls reproduce the matching
+ * scan over T tokens.  The calls allocate nothing, never synchronise and
+ * issue no memset, so a loop of them can be captured into a HIP graph.
+ * Same conventions as above; shapes are the scan's with the L axis removed.
+ * ======================================================================== */
+
+/* h = a (.) h + b;  out = h (io; may be NULL).
+ *   a, b, out: [B, D] io    h: [B, D] fp32 in/out */
+lr_status lr_diag_step(lr_dtype io, int64_t B, int64_t D, const void* a,
+                       const void* b, float* h, void* out, void* stream);
+
+/* One token of lr_selective_scan.
+ *   x, dt, y: [B, D] io    Bm, Cm: [B, N] io    A: [D, N]    Dskip: [D] or NULL
+ *   h: [B, D, N] fp32 in/out.  Supported: 1 <= N <= 64. */
+lr_status lr_selective_step(lr_dtype io, lr_disc disc, int64_t B, int64_t D,
+                            int64_t N, const void* x, const void* dt,
+                            const float* A, const void* Bm, const void* Cm,
+                            const float* Dskip, float* h, void* y,
+                            void* stream);
+
+/* One token of lr_ssd_scan.
+ *   x, y: [B, H, P] io    dt: [B, H] io    Bm, Cm: [B, G, N] io
+ *   A: [H]    Dskip: [H] or NULL    h: [B, H, P, N] fp32 in/out.
+ * Supported: io = LR_BF16; N in {64, 128}; H % G == 0. */
+lr_status lr_ssd_step(lr_dtype io, lr_disc disc, int64_t B, int64_t H,
+                      int64_t P, int64_t G, int64_t N, const void* x,
+                      const void* dt, const float* A, const void* Bm,
+                      const void* Cm, const float* Dskip, float* h, void* y,
+                      void* stream);
+
+/* One token of lr_gla_scan.
+ *   q, k: [B, H, K] io    v, o: [B, H, V] io    g: [B, H] io
+ *   S: [B, H, K, V] fp32 in/out.  Supported: io = LR_BF16; V % 64 == 0. */
+lr_status lr_gla_step(lr_dtype io, int64_t B, int64_t H, int64_t K, int64_t V,
+                      const void* q, const void* k, const void* v,
+                      const void* g, float* S, void* o, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -16,7 +16,8 @@ from ._lib import (LR_BF16, LR_DISC_EULER, LR_DISC_ZOH, LR_F32, LrError,  # noqa
 __all__ = ["lr_diag_scan", "lr_diag_scan_bwd", "lr_selective_scan", "lr_selective_scan_bwd",
            "lr_selective_scan_bwd_workspace_bytes", "lr_ssd_scan", "lr_ssd_scan_bwd",
            "lr_ssd_scan_bwd_workspace_bytes", "lr_gla_scan", "lr_gla_scan_bwd",
-           "lr_gla_scan_bwd_workspace_bytes", "lr_version", "LrError"]
+           "lr_gla_scan_bwd_workspace_bytes", "lr_diag_step", "lr_selective_step", "lr_ssd_step",
+           "lr_gla_step", "lr_version", "LrError"]
 
 _DISC = {"zoh": LR_DISC_ZOH, "euler": LR_DISC_EULER}
 
@@ -212,3 +213,52 @@ def lr_gla_scan_bwd(q, k, v, g, ckpt, dout, dS_last=None, chunk=64, seg=64, work
         _ptr(dout), _f32(dS_last, "dS_last"), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg),
         _f32(dS0, "dS0"), _ptr(workspace), workspace.numel(), _stream(q)))
     return dict(dq=dq, dk=dk, dv=dv, dg=dg, dS0=dS0)
+
+
+# ------------------------------------------------------------------ steps
+def lr_diag_step(a, b, h, out=None):
+    """h <- a h + b in place (h fp32 [B, D]); returns out = h in a's dtype."""
+    B, D = a.shape
+    if out is None:
+        out = torch.empty_like(a)
+    check("lr_diag_step", lib().lr_diag_step(_io(a), B, D, _ptr(a), _ptr(b), _f32(h, "h"),
+                                             _ptr(out), _stream(a)))
+    return out
+
+
+def lr_selective_step(x, dt, A, Bm, Cm, Dskip, h, disc="zoh", y=None):
+    """One token of lr_selective_scan; x, dt: [B, D]; Bm, Cm: [B, N]; h fp32
+    [B, D, N] updated in place.  Returns y [B, D]."""
+    B, D = x.shape
+    N = A.shape[1]
+    if y is None:
+        y = torch.empty_like(x)
+    check("lr_selective_step", lib().lr_selective_step(
+        _io(x), _DISC[disc], B, D, N, _ptr(x), _ptr(dt), _f32(A, "A"), _ptr(Bm), _ptr(Cm),
+        _f32(Dskip, "Dskip"), _f32(h, "h"), _ptr(y), _stream(x)))
+    return y
+
+
+def lr_ssd_step(x, dt, A, Bm, Cm, Dskip, h, disc="zoh", y=None):
+    """One token of lr_ssd_scan; x: [B, H, P]; dt: [B, H]; Bm, Cm: [B, G, N];
+    h fp32 [B, H, P, N] updated in place.  Returns y [B, H, P]."""
+    B, H, P = x.shape
+    G, N = Bm.shape[1], Bm.shape[2]
+    if y is None:
+        y = torch.empty_like(x)
+    check("lr_ssd_step", lib().lr_ssd_step(
+        _io(x), _DISC[disc], B, H, P, G, N, _ptr(x), _ptr(dt), _f32(A, "A"), _ptr(Bm), _ptr(Cm),
+        _f32(Dskip, "Dskip"), _f32(h, "h"), _ptr(y), _stream(x)))
+    return y
+
+
+def lr_gla_step(q, k, v, g, S, o=None):
+    """One token of lr_gla_scan; q, k: [B, H, K]; v: [B, H, V]; g: [B, H];
+    S fp32 [B, H, K, V] updated in place.  Returns o [B, H, V]."""
+    B, H, K = q.shape
+    V = v.shape[2]
+    if o is None:
+        o = torch.empty_like(v)
+    check("lr_gla_step", lib().lr_gla_step(_io(q), B, H, K, V, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                           _f32(S, "S"), _ptr(o), _stream(q)))
+    return o

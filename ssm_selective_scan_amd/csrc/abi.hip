@@ -58,6 +58,18 @@ hipError_t launch_ssd_bwd(int disc, const void* x, const void* dt, const float* 
                           void* dCm, float* dD, float* dh0, void* ws, int64_t B, int64_t L,
                           int64_t H, int64_t P, int64_t G, int64_t N, int64_t seg,
                           hipStream_t stream);
+template <typename T>
+hipError_t launch_diag_step(const void* a, const void* b, float* h, void* out, int64_t n,
+                            hipStream_t s);
+template <typename T>
+hipError_t launch_selective_step(int disc, const void* x, const void* dt, const float* A,
+                                 const void* Bm, const void* Cm, const float* Dskip, float* h,
+                                 void* y, int64_t B, int64_t D, int N, hipStream_t s);
+hipError_t launch_ssd_step(int disc, const void* x, const void* dt, const float* A, const void* Bm,
+                           const void* Cm, const float* Dskip, float* h, void* y, int64_t B,
+                           int64_t H, int64_t P, int64_t G, int64_t N, hipStream_t s);
+hipError_t launch_gla_step(const void* q, const void* k, const void* v, const void* g, float* S,
+                           void* o, int64_t B, int64_t H, int64_t K, int64_t V, hipStream_t s);
 }  // namespace lr
 
 namespace {
@@ -352,6 +364,70 @@ lr_status lr_gla_scan_bwd(lr_dtype io, int64_t B, int64_t L, int64_t H, int64_t 
   return hip_status(lr::launch_gla_bwd(q, k, v, g, ckpt, dout, dS_last, dq, dk, dv, dg, dS0,
                                        workspace, B, L, H, K, V, seg,
                                        static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------- steps
+lr_status lr_diag_step(lr_dtype io, int64_t B, int64_t D, const void* a, const void* b, float* h,
+                       void* out, void* stream) {
+  if (!valid_io(io)) return LR_E_DTYPE;
+  if (B < 0 || D < 1) return LR_E_SHAPE;
+  if (!elems_ok({B, D}) || (B * D + 255) / 256 > kMaxGrid) return LR_E_OVERFLOW;
+  if (B > 0 && any_null({a, b, h})) return LR_E_NULLPTR;
+  if (!all_aligned({a, b, h, out})) return LR_E_ALIGN;
+  if (B == 0) return LR_OK;
+  auto s = static_cast<hipStream_t>(stream);
+  return hip_status(io == LR_F32 ? lr::launch_diag_step<float>(a, b, h, out, B * D, s)
+                                 : lr::launch_diag_step<uint16_t>(a, b, h, out, B * D, s));
+}
+
+lr_status lr_selective_step(lr_dtype io, lr_disc disc, int64_t B, int64_t D, int64_t N,
+                            const void* x, const void* dt, const float* A, const void* Bm,
+                            const void* Cm, const float* Dskip, float* h, void* y, void* stream) {
+  if (!valid_io(io) || !valid_disc(disc)) return LR_E_DTYPE;
+  if (B < 0 || D < 1 || N < 1) return LR_E_SHAPE;
+  if (N > 64) return LR_E_UNSUPPORTED;
+  if (!elems_ok({B, D, 64}) || (B * D * 64 + 255) / 256 > kMaxGrid) return LR_E_OVERFLOW;
+  if (A == nullptr) return LR_E_NULLPTR;
+  if (B > 0 && any_null({x, dt, Bm, Cm, h, y})) return LR_E_NULLPTR;
+  if (!all_aligned({x, dt, A, Bm, Cm, Dskip, h, y})) return LR_E_ALIGN;
+  if (B == 0) return LR_OK;
+  auto s = static_cast<hipStream_t>(stream);
+  const int n = static_cast<int>(N);
+  return hip_status(io == LR_F32
+                        ? lr::launch_selective_step<float>(disc, x, dt, A, Bm, Cm, Dskip, h, y, B, D, n, s)
+                        : lr::launch_selective_step<uint16_t>(disc, x, dt, A, Bm, Cm, Dskip, h, y, B, D, n, s));
+}
+
+lr_status lr_ssd_step(lr_dtype io, lr_disc disc, int64_t B, int64_t H, int64_t P, int64_t G,
+                      int64_t N, const void* x, const void* dt, const float* A, const void* Bm,
+                      const void* Cm, const float* Dskip, float* h, void* y, void* stream) {
+  if (!valid_io(io) || !valid_disc(disc)) return LR_E_DTYPE;
+  if (B < 0 || H < 1 || P < 1 || G < 1 || N < 1 || H % G != 0) return LR_E_SHAPE;
+  if (io != LR_BF16 || (N != 64 && N != 128)) return LR_E_UNSUPPORTED;
+  if (!elems_ok({B, H, P, N}) || (B * H * P * 4 + 255) / 256 > kMaxGrid) return LR_E_OVERFLOW;
+  if (A == nullptr) return LR_E_NULLPTR;
+  if (B > 0 && any_null({x, dt, Bm, Cm, h, y})) return LR_E_NULLPTR;
+  if (!all_aligned({x, dt, A, Bm, Cm, Dskip, h, y})) return LR_E_ALIGN;
+  if (B == 0) return LR_OK;
+  return hip_status(lr::launch_ssd_step(disc, x, dt, A, Bm, Cm, Dskip, h, y, B, H, P, G, N,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+lr_status lr_gla_step(lr_dtype io, int64_t B, int64_t H, int64_t K, int64_t V, const void* q,
+                      const void* k, const void* v, const void* g, float* S, void* o,
+                      void* stream) {
+  if (!valid_io(io)) return LR_E_DTYPE;
+  if (B < 0 || H < 1 || K < 1 || V < 1) return LR_E_SHAPE;
+  if (io != LR_BF16 || V % 64 != 0) return LR_E_UNSUPPORTED;
+  if (!elems_ok({B, H, K, V})) return LR_E_OVERFLOW;
+  int64_t nwg = 1;
+  if (!mul_ok(nwg, B) || !mul_ok(nwg, H) || !mul_ok(nwg, V / 64) || nwg > kMaxGrid)
+    return LR_E_OVERFLOW;
+  if (B > 0 && any_null({q, k, v, g, S, o})) return LR_E_NULLPTR;
+  if (!all_aligned({q, k, v, g, S, o})) return LR_E_ALIGN;
+  if (B == 0) return LR_OK;
+  return hip_status(lr::launch_gla_step(q, k, v, g, S, o, B, H, K, V,
+                                        static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -183,3 +183,28 @@ def test_gla_bwd_validation(L):
     assert L.lr_gla_scan_bwd(*bad, P, ws, None) == ALIGN
     assert L.lr_gla_scan_bwd(*args, P, ws - 256, None) == WS
     assert L.lr_gla_scan_bwd(*args, None, ws, None) == WS
+
+
+def test_step_validation(L):
+    assert L.lr_diag_step(4, 1, 8, P, P, P, None, None) == DTYPE
+    assert L.lr_diag_step(0, 1, 0, P, P, P, None, None) == SHAPE
+    assert L.lr_diag_step(0, 1, 8, P, None, P, None, None) == NULL
+    assert L.lr_diag_step(0, 1, 8, P, P, MIS, None, None) == ALIGN
+    assert L.lr_diag_step(0, 0, 8, None, None, None, None, None) == OK
+    sel = lambda io=0, disc=0, N=16, h=P: L.lr_selective_step(io, disc, 1, 8, N, P, P, P, P, P,
+                                                              None, h, P, None)
+    assert sel(disc=5) == DTYPE
+    assert sel(N=65) == UNSUP
+    assert sel(h=None) == NULL
+    assert sel(h=MIS) == ALIGN
+    ssd = lambda io=1, N=128, G=1, H=4, h=P: L.lr_ssd_step(io, 0, 1, H, 64, G, N, P, P, P, P, P,
+                                                           None, h, P, None)
+    assert ssd(io=0) == UNSUP
+    assert ssd(N=96) == UNSUP
+    assert ssd(G=3) == SHAPE
+    assert ssd(h=None) == NULL
+    gla = lambda io=1, V=128, S=P: L.lr_gla_step(io, 1, 2, 128, V, P, P, P, P, S, P, None)
+    assert gla(V=100) == UNSUP
+    assert gla(io=0) == UNSUP
+    assert gla(S=None) == NULL
+    assert gla(S=MIS) == ALIGN
