@@ -261,6 +261,65 @@ def measure_gla_bwd(warmup, iters):
                 bwd_workspace_bytes=ws.numel())
 
 
+def measure_decode(warmup, iters, T=64):
+    """Decode: T single-token steps captured in one HIP graph, for the SSD,
+    GLA and Mamba-1 state shapes of the prefill workloads.  Reports the time
+    per step (graph replay / T), batch tokens/s and the state bytes moved
+    (read + write of the fp32 state) per second."""
+    out = {}
+    gs = lrgen.make(3, L=T)
+    ps = gs.params
+    B, H, P, N = ps["B"], ps["H"], ps["P"], ps["N"]
+    X = {k: dev(gs.t(k)) for k in ("x", "dt", "B", "C")}
+    A, Dk = dev(gs.t("A")), dev(gs.t("Dskip"))
+    steps_ssd = [tuple(X[k][:, t].contiguous() for k in ("x", "dt", "B", "C")) for t in range(T)]
+    h = torch.zeros(B, H, P, N, device="cuda")
+    ys = [torch.empty(B, H, P, device="cuda", dtype=torch.bfloat16) for _ in range(T)]
+    ssd_loop = lambda: [lr.lr_ssd_step(x, d, A, b, c, Dk, h, y=ys[t])
+                        for t, (x, d, b, c) in enumerate(steps_ssd)]
+
+    gg = lrgen.make(4, L=T)
+    pg = gg.params
+    Bg, Hg, K, V = pg["B"], pg["H"], pg["K"], pg["V"]
+    Y = {k: dev(gg.t(k)) for k in ("q", "k", "v", "g")}
+    steps_gla = [tuple(Y[k][:, t].contiguous() for k in ("q", "k", "v", "g")) for t in range(T)]
+    S = torch.zeros(Bg, Hg, K, V, device="cuda")
+    os_ = [torch.empty(Bg, Hg, V, device="cuda", dtype=torch.bfloat16) for _ in range(T)]
+    gla_loop = lambda: [lr.lr_gla_step(q, k, v, g_, S, o=os_[t])
+                        for t, (q, k, v, g_) in enumerate(steps_gla)]
+
+    gm = lrgen.make(2, L=T)
+    pm = gm.params
+    Bm_, D, Nm = pm["B"], pm["D"], pm["N"]
+    Z = {k: dev(gm.t(k)) for k in ("x", "dt", "B", "C")}
+    Am, Dm = dev(gm.t("A")), dev(gm.t("Dskip"))
+    steps_sel = [tuple(Z[k][:, t].contiguous() for k in ("x", "dt", "B", "C")) for t in range(T)]
+    hm = torch.zeros(Bm_, D, Nm, device="cuda")
+    yms = [torch.empty(Bm_, D, device="cuda", dtype=torch.bfloat16) for _ in range(T)]
+    sel_loop = lambda: [lr.lr_selective_step(x, d, Am, b, c, Dm, hm, y=yms[t])
+                        for t, (x, d, b, c) in enumerate(steps_sel)]
+
+    for name, loop, batch, state_bytes in (
+            ("ssd", ssd_loop, B, h.numel() * 4), ("gla", gla_loop, Bg, S.numel() * 4),
+            ("selective", sel_loop, Bm_, hm.numel() * 4)):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            loop()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            loop()
+        t, _ = time_launches(lambda s: graph.replay(), [None], warmup, iters)
+        ts = t / T
+        out[name] = dict(steps_per_graph=T, us_per_step=ts * 1e6, tokens_per_s=batch / ts,
+                         state_bytes=state_bytes, state_GBs=2 * state_bytes / ts / 1e9,
+                         state_hbm_frac=2 * state_bytes / ts / 1e9 / HBM_PEAK_GBS)
+        del graph
+    return out
+
+
 def copy_bandwidth(nbytes=1 << 30, iters=10):
     a = torch.empty(nbytes // 4, device="cuda", dtype=torch.float32).fill_(1.0)
     b = torch.empty_like(a)
@@ -308,7 +367,8 @@ def load_traffic():
 
 SECONDARY = {"diag": measure_diag, "ssd": measure_ssd, "gla": measure_gla,
              "ssd_fwd_bwd": measure_ssd_bwd, "diag_bwd": measure_diag_bwd,
-             "selective_fwd_bwd": measure_selective_bwd, "gla_fwd_bwd": measure_gla_bwd}
+             "selective_fwd_bwd": measure_selective_bwd, "gla_fwd_bwd": measure_gla_bwd,
+             "decode": measure_decode}
 
 
 def main():
