@@ -101,18 +101,27 @@ def diag_scan_bwd(a, h, dh, h0=None, dh_last=None):
 # Discretisation  [LX, Key Contributions 2-3: ZOH]
 # ---------------------------------------------------------------------------
 def discretize(dt, A, disc="zoh"):
-    """Return (e, phi) with e = exp(dt*A) and
-    zoh:   phi = expm1(dt*A) / A   (phi = dt where A == 0)
-    euler: phi = dt
+    """Return (e, phi): the decay e and the input factor phi of one step, so
+    that h <- e h + phi B x.  With l = dt*A:
+    zoh:      e = exp(l),                phi = expm1(l) / A  (phi = dt at A = 0)
+    euler:    e = exp(l),                phi = dt
+    bilinear: e = (1 + l/2) / (1 - l/2), phi = dt / (1 - l/2)   (Tustin)
+    dirac:    e = exp(l),                phi = 1   (the input is an impulse of
+              area x at the sample: the state jumps by B x, no dt factor)
     ``dt`` and ``A`` broadcast against each other."""
     dt, A = np.broadcast_arrays(_f(dt), _f(A))
     lam = dt * A
+    if disc == "bilinear":
+        den = 1.0 - 0.5 * lam
+        return (1.0 + 0.5 * lam) / den, dt / den
     e = np.exp(lam)
     if disc == "zoh":
         safe = np.where(A == 0.0, 1.0, A)
         phi = np.where(A == 0.0, dt, np.expm1(lam) / safe)
     elif disc == "euler":
         phi = dt.copy()
+    elif disc == "dirac":
+        phi = np.ones_like(dt)
     else:
         raise ValueError(disc)
     return e, phi
@@ -122,8 +131,13 @@ def discretize_grads(dt, A, e, phi, disc="zoh"):
     """Partial derivatives (de/ddt, de/dA, dphi/ddt, dphi/dA).
 
     zoh: dphi/dA = (dt*e - phi)/A, evaluated as dt^2 (1/2 + l/3 + l^2/8 +
-    l^3/30) for |l| = |dt*A| < 1e-3 to avoid cancellation."""
+    l^3/30) for |l| = |dt*A| < 1e-3 to avoid cancellation.
+    bilinear: with den = 1 - l/2, de/dl = 1/den^2, dphi/ddt = 1/den^2 and
+    dphi/dA = dt^2 / (2 den^2)."""
     dt, A = np.broadcast_arrays(_f(dt), _f(A))
+    if disc == "bilinear":
+        den2 = (1.0 - 0.5 * dt * A) ** 2
+        return A / den2, dt / den2, 1.0 / den2, dt * dt / (2.0 * den2)
     de_ddt = A * e
     de_dA = dt * e
     if disc == "zoh":
@@ -134,14 +148,15 @@ def discretize_grads(dt, A, e, phi, disc="zoh"):
         series = dt * dt * (0.5 + lam / 3.0 + lam * lam / 8.0 + lam ** 3 / 30.0)
         dphi_ddt = e
         dphi_dA = np.where(small, series, direct)
-    else:
+    elif disc == "euler":
         dphi_ddt = np.ones_like(dt)
+        dphi_dA = np.zeros_like(dt)
+    else:  # dirac
+        dphi_ddt = np.zeros_like(dt)
         dphi_dA = np.zeros_like(dt)
     return de_ddt, de_dA, dphi_ddt, dphi_dA
 
 
-# ---------------------------------------------------------------------------
-# Mamba-1 selective scan with fused readout  [LX, Key Contributions 3]
 # ---------------------------------------------------------------------------
 def selective_scan(x, dt, A, Bm, Cm, Dskip=None, h0=None, disc="zoh"):
     """x, dt: [B, L, D]; A: [D, N]; Bm, Cm: [B, L, N]; Dskip: [D]; h0: [B, D, N].

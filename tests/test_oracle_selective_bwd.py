@@ -38,6 +38,11 @@ def _torch_grads(x, dt, A, Bm, Cm, Dk, h0, dy, dhl, disc):
             ser = 1 + lam / 2 + lam ** 2 / 6 + lam ** 3 / 24 + lam ** 4 / 120
             q = torch.where(lam.abs() < 1e-3, ser, torch.expm1(lam) / torch.where(lam == 0, 1.0, lam))
             phi = tdt[:, t, :, None] * q
+        elif disc == "bilinear":
+            e = (1 + lam / 2) / (1 - lam / 2)
+            phi = tdt[:, t, :, None] / (1 - lam / 2)
+        elif disc == "dirac":
+            phi = torch.ones_like(lam)
         else:
             phi = tdt[:, t, :, None].expand_as(lam)
         th = e * th + phi * tB[:, t, None, :] * tx[:, t, :, None]
@@ -48,7 +53,7 @@ def _torch_grads(x, dt, A, Bm, Cm, Dk, h0, dy, dhl, disc):
     return [t.grad.numpy() for t in T]
 
 
-@pytest.mark.parametrize("disc", ["zoh", "euler"])
+@pytest.mark.parametrize("disc", ["zoh", "euler", "bilinear", "dirac"])
 @pytest.mark.parametrize("zero_A", [False, True])
 def test_matches_autograd(disc, zero_A):
     c = _case(0, zero_A=zero_A)
