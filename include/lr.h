@@ -46,11 +46,17 @@ extern "C" {
 typedef enum { LR_F32 = 0, LR_BF16 = 1 } lr_dtype;
 
 /* Discretisation of a continuous-time decay A over a step dt ("lrnnx: A
- * library for Linear RNNs", Key Contributions 2, which names ZOH among the
- * supported schemes; the pages give no formula).  Reading used here:
- *   LR_DISC_ZOH:   abar = exp(dt*A), bbar = expm1(dt*A)/A * B   (= dt*B at A=0)
- *   LR_DISC_EULER: abar = exp(dt*A), bbar = dt * B                            */
-typedef enum { LR_DISC_ZOH = 0, LR_DISC_EULER = 1 } lr_disc;
+ * library for Linear RNNs", Key Contributions 2-3, which name ZOH, bilinear
+ * and dirac among the schemes of its fused kernels; the pages give no
+ * formulas).  Readings used here, with l = dt*A:
+ *   LR_DISC_ZOH:      abar = exp(l),                bbar = expm1(l)/A * B  (= dt*B at A=0)
+ *   LR_DISC_EULER:    abar = exp(l),                bbar = dt * B
+ *   LR_DISC_BILINEAR: abar = (1 + l/2) / (1 - l/2), bbar = dt / (1 - l/2) * B  (Tustin)
+ *   LR_DISC_DIRAC:    abar = exp(l),                bbar = B  (the input is an
+ *                     impulse of area x at the sample: no dt factor)           */
+typedef enum {
+  LR_DISC_ZOH = 0, LR_DISC_EULER = 1, LR_DISC_BILINEAR = 2, LR_DISC_DIRAC = 3
+} lr_disc;
 
 typedef enum {
   LR_OK = 0,
@@ -195,7 +201,8 @@ size_t lr_ssd_scan_bwd_workspace_bytes(int64_t B, int64_t L, int64_t H,
  *   dBm, dCm: [B, L, G, N] io (summed over the heads of each group)
  *   dA: [H] fp32    dD: [H] fp32 or NULL    dh0: [B, H, P, N] fp32 or NULL
  *   workspace: device memory of at least lr_ssd_scan_bwd_workspace_bytes().
- * Supported: as lr_ssd_scan, with P == 64 and seg in {64, 128, 192, 256}.
+ * Supported: as lr_ssd_scan, with P == 64, seg in {64, 128, 192, 256} and
+ * disc in {ZOH, EULER, DIRAC}.
  * ------------------------------------------------------------------------- */
 lr_status lr_ssd_scan_bwd(lr_dtype io, lr_disc disc, int64_t B, int64_t L,
                           int64_t H, int64_t P, int64_t G, int64_t N,

@@ -10,8 +10,8 @@ from __future__ import annotations
 
 import torch
 
-from ._lib import (LR_BF16, LR_DISC_EULER, LR_DISC_ZOH, LR_F32, LrError,  # noqa: F401
-                   check, lib)
+from ._lib import (LR_BF16, LR_DISC_BILINEAR, LR_DISC_DIRAC, LR_DISC_EULER,  # noqa: F401
+                   LR_DISC_ZOH, LR_F32, LrError, check, lib)
 
 __all__ = ["lr_diag_scan", "lr_diag_scan_bwd", "lr_selective_scan", "lr_selective_scan_bwd",
            "lr_selective_scan_bwd_workspace_bytes", "lr_ssd_scan", "lr_ssd_scan_bwd",
@@ -19,7 +19,8 @@ __all__ = ["lr_diag_scan", "lr_diag_scan_bwd", "lr_selective_scan", "lr_selectiv
            "lr_gla_scan_bwd_workspace_bytes", "lr_diag_step", "lr_selective_step", "lr_ssd_step",
            "lr_gla_step", "lr_version", "LrError"]
 
-_DISC = {"zoh": LR_DISC_ZOH, "euler": LR_DISC_EULER}
+_DISC = {"zoh": LR_DISC_ZOH, "euler": LR_DISC_EULER, "bilinear": LR_DISC_BILINEAR,
+         "dirac": LR_DISC_DIRAC}
 
 
 def _io(t: torch.Tensor) -> int:

@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(PKG, "liblr.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "lr.h")
 
 LR_F32, LR_BF16 = 0, 1
-LR_DISC_ZOH, LR_DISC_EULER = 0, 1
+LR_DISC_ZOH, LR_DISC_EULER, LR_DISC_BILINEAR, LR_DISC_DIRAC = 0, 1, 2, 3
 STATUS = {0: "LR_OK", 1: "LR_E_NULLPTR", 2: "LR_E_SHAPE", 3: "LR_E_DTYPE", 4: "LR_E_ALIGN",
           5: "LR_E_UNSUPPORTED", 6: "LR_E_WORKSPACE", 7: "LR_E_OVERFLOW", 8: "LR_E_HIP"}
 

@@ -109,7 +109,9 @@ bool any_null(std::initializer_list<const void*> ps) {
 lr_status hip_status(hipError_t e) { return e == hipSuccess ? LR_OK : LR_E_HIP; }
 
 bool valid_io(int io) { return io == LR_F32 || io == LR_BF16; }
-bool valid_disc(int d) { return d == LR_DISC_ZOH || d == LR_DISC_EULER; }
+bool valid_disc(int d) {
+  return d == LR_DISC_ZOH || d == LR_DISC_EULER || d == LR_DISC_BILINEAR || d == LR_DISC_DIRAC;
+}
 
 // Checks shared by the SSD forward and backward.
 lr_status check_ssd_sizes(int io, int disc, int64_t B, int64_t L, int64_t H, int64_t P, int64_t G,
@@ -284,7 +286,7 @@ lr_status lr_ssd_scan_bwd(lr_dtype io, lr_disc disc, int64_t B, int64_t L, int64
   lr_status st = check_ssd_sizes(io, disc, B, L, H, P, G, N, chunk, seg);
   if (st != LR_OK) return st;
   if (seg < 1) return LR_E_SHAPE;
-  if (!lr::ssd_bwd_supported(P, N, seg)) return LR_E_UNSUPPORTED;
+  if (!lr::ssd_bwd_supported(P, N, seg) || disc == LR_DISC_BILINEAR) return LR_E_UNSUPPORTED;
   if (A == nullptr || dA == nullptr) return LR_E_NULLPTR;
   if (B * L > 0 && any_null({x, dt, Bm, Cm, ckpt, dy, dx, ddt, dBm, dCm})) return LR_E_NULLPTR;
   if (!all_aligned({x, dt, A, Bm, Cm, Dskip, h0, ckpt, dy, dh_last, dx, ddt, dA, dBm, dCm, dD,

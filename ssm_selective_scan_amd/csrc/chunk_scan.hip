@@ -40,7 +40,7 @@ constexpr int kCQ = 64;        // tokens per block
 constexpr int kCPS = 64;       // p columns per workgroup
 constexpr int kLdM = kCQ + 8;  // pitch of M[t][s] (36 words: conflict-free 16-byte reads)
 
-enum { kModeSsdZoh = 0, kModeSsdEuler = 1, kModeGla = 2 };
+enum { kModeSsdZoh = 0, kModeSsdEuler = 1, kModeGla = 2, kModeSsdBilinear = 3, kModeSsdDirac = 4 };
 
 struct ChunkFwdArgs {
   const uint16_t* x;    // SSD x / GLA v      [B, L, H, P]
@@ -74,14 +74,29 @@ struct ChunkBuf {
   uint16_t Xw[kCQ * kLdX];     // 2^(cum_end - cum_s) phi_s x[s][p]
   float cum[kCQ];
   float phi[kCQ];
+  float sg[kCQ];               // bilinear only: sign of the decay product up to t
 };
 
-// Per-token log2-decay and input scale of one token.
+// Per-token log2-decay, input scale and (bilinear only) decay of one token.
+// The bilinear decay (1 + l/2)/(1 - l/2) is negative for l < -2: its
+// magnitude goes into the log2 sum and its sign into a parity scan.
 template <int MODE>
-__device__ __forceinline__ void chunk_scalars(uint16_t graw, bool ok, float Ah, float& l2, float& ph) {
+__device__ __forceinline__ void chunk_scalars(uint16_t graw, bool ok, float Ah, float& l2, float& ph,
+                                              float& ad) {
+  ad = 1.f;
   if (MODE == kModeGla) {
     const float gv = ok ? bf2f(graw) : 1.f;
     l2 = fast_log2(gv);
+    ph = ok ? 1.f : 0.f;
+  } else if (MODE == kModeSsdBilinear) {
+    const float dtv = ok ? bf2f(graw) : 0.f;
+    const float r = __builtin_amdgcn_rcpf(1.f - 0.5f * dtv * Ah);
+    ad = (1.f + 0.5f * dtv * Ah) * r;
+    l2 = fmaxf(fast_log2(fabsf(ad)), -126.f);
+    ph = dtv * r;
+  } else if (MODE == kModeSsdDirac) {
+    const float dtv = ok ? bf2f(graw) : 0.f;
+    l2 = dtv * Ah * kLog2e;
     ph = ok ? 1.f : 0.f;
   } else {
     const float dtv = ok ? bf2f(graw) : 0.f;
@@ -205,14 +220,22 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkFwdArgs g) {
   auto stage = [&](int64_t blk, ChunkBuf<NS>& bf) {
     const int64_t t0 = blk * kCQ;
     const int nv = static_cast<int>((g.L - t0) < kCQ ? (g.L - t0) : kCQ);
-    float l2, ph;
-    chunk_scalars<MODE>(greg, lane < nv, Ah, l2, ph);
+    float l2, ph, ad;
+    chunk_scalars<MODE>(greg, lane < nv, Ah, l2, ph, ad);
     const float c = wave_incl_sum(l2);
     const float cend = __shfl(c, 63);
-    const float wsc = fast_exp2(cend - c) * ph;      // weight of token `lane` in the state update
+    float sgc = 1.f, sge = 1.f;
+    if constexpr (MODE == kModeSsdBilinear) {
+      const float nneg = wave_incl_sum(ad < 0.f ? 1.f : 0.f);
+      sgc = (static_cast<int>(nneg) & 1) ? -1.f : 1.f;
+      sge = __shfl(sgc, 63);
+    }
+    // weight of token `lane` in the state update
+    const float wsc = fast_exp2(cend - c) * ph * (sgc * sge);
     if (w == 0) {
       bf.cum[lane] = c;
       bf.phi[lane] = ph;
+      bf.sg[lane] = sgc;
     }
 #pragma unroll
     for (int k = 0; k < kCB; ++k) {
@@ -286,6 +309,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkFwdArgs g) {
           for (int r = 0; r < 4; ++r) {
             const int sr = s0 + r;
             float m = (sr <= t) ? z[r] * fast_exp2(ct - cur.cum[sr]) * cur.phi[sr] : 0.f;
+            if (MODE == kModeSsdBilinear) m *= cur.sg[t] * cur.sg[sr];
             if (sr == t) m += Dh;   // D x_t folded into the diagonal
             out[r] = f2bf(m);
           }
@@ -308,7 +332,10 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkFwdArgs g) {
         yacc[ti] = mfma16x16x32(hb, lds_tile_perm(cur.Cs, kLdC, 16 * ti, 32 * kk, lane), yacc[ti]);
     }
 #pragma unroll
-    for (int ti = 0; ti < 4; ++ti) yacc[ti] *= fast_exp2(cur.cum[16 * ti + c16]);
+    for (int ti = 0; ti < 4; ++ti) {
+      const int t = 16 * ti + c16;
+      yacc[ti] *= (MODE == kModeSsdBilinear) ? fast_exp2(cur.cum[t]) * cur.sg[t] : fast_exp2(cur.cum[t]);
+    }
     {
       const bf16x8 x0 = lds_tile_tr(cur.Xs, kLdX, 0, 16 * w, lane);
       const bf16x8 x1 = lds_tile_tr(cur.Xs, kLdX, 32, 16 * w, lane);
@@ -331,7 +358,8 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkFwdArgs g) {
 
     // ---- h_next = 2^cum_end h_prev + B^T (decay-weighted x)
     {
-      const float dec = fast_exp2(cur.cum[kCQ - 1]);
+      const float dec = (MODE == kModeSsdBilinear) ? fast_exp2(cur.cum[kCQ - 1]) * cur.sg[kCQ - 1]
+                                                   : fast_exp2(cur.cum[kCQ - 1]);
       const bf16x8 xw0 = lds_tile_tr(cur.Xw, kLdX, 0, 16 * w, lane);
       const bf16x8 xw1 = lds_tile_tr(cur.Xw, kLdX, 32, 16 * w, lane);
 #pragma unroll
@@ -381,10 +409,20 @@ hipError_t launch_ssd_fwd(int disc, const void* x, const void* dt, const float* 
   a.B = B; a.L = L; a.H = H; a.P = P; a.G = G; a.seg = seg > 0 ? seg : 1;
   a.bc_row = G * N;
   a.st_p = N; a.st_n = 1;
-  if (N == 128) return disc == 1 ? launch_chunk<kModeSsdEuler, 128>(a, stream)
-                                 : launch_chunk<kModeSsdZoh, 128>(a, stream);
-  return disc == 1 ? launch_chunk<kModeSsdEuler, 64>(a, stream)
-                   : launch_chunk<kModeSsdZoh, 64>(a, stream);
+  if (N == 128) {
+    switch (disc) {
+      case 1: return launch_chunk<kModeSsdEuler, 128>(a, stream);
+      case 2: return launch_chunk<kModeSsdBilinear, 128>(a, stream);
+      case 3: return launch_chunk<kModeSsdDirac, 128>(a, stream);
+      default: return launch_chunk<kModeSsdZoh, 128>(a, stream);
+    }
+  }
+  switch (disc) {
+    case 1: return launch_chunk<kModeSsdEuler, 64>(a, stream);
+    case 2: return launch_chunk<kModeSsdBilinear, 64>(a, stream);
+    case 3: return launch_chunk<kModeSsdDirac, 64>(a, stream);
+    default: return launch_chunk<kModeSsdZoh, 64>(a, stream);
+  }
 }
 
 hipError_t launch_gla_fwd(const void* q, const void* k, const void* v, const void* gate,

@@ -34,7 +34,7 @@ constexpr int kSbNW = 8;      // waves (2 state indices each: N <= 16)
 constexpr int kSbSub = 16;    // chunks per segment (seg <= 256)
 constexpr int kSbCT = 64;     // channels per workgroup
 
-enum { kSbZoh = 0, kSbEuler = 1 };
+enum { kSbZoh = 0, kSbEuler = 1, kSbBilinear = 2, kSbDirac = 3 };
 
 struct SelBwdArgs {
   const void* x; const void* dt; const float* A; const void* Bm; const void* Cm;
@@ -49,13 +49,22 @@ struct SelBwdArgs {
 
 // e, phi and their derivatives for one (dt, A).  ZOH: phi = expm1(dt A) / A
 // through a series near dt A = 0 (A = 0 included); dphi/dA = (dt e - phi)/A,
-// also through its series there.
+// also through its series there.  Bilinear: e = (1 + l/2) r, phi = dt r with
+// r = 1 / (1 - l/2).  Dirac: phi = 1.
 template <int DISC>
 __device__ __forceinline__ void sb_disc(float dtv, float Av, float& e, float& phi) {
   const float lam = dtv * Av;
+  if (DISC == kSbBilinear) {
+    const float r = __builtin_amdgcn_rcpf(1.f - 0.5f * lam);
+    e = (1.f + 0.5f * lam) * r;
+    phi = dtv * r;
+    return;
+  }
   e = fast_exp2(lam * kLog2e);
   if (DISC == kSbEuler) {
     phi = dtv;
+  } else if (DISC == kSbDirac) {
+    phi = 1.f;
   } else {
     const float ser =
         dtv * fmaf(lam, fmaf(lam, fmaf(lam, fmaf(lam, 1.f / 120.f, 1.f / 24.f), 1.f / 6.f), 0.5f), 1.f);
@@ -63,13 +72,34 @@ __device__ __forceinline__ void sb_disc(float dtv, float Av, float& e, float& ph
   }
 }
 
+// (de/ddt, de/dA, dphi/ddt, dphi/dA) at (dt, A) with e, phi from sb_disc.
 template <int DISC>
-__device__ __forceinline__ float sb_dphi_dA(float dtv, float Av, float e, float phi) {
-  if (DISC == kSbEuler) return 0.f;
-  const float lam = dtv * Av;
-  const float ser = dtv * dtv *
-                    fmaf(lam, fmaf(lam, fmaf(lam, fmaf(lam, 1.f / 144.f, 1.f / 30.f), 1.f / 8.f), 1.f / 3.f), 0.5f);
-  return fabsf(lam) < 0.1f ? ser : (dtv * e - phi) / Av;
+__device__ __forceinline__ void sb_grads(float dtv, float Av, float e, float phi, float& dedt,
+                                         float& dedA, float& dpdt, float& dpdA) {
+  if (DISC == kSbBilinear) {
+    const float r = __builtin_amdgcn_rcpf(1.f - 0.5f * dtv * Av);
+    const float r2 = r * r;
+    dedt = Av * r2;
+    dedA = dtv * r2;
+    dpdt = r2;
+    dpdA = 0.5f * dtv * dtv * r2;
+    return;
+  }
+  dedt = Av * e;
+  dedA = dtv * e;
+  if (DISC == kSbEuler) {
+    dpdt = 1.f;
+    dpdA = 0.f;
+  } else if (DISC == kSbDirac) {
+    dpdt = 0.f;
+    dpdA = 0.f;
+  } else {
+    const float lam = dtv * Av;
+    const float ser = dtv * dtv *
+                      fmaf(lam, fmaf(lam, fmaf(lam, fmaf(lam, 1.f / 144.f, 1.f / 30.f), 1.f / 8.f), 1.f / 3.f), 0.5f);
+    dpdt = e;
+    dpdA = fabsf(lam) < 0.1f ? ser : (dtv * e - phi) / Av;
+  }
 }
 
 struct SbLds {
@@ -211,9 +241,10 @@ __global__ __launch_bounds__(512) void selective_bwd_kernel(SelBwdArgs a) {
           const float hp = i > 0 ? hs[i - 1][j] : hin[j];
           const float de = G[j] * hp;
           const float dphi = G[j] * Bv * xv;
-          const float dphidt = DISC == kSbEuler ? 1.f : e;
-          ddtp += fmaf(de * Av[j], e, dphi * dphidt);
-          dAacc[j] += fmaf(de * dtv, e, dphi * sb_dphi_dA<DISC>(dtv, Av[j], e, ph));
+          float dedt, dedA, dpdt, dpdA;
+          sb_grads<DISC>(dtv, Av[j], e, ph, dedt, dedA, dpdt, dpdA);
+          ddtp += fmaf(de, dedt, dphi * dpdt);
+          dAacc[j] += fmaf(de, dedA, dphi * dpdA);
           G[j] *= e;
         }
         // butterfly: lanes l, l^16, l^32, l^48 end with one of the four values
@@ -367,8 +398,19 @@ hipError_t launch_selective_bwd(int disc, const void* x, const void* dt, const f
   a.B = B; a.L = L; a.D = D; a.N = N; a.seg = seg; a.nseg = (L + seg - 1) / seg;
   a.ntile = (D + kSbCT - 1) / kSbCT;
   const dim3 grid(static_cast<unsigned>(B * a.ntile));
-  if (disc == kSbEuler) hipLaunchKernelGGL((selective_bwd_kernel<T, kSbEuler>), grid, dim3(512), 0, stream, a);
-  else hipLaunchKernelGGL((selective_bwd_kernel<T, kSbZoh>), grid, dim3(512), 0, stream, a);
+  switch (disc) {
+    case kSbEuler:
+      hipLaunchKernelGGL((selective_bwd_kernel<T, kSbEuler>), grid, dim3(512), 0, stream, a);
+      break;
+    case kSbBilinear:
+      hipLaunchKernelGGL((selective_bwd_kernel<T, kSbBilinear>), grid, dim3(512), 0, stream, a);
+      break;
+    case kSbDirac:
+      hipLaunchKernelGGL((selective_bwd_kernel<T, kSbDirac>), grid, dim3(512), 0, stream, a);
+      break;
+    default:
+      hipLaunchKernelGGL((selective_bwd_kernel<T, kSbZoh>), grid, dim3(512), 0, stream, a);
+  }
   const int64_t nred = B * L * N + D * N + D;
   hipLaunchKernelGGL(selective_bwd_reduce_kernel<T>, dim3((nred + 255) / 256), dim3(256), 0, stream, a);
   return hipGetLastError();

@@ -1,4 +1,5 @@
-// selective_scan.hip — Mamba-1 selective scan with ZOH/Euler discretisation
+// selective_scan.hip — Mamba-1 selective scan with ZOH, Euler, bilinear or
+// dirac discretisation
 // and the readout y = C.h + D.x fused into the scan (one launch).
 //
 // ("lrnnx: A library for Linear RNNs", Key Contributions 2-3: time-varying
@@ -22,13 +23,15 @@
 // |A| < 0.5 (including A = 0) switches, uniformly, to the precise form
 // phi = dt (1 + l/2 + l^2/6 + l^3/24) for |l| = |dt A| < 0.1, else
 // (e - 1)/A, which keeps phi accurate to fp32 rounding at every A.
+// Bilinear (Tustin): e = (1 + dt A/2) / (1 - dt A/2), phi = dt / (1 - dt A/2),
+// one v_rcp_f32 in place of the exponential; dirac: phi = 1.
 #include "common.hpp"
 
 namespace lr {
 
 constexpr int kSelCT = 64;     // channels per workgroup (one per lane)
 
-enum { kDiscZoh = 0, kDiscEuler = 1 };
+enum { kDiscZoh = 0, kDiscEuler = 1, kDiscBilinear = 2, kDiscDirac = 3 };
 
 // Register staging of one tile of TT tokens.  x and dt are moved in 8-channel
 // chunks (16-byte loads for bf16 when VEC, i.e. D % 8 == 0), B and C as the
@@ -164,13 +167,23 @@ struct SelGroup {
 #pragma unroll
     for (int i = 0; i < GS; ++i) {
       const float xt = xv[i], dtt = dv[i];
-      const float ux = (DISC == kDiscEuler) ? dtt * xt : 0.f;
+      const float ux = (DISC == kDiscEuler || DISC == kDiscBilinear) ? dtt * xt : 0.f;
       float yj[NPW];
 #pragma unroll
       for (int j = 0; j < NPW; ++j) {
+        if (DISC == kDiscBilinear) {
+          // A2 holds A / 2: e = (1 + l/2) / (1 - l/2), phi = dt / (1 - l/2)
+          const float lh = dtt * A2[j];
+          const float r = __builtin_amdgcn_rcpf(1.f - lh);
+          h[j] = fmaf((1.f + lh) * r, h[j], (bb[i][j] * ux) * r);
+          yj[j] = cc[i][j] * h[j];
+          continue;
+        }
         const float e = fast_exp2(dtt * A2[j]);
         if (DISC == kDiscEuler) {
           h[j] = fmaf(e, h[j], bb[i][j] * ux);
+        } else if (DISC == kDiscDirac) {
+          h[j] = fmaf(e, h[j], bb[i][j] * xt);
         } else if (!PRECISE) {
           const float v = (bb[i][j] * xt) * iA[j];
           h[j] = fmaf(e, h[j] + v, -v);
@@ -318,7 +331,7 @@ __global__ __launch_bounds__(64 * NW) void selective_scan_kernel(
     const bool ok = dok && n < N;
     const float a = ok ? A[d * N + n] : 0.f;
     An[j] = a;
-    A2[j] = a * kLog2e;
+    A2[j] = DISC == kDiscBilinear ? 0.5f * a : a * kLog2e;
     iA[j] = ok ? 1.f / a : 0.f;
     small |= ok && fabsf(a) < 0.5f;
     h[j] = (ok && h0 != nullptr) ? h0[(bi * D + d) * N + n] : 0.f;
@@ -332,7 +345,7 @@ __global__ __launch_bounds__(64 * NW) void selective_scan_kernel(
   const bool precise = __syncthreads_or(small ? 1 : 0) != 0;
   float* ck = (ckpt != nullptr && dok) ? ckpt + (bi * D + d) * N + n0 : nullptr;
 
-  if (DISC == kDiscEuler) {
+  if (DISC != kDiscZoh) {
     selective_body<T, DISC, false, TT, NPW, NW, GS, VEC>(x, dt, Bm, Cm, y, smem, h, A2, iA, An,
                                                         bi, d0, L, D, N, ck, ck_step, seg);
   } else if (precise) {
@@ -392,9 +405,16 @@ hipError_t launch_selective_scan(int disc, const void* x, const void* dt, const 
                                  const void* Bm, const void* Cm, const float* Dskip,
                                  const float* h0, void* y, float* h_last, float* ckpt, int64_t B,
                                  int64_t L, int64_t D, int N, int64_t seg, hipStream_t stream) {
-  return disc == kDiscEuler
-             ? launch_sel_n<T, kDiscEuler>(x, dt, A, Bm, Cm, Dskip, h0, y, h_last, ckpt, B, L, D, N, seg, stream)
-             : launch_sel_n<T, kDiscZoh>(x, dt, A, Bm, Cm, Dskip, h0, y, h_last, ckpt, B, L, D, N, seg, stream);
+  switch (disc) {
+    case kDiscEuler:
+      return launch_sel_n<T, kDiscEuler>(x, dt, A, Bm, Cm, Dskip, h0, y, h_last, ckpt, B, L, D, N, seg, stream);
+    case kDiscBilinear:
+      return launch_sel_n<T, kDiscBilinear>(x, dt, A, Bm, Cm, Dskip, h0, y, h_last, ckpt, B, L, D, N, seg, stream);
+    case kDiscDirac:
+      return launch_sel_n<T, kDiscDirac>(x, dt, A, Bm, Cm, Dskip, h0, y, h_last, ckpt, B, L, D, N, seg, stream);
+    default:
+      return launch_sel_n<T, kDiscZoh>(x, dt, A, Bm, Cm, Dskip, h0, y, h_last, ckpt, B, L, D, N, seg, stream);
+  }
 }
 
 template hipError_t launch_selective_scan<float>(int, const void*, const void*, const float*,

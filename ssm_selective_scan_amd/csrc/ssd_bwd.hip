@@ -45,7 +45,7 @@ constexpr int kBLd = kBQ + 8;    // leading dim of 64-wide LDS tiles
 // the same recurrence with x <-> v, B <-> k, C <-> q, phi = 1 and the decay
 // given directly as the gate g (log-decay ln g).  A GLA head of V columns is
 // run as V / 64 "heads" of 64 columns that form one group sharing k and q.
-enum { kBwdZoh = 0, kBwdEuler = 1, kBwdGla = 2 };
+enum { kBwdZoh = 0, kBwdEuler = 1, kBwdGla = 2, kBwdDirac = 3 };
 
 struct BwdArgs {
   const uint16_t* x; const uint16_t* dt; const float* A; const uint16_t* Bm; const uint16_t* Cm;
@@ -97,7 +97,9 @@ __device__ __forceinline__ void block_scalars(float gate, bool ok, float Ah, flo
   const float lam = dtv * Ah;
   l2 = lam * kLog2e;
   ek = fast_exp2(l2);
-  if (DISC == kBwdEuler) {
+  if (DISC == kBwdDirac) {
+    ph = ok ? 1.f : 0.f;
+  } else if (DISC == kBwdEuler) {
     ph = dtv;
   } else {
     const float ser = dtv * fmaf(lam, fmaf(lam, fmaf(lam, 1.f / 24.f, 1.f / 6.f), 0.5f), 1.f);
@@ -637,6 +639,9 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
       if (DISC == kBwdGla) {
         // phi is constant: the log-gate gradient goes out per 64-column slice
         if (k < nv) a.dgpart[(h * a.B + b) * a.L + t0 + k] = dlam;
+      } else if (DISC == kBwdDirac) {   // phi = 1: no input-factor term
+        ddt = dlam * Ah;
+        dAk = dlam * dtv;
       } else if (DISC == kBwdEuler) {
         ddt = dlam * Ah + dph;
         dAk = dlam * dtv;
@@ -824,7 +829,9 @@ hipError_t launch_ssd_bwd(int disc, const void* x, const void* dt, const float* 
   a.dx = static_cast<uint16_t*>(dx); a.ddt = static_cast<uint16_t*>(ddt); a.dA = dA;
   a.dBm = static_cast<uint16_t*>(dBm); a.dCm = static_cast<uint16_t*>(dCm); a.dD = dD; a.dh0 = dh0;
   a.B = B; a.L = L; a.H = H; a.G = G; a.N = N; a.seg = seg;
-  return disc == kBwdEuler ? launch_bwd<kBwdEuler>(a, ws, stream) : launch_bwd<kBwdZoh>(a, ws, stream);
+  if (disc == kBwdEuler) return launch_bwd<kBwdEuler>(a, ws, stream);
+  if (disc == kBwdDirac) return launch_bwd<kBwdDirac>(a, ws, stream);
+  return launch_bwd<kBwdZoh>(a, ws, stream);
 }
 
 hipError_t launch_gla_bwd(const void* q, const void* k, const void* v, const void* g,

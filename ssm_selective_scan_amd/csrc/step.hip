@@ -15,14 +15,22 @@
 
 namespace lr {
 
-enum { kStepZoh = 0, kStepEuler = 1 };
+enum { kStepZoh = 0, kStepEuler = 1, kStepBilinear = 2, kStepDirac = 3 };
 
 template <int DISC>
 __device__ __forceinline__ void step_disc(float dtv, float Av, float& e, float& phi) {
   const float lam = dtv * Av;
+  if (DISC == kStepBilinear) {
+    const float r = __builtin_amdgcn_rcpf(1.f - 0.5f * lam);
+    e = (1.f + 0.5f * lam) * r;
+    phi = dtv * r;
+    return;
+  }
   e = fast_exp2(lam * kLog2e);
   if (DISC == kStepEuler) {
     phi = dtv;
+  } else if (DISC == kStepDirac) {
+    phi = 1.f;
   } else {
     const float ser =
         dtv * fmaf(lam, fmaf(lam, fmaf(lam, fmaf(lam, 1.f / 120.f, 1.f / 24.f), 1.f / 6.f), 0.5f), 1.f);
@@ -179,8 +187,12 @@ hipError_t launch_selective_step(int disc, const void* x, const void* dt, const 
                        static_cast<const T*>(dt), A, static_cast<const T*>(Bm),
                        static_cast<const T*>(Cm), Dskip, h, static_cast<T*>(y), B, D, N, lg);
   };
-  if (disc == kStepEuler) go(selective_step_kernel<T, kStepEuler>);
-  else go(selective_step_kernel<T, kStepZoh>);
+  switch (disc) {
+    case kStepEuler: go(selective_step_kernel<T, kStepEuler>); break;
+    case kStepBilinear: go(selective_step_kernel<T, kStepBilinear>); break;
+    case kStepDirac: go(selective_step_kernel<T, kStepDirac>); break;
+    default: go(selective_step_kernel<T, kStepZoh>);
+  }
   return hipGetLastError();
 }
 
@@ -196,11 +208,19 @@ hipError_t launch_ssd_step(int disc, const void* x, const void* dt, const float*
                        P, G);
   };
   if (N == 128) {
-    if (disc == kStepEuler) go(ssd_step_kernel<kStepEuler, 128>);
-    else go(ssd_step_kernel<kStepZoh, 128>);
+    switch (disc) {
+      case kStepEuler: go(ssd_step_kernel<kStepEuler, 128>); break;
+      case kStepBilinear: go(ssd_step_kernel<kStepBilinear, 128>); break;
+      case kStepDirac: go(ssd_step_kernel<kStepDirac, 128>); break;
+      default: go(ssd_step_kernel<kStepZoh, 128>);
+    }
   } else {
-    if (disc == kStepEuler) go(ssd_step_kernel<kStepEuler, 64>);
-    else go(ssd_step_kernel<kStepZoh, 64>);
+    switch (disc) {
+      case kStepEuler: go(ssd_step_kernel<kStepEuler, 64>); break;
+      case kStepBilinear: go(ssd_step_kernel<kStepBilinear, 64>); break;
+      case kStepDirac: go(ssd_step_kernel<kStepDirac, 64>); break;
+      default: go(ssd_step_kernel<kStepZoh, 64>);
+    }
   }
   return hipGetLastError();
 }

@@ -104,6 +104,7 @@ def test_selective_ckpt_and_bwd_validation(L):
 
 def test_selective_validation(L):
     assert sel(L, disc=7) == DTYPE
+    assert sel(L, disc=4) == DTYPE
     assert sel(L, N=0) == SHAPE
     assert sel(L, N=65) == UNSUP
     assert sel(L, A=None) == NULL
@@ -137,6 +138,9 @@ def test_ssd_bwd_validation(L):
     if ws > 0:
         assert L.lr_ssd_scan_bwd(*args, None, 0, None) == WS
         assert L.lr_ssd_scan_bwd(*args, P, ws - 1, None) == WS
+    bad = list(args)
+    bad[1] = 2     # bilinear: no backward for the SSD path
+    assert L.lr_ssd_scan_bwd(*bad, P, ws, None) == UNSUP
     bad = list(args)
     bad[9] = 0     # seg = 0
     assert L.lr_ssd_scan_bwd(*bad, P, ws, None) == SHAPE
