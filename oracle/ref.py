@@ -375,3 +375,30 @@ def gla_scan_bwd(q, k, v, g, S0, do, dS_last=None):
         dg[:, t] = np.einsum("bhkv,bhkv->bh", Gt, hist[t])
         Gt = g[:, t, :, None, None] * Gt
     return dict(dq=dq, dk=dk, dv=dv, dg=dg, dS0=Gt)
+
+
+# ---------------------------------------------------------------------------
+# Rotational LRU  ["mlx-recurrence" post, rotlru_scan: complex-diagonal
+# recurrence, magnitude gate, per-step rotation of two-dimensional channel
+# pairs, state [B, D] as interleaved pairs]
+# ---------------------------------------------------------------------------
+def rotlru_scan(r, theta, u, h0=None):
+    """r, theta: [B, L, D/2]; u: [B, L, D] (pairs (2i, 2i+1) = (re, im)).
+
+    Per pair, with z = h[2i] + 1j h[2i+1]:
+        z_t = r_t exp(1j theta_t) z_{t-1} + (u_t[2i] + 1j u_t[2i+1])
+    i.e. each pair is rotated by theta_t, scaled by the gate r_t, then the
+    input pair is added.  Returns (h [B, L, D], h_last [B, D]) in float64."""
+    r, theta, u = map(_f, (r, theta, u))
+    Bn, L, D = u.shape
+    z = np.zeros((Bn, D // 2), np.complex128) if h0 is None else _f(h0)[:, 0::2] + 1j * _f(h0)[:, 1::2]
+    out = np.empty((Bn, L, D), F64)
+    for t in range(L):
+        a = r[:, t] * np.exp(1j * theta[:, t])
+        z = a * z + (u[:, t, 0::2] + 1j * u[:, t, 1::2])
+        out[:, t, 0::2] = z.real
+        out[:, t, 1::2] = z.imag
+    last = np.empty((Bn, D), F64)
+    last[:, 0::2] = z.real
+    last[:, 1::2] = z.imag
+    return out, last
