@@ -202,6 +202,19 @@ def measure_ssd_bwd(warmup, iters):
     return out
 
 
+def measure_rotlru(warmup, iters):
+    g = lrgen.make(6)
+    r, th, u = dev(g.t("r")), dev(g.t("theta")), dev(g.t("u"))
+    h = torch.empty_like(u)
+    t, _ = time_launches(lambda s: lr.lr_rotlru_scan(r, th, u, h=h), [None], warmup, iters)
+    p = g.params
+    nb = 2 * p["B"] * p["L"] * p["D"] * 4 + 2 * p["B"] * p["L"] * (p["D"] // 2) * 4
+    return dict(workload=lrgen.NAMES[6], kernel="rotlru_scan_kernel", us=t * 1e6,
+                tokens_per_s=p["B"] * p["L"] / t, elems_per_s=p["B"] * p["L"] * p["D"] / t,
+                alg_bytes=nb, GBs=nb / t / 1e9, hbm_frac=nb / t / 1e9 / HBM_PEAK_GBS,
+                note="3 MB working set: launch/latency bound")
+
+
 def measure_diag_bwd(warmup, iters):
     g = lrgen.make(1, grads=True)
     a, b, dh = dev(g.t("a")), dev(g.t("b")), dev(g.t("dh"))
@@ -368,7 +381,7 @@ def load_traffic():
 SECONDARY = {"diag": measure_diag, "ssd": measure_ssd, "gla": measure_gla,
              "ssd_fwd_bwd": measure_ssd_bwd, "diag_bwd": measure_diag_bwd,
              "selective_fwd_bwd": measure_selective_bwd, "gla_fwd_bwd": measure_gla_bwd,
-             "decode": measure_decode}
+             "decode": measure_decode, "rotlru": measure_rotlru}
 
 
 def main():

@@ -106,6 +106,20 @@ lr_status lr_diag_scan_bwd(lr_dtype io, int64_t B, int64_t L, int64_t D,
                            void* db, float* dh0, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Rotational LRU ("mlx-recurrence" post, rotlru_scan: complex-diagonal
+ * recurrence, magnitude gate, per-step rotation of two-dimensional channel
+ * pairs, state [B, D] as interleaved pairs).  With z = h[2i] + i h[2i+1]:
+ *     z_t = r_t (cos theta_t + i sin theta_t) z_{t-1} + (u_t[2i] + i u_t[2i+1])
+ * (reading: the gate scales, theta rotates, the input pair is added).
+ *   r, theta: [B, L, D/2] io (gate, angle in radians)    u, h: [B, L, D] io
+ *   h0, h_last: [B, D] fp32 or NULL.  State arithmetic is fp32.
+ * Supported: any B, L >= 0; D >= 2 and even.
+ * ------------------------------------------------------------------------- */
+lr_status lr_rotlru_scan(lr_dtype io, int64_t B, int64_t L, int64_t D,
+                         const void* r, const void* theta, const void* u,
+                         const float* h0, void* h, float* h_last, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Mamba-1 selective scan with ZOH (or Euler) discretisation and a fused
  * readout ("lrnnx: A library for Linear RNNs", Key Contributions 3: fused
  * scan + output projection; the hidden state never reaches memory).

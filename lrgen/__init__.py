@@ -18,6 +18,7 @@ Distributions (per workload, see ``CONFIGS``):
     ssd        x, B, C ~ N(0, 1); dt = softplus(N(-4, 1));
                A_h = -exp(U(0, ln 16)); Dskip ~ N(0, 1); dy ~ N(0, 1)
     gla        q, k ~ N(0, 1)/sqrt(K); v ~ N(0, 1); g = sigmoid(N(3, 1))
+    rotlru     r ~ U(0.90, 0.999), theta ~ U(-pi, pi), u ~ N(0, 1)
 """
 from __future__ import annotations
 
@@ -36,6 +37,8 @@ CONFIGS = {
     4: dict(kind="gla", io="bf16", B=8, L=4096, H=16, K=128, V=128, chunk=64),
     5: dict(kind="ssd_bwd", io="bf16", B=4, L=8192, H=32, P=64, G=1, N=128,
             chunk=256, seg=256),
+    # rotational LRU on the diagonal workload's shape (D/2 = 128 channel pairs)
+    6: dict(kind="rotlru", io="f32", B=1, L=1024, D=256),
 }
 
 NAMES = {
@@ -44,6 +47,7 @@ NAMES = {
     3: "mamba2_ssd_bf16_B8_H32_P64_N128_L2048",
     4: "gla_bf16_B8_H16_K128_V128_L4096",
     5: "ssd_fwd_bwd_ckpt_bf16_B4_H32_P64_N128_L8192_seg256",
+    6: "rotlru_fp32_B1_D256_L1024",
 }
 
 _CHUNK = 1 << 22  # elements per draw call; keeps peak host memory bounded
@@ -166,6 +170,11 @@ def make(cfg_id: int, seed: int = SEED, **over) -> Inputs:
         put("b", _Stream(seed, cfg_id, 1).normal((B, L, D)), io)
         if p.get("grads"):
             put("dh", _Stream(seed, cfg_id, 2).normal((B, L, D)), io)
+    elif kind == "rotlru":
+        B, L, D = p["B"], p["L"], p["D"]
+        put("r", _Stream(seed, cfg_id, 0).uniform((B, L, D // 2), 0.90, 0.999), io)
+        put("theta", _Stream(seed, cfg_id, 1).uniform((B, L, D // 2), -math.pi, math.pi), io)
+        put("u", _Stream(seed, cfg_id, 2).normal((B, L, D)), io)
     elif kind == "selective":
         B, L, D, N = p["B"], p["L"], p["D"], p["N"]
         put("x", _Stream(seed, cfg_id, 0).normal((B, L, D)), io)

@@ -13,7 +13,7 @@ import torch
 from ._lib import (LR_BF16, LR_DISC_BILINEAR, LR_DISC_DIRAC, LR_DISC_EULER,  # noqa: F401
                    LR_DISC_ZOH, LR_F32, LrError, check, lib)
 
-__all__ = ["lr_diag_scan", "lr_diag_scan_bwd", "lr_selective_scan", "lr_selective_scan_bwd",
+__all__ = ["lr_diag_scan", "lr_diag_scan_bwd", "lr_rotlru_scan", "lr_selective_scan", "lr_selective_scan_bwd",
            "lr_selective_scan_bwd_workspace_bytes", "lr_ssd_scan", "lr_ssd_scan_bwd",
            "lr_ssd_scan_bwd_workspace_bytes", "lr_gla_scan", "lr_gla_scan_bwd",
            "lr_gla_scan_bwd_workspace_bytes", "lr_diag_step", "lr_selective_step", "lr_ssd_step",
@@ -79,6 +79,19 @@ def lr_diag_scan_bwd(a, h, dh, h0=None, dh_last=None, want_dh0=False):
         _io(a), B, L, D, _ptr(a), _ptr(h), _f32(h0, "h0"), _ptr(dh), _f32(dh_last, "dh_last"),
         _ptr(da), _ptr(db), _f32(dh0, "dh0"), _stream(a)))
     return da, db, dh0
+
+
+def lr_rotlru_scan(r, theta, u, h0=None, h=None, h_last=None, want_last=False):
+    """Rotational LRU; r, theta: [B, L, D/2]; u: [B, L, D] (interleaved pairs)."""
+    B, L, D = u.shape
+    if h is None:
+        h = torch.empty_like(u)
+    if want_last and h_last is None:
+        h_last = torch.empty(B, D, device=u.device, dtype=torch.float32)
+    check("lr_rotlru_scan", lib().lr_rotlru_scan(
+        _io(u), B, L, D, _ptr(r), _ptr(theta), _ptr(u), _f32(h0, "h0"), _ptr(h),
+        _f32(h_last, "h_last"), _stream(u)))
+    return h, h_last
 
 
 def lr_selective_scan(x, dt, A, Bm, Cm, Dskip=None, h0=None, disc="zoh", seg=0, y=None,

@@ -19,7 +19,7 @@ LIB = os.path.join(PKG, "liblr.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["abi.hip", "diag_scan.hip", "selective_scan.hip", "selective_bwd.hip", "chunk_scan.hip",
-           "ssd_bwd.hip", "step.hip"]
+           "ssd_bwd.hip", "step.hip", "rotlru.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -59,6 +59,10 @@ hipError_t launch_ssd_bwd(int disc, const void* x, const void* dt, const float* 
                           int64_t H, int64_t P, int64_t G, int64_t N, int64_t seg,
                           hipStream_t stream);
 template <typename T>
+hipError_t launch_rotlru_scan(const void* r, const void* theta, const void* u, const float* h0,
+                              void* h, float* h_last, int64_t B, int64_t L, int64_t D,
+                              hipStream_t stream);
+template <typename T>
 hipError_t launch_diag_step(const void* a, const void* b, float* h, void* out, int64_t n,
                             hipStream_t s);
 template <typename T>
@@ -366,6 +370,22 @@ lr_status lr_gla_scan_bwd(lr_dtype io, int64_t B, int64_t L, int64_t H, int64_t 
   return hip_status(lr::launch_gla_bwd(q, k, v, g, ckpt, dout, dS_last, dq, dk, dv, dg, dS0,
                                        workspace, B, L, H, K, V, seg,
                                        static_cast<hipStream_t>(stream)));
+}
+
+lr_status lr_rotlru_scan(lr_dtype io, int64_t B, int64_t L, int64_t D, const void* r,
+                         const void* theta, const void* u, const float* h0, void* h,
+                         float* h_last, void* stream) {
+  if (!valid_io(io)) return LR_E_DTYPE;
+  if (B < 0 || L < 0 || D < 2 || D % 2 != 0) return LR_E_SHAPE;
+  if (!elems_ok({B, L, D})) return LR_E_OVERFLOW;
+  int64_t nwg = 1;
+  if (!mul_ok(nwg, B) || !mul_ok(nwg, (D / 2 + 15) / 16) || nwg > kMaxGrid) return LR_E_OVERFLOW;
+  if (B * L > 0 && any_null({r, theta, u, h})) return LR_E_NULLPTR;
+  if (!all_aligned({r, theta, u, h0, h, h_last})) return LR_E_ALIGN;
+  if (B == 0) return LR_OK;
+  auto s = static_cast<hipStream_t>(stream);
+  return hip_status(io == LR_F32 ? lr::launch_rotlru_scan<float>(r, theta, u, h0, h, h_last, B, L, D, s)
+                                 : lr::launch_rotlru_scan<uint16_t>(r, theta, u, h0, h, h_last, B, L, D, s));
 }
 
 // ---------------------------------------------------------------- steps

@@ -1,0 +1,166 @@
+// rotlru.hip — rotational LRU: a complex-diagonal recurrence over channel
+// pairs with a magnitude gate and a per-step rotation (one launch).
+//
+// ("mlx-recurrence" post, Apple Developer Forums thread 840535, rotlru_scan:
+// state [B, D] as interleaved channel pairs.)  Pair i of the state is the
+// complex number z = h[2i] + i h[2i+1] and
+//     z_t = a_t z_{t-1} + w_t,   a_t = r_t (cos theta_t + i sin theta_t),
+//     w_t = u_t[2i] + i u_t[2i+1]
+// which is the recurrence of the diagonal scan with complex (a, b) and the
+// same associative combine (a2, b2) o (a1, b1) = (a2 a1, a2 b1 + b2)
+// (IBM Research blog "K-Search for MLX", section "A 20x faster prefill: the
+// Mamba SSM kernel", combine equation), here with complex products.
+//
+// Work split as the diagonal scan: one workgroup owns 16 pairs of one batch
+// row and walks the sequence in tiles of 512 steps; 1024 threads split a
+// tile into 64 segments of 8 steps scanned sequentially per lane, one wave
+// per pair combines the 64 segment aggregates with a DPP complex pair scan,
+// and the carry between tiles stays in LDS.
+#include "common.hpp"
+
+namespace lr {
+
+constexpr int kRotCP = 16;          // pairs per workgroup
+constexpr int kRotSeg = 8;          // steps per lane segment
+constexpr int kRotThreads = 1024;
+constexpr int kRotSegs = kRotThreads / kRotCP;   // 64
+constexpr int kRotTile = kRotSegs * kRotSeg;     // 512 steps
+
+struct cplx {
+  float re, im;
+};
+__device__ __forceinline__ cplx cmul(cplx a, cplx b) {
+  return {fmaf(a.re, b.re, -a.im * b.im), fmaf(a.re, b.im, a.im * b.re)};
+}
+__device__ __forceinline__ cplx cfma(cplx a, cplx b, cplx c) {   // a b + c
+  return {fmaf(a.re, b.re, fmaf(-a.im, b.im, c.re)), fmaf(a.re, b.im, fmaf(a.im, b.re, c.im))};
+}
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void cpair_step(cplx& a, cplx& b) {
+  const cplx pa = {dpp_f<CTRL, ROW_MASK>(1.f, a.re), dpp_f<CTRL, ROW_MASK>(0.f, a.im)};
+  const cplx pb = {dpp_f<CTRL, ROW_MASK>(0.f, b.re), dpp_f<CTRL, ROW_MASK>(0.f, b.im)};
+  b = cfma(a, pb, b);
+  a = cmul(a, pa);
+}
+
+// inclusive scan of complex (a, b) pairs over the 64 lanes (lane 0 earliest)
+__device__ __forceinline__ void cwave_incl_pair_scan(cplx& a, cplx& b) {
+  cpair_step<0x111, 0xf>(a, b);
+  cpair_step<0x112, 0xf>(a, b);
+  cpair_step<0x114, 0xf>(a, b);
+  cpair_step<0x118, 0xf>(a, b);
+  cpair_step<0x142, 0xa>(a, b);
+  cpair_step<0x143, 0xc>(a, b);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kRotThreads) void rotlru_scan_kernel(
+    const T* __restrict__ r, const T* __restrict__ theta, const T* __restrict__ u,
+    const float* __restrict__ h0, T* __restrict__ h, float* __restrict__ h_last, int64_t L,
+    int64_t Dp) {
+  __shared__ cplx aggA[kRotSegs][kRotCP];
+  __shared__ cplx aggB[kRotSegs][kRotCP];
+  __shared__ cplx carry_in[kRotSegs][kRotCP];
+  __shared__ cplx tile_carry[kRotCP];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int pr = lane & (kRotCP - 1);
+  const int seg = wave * 4 + (lane >> 4);
+  const int64_t ntile = (Dp + kRotCP - 1) / kRotCP;
+  const int64_t bi = blockIdx.x / ntile;
+  const int64_t p0 = (blockIdx.x % ntile) * kRotCP;
+  const int64_t p = p0 + pr;
+  const bool pok = p < Dp;
+  const int64_t D = 2 * Dp;
+
+  if (tid < kRotCP) {
+    const int64_t pp = p0 + tid;
+    tile_carry[tid] = (h0 != nullptr && pp < Dp) ? cplx{h0[bi * D + 2 * pp], h0[bi * D + 2 * pp + 1]}
+                                                 : cplx{0.f, 0.f};
+  }
+  __syncthreads();
+
+  for (int64_t t0 = 0; t0 < L; t0 += kRotTile) {
+    const int64_t ts = t0 + static_cast<int64_t>(seg) * kRotSeg;
+    const int nok = pok ? static_cast<int>(L - ts < kRotSeg ? (L - ts > 0 ? L - ts : 0) : kRotSeg) : 0;
+    cplx Pv[kRotSeg], Hv[kRotSeg];
+    {
+      cplx P = {1.f, 0.f}, Hs = {0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < kRotSeg; ++i) {
+        cplx a = {1.f, 0.f}, w = {0.f, 0.f};
+        if (i < nok) {
+          const int64_t rowp = (bi * L + ts + i) * Dp + p;
+          const int64_t rowu = (bi * L + ts + i) * D + 2 * p;
+          const float rv = Io<T>::load(r + rowp);
+          float sn, cs;
+          sincosf(Io<T>::load(theta + rowp), &sn, &cs);
+          a = {rv * cs, rv * sn};
+          w = {Io<T>::load(u + rowu), Io<T>::load(u + rowu + 1)};
+        }
+        Hs = cfma(a, Hs, w);
+        P = cmul(a, P);
+        Pv[i] = P;
+        Hv[i] = Hs;
+      }
+      aggA[seg][pr] = P;
+      aggB[seg][pr] = Hs;
+    }
+    __syncthreads();
+
+    if (wave < kRotCP) {
+      const int c = wave;
+      cplx pa = aggA[lane][c], pb = aggB[lane][c];
+      const cplx tc = tile_carry[c];
+      cwave_incl_pair_scan(pa, pb);
+      // exclusive prefix: the previous lane's pair (identity at lane 0)
+      const cplx ea = {wave_shr1(pa.re, 1.f), wave_shr1(pa.im, 0.f)};
+      const cplx eb = {wave_shr1(pb.re, 0.f), wave_shr1(pb.im, 0.f)};
+      carry_in[lane][c] = cfma(ea, tc, eb);
+      if (lane == 63) tile_carry[c] = cfma(pa, tc, pb);
+    }
+    __syncthreads();
+
+    const cplx cin = carry_in[seg][pr];
+#pragma unroll
+    for (int i = 0; i < kRotSeg; ++i) {
+      if (i < nok) {
+        const cplx z = cfma(Pv[i], cin, Hv[i]);
+        const int64_t rowu = (bi * L + ts + i) * D + 2 * p;
+        Io<T>::store(h + rowu, z.re);
+        Io<T>::store(h + rowu + 1, z.im);
+      }
+    }
+  }
+  __syncthreads();
+  if (h_last != nullptr && tid < kRotCP) {
+    const int64_t pp = p0 + tid;
+    if (pp < Dp) {
+      h_last[bi * D + 2 * pp] = tile_carry[tid].re;
+      h_last[bi * D + 2 * pp + 1] = tile_carry[tid].im;
+    }
+  }
+}
+
+template <typename T>
+hipError_t launch_rotlru_scan(const void* r, const void* theta, const void* u, const float* h0,
+                              void* h, float* h_last, int64_t B, int64_t L, int64_t D,
+                              hipStream_t stream) {
+  const int64_t Dp = D / 2;
+  dim3 grid(static_cast<unsigned>(B * ((Dp + kRotCP - 1) / kRotCP)));
+  hipLaunchKernelGGL(rotlru_scan_kernel<T>, grid, dim3(kRotThreads), 0, stream,
+                     static_cast<const T*>(r), static_cast<const T*>(theta),
+                     static_cast<const T*>(u), h0, static_cast<T*>(h), h_last, L, Dp);
+  return hipGetLastError();
+}
+
+template hipError_t launch_rotlru_scan<float>(const void*, const void*, const void*, const float*,
+                                              void*, float*, int64_t, int64_t, int64_t,
+                                              hipStream_t);
+template hipError_t launch_rotlru_scan<uint16_t>(const void*, const void*, const void*,
+                                                 const float*, void*, float*, int64_t, int64_t,
+                                                 int64_t, hipStream_t);
+
+}  // namespace lr

@@ -212,3 +212,16 @@ def test_step_validation(L):
     assert gla(io=0) == UNSUP
     assert gla(S=None) == NULL
     assert gla(S=MIS) == ALIGN
+
+
+def test_rotlru_validation(L):
+    rot = lambda io=0, B=1, D=8, r=P, th=P, u=P, h=P, h0=None: L.lr_rotlru_scan(
+        io, B, 16, D, r, th, u, h0, h, None, None)
+    assert rot(io=2) == DTYPE
+    assert rot(D=7) == SHAPE
+    assert rot(D=0) == SHAPE
+    assert rot(th=None) == NULL
+    assert rot(h=None) == NULL
+    assert rot(u=MIS) == ALIGN
+    assert rot(h0=MIS) == ALIGN
+    assert rot(B=0, r=None, th=None, u=None, h=None) == OK
