@@ -25,6 +25,8 @@
 // (e - 1)/A, which keeps phi accurate to fp32 rounding at every A.
 // Bilinear (Tustin): e = (1 + dt A/2) / (1 - dt A/2), phi = dt / (1 - dt A/2),
 // one v_rcp_f32 in place of the exponential; dirac: phi = 1.
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace lr {
@@ -203,7 +205,7 @@ struct SelGroup {
   }
 };
 
-template <typename T, int DISC, bool PRECISE, int TT, int NPW, int NW, int GS, bool VEC>
+template <typename T, int DISC, bool PRECISE, int TT, int NPW, int NW, int GS, bool VEC, bool CK>
 __device__ __forceinline__ void selective_body(
     const T* __restrict__ x, const T* __restrict__ dt, const T* __restrict__ Bm,
     const T* __restrict__ Cm, T* __restrict__ y, float* __restrict__ smem, float (&h)[NPW],
@@ -239,7 +241,7 @@ __device__ __forceinline__ void selective_body(
   }
   int64_t ck_t = 0;   // token of the next segment checkpoint
   for (int64_t t0 = 0; t0 < L; t0 += TT) {
-    if (ck != nullptr && t0 == ck_t) {   // the state entering token t0 (seg % TT == 0)
+    if (CK && t0 == ck_t) {   // the state entering token t0 (seg % TT == 0)
 #pragma unroll
       for (int j = 0; j < NPW; ++j)
         if (n0 + j < N) ck[j] = h[j];
@@ -345,15 +347,20 @@ __global__ __launch_bounds__(64 * NW) void selective_scan_kernel(
   const bool precise = __syncthreads_or(small ? 1 : 0) != 0;
   float* ck = (ckpt != nullptr && dok) ? ckpt + (bi * D + d) * N + n0 : nullptr;
 
-  if (DISC != kDiscZoh) {
-    selective_body<T, DISC, false, TT, NPW, NW, GS, VEC>(x, dt, Bm, Cm, y, smem, h, A2, iA, An,
-                                                        bi, d0, L, D, N, ck, ck_step, seg);
-  } else if (precise) {
-    selective_body<T, DISC, true, TT, NPW, NW, GS, VEC>(x, dt, Bm, Cm, y, smem, h, A2, iA, An,
-                                                       bi, d0, L, D, N, ck, ck_step, seg);
+  // the checkpointing and plain forms are separate instances, so the plain
+  // loop carries no checkpoint state
+  auto body = [&](auto precise_c, auto ck_c) {
+    selective_body<T, DISC, decltype(precise_c)::value, TT, NPW, NW, GS, VEC, decltype(ck_c)::value>(
+        x, dt, Bm, Cm, y, smem, h, A2, iA, An, bi, d0, L, D, N, ck, ck_step, seg);
+  };
+  using F = std::false_type;
+  using Tr = std::true_type;
+  if (DISC == kDiscZoh && precise) {
+    if (ck != nullptr) body(Tr{}, Tr{});
+    else body(Tr{}, F{});
   } else {
-    selective_body<T, DISC, false, TT, NPW, NW, GS, VEC>(x, dt, Bm, Cm, y, smem, h, A2, iA, An,
-                                                        bi, d0, L, D, N, ck, ck_step, seg);
+    if (ck != nullptr) body(F{}, Tr{});
+    else body(F{}, F{});
   }
 
   if (h_last != nullptr && dok) {
