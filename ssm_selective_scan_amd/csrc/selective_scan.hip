@@ -242,10 +242,12 @@ __device__ __forceinline__ void selective_body(
   int64_t ck_t = 0;   // token of the next segment checkpoint
   for (int64_t t0 = 0; t0 < L; t0 += TT) {
     if (CK && t0 == ck_t) {   // the state entering token t0 (seg % TT == 0)
+      if (ck != nullptr) {       // null for lanes past the last channel
 #pragma unroll
-      for (int j = 0; j < NPW; ++j)
-        if (n0 + j < N) ck[j] = h[j];
-      ck += ck_step;
+        for (int j = 0; j < NPW; ++j)
+          if (n0 + j < N) ck[j] = h[j];
+        ck += ck_step;
+      }
       ck_t += seg;
     }
     st.store(xs, dts, Bs, Cs);
@@ -348,7 +350,7 @@ __global__ __launch_bounds__(64 * NW) void selective_scan_kernel(
   float* ck = (ckpt != nullptr && dok) ? ckpt + (bi * D + d) * N + n0 : nullptr;
 
   // the checkpointing and plain forms are separate instances, so the plain
-  // loop carries no checkpoint state
+  // loop carries no checkpoint state (the choice is uniform: ckpt, not ck)
   auto body = [&](auto precise_c, auto ck_c) {
     selective_body<T, DISC, decltype(precise_c)::value, TT, NPW, NW, GS, VEC, decltype(ck_c)::value>(
         x, dt, Bm, Cm, y, smem, h, A2, iA, An, bi, d0, L, D, N, ck, ck_step, seg);
@@ -356,10 +358,10 @@ __global__ __launch_bounds__(64 * NW) void selective_scan_kernel(
   using F = std::false_type;
   using Tr = std::true_type;
   if (DISC == kDiscZoh && precise) {
-    if (ck != nullptr) body(Tr{}, Tr{});
+    if (ckpt != nullptr) body(Tr{}, Tr{});
     else body(Tr{}, F{});
   } else {
-    if (ck != nullptr) body(F{}, Tr{});
+    if (ckpt != nullptr) body(F{}, Tr{});
     else body(F{}, F{});
   }
 
