@@ -150,27 +150,52 @@ __global__ __launch_bounds__(512) void selective_bwd_kernel(SelBwdArgs a) {
   }
   __syncthreads();
 
-  // stage tokens t0 .. t0 + nv - 1 (missing tokens and channels as zeros:
-  // dt = 0 gives e = 1, phi = 0, so they leave the state unchanged)
-  auto stage = [&](int64_t t0, int nv, bool with_dy) {
+  // Staging: a chunk's inputs are loaded into registers one chunk ahead
+  // (fetch) and written to LDS when the chunk starts (put).  Missing tokens
+  // and channels are zeros: dt = 0 gives e = 1, phi = 0, so they leave the
+  // state unchanged.
+  float rx[2], rdt[2], rdy[2], rb = 0.f, rc = 0.f;
+  auto fetch = [&](int64_t t0, int nv, bool with_dy) {
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int i = tid + 512 * k;     // [TC][64]
       const int r = i >> 6, c = i & 63;
       const bool ok = r < nv && d0 + c < D;
       const int64_t off = (b * L + t0 + r) * D + d0 + c;
-      sm.xs[r][c] = ok ? Io<T>::load(x + off) : 0.f;
-      sm.dts[r][c] = ok ? Io<T>::load(dt + off) : 0.f;
-      if (with_dy) sm.dys[r][c] = ok ? Io<T>::load(dy + off) : 0.f;
+      rx[k] = ok ? Io<T>::load(x + off) : 0.f;
+      rdt[k] = ok ? Io<T>::load(dt + off) : 0.f;
+      rdy[k] = (ok && with_dy) ? Io<T>::load(dy + off) : 0.f;
     }
     if (tid < kSbTC * N) {
       const int r = tid / N, n = tid % N;
       const bool ok = r < nv;
       const int64_t off = (b * L + t0 + r) * N + n;
-      sm.Bs[r][n] = ok ? Io<T>::load(Bm + off) : 0.f;
-      sm.Cs[r][n] = ok ? Io<T>::load(Cm + off) : 0.f;
+      rb = ok ? Io<T>::load(Bm + off) : 0.f;
+      rc = ok ? Io<T>::load(Cm + off) : 0.f;
     }
   };
+  auto put = [&]() {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int i = tid + 512 * k;
+      const int r = i >> 6, c = i & 63;
+      sm.xs[r][c] = rx[k];
+      sm.dts[r][c] = rdt[k];
+      sm.dys[r][c] = rdy[k];
+    }
+    if (tid < kSbTC * N) {
+      const int r = tid / N, n = tid % N;
+      sm.Bs[r][n] = rb;
+      sm.Cs[r][n] = rc;
+    }
+  };
+  auto chunk_len = [&](int64_t t0, int64_t tse) {
+    return static_cast<int>((tse - t0) < kSbTC ? (tse - t0) : kSbTC);
+  };
+  if (a.nseg > 0) {
+    const int64_t ts0 = (a.nseg - 1) * a.seg;
+    fetch(ts0, chunk_len(ts0, (ts0 + a.seg < L) ? ts0 + a.seg : L), false);
+  }
 
   for (int64_t s = a.nseg - 1; s >= 0; --s) {
     const int64_t ts0 = s * a.seg;
@@ -184,11 +209,15 @@ __global__ __launch_bounds__(512) void selective_bwd_kernel(SelBwdArgs a) {
     // ---- forward over the segment: the state entering every chunk
     for (int c = 0; c < nch; ++c) {
       const int64_t t0 = ts0 + static_cast<int64_t>(c) * kSbTC;
-      const int nv = static_cast<int>((tse - t0) < kSbTC ? (tse - t0) : kSbTC);
       sm.sub[c][w][0][lane] = h[0];
       sm.sub[c][w][1][lane] = h[1];
-      stage(t0, nv, false);
+      put();
       __syncthreads();
+      {
+        // next: chunk c + 1, or the segment's last chunk (with dy) for the reverse pass
+        const int64_t tn = c + 1 < nch ? t0 + kSbTC : ts0 + static_cast<int64_t>(nch - 1) * kSbTC;
+        fetch(tn, chunk_len(tn, tse), c + 1 >= nch);
+      }
 #pragma unroll
       for (int i = 0; i < kSbTC; ++i) {
         const float xv = sm.xs[i][lane], dtv = sm.dts[i][lane];
@@ -205,9 +234,15 @@ __global__ __launch_bounds__(512) void selective_bwd_kernel(SelBwdArgs a) {
     // ---- chunks last to first
     for (int c = nch - 1; c >= 0; --c) {
       const int64_t t0 = ts0 + static_cast<int64_t>(c) * kSbTC;
-      const int nv = static_cast<int>((tse - t0) < kSbTC ? (tse - t0) : kSbTC);
-      stage(t0, nv, true);
+      const int nv = chunk_len(t0, tse);
+      put();
       __syncthreads();
+      if (c > 0) {
+        fetch(t0 - kSbTC, kSbTC, true);
+      } else if (s > 0) {   // the previous segment's first chunk, for its forward pass
+        const int64_t tp = (s - 1) * a.seg;
+        fetch(tp, chunk_len(tp, ts0), false);
+      }
       float hs[kSbTC][2];
       float hin[2] = {sm.sub[c][w][0][lane], sm.sub[c][w][1][lane]};
       {
