@@ -51,8 +51,9 @@ struct SelBwdArgs {
 // through a series near dt A = 0 (A = 0 included); dphi/dA = (dt e - phi)/A,
 // also through its series there.  Bilinear: e = (1 + l/2) r, phi = dt r with
 // r = 1 / (1 - l/2).  Dirac: phi = 1.
+// iA = 1/A (any value where A == 0: the series branch is taken there).
 template <int DISC>
-__device__ __forceinline__ void sb_disc(float dtv, float Av, float& e, float& phi) {
+__device__ __forceinline__ void sb_disc(float dtv, float Av, float iA, float& e, float& phi) {
   const float lam = dtv * Av;
   if (DISC == kSbBilinear) {
     const float r = __builtin_amdgcn_rcpf(1.f - 0.5f * lam);
@@ -68,14 +69,14 @@ __device__ __forceinline__ void sb_disc(float dtv, float Av, float& e, float& ph
   } else {
     const float ser =
         dtv * fmaf(lam, fmaf(lam, fmaf(lam, fmaf(lam, 1.f / 120.f, 1.f / 24.f), 1.f / 6.f), 0.5f), 1.f);
-    phi = fabsf(lam) < 0.1f ? ser : (e - 1.f) / Av;
+    phi = fabsf(lam) < 0.1f ? ser : (e - 1.f) * iA;
   }
 }
 
 // (de/ddt, de/dA, dphi/ddt, dphi/dA) at (dt, A) with e, phi from sb_disc.
 template <int DISC>
-__device__ __forceinline__ void sb_grads(float dtv, float Av, float e, float phi, float& dedt,
-                                         float& dedA, float& dpdt, float& dpdA) {
+__device__ __forceinline__ void sb_grads(float dtv, float Av, float iA, float e, float phi,
+                                         float& dedt, float& dedA, float& dpdt, float& dpdA) {
   if (DISC == kSbBilinear) {
     const float r = __builtin_amdgcn_rcpf(1.f - 0.5f * dtv * Av);
     const float r2 = r * r;
@@ -98,7 +99,7 @@ __device__ __forceinline__ void sb_grads(float dtv, float Av, float e, float phi
     const float ser = dtv * dtv *
                       fmaf(lam, fmaf(lam, fmaf(lam, fmaf(lam, 1.f / 144.f, 1.f / 30.f), 1.f / 8.f), 1.f / 3.f), 0.5f);
     dpdt = e;
-    dpdA = fabsf(lam) < 0.1f ? ser : (dtv * e - phi) / Av;
+    dpdA = fabsf(lam) < 0.1f ? ser : (dtv * e - phi) * iA;
   }
 }
 
@@ -132,12 +133,13 @@ __global__ __launch_bounds__(512) void selective_bwd_kernel(SelBwdArgs a) {
   const int n0 = 2 * w;
   const int64_t D = a.D, L = a.L;
 
-  float Av[2], G[2], dAacc[2] = {0.f, 0.f};
+  float Av[2], iAv[2], G[2], dAacc[2] = {0.f, 0.f};
   bool okj[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     okj[j] = dok && n0 + j < N;
     Av[j] = okj[j] ? a.A[d * N + n0 + j] : 0.f;
+    iAv[j] = Av[j] != 0.f ? 1.f / Av[j] : 0.f;
     G[j] = (okj[j] && a.dh_last != nullptr) ? a.dh_last[(b * D + d) * N + n0 + j] : 0.f;
   }
   const float Dd = (dok && a.Dskip != nullptr) ? a.Dskip[d] : 0.f;
@@ -224,7 +226,7 @@ __global__ __launch_bounds__(512) void selective_bwd_kernel(SelBwdArgs a) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           float e, phi;
-          sb_disc<DISC>(dtv, Av[j], e, phi);
+          sb_disc<DISC>(dtv, Av[j], iAv[j], e, phi);
           h[j] = fmaf(e, h[j], phi * sm.Bs[i][n0 + j] * xv);
         }
       }
@@ -253,7 +255,7 @@ __global__ __launch_bounds__(512) void selective_bwd_kernel(SelBwdArgs a) {
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
             float e, phi;
-            sb_disc<DISC>(dtv, Av[j], e, phi);
+            sb_disc<DISC>(dtv, Av[j], iAv[j], e, phi);
             hh[j] = fmaf(e, hh[j], phi * sm.Bs[i][n0 + j] * xv);
             hs[i][j] = hh[j];
           }
@@ -267,7 +269,7 @@ __global__ __launch_bounds__(512) void selective_bwd_kernel(SelBwdArgs a) {
         for (int j = 0; j < 2; ++j) {
           const float Bv = sm.Bs[i][n0 + j], Cv = sm.Cs[i][n0 + j];
           float e, ph;
-          sb_disc<DISC>(dtv, Av[j], e, ph);
+          sb_disc<DISC>(dtv, Av[j], iAv[j], e, ph);
           G[j] = fmaf(dyv, Cv, G[j]);
           const float gphi = G[j] * ph;
           dxp = fmaf(gphi, Bv, dxp);
@@ -277,7 +279,7 @@ __global__ __launch_bounds__(512) void selective_bwd_kernel(SelBwdArgs a) {
           const float de = G[j] * hp;
           const float dphi = G[j] * Bv * xv;
           float dedt, dedA, dpdt, dpdA;
-          sb_grads<DISC>(dtv, Av[j], e, ph, dedt, dedA, dpdt, dpdA);
+          sb_grads<DISC>(dtv, Av[j], iAv[j], e, ph, dedt, dedA, dpdt, dpdA);
           ddtp += fmaf(de, dedt, dphi * dpdt);
           dAacc[j] += fmaf(de, dedA, dphi * dpdA);
           G[j] *= e;
