@@ -197,8 +197,9 @@ lr_status lr_ssd_scan(lr_dtype io, lr_disc disc, int64_t B, int64_t L,
                       void* y, float* h_last, float* ckpt, void* stream);
 
 /* Workspace bytes needed by lr_ssd_scan_bwd for these sizes (0 on invalid
- * sizes).  The workspace holds fp32 per-head partial sums of dB and dC, the
- * adjoint state at segment boundaries and per-segment partials of dA, dD. */
+ * sizes).  The workspace holds per-head partial sums of dB and dC (bf16),
+ * the adjoint state at segment boundaries and per-segment partials of dA,
+ * dD (fp32). */
 size_t lr_ssd_scan_bwd_workspace_bytes(int64_t B, int64_t L, int64_t H,
                                        int64_t P, int64_t G, int64_t N,
                                        int64_t chunk, int64_t seg);

@@ -30,9 +30,11 @@
 //             (the (a, b) combine again, run in reverse); also gives dh0.
 //   main:     per (b, h, segment): recompute the block-entry states from the
 //             checkpoint (kept in registers), then the blocks in reverse.
-//             Writes dx, ddt and per-head partial sums of dB, dC, dA, dD.
-//   reduce:   fixed-order sums of the partials over heads (and batch and
-//             segments for dA, dD), so results are deterministic.
+//             Writes dx, ddt and per-head partial sums of dB, dC (rounded to
+//             bf16, the precision of the final dB, dC; this halves the
+//             partial traffic), dA, dD (fp32).
+//   reduce:   fixed-order fp32 sums of the partials over heads (and batch
+//             and segments for dA, dD), so results are deterministic.
 #include "common.hpp"
 
 namespace lr {
@@ -51,7 +53,7 @@ struct BwdArgs {
   const uint16_t* x; const uint16_t* dt; const float* A; const uint16_t* Bm; const uint16_t* Cm;
   const float* Dskip; const float* ckpt; const uint16_t* dy; const float* dh_last;
   uint16_t* dx; uint16_t* ddt; float* dA; uint16_t* dBm; uint16_t* dCm; float* dD; float* dh0;
-  float* dBpart; float* dCpart;   // [H][B][L][N]
+  uint16_t* dBpart; uint16_t* dCpart;   // [H][B][L][N] bf16 per-head partials
   float* gseg;                    // [nseg][B][H][P][N]: Gamma_loc, then Gamma_out
   float* lam;                     // [nseg][B][H]
   float* dApart; float* dDpart;   // [B][H][nseg]
@@ -560,7 +562,8 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
           f32x4 v;
 #pragma unroll
           for (int r = 0; r < 4; ++r) v[r] = ph * fmaf(se, d2[r], d1[r]);
-          *reinterpret_cast<f32x4*>(a.dBpart + ((h * a.B + b) * a.L + t0 + t) * NS + 16 * nt + 4 * g4) = v;
+          *reinterpret_cast<u16x4*>(a.dBpart + ((h * a.B + b) * a.L + t0 + t) * NS + 16 * nt + 4 * g4) =
+              u16x4{f2bf(v[0]), f2bf(v[1]), f2bf(v[2]), f2bf(v[3])};
         }
       }
     }
@@ -608,7 +611,8 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
           f32x4 v;
 #pragma unroll
           for (int r = 0; r < 4; ++r) v[r] = fmaf(e, d2[r], d1[r]);
-          *reinterpret_cast<f32x4*>(a.dCpart + ((h * a.B + b) * a.L + t0 + u) * NS + 16 * nt + 4 * g4) = v;
+          *reinterpret_cast<u16x4*>(a.dCpart + ((h * a.B + b) * a.L + t0 + u) * NS + 16 * nt + 4 * g4) =
+              u16x4{f2bf(v[0]), f2bf(v[1]), f2bf(v[2]), f2bf(v[3])};
         }
       }
     }
@@ -683,8 +687,13 @@ __global__ __launch_bounds__(256) void ssd_bwd_reduce_kernel(BwdArgs a) {
     f32x4 sb = {0.f, 0.f, 0.f, 0.f}, sc = sb;
     for (int64_t hh = g * hpg; hh < (g + 1) * hpg; ++hh) {
       const int64_t off = (hh * a.B * a.L + bt) * a.N + 4 * c4;
-      sb += *reinterpret_cast<const f32x4*>(a.dBpart + off);
-      sc += *reinterpret_cast<const f32x4*>(a.dCpart + off);
+      const u16x4 pb = *reinterpret_cast<const u16x4*>(a.dBpart + off);
+      const u16x4 pc = *reinterpret_cast<const u16x4*>(a.dCpart + off);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sb[r] += bf2f(pb[r]);
+        sc[r] += bf2f(pc[r]);
+      }
     }
     const int64_t o = (bt * a.G + g) * a.N + 4 * c4;
     u16x4 vb = {f2bf(sb[0]), f2bf(sb[1]), f2bf(sb[2]), f2bf(sb[3])};
@@ -749,8 +758,8 @@ static WsLayout ws_layout(int64_t B, int64_t L, int64_t H, int64_t N, int64_t se
   const int64_t nseg = (L + seg - 1) / seg;
   WsLayout w;
   int64_t o = 0;
-  w.dB = o; o = align256(o + H * B * L * N * 4);
-  w.dC = o; o = align256(o + H * B * L * N * 4);
+  w.dB = o; o = align256(o + H * B * L * N * 2);
+  w.dC = o; o = align256(o + H * B * L * N * 2);
   w.g = o; o = align256(o + nseg * B * H * kBP * N * 4);
   w.lam = o; o = align256(o + nseg * B * H * 4);
   w.dA = o; o = align256(o + B * H * nseg * 4);
@@ -788,8 +797,8 @@ template <int MODE>
 static hipError_t launch_bwd(BwdArgs a, void* ws, hipStream_t stream) {
   const WsLayout lay = ws_layout(a.B, a.L, a.H, a.N, a.seg, MODE == kBwdGla);
   char* base = static_cast<char*>(ws);
-  a.dBpart = reinterpret_cast<float*>(base + lay.dB);
-  a.dCpart = reinterpret_cast<float*>(base + lay.dC);
+  a.dBpart = reinterpret_cast<uint16_t*>(base + lay.dB);
+  a.dCpart = reinterpret_cast<uint16_t*>(base + lay.dC);
   a.gseg = reinterpret_cast<float*>(base + lay.g);
   a.lam = reinterpret_cast<float*>(base + lay.lam);
   a.dApart = reinterpret_cast<float*>(base + lay.dA);
