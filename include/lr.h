@@ -143,8 +143,9 @@ lr_status lr_selective_scan(lr_dtype io, lr_disc disc, int64_t B, int64_t L,
                             float* ckpt, void* stream);
 
 /* Workspace bytes needed by lr_selective_scan_bwd (0 on invalid or
- * unsupported sizes): fp32 partial sums of dB and dC per 64-channel tile and
- * of dA and dD per batch row. */
+ * unsupported sizes): fp32 partial sums of dB and dC per 64-channel tile, of
+ * dA and dD per batch row, and the recomputed state every 16 tokens of the
+ * segment being processed. */
 size_t lr_selective_scan_bwd_workspace_bytes(int64_t B, int64_t L, int64_t D,
                                              int64_t N, int64_t seg);
 

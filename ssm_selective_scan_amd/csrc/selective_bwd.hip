@@ -18,9 +18,9 @@
 // owning state indices n = 2w, 2w + 1 of every channel (lane = channel), as
 // in the forward.  The workgroup walks the segments last to first carrying
 // G in registers.  Per segment it first runs the forward from the segment's
-// checkpoint, keeping the state every 16 tokens in LDS, then walks the
-// 16-token chunks last to first: recompute the chunk's 16 states into
-// registers, then the reverse steps.  Sums over n (dx, ddt) go through LDS
+// checkpoint, keeping the state every 16 tokens in a workspace slice of its
+// own (cache resident), then walks the 16-token chunks last to first:
+// recompute the chunk's 16 states into LDS, then the reverse steps.  Sums over n (dx, ddt) go through LDS
 // across the waves; sums over the 64 channels of a wave (dB, dC) use a
 // butterfly reduction of the four values (dB, dC at n = 2w, 2w + 1); sums
 // over channel tiles (dB, dC) and batch rows (dA, dD) are fixed-order
@@ -43,6 +43,7 @@ struct SelBwdArgs {
   float* dBpart; float* dCpart;   // [ntile][B][L][N]
   float* dApart;                  // [B][D][N]
   float* dDpart;                  // [B][D]
+  float* subck;                   // [B * ntile][kSbSub][kSbNW][2][64]: state entering each chunk
   void* dBm; void* dCm; float* dA; float* dD;
   int64_t B, L, D, N, seg, nseg, ntile;
 };
@@ -107,7 +108,7 @@ struct SbLds {
   float xs[kSbTC][kSbCT], dts[kSbTC][kSbCT], dys[kSbTC][kSbCT];
   float Bs[kSbTC][16], Cs[kSbTC][16];                 // n >= N stay zero
   float pdx[kSbNW][kSbTC][kSbCT], pddt[kSbNW][kSbTC][kSbCT];
-  float sub[kSbSub][kSbNW][2][kSbCT];                 // state entering each chunk
+  float hsl[kSbNW][kSbTC][2][kSbCT];                  // each wave's states of the chunk
   float rbc[kSbTC][2][16];                            // dB, dC of the chunk
 };
 
@@ -144,6 +145,7 @@ __global__ __launch_bounds__(512) void selective_bwd_kernel(SelBwdArgs a) {
   }
   const float Dd = (dok && a.Dskip != nullptr) ? a.Dskip[d] : 0.f;
   float dDacc = 0.f;
+  float* subp = a.subck + static_cast<int64_t>(blockIdx.x) * kSbSub * kSbNW * 2 * kSbCT;
 
   // B and C columns n >= N stay zero for the whole kernel
   for (int i = tid; i < kSbTC * 16; i += 512) {
@@ -211,8 +213,8 @@ __global__ __launch_bounds__(512) void selective_bwd_kernel(SelBwdArgs a) {
     // ---- forward over the segment: the state entering every chunk
     for (int c = 0; c < nch; ++c) {
       const int64_t t0 = ts0 + static_cast<int64_t>(c) * kSbTC;
-      sm.sub[c][w][0][lane] = h[0];
-      sm.sub[c][w][1][lane] = h[1];
+      subp[(c * kSbNW + w) * 2 * kSbCT + lane] = h[0];
+      subp[((c * kSbNW + w) * 2 + 1) * kSbCT + lane] = h[1];
       put();
       __syncthreads();
       {
@@ -245,8 +247,9 @@ __global__ __launch_bounds__(512) void selective_bwd_kernel(SelBwdArgs a) {
         const int64_t tp = (s - 1) * a.seg;
         fetch(tp, chunk_len(tp, ts0), false);
       }
-      float hs[kSbTC][2];
-      float hin[2] = {sm.sub[c][w][0][lane], sm.sub[c][w][1][lane]};
+      // this wave's states of the chunk -> LDS (read back by the same lanes)
+      float hin[2] = {subp[(c * kSbNW + w) * 2 * kSbCT + lane],
+                      subp[((c * kSbNW + w) * 2 + 1) * kSbCT + lane]};
       {
         float hh[2] = {hin[0], hin[1]};
 #pragma unroll
@@ -257,11 +260,11 @@ __global__ __launch_bounds__(512) void selective_bwd_kernel(SelBwdArgs a) {
             float e, phi;
             sb_disc<DISC>(dtv, Av[j], iAv[j], e, phi);
             hh[j] = fmaf(e, hh[j], phi * sm.Bs[i][n0 + j] * xv);
-            hs[i][j] = hh[j];
+            sm.hsl[w][i][j][lane] = hh[j];
           }
         }
       }
-#pragma unroll
+#pragma unroll 2
       for (int i = kSbTC - 1; i >= 0; --i) {
         const float xv = sm.xs[i][lane], dtv = sm.dts[i][lane], dyv = sm.dys[i][lane];
         float dxp = 0.f, ddtp = 0.f, v[4];
@@ -274,8 +277,8 @@ __global__ __launch_bounds__(512) void selective_bwd_kernel(SelBwdArgs a) {
           const float gphi = G[j] * ph;
           dxp = fmaf(gphi, Bv, dxp);
           v[j] = gphi * xv;                 // dB partial
-          v[2 + j] = hs[i][j] * dyv;        // dC partial
-          const float hp = i > 0 ? hs[i - 1][j] : hin[j];
+          v[2 + j] = sm.hsl[w][i][j][lane] * dyv;        // dC partial
+          const float hp = i > 0 ? sm.hsl[w][i > 0 ? i - 1 : 0][j][lane] : hin[j];
           const float de = G[j] * hp;
           const float dphi = G[j] * Bv * xv;
           float dedt, dedA, dpdt, dpdA;
@@ -386,7 +389,7 @@ __global__ __launch_bounds__(256) void selective_bwd_empty_kernel(float* dA, flo
 
 static inline int64_t sb_align(int64_t v) { return (v + 255) & ~int64_t(255); }
 
-struct SbLayout { int64_t dB, dC, dA, dD, total; };
+struct SbLayout { int64_t dB, dC, dA, dD, sub, total; };
 
 static SbLayout sb_layout(int64_t B, int64_t L, int64_t D, int64_t N) {
   const int64_t nt = (D + kSbCT - 1) / kSbCT;
@@ -396,6 +399,7 @@ static SbLayout sb_layout(int64_t B, int64_t L, int64_t D, int64_t N) {
   w.dC = o; o = sb_align(o + nt * B * L * N * 4);
   w.dA = o; o = sb_align(o + B * D * N * 4);
   w.dD = o; o = sb_align(o + B * D * 4);
+  w.sub = o; o = sb_align(o + B * nt * kSbSub * kSbNW * 2 * kSbCT * 4);
   w.total = o;
   return w;
 }
@@ -431,6 +435,7 @@ hipError_t launch_selective_bwd(int disc, const void* x, const void* dt, const f
   a.dCpart = reinterpret_cast<float*>(base + lay.dC);
   a.dApart = reinterpret_cast<float*>(base + lay.dA);
   a.dDpart = reinterpret_cast<float*>(base + lay.dD);
+  a.subck = reinterpret_cast<float*>(base + lay.sub);
   a.dBm = dBm; a.dCm = dCm; a.dA = dA; a.dD = dD;
   a.B = B; a.L = L; a.D = D; a.N = N; a.seg = seg; a.nseg = (L + seg - 1) / seg;
   a.ntile = (D + kSbCT - 1) / kSbCT;
