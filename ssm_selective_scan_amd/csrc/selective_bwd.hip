@@ -18,20 +18,22 @@
 // owning state indices n = 2w, 2w + 1 of every channel (lane = channel), as
 // in the forward.  The workgroup walks the segments last to first carrying
 // G in registers.  Per segment it first runs the forward from the segment's
-// checkpoint, keeping the state every 16 tokens in a workspace slice of its
-// own (cache resident), then walks the 16-token chunks last to first:
-// recompute the chunk's 16 states into LDS, then the reverse steps.  Sums over n (dx, ddt) go through LDS
-// across the waves; sums over the 64 channels of a wave (dB, dC) use a
-// butterfly reduction of the four values (dB, dC at n = 2w, 2w + 1); sums
-// over channel tiles (dB, dC) and batch rows (dA, dD) are fixed-order
-// partial sums reduced by a second launch, so results are deterministic.
+// checkpoint, keeping the state entering every 32-token chunk in a
+// workspace slice of its own (cache resident), then walks the chunks last to
+// first: recompute the chunk's 32 states into LDS, then the reverse steps.
+// Sums over n (dx, ddt) go through LDS across the waves (written over the
+// chunk's states once a step has read them); sums over the 64 channels of a
+// wave (dB, dC) pair lanes with the gfx950 lane-swap instructions and finish
+// with DPP row shifts; sums over channel tiles (dB, dC) and batch rows (dA,
+// dD) are fixed-order partial sums reduced by a second launch, so results
+// are deterministic.
 #include "common.hpp"
 
 namespace lr {
 
-constexpr int kSbTC = 16;     // tokens per chunk
+constexpr int kSbTC = 32;     // tokens per chunk
 constexpr int kSbNW = 8;      // waves (2 state indices each: N <= 16)
-constexpr int kSbSub = 16;    // chunks per segment (seg <= 256)
+constexpr int kSbSub = 8;     // chunks per segment (seg <= 256)
 constexpr int kSbCT = 64;     // channels per workgroup
 
 enum { kSbZoh = 0, kSbEuler = 1, kSbBilinear = 2, kSbDirac = 3 };
@@ -107,14 +109,47 @@ __device__ __forceinline__ void sb_grads(float dtv, float Av, float iA, float e,
 struct SbLds {
   float xs[kSbTC][kSbCT], dts[kSbTC][kSbCT], dys[kSbTC][kSbCT];
   float Bs[kSbTC][16], Cs[kSbTC][16];                 // n >= N stay zero
-  float pdx[kSbNW][kSbTC][kSbCT], pddt[kSbNW][kSbTC][kSbCT];
-  float hsl[kSbNW][kSbTC][2][kSbCT];                  // each wave's states of the chunk
+  // each wave's states of the chunk; the reverse step of token i overwrites
+  // its slot with the wave's partial sums of dx ([0]) and ddt ([1])
+  float hsl[kSbNW][kSbTC][2][kSbCT];
   float rbc[kSbTC][2][16];                            // dB, dC of the chunk
-};
+};   // 160 KB
 
-template <typename T, int DISC>
-__global__ __launch_bounds__(512) void selective_bwd_kernel(SelBwdArgs a) {
-  __shared__ SbLds sm;
+// Sum over the 64 lanes of v[0..3]; on return lane 15 of row q (lanes
+// 16 q .. 16 q + 15) holds the total of v[q].  Halves and rows are paired
+// with the gfx950 lane-swap instructions (permlane32_swap exchanges the
+// upper 32 lanes of its first operand with the lower 32 of its second,
+// permlane16_swap the odd rows of the first with the even rows of the
+// second), then each row is reduced with DPP row shifts.
+__device__ __forceinline__ float sum4_over_lanes(const float (&v)[4]) {
+  const auto p0 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[0]), __float_as_uint(v[2]),
+                                                   false, false);
+  const auto p1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[1]), __float_as_uint(v[3]),
+                                                   false, false);
+  // lanes < 32: sums of v[0], v[1] over lane pairs (l, l + 32); lanes >= 32: of v[2], v[3]
+  const float a0 = __uint_as_float(p0[0]) + __uint_as_float(p0[1]);
+  const float a1 = __uint_as_float(p1[0]) + __uint_as_float(p1[1]);
+  const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(a0), __float_as_uint(a1), false,
+                                                  false);
+  float r = __uint_as_float(q[0]) + __uint_as_float(q[1]);
+  r += dpp_f<0x111, 0xf>(0.f, r);   // row_shr:1
+  r += dpp_f<0x112, 0xf>(0.f, r);   // row_shr:2
+  r += dpp_f<0x114, 0xf>(0.f, r);   // row_shr:4
+  r += dpp_f<0x118, 0xf>(0.f, r);   // row_shr:8
+  return r;
+}
+
+// FAST: ZOH with every |A| of the workgroup >= 0.5, where phi = (e - 1)/A and
+// v = B x / A need no series.  Then, with h_t the state after step t,
+//   dh_t/ddt = A h_t + B x                  (the continuous-time derivative)
+//   dh_t/dA  = dt h_t + (dt - phi) B x / A
+// which use h_t only (no h_{t-1}).  Other cases use sb_disc/sb_grads.
+template <typename T, int DISC, bool FAST>
+__device__ __forceinline__ void selective_bwd_body(const SelBwdArgs& a, SbLds& sm, int64_t b,
+                                                   int64_t tile, const float (&Av)[2],
+                                                   const float (&iAv)[2], const bool (&okj)[2],
+                                                   float (&G)[2], float (&dAacc)[2],
+                                                   float& dDacc) {
   const T* x = static_cast<const T*>(a.x);
   const T* dt = static_cast<const T*>(a.dt);
   const T* Bm = static_cast<const T*>(a.Bm);
@@ -122,46 +157,37 @@ __global__ __launch_bounds__(512) void selective_bwd_kernel(SelBwdArgs a) {
   const T* dy = static_cast<const T*>(a.dy);
   T* dx = static_cast<T*>(a.dx);
   T* ddt = static_cast<T*>(a.ddt);
-
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int64_t tile = blockIdx.x % a.ntile;
-  const int64_t b = blockIdx.x / a.ntile;
   const int64_t d0 = tile * kSbCT;
-  const int64_t d = d0 + lane;
-  const bool dok = d < a.D;
   const int N = static_cast<int>(a.N);
   const int n0 = 2 * w;
   const int64_t D = a.D, L = a.L;
-
-  float Av[2], iAv[2], G[2], dAacc[2] = {0.f, 0.f};
-  bool okj[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    okj[j] = dok && n0 + j < N;
-    Av[j] = okj[j] ? a.A[d * N + n0 + j] : 0.f;
-    iAv[j] = Av[j] != 0.f ? 1.f / Av[j] : 0.f;
-    G[j] = (okj[j] && a.dh_last != nullptr) ? a.dh_last[(b * D + d) * N + n0 + j] : 0.f;
-  }
-  const float Dd = (dok && a.Dskip != nullptr) ? a.Dskip[d] : 0.f;
-  float dDacc = 0.f;
   float* subp = a.subck + static_cast<int64_t>(blockIdx.x) * kSbSub * kSbNW * 2 * kSbCT;
+  const float Dd = (a.Dskip != nullptr && d0 + lane < D) ? a.Dskip[d0 + lane] : 0.f;
+  float A2[2];   // A log2(e)
+#pragma unroll
+  for (int j = 0; j < 2; ++j) A2[j] = Av[j] * kLog2e;
 
-  // B and C columns n >= N stay zero for the whole kernel
-  for (int i = tid; i < kSbTC * 16; i += 512) {
-    (&sm.Bs[0][0])[i] = 0.f;
-    (&sm.Cs[0][0])[i] = 0.f;
-  }
-  __syncthreads();
+  // e, phi of one step
+  auto disc = [&](float dtv, int j, float& e, float& phi) {
+    if constexpr (FAST) {
+      e = fast_exp2(dtv * A2[j]);
+      phi = (e - 1.f) * iAv[j];
+    } else {
+      sb_disc<DISC>(dtv, Av[j], iAv[j], e, phi);
+    }
+  };
 
   // Staging: a chunk's inputs are loaded into registers one chunk ahead
   // (fetch) and written to LDS when the chunk starts (put).  Missing tokens
   // and channels are zeros: dt = 0 gives e = 1, phi = 0, so they leave the
   // state unchanged.
-  float rx[2], rdt[2], rdy[2], rb = 0.f, rc = 0.f;
+  constexpr int kSt = kSbTC * kSbCT / 512;   // staged x/dt/dy elements per thread
+  float rx[kSt], rdt[kSt], rdy[kSt], rb = 0.f, rc = 0.f;
   auto fetch = [&](int64_t t0, int nv, bool with_dy) {
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int k = 0; k < kSt; ++k) {
       const int i = tid + 512 * k;     // [TC][64]
       const int r = i >> 6, c = i & 63;
       const bool ok = r < nv && d0 + c < D;
@@ -180,7 +206,7 @@ __global__ __launch_bounds__(512) void selective_bwd_kernel(SelBwdArgs a) {
   };
   auto put = [&]() {
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int k = 0; k < kSt; ++k) {
       const int i = tid + 512 * k;
       const int r = i >> 6, c = i & 63;
       sm.xs[r][c] = rx[k];
@@ -208,7 +234,7 @@ __global__ __launch_bounds__(512) void selective_bwd_kernel(SelBwdArgs a) {
     float h[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
-      h[j] = okj[j] ? a.ckpt[((s * a.B + b) * D + d) * N + n0 + j] : 0.f;
+      h[j] = okj[j] ? a.ckpt[((s * a.B + b) * D + d0 + lane) * N + n0 + j] : 0.f;
 
     // ---- forward over the segment: the state entering every chunk
     for (int c = 0; c < nch; ++c) {
@@ -227,9 +253,15 @@ __global__ __launch_bounds__(512) void selective_bwd_kernel(SelBwdArgs a) {
         const float xv = sm.xs[i][lane], dtv = sm.dts[i][lane];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          float e, phi;
-          sb_disc<DISC>(dtv, Av[j], iAv[j], e, phi);
-          h[j] = fmaf(e, h[j], phi * sm.Bs[i][n0 + j] * xv);
+          if constexpr (FAST) {   // h = e (h + v) - v, v = B x / A
+            const float e = fast_exp2(dtv * A2[j]);
+            const float v = (sm.Bs[i][n0 + j] * xv) * iAv[j];
+            h[j] = fmaf(e, h[j] + v, -v);
+          } else {
+            float e, phi;
+            disc(dtv, j, e, phi);
+            h[j] = fmaf(e, h[j], phi * sm.Bs[i][n0 + j] * xv);
+          }
         }
       }
       __syncthreads();
@@ -248,8 +280,8 @@ __global__ __launch_bounds__(512) void selective_bwd_kernel(SelBwdArgs a) {
         fetch(tp, chunk_len(tp, ts0), false);
       }
       // this wave's states of the chunk -> LDS (read back by the same lanes)
-      float hin[2] = {subp[(c * kSbNW + w) * 2 * kSbCT + lane],
-                      subp[((c * kSbNW + w) * 2 + 1) * kSbCT + lane]};
+      const float hin[2] = {subp[(c * kSbNW + w) * 2 * kSbCT + lane],
+                            subp[((c * kSbNW + w) * 2 + 1) * kSbCT + lane]};
       {
         float hh[2] = {hin[0], hin[1]};
 #pragma unroll
@@ -258,8 +290,8 @@ __global__ __launch_bounds__(512) void selective_bwd_kernel(SelBwdArgs a) {
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
             float e, phi;
-            sb_disc<DISC>(dtv, Av[j], iAv[j], e, phi);
-            hh[j] = fmaf(e, hh[j], phi * sm.Bs[i][n0 + j] * xv);
+            disc(dtv, j, e, phi);
+            hh[j] = fmaf(e, hh[j], phi * (sm.Bs[i][n0 + j] * xv));
             sm.hsl[w][i][j][lane] = hh[j];
           }
         }
@@ -267,59 +299,55 @@ __global__ __launch_bounds__(512) void selective_bwd_kernel(SelBwdArgs a) {
 #pragma unroll 2
       for (int i = kSbTC - 1; i >= 0; --i) {
         const float xv = sm.xs[i][lane], dtv = sm.dts[i][lane], dyv = sm.dys[i][lane];
+        const float hsl_i[2] = {sm.hsl[w][i][0][lane], sm.hsl[w][i][1][lane]};
         float dxp = 0.f, ddtp = 0.f, v[4];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const float Bv = sm.Bs[i][n0 + j], Cv = sm.Cs[i][n0 + j];
           float e, ph;
-          sb_disc<DISC>(dtv, Av[j], iAv[j], e, ph);
-          G[j] = fmaf(dyv, Cv, G[j]);
+          disc(dtv, j, e, ph);
+          const float ht = hsl_i[j];
+          G[j] = fmaf(dyv, Cv, G[j]);        // dl/dh_t
           const float gphi = G[j] * ph;
           dxp = fmaf(gphi, Bv, dxp);
-          v[j] = gphi * xv;                 // dB partial
-          v[2 + j] = sm.hsl[w][i][j][lane] * dyv;        // dC partial
-          const float hp = i > 0 ? sm.hsl[w][i > 0 ? i - 1 : 0][j][lane] : hin[j];
-          const float de = G[j] * hp;
-          const float dphi = G[j] * Bv * xv;
-          float dedt, dedA, dpdt, dpdA;
-          sb_grads<DISC>(dtv, Av[j], iAv[j], e, ph, dedt, dedA, dpdt, dpdA);
-          ddtp += fmaf(de, dedt, dphi * dpdt);
-          dAacc[j] += fmaf(de, dedA, dphi * dpdA);
+          v[j] = gphi * xv;                  // dB partial
+          v[2 + j] = ht * dyv;               // dC partial
+          const float bx = Bv * xv;
+          if constexpr (FAST) {
+            ddtp = fmaf(G[j], fmaf(Av[j], ht, bx), ddtp);
+            dAacc[j] = fmaf(G[j], fmaf(dtv, ht, (dtv - ph) * (bx * iAv[j])), dAacc[j]);
+          } else {
+            const float hp = i > 0 ? sm.hsl[w][i > 0 ? i - 1 : 0][j][lane] : hin[j];
+            const float de = G[j] * hp;
+            const float dphi = G[j] * bx;
+            float dedt, dedA, dpdt, dpdA;
+            sb_grads<DISC>(dtv, Av[j], iAv[j], e, ph, dedt, dedA, dpdt, dpdA);
+            ddtp += fmaf(de, dedt, dphi * dpdt);
+            dAacc[j] += fmaf(de, dedA, dphi * dpdA);
+          }
           G[j] *= e;
         }
-        // butterfly: lanes l, l^16, l^32, l^48 end with one of the four values
-        const bool hi = (lane & 32) != 0, mid = (lane & 16) != 0;
-        float a0 = hi ? v[2] : v[0], a1 = hi ? v[3] : v[1];
-        const float s0 = __shfl_xor(hi ? v[0] : v[2], 32), s1 = __shfl_xor(hi ? v[1] : v[3], 32);
-        a0 += s0;
-        a1 += s1;
-        float r = mid ? a1 : a0;
-        r += __shfl_xor(mid ? a0 : a1, 16);
-        r += __shfl_xor(r, 8);
-        r += __shfl_xor(r, 4);
-        r += __shfl_xor(r, 2);
-        r += __shfl_xor(r, 1);
-        if ((lane & 15) == 0) sm.rbc[i][hi ? 1 : 0][n0 + (mid ? 1 : 0)] = r;
-        sm.pdx[w][i][lane] = dxp;
-        sm.pddt[w][i][lane] = ddtp;
+        const float r = sum4_over_lanes(v);
+        if ((lane & 15) == 15) sm.rbc[i][lane >> 5][n0 + ((lane >> 4) & 1)] = r;
+        sm.hsl[w][i][0][lane] = dxp;   // h of token i is no longer needed
+        sm.hsl[w][i][1][lane] = ddtp;
         if (w == 0) dDacc = fmaf(dyv, xv, dDacc);
       }
       __syncthreads();
       // sums over the waves -> dx, ddt; the chunk's dB, dC partials
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
+      for (int k = 0; k < kSt; ++k) {
         const int i = tid + 512 * k;
         const int r = i >> 6, cc = i & 63;
         if (r < nv && d0 + cc < D) {
           float sx = 0.f, st = 0.f;
 #pragma unroll
           for (int ww = 0; ww < kSbNW; ++ww) {
-            sx += sm.pdx[ww][r][cc];
-            st += sm.pddt[ww][r][cc];
+            sx += sm.hsl[ww][r][0][cc];
+            st += sm.hsl[ww][r][1][cc];
           }
-          const float Dc = a.Dskip != nullptr ? a.Dskip[d0 + cc] : 0.f;
           const int64_t off = (b * L + t0 + r) * D + d0 + cc;
-          Io<T>::store(dx + off, fmaf(Dc, sm.dys[r][cc], sx));
+          Io<T>::store(dx + off, fmaf(Dd, sm.dys[r][cc], sx));   // cc == lane
           Io<T>::store(ddt + off, st);
         }
       }
@@ -334,7 +362,54 @@ __global__ __launch_bounds__(512) void selective_bwd_kernel(SelBwdArgs a) {
       __syncthreads();
     }
   }
-  (void)Dd;
+}
+
+template <typename T, int DISC>
+__global__ __launch_bounds__(512) void selective_bwd_kernel(SelBwdArgs a) {
+  __shared__ SbLds sm;
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int64_t tile = blockIdx.x % a.ntile;
+  const int64_t b = blockIdx.x / a.ntile;
+  const int64_t d = tile * kSbCT + lane;
+  const bool dok = d < a.D;
+  const int N = static_cast<int>(a.N);
+  const int n0 = 2 * w;
+  const int64_t D = a.D;
+
+  float Av[2], iAv[2], G[2], dAacc[2] = {0.f, 0.f};
+  bool okj[2];
+  bool small = false;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    okj[j] = dok && n0 + j < N;
+    Av[j] = okj[j] ? a.A[d * N + n0 + j] : 0.f;
+    iAv[j] = Av[j] != 0.f ? 1.f / Av[j] : 0.f;
+    small |= okj[j] && fabsf(Av[j]) < 0.5f;
+    G[j] = (okj[j] && a.dh_last != nullptr) ? a.dh_last[(b * D + d) * N + n0 + j] : 0.f;
+  }
+  float dDacc = 0.f;
+
+  // B and C columns n >= N stay zero for the whole kernel
+  for (int i = tid; i < kSbTC * 16; i += 512) {
+    (&sm.Bs[0][0])[i] = 0.f;
+    (&sm.Cs[0][0])[i] = 0.f;
+  }
+  // the choice is uniform over the workgroup: one flag per wave in the dB/dC
+  // slots (first written after several more barriers); the barrier also
+  // orders the zeros above
+  float* flags = &sm.rbc[0][0][0];
+  const bool wsmall = __builtin_amdgcn_ballot_w64(small) != 0;   // all lanes take part
+  if (lane == 0) flags[w] = wsmall ? 1.f : 0.f;
+  __syncthreads();
+  bool precise = false;
+#pragma unroll
+  for (int ww = 0; ww < kSbNW; ++ww) precise |= flags[ww] != 0.f;
+  if (DISC == kSbZoh && !precise)
+    selective_bwd_body<T, DISC, true>(a, sm, b, tile, Av, iAv, okj, G, dAacc, dDacc);
+  else
+    selective_bwd_body<T, DISC, false>(a, sm, b, tile, Av, iAv, okj, G, dAacc, dDacc);
+
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     if (okj[j]) {
