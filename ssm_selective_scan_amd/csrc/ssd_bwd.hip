@@ -109,21 +109,28 @@ __device__ __forceinline__ void block_scalars(float gate, bool ok, float Ah, flo
   }
 }
 
-// Sum over the 16 lanes of a DPP row (lanes with the same l / 16).
-__device__ __forceinline__ float row16_sum(float v) {
-  v += __shfl_xor(v, 1);
-  v += __shfl_xor(v, 2);
-  v += __shfl_xor(v, 4);
-  v += __shfl_xor(v, 8);
+// Sum over the 16 lanes of a DPP row (lanes with the same l / 16): an
+// inclusive row scan, so the total lands in the row's last lane (l % 16 == 15).
+__device__ __forceinline__ float row16_sum_last(float v) {
+  v += dpp_f<0x111, 0xf>(0.f, v);   // row_shr:1
+  v += dpp_f<0x112, 0xf>(0.f, v);   // row_shr:2
+  v += dpp_f<0x114, 0xf>(0.f, v);   // row_shr:4
+  v += dpp_f<0x118, 0xf>(0.f, v);   // row_shr:8
   return v;
 }
-// Sum over the 4 lanes l % 16 == c (the 4 row groups of a wave).
+// Sum over the 4 lanes l % 16 == c (the 4 rows of a wave), in all of them:
+// gfx950's permlane16_swap pairs rows (0, 1) and (2, 3), permlane32_swap the
+// two halves.
 __device__ __forceinline__ float col4_sum(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
-__device__ __forceinline__ float wave_sum(float v) { return col4_sum(row16_sum(v)); }
+// Sum over the wave, the same in every lane.
+__device__ __forceinline__ float wave_sum(float v) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_incl_sum(v)), 63));
+}
 
 // ---------------------------------------------------------------------------
 // gloc: Gamma_loc(s) = sum_u E_u dy_u (x) C_u over the segment (E from the
@@ -376,7 +383,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
       float l2, ph, ek;
       block_scalars<DISC>(dtv, ok, Ah, l2, ph, ek);
       const float c = wave_incl_sum(l2);
-      const float cend = __shfl(c, 63);
+      const float cend = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), 63));
       sm.cum[lane] = c;
       sm.E[lane] = fast_exp2(c);
       sm.sE[lane] = fast_exp2(cend - c);
@@ -463,8 +470,8 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
       for (int r = 0; r < 4; ++r) sm.Wu[(u0 + r) * kBLd + t] = ow[r];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float rs = row16_sum(rsum[r]);
-        if (c16 == 0) sm.rowTp[tile][4 * g4 + r] = rs;
+        const float rs = row16_sum_last(rsum[r]);
+        if (c16 == 15) sm.rowTp[tile][4 * g4 + r] = rs;
       }
       const float cs = col4_sum(csum);
       if (g4 == 0) sm.colTp[tile][c16] = cs;
@@ -511,10 +518,10 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
           const float gB = dxa[ti][r] + xb;
           const float ph = sm.phi[t];
           if (t < nv) a.dx[(b * a.L + t0 + t) * xrow + xoff + p] = f2bf(fmaf(ph, gB, Dh * dyv));
-          const float toff = row16_sum(sm.E[t] * yo[ti][r] * dyv);
-          const float dph = row16_sum(xv * gB);
-          const float uu = row16_sum(ph * xv * xb);
-          if (c16 == 0) {
+          const float toff = row16_sum_last(sm.E[t] * yo[ti][r] * dyv);
+          const float dph = row16_sum_last(xv * gB);
+          const float uu = row16_sum_last(ph * xv * xb);
+          if (c16 == 15) {
             sm.toffp[w][t] = toff;
             sm.dphip[w][t] = dph;
             sm.up[w][t] = uu;
@@ -636,7 +643,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
       if (k == kBQ - 1) dcum += uprev + usum;
       // reverse inclusive prefix sum: dlam_k = sum_{j >= k} dcum_j
       const float incl = wave_incl_sum(dcum);
-      const float total = __shfl(incl, 63);
+      const float total = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(incl), 63));
       const float dlam = total - incl + dcum;
       const float dtv = sm.dtv[k], ek = sm.ek[k], ph = sm.phi[k];
       float ddt = 0.f, dAk = 0.f;
