@@ -138,9 +138,9 @@ __device__ __forceinline__ float wave_sum(float v) {
 // ---------------------------------------------------------------------------
 template <int NS>
 struct GlocLds {
-  uint16_t CT[NS * kBLd];      // C[u][n] as [n][u]
+  uint16_t Cs[kBQ * (NS + 8)]; // C[u][n]
   uint16_t dys[kBQ * kBLd];    // dy[u][p]
-  uint16_t dyET[kBP * kBLd];   // E_u dy[u][p] as [p][u]
+  uint16_t dyE[kBQ * kBLd];    // E_u dy[u][p]
   float cum[kBQ];
   float E[kBQ];
 };
@@ -177,13 +177,12 @@ __global__ __launch_bounds__(256) void ssd_bwd_gloc_kernel(BwdArgs a) {
       sm.cum[lane] = c;
       sm.E[lane] = fast_exp2(c);
     }
-    // C transposed: lanes walk tokens
+    // token-major copies; the contraction over tokens reads them transposed
     for (int idx = tid; idx < kBQ * (NS / 8); idx += 256) {
-      const int u = idx & 63, c = idx >> 6;
+      const int u = idx / (NS / 8), c = idx % (NS / 8);
       u16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
       if (u < nv) v = *reinterpret_cast<const u16x8*>(a.Cm + ((b * a.L + t0 + u) * a.G + grp) * NS + 8 * c);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) sm.CT[(8 * c + i) * kBLd + u] = v[i];
+      *reinterpret_cast<u16x8*>(sm.Cs + u * (NS + 8) + 8 * c) = v;
     }
     for (int idx = tid; idx < kBQ * (kBP / 8); idx += 256) {
       const int u = idx >> 3, c = idx & 7;
@@ -193,11 +192,13 @@ __global__ __launch_bounds__(256) void ssd_bwd_gloc_kernel(BwdArgs a) {
     }
     __syncthreads();
     for (int idx = tid; idx < kBQ * (kBP / 8); idx += 256) {
-      const int u = idx & 63, c = idx >> 6;
+      const int u = idx >> 3, c = idx & 7;
       const u16x8 v = *reinterpret_cast<const u16x8*>(sm.dys + u * kBLd + 8 * c);
       const float e = sm.E[u];
+      u16x8 o;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) sm.dyET[(8 * c + i) * kBLd + u] = f2bf(bf2f(v[i]) * e);
+      for (int i = 0; i < 8; ++i) o[i] = f2bf(bf2f(v[i]) * e);
+      *reinterpret_cast<u16x8*>(sm.dyE + u * kBLd + 8 * c) = o;
     }
     __syncthreads();
     const float cend = sm.cum[kBQ - 1];
@@ -208,8 +209,8 @@ __global__ __launch_bounds__(256) void ssd_bwd_gloc_kernel(BwdArgs a) {
       gacc[nt] *= dec;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
-        gacc[nt] = mfma16x16x32(lds_tile(sm.CT, kBLd, 16 * nt, 32 * ks, lane),
-                                lds_tile(sm.dyET, kBLd, 16 * w, 32 * ks, lane), gacc[nt]);
+        gacc[nt] = mfma16x16x32(lds_tile_tr(sm.Cs, NS + 8, 32 * ks, 16 * nt, lane),
+                                lds_tile_tr(sm.dyE, kBLd, 32 * ks, 16 * w, lane), gacc[nt]);
     }
     __syncthreads();
   }
@@ -252,14 +253,14 @@ struct MainLds {
   uint16_t Bs[kBQ * kLdN];     // B[t][n]
   uint16_t xs[kBQ * kBLd];     // x[t][p]
   uint16_t dys[kBQ * kBLd];    // dy[u][p]
-  uint16_t dyT[kBP * kBLd];    // dy[u][p] as [p][u]          (recompute: x as [p][s])
-  uint16_t dyET[kBP * kBLd];   // E_u dy[u][p] as [p][u]
-  uint16_t CT[NS * kBLd];      // C[u][n] as [n][u]           (recompute: B_w as [n][s])
-  uint16_t pBT[NS * kBLd];     // phi_t B[t][n] as [n][t]
+  uint16_t dyE[kBQ * kBLd];    // E_u dy[u][p]
+  uint16_t pB[kBQ * kLdN];     // phi_t B[t][n]               (recompute: B_w[s][n])
   uint16_t Mt[kBQ * kBLd];     // Mp[u][t] as [t][u]
   uint16_t Wt[kBQ * kBLd];     // W[u][t] as [t][u]
-  uint16_t Wu[kBQ * kBLd];     // W[u][t] as [u][t]
-  uint16_t GT[NS * kBLd];      // Gamma[p][n] as [n][p], then h_prev[p][n] as [n][p]
+  uint16_t Gs[kBP * kLdN];     // Gamma[p][n], then h_prev[p][n]
+  // Operands that contract over tokens (or over p) are read from these
+  // row-major tiles with the transposing LDS read (lds_tile_tr), so every
+  // tile is written with 8- or 16-byte stores.
   float cum[kBQ], E[kBQ], sE[kBQ], phi[kBQ], dtv[kBQ], ek[kBQ];
   float rowTp[12][16], colTp[12][16];
   float toffp[4][kBQ], dphip[4][kBQ], up[4][kBQ];
@@ -325,20 +326,21 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
         *reinterpret_cast<u16x8*>(sm.Bs + r * kLdN + 8 * c) = v;
       }
       for (int idx = tid; idx < kBQ * (kBP / 8); idx += 256) {
-        const int s = idx & 63, c = idx >> 6;
+        const int s = idx >> 3, c = idx & 7;
         u16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
         if (s < nv) v = *reinterpret_cast<const u16x8*>(a.x + (b * a.L + t0 + s) * xrow + xoff + 8 * c);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) sm.dyT[(8 * c + i) * kBLd + s] = v[i];   // XT
+        *reinterpret_cast<u16x8*>(sm.xs + s * kBLd + 8 * c) = v;
       }
       __syncthreads();
       const float cend = sm.cum[kBQ - 1];
       for (int idx = tid; idx < kBQ * (NS / 8); idx += 256) {
-        const int s = idx & 63, c = idx >> 6;
+        const int s = idx / (NS / 8), c = idx % (NS / 8);
         const float ws = fast_exp2(cend - sm.cum[s]) * sm.phi[s];
         const u16x8 v = *reinterpret_cast<const u16x8*>(sm.Bs + s * kLdN + 8 * c);
+        u16x8 o;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) sm.CT[(8 * c + i) * kBLd + s] = f2bf(bf2f(v[i]) * ws);   // BwT
+        for (int i = 0; i < 8; ++i) o[i] = f2bf(bf2f(v[i]) * ws);
+        *reinterpret_cast<u16x8*>(sm.pB + s * kLdN + 8 * c) = o;   // B_w
       }
       __syncthreads();
       const float dec = fast_exp2(cend);
@@ -347,8 +349,8 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
         hacc[nt] *= dec;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
-          hacc[nt] = mfma16x16x32(lds_tile(sm.CT, kBLd, 16 * nt, 32 * ks, lane),
-                                  lds_tile(sm.dyT, kBLd, 16 * w, 32 * ks, lane), hacc[nt]);
+          hacc[nt] = mfma16x16x32(lds_tile_tr(sm.pB, kLdN, 32 * ks, 16 * nt, lane),
+                                  lds_tile_tr(sm.xs, kBLd, 32 * ks, 16 * w, lane), hacc[nt]);
       }
       __syncthreads();
     }
@@ -392,7 +394,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
       sm.ek[lane] = ek;
     }
     for (int idx = tid; idx < kBQ * (NS / 8); idx += 256) {
-      const int r = idx & 63, c = idx >> 6;     // lanes walk tokens (transposed writes)
+      const int r = idx & 63, c = idx >> 6;
       u16x8 vc = {0, 0, 0, 0, 0, 0, 0, 0}, vb = vc;
       float ph = 0.f;
       if (r < nv) {
@@ -404,11 +406,10 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
       }
       *reinterpret_cast<u16x8*>(sm.Cs + r * kLdN + 8 * c) = vc;
       *reinterpret_cast<u16x8*>(sm.Bs + r * kLdN + 8 * c) = vb;
+      u16x8 pb;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        sm.CT[(8 * c + i) * kBLd + r] = vc[i];
-        sm.pBT[(8 * c + i) * kBLd + r] = f2bf(bf2f(vb[i]) * ph);
-      }
+      for (int i = 0; i < 8; ++i) pb[i] = f2bf(bf2f(vb[i]) * ph);
+      *reinterpret_cast<u16x8*>(sm.pB + r * kLdN + 8 * c) = pb;
     }
     for (int idx = tid; idx < kBQ * (kBP / 8); idx += 256) {
       const int r = idx & 63, c = idx >> 6;
@@ -420,18 +421,18 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
       }
       *reinterpret_cast<u16x8*>(sm.xs + r * kBLd + 8 * c) = vx;
       *reinterpret_cast<u16x8*>(sm.dys + r * kBLd + 8 * c) = vd;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) sm.dyT[(8 * c + i) * kBLd + r] = vd[i];
     }
     __syncthreads();
 
-    // ---- E-scaled dy transposed; decayed masks and the T sums
+    // ---- E-scaled dy; decayed masks and the T sums
     for (int idx = tid; idx < kBQ * (kBP / 8); idx += 256) {
-      const int u = idx & 63, c = idx >> 6;
+      const int u = idx >> 3, c = idx & 7;
       const u16x8 v = *reinterpret_cast<const u16x8*>(sm.dys + u * kBLd + 8 * c);
       const float e = sm.E[u];
+      u16x8 o;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) sm.dyET[(8 * c + i) * kBLd + u] = f2bf(bf2f(v[i]) * e);
+      for (int i = 0; i < 8; ++i) o[i] = f2bf(bf2f(v[i]) * e);
+      *reinterpret_cast<u16x8*>(sm.dyE + u * kBLd + 8 * c) = o;
     }
 #pragma unroll
     for (int q = 0; q < 3; ++q) {
@@ -467,8 +468,6 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
       *reinterpret_cast<u16x4*>(sm.Mt + t * kBLd + u0) = om;
       *reinterpret_cast<u16x4*>(sm.Wt + t * kBLd + u0) = ow;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sm.Wu[(u0 + r) * kBLd + t] = ow[r];
-#pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float rs = row16_sum_last(rsum[r]);
         if (c16 == 15) sm.rowTp[tile][4 * g4 + r] = rs;
@@ -503,7 +502,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
         for (int ks = 0; ks < 2; ++ks) {
           if (ks == 0 && ti >= 2) continue;
           dxa[ti] = mfma16x16x32(lds_tile(sm.Mt, kBLd, 16 * ti, 32 * ks, lane),
-                                 lds_tile(sm.dyT, kBLd, 16 * w, 32 * ks, lane), dxa[ti]);
+                                 lds_tile_tr(sm.dys, kBLd, 32 * ks, 16 * w, lane), dxa[ti]);
         }
       }
       float ddsum = 0.f;
@@ -544,8 +543,8 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
     // ---- dB: Gamma to LDS, then phi_t (W^T C + sE_t x Gamma)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sm.GT[(16 * nt + 4 * g4 + r) * kBLd + p] = f2bf(gacc[nt][r]);
+      *reinterpret_cast<u16x4*>(sm.Gs + p * kLdN + 16 * nt + 4 * g4) =
+          u16x4{f2bf(gacc[nt][0]), f2bf(gacc[nt][1]), f2bf(gacc[nt][2]), f2bf(gacc[nt][3])};
     __syncthreads();
 #pragma unroll
     for (int aa = 0; aa < NT / 4; ++aa) {
@@ -556,12 +555,12 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           if (ks == 0 && ti >= 2) continue;
-          d1 = mfma16x16x32(lds_tile(sm.CT, kBLd, 16 * nt, 32 * ks, lane),
+          d1 = mfma16x16x32(lds_tile_tr(sm.Cs, kLdN, 32 * ks, 16 * nt, lane),
                             lds_tile(sm.Wt, kBLd, 16 * ti, 32 * ks, lane), d1);
         }
 #pragma unroll
         for (int kp = 0; kp < 2; ++kp)
-          d2 = mfma16x16x32(lds_tile(sm.GT, kBLd, 16 * nt, 32 * kp, lane),
+          d2 = mfma16x16x32(lds_tile_tr(sm.Gs, kLdN, 32 * kp, 16 * nt, lane),
                             lds_tile(sm.xs, kBLd, 16 * ti, 32 * kp, lane), d2);
         const int t = 16 * ti + c16;
         if (t < nv) {
@@ -582,8 +581,8 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
         gacc[nt] *= dec;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
-          gacc[nt] = mfma16x16x32(lds_tile(sm.CT, kBLd, 16 * nt, 32 * ks, lane),
-                                  lds_tile(sm.dyET, kBLd, 16 * w, 32 * ks, lane), gacc[nt]);
+          gacc[nt] = mfma16x16x32(lds_tile_tr(sm.Cs, kLdN, 32 * ks, 16 * nt, lane),
+                                  lds_tile_tr(sm.dyE, kBLd, 32 * ks, 16 * w, lane), gacc[nt]);
       }
     }
     __syncthreads();
@@ -592,8 +591,8 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const u16x8 hv = __builtin_bit_cast(u16x8, hcur[nt >> 1]);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sm.GT[(16 * nt + 4 * g4 + r) * kBLd + p] = hv[4 * (nt & 1) + r];
+      *reinterpret_cast<u16x4*>(sm.Gs + p * kLdN + 16 * nt + 4 * g4) =
+          u16x4{hv[4 * (nt & 1)], hv[4 * (nt & 1) + 1], hv[4 * (nt & 1) + 2], hv[4 * (nt & 1) + 3]};
     }
     __syncthreads();
 #pragma unroll
@@ -605,12 +604,12 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           if (ks == 1 && tj < 2) continue;
-          d1 = mfma16x16x32(lds_tile(sm.pBT, kBLd, 16 * nt, 32 * ks, lane),
-                            lds_tile(sm.Wu, kBLd, 16 * tj, 32 * ks, lane), d1);
+          d1 = mfma16x16x32(lds_tile_tr(sm.pB, kLdN, 32 * ks, 16 * nt, lane),
+                            lds_tile_tr(sm.Wt, kBLd, 32 * ks, 16 * tj, lane), d1);
         }
 #pragma unroll
         for (int kp = 0; kp < 2; ++kp)
-          d2 = mfma16x16x32(lds_tile(sm.GT, kBLd, 16 * nt, 32 * kp, lane),
+          d2 = mfma16x16x32(lds_tile_tr(sm.Gs, kLdN, 32 * kp, 16 * nt, lane),
                             lds_tile(sm.dys, kBLd, 16 * tj, 32 * kp, lane), d2);
         const int u = 16 * tj + c16;
         if (u < nv) {
