@@ -681,43 +681,60 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
 // reduce: dB, dC over the heads of each group (fixed order); dA, dD over
 // (batch, segment) per head.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void ssd_bwd_reduce_kernel(BwdArgs a) {
-  const int64_t n4 = a.N / 4;
-  const int64_t total = a.B * a.L * a.G * n4;
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  const int64_t hpg = a.H / a.G;
-  if (idx < total) {
-    const int64_t c4 = idx % n4;
-    const int64_t g = (idx / n4) % a.G;
-    const int64_t bt = idx / (n4 * a.G);     // b * L + t
-    f32x4 sb = {0.f, 0.f, 0.f, 0.f}, sc = sb;
-    for (int64_t hh = g * hpg; hh < (g + 1) * hpg; ++hh) {
-      const int64_t off = (hh * a.B * a.L + bt) * a.N + 4 * c4;
-      const u16x4 pb = *reinterpret_cast<const u16x4*>(a.dBpart + off);
-      const u16x4 pc = *reinterpret_cast<const u16x4*>(a.dCpart + off);
+// The first nblk_bc blocks: dB, dC, one thread per 8 consecutive n of a
+// (b, t, group) row, heads summed in order.  The blocks after them: dA, dD,
+// one wave per head; lane l sums partials l, l + 64, ... in order and the
+// wave adds the 64 lane sums in a fixed pattern.
+__global__ __launch_bounds__(256) void ssd_bwd_reduce_kernel(BwdArgs a, int64_t nblk_bc) {
+  if (blockIdx.x < nblk_bc) {
+    const int64_t n8 = a.N / 8;
+    const int64_t total = a.B * a.L * a.G * n8;
+    const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (idx >= total) return;
+    const int64_t hpg = a.H / a.G;
+    const int64_t c8 = idx % n8;
+    const int64_t g = (idx / n8) % a.G;
+    const int64_t bt = idx / (n8 * a.G);     // b * L + t
+    const int64_t hstride = a.B * a.L * a.N;
+    const uint16_t* pb = a.dBpart + (g * hpg * a.B * a.L + bt) * a.N + 8 * c8;
+    const uint16_t* pc = a.dCpart + (g * hpg * a.B * a.L + bt) * a.N + 8 * c8;
+    float sb[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, sc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int64_t k = 0; k < hpg; ++k) {
+      const u16x8 vb = *reinterpret_cast<const u16x8*>(pb + k * hstride);
+      const u16x8 vc = *reinterpret_cast<const u16x8*>(pc + k * hstride);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        sb[r] += bf2f(pb[r]);
-        sc[r] += bf2f(pc[r]);
+      for (int r = 0; r < 8; ++r) {
+        sb[r] += bf2f(vb[r]);
+        sc[r] += bf2f(vc[r]);
       }
     }
-    const int64_t o = (bt * a.G + g) * a.N + 4 * c4;
-    u16x4 vb = {f2bf(sb[0]), f2bf(sb[1]), f2bf(sb[2]), f2bf(sb[3])};
-    u16x4 vc = {f2bf(sc[0]), f2bf(sc[1]), f2bf(sc[2]), f2bf(sc[3])};
-    *reinterpret_cast<u16x4*>(a.dBm + o) = vb;
-    *reinterpret_cast<u16x4*>(a.dCm + o) = vc;
-  }
-  if (blockIdx.x == 0 && a.dA != nullptr) {
-    for (int64_t hh = threadIdx.x; hh < a.H; hh += 256) {
-      float sa = 0.f, sd = 0.f;
-      for (int64_t bb = 0; bb < a.B; ++bb)
-        for (int64_t s = 0; s < a.nseg; ++s) {
-          sa += a.dApart[(bb * a.H + hh) * a.nseg + s];
-          sd += a.dDpart[(bb * a.H + hh) * a.nseg + s];
-        }
-      a.dA[hh] = sa;
-      if (a.dD != nullptr) a.dD[hh] = sd;
+    const int64_t o = (bt * a.G + g) * a.N + 8 * c8;
+    u16x8 ob, oc;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      ob[r] = f2bf(sb[r]);
+      oc[r] = f2bf(sc[r]);
     }
+    *reinterpret_cast<u16x8*>(a.dBm + o) = ob;
+    *reinterpret_cast<u16x8*>(a.dCm + o) = oc;
+    return;
+  }
+  if (a.dA == nullptr) return;
+  const int lane = threadIdx.x & 63;
+  const int64_t hh = (blockIdx.x - nblk_bc) * 4 + (threadIdx.x >> 6);
+  if (hh >= a.H) return;   // whole waves leave together
+  float sa = 0.f, sd = 0.f;
+  for (int64_t i = lane; i < a.B * a.nseg; i += 64) {
+    const int64_t bb = i / a.nseg, sgi = i % a.nseg;
+    sa += a.dApart[(bb * a.H + hh) * a.nseg + sgi];
+    sd += a.dDpart[(bb * a.H + hh) * a.nseg + sgi];
+  }
+  sa = wave_sum(sa);
+  sd = wave_sum(sd);
+  if (lane == 0) {
+    a.dA[hh] = sa;
+    if (a.dD != nullptr) a.dD[hh] = sd;
   }
 }
 
@@ -820,8 +837,8 @@ static hipError_t launch_bwd(BwdArgs a, void* ws, hipStream_t stream) {
   const int nbs = static_cast<int>(a.seg / kBQ);
   if (a.N == 128) launch_main<MODE, 128>(a, nwg, nbs, stream);
   else launch_main<MODE, 64>(a, nwg, nbs, stream);
-  const int64_t red = (a.B * a.L * a.G * (a.N / 4) + 255) / 256;
-  hipLaunchKernelGGL(ssd_bwd_reduce_kernel, dim3(red > 0 ? red : 1), dim3(256), 0, stream, a);
+  const int64_t red = (a.B * a.L * a.G * (a.N / 8) + 255) / 256;
+  hipLaunchKernelGGL(ssd_bwd_reduce_kernel, dim3(red + (a.H + 3) / 4), dim3(256), 0, stream, a, red);
   if (MODE == kBwdGla) {
     const int64_t nd = (a.B * a.L * a.G + 255) / 256;
     hipLaunchKernelGGL(gla_bwd_dg_kernel, dim3(nd), dim3(256), 0, stream, a);
