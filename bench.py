@@ -124,13 +124,16 @@ def measure_ssd(warmup, iters):
     sets = [dict(x=x if i == 0 else x.clone(), dt=dt if i == 0 else dt.clone(),
                  Bm=Bm if i == 0 else Bm.clone(), Cm=Cm if i == 0 else Cm.clone(),
                  y=torch.empty_like(x)) for i in range(rotations(per))]
-    t, _ = time_launches(lambda s: lr.lr_ssd_scan(s["x"], s["dt"], A, s["Bm"], s["Cm"], Dk,
-                                                  chunk=p["chunk"], y=s["y"]),
-                         sets, warmup, iters)
     B, L, H, P, N = p["B"], p["L"], p["H"], p["P"], p["N"]
+    wsb = lr.lr_ssd_scan_workspace_bytes(B, L, H, P, p["G"], N, p["chunk"])
+    ws = torch.empty(wsb, device="cuda", dtype=torch.uint8) if wsb else None
+    t, _ = time_launches(lambda s: lr.lr_ssd_scan(s["x"], s["dt"], A, s["Bm"], s["Cm"], Dk,
+                                                  chunk=p["chunk"], y=s["y"], workspace=ws),
+                         sets, warmup, iters)
     nb = 2 * B * L * H * P * 2 + B * L * H * 2 + 2 * B * L * N * 2 + 2 * H * 4
     fl = ssd_mfma_flops(B, L, H, P, N)
-    return dict(workload=lrgen.NAMES[3], kernel="chunk_fwd_kernel<SSD>", us=t * 1e6,
+    return dict(workload=lrgen.NAMES[3], kernel="chunk_fwd_kernel<SSD> (state pre-pass + main)",
+                fwd_workspace_bytes=wsb, us=t * 1e6,
                 tokens_per_s=B * L / t, elems_per_s=B * L * H * P / t, alg_bytes=nb,
                 GBs=nb / t / 1e9, hbm_frac=nb / t / 1e9 / HBM_PEAK_GBS,
                 mfma_tflops=fl / t / 1e12, mfma_frac=fl / t / 1e12 / MFMA_BF16_PEAK_TFLOPS)
@@ -151,13 +154,16 @@ def measure_gla(warmup, iters):
     sets = [dict(q=q if i == 0 else q.clone(), k=k if i == 0 else k.clone(),
                  v=v if i == 0 else v.clone(), g=gg, o=torch.empty_like(v))
             for i in range(rotations(per, floor=2))]
-    t, _ = time_launches(lambda s: lr.lr_gla_scan(s["q"], s["k"], s["v"], s["g"],
-                                                  chunk=p["chunk"], o=s["o"]),
-                         sets, warmup, iters)
     B, L, H, K, V = p["B"], p["L"], p["H"], p["K"], p["V"]
+    wsb = lr.lr_gla_scan_workspace_bytes(B, L, H, K, V, p["chunk"])
+    ws = torch.empty(wsb, device="cuda", dtype=torch.uint8) if wsb else None
+    t, _ = time_launches(lambda s: lr.lr_gla_scan(s["q"], s["k"], s["v"], s["g"],
+                                                  chunk=p["chunk"], o=s["o"], workspace=ws),
+                         sets, warmup, iters)
     nb = 2 * B * L * H * K * 2 + 2 * B * L * H * V * 2 + B * L * H * 2
     fl = (V // 64) * ssd_mfma_flops(B, L, H, 64, K)
-    return dict(workload=lrgen.NAMES[4], kernel="chunk_fwd_kernel<GLA>", us=t * 1e6,
+    return dict(workload=lrgen.NAMES[4], kernel="chunk_fwd_kernel<GLA> (state pre-pass + main)",
+                fwd_workspace_bytes=wsb, us=t * 1e6,
                 tokens_per_s=B * L / t, elems_per_s=B * L * H * V / t, alg_bytes=nb,
                 GBs=nb / t / 1e9, hbm_frac=nb / t / 1e9 / HBM_PEAK_GBS,
                 mfma_tflops=fl / t / 1e12, mfma_frac=fl / t / 1e12 / MFMA_BF16_PEAK_TFLOPS)
@@ -175,15 +181,18 @@ def measure_ssd_bwd(warmup, iters):
     torch.cuda.synchronize()
     base = torch.cuda.memory_allocated()
     torch.cuda.reset_peak_memory_stats()
+    fwsb = lr.lr_ssd_scan_workspace_bytes(B, L, H, P, G, N, p["chunk"])
+    fws = torch.empty(fwsb, device="cuda", dtype=torch.uint8) if fwsb else None
     tf, _ = time_launches(lambda s: lr.lr_ssd_scan(x, dt, A, Bm, Cm, Dk, chunk=p["chunk"],
-                                                   seg=seg, y=y, ckpt=ckpt),
+                                                   seg=seg, y=y, ckpt=ckpt, workspace=fws),
                           [None], warmup, iters)
     ws_bytes = lr.lr_ssd_scan_bwd_workspace_bytes(B, L, H, P, G, N, p["chunk"], seg)
+    # state-related memory: checkpoints, the forward's part states, the backward's workspace
     out = dict(workload=lrgen.NAMES[5], fwd_us=tf * 1e6,
                ckpt_bytes=ckpt.numel() * 4,
                full_state_bytes=L * B * H * P * N * 4,
-               state_mem_ratio=(L * B * H * P * N * 4) / (ckpt.numel() * 4 + ws_bytes),
-               bwd_workspace_bytes=ws_bytes)
+               state_mem_ratio=(L * B * H * P * N * 4) / (ckpt.numel() * 4 + ws_bytes + fwsb),
+               fwd_workspace_bytes=fwsb, bwd_workspace_bytes=ws_bytes)
     fwd_bytes = 2 * B * L * H * P * 2 + B * L * H * 2 + 2 * B * L * N * 2 + ckpt.numel() * 4
     out["fwd_GBs"] = fwd_bytes / tf / 1e9
     try:
@@ -260,8 +269,10 @@ def measure_gla_bwd(warmup, iters):
     q, k, v, gg, do = (dev(g.t(n)) for n in ("q", "k", "v", "g", "do"))
     o = torch.empty_like(v)
     ckpt = torch.empty((L + seg - 1) // seg, B, H, V, K, device="cuda", dtype=torch.float32)
+    fwsb = lr.lr_gla_scan_workspace_bytes(B, L, H, K, V, p["chunk"])
+    fws = torch.empty(fwsb, device="cuda", dtype=torch.uint8) if fwsb else None
     tf, _ = time_launches(lambda s: lr.lr_gla_scan(q, k, v, gg, chunk=p["chunk"], seg=seg, o=o,
-                                                   ckpt=ckpt), [None], warmup, iters)
+                                                   ckpt=ckpt, workspace=fws), [None], warmup, iters)
     ws = torch.empty(max(lr.lr_gla_scan_bwd_workspace_bytes(B, L, H, K, V, p["chunk"], seg), 16),
                      device="cuda", dtype=torch.uint8)
     tb, _ = time_launches(lambda s: lr.lr_gla_scan_bwd(q, k, v, gg, ckpt, do, chunk=p["chunk"],

@@ -195,7 +195,21 @@ lr_status lr_ssd_scan(lr_dtype io, lr_disc disc, int64_t B, int64_t L,
                       int64_t chunk, int64_t seg, const void* x,
                       const void* dt, const float* A, const void* Bm,
                       const void* Cm, const float* Dskip, const float* h0,
-                      void* y, float* h_last, float* ckpt, void* stream);
+                      void* y, float* h_last, float* ckpt, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* Optional workspace of lr_ssd_scan (0 when the sizes are invalid or when
+ * the call does not split the sequence).  With too few (batch, head) pairs
+ * to fill the GPU, the forward cuts the sequence into parts run side by
+ * side: a first launch computes each part's end state from zero and its
+ * decay product into the workspace (the (a, b) combine of the "K-Search
+ * for MLX" blog, section "A 20x faster prefill", applied to whole parts),
+ * and the main launch folds them into the state entering every part.
+ *   workspace == NULL: single pass, same results up to rounding.
+ *   workspace != NULL with fewer bytes than this: LR_E_WORKSPACE.
+ * The caller owns the workspace; its contents are scratch. */
+size_t lr_ssd_scan_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t P,
+                                   int64_t G, int64_t N, int64_t chunk);
 
 /* Workspace bytes needed by lr_ssd_scan_bwd for these sizes (0 on invalid
  * sizes).  The workspace holds per-head partial sums of dB and dC (bf16),
@@ -250,7 +264,11 @@ lr_status lr_gla_scan(lr_dtype io, int64_t B, int64_t L, int64_t H, int64_t K,
                       int64_t V, int64_t chunk, int64_t seg, const void* q,
                       const void* k, const void* v, const void* g,
                       const float* S0, void* o, float* S_last, float* ckpt,
-                      void* stream);
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Optional workspace of lr_gla_scan: as lr_ssd_scan_workspace_bytes. */
+size_t lr_gla_scan_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t K,
+                                   int64_t V, int64_t chunk);
 
 /* Workspace bytes needed by lr_gla_scan_bwd (0 on invalid sizes): fp32
  * partial sums of dk, dq and of the log-gate gradient per 64 columns of v,

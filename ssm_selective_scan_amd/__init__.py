@@ -141,12 +141,27 @@ def lr_selective_scan_bwd(x, dt, A, Bm, Cm, Dskip, ckpt, dy, dh_last=None, disc=
     return dict(dx=dx, ddt=ddt, dA=dA, dB=dB, dC=dC, dD=dD, dh0=dh0)
 
 
+def _fwd_workspace(workspace, need, dev):
+    """"auto": a fresh buffer of `need` bytes (None when no split is used);
+    None: single pass; a uint8 tensor: used as given."""
+    if isinstance(workspace, str):
+        return torch.empty(need, device=dev, dtype=torch.uint8) if need > 0 else None
+    return workspace
+
+
+def lr_ssd_scan_workspace_bytes(B, L, H, P, G, N, chunk=64) -> int:
+    return int(lib().lr_ssd_scan_workspace_bytes(B, L, H, P, G, N, chunk))
+
+
 def lr_ssd_scan(x, dt, A, Bm, Cm, Dskip=None, h0=None, disc="zoh", chunk=64, seg=0, y=None,
-                h_last=None, ckpt=None, want_last=False):
+                h_last=None, ckpt=None, want_last=False, workspace="auto"):
     """Mamba-2 SSD scan; x: [B, L, H, P], dt: [B, L, H], A: [H],
-    Bm, Cm: [B, L, G, N].  With seg > 0 also returns the segment checkpoints."""
+    Bm, Cm: [B, L, G, N].  With seg > 0 also returns the segment checkpoints.
+    workspace: "auto", None (single pass) or a uint8 device tensor of at
+    least lr_ssd_scan_workspace_bytes() bytes."""
     B, L, H, P = x.shape
     G, N = Bm.shape[2], Bm.shape[3]
+    ws = _fwd_workspace(workspace, lr_ssd_scan_workspace_bytes(B, L, H, P, G, N, chunk), x.device)
     if y is None:
         y = torch.empty_like(x)
     if want_last and h_last is None:
@@ -156,7 +171,8 @@ def lr_ssd_scan(x, dt, A, Bm, Cm, Dskip=None, h0=None, disc="zoh", chunk=64, seg
     check("lr_ssd_scan", lib().lr_ssd_scan(
         _io(x), _DISC[disc], B, L, H, P, G, N, chunk, seg, _ptr(x), _ptr(dt), _f32(A, "A"),
         _ptr(Bm), _ptr(Cm), _f32(Dskip, "Dskip"), _f32(h0, "h0"), _ptr(y),
-        _f32(h_last, "h_last"), _f32(ckpt, "ckpt"), _stream(x)))
+        _f32(h_last, "h_last"), _f32(ckpt, "ckpt"), _ptr(ws), ws.numel() if ws is not None else 0,
+        _stream(x)))
     return y, h_last, ckpt
 
 
@@ -187,13 +203,18 @@ def lr_ssd_scan_bwd(x, dt, A, Bm, Cm, Dskip, h0, ckpt, dy, dh_last=None, disc="z
     return dict(dx=dx, ddt=ddt, dA=dA, dB=dB, dC=dC, dD=dD, dh0=dh0)
 
 
+def lr_gla_scan_workspace_bytes(B, L, H, K, V, chunk=64) -> int:
+    return int(lib().lr_gla_scan_workspace_bytes(B, L, H, K, V, chunk))
+
+
 def lr_gla_scan(q, k, v, g, S0=None, chunk=64, seg=0, o=None, S_last=None, ckpt=None,
-                want_last=False):
+                want_last=False, workspace="auto"):
     """GLA; q, k: [B, L, H, K], v: [B, L, H, V], g: [B, L, H].  With seg > 0
     the segment checkpoints ([ceil(L/seg), B, H, V, K], the state transposed)
-    are returned as the third value."""
+    are returned as the third value.  workspace: as in lr_ssd_scan."""
     B, L, H, K = q.shape
     V = v.shape[3]
+    ws = _fwd_workspace(workspace, lr_gla_scan_workspace_bytes(B, L, H, K, V, chunk), q.device)
     if o is None:
         o = torch.empty_like(v)
     if want_last and S_last is None:
@@ -202,7 +223,8 @@ def lr_gla_scan(q, k, v, g, S0=None, chunk=64, seg=0, o=None, S_last=None, ckpt=
         ckpt = torch.empty((L + seg - 1) // seg, B, H, V, K, device=q.device, dtype=torch.float32)
     check("lr_gla_scan", lib().lr_gla_scan(
         _io(q), B, L, H, K, V, chunk, seg, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _f32(S0, "S0"),
-        _ptr(o), _f32(S_last, "S_last"), _f32(ckpt, "ckpt"), _stream(q)))
+        _ptr(o), _f32(S_last, "S_last"), _f32(ckpt, "ckpt"), _ptr(ws),
+        ws.numel() if ws is not None else 0, _stream(q)))
     return (o, S_last, ckpt) if seg > 0 else (o, S_last)
 
 

@@ -34,12 +34,15 @@ SIGNATURES = {
                                                                  _p, _p, _f32p, _f32p, _p, _sz,
                                                                  _p]),
     "lr_ssd_scan": (_int, [_int, _int, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _p, _p,
-                           _f32p, _p, _p, _f32p, _f32p, _p, _f32p, _f32p, _p]),
+                           _f32p, _p, _p, _f32p, _f32p, _p, _f32p, _f32p, _p, _sz, _p]),
+    "lr_ssd_scan_workspace_bytes": (_sz, [_i64] * 7),
     "lr_ssd_scan_bwd_workspace_bytes": (_sz, [_i64] * 8),
     "lr_ssd_scan_bwd": (_int, [_int, _int] + [_i64] * 8 + [_p, _p, _f32p, _p, _p, _f32p, _f32p,
                                                             _f32p, _p, _f32p, _p, _p, _f32p, _p,
                                                             _p, _f32p, _f32p, _p, _sz, _p]),
-    "lr_gla_scan": (_int, [_int] + [_i64] * 7 + [_p, _p, _p, _p, _f32p, _p, _f32p, _f32p, _p]),
+    "lr_gla_scan": (_int, [_int] + [_i64] * 7 + [_p, _p, _p, _p, _f32p, _p, _f32p, _f32p, _p, _sz,
+                                                 _p]),
+    "lr_gla_scan_workspace_bytes": (_sz, [_i64] * 6),
     "lr_gla_scan_bwd_workspace_bytes": (_sz, [_i64] * 7),
     "lr_gla_scan_bwd": (_int, [_int] + [_i64] * 7 + [_p, _p, _p, _p, _f32p, _p, _f32p, _p, _p, _p,
                                                      _p, _f32p, _p, _sz, _p]),

@@ -37,11 +37,14 @@ hipError_t launch_selective_bwd(int disc, const void* x, const void* dt, const f
 hipError_t launch_ssd_fwd(int disc, const void* x, const void* dt, const float* A, const void* Bm,
                           const void* Cm, const float* Dskip, const float* h0, void* y,
                           float* h_last, float* ckpt, int64_t B, int64_t L, int64_t H, int64_t P,
-                          int64_t G, int64_t N, int64_t seg, hipStream_t stream);
+                          int64_t G, int64_t N, int64_t seg, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
 hipError_t launch_gla_fwd(const void* q, const void* k, const void* v, const void* gate,
                           const float* S0, void* o, float* S_last, float* ckpt, int64_t B,
-                          int64_t L, int64_t H, int64_t K, int64_t V, int64_t seg,
-                          hipStream_t stream);
+                          int64_t L, int64_t H, int64_t K, int64_t V, int64_t seg, void* ws,
+                          size_t ws_bytes, hipStream_t stream);
+size_t ssd_fwd_workspace(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N);
+size_t gla_fwd_workspace(int64_t B, int64_t L, int64_t H, int64_t K, int64_t V);
 size_t gla_bwd_workspace(int64_t B, int64_t L, int64_t H, int64_t K, int64_t V, int64_t seg);
 hipError_t launch_gla_bwd(const void* q, const void* k, const void* v, const void* g,
                           const float* ckpt, const void* dout, const float* dS_last, void* dq,
@@ -260,16 +263,25 @@ lr_status lr_ssd_scan(lr_dtype io, lr_disc disc, int64_t B, int64_t L, int64_t H
                       int64_t G, int64_t N, int64_t chunk, int64_t seg, const void* x,
                       const void* dt, const float* A, const void* Bm, const void* Cm,
                       const float* Dskip, const float* h0, void* y, float* h_last, float* ckpt,
-                      void* stream) {
+                      void* workspace, size_t workspace_bytes, void* stream) {
   lr_status st = check_ssd_sizes(io, disc, B, L, H, P, G, N, chunk, seg);
   if (st != LR_OK) return st;
+  if (workspace != nullptr && workspace_bytes < lr::ssd_fwd_workspace(B, L, H, P, N))
+    return LR_E_WORKSPACE;
   if (A == nullptr) return LR_E_NULLPTR;
   if (B * L > 0 && any_null({x, dt, Bm, Cm, y})) return LR_E_NULLPTR;
   if (seg > 0 && B * L > 0 && ckpt == nullptr) return LR_E_NULLPTR;
-  if (!all_aligned({x, dt, A, Bm, Cm, Dskip, h0, y, h_last, ckpt})) return LR_E_ALIGN;
+  if (!all_aligned({x, dt, A, Bm, Cm, Dskip, h0, y, h_last, ckpt, workspace})) return LR_E_ALIGN;
   if (B == 0) return LR_OK;
   return hip_status(lr::launch_ssd_fwd(disc, x, dt, A, Bm, Cm, Dskip, h0, y, h_last, ckpt, B, L,
-                                       H, P, G, N, seg, static_cast<hipStream_t>(stream)));
+                                       H, P, G, N, seg, workspace, workspace_bytes,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+size_t lr_ssd_scan_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G,
+                                   int64_t N, int64_t chunk) {
+  if (check_ssd_sizes(LR_BF16, LR_DISC_ZOH, B, L, H, P, G, N, chunk, 0) != LR_OK) return 0;
+  return lr::ssd_fwd_workspace(B, L, H, P, N);
 }
 
 size_t lr_ssd_scan_bwd_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G,
@@ -330,15 +342,24 @@ static lr_status check_gla_sizes(int io, int64_t B, int64_t L, int64_t H, int64_
 lr_status lr_gla_scan(lr_dtype io, int64_t B, int64_t L, int64_t H, int64_t K, int64_t V,
                       int64_t chunk, int64_t seg, const void* q, const void* k, const void* v,
                       const void* g, const float* S0, void* o, float* S_last, float* ckpt,
-                      void* stream) {
+                      void* workspace, size_t workspace_bytes, void* stream) {
   const lr_status st = check_gla_sizes(io, B, L, H, K, V, chunk, seg);
   if (st != LR_OK) return st;
+  if (workspace != nullptr && workspace_bytes < lr::gla_fwd_workspace(B, L, H, K, V))
+    return LR_E_WORKSPACE;
   if (B * L > 0 && any_null({q, k, v, g, o})) return LR_E_NULLPTR;
   if (B * L > 0 && seg > 0 && ckpt == nullptr) return LR_E_NULLPTR;
-  if (!all_aligned({q, k, v, g, S0, o, S_last, ckpt})) return LR_E_ALIGN;
+  if (!all_aligned({q, k, v, g, S0, o, S_last, ckpt, workspace})) return LR_E_ALIGN;
   if (B == 0) return LR_OK;
   return hip_status(lr::launch_gla_fwd(q, k, v, g, S0, o, S_last, seg > 0 ? ckpt : nullptr, B, L,
-                                       H, K, V, seg, static_cast<hipStream_t>(stream)));
+                                       H, K, V, seg, workspace, workspace_bytes,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+size_t lr_gla_scan_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t K, int64_t V,
+                                   int64_t chunk) {
+  if (check_gla_sizes(LR_BF16, B, L, H, K, V, chunk, 0) != LR_OK) return 0;
+  return lr::gla_fwd_workspace(B, L, H, K, V);
 }
 
 size_t lr_gla_scan_bwd_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t K, int64_t V,

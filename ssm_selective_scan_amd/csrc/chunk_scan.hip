@@ -28,10 +28,17 @@
 // Every input tile sits in LDS exactly as it lies in memory (token rows):
 // operands whose contraction runs over tokens (x in M X, B and the
 // decay-weighted x in the state update) are read with gfx950's transposing
-// LDS read, so staging is a plain 16-byte copy.  Two LDS buffers: while
-// block k is computed from one, block k+1 (loaded from HBM into registers
-// during block k-1) is written into the other.  Row pitches are chosen per
-// tile for its read pattern (see ChunkBuf).  Two barriers per block.
+// LDS read, so staging is a plain 16-byte copy.  One LDS buffer (66 KB, so
+// two workgroups share a CU): block k+1, loaded from HBM into registers
+// during block k, is written into it once block k is done.  Row pitches are
+// chosen per tile for its read pattern (see ChunkBuf).
+//
+// With fewer than two workgroups per CU the sequence is cut into parts that
+// run side by side.  The parts' end states from a zero start and their decay
+// products come from a state-only pre-pass (SO); every part then folds those
+// of the parts before it into its entering state with the combine
+// (a2, b2) o (a1, b1) = (a2 a1, a2 b1 + b2) ("K-Search for MLX" blog,
+// section "A 20x faster prefill", combine equation), applied to whole parts.
 #include "common.hpp"
 
 namespace lr {
@@ -56,6 +63,14 @@ struct ChunkFwdArgs {
   int64_t B, L, H, P, G, seg;
   int64_t bc_row;       // elements between consecutive tokens of Bm/Cm
   int64_t st_p, st_n;   // state strides of p and n (SSD: N, 1; GLA: 1, V)
+  // Sequence split: part q covers blocks [q bpp, (q + 1) bpp).  part_state
+  // [q][B][H][P][N] holds the state at the end of part q started from zero,
+  // part_dec [q][B][H] the product of its decays (parts 0 .. nparts - 2).
+  float* part_state;
+  float* part_dec;
+  int64_t nparts;       // parts of the sequence
+  int64_t bpp;          // 64-token blocks per part
+  int64_t grid_parts;   // parts covered by this launch (main: nparts, pre-pass: nparts - 1)
 };
 
 // One block of inputs in LDS, token-major.  Every row starts 16-byte
@@ -111,7 +126,9 @@ __device__ __forceinline__ void chunk_scalars(uint16_t graw, bool ok, float Ah, 
   }
 }
 
-template <int MODE, int NS>
+// SO (state only): the pre-pass of a split sequence; it skips C, the mask and
+// the outputs and writes the part's end state and decay product.
+template <int MODE, int NS, bool SO>
 __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkFwdArgs g) {
   constexpr int NT = NS / 16;     // 16-row tiles of n
   constexpr int NK = NS / 32;     // 32-wide k steps over n
@@ -120,8 +137,10 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkFwdArgs g) {
   constexpr int kRowCB = NS / 8, kRowX = kCPS / 8;
   constexpr int kCB = kCQ * kRowCB / 256;   // C, B
   constexpr int kXC = kCQ * kRowX / 256;    // x
-  __shared__ ChunkBuf<NS> sm[2];
-  __shared__ uint16_t Ms[kCQ * kLdM];   // M[t][s]
+  // One input buffer: the next block is staged after the current one is
+  // done (66 KB of LDS, so two workgroups share a CU).
+  __shared__ ChunkBuf<NS> sm[1];
+  __shared__ uint16_t Ms[SO ? 8 : kCQ * kLdM];   // M[t][s]
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63;
@@ -129,8 +148,9 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkFwdArgs g) {
 
   const int64_t nps = g.P / kCPS;
   const int64_t wid = xcd_remap(blockIdx.x, gridDim.x);
-  const int64_t ps = wid % nps;
-  const int64_t bh = wid / nps;
+  const int64_t part = wid % g.grid_parts;
+  const int64_t ps = (wid / g.grid_parts) % nps;
+  const int64_t bh = (wid / g.grid_parts) / nps;
   const int64_t h = bh % g.H;
   const int64_t b = bh / g.H;
   const int64_t grp = (MODE == kModeGla) ? h : h / (g.H / g.G);
@@ -153,11 +173,28 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkFwdArgs g) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int64_t n = 16 * nt + 4 * g4 + r;
-      hacc[nt][r] = g.h0 ? g.h0[sbase + pcol * g.st_p + n * g.st_n] : 0.f;
+      hacc[nt][r] = (!SO && g.h0) ? g.h0[sbase + pcol * g.st_p + n * g.st_n] : 0.f;
+    }
+  }
+  // the state entering this part: fold the earlier parts' end states with the
+  // combine (h <- dec_q h + state_q), in order
+  const int64_t pstride = g.B * g.H * g.P * NS;
+  if (!SO) {
+    for (int64_t q = 0; q < part; ++q) {
+      const float dq = g.part_dec[q * g.B * g.H + b * g.H + h];
+      const float* sq = g.part_state + q * pstride + sbase + pcol * NS + 4 * g4;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(sq + 16 * nt);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) hacc[nt][r] = fmaf(dq, hacc[nt][r], v[r]);
+      }
     }
   }
 
-  const int64_t nblk = (g.L + kCQ - 1) / kCQ;
+  const int64_t nblk_all = (g.L + kCQ - 1) / kCQ;
+  const int64_t blk_lo = part * g.bpp;
+  const int64_t nblk = (blk_lo + g.bpp < nblk_all) ? blk_lo + g.bpp : nblk_all;   // end block
 
   // ---- register staging of one block: chunk q = tid + 256 k is token
   // q / kRow, columns 8 (q % kRow) .. + 7 (consecutive lanes read consecutive
@@ -189,7 +226,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkFwdArgs g) {
     if (nv == kCQ) {   // full block: no bounds
 #pragma unroll
       for (int k = 0; k < kCB; ++k) {
-        creg[k] = ld16(cblk, cboff[k]);
+        if constexpr (!SO) creg[k] = ld16(cblk, cboff[k]);
         breg[k] = ld16(bblk, cboff[k]);
       }
 #pragma unroll
@@ -201,7 +238,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkFwdArgs g) {
         creg[k] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
         breg[k] = creg[k];
         if (row < nv) {
-          creg[k] = ld16(cblk, cboff[k]);
+          if constexpr (!SO) creg[k] = ld16(cblk, cboff[k]);
           breg[k] = ld16(bblk, cboff[k]);
         }
       }
@@ -240,7 +277,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkFwdArgs g) {
 #pragma unroll
     for (int k = 0; k < kCB; ++k) {
       const int q = tid + 256 * k, row = q / kRowCB, col = 8 * (q % kRowCB);
-      *reinterpret_cast<u16x8*>(bf.Cs + row * kLdC + col) = creg[k];
+      if constexpr (!SO) *reinterpret_cast<u16x8*>(bf.Cs + row * kLdC + col) = creg[k];
       *reinterpret_cast<u16x8*>(bf.Bs + row * kLdB + col) = breg[k];
     }
 #pragma unroll
@@ -255,36 +292,31 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkFwdArgs g) {
     }
   };
 
-  if (nblk > 0) {
-    prefetch(0);
-    stage(0, sm[0]);
-    if (nblk > 1) prefetch(1);
+  if (blk_lo < nblk) {
+    prefetch(blk_lo);
+    stage(blk_lo, sm[0]);
+    if (blk_lo + 1 < nblk) prefetch(blk_lo + 1);
   }
   __syncthreads();
 
   // checkpoint s (the state entering token s * seg) goes to ckpt + s * ck_step
   const int64_t ck_step = g.B * g.H * g.P * NS;
-  float* ck_next = g.ckpt != nullptr ? g.ckpt + sbase + pcol * NS + 4 * g4 : nullptr;
-  int64_t ck_t = 0;
+  float* ck_base = (!SO && g.ckpt != nullptr) ? g.ckpt + sbase + pcol * NS + 4 * g4 : nullptr;
+  float dprod = 1.f;   // SO: product of the part's block decays
   // per-lane byte offset of this lane's 4 outputs of token c16 in a 16-token tile
   const uint32_t yoff = 2u * (static_cast<uint32_t>(c16) * static_cast<uint32_t>(xrow) + 16 * w + 4 * g4);
 
-  for (int64_t blk = 0; blk < nblk; ++blk) {
-    ChunkBuf<NS>& cur = sm[blk & 1];
+  for (int64_t blk = blk_lo; blk < nblk; ++blk) {
+    ChunkBuf<NS>& cur = sm[0];
     const int64_t t0 = blk * kCQ;
     const int nv = static_cast<int>((g.L - t0) < kCQ ? (g.L - t0) : kCQ);
 
-    if (ck_next != nullptr && t0 == ck_t) {
+    if (ck_base != nullptr && t0 % g.seg == 0) {
+      float* ck = ck_base + (t0 / g.seg) * ck_step;
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) *reinterpret_cast<f32x4*>(ck_next + 16 * nt) = hacc[nt];
-      ck_next += ck_step;
-      ck_t += g.seg;
+      for (int nt = 0; nt < NT; ++nt) *reinterpret_cast<f32x4*>(ck + 16 * nt) = hacc[nt];
     }
-    // next block into the other buffer, the one after into registers
-    if (blk + 1 < nblk) {
-      stage(blk + 1, sm[(blk + 1) & 1]);
-      if (blk + 2 < nblk) prefetch(blk + 2);
-    }
+    if constexpr (!SO) {
 
     // ---- decayed causal mask M[t][s]: 12 tiles of 16x16 (3 per wave), the
     //      10 with s-tile <= t-tile plus the all-zero (0,1) and (2,3) that
@@ -356,6 +388,8 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkFwdArgs g) {
       }
     }
 
+    }   // !SO
+
     // ---- h_next = 2^cum_end h_prev + B^T (decay-weighted x)
     {
       const float dec = (MODE == kModeSsdBilinear) ? fast_exp2(cur.cum[kCQ - 1]) * cur.sg[kCQ - 1]
@@ -368,11 +402,26 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkFwdArgs g) {
         hacc[nt] = mfma16x16x32(lds_tile_tr(cur.Bs, kLdB, 0, 16 * nt, lane), xw0, hacc[nt]);
         hacc[nt] = mfma16x16x32(lds_tile_tr(cur.Bs, kLdB, 32, 16 * nt, lane), xw1, hacc[nt]);
       }
+      dprod *= dec;
     }
     __syncthreads();
+    // the next block into the buffer (every wave is done with it), the one
+    // after into registers
+    if (blk + 1 < nblk) {
+      stage(blk + 1, sm[0]);
+      if (blk + 2 < nblk) prefetch(blk + 2);
+      __syncthreads();
+    }
   }
 
-  if (g.h_last != nullptr) {
+  if constexpr (SO) {
+    float* out = g.part_state + part * pstride + sbase + pcol * NS + 4 * g4;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) *reinterpret_cast<f32x4*>(out + 16 * nt) = hacc[nt];
+    if (tid == 0) g.part_dec[part * g.B * g.H + b * g.H + h] = dprod;
+    return;
+  }
+  if (g.h_last != nullptr && nblk == nblk_all) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -383,18 +432,63 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkFwdArgs g) {
   }
 }
 
+// Sequence split of the forward: with fewer than two workgroups per CU
+// (512 on MI355X's 256 CUs) the sequence is cut into parts of at least 8
+// blocks, each run by its own workgroups from the state the pre-pass and
+// the fold give it.  Workspace: the parts' end states and decay products.
+struct ChunkSplit { int64_t nblk, nparts, bpp, dec_off; size_t bytes; };
+static ChunkSplit chunk_split(int64_t B, int64_t L, int64_t H, int64_t P, int64_t NS) {
+  ChunkSplit sp;
+  sp.nblk = (L + kCQ - 1) / kCQ;
+  const int64_t nwg = B * H * (P / kCPS);
+  int64_t want = nwg > 0 ? (512 + nwg - 1) / nwg : 1;
+  const int64_t cap = sp.nblk / 8 > 1 ? sp.nblk / 8 : 1;
+  if (want > cap) want = cap;
+  if (want > 16) want = 16;
+  if (want < 1) want = 1;
+  sp.bpp = sp.nblk > 0 ? (sp.nblk + want - 1) / want : 1;
+  sp.nparts = sp.nblk > 0 ? (sp.nblk + sp.bpp - 1) / sp.bpp : 1;
+  const int64_t st = (sp.nparts - 1) * B * H * P * NS * 4;
+  sp.dec_off = (st + 255) & ~int64_t(255);
+  sp.bytes = sp.nparts > 1 ? static_cast<size_t>(sp.dec_off + (sp.nparts - 1) * B * H * 4) : 0;
+  return sp;
+}
+
+size_t ssd_fwd_workspace(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N) {
+  return chunk_split(B, L, H, P, N).bytes;
+}
+size_t gla_fwd_workspace(int64_t B, int64_t L, int64_t H, int64_t K, int64_t V) {
+  return chunk_split(B, L, H, V, K).bytes;
+}
+
 template <int MODE, int NS>
-static hipError_t launch_chunk(const ChunkFwdArgs& a, hipStream_t stream) {
+static hipError_t launch_chunk(ChunkFwdArgs a, void* ws, size_t ws_bytes, hipStream_t stream) {
   const int64_t nwg = a.B * a.H * (a.P / kCPS);
-  hipLaunchKernelGGL((chunk_fwd_kernel<MODE, NS>), dim3(static_cast<unsigned>(nwg)), dim3(256),
-                     0, stream, a);
+  const ChunkSplit sp = chunk_split(a.B, a.L, a.H, a.P, NS);
+  a.nparts = 1;
+  a.bpp = sp.nblk > 0 ? sp.nblk : 1;
+  a.part_state = nullptr;
+  a.part_dec = nullptr;
+  if (ws != nullptr && sp.nparts > 1 && ws_bytes >= sp.bytes) {
+    a.nparts = sp.nparts;
+    a.bpp = sp.bpp;
+    a.part_state = static_cast<float*>(ws);
+    a.part_dec = reinterpret_cast<float*>(static_cast<char*>(ws) + sp.dec_off);
+    a.grid_parts = a.nparts - 1;   // pre-pass: the end states of parts 0 .. nparts - 2
+    hipLaunchKernelGGL((chunk_fwd_kernel<MODE, NS, true>),
+                       dim3(static_cast<unsigned>(nwg * a.grid_parts)), dim3(256), 0, stream, a);
+  }
+  a.grid_parts = a.nparts;
+  hipLaunchKernelGGL((chunk_fwd_kernel<MODE, NS, false>),
+                     dim3(static_cast<unsigned>(nwg * a.nparts)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_ssd_fwd(int disc, const void* x, const void* dt, const float* A, const void* Bm,
                           const void* Cm, const float* Dskip, const float* h0, void* y,
                           float* h_last, float* ckpt, int64_t B, int64_t L, int64_t H, int64_t P,
-                          int64_t G, int64_t N, int64_t seg, hipStream_t stream) {
+                          int64_t G, int64_t N, int64_t seg, void* ws, size_t ws_bytes,
+                          hipStream_t stream) {
   ChunkFwdArgs a;
   a.x = static_cast<const uint16_t*>(x);
   a.gate = static_cast<const uint16_t*>(dt);
@@ -411,24 +505,24 @@ hipError_t launch_ssd_fwd(int disc, const void* x, const void* dt, const float* 
   a.st_p = N; a.st_n = 1;
   if (N == 128) {
     switch (disc) {
-      case 1: return launch_chunk<kModeSsdEuler, 128>(a, stream);
-      case 2: return launch_chunk<kModeSsdBilinear, 128>(a, stream);
-      case 3: return launch_chunk<kModeSsdDirac, 128>(a, stream);
-      default: return launch_chunk<kModeSsdZoh, 128>(a, stream);
+      case 1: return launch_chunk<kModeSsdEuler, 128>(a, ws, ws_bytes, stream);
+      case 2: return launch_chunk<kModeSsdBilinear, 128>(a, ws, ws_bytes, stream);
+      case 3: return launch_chunk<kModeSsdDirac, 128>(a, ws, ws_bytes, stream);
+      default: return launch_chunk<kModeSsdZoh, 128>(a, ws, ws_bytes, stream);
     }
   }
   switch (disc) {
-    case 1: return launch_chunk<kModeSsdEuler, 64>(a, stream);
-    case 2: return launch_chunk<kModeSsdBilinear, 64>(a, stream);
-    case 3: return launch_chunk<kModeSsdDirac, 64>(a, stream);
-    default: return launch_chunk<kModeSsdZoh, 64>(a, stream);
+    case 1: return launch_chunk<kModeSsdEuler, 64>(a, ws, ws_bytes, stream);
+    case 2: return launch_chunk<kModeSsdBilinear, 64>(a, ws, ws_bytes, stream);
+    case 3: return launch_chunk<kModeSsdDirac, 64>(a, ws, ws_bytes, stream);
+    default: return launch_chunk<kModeSsdZoh, 64>(a, ws, ws_bytes, stream);
   }
 }
 
 hipError_t launch_gla_fwd(const void* q, const void* k, const void* v, const void* gate,
                           const float* S0, void* o, float* S_last, float* ckpt, int64_t B,
-                          int64_t L, int64_t H, int64_t K, int64_t V, int64_t seg,
-                          hipStream_t stream) {
+                          int64_t L, int64_t H, int64_t K, int64_t V, int64_t seg, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
   ChunkFwdArgs a;
   a.x = static_cast<const uint16_t*>(v);
   a.gate = static_cast<const uint16_t*>(gate);
@@ -443,8 +537,8 @@ hipError_t launch_gla_fwd(const void* q, const void* k, const void* v, const voi
   a.B = B; a.L = L; a.H = H; a.P = V; a.G = H; a.seg = seg > 0 ? seg : 1;
   a.bc_row = H * K;
   a.st_p = 1; a.st_n = V;
-  if (K == 128) return launch_chunk<kModeGla, 128>(a, stream);
-  return launch_chunk<kModeGla, 64>(a, stream);
+  if (K == 128) return launch_chunk<kModeGla, 128>(a, ws, ws_bytes, stream);
+  return launch_chunk<kModeGla, 64>(a, ws, ws_bytes, stream);
 }
 
 }  // namespace lr

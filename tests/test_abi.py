@@ -113,9 +113,10 @@ def test_selective_validation(L):
     assert sel(L, B=0, x=None, dt=None, Bm=None, Cm=None, y=None) == OK
 
 
-def ssd(L, io=1, disc=0, B=1, Lq=64, H=2, Pp=64, G=1, N=128, chunk=64, seg=0, x=P, ck=None):
+def ssd(L, io=1, disc=0, B=1, Lq=64, H=2, Pp=64, G=1, N=128, chunk=64, seg=0, x=P, ck=None,
+        ws=None, wsb=0):
     return L.lr_ssd_scan(io, disc, B, Lq, H, Pp, G, N, chunk, seg, x, P, P, P, P, None, None, P,
-                         None, ck, None)
+                         None, ck, ws, wsb, None)
 
 
 def test_ssd_validation(L):
@@ -129,6 +130,22 @@ def test_ssd_validation(L):
     assert ssd(L, x=None) == NULL
     assert ssd(L, x=MIS) == ALIGN
     assert ssd(L, B=0, x=None) == OK
+
+
+def test_ssd_fwd_workspace(L):
+    # few (batch, head) pairs and a long sequence: the forward splits the sequence
+    need = L.lr_ssd_scan_workspace_bytes(1, 4096, 2, 64, 1, 128, 64)
+    assert need > 0
+    assert ssd(L, Lq=4096, ws=P, wsb=need - 1) == WS
+    assert ssd(L, Lq=4096, ws=MIS, wsb=need) == ALIGN
+    assert ssd(L, Lq=4096, x=None, ws=P, wsb=need) == NULL
+    # enough workgroups already, or too short to split: no workspace
+    assert L.lr_ssd_scan_workspace_bytes(8, 4096, 64, 64, 1, 128, 64) == 0
+    assert L.lr_ssd_scan_workspace_bytes(1, 256, 2, 64, 1, 128, 64) == 0
+    # invalid sizes
+    assert L.lr_ssd_scan_workspace_bytes(1, 4096, 2, 48, 1, 128, 64) == 0
+    assert L.lr_gla_scan_workspace_bytes(1, 4096, 2, 128, 128, 64) > 0
+    assert L.lr_gla_scan_workspace_bytes(1, 4096, 2, 32, 128, 64) == 0
 
 
 def test_ssd_bwd_validation(L):
@@ -150,8 +167,9 @@ def test_ssd_bwd_validation(L):
 
 
 def test_gla_validation(L):
-    def gla(io=1, K=128, V=128, chunk=64, seg=0, q=P, g=P, ck=None):
-        return L.lr_gla_scan(io, 1, 64, 2, K, V, chunk, seg, q, P, P, g, None, P, None, ck, None)
+    def gla(io=1, K=128, V=128, chunk=64, seg=0, q=P, g=P, ck=None, ws=None, wsb=0, Lq=64):
+        return L.lr_gla_scan(io, 1, Lq, 2, K, V, chunk, seg, q, P, P, g, None, P, None, ck, ws, wsb,
+                             None)
     assert gla(io=3) == DTYPE
     assert gla(K=32) == UNSUP
     assert gla(V=96) == UNSUP
@@ -162,6 +180,8 @@ def test_gla_validation(L):
     assert gla(seg=64) == NULL          # checkpoints requested without a buffer
     assert gla(g=MIS) == ALIGN
     assert gla(seg=64, ck=MIS) == ALIGN
+    need = L.lr_gla_scan_workspace_bytes(1, 4096, 2, 128, 128, 64)
+    assert gla(Lq=4096, ws=P, wsb=need - 1) == WS
 
 
 def test_gla_bwd_validation(L):

@@ -136,6 +136,36 @@ def test_ssd_chunk_invariance_and_determinism():
     assert torch.equal(y64, y256) and torch.equal(h64, h256)
 
 
+@pytest.mark.parametrize("disc,L,seg,dt_scale,N,G", [("zoh", 1100, 128, 1.0, 128, 1),
+                                                      ("euler", 2000, 64, 1.0, 64, 2),
+                                                      ("bilinear", 1600, 192, 32.0, 128, 1),
+                                                      ("dirac", 1031, 0, 1.0, 128, 1)])
+def test_ssd_sequence_split(disc, L, seg, dt_scale, N, G):
+    """Few (batch, head) pairs and a long sequence: the forward runs in parts
+    (state-only pre-pass, then the fold of the parts' end states), including
+    a ragged last part, checkpoints across part boundaries and, for bilinear,
+    negative decays inside the parts' decay products."""
+    B, H, P = 1, 2, 64
+    print(f"ssd split disc={disc} L={L} seg={seg} dt_scale={dt_scale} N={N} G={G}", flush=True)
+    assert lr.lr_ssd_scan_workspace_bytes(B, L, H, P, G, N) > 0
+    g = lrgen.make(3, B=B, L=L, H=H, P=P, G=G, N=N)
+    dt = lrgen.round_bf16(g["dt"] * dt_scale)
+    h0 = lrgen.state_normal((B, H, P, N), 3, std=0.3)
+    args = (dev(g.t("x")), dev(dt, "bf16"), dev(g.t("A")), dev(g.t("B")), dev(g.t("C")),
+            dev(g.t("Dskip")), dev(h0, "f32"))
+    y, hl, ck = lr.lr_ssd_scan(*args, disc=disc, seg=seg, want_last=True)
+    y1, hl1, _ = lr.lr_ssd_scan(*args, disc=disc, seg=seg, want_last=True, workspace=None)
+    _sync()
+    ry, rl, rck = oracle.ssd_scan(g["x"], dt, g["A"], g["B"], g["C"], g["Dskip"], h0, disc,
+                                  seg=seg)
+    check("y", y, ry, TOL["bf16"])
+    check("h_last", hl, rl, TOL["bf16"])
+    if seg:
+        check("ckpt", ck, rck, TOL["bf16"])
+    check("y (single pass)", y1, ry, TOL["bf16"])
+    check("h_last (single pass)", hl1, rl, TOL["bf16"])
+
+
 def test_ssd_full_size_sampled():
     print("ssd full size (B=8, L=2048, H=32, P=64, N=128), sampled heads", flush=True)
     g = lrgen.make(3)
@@ -162,6 +192,26 @@ def test_gla_parity(B, L, H, K, V):
     ro, rS = oracle.gla_scan(g["q"], g["k"], g["v"], g["g"], S0)
     check("o", o, ro, TOL["bf16"])
     check("S_last", Sl, rS, TOL["bf16"])
+
+
+def test_gla_sequence_split():
+    """GLA with two 64-column slices of V, run in sequence parts, with S0 and
+    checkpoints across part boundaries."""
+    B, L, H, K, V, seg = 1, 1500, 2, 128, 128, 128
+    print(f"gla split B={B} L={L} H={H} K={K} V={V} seg={seg}", flush=True)
+    assert lr.lr_gla_scan_workspace_bytes(B, L, H, K, V) > 0
+    g = lrgen.make(4, B=B, L=L, H=H, K=K, V=V)
+    S0 = lrgen.state_normal((B, H, K, V), 4, std=0.3)
+    o, Sl, ck = lr.lr_gla_scan(dev(g.t("q")), dev(g.t("k")), dev(g.t("v")), dev(g.t("g")),
+                               S0=dev(S0), seg=seg, want_last=True)
+    _sync()
+    ro, rS = oracle.gla_scan(g["q"], g["k"], g["v"], g["g"], S0)
+    check("o", o, ro, TOL["bf16"])
+    check("S_last", Sl, rS, TOL["bf16"])
+    for s_ in (0, 5, 11):
+        _, st = oracle.gla_scan(g["q"][:, :s_ * seg], g["k"][:, :s_ * seg], g["v"][:, :s_ * seg],
+                                g["g"][:, :s_ * seg], S0)
+        check(f"ckpt[{s_}]", host(ck[s_]), np.swapaxes(st, -1, -2), TOL["bf16"])
 
 
 def test_gla_full_size_sampled():
