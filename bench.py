@@ -460,7 +460,7 @@ def main():
     roofline = {"bound": "alu", "achieved": ops / kt / 1e12, "peak": VALU_PEAK_TOPS,
                 "unit": "Tops/s (fp32 VALU lane-ops)",
                 "frac": ops / kt / 1e12 / VALU_PEAK_TOPS, "traffic": traffic,
-                "kernel": "selective_scan_kernel<bf16, ZOH>",
+                "kernel": "selective_pair_kernel<bf16, ZOH>",
                 "alg_ops_per_launch": ops, "alg_bytes_per_launch": nbytes,
                 "hbm_GBs": nbytes / kt / 1e9, "hbm_frac": nbytes / kt / 1e9 / HBM_PEAK_GBS}
 

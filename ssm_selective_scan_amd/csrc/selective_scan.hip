@@ -7,7 +7,8 @@
 // Research blog "K-Search for MLX", section "Translating CUDA expertise to
 // MLX": evaluate exp as exp2 with log2(e) folded into the argument.)
 //
-// Work split: a workgroup owns one batch row and 64 consecutive channels d
+// Work split (the paired layout used for 8 < N <= 16 is described at
+// selective_pair_kernel): a workgroup owns one batch row and 64 consecutive channels d
 // (lane = d, so every per-token load and store is a coalesced row segment).
 // Its waves split the state index n: wave w owns n in [NPW w, NPW w + NPW),
 // so the (d, n) chains it carries stay in registers for the whole sequence
@@ -26,6 +27,7 @@
 // Bilinear (Tustin): e = (1 + dt A/2) / (1 - dt A/2), phi = dt / (1 - dt A/2),
 // one v_rcp_f32 in place of the exponential; dirac: phi = 1.
 #include <type_traits>
+#include <utility>
 
 #include "common.hpp"
 
@@ -132,40 +134,68 @@ struct SelStage {
   }
 };
 
-// One group of GS steps of this wave's NPW chains: the LDS values it needs
-// (x, dt of the lane's channel; B, C of the wave's state indices) and the
-// recurrence over them.
-template <int NPW, int GS>
+// One step of one chain: h <- e h + phi B x for the discretisation DISC
+// (b = B of the step and state index, ux = dt x for Euler and bilinear).
+template <int DISC, bool PRECISE>
+__device__ __forceinline__ void sel_update(float& h, float b, float xt, float dtt, float ux,
+                                           float A2, float iA, float An) {
+  if (DISC == kDiscBilinear) {
+    // A2 holds A / 2: e = (1 + l/2) / (1 - l/2), phi = dt / (1 - l/2)
+    const float lh = dtt * A2;
+    const float r = __builtin_amdgcn_rcpf(1.f - lh);
+    h = fmaf((1.f + lh) * r, h, (b * ux) * r);
+    return;
+  }
+  const float e = fast_exp2(dtt * A2);
+  if (DISC == kDiscEuler) {
+    h = fmaf(e, h, b * ux);
+  } else if (DISC == kDiscDirac) {
+    h = fmaf(e, h, b * xt);
+  } else if (!PRECISE) {
+    const float v = (b * xt) * iA;
+    h = fmaf(e, h + v, -v);
+  } else {
+    const float l = dtt * An;
+    const float ser = dtt * fmaf(l, fmaf(l, fmaf(l, 1.f / 24.f, 1.f / 6.f), 0.5f), 1.f);
+    const float phi = fabsf(l) < 0.1f ? ser : (e - 1.f) * iA;
+    h = fmaf(e, h, phi * (b * xt));
+  }
+}
+
+// One group of GS steps of a lane's NPW chains: the LDS values it needs
+// (x, dt of the lane's channel; B, C of its state indices) and the
+// recurrence over them.  XLD, BLD: row strides of the x/dt and B/C tiles.
+template <int NPW, int GS, int XLD = 64, int BLD = 64>
 struct SelGroup {
   float xv[GS], dv[GS], bb[GS][NPW], cc[GS][NPW];
 
+  // xcol: the lane's column of the x/dt tiles; n0: its first state index
   __device__ __forceinline__ void read(const float* xs, const float* dts, const float* Bs,
-                                       const float* Cs, int g0, int lane, int n0) {
+                                       const float* Cs, int g0, int xcol, int n0) {
 #pragma unroll
     for (int i = 0; i < GS; ++i) {
       const int tt = g0 + i;
-      xv[i] = xs[tt * 64 + lane];
-      dv[i] = dts[tt * 64 + lane];
+      xv[i] = xs[tt * XLD + xcol];
+      dv[i] = dts[tt * XLD + xcol];
       if constexpr (NPW == 4) {
-        const float4 b4 = *reinterpret_cast<const float4*>(Bs + tt * 64 + n0);
-        const float4 c4 = *reinterpret_cast<const float4*>(Cs + tt * 64 + n0);
+        const float4 b4 = *reinterpret_cast<const float4*>(Bs + tt * BLD + n0);
+        const float4 c4 = *reinterpret_cast<const float4*>(Cs + tt * BLD + n0);
         bb[i][0] = b4.x; bb[i][1] = b4.y; bb[i][2] = b4.z; bb[i][3] = b4.w;
         cc[i][0] = c4.x; cc[i][1] = c4.y; cc[i][2] = c4.z; cc[i][3] = c4.w;
       } else {
-        const float2 b2 = *reinterpret_cast<const float2*>(Bs + tt * 64 + n0);
-        const float2 c2 = *reinterpret_cast<const float2*>(Cs + tt * 64 + n0);
+        const float2 b2 = *reinterpret_cast<const float2*>(Bs + tt * BLD + n0);
+        const float2 c2 = *reinterpret_cast<const float2*>(Cs + tt * BLD + n0);
         bb[i][0] = b2.x; bb[i][1] = b2.y;
         cc[i][0] = c2.x; cc[i][1] = c2.y;
       }
     }
   }
 
-  // yp_lane: this lane's partial-readout slot of the group's first step
+  // yv[i]: the lane's partial readout sum_j C h of step i
   template <int DISC, bool PRECISE>
   __device__ __forceinline__ void step(float (&h)[NPW], const float (&A2)[NPW],
                                        const float (&iA)[NPW], const float (&An)[NPW],
-                                       float* yp_lane) const {
-    float yv[GS];
+                                       float (&yv)[GS]) const {
 #pragma unroll
     for (int i = 0; i < GS; ++i) {
       const float xt = xv[i], dtt = dv[i];
@@ -173,35 +203,12 @@ struct SelGroup {
       float yj[NPW];
 #pragma unroll
       for (int j = 0; j < NPW; ++j) {
-        if (DISC == kDiscBilinear) {
-          // A2 holds A / 2: e = (1 + l/2) / (1 - l/2), phi = dt / (1 - l/2)
-          const float lh = dtt * A2[j];
-          const float r = __builtin_amdgcn_rcpf(1.f - lh);
-          h[j] = fmaf((1.f + lh) * r, h[j], (bb[i][j] * ux) * r);
-          yj[j] = cc[i][j] * h[j];
-          continue;
-        }
-        const float e = fast_exp2(dtt * A2[j]);
-        if (DISC == kDiscEuler) {
-          h[j] = fmaf(e, h[j], bb[i][j] * ux);
-        } else if (DISC == kDiscDirac) {
-          h[j] = fmaf(e, h[j], bb[i][j] * xt);
-        } else if (!PRECISE) {
-          const float v = (bb[i][j] * xt) * iA[j];
-          h[j] = fmaf(e, h[j] + v, -v);
-        } else {
-          const float l = dtt * An[j];
-          const float ser = dtt * fmaf(l, fmaf(l, fmaf(l, 1.f / 24.f, 1.f / 6.f), 0.5f), 1.f);
-          const float phi = fabsf(l) < 0.1f ? ser : (e - 1.f) * iA[j];
-          h[j] = fmaf(e, h[j], phi * (bb[i][j] * xt));
-        }
+        sel_update<DISC, PRECISE>(h[j], bb[i][j], xt, dtt, ux, A2[j], iA[j], An[j]);
         yj[j] = cc[i][j] * h[j];
       }
       yv[i] = (NPW == 4) ? (yj[0] + yj[1 % NPW]) + (yj[2 % NPW] + yj[3 % NPW])
                          : yj[0] + yj[1 % NPW];
     }
-#pragma unroll
-    for (int i = 0; i < GS; ++i) yp_lane[i * 64] = yv[i];
   }
 };
 
@@ -266,13 +273,18 @@ __device__ __forceinline__ void selective_body(
     // reads of the next group are issued before the current group is
     // computed, and a group's partial readouts are stored after it.
     SelGroup<NPW, GS> ga, gb;
+    float yv[GS];
     ga.read(xs, dts, Bs, Cs, 0, lane, n0);
 #pragma unroll 1
     for (int gs = 0; gs < TT; gs += 2 * GS) {
       gb.read(xs, dts, Bs, Cs, gs + GS, lane, n0);
-      ga.template step<DISC, PRECISE>(h, A2, iA, An, yp + (w * TT + gs) * 64 + lane);
+      ga.template step<DISC, PRECISE>(h, A2, iA, An, yv);
+#pragma unroll
+      for (int i = 0; i < GS; ++i) yp[(w * TT + gs + i) * 64 + lane] = yv[i];
       if (gs + 2 * GS < TT) ga.read(xs, dts, Bs, Cs, gs + 2 * GS, lane, n0);
-      gb.template step<DISC, PRECISE>(h, A2, iA, An, yp + (w * TT + gs + GS) * 64 + lane);
+      gb.template step<DISC, PRECISE>(h, A2, iA, An, yv);
+#pragma unroll
+      for (int i = 0; i < GS; ++i) yp[(w * TT + gs + GS + i) * 64 + lane] = yv[i];
     }
     __syncthreads();
 
@@ -372,6 +384,384 @@ __global__ __launch_bounds__(64 * NW) void selective_scan_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Paired-lane layout, used for 8 < N <= 16.  A workgroup of NW waves owns 32
+// channels of one batch row: lanes l and l + 32 carry channel l & 31, and
+// wave w holds the state indices 4 w + 2 (l >> 5) + {0, 1}.  A step's readout
+// is summed over the two lane halves first: gfx950's permlane32_swap
+// exchanges the upper 32 lanes of one register with the lower 32 of another,
+// so one swap and one add give the half-sums of two consecutive steps (lanes
+// below 32 the first step, the others the second).  The NW per-wave partials
+// are then added through LDS as above, half as many of them per output.
+// With 32 channels per workgroup there are twice as many workgroups as with
+// 64, so two of them share a CU and the barriers and readout of one overlap
+// the recurrence of the other.
+constexpr int kPairCT = 32;
+
+// DPP row_newbcast:K: every lane reads lane K of its 16-lane row.  With
+// bound_ctrl set the compiler folds the move into the multiply that uses
+// it, as a DPP source operand.
+template <int K>
+__device__ __forceinline__ float row_bcast(float v) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + K, 0xf, 0xf, true));
+}
+
+template <int I0, typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, I0 + Is>{}), ...);
+}
+template <int I0, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl<I0>(f, std::make_integer_sequence<int, N>{});
+}
+
+// A group of GS steps in the paired layout.  B of a block of 16 steps is
+// held one step per lane of each 16-lane row (lane 16 r + i: step i, the
+// row's two state indices) and broadcast to the row with DPP inside the
+// multiply B x, so B costs one LDS read per lane and block instead of one
+// per lane and step (this relieves the LDS, whose reads otherwise approach
+// the VALU time).  C stays an LDS read per step: broadcasting it would add
+// a move, as its product is an FMA, which takes no DPP operand.  I0: the
+// position of the group inside its block.
+template <int GS, int NP>
+struct PairGroup {
+  float xv[GS], dv[GS], cc[GS][2];
+
+  __device__ __forceinline__ void read(const float* xs, const float* dts, const float* Cs, int g0,
+                                       int col, int n0) {
+#pragma unroll
+    for (int i = 0; i < GS; ++i) {
+      xv[i] = xs[(g0 + i) * kPairCT + col];
+      dv[i] = dts[(g0 + i) * kPairCT + col];
+      const float2 c2 = *reinterpret_cast<const float2*>(Cs + (g0 + i) * NP + n0);
+      cc[i][0] = c2.x; cc[i][1] = c2.y;
+    }
+  }
+
+  template <int DISC, bool PRECISE, int I0>
+  __device__ __forceinline__ void step(float (&h)[2], const float (&A2)[2], const float (&iA)[2],
+                                       const float (&An)[2], const float (&vb)[2],
+                                       float (&yv)[GS]) const {
+    static_for<0, GS>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      const float xt = xv[i], dtt = dv[i];
+      const float ux = (DISC == kDiscEuler || DISC == kDiscBilinear) ? dtt * xt : 0.f;
+      float yj[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        sel_update<DISC, PRECISE>(h[j], row_bcast<I0 + i>(vb[j]), xt, dtt, ux, A2[j], iA[j], An[j]);
+        yj[j] = cc[i][j] * h[j];
+      }
+      yv[i] = yj[0] + yj[1];
+    });
+  }
+};
+
+// Register staging of one tile: x and dt as 8-channel chunks (one 16-byte
+// load for bf16 when VEC), B and C as the contiguous TT*N block of the tile.
+template <typename T, int TT, int NP, int NT, bool VEC>
+struct PairStage {
+  static constexpr int kRowChunks = kPairCT / 8;
+  static constexpr int kChunks = 2 * TT * kRowChunks;   // x chunks, then dt chunks
+  static constexpr int MK = (kChunks + NT - 1) / NT;
+  static constexpr int ME = (TT * NP + NT - 1) / NT;    // B/C elements per thread (N <= NP)
+  T r[MK][8];
+  T br[ME], cr[ME];
+  int goff[MK], lofs[MK], row[MK];   // offset from the tile base, LDS offset, token
+  bool isdt[MK];
+  int ce[ME], clds[ME], crow[ME];
+
+  __device__ __forceinline__ void init(int64_t D, int N) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int k = 0; k < MK; ++k) {
+      const int c = tid + k * NT;
+      const int cc = c % (TT * kRowChunks);
+      isdt[k] = c >= TT * kRowChunks;
+      row[k] = c < kChunks ? cc / kRowChunks : TT;   // TT marks an unused slot
+      goff[k] = (cc / kRowChunks) * static_cast<int>(D) + 8 * (cc % kRowChunks);
+      lofs[k] = (isdt[k] ? TT * kPairCT : 0) + (cc / kRowChunks) * kPairCT + 8 * (cc % kRowChunks);
+    }
+#pragma unroll
+    for (int k = 0; k < ME; ++k) {
+      const int e = tid + k * NT;
+      crow[k] = e / N;
+      ce[k] = e;
+      clds[k] = crow[k] * NP + (e - crow[k] * N);
+    }
+  }
+
+  // x0, dt0: tile base (token t0, channel d0); B0, C0: tile base of Bm, Cm.
+  // nt = tokens of the tile inside the sequence; dcols = channels < D left.
+  __device__ __forceinline__ void load(const T* x0, const T* dt0, const T* B0, const T* C0, int nt,
+                                       int dcols, int N) {
+#pragma unroll
+    for (int k = 0; k < MK; ++k) {
+      const T* src = (isdt[k] ? dt0 : x0) + goff[k];
+      const int c8 = lofs[k] & (kPairCT - 1);
+      if (VEC && row[k] < nt && c8 + 8 <= dcols) {
+        if constexpr (sizeof(T) == 2) {
+          const u16x8 v = *reinterpret_cast<const u16x8*>(src);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) r[k][i] = v[i];
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; i += 4) {
+            const float4 v = *reinterpret_cast<const float4*>(src + i);
+            r[k][i] = v.x; r[k][i + 1] = v.y; r[k][i + 2] = v.z; r[k][i + 3] = v.w;
+          }
+        }
+      } else if (!VEC) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) r[k][i] = (row[k] < nt && c8 + i < dcols) ? src[i] : T(0);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) r[k][i] = T(0);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < ME; ++k) {
+      const bool ok = ce[k] < nt * N;
+      br[k] = ok ? B0[ce[k]] : T(0);
+      cr[k] = ok ? C0[ce[k]] : T(0);
+    }
+  }
+
+  // xs: x tile followed by the dt tile
+  __device__ __forceinline__ void store(float* xs, float* Bs, float* Cs) const {
+#pragma unroll
+    for (int k = 0; k < MK; ++k) {
+      if (row[k] < TT) {
+        float f[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = Io<T>::cvt(r[k][i]);
+        float* p = xs + lofs[k];
+        *reinterpret_cast<float4*>(p) = make_float4(f[0], f[1], f[2], f[3]);
+        *reinterpret_cast<float4*>(p + 4) = make_float4(f[4], f[5], f[6], f[7]);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < ME; ++k) {
+      if (crow[k] < TT) {
+        Bs[clds[k]] = Io<T>::cvt(br[k]);
+        Cs[clds[k]] = Io<T>::cvt(cr[k]);
+      }
+    }
+  }
+};
+
+template <typename T, int DISC, bool PRECISE, int TT, int NW, bool VEC, bool CK>
+__device__ __forceinline__ void pair_body(
+    const T* __restrict__ x, const T* __restrict__ dt, const T* __restrict__ Bm,
+    const T* __restrict__ Cm, T* __restrict__ y, float* __restrict__ smem, float (&h)[2],
+    const float (&A2)[2], const float (&iA)[2], const float (&An)[2], int64_t bi, int64_t d0,
+    int64_t L, int64_t D, int N, float* ck, int64_t ck_step, int64_t seg) {
+  constexpr int NT = 64 * NW, NP = 4 * NW;
+  constexpr int GS = 8;                    // two groups per 16-step block
+  constexpr int kPairs = TT / 2;           // step pairs per tile
+  constexpr int kRows = kPairs / NW;       // output pairs per thread per tile
+  static_assert(kPairs % NW == 0 && TT % (2 * GS) == 0, "tile shape");
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & (kPairCT - 1);
+  const int n0 = 4 * w + 2 * (lane >> 5);
+  float* xs = smem;                   // [TT][32]
+  float* dts = xs + TT * kPairCT;     // [TT][32]
+  float* Bs = dts + TT * kPairCT;     // [TT][NP]  columns n >= N stay zero
+  float* Cs = Bs + TT * NP;           // [TT][NP]
+  float* Dk = Cs + TT * NP;           // [32]
+  float* yp = Dk + kPairCT;           // [NW][kPairs][64]
+  const int dcols = static_cast<int>((D - d0) < kPairCT ? (D - d0) : kPairCT);
+  const int Di = static_cast<int>(D);
+
+  // the NW partials of a step pair go to yp[w][pair][lane]
+  auto put = [&](const float (&yv)[GS], int g0) {
+#pragma unroll
+    for (int i = 0; i < GS; i += 2) {
+      const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(yv[i]),
+                                                      __float_as_uint(yv[i + 1]), false, false);
+      yp[(w * kPairs + (g0 + i) / 2) * 64 + lane] = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    }
+  };
+
+  PairStage<T, TT, NP, NT, VEC> st;
+  st.init(D, N);
+  const int64_t row0 = bi * L;
+  if (L > 0) {
+    const int nt = static_cast<int>(L < TT ? L : TT);
+    st.load(x + row0 * D + d0, dt + row0 * D + d0, Bm + row0 * N, Cm + row0 * N, nt, dcols, N);
+  }
+  int64_t ck_t = 0;   // token of the next segment checkpoint
+  for (int64_t t0 = 0; t0 < L; t0 += TT) {
+    st.store(xs, Bs, Cs);
+    __syncthreads();
+    if (t0 + TT < L) {
+      const int64_t t1 = t0 + TT;
+      const int nt = static_cast<int>((L - t1) < TT ? (L - t1) : TT);
+      st.load(x + (row0 + t1) * D + d0, dt + (row0 + t1) * D + d0, Bm + (row0 + t1) * N,
+              Cm + (row0 + t1) * N, nt, dcols, N);
+    }
+
+    // Steps past L carry x = dt = 0 and leave h unchanged (see
+    // selective_body).  The tile is walked in 16-step blocks of two groups;
+    // the LDS reads of the next group (and the next block's B) are issued
+    // before the current group is computed.
+    PairGroup<GS, NP> ga, gb;
+    float yv[GS];
+    const int boff = (lane & 15) * NP + n0;   // this lane's step and state indices
+    float vb[2], nb[2];
+    auto blk = [&](float (&b)[2], int g0) {
+      const float2 b2 = *reinterpret_cast<const float2*>(Bs + g0 * NP + boff);
+      b[0] = b2.x; b[1] = b2.y;
+    };
+    blk(vb, 0);
+    ga.read(xs, dts, Cs, 0, col, n0);
+#pragma unroll 1
+    for (int gs = 0; gs < TT; gs += 2 * GS) {
+      // the state entering token t0 + gs (seg is a multiple of 32)
+      if (CK && (gs & 31) == 0 && t0 + gs == ck_t && t0 + gs < L) {
+        if (ck != nullptr) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            if (n0 + j < N) ck[j] = h[j];
+          ck += ck_step;
+        }
+        ck_t += seg;
+      }
+      gb.read(xs, dts, Cs, gs + GS, col, n0);
+      if (gs + 2 * GS < TT) blk(nb, gs + 2 * GS);
+      ga.template step<DISC, PRECISE, 0>(h, A2, iA, An, vb, yv);
+      put(yv, gs);
+      if (gs + 2 * GS < TT) ga.read(xs, dts, Cs, gs + 2 * GS, col, n0);
+      gb.template step<DISC, PRECISE, GS>(h, A2, iA, An, vb, yv);
+      put(yv, gs + GS);
+      vb[0] = nb[0];
+      vb[1] = nb[1];
+    }
+    __syncthreads();
+
+    // ---- thread (slot s, pair row r0) adds the NW partials of pairs r0,
+    // r0 + NW, ...; slot s is token 2 pair + (s >> 5) of channel s & 31.
+    {
+      const int nt = static_cast<int>((L - t0) < TT ? (L - t0) : TT);
+      T* y0 = y + (row0 + t0) * D + d0;
+      const int s = lane, r0 = tid >> 6;
+      const int ch = s & (kPairCT - 1), half = s >> 5;
+      const float dk = Dk[ch];
+      float part[kRows][NW];
+      float acc[kRows];
+#pragma unroll
+      for (int k = 0; k < kRows; ++k) {
+        const int pr = r0 + k * NW;
+        acc[k] = dk * xs[(2 * pr + half) * kPairCT + ch];
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) part[k][ww] = yp[(ww * kPairs + pr) * 64 + s];
+      }
+#pragma unroll
+      for (int k = 0; k < kRows; ++k) {
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) acc[k] += part[k][ww];
+      }
+      if (ch < dcols) {
+#pragma unroll
+        for (int k = 0; k < kRows; ++k) {
+          const int tt = 2 * (r0 + k * NW) + half;
+          if (tt < nt) Io<T>::store(y0 + tt * Di + ch, acc[k]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// Workgroups are swizzled so that the two 32-channel halves of each
+// 64-channel block (one 128-byte line of x, dt and y for bf16) run on the
+// same XCD (workgroups are dealt to the 8 XCDs round-robin) and share its L2.
+template <typename T, int DISC, int TT, int NW, bool VEC>
+__global__ __launch_bounds__(64 * NW) void selective_pair_kernel(
+    const T* __restrict__ x, const T* __restrict__ dt, const float* __restrict__ A,
+    const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ Dskip,
+    const float* __restrict__ h0, T* __restrict__ y, float* __restrict__ h_last,
+    float* __restrict__ ckpt, int64_t L, int64_t D, int N, int64_t seg, int64_t ck_step) {
+  extern __shared__ float smem[];
+  constexpr int NP = 4 * NW;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63;
+  const int64_t ndt = (D + kPairCT - 1) / kPairCT;
+  const int64_t nwork = static_cast<int64_t>(gridDim.x);
+  const int64_t g = blockIdx.x;
+  const int64_t q = g < (nwork & ~int64_t(15)) ? (g & ~int64_t(15)) + ((g & 7) << 1) + ((g >> 3) & 1) : g;
+  const int64_t bi = q / ndt;
+  const int64_t d0 = (q % ndt) * kPairCT;
+  const int64_t d = d0 + (lane & (kPairCT - 1));
+  const bool dok = d < D;
+  const int n0 = 4 * w + 2 * (lane >> 5);
+
+  float A2[2], iA[2], An[2], h[2];
+  bool small = false;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int n = n0 + j;
+    const bool ok = dok && n < N;
+    const float a = ok ? A[d * N + n] : 0.f;
+    An[j] = a;
+    A2[j] = DISC == kDiscBilinear ? 0.5f * a : a * kLog2e;
+    iA[j] = ok ? 1.f / a : 0.f;
+    small |= ok && fabsf(a) < 0.5f;
+    h[j] = (ok && h0 != nullptr) ? h0[(bi * D + d) * N + n] : 0.f;
+  }
+  {
+    float* Bs = smem + 2 * TT * kPairCT;
+    for (int i = tid; i < 2 * TT * NP; i += 64 * NW) Bs[i] = 0.f;   // Bs and Cs
+    float* Dk = Bs + 2 * TT * NP;
+    if (tid < kPairCT) Dk[tid] = (Dskip != nullptr && d0 + tid < D) ? Dskip[d0 + tid] : 0.f;
+  }
+  const bool precise = __syncthreads_or(small ? 1 : 0) != 0;
+  float* ck = (ckpt != nullptr && dok) ? ckpt + (bi * D + d) * N + n0 : nullptr;
+
+  auto body = [&](auto precise_c, auto ck_c) {
+    pair_body<T, DISC, decltype(precise_c)::value, TT, NW, VEC, decltype(ck_c)::value>(
+        x, dt, Bm, Cm, y, smem, h, A2, iA, An, bi, d0, L, D, N, ck, ck_step, seg);
+  };
+  using F = std::false_type;
+  using Tr = std::true_type;
+  if (DISC == kDiscZoh && precise) {
+    if (ckpt != nullptr) body(Tr{}, Tr{});
+    else body(Tr{}, F{});
+  } else {
+    if (ckpt != nullptr) body(F{}, Tr{});
+    else body(F{}, F{});
+  }
+
+  if (h_last != nullptr && dok) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      if (n0 + j < N) h_last[(bi * D + d) * N + n0 + j] = h[j];
+  }
+}
+
+template <typename T, int DISC, int TT, int NW>
+static hipError_t launch_pair(const void* x, const void* dt, const float* A, const void* Bm,
+                              const void* Cm, const float* Dskip, const float* h0, void* y,
+                              float* h_last, float* ckpt, int64_t B, int64_t L, int64_t D, int N,
+                              int64_t seg, hipStream_t stream) {
+  constexpr int NP = 4 * NW;
+  const size_t lds = (2 * TT * kPairCT + 2 * TT * NP + kPairCT +
+                      static_cast<size_t>(NW) * (TT / 2) * 64) * sizeof(float);
+  dim3 grid(static_cast<unsigned>(B * ((D + kPairCT - 1) / kPairCT)));
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, dim3(64 * NW), lds, stream, static_cast<const T*>(x),
+                       static_cast<const T*>(dt), A, static_cast<const T*>(Bm),
+                       static_cast<const T*>(Cm), Dskip, h0, static_cast<T*>(y), h_last, ckpt, L, D,
+                       N, seg, B * D * N);
+  };
+  if (D % 8 == 0) go(selective_pair_kernel<T, DISC, TT, NW, true>);
+  else go(selective_pair_kernel<T, DISC, TT, NW, false>);
+  return hipGetLastError();
+}
+
 template <typename T, int DISC, int TT, int NPW, int NW>
 static hipError_t launch_sel(const void* x, const void* dt, const float* A, const void* Bm,
                              const void* Cm, const float* Dskip, const float* h0, void* y,
@@ -392,7 +782,8 @@ static hipError_t launch_sel(const void* x, const void* dt, const float* A, cons
 
 // Instances by state size (state indices per wave x waves, tile length):
 //   N <=  8: 2 x 4,  TT = 32
-//   N <= 16: 2 x 8,  TT = 32
+//   N <= 16: the paired layout, 4 waves of 32 channels x 4 indices, TT = 64
+//            (57 KB of LDS, two workgroups per CU)
 //   N <= 32: 4 x 8,  TT = 32
 //   N <= 64: 4 x 16, TT = 16 (the partial readouts must fit in LDS)
 template <typename T, int DISC>
@@ -403,7 +794,7 @@ static hipError_t launch_sel_n(const void* x, const void* dt, const float* A, co
   if (N <= 8)
     return launch_sel<T, DISC, 32, 2, 4>(x, dt, A, Bm, Cm, Dskip, h0, y, h_last, ckpt, B, L, D, N, seg, stream);
   if (N <= 16)
-    return launch_sel<T, DISC, 32, 2, 8>(x, dt, A, Bm, Cm, Dskip, h0, y, h_last, ckpt, B, L, D, N, seg, stream);
+    return launch_pair<T, DISC, 64, 4>(x, dt, A, Bm, Cm, Dskip, h0, y, h_last, ckpt, B, L, D, N, seg, stream);
   if (N <= 32)
     return launch_sel<T, DISC, 32, 4, 8>(x, dt, A, Bm, Cm, Dskip, h0, y, h_last, ckpt, B, L, D, N, seg, stream);
   return launch_sel<T, DISC, 16, 4, 16>(x, dt, A, Bm, Cm, Dskip, h0, y, h_last, ckpt, B, L, D, N, seg, stream);

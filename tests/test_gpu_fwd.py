@@ -70,7 +70,8 @@ def _sel_case(io, disc, B, L, D, N, zero_A=False, seed_cfg=2):
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 @pytest.mark.parametrize("disc", ["zoh", "euler"])
 @pytest.mark.parametrize("B,L,D,N", [(1, 1, 1, 1), (2, 65, 33, 16), (1, 100, 70, 5),
-                                     (2, 129, 64, 64), (1, 40, 20, 32)])
+                                     (2, 129, 64, 64), (1, 40, 20, 32), (3, 77, 200, 12),
+                                     (2, 96, 128, 9)])
 def test_selective_parity(io, disc, B, L, D, N):
     print(f"selective io={io} disc={disc} B={B} L={L} D={D} N={N}", flush=True)
     _sel_case(io, disc, B, L, D, N)
