@@ -296,7 +296,7 @@ __device__ __forceinline__ void selective_bwd_body(const SelBwdArgs& a, SbLds& s
           }
         }
       }
-#pragma unroll 2
+#pragma unroll 8
       for (int i = kSbTC - 1; i >= 0; --i) {
         const float xv = sm.xs[i][lane], dtv = sm.dts[i][lane], dyv = sm.dys[i][lane];
         const float hsl_i[2] = {sm.hsl[w][i][0][lane], sm.hsl[w][i][1][lane]};
