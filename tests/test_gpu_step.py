@@ -48,9 +48,9 @@ def test_selective_step(io, disc, N):
     check("steps vs parallel scan", host(torch.stack(ys, 1)), host(yp), TOL[io])
 
 
-@pytest.mark.parametrize("N,G", [(128, 1), (64, 2)])
-def test_ssd_step(N, G):
-    B, T, H, P = 2, 23, 4, 64
+@pytest.mark.parametrize("N,G,P", [(128, 1, 64), (64, 2, 64), (128, 1, 5), (64, 1, 3)])
+def test_ssd_step(N, G, P):
+    B, T, H = 2, 23, 4
     g = lrgen.make(3, B=B, L=T, H=H, P=P, G=G, N=N)
     h0 = lrgen.state_normal((B, H, P, N), 3, std=0.3)
     X = {k: dev(g.t(k)) for k in ("x", "dt", "B", "C")}
@@ -65,7 +65,7 @@ def test_ssd_step(N, G):
     check("state (steps)", h, rh, TOL["bf16"])
 
 
-@pytest.mark.parametrize("K,V", [(128, 128), (64, 192)])
+@pytest.mark.parametrize("K,V", [(128, 128), (64, 192), (200, 64), (5, 64)])
 def test_gla_step(K, V):
     B, T, H = 2, 21, 3
     g = lrgen.make(4, B=B, L=T, H=H, K=K, V=V)
