@@ -133,7 +133,7 @@ lr_status lr_rotlru_scan(lr_dtype io, int64_t B, int64_t L, int64_t D,
  *   seg:    0, or a multiple of 32: then ckpt[s] receives the state entering
  *           token s*seg (ckpt[0] = h0 or 0); ckpt: [ceil(L/seg), B, D, N]
  *           fp32, required iff seg > 0 (consumed by lr_selective_scan_bwd).
- * Supported: 1 <= N <= 64, any D >= 1.
+ * Supported: 1 <= N <= 64, 1 <= D <= 2^24 (LR_E_UNSUPPORTED beyond).
  * ------------------------------------------------------------------------- */
 lr_status lr_selective_scan(lr_dtype io, lr_disc disc, int64_t B, int64_t L,
                             int64_t D, int64_t N, int64_t seg, const void* x,

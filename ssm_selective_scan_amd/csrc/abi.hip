@@ -83,6 +83,7 @@ namespace {
 
 constexpr int64_t kMaxElems = int64_t(1) << 46;   // per tensor; keeps every index in int64
 constexpr int64_t kMaxGrid = std::numeric_limits<int32_t>::max();
+constexpr int64_t kMaxSelD = int64_t(1) << 24;   // channels of lr_selective_scan
 
 // Checked product of non-negative sizes; false on overflow.
 bool mul_ok(int64_t& acc, int64_t v) {
@@ -201,10 +202,12 @@ lr_status lr_selective_scan(lr_dtype io, lr_disc disc, int64_t B, int64_t L, int
   if (!valid_io(io) || !valid_disc(disc)) return LR_E_DTYPE;
   if (B < 0 || L < 0 || D < 1 || N < 1 || seg < 0) return LR_E_SHAPE;
   if (N > 64 || seg % 32 != 0) return LR_E_UNSUPPORTED;
+  // tile offsets (64 tokens x D) are 32-bit in the kernels
+  if (D > kMaxSelD) return LR_E_UNSUPPORTED;
   if (!elems_ok({B, L, D}) || !elems_ok({B, D, N}) || !elems_ok({D, N})) return LR_E_OVERFLOW;
   if (seg > 0 && !elems_ok({(L + seg - 1) / seg, B, D, N})) return LR_E_OVERFLOW;
-  int64_t nwg = 1;
-  if (!mul_ok(nwg, B) || !mul_ok(nwg, (D + 63) / 64) || nwg > kMaxGrid) return LR_E_OVERFLOW;
+  int64_t nwg = 1;   // 32 channels per workgroup in the smallest layout
+  if (!mul_ok(nwg, B) || !mul_ok(nwg, (D + 31) / 32) || nwg > kMaxGrid) return LR_E_OVERFLOW;
   if (A == nullptr) return LR_E_NULLPTR;
   if (B * L > 0 && any_null({x, dt, Bm, Cm, y})) return LR_E_NULLPTR;
   if (B * L > 0 && seg > 0 && ckpt == nullptr) return LR_E_NULLPTR;

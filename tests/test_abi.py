@@ -111,6 +111,8 @@ def test_selective_validation(L):
     assert sel(L, Cm=None) == NULL
     assert sel(L, dt=MIS) == ALIGN
     assert sel(L, B=0, x=None, dt=None, Bm=None, Cm=None, y=None) == OK
+    assert sel(L, B=1, Lq=1, D=(1 << 24) + 1) == UNSUP   # 32-bit tile offsets
+    assert sel(L, B=1 << 37, Lq=1, D=1 << 10, N=1) == OVF  # grid of 32-channel workgroups
 
 
 def ssd(L, io=1, disc=0, B=1, Lq=64, H=2, Pp=64, G=1, N=128, chunk=64, seg=0, x=P, ck=None,
