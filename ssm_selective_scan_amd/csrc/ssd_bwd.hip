@@ -139,15 +139,18 @@ __device__ __forceinline__ float wave_sum(float v) {
 template <int NS>
 struct GlocLds {
   uint16_t Cs[kBQ * (NS + 8)]; // C[u][n]
-  uint16_t dys[kBQ * kBLd];    // dy[u][p]
   uint16_t dyE[kBQ * kBLd];    // E_u dy[u][p]
-  float cum[kBQ];
-  float E[kBQ];
 };
 
+// Per segment, last block first.  A block's C, dy and gates are loaded into
+// registers one block ahead (in flight during the previous block's MFMA);
+// every wave scans the block's gates itself (lane = token), so dy is scaled
+// by E_u while it is written to LDS, with no extra pass or barrier.
 template <int MODE, int NS>
 __global__ __launch_bounds__(256) void ssd_bwd_gloc_kernel(BwdArgs a) {
   constexpr int NT = NS / 16;
+  constexpr int kCC = kBQ * (NS / 8) / 256;    // 16-byte C chunks per thread
+  constexpr int kDC = kBQ * (kBP / 8) / 256;   // 16-byte dy chunks per thread
   __shared__ GlocLds<NS> sm;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int g4 = lane >> 4, c16 = lane & 15;
@@ -161,47 +164,57 @@ __global__ __launch_bounds__(256) void ssd_bwd_gloc_kernel(BwdArgs a) {
   const int64_t tse = (ts0 + a.seg < a.L) ? ts0 + a.seg : a.L;
   const int nb = static_cast<int>((tse - ts0 + kBQ - 1) / kBQ);
 
+  u16x8 creg[kCC], dreg[kDC];
+  float gv = 0.f;   // gate of token `lane` of the block
+  auto fetch = [&](int j) {
+    const int64_t t0 = ts0 + static_cast<int64_t>(j) * kBQ;
+    const int nv = static_cast<int>((tse - t0) < kBQ ? (tse - t0) : kBQ);
+#pragma unroll
+    for (int k = 0; k < kCC; ++k) {
+      const int idx = tid + 256 * k, u = idx / (NS / 8), c = idx % (NS / 8);
+      creg[k] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      if (u < nv) creg[k] = *reinterpret_cast<const u16x8*>(a.Cm + ((b * a.L + t0 + u) * a.G + grp) * NS + 8 * c);
+    }
+#pragma unroll
+    for (int k = 0; k < kDC; ++k) {
+      const int idx = tid + 256 * k, u = idx >> 3, c = idx & 7;
+      dreg[k] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      if (u < nv) dreg[k] = *reinterpret_cast<const u16x8*>(a.dy + ((b * a.L + t0 + u) * a.H + h) * kBP + 8 * c);
+    }
+    gv = lane < nv ? gate_at<MODE>(a, b, t0 + lane, h, grp) : 0.f;
+  };
+
   f32x4 gacc[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) gacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float lsum = 0.f;   // log2 of the segment decay
 
+  if (nb > 0) fetch(nb - 1);
   for (int j = nb - 1; j >= 0; --j) {
     const int64_t t0 = ts0 + static_cast<int64_t>(j) * kBQ;
     const int nv = static_cast<int>((tse - t0) < kBQ ? (tse - t0) : kBQ);
-    if (w == 0) {
-      const bool ok = lane < nv;
-      float l2, ph, ek;
-      block_scalars<MODE>(ok ? gate_at<MODE>(a, b, t0 + lane, h, grp) : 0.f, ok, Ah, l2, ph, ek);
-      const float c = wave_incl_sum(l2);
-      sm.cum[lane] = c;
-      sm.E[lane] = fast_exp2(c);
-    }
+    float l2, ph, ek;
+    block_scalars<MODE>(gv, lane < nv, Ah, l2, ph, ek);
+    const float c = wave_incl_sum(l2);
+    const float cend = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), 63));
+    const float el = fast_exp2(c);
     // token-major copies; the contraction over tokens reads them transposed
-    for (int idx = tid; idx < kBQ * (NS / 8); idx += 256) {
-      const int u = idx / (NS / 8), c = idx % (NS / 8);
-      u16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (u < nv) v = *reinterpret_cast<const u16x8*>(a.Cm + ((b * a.L + t0 + u) * a.G + grp) * NS + 8 * c);
-      *reinterpret_cast<u16x8*>(sm.Cs + u * (NS + 8) + 8 * c) = v;
+#pragma unroll
+    for (int k = 0; k < kCC; ++k) {
+      const int idx = tid + 256 * k, u = idx / (NS / 8), cc = idx % (NS / 8);
+      *reinterpret_cast<u16x8*>(sm.Cs + u * (NS + 8) + 8 * cc) = creg[k];
     }
-    for (int idx = tid; idx < kBQ * (kBP / 8); idx += 256) {
-      const int u = idx >> 3, c = idx & 7;
-      u16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (u < nv) v = *reinterpret_cast<const u16x8*>(a.dy + ((b * a.L + t0 + u) * a.H + h) * kBP + 8 * c);
-      *reinterpret_cast<u16x8*>(sm.dys + u * kBLd + 8 * c) = v;
-    }
-    __syncthreads();
-    for (int idx = tid; idx < kBQ * (kBP / 8); idx += 256) {
-      const int u = idx >> 3, c = idx & 7;
-      const u16x8 v = *reinterpret_cast<const u16x8*>(sm.dys + u * kBLd + 8 * c);
-      const float e = sm.E[u];
+#pragma unroll
+    for (int k = 0; k < kDC; ++k) {
+      const int idx = tid + 256 * k, u = idx >> 3, cc = idx & 7;
+      const float e = __shfl(el, u);
       u16x8 o;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) o[i] = f2bf(bf2f(v[i]) * e);
-      *reinterpret_cast<u16x8*>(sm.dyE + u * kBLd + 8 * c) = o;
+      for (int i = 0; i < 8; ++i) o[i] = f2bf(bf2f(dreg[k][i]) * e);
+      *reinterpret_cast<u16x8*>(sm.dyE + u * kBLd + 8 * cc) = o;
     }
     __syncthreads();
-    const float cend = sm.cum[kBQ - 1];
+    if (j > 0) fetch(j - 1);
     const float dec = fast_exp2(cend);
     lsum += cend;
 #pragma unroll
