@@ -318,6 +318,30 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) hacc[nt] = *reinterpret_cast<const f32x4*>(cp + p * NS + 16 * nt + 4 * g4);
   }
+  // B, x and the gate of the next recompute block, loaded into registers
+  // during the current block's MFMA; every wave scans the block's gates
+  // (lane = token) so B is scaled to B_w while it is written to LDS
+  constexpr int kRB = kBQ * (NS / 8) / 256, kRX = kBQ * (kBP / 8) / 256;
+  u16x8 rb[kRB], rx[kRX];
+  float rg = 0.f;
+  auto rfetch = [&](int j) {
+    const int64_t t0 = ts0 + static_cast<int64_t>(j) * kBQ;
+    const int nv = static_cast<int>((tse - t0) < kBQ ? (tse - t0) : kBQ);
+#pragma unroll
+    for (int k = 0; k < kRB; ++k) {
+      const int idx = tid + 256 * k, r = idx / (NS / 8), c = idx % (NS / 8);
+      rb[k] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      if (r < nv) rb[k] = *reinterpret_cast<const u16x8*>(a.Bm + (b * a.L + t0 + r) * bcrow + bcoff + 8 * c);
+    }
+#pragma unroll
+    for (int k = 0; k < kRX; ++k) {
+      const int idx = tid + 256 * k, r = idx >> 3, c = idx & 7;
+      rx[k] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      if (r < nv) rx[k] = *reinterpret_cast<const u16x8*>(a.x + (b * a.L + t0 + r) * xrow + xoff + 8 * c);
+    }
+    rg = lane < nv ? gate_at<DISC>(a, b, t0 + lane, h, grp) : 0.f;
+  };
+  if (nb > 1) rfetch(0);
 #pragma unroll
   for (int j = 0; j < NBS; ++j) {
 #pragma unroll
@@ -325,37 +349,27 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
     if (j + 1 < nb) {
       const int64_t t0 = ts0 + static_cast<int64_t>(j) * kBQ;
       const int nv = static_cast<int>((tse - t0) < kBQ ? (tse - t0) : kBQ);
-      if (w == 0) {
-        const bool ok = lane < nv;
-        float l2, ph, ek;
-        block_scalars<DISC>(ok ? gate_at<DISC>(a, b, t0 + lane, h, grp) : 0.f, ok, Ah, l2, ph, ek);
-        sm.cum[lane] = wave_incl_sum(l2);
-        sm.phi[lane] = lane < nv ? ph : 0.f;
-      }
-      for (int idx = tid; idx < kBQ * (NS / 8); idx += 256) {
-        const int r = idx / (NS / 8), c = idx % (NS / 8);
-        u16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (r < nv) v = *reinterpret_cast<const u16x8*>(a.Bm + (b * a.L + t0 + r) * bcrow + bcoff + 8 * c);
-        *reinterpret_cast<u16x8*>(sm.Bs + r * kLdN + 8 * c) = v;
-      }
-      for (int idx = tid; idx < kBQ * (kBP / 8); idx += 256) {
-        const int s = idx >> 3, c = idx & 7;
-        u16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (s < nv) v = *reinterpret_cast<const u16x8*>(a.x + (b * a.L + t0 + s) * xrow + xoff + 8 * c);
-        *reinterpret_cast<u16x8*>(sm.xs + s * kBLd + 8 * c) = v;
-      }
-      __syncthreads();
-      const float cend = sm.cum[kBQ - 1];
-      for (int idx = tid; idx < kBQ * (NS / 8); idx += 256) {
-        const int s = idx / (NS / 8), c = idx % (NS / 8);
-        const float ws = fast_exp2(cend - sm.cum[s]) * sm.phi[s];
-        const u16x8 v = *reinterpret_cast<const u16x8*>(sm.Bs + s * kLdN + 8 * c);
+      float l2, ph, ek;
+      block_scalars<DISC>(rg, lane < nv, Ah, l2, ph, ek);
+      const float c = wave_incl_sum(l2);
+      const float cend = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), 63));
+      const float wsl = fast_exp2(cend - c) * (lane < nv ? ph : 0.f);
+#pragma unroll
+      for (int k = 0; k < kRB; ++k) {
+        const int idx = tid + 256 * k, r = idx / (NS / 8), cc = idx % (NS / 8);
+        const float ws = __shfl(wsl, r);
         u16x8 o;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) o[i] = f2bf(bf2f(v[i]) * ws);
-        *reinterpret_cast<u16x8*>(sm.pB + s * kLdN + 8 * c) = o;   // B_w
+        for (int i = 0; i < 8; ++i) o[i] = f2bf(bf2f(rb[k][i]) * ws);
+        *reinterpret_cast<u16x8*>(sm.pB + r * kLdN + 8 * cc) = o;   // B_w
+      }
+#pragma unroll
+      for (int k = 0; k < kRX; ++k) {
+        const int idx = tid + 256 * k, r = idx >> 3, cc = idx & 7;
+        *reinterpret_cast<u16x8*>(sm.xs + r * kBLd + 8 * cc) = rx[k];
       }
       __syncthreads();
+      if (j + 2 < nb) rfetch(j + 1);
       const float dec = fast_exp2(cend);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
