@@ -405,62 +405,61 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
     const int64_t t0 = ts0 + static_cast<int64_t>(j) * kBQ;
     const int nv = static_cast<int>((tse - t0) < kBQ ? (tse - t0) : kBQ);
 
-    // ---- stage the block
-    if (w == 0) {
+    // ---- stage the block.  Every staged row below is token `lane` of the
+    // block, so each wave computes the per-token scalars itself and scales B
+    // (by phi) and dy (by E) as they are written; wave 0 also keeps the
+    // scalars in LDS for the later phases.
+    {
       const bool ok = lane < nv;
       const float dtv = ok ? gate_at<DISC>(a, b, t0 + lane, h, grp) : 0.f;
       float l2, ph, ek;
       block_scalars<DISC>(dtv, ok, Ah, l2, ph, ek);
+      ph = ok ? ph : 0.f;
       const float c = wave_incl_sum(l2);
-      const float cend = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), 63));
-      sm.cum[lane] = c;
-      sm.E[lane] = fast_exp2(c);
-      sm.sE[lane] = fast_exp2(cend - c);
-      sm.phi[lane] = lane < nv ? ph : 0.f;
-      sm.dtv[lane] = dtv;
-      sm.ek[lane] = ek;
-    }
-    for (int idx = tid; idx < kBQ * (NS / 8); idx += 256) {
-      const int r = idx & 63, c = idx >> 6;
-      u16x8 vc = {0, 0, 0, 0, 0, 0, 0, 0}, vb = vc;
-      float ph = 0.f;
-      if (r < nv) {
-        const int64_t off = (b * a.L + t0 + r) * bcrow + bcoff + 8 * c;
-        vc = *reinterpret_cast<const u16x8*>(a.Cm + off);
-        vb = *reinterpret_cast<const u16x8*>(a.Bm + off);
-        float l2, ek;
-        block_scalars<DISC>(gate_at<DISC>(a, b, t0 + r, h, grp), true, Ah, l2, ph, ek);
+      const float el = fast_exp2(c);
+      if (w == 0) {
+        const float cend = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), 63));
+        sm.cum[lane] = c;
+        sm.E[lane] = el;
+        sm.sE[lane] = fast_exp2(cend - c);
+        sm.phi[lane] = ph;
+        sm.dtv[lane] = dtv;
+        sm.ek[lane] = ek;
       }
-      *reinterpret_cast<u16x8*>(sm.Cs + r * kLdN + 8 * c) = vc;
-      *reinterpret_cast<u16x8*>(sm.Bs + r * kLdN + 8 * c) = vb;
-      u16x8 pb;
+      for (int idx = tid; idx < kBQ * (NS / 8); idx += 256) {
+        const int r = idx & 63, cc = idx >> 6;   // r == lane
+        u16x8 vc = {0, 0, 0, 0, 0, 0, 0, 0}, vb = vc;
+        if (r < nv) {
+          const int64_t off = (b * a.L + t0 + r) * bcrow + bcoff + 8 * cc;
+          vc = *reinterpret_cast<const u16x8*>(a.Cm + off);
+          vb = *reinterpret_cast<const u16x8*>(a.Bm + off);
+        }
+        *reinterpret_cast<u16x8*>(sm.Cs + r * kLdN + 8 * cc) = vc;
+        *reinterpret_cast<u16x8*>(sm.Bs + r * kLdN + 8 * cc) = vb;
+        u16x8 pb;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) pb[i] = f2bf(bf2f(vb[i]) * ph);
-      *reinterpret_cast<u16x8*>(sm.pB + r * kLdN + 8 * c) = pb;
-    }
-    for (int idx = tid; idx < kBQ * (kBP / 8); idx += 256) {
-      const int r = idx & 63, c = idx >> 6;
-      u16x8 vx = {0, 0, 0, 0, 0, 0, 0, 0}, vd = vx;
-      if (r < nv) {
-        const int64_t off = (b * a.L + t0 + r) * xrow + xoff + 8 * c;
-        vx = *reinterpret_cast<const u16x8*>(a.x + off);
-        vd = *reinterpret_cast<const u16x8*>(a.dy + off);
+        for (int i = 0; i < 8; ++i) pb[i] = f2bf(bf2f(vb[i]) * ph);
+        *reinterpret_cast<u16x8*>(sm.pB + r * kLdN + 8 * cc) = pb;
       }
-      *reinterpret_cast<u16x8*>(sm.xs + r * kBLd + 8 * c) = vx;
-      *reinterpret_cast<u16x8*>(sm.dys + r * kBLd + 8 * c) = vd;
+      for (int idx = tid; idx < kBQ * (kBP / 8); idx += 256) {
+        const int r = idx & 63, cc = idx >> 6;   // r == lane
+        u16x8 vx = {0, 0, 0, 0, 0, 0, 0, 0}, vd = vx;
+        if (r < nv) {
+          const int64_t off = (b * a.L + t0 + r) * xrow + xoff + 8 * cc;
+          vx = *reinterpret_cast<const u16x8*>(a.x + off);
+          vd = *reinterpret_cast<const u16x8*>(a.dy + off);
+        }
+        *reinterpret_cast<u16x8*>(sm.xs + r * kBLd + 8 * cc) = vx;
+        *reinterpret_cast<u16x8*>(sm.dys + r * kBLd + 8 * cc) = vd;
+        u16x8 de;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) de[i] = f2bf(bf2f(vd[i]) * el);
+        *reinterpret_cast<u16x8*>(sm.dyE + r * kBLd + 8 * cc) = de;
+      }
     }
     __syncthreads();
 
-    // ---- E-scaled dy; decayed masks and the T sums
-    for (int idx = tid; idx < kBQ * (kBP / 8); idx += 256) {
-      const int u = idx >> 3, c = idx & 7;
-      const u16x8 v = *reinterpret_cast<const u16x8*>(sm.dys + u * kBLd + 8 * c);
-      const float e = sm.E[u];
-      u16x8 o;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) o[i] = f2bf(bf2f(v[i]) * e);
-      *reinterpret_cast<u16x8*>(sm.dyE + u * kBLd + 8 * c) = o;
-    }
+    // ---- decayed masks and the T sums
 #pragma unroll
     for (int q = 0; q < 3; ++q) {
       const int tile = 3 * w + q;
