@@ -271,6 +271,10 @@ __device__ __forceinline__ void selective_bwd_body(const SelBwdArgs& a, SbLds& s
     for (int c = nch - 1; c >= 0; --c) {
       const int64_t t0 = ts0 + static_cast<int64_t>(c) * kSbTC;
       const int nv = chunk_len(t0, tse);
+      // the state entering the chunk (this lane wrote it in the forward
+      // pass); loaded before the barrier so its latency overlaps the staging
+      const float hin[2] = {subp[(c * kSbNW + w) * 2 * kSbCT + lane],
+                            subp[((c * kSbNW + w) * 2 + 1) * kSbCT + lane]};
       put();
       __syncthreads();
       if (c > 0) {
@@ -280,8 +284,6 @@ __device__ __forceinline__ void selective_bwd_body(const SelBwdArgs& a, SbLds& s
         fetch(tp, chunk_len(tp, ts0), false);
       }
       // this wave's states of the chunk -> LDS (read back by the same lanes)
-      const float hin[2] = {subp[(c * kSbNW + w) * 2 * kSbCT + lane],
-                            subp[((c * kSbNW + w) * 2 + 1) * kSbCT + lane]};
       {
         float hh[2] = {hin[0], hin[1]};
 #pragma unroll
