@@ -224,7 +224,7 @@ __device__ __forceinline__ void selective_bwd_body(const SelBwdArgs& a, SbLds& s
   };
   if (a.nseg > 0) {
     const int64_t ts0 = (a.nseg - 1) * a.seg;
-    fetch(ts0, chunk_len(ts0, (ts0 + a.seg < L) ? ts0 + a.seg : L), false);
+    fetch(ts0, chunk_len(ts0, (ts0 + a.seg < L) ? ts0 + a.seg : L), true);
   }
 
   for (int64_t s = a.nseg - 1; s >= 0; --s) {
@@ -236,8 +236,10 @@ __device__ __forceinline__ void selective_bwd_body(const SelBwdArgs& a, SbLds& s
     for (int j = 0; j < 2; ++j)
       h[j] = okj[j] ? a.ckpt[((s * a.B + b) * D + d0 + lane) * N + n0 + j] : 0.f;
 
-    // ---- forward over the segment: the state entering every chunk
-    for (int c = 0; c < nch; ++c) {
+    // ---- forward over the segment: the state entering every chunk (the
+    // last chunk's own steps are not needed; the staged registers hold this
+    // segment's first chunk with dy, which the reverse pass uses if nch == 1)
+    for (int c = 0; c < nch - 1; ++c) {
       const int64_t t0 = ts0 + static_cast<int64_t>(c) * kSbTC;
       subp[(c * kSbNW + w) * 2 * kSbCT + lane] = h[0];
       subp[((c * kSbNW + w) * 2 + 1) * kSbCT + lane] = h[1];
@@ -245,8 +247,8 @@ __device__ __forceinline__ void selective_bwd_body(const SelBwdArgs& a, SbLds& s
       __syncthreads();
       {
         // next: chunk c + 1, or the segment's last chunk (with dy) for the reverse pass
-        const int64_t tn = c + 1 < nch ? t0 + kSbTC : ts0 + static_cast<int64_t>(nch - 1) * kSbTC;
-        fetch(tn, chunk_len(tn, tse), c + 1 >= nch);
+        const int64_t tn = c + 2 < nch ? t0 + kSbTC : ts0 + static_cast<int64_t>(nch - 1) * kSbTC;
+        fetch(tn, chunk_len(tn, tse), c + 2 >= nch);
       }
 #pragma unroll
       for (int i = 0; i < kSbTC; ++i) {
@@ -266,6 +268,10 @@ __device__ __forceinline__ void selective_bwd_body(const SelBwdArgs& a, SbLds& s
       }
       __syncthreads();
     }
+    if (nch > 0) {
+      subp[((nch - 1) * kSbNW + w) * 2 * kSbCT + lane] = h[0];
+      subp[(((nch - 1) * kSbNW + w) * 2 + 1) * kSbCT + lane] = h[1];
+    }
 
     // ---- chunks last to first
     for (int c = nch - 1; c >= 0; --c) {
@@ -279,9 +285,9 @@ __device__ __forceinline__ void selective_bwd_body(const SelBwdArgs& a, SbLds& s
       __syncthreads();
       if (c > 0) {
         fetch(t0 - kSbTC, kSbTC, true);
-      } else if (s > 0) {   // the previous segment's first chunk, for its forward pass
+      } else if (s > 0) {   // the previous segment's first chunk (with dy, see above)
         const int64_t tp = (s - 1) * a.seg;
-        fetch(tp, chunk_len(tp, ts0), false);
+        fetch(tp, chunk_len(tp, ts0), true);
       }
       // this wave's states of the chunk -> LDS (read back by the same lanes)
       {
