@@ -27,14 +27,24 @@
 // with DPP row shifts; sums over channel tiles (dB, dC) and batch rows (dA,
 // dD) are fixed-order partial sums reduced by a second launch, so results
 // are deterministic.
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace lr {
 
-constexpr int kSbTC = 32;     // tokens per chunk
-constexpr int kSbNW = 8;      // waves (2 state indices each: N <= 16)
-constexpr int kSbSub = 8;     // chunks per segment (seg <= 256)
+constexpr int kSbNW = 8;      // waves
 constexpr int kSbCT = 64;     // channels per workgroup
+
+// NPW state indices per lane, so a workgroup covers NN = 8 NPW of them;
+// chunks of TC tokens, SUB chunks per segment (seg <= 256).  N <= 16 runs
+// with 2 x 32, N <= 32 with 4 x 16 (the chunk's states fill the same LDS).
+template <int NPW>
+struct SbCfg {
+  static constexpr int TC = NPW == 2 ? 32 : 16;
+  static constexpr int SUB = 256 / TC;
+  static constexpr int NN = NPW * kSbNW;
+};
 
 enum { kSbZoh = 0, kSbEuler = 1, kSbBilinear = 2, kSbDirac = 3 };
 
@@ -45,7 +55,7 @@ struct SelBwdArgs {
   float* dBpart; float* dCpart;   // [ntile][B][L][N]
   float* dApart;                  // [B][D][N]
   float* dDpart;                  // [B][D]
-  float* subck;                   // [B * ntile][kSbSub][kSbNW][2][64]: state entering each chunk
+  float* subck;                   // [B * ntile][SUB][kSbNW][NPW][64]: state entering each chunk
   void* dBm; void* dCm; float* dA; float* dD;
   int64_t B, L, D, N, seg, nseg, ntile;
 };
@@ -106,14 +116,16 @@ __device__ __forceinline__ void sb_grads(float dtv, float Av, float iA, float e,
   }
 }
 
+template <int NPW>
 struct SbLds {
-  float xs[kSbTC][kSbCT], dts[kSbTC][kSbCT], dys[kSbTC][kSbCT];
-  float Bs[kSbTC][16], Cs[kSbTC][16];                 // n >= N stay zero
+  static constexpr int TC = SbCfg<NPW>::TC, NN = SbCfg<NPW>::NN;
+  float xs[TC][kSbCT], dts[TC][kSbCT], dys[TC][kSbCT];
+  float Bs[TC][NN], Cs[TC][NN];                       // n >= N stay zero
   // each wave's states of the chunk; the reverse step of token i overwrites
   // its slot with the wave's partial sums of dx ([0]) and ddt ([1])
-  float hsl[kSbNW][kSbTC][2][kSbCT];
-  float rbc[kSbTC][2][16];                            // dB, dC of the chunk
-};   // 160 KB
+  float hsl[kSbNW][TC][NPW][kSbCT];
+  float rbc[TC][2][NN];                               // dB, dC of the chunk
+};   // 160 KB (NPW = 2), 148 KB (NPW = 4)
 
 // Sum over the 64 lanes of v[0..3]; on return lane 15 of row q (lanes
 // 16 q .. 16 q + 15) holds the total of v[q].  Halves and rows are paired
@@ -144,12 +156,13 @@ __device__ __forceinline__ float sum4_over_lanes(const float (&v)[4]) {
 //   dh_t/ddt = A h_t + B x                  (the continuous-time derivative)
 //   dh_t/dA  = dt h_t + (dt - phi) B x / A
 // which use h_t only (no h_{t-1}).  Other cases use sb_disc/sb_grads.
-template <typename T, int DISC, bool FAST>
-__device__ __forceinline__ void selective_bwd_body(const SelBwdArgs& a, SbLds& sm, int64_t b,
-                                                   int64_t tile, const float (&Av)[2],
-                                                   const float (&iAv)[2], const bool (&okj)[2],
-                                                   float (&G)[2], float (&dAacc)[2],
+template <typename T, int DISC, bool FAST, int NPW>
+__device__ __forceinline__ void selective_bwd_body(const SelBwdArgs& a, SbLds<NPW>& sm, int64_t b,
+                                                   int64_t tile, const float (&Av)[NPW],
+                                                   const float (&iAv)[NPW], const bool (&okj)[NPW],
+                                                   float (&G)[NPW], float (&dAacc)[NPW],
                                                    float& dDacc) {
+  constexpr int kSbTC = SbCfg<NPW>::TC, kSbSub = SbCfg<NPW>::SUB;
   const T* x = static_cast<const T*>(a.x);
   const T* dt = static_cast<const T*>(a.dt);
   const T* Bm = static_cast<const T*>(a.Bm);
@@ -161,13 +174,15 @@ __device__ __forceinline__ void selective_bwd_body(const SelBwdArgs& a, SbLds& s
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int64_t d0 = tile * kSbCT;
   const int N = static_cast<int>(a.N);
-  const int n0 = 2 * w;
+  const int n0 = NPW * w;
   const int64_t D = a.D, L = a.L;
-  float* subp = a.subck + static_cast<int64_t>(blockIdx.x) * kSbSub * kSbNW * 2 * kSbCT;
+  float* subp = a.subck + static_cast<int64_t>(blockIdx.x) * kSbSub * kSbNW * NPW * kSbCT;
+  // this lane's slot of chain j in the state entering chunk c
+  auto sub_at = [&](int c, int j) -> float& { return subp[((c * kSbNW + w) * NPW + j) * kSbCT + lane]; };
   const float Dd = (a.Dskip != nullptr && d0 + lane < D) ? a.Dskip[d0 + lane] : 0.f;
-  float A2[2];   // A log2(e)
+  float A2[NPW];   // A log2(e)
 #pragma unroll
-  for (int j = 0; j < 2; ++j) A2[j] = Av[j] * kLog2e;
+  for (int j = 0; j < NPW; ++j) A2[j] = Av[j] * kLog2e;
 
   // e, phi of one step
   auto disc = [&](float dtv, int j, float& e, float& phi) {
@@ -231,9 +246,9 @@ __device__ __forceinline__ void selective_bwd_body(const SelBwdArgs& a, SbLds& s
     const int64_t ts0 = s * a.seg;
     const int64_t tse = (ts0 + a.seg < L) ? ts0 + a.seg : L;
     const int nch = static_cast<int>((tse - ts0 + kSbTC - 1) / kSbTC);
-    float h[2];
+    float h[NPW];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NPW; ++j)
       h[j] = okj[j] ? a.ckpt[((s * a.B + b) * D + d0 + lane) * N + n0 + j] : 0.f;
 
     // ---- forward over the segment: the state entering every chunk (the
@@ -241,8 +256,8 @@ __device__ __forceinline__ void selective_bwd_body(const SelBwdArgs& a, SbLds& s
     // segment's first chunk with dy, which the reverse pass uses if nch == 1)
     for (int c = 0; c < nch - 1; ++c) {
       const int64_t t0 = ts0 + static_cast<int64_t>(c) * kSbTC;
-      subp[(c * kSbNW + w) * 2 * kSbCT + lane] = h[0];
-      subp[((c * kSbNW + w) * 2 + 1) * kSbCT + lane] = h[1];
+#pragma unroll
+      for (int j = 0; j < NPW; ++j) sub_at(c, j) = h[j];
       put();
       __syncthreads();
       {
@@ -254,7 +269,7 @@ __device__ __forceinline__ void selective_bwd_body(const SelBwdArgs& a, SbLds& s
       for (int i = 0; i < kSbTC; ++i) {
         const float xv = sm.xs[i][lane], dtv = sm.dts[i][lane];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < NPW; ++j) {
           if constexpr (FAST) {   // h = e (h + v) - v, v = B x / A
             const float e = fast_exp2(dtv * A2[j]);
             const float v = (sm.Bs[i][n0 + j] * xv) * iAv[j];
@@ -269,8 +284,8 @@ __device__ __forceinline__ void selective_bwd_body(const SelBwdArgs& a, SbLds& s
       __syncthreads();
     }
     if (nch > 0) {
-      subp[((nch - 1) * kSbNW + w) * 2 * kSbCT + lane] = h[0];
-      subp[(((nch - 1) * kSbNW + w) * 2 + 1) * kSbCT + lane] = h[1];
+#pragma unroll
+      for (int j = 0; j < NPW; ++j) sub_at(nch - 1, j) = h[j];
     }
 
     // ---- chunks last to first
@@ -279,8 +294,9 @@ __device__ __forceinline__ void selective_bwd_body(const SelBwdArgs& a, SbLds& s
       const int nv = chunk_len(t0, tse);
       // the state entering the chunk (this lane wrote it in the forward
       // pass); loaded before the barrier so its latency overlaps the staging
-      const float hin[2] = {subp[(c * kSbNW + w) * 2 * kSbCT + lane],
-                            subp[((c * kSbNW + w) * 2 + 1) * kSbCT + lane]};
+      float hin[NPW];
+#pragma unroll
+      for (int j = 0; j < NPW; ++j) hin[j] = sub_at(c, j);
       put();
       __syncthreads();
       if (c > 0) {
@@ -291,12 +307,14 @@ __device__ __forceinline__ void selective_bwd_body(const SelBwdArgs& a, SbLds& s
       }
       // this wave's states of the chunk -> LDS (read back by the same lanes)
       {
-        float hh[2] = {hin[0], hin[1]};
+        float hh[NPW];
+#pragma unroll
+        for (int j = 0; j < NPW; ++j) hh[j] = hin[j];
 #pragma unroll
         for (int i = 0; i < kSbTC; ++i) {
           const float xv = sm.xs[i][lane], dtv = sm.dts[i][lane];
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
+          for (int j = 0; j < NPW; ++j) {
             float e, phi;
             disc(dtv, j, e, phi);
             hh[j] = fmaf(e, hh[j], phi * (sm.Bs[i][n0 + j] * xv));
@@ -304,13 +322,16 @@ __device__ __forceinline__ void selective_bwd_body(const SelBwdArgs& a, SbLds& s
           }
         }
       }
-#pragma unroll 8
+      constexpr int kUnroll = NPW == 2 ? 8 : 4;
+#pragma unroll kUnroll
       for (int i = kSbTC - 1; i >= 0; --i) {
         const float xv = sm.xs[i][lane], dtv = sm.dts[i][lane], dyv = sm.dys[i][lane];
-        const float hsl_i[2] = {sm.hsl[w][i][0][lane], sm.hsl[w][i][1][lane]};
-        float dxp = 0.f, ddtp = 0.f, v[4];
+        float hsl_i[NPW];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < NPW; ++j) hsl_i[j] = sm.hsl[w][i][j][lane];
+        float dxp = 0.f, ddtp = 0.f, v[2 * NPW];
+#pragma unroll
+        for (int j = 0; j < NPW; ++j) {
           const float Bv = sm.Bs[i][n0 + j], Cv = sm.Cs[i][n0 + j];
           float e, ph;
           disc(dtv, j, e, ph);
@@ -319,7 +340,7 @@ __device__ __forceinline__ void selective_bwd_body(const SelBwdArgs& a, SbLds& s
           const float gphi = G[j] * ph;
           dxp = fmaf(gphi, Bv, dxp);
           v[j] = gphi * xv;                  // dB partial
-          v[2 + j] = ht * dyv;               // dC partial
+          v[NPW + j] = ht * dyv;             // dC partial
           const float bx = Bv * xv;
           if constexpr (FAST) {
             ddtp = fmaf(G[j], fmaf(Av[j], ht, bx), ddtp);
@@ -335,8 +356,13 @@ __device__ __forceinline__ void selective_bwd_body(const SelBwdArgs& a, SbLds& s
           }
           G[j] *= e;
         }
-        const float r = sum4_over_lanes(v);
-        if ((lane & 15) == 15) sm.rbc[i][lane >> 5][n0 + ((lane >> 4) & 1)] = r;
+        // pairs of state indices: (dB, dB, dC, dC) of n0 + 2k, n0 + 2k + 1
+#pragma unroll
+        for (int k = 0; k < NPW / 2; ++k) {
+          const float vk[4] = {v[2 * k], v[2 * k + 1], v[NPW + 2 * k], v[NPW + 2 * k + 1]};
+          const float r = sum4_over_lanes(vk);
+          if ((lane & 15) == 15) sm.rbc[i][lane >> 5][n0 + 2 * k + ((lane >> 4) & 1)] = r;
+        }
         sm.hsl[w][i][0][lane] = dxp;   // h of token i is no longer needed
         sm.hsl[w][i][1][lane] = ddtp;
         if (w == 0) dDacc = fmaf(dyv, xv, dDacc);
@@ -372,9 +398,10 @@ __device__ __forceinline__ void selective_bwd_body(const SelBwdArgs& a, SbLds& s
   }
 }
 
-template <typename T, int DISC>
+template <typename T, int DISC, int NPW>
 __global__ __launch_bounds__(512) void selective_bwd_kernel(SelBwdArgs a) {
-  __shared__ SbLds sm;
+  constexpr int kSbTC = SbCfg<NPW>::TC, NN = SbCfg<NPW>::NN;
+  __shared__ SbLds<NPW> sm;
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int64_t tile = blockIdx.x % a.ntile;
@@ -382,14 +409,15 @@ __global__ __launch_bounds__(512) void selective_bwd_kernel(SelBwdArgs a) {
   const int64_t d = tile * kSbCT + lane;
   const bool dok = d < a.D;
   const int N = static_cast<int>(a.N);
-  const int n0 = 2 * w;
+  const int n0 = NPW * w;
   const int64_t D = a.D;
 
-  float Av[2], iAv[2], G[2], dAacc[2] = {0.f, 0.f};
-  bool okj[2];
+  float Av[NPW], iAv[NPW], G[NPW], dAacc[NPW];
+  bool okj[NPW];
   bool small = false;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < NPW; ++j) {
+    dAacc[j] = 0.f;
     okj[j] = dok && n0 + j < N;
     Av[j] = okj[j] ? a.A[d * N + n0 + j] : 0.f;
     iAv[j] = Av[j] != 0.f ? 1.f / Av[j] : 0.f;
@@ -399,7 +427,7 @@ __global__ __launch_bounds__(512) void selective_bwd_kernel(SelBwdArgs a) {
   float dDacc = 0.f;
 
   // B and C columns n >= N stay zero for the whole kernel
-  for (int i = tid; i < kSbTC * 16; i += 512) {
+  for (int i = tid; i < kSbTC * NN; i += 512) {
     (&sm.Bs[0][0])[i] = 0.f;
     (&sm.Cs[0][0])[i] = 0.f;
   }
@@ -414,12 +442,12 @@ __global__ __launch_bounds__(512) void selective_bwd_kernel(SelBwdArgs a) {
 #pragma unroll
   for (int ww = 0; ww < kSbNW; ++ww) precise |= flags[ww] != 0.f;
   if (DISC == kSbZoh && !precise)
-    selective_bwd_body<T, DISC, true>(a, sm, b, tile, Av, iAv, okj, G, dAacc, dDacc);
+    selective_bwd_body<T, DISC, true, NPW>(a, sm, b, tile, Av, iAv, okj, G, dAacc, dDacc);
   else
-    selective_bwd_body<T, DISC, false>(a, sm, b, tile, Av, iAv, okj, G, dAacc, dDacc);
+    selective_bwd_body<T, DISC, false, NPW>(a, sm, b, tile, Av, iAv, okj, G, dAacc, dDacc);
 
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < NPW; ++j) {
     if (okj[j]) {
       const int64_t o = (b * D + d) * N + n0 + j;
       if (a.dh0 != nullptr) a.dh0[o] = G[j];
@@ -482,13 +510,14 @@ static SbLayout sb_layout(int64_t B, int64_t L, int64_t D, int64_t N) {
   w.dC = o; o = sb_align(o + nt * B * L * N * 4);
   w.dA = o; o = sb_align(o + B * D * N * 4);
   w.dD = o; o = sb_align(o + B * D * 4);
-  w.sub = o; o = sb_align(o + B * nt * kSbSub * kSbNW * 2 * kSbCT * 4);
+  const int64_t sub = N <= 2 * kSbNW ? SbCfg<2>::SUB * 2 : SbCfg<4>::SUB * 4;   // SUB x NPW
+  w.sub = o; o = sb_align(o + B * nt * sub * kSbNW * kSbCT * 4);
   w.total = o;
   return w;
 }
 
 bool selective_bwd_supported(int64_t N, int64_t seg) {
-  return N >= 1 && N <= 2 * kSbNW && seg >= 32 && seg <= kSbTC * kSbSub && seg % 32 == 0;
+  return N >= 1 && N <= 4 * kSbNW && seg >= 32 && seg <= 256 && seg % 32 == 0;
 }
 
 size_t selective_bwd_workspace(int64_t B, int64_t L, int64_t D, int64_t N) {
@@ -523,19 +552,24 @@ hipError_t launch_selective_bwd(int disc, const void* x, const void* dt, const f
   a.B = B; a.L = L; a.D = D; a.N = N; a.seg = seg; a.nseg = (L + seg - 1) / seg;
   a.ntile = (D + kSbCT - 1) / kSbCT;
   const dim3 grid(static_cast<unsigned>(B * a.ntile));
-  switch (disc) {
-    case kSbEuler:
-      hipLaunchKernelGGL((selective_bwd_kernel<T, kSbEuler>), grid, dim3(512), 0, stream, a);
-      break;
-    case kSbBilinear:
-      hipLaunchKernelGGL((selective_bwd_kernel<T, kSbBilinear>), grid, dim3(512), 0, stream, a);
-      break;
-    case kSbDirac:
-      hipLaunchKernelGGL((selective_bwd_kernel<T, kSbDirac>), grid, dim3(512), 0, stream, a);
-      break;
-    default:
-      hipLaunchKernelGGL((selective_bwd_kernel<T, kSbZoh>), grid, dim3(512), 0, stream, a);
-  }
+  auto go = [&](auto npw) {
+    constexpr int NPW = decltype(npw)::value;
+    switch (disc) {
+      case kSbEuler:
+        hipLaunchKernelGGL((selective_bwd_kernel<T, kSbEuler, NPW>), grid, dim3(512), 0, stream, a);
+        break;
+      case kSbBilinear:
+        hipLaunchKernelGGL((selective_bwd_kernel<T, kSbBilinear, NPW>), grid, dim3(512), 0, stream, a);
+        break;
+      case kSbDirac:
+        hipLaunchKernelGGL((selective_bwd_kernel<T, kSbDirac, NPW>), grid, dim3(512), 0, stream, a);
+        break;
+      default:
+        hipLaunchKernelGGL((selective_bwd_kernel<T, kSbZoh, NPW>), grid, dim3(512), 0, stream, a);
+    }
+  };
+  if (N <= 2 * kSbNW) go(std::integral_constant<int, 2>{});
+  else go(std::integral_constant<int, 4>{});
   const int64_t nred = B * L * N + D * N + D;
   hipLaunchKernelGGL(selective_bwd_reduce_kernel<T>, dim3((nred + 255) / 256), dim3(256), 0, stream, a);
   return hipGetLastError();

@@ -16,9 +16,10 @@ pytestmark = pytest.mark.gpu
 
 @pytest.mark.parametrize("disc", ["bilinear", "dirac"])
 @pytest.mark.parametrize("io", ["f32", "bf16"])
-def test_selective_fwd_bwd(disc, io):
-    B, L, D, N, seg = 2, 300, 70, 16, 64
-    print(f"selective {disc} io={io}", flush=True)
+@pytest.mark.parametrize("N", [16, 28])
+def test_selective_fwd_bwd(disc, io, N):
+    B, L, D, seg = 2, 300, 70, 64
+    print(f"selective {disc} io={io} N={N}", flush=True)
     g = lrgen.make(2, io=io, B=B, L=L, D=D, N=N, grads=True)
     h0 = lrgen.state_normal((B, D, N), 2, tensor_id=21, std=0.5)
     dhl = lrgen.state_normal((B, D, N), 2, tensor_id=22, std=0.5)

@@ -39,6 +39,10 @@ def _fwd_bwd(T, seg, disc, h0=None, dhl=None):
     ("f32", "zoh", 1, 1, 3, 1, 32, False),
     ("f32", "zoh", 2, 200, 64, 16, 96, True),
     ("bf16", "zoh", 1, 777, 192, 12, 128, True),
+    ("f32", "zoh", 2, 150, 70, 32, 32, False),
+    ("bf16", "zoh", 1, 400, 64, 24, 256, False),
+    ("f32", "euler", 1, 97, 130, 17, 96, False),
+    ("f32", "zoh", 2, 260, 64, 32, 64, True),
 ])
 def test_selective_bwd_parity(io, disc, B, L, D, N, seg, zero_A):
     print(f"selective bwd io={io} disc={disc} B={B} L={L} D={D} N={N} seg={seg} zero_A={zero_A}",
