@@ -159,7 +159,7 @@ size_t lr_selective_scan_bwd_workspace_bytes(int64_t B, int64_t L, int64_t D,
  *   dx, ddt: [B, L, D] io       dBm, dCm: [B, L, N] io
  *   dA: [D, N] fp32    dD: [D] fp32 or NULL    dh0: [B, D, N] fp32 or NULL
  *   workspace: device memory of at least lr_selective_scan_bwd_workspace_bytes().
- * Supported: 1 <= N <= 32; seg a multiple of 32 with 32 <= seg <= 256.
+ * Supported: 1 <= N <= 64; seg a multiple of 32 with 32 <= seg <= 256.
  * ------------------------------------------------------------------------- */
 lr_status lr_selective_scan_bwd(lr_dtype io, lr_disc disc, int64_t B,
                                 int64_t L, int64_t D, int64_t N, int64_t seg,

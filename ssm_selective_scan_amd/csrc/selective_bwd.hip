@@ -38,10 +38,11 @@ constexpr int kSbCT = 64;     // channels per workgroup
 
 // NPW state indices per lane, so a workgroup covers NN = 8 NPW of them;
 // chunks of TC tokens, SUB chunks per segment (seg <= 256).  N <= 16 runs
-// with 2 x 32, N <= 32 with 4 x 16 (the chunk's states fill the same LDS).
+// with 2 x 32, N <= 32 with 4 x 16, N <= 64 with 8 x 8 (the chunk's states
+// fill the same LDS).
 template <int NPW>
 struct SbCfg {
-  static constexpr int TC = NPW == 2 ? 32 : 16;
+  static constexpr int TC = NPW == 2 ? 32 : (NPW == 4 ? 16 : 8);
   static constexpr int SUB = 256 / TC;
   static constexpr int NN = NPW * kSbNW;
 };
@@ -125,7 +126,7 @@ struct SbLds {
   // its slot with the wave's partial sums of dx ([0]) and ddt ([1])
   float hsl[kSbNW][TC][NPW][kSbCT];
   float rbc[TC][2][NN];                               // dB, dC of the chunk
-};   // 160 KB (NPW = 2), 148 KB (NPW = 4)
+};   // 160 KB (NPW = 2), 148 KB (NPW = 4), 142 KB (NPW = 8)
 
 // Sum over the 64 lanes of v[0..3]; on return lane 15 of row q (lanes
 // 16 q .. 16 q + 15) holds the total of v[q].  Halves and rows are paired
@@ -322,7 +323,7 @@ __device__ __forceinline__ void selective_bwd_body(const SelBwdArgs& a, SbLds<NP
           }
         }
       }
-      constexpr int kUnroll = NPW == 2 ? 8 : 4;
+      constexpr int kUnroll = NPW == 2 ? 8 : (NPW == 4 ? 4 : 2);
 #pragma unroll kUnroll
       for (int i = kSbTC - 1; i >= 0; --i) {
         const float xv = sm.xs[i][lane], dtv = sm.dts[i][lane], dyv = sm.dys[i][lane];
@@ -510,14 +511,15 @@ static SbLayout sb_layout(int64_t B, int64_t L, int64_t D, int64_t N) {
   w.dC = o; o = sb_align(o + nt * B * L * N * 4);
   w.dA = o; o = sb_align(o + B * D * N * 4);
   w.dD = o; o = sb_align(o + B * D * 4);
-  const int64_t sub = N <= 2 * kSbNW ? SbCfg<2>::SUB * 2 : SbCfg<4>::SUB * 4;   // SUB x NPW
+  const int64_t sub = N <= 2 * kSbNW ? SbCfg<2>::SUB * 2
+                      : (N <= 4 * kSbNW ? SbCfg<4>::SUB * 4 : SbCfg<8>::SUB * 8);   // SUB x NPW
   w.sub = o; o = sb_align(o + B * nt * sub * kSbNW * kSbCT * 4);
   w.total = o;
   return w;
 }
 
 bool selective_bwd_supported(int64_t N, int64_t seg) {
-  return N >= 1 && N <= 4 * kSbNW && seg >= 32 && seg <= 256 && seg % 32 == 0;
+  return N >= 1 && N <= 8 * kSbNW && seg >= 32 && seg <= 256 && seg % 32 == 0;
 }
 
 size_t selective_bwd_workspace(int64_t B, int64_t L, int64_t D, int64_t N) {
@@ -569,7 +571,8 @@ hipError_t launch_selective_bwd(int disc, const void* x, const void* dt, const f
     }
   };
   if (N <= 2 * kSbNW) go(std::integral_constant<int, 2>{});
-  else go(std::integral_constant<int, 4>{});
+  else if (N <= 4 * kSbNW) go(std::integral_constant<int, 4>{});
+  else go(std::integral_constant<int, 8>{});
   const int64_t nred = B * L * N + D * N + D;
   hipLaunchKernelGGL(selective_bwd_reduce_kernel<T>, dim3((nred + 255) / 256), dim3(256), 0, stream, a);
   return hipGetLastError();

@@ -77,7 +77,7 @@ def test_selective_ckpt_and_bwd_validation(L):
     assert sel(L, seg=32, ck=MIS) == ALIGN
     ws = L.lr_selective_scan_bwd_workspace_bytes(2, 100, 70, 16, 64)
     assert ws > 0
-    assert L.lr_selective_scan_bwd_workspace_bytes(2, 100, 70, 33, 64) == 0
+    assert L.lr_selective_scan_bwd_workspace_bytes(2, 100, 70, 65, 64) == 0
     assert L.lr_selective_scan_bwd_workspace_bytes(2, 100, 70, 16, 48) == 0
     #       io disc B  L    D   N   seg x  dt A  Bm Cm Dk    ckpt dy dhl   dx ddt dA dB dC dD    dh0
     args = [1, 0, 2, 100, 70, 16, 64, P, P, P, P, P, None, P, P, None, P, P, P, P, P, None, None]
@@ -88,7 +88,7 @@ def test_selective_ckpt_and_bwd_validation(L):
     bad[6] = 0
     assert L.lr_selective_scan_bwd(*bad, P, ws, None) == SHAPE
     bad = list(args)
-    bad[5] = 33
+    bad[5] = 65
     assert L.lr_selective_scan_bwd(*bad, P, ws, None) == UNSUP
     bad = list(args)
     bad[13] = None   # ckpt

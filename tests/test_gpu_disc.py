@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
 
 @pytest.mark.parametrize("disc", ["bilinear", "dirac"])
 @pytest.mark.parametrize("io", ["f32", "bf16"])
-@pytest.mark.parametrize("N", [16, 28])
+@pytest.mark.parametrize("N", [16, 28, 50])
 def test_selective_fwd_bwd(disc, io, N):
     B, L, D, seg = 2, 300, 70, 64
     print(f"selective {disc} io={io} N={N}", flush=True)

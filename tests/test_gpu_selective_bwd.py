@@ -43,6 +43,9 @@ def _fwd_bwd(T, seg, disc, h0=None, dhl=None):
     ("bf16", "zoh", 1, 400, 64, 24, 256, False),
     ("f32", "euler", 1, 97, 130, 17, 96, False),
     ("f32", "zoh", 2, 260, 64, 32, 64, True),
+    ("f32", "zoh", 1, 130, 70, 64, 32, False),
+    ("bf16", "euler", 2, 300, 64, 40, 128, False),
+    ("f32", "zoh", 1, 75, 66, 48, 64, True),
 ])
 def test_selective_bwd_parity(io, disc, B, L, D, N, seg, zero_A):
     print(f"selective bwd io={io} disc={disc} B={B} L={L} D={D} N={N} seg={seg} zero_A={zero_A}",
