@@ -231,8 +231,9 @@ size_t lr_ssd_scan_bwd_workspace_bytes(int64_t B, int64_t L, int64_t H,
  *   dBm, dCm: [B, L, G, N] io (summed over the heads of each group)
  *   dA: [H] fp32    dD: [H] fp32 or NULL    dh0: [B, H, P, N] fp32 or NULL
  *   workspace: device memory of at least lr_ssd_scan_bwd_workspace_bytes().
- * Supported: as lr_ssd_scan, with P == 64, seg in {64, 128, 192, 256} and
- * disc in {ZOH, EULER, DIRAC}.
+ * Supported: as lr_ssd_scan, with P == 64 and seg in {64, 128, 192, 256};
+ * every disc, bilinear with negative decays included (their signs are
+ * tracked as in the forward).
  * ------------------------------------------------------------------------- */
 lr_status lr_ssd_scan_bwd(lr_dtype io, lr_disc disc, int64_t B, int64_t L,
                           int64_t H, int64_t P, int64_t G, int64_t N,

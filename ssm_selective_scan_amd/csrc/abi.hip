@@ -305,7 +305,7 @@ lr_status lr_ssd_scan_bwd(lr_dtype io, lr_disc disc, int64_t B, int64_t L, int64
   lr_status st = check_ssd_sizes(io, disc, B, L, H, P, G, N, chunk, seg);
   if (st != LR_OK) return st;
   if (seg < 1) return LR_E_SHAPE;
-  if (!lr::ssd_bwd_supported(P, N, seg) || disc == LR_DISC_BILINEAR) return LR_E_UNSUPPORTED;
+  if (!lr::ssd_bwd_supported(P, N, seg)) return LR_E_UNSUPPORTED;
   if (A == nullptr || dA == nullptr) return LR_E_NULLPTR;
   if (B * L > 0 && any_null({x, dt, Bm, Cm, ckpt, dy, dx, ddt, dBm, dCm})) return LR_E_NULLPTR;
   if (!all_aligned({x, dt, A, Bm, Cm, Dskip, h0, ckpt, dy, dh_last, dx, ddt, dA, dBm, dCm, dD,

@@ -47,7 +47,7 @@ constexpr int kBLd = kBQ + 8;    // leading dim of 64-wide LDS tiles
 // the same recurrence with x <-> v, B <-> k, C <-> q, phi = 1 and the decay
 // given directly as the gate g (log-decay ln g).  A GLA head of V columns is
 // run as V / 64 "heads" of 64 columns that form one group sharing k and q.
-enum { kBwdZoh = 0, kBwdEuler = 1, kBwdGla = 2, kBwdDirac = 3 };
+enum { kBwdZoh = 0, kBwdEuler = 1, kBwdGla = 2, kBwdDirac = 3, kBwdBilinear = 4 };
 
 struct BwdArgs {
   const uint16_t* x; const uint16_t* dt; const float* A; const uint16_t* Bm; const uint16_t* Cm;
@@ -97,6 +97,15 @@ __device__ __forceinline__ void block_scalars(float gate, bool ok, float Ah, flo
   }
   const float dtv = ok ? gate : 0.f;
   const float lam = dtv * Ah;
+  if (DISC == kBwdBilinear) {
+    // e = (1 + l/2)/(1 - l/2), negative for l < -2: its magnitude goes into
+    // the log2 sums and its sign into a parity scan (sign_scan)
+    const float r = __builtin_amdgcn_rcpf(1.f - 0.5f * lam);
+    ek = (1.f + 0.5f * lam) * r;
+    l2 = fmaxf(fast_log2(fabsf(ek)), -126.f);
+    ph = dtv * r;
+    return;
+  }
   l2 = lam * kLog2e;
   ek = fast_exp2(l2);
   if (DISC == kBwdDirac) {
@@ -106,6 +115,20 @@ __device__ __forceinline__ void block_scalars(float gate, bool ok, float Ah, flo
   } else {
     const float ser = dtv * fmaf(lam, fmaf(lam, fmaf(lam, 1.f / 24.f, 1.f / 6.f), 0.5f), 1.f);
     ph = fabsf(lam) < 0.1f ? ser : (ek - 1.f) / Ah;
+  }
+}
+
+// Bilinear only (else both signs are 1): sgc = sign of the decay product
+// from the block start through token `lane` (parity of the negative decays),
+// sge = the same over the whole block.
+template <int DISC>
+__device__ __forceinline__ void sign_scan(float ek, float& sgc, float& sge) {
+  sgc = 1.f;
+  sge = 1.f;
+  if constexpr (DISC == kBwdBilinear) {
+    const float nneg = wave_incl_sum(ek < 0.f ? 1.f : 0.f);
+    sgc = (static_cast<int>(nneg) & 1) ? -1.f : 1.f;
+    sge = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sgc), 63));
   }
 }
 
@@ -187,7 +210,8 @@ __global__ __launch_bounds__(256) void ssd_bwd_gloc_kernel(BwdArgs a) {
   f32x4 gacc[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) gacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float lsum = 0.f;   // log2 of the segment decay
+  float lsum = 0.f;   // log2 of the segment decay's magnitude
+  float ssign = 1.f;  // and its sign
 
   if (nb > 0) fetch(nb - 1);
   for (int j = nb - 1; j >= 0; --j) {
@@ -195,9 +219,11 @@ __global__ __launch_bounds__(256) void ssd_bwd_gloc_kernel(BwdArgs a) {
     const int nv = static_cast<int>((tse - t0) < kBQ ? (tse - t0) : kBQ);
     float l2, ph, ek;
     block_scalars<MODE>(gv, lane < nv, Ah, l2, ph, ek);
+    float sgc, sge;
+    sign_scan<MODE>(ek, sgc, sge);
     const float c = wave_incl_sum(l2);
     const float cend = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), 63));
-    const float el = fast_exp2(c);
+    const float el = fast_exp2(c) * sgc;
     // token-major copies; the contraction over tokens reads them transposed
 #pragma unroll
     for (int k = 0; k < kCC; ++k) {
@@ -215,8 +241,9 @@ __global__ __launch_bounds__(256) void ssd_bwd_gloc_kernel(BwdArgs a) {
     }
     __syncthreads();
     if (j > 0) fetch(j - 1);
-    const float dec = fast_exp2(cend);
+    const float dec = fast_exp2(cend) * sge;
     lsum += cend;
+    ssign *= sge;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       gacc[nt] *= dec;
@@ -232,7 +259,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_gloc_kernel(BwdArgs a) {
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
     *reinterpret_cast<f32x4*>(out + p * NS + 16 * nt + 4 * g4) = gacc[nt];
-  if (tid == 0) a.lam[(sg * a.B + b) * a.H + h] = fast_exp2(lsum);
+  if (tid == 0) a.lam[(sg * a.B + b) * a.H + h] = fast_exp2(lsum) * ssign;
 }
 
 // ---------------------------------------------------------------------------
@@ -275,6 +302,7 @@ struct MainLds {
   // row-major tiles with the transposing LDS read (lds_tile_tr), so every
   // tile is written with 8- or 16-byte stores.
   float cum[kBQ], E[kBQ], sE[kBQ], phi[kBQ], dtv[kBQ], ek[kBQ];
+  float sg[kBQ];               // sign of the decay product from the block start (bilinear)
   float rowTp[12][16], colTp[12][16];
   float toffp[4][kBQ], dphip[4][kBQ], up[4][kBQ];
   float uprevp[4];
@@ -351,9 +379,11 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
       const int nv = static_cast<int>((tse - t0) < kBQ ? (tse - t0) : kBQ);
       float l2, ph, ek;
       block_scalars<DISC>(rg, lane < nv, Ah, l2, ph, ek);
+      float sgc, sge;
+      sign_scan<DISC>(ek, sgc, sge);
       const float c = wave_incl_sum(l2);
       const float cend = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), 63));
-      const float wsl = fast_exp2(cend - c) * (lane < nv ? ph : 0.f);
+      const float wsl = fast_exp2(cend - c) * (sge * sgc) * (lane < nv ? ph : 0.f);
 #pragma unroll
       for (int k = 0; k < kRB; ++k) {
         const int idx = tid + 256 * k, r = idx / (NS / 8), cc = idx % (NS / 8);
@@ -370,7 +400,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
       }
       __syncthreads();
       if (j + 2 < nb) rfetch(j + 1);
-      const float dec = fast_exp2(cend);
+      const float dec = fast_exp2(cend) * sge;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         hacc[nt] *= dec;
@@ -415,13 +445,16 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
       float l2, ph, ek;
       block_scalars<DISC>(dtv, ok, Ah, l2, ph, ek);
       ph = ok ? ph : 0.f;
+      float sgc, sge;
+      sign_scan<DISC>(ek, sgc, sge);
       const float c = wave_incl_sum(l2);
-      const float el = fast_exp2(c);
+      const float el = fast_exp2(c) * sgc;
       if (w == 0) {
         const float cend = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), 63));
         sm.cum[lane] = c;
+        sm.sg[lane] = sgc;
         sm.E[lane] = el;
-        sm.sE[lane] = fast_exp2(cend - c);
+        sm.sE[lane] = fast_exp2(cend - c) * (sge * sgc);
         sm.phi[lane] = ph;
         sm.dtv[lane] = dtv;
         sm.ek[lane] = ek;
@@ -479,10 +512,12 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
           rr = mfma16x16x32(lds_tile(sm.dys, kBLd, 16 * tj, 32 * kp, lane),
                             lds_tile(sm.xs, kBLd, 16 * ti, 32 * kp, lane), rr);
         const float ct = sm.cum[t], pt = sm.phi[t];
+        const float st = DISC == kBwdBilinear ? sm.sg[t] : 1.f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int u = u0 + r;
-          const float m = (u >= t) ? fast_exp2(sm.cum[u] - ct) : 0.f;
+          float m = (u >= t) ? fast_exp2(sm.cum[u] - ct) : 0.f;
+          if (DISC == kBwdBilinear) m *= st * sm.sg[u];
           const float mp = s[r] * m, wv = rr[r] * m;
           const float tv = mp * pt * rr[r];
           om[r] = f2bf(mp);
@@ -601,7 +636,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
     }
     // ---- Gamma for the previous block: E_end Gamma + sum_u E_u dy_u (x) C_u
     {
-      const float dec = fast_exp2(sm.cum[kBQ - 1]);
+      const float dec = fast_exp2(sm.cum[kBQ - 1]) * (DISC == kBwdBilinear ? sm.sg[kBQ - 1] : 1.f);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         gacc[nt] *= dec;
@@ -661,7 +696,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
       const float toff = sm.toffp[0][k] + sm.toffp[1][k] + sm.toffp[2][k] + sm.toffp[3][k];
       const float dph = sm.dphip[0][k] + sm.dphip[1][k] + sm.dphip[2][k] + sm.dphip[3][k];
       const float uu = sm.up[0][k] + sm.up[1][k] + sm.up[2][k] + sm.up[3][k];
-      const float uprev = fast_exp2(sm.cum[kBQ - 1]) *
+      const float uprev = fast_exp2(sm.cum[kBQ - 1]) * (DISC == kBwdBilinear ? sm.sg[kBQ - 1] : 1.f) *
                           (sm.uprevp[0] + sm.uprevp[1] + sm.uprevp[2] + sm.uprevp[3]);
       const float usum = wave_sum(uu);
       float dcum = rowT - colT + toff - uu;
@@ -681,6 +716,15 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
       } else if (DISC == kBwdEuler) {
         ddt = dlam * Ah + dph;
         dAk = dlam * dtv;
+      } else if (DISC == kBwdBilinear) {
+        // dlam is the gradient wrt ln|e|: d ln|e| / dl = 1 / ((1 - l/2)(1 + l/2));
+        // dphi/ddt = r^2, dphi/dA = dt^2 r^2 / 2 with r = 1 / (1 - l/2)
+        const float lam = dtv * Ah;
+        const float r = __builtin_amdgcn_rcpf(1.f - 0.5f * lam);
+        const float dln = r * __builtin_amdgcn_rcpf(1.f + 0.5f * lam);
+        const float gl = isfinite(dln) ? dlam * dln : 0.f;
+        ddt = fmaf(gl, Ah, dph * r * r);
+        dAk = fmaf(gl, dtv, dph * 0.5f * dtv * dtv * r * r);
       } else {
         const float lam = dtv * Ah;
         const float dphidA = fabsf(lam) < 1e-3f
@@ -887,8 +931,10 @@ hipError_t launch_ssd_bwd(int disc, const void* x, const void* dt, const float* 
   a.dx = static_cast<uint16_t*>(dx); a.ddt = static_cast<uint16_t*>(ddt); a.dA = dA;
   a.dBm = static_cast<uint16_t*>(dBm); a.dCm = static_cast<uint16_t*>(dCm); a.dD = dD; a.dh0 = dh0;
   a.B = B; a.L = L; a.H = H; a.G = G; a.N = N; a.seg = seg;
+  // disc holds the public discretisation code (ZOH 0, Euler 1, bilinear 2, dirac 3)
   if (disc == kBwdEuler) return launch_bwd<kBwdEuler>(a, ws, stream);
   if (disc == kBwdDirac) return launch_bwd<kBwdDirac>(a, ws, stream);
+  if (disc == 2) return launch_bwd<kBwdBilinear>(a, ws, stream);
   return launch_bwd<kBwdZoh>(a, ws, stream);
 }
 

@@ -158,8 +158,8 @@ def test_ssd_bwd_validation(L):
         assert L.lr_ssd_scan_bwd(*args, None, 0, None) == WS
         assert L.lr_ssd_scan_bwd(*args, P, ws - 1, None) == WS
     bad = list(args)
-    bad[1] = 2     # bilinear: no backward for the SSD path
-    assert L.lr_ssd_scan_bwd(*bad, P, ws, None) == UNSUP
+    bad[1] = 9     # no such discretisation
+    assert L.lr_ssd_scan_bwd(*bad, P, ws, None) == DTYPE
     bad = list(args)
     bad[9] = 0     # seg = 0
     assert L.lr_ssd_scan_bwd(*bad, P, ws, None) == SHAPE

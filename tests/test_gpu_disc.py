@@ -76,6 +76,34 @@ def test_ssd_bwd_dirac():
         check(k, gr[k], ref[k], TOL["bf16"])
 
 
+@pytest.mark.parametrize("dt_scale,seg,dhl", [(1.0, 128, False), (32.0, 64, True),
+                                          (32.0, 256, False)])
+def test_ssd_bwd_bilinear(dt_scale, seg, dhl):
+    """Bilinear SSD backward; dt_scale = 32 gives negative decays, whose signs
+    the block algebra tracks as the forward does."""
+    B, L, H, G, N = 2, 300, 3, 1, 128
+    print(f"ssd bwd bilinear dt_scale={dt_scale} seg={seg} dh_last={dhl}", flush=True)
+    g = lrgen.make(5, B=B, L=L, H=H, G=G, N=N, seg=seg)
+    dt = lrgen.round_bf16(g["dt"] * dt_scale)   # power-of-two scale keeps bf16 values exact
+    h0 = lrgen.state_normal((B, H, 64, N), 5, tensor_id=21, std=0.3)
+    dh_last = lrgen.state_normal((B, H, 64, N), 5, tensor_id=22, std=0.3) if dhl else None
+    T = {k: dev(g.t(k)) for k in ("x", "A", "B", "C", "Dskip", "dy")}
+    dtd = dev(dt, "bf16")
+    y, hl, ck = lr.lr_ssd_scan(T["x"], dtd, T["A"], T["B"], T["C"], T["Dskip"], dev(h0, "f32"),
+                               disc="bilinear", seg=seg, want_last=True)
+    gr = lr.lr_ssd_scan_bwd(T["x"], dtd, T["A"], T["B"], T["C"], T["Dskip"], dev(h0, "f32"), ck,
+                            T["dy"], None if dh_last is None else dev(dh_last, "f32"),
+                            disc="bilinear", seg=seg, want_dh0=True)
+    torch.cuda.synchronize()
+    if dt_scale > 1:
+        e, _ = oracle.discretize(dt, g["A"][None, None], "bilinear")
+        assert (e < 0).mean() > 0.05, "the case must contain negative decays"
+    ref = oracle.ssd_scan_bwd(g["x"], dt, g["A"], g["B"], g["C"], g["Dskip"], h0, g["dy"],
+                              dh_last, "bilinear")
+    for k in ("dx", "ddt", "dA", "dB", "dC", "dD", "dh0"):
+        check(k, gr[k], ref[k], TOL["bf16"])
+
+
 @pytest.mark.parametrize("disc", ["bilinear", "dirac"])
 def test_steps(disc):
     g = lrgen.make(2, io="f32", B=2, L=17, D=64, N=16)
