@@ -402,3 +402,37 @@ def rotlru_scan(r, theta, u, h0=None):
     last[:, 0::2] = z.real
     last[:, 1::2] = z.imag
     return out, last
+
+
+def rotlru_scan_bwd(r, theta, h, dh, h0=None, dh_last=None):
+    """Reverse-time adjoint of ``rotlru_scan`` for the loss
+    sum_t <dh[:, t], h[:, t]> + <dh_last, h_last>  (h = forward outputs,
+    real inner products over the interleaved pairs).
+
+    With z, g complex per pair (g = dl/dre + 1j dl/dim), a_t = r_t e^{1j theta_t}:
+        g_{L-1} = dh_{L-1} + dh_last,   g_t = dh_t + conj(a_{t+1}) g_{t+1}
+    then du_t = g_t (split back into (re, im)), and with q = g_t conj(e^{1j theta_t} z_{t-1})
+    (z_{-1} = h0 or 0):  dr_t = Re q,  dtheta_t = r_t Im q;  dh0 = conj(a_0) g_0.
+    Returns (dr, dtheta, du, dh0) in float64 (dh0 = dh_last when L = 0)."""
+    r, theta, h, dh = map(_f, (r, theta, h, dh))
+    Bn, L, D = h.shape
+    c = lambda v: v[..., 0::2] + 1j * v[..., 1::2]   # noqa: E731
+    g = np.zeros((Bn, D // 2), np.complex128) if dh_last is None else c(_f(dh_last))
+    zm1 = np.zeros((Bn, D // 2), np.complex128) if h0 is None else c(_f(h0))
+    dr = np.empty((Bn, L, D // 2), F64)
+    dth = np.empty((Bn, L, D // 2), F64)
+    du = np.empty((Bn, L, D), F64)
+    for t in range(L - 1, -1, -1):
+        if t < L - 1:
+            g = np.conj(r[:, t + 1] * np.exp(1j * theta[:, t + 1])) * g
+        g = g + c(dh[:, t])
+        du[:, t, 0::2], du[:, t, 1::2] = g.real, g.imag
+        zp = c(h[:, t - 1]) if t > 0 else zm1
+        q = g * np.conj(np.exp(1j * theta[:, t]) * zp)
+        dr[:, t] = q.real
+        dth[:, t] = r[:, t] * q.imag
+    if L > 0:
+        g = np.conj(r[:, 0] * np.exp(1j * theta[:, 0])) * g
+    dh0 = np.empty((Bn, D), F64)
+    dh0[:, 0::2], dh0[:, 1::2] = g.real, g.imag
+    return dr, dth, du, dh0
