@@ -218,10 +218,17 @@ def measure_rotlru(warmup, iters):
     t, _ = time_launches(lambda s: lr.lr_rotlru_scan(r, th, u, h=h), [None], warmup, iters)
     p = g.params
     nb = 2 * p["B"] * p["L"] * p["D"] * 4 + 2 * p["B"] * p["L"] * (p["D"] // 2) * 4
-    return dict(workload=lrgen.NAMES[6], kernel="rotlru_scan_kernel", us=t * 1e6,
-                tokens_per_s=p["B"] * p["L"] / t, elems_per_s=p["B"] * p["L"] * p["D"] / t,
-                alg_bytes=nb, GBs=nb / t / 1e9, hbm_frac=nb / t / 1e9 / HBM_PEAK_GBS,
-                note="3 MB working set: launch/latency bound")
+    out = dict(workload=lrgen.NAMES[6], kernel="rotlru_scan_kernel", us=t * 1e6,
+               tokens_per_s=p["B"] * p["L"] / t, elems_per_s=p["B"] * p["L"] * p["D"] / t,
+               alg_bytes=nb, GBs=nb / t / 1e9, hbm_frac=nb / t / 1e9 / HBM_PEAK_GBS,
+               note="3 MB working set: launch/latency bound")
+    dh = dev(lrgen.make(6, grads=True).t("dh"))
+    tb, _ = time_launches(lambda s: lr.lr_rotlru_scan_bwd(r, th, h, dh), [None], warmup, iters)
+    # read r, theta, h, dh; write dr, dtheta, du
+    nbb = 3 * p["B"] * p["L"] * p["D"] * 4 + 4 * p["B"] * p["L"] * (p["D"] // 2) * 4
+    out.update(bwd_kernel="rotlru_scan_bwd_kernel", bwd_us=tb * 1e6, bwd_alg_bytes=nbb,
+               bwd_GBs=nbb / tb / 1e9)
+    return out
 
 
 def measure_diag_bwd(warmup, iters):

@@ -120,6 +120,27 @@ lr_status lr_rotlru_scan(lr_dtype io, int64_t B, int64_t L, int64_t D,
                          const float* h0, void* h, float* h_last, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Backward of lr_rotlru_scan (the post's rotlru_scan kernel has a forward and
+ * a backward) for the loss
+ *     sum_t <dh[b,t,:], h[b,t,:]> + <dh_last[b,:], h_last[b,:]>.
+ * In complex form per pair (G_t = gradient w.r.t. z_t, real + i imaginary):
+ * G_{L-1} = dh_{L-1} + dh_last, G_t = conj(a_{t+1}) G_{t+1} + dh_t; then
+ * du_t = G_t, and with q = G_t conj(e^{i theta_t} z_{t-1}) (z_{-1} = h0):
+ * dr_t = Re q, dtheta_t = r_t Im q; dh0 = conj(a_0) G_0.  h is the forward's
+ * output; nothing is recomputed.
+ *   r, theta: [B, L, D/2] io     h, dh: [B, L, D] io
+ *   h0, dh_last: [B, D] fp32 or NULL (= 0)
+ *   dr, dtheta: [B, L, D/2] io   du: [B, L, D] io
+ *   dh0: [B, D] fp32 or NULL; dh0 = dh_last at L = 0
+ * Supported: as lr_rotlru_scan.
+ * ------------------------------------------------------------------------- */
+lr_status lr_rotlru_scan_bwd(lr_dtype io, int64_t B, int64_t L, int64_t D,
+                             const void* r, const void* theta, const void* h,
+                             const float* h0, const void* dh, const float* dh_last,
+                             void* dr, void* dtheta, void* du, float* dh0,
+                             void* stream);
+
+/* ---------------------------------------------------------------------------
  * Mamba-1 selective scan with ZOH (or Euler) discretisation and a fused
  * readout ("lrnnx: A library for Linear RNNs", Key Contributions 3: fused
  * scan + output projection; the hidden state never reaches memory).

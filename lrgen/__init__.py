@@ -175,6 +175,8 @@ def make(cfg_id: int, seed: int = SEED, **over) -> Inputs:
         put("r", _Stream(seed, cfg_id, 0).uniform((B, L, D // 2), 0.90, 0.999), io)
         put("theta", _Stream(seed, cfg_id, 1).uniform((B, L, D // 2), -math.pi, math.pi), io)
         put("u", _Stream(seed, cfg_id, 2).normal((B, L, D)), io)
+        if p.get("grads"):
+            put("dh", _Stream(seed, cfg_id, 3).normal((B, L, D)), io)
     elif kind == "selective":
         B, L, D, N = p["B"], p["L"], p["D"], p["N"]
         put("x", _Stream(seed, cfg_id, 0).normal((B, L, D)), io)

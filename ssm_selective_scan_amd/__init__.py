@@ -13,7 +13,7 @@ import torch
 from ._lib import (LR_BF16, LR_DISC_BILINEAR, LR_DISC_DIRAC, LR_DISC_EULER,  # noqa: F401
                    LR_DISC_ZOH, LR_F32, LrError, check, lib)
 
-__all__ = ["lr_diag_scan", "lr_diag_scan_bwd", "lr_rotlru_scan", "lr_selective_scan", "lr_selective_scan_bwd",
+__all__ = ["lr_diag_scan", "lr_diag_scan_bwd", "lr_rotlru_scan", "lr_rotlru_scan_bwd", "lr_selective_scan", "lr_selective_scan_bwd",
            "lr_selective_scan_bwd_workspace_bytes", "lr_ssd_scan", "lr_ssd_scan_bwd",
            "lr_ssd_scan_bwd_workspace_bytes", "lr_gla_scan", "lr_gla_scan_bwd",
            "lr_gla_scan_bwd_workspace_bytes", "lr_diag_step", "lr_selective_step", "lr_ssd_step",
@@ -93,6 +93,20 @@ def lr_rotlru_scan(r, theta, u, h0=None, h=None, h_last=None, want_last=False):
         _f32(h_last, "h_last"), _stream(u)))
     return h, h_last
 
+
+
+def lr_rotlru_scan_bwd(r, theta, h, dh, h0=None, dh_last=None, want_dh0=False):
+    """Gradients (dr, dtheta, du, dh0) of sum <dh, h> + <dh_last, h_last>
+    through lr_rotlru_scan; h is the forward's output [B, L, D]."""
+    B, L, D = h.shape
+    dr = torch.empty_like(r)
+    dtheta = torch.empty_like(theta)
+    du = torch.empty_like(h)
+    dh0 = torch.empty(B, D, device=h.device, dtype=torch.float32) if want_dh0 else None
+    check("lr_rotlru_scan_bwd", lib().lr_rotlru_scan_bwd(
+        _io(h), B, L, D, _ptr(r), _ptr(theta), _ptr(h), _f32(h0, "h0"), _ptr(dh),
+        _f32(dh_last, "dh_last"), _ptr(dr), _ptr(dtheta), _ptr(du), _f32(dh0, "dh0"), _stream(h)))
+    return dr, dtheta, du, dh0
 
 def lr_selective_scan(x, dt, A, Bm, Cm, Dskip=None, h0=None, disc="zoh", seg=0, y=None,
                       h_last=None, ckpt=None, want_last=False):

@@ -47,6 +47,8 @@ SIGNATURES = {
     "lr_gla_scan_bwd": (_int, [_int] + [_i64] * 7 + [_p, _p, _p, _p, _f32p, _p, _f32p, _p, _p, _p,
                                                      _p, _f32p, _p, _sz, _p]),
     "lr_rotlru_scan": (_int, [_int, _i64, _i64, _i64, _p, _p, _p, _f32p, _p, _f32p, _p]),
+    "lr_rotlru_scan_bwd": (_int, [_int, _i64, _i64, _i64, _p, _p, _p, _f32p, _p, _f32p, _p, _p,
+                                  _p, _f32p, _p]),
     "lr_diag_step": (_int, [_int, _i64, _i64, _p, _p, _f32p, _p, _p]),
     "lr_selective_step": (_int, [_int, _int, _i64, _i64, _i64, _p, _p, _f32p, _p, _p, _f32p,
                                  _f32p, _p, _p]),

@@ -66,6 +66,11 @@ hipError_t launch_rotlru_scan(const void* r, const void* theta, const void* u, c
                               void* h, float* h_last, int64_t B, int64_t L, int64_t D,
                               hipStream_t stream);
 template <typename T>
+hipError_t launch_rotlru_scan_bwd(const void* r, const void* theta, const void* h, const float* h0,
+                                  const void* dh, const float* dh_last, void* dr, void* dtheta,
+                                  void* du, float* dh0, int64_t B, int64_t L, int64_t D,
+                                  hipStream_t stream);
+template <typename T>
 hipError_t launch_diag_step(const void* a, const void* b, float* h, void* out, int64_t n,
                             hipStream_t s);
 template <typename T>
@@ -410,6 +415,26 @@ lr_status lr_rotlru_scan(lr_dtype io, int64_t B, int64_t L, int64_t D, const voi
   auto s = static_cast<hipStream_t>(stream);
   return hip_status(io == LR_F32 ? lr::launch_rotlru_scan<float>(r, theta, u, h0, h, h_last, B, L, D, s)
                                  : lr::launch_rotlru_scan<uint16_t>(r, theta, u, h0, h, h_last, B, L, D, s));
+}
+
+lr_status lr_rotlru_scan_bwd(lr_dtype io, int64_t B, int64_t L, int64_t D, const void* r,
+                             const void* theta, const void* h, const float* h0, const void* dh,
+                             const float* dh_last, void* dr, void* dtheta, void* du, float* dh0,
+                             void* stream) {
+  if (!valid_io(io)) return LR_E_DTYPE;
+  if (B < 0 || L < 0 || D < 2 || D % 2 != 0) return LR_E_SHAPE;
+  if (!elems_ok({B, L, D})) return LR_E_OVERFLOW;
+  int64_t nwg = 1;
+  if (!mul_ok(nwg, B) || !mul_ok(nwg, (D / 2 + 15) / 16) || nwg > kMaxGrid) return LR_E_OVERFLOW;
+  if (B * L > 0 && any_null({r, theta, h, dh, dr, dtheta, du})) return LR_E_NULLPTR;
+  if (!all_aligned({r, theta, h, h0, dh, dh_last, dr, dtheta, du, dh0})) return LR_E_ALIGN;
+  if (B == 0) return LR_OK;
+  auto s = static_cast<hipStream_t>(stream);
+  return hip_status(io == LR_F32
+                        ? lr::launch_rotlru_scan_bwd<float>(r, theta, h, h0, dh, dh_last, dr, dtheta,
+                                                            du, dh0, B, L, D, s)
+                        : lr::launch_rotlru_scan_bwd<uint16_t>(r, theta, h, h0, dh, dh_last, dr,
+                                                               dtheta, du, dh0, B, L, D, s));
 }
 
 // ---------------------------------------------------------------- steps

@@ -144,6 +144,178 @@ __global__ __launch_bounds__(kRotThreads) void rotlru_scan_kernel(
   }
 }
 
+// Backward of the rotational LRU for the loss sum_t <dh_t, h_t> + <dh_last, h_last>
+// (real inner products over the interleaved pairs).  In complex form, with
+// G_t the gradient of the loss with respect to z_t (real part + i imaginary
+// part), the adjoint runs the same recurrence backwards in time with the
+// conjugate coefficient:
+//     G_{L-1} = dh_{L-1} + dh_last,   G_t = conj(a_{t+1}) G_{t+1} + dh_t,
+// so it is scanned with the same combine over reversed steps.  Each step then
+// gives du_t = G_t and, with q = G_t conj(e^{i theta_t} z_{t-1}) (z_{-1} = h0),
+// dr_t = Re q and dtheta_t = r_t Im q; dh0 = conj(a_0) G_0.  The forward
+// already wrote every state, so nothing is recomputed.  Work split as the
+// forward: 16 pairs per workgroup, 64 segments of 8 reversed steps per tile.
+template <typename T>
+__global__ __launch_bounds__(kRotThreads) void rotlru_scan_bwd_kernel(
+    const T* __restrict__ r, const T* __restrict__ theta, const T* __restrict__ h,
+    const float* __restrict__ h0, const T* __restrict__ dh, const float* __restrict__ dh_last,
+    T* __restrict__ dr, T* __restrict__ dtheta, T* __restrict__ du, float* __restrict__ dh0,
+    int64_t L, int64_t Dp) {
+  __shared__ cplx aggA[kRotSegs][kRotCP];
+  __shared__ cplx aggB[kRotSegs][kRotCP];
+  __shared__ cplx carry_in[kRotSegs][kRotCP];
+  __shared__ cplx tile_carry[kRotCP];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int pr = lane & (kRotCP - 1);
+  const int seg = wave * 4 + (lane >> 4);
+  const int64_t ntile = (Dp + kRotCP - 1) / kRotCP;
+  const int64_t bi = blockIdx.x / ntile;
+  const int64_t p0 = (blockIdx.x % ntile) * kRotCP;
+  const int64_t p = p0 + pr;
+  const bool pok = p < Dp;
+  const int64_t D = 2 * Dp;
+
+  if (tid < kRotCP) {
+    const int64_t pp = p0 + tid;
+    tile_carry[tid] = (dh_last != nullptr && pp < Dp)
+                          ? cplx{dh_last[bi * D + 2 * pp], dh_last[bi * D + 2 * pp + 1]}
+                          : cplx{0.f, 0.f};
+  }
+  __syncthreads();
+
+  const int64_t row = bi * L;  // token offset of this batch row
+  for (int64_t u0 = 0; u0 < L; u0 += kRotTile) {
+    const int64_t us = u0 + static_cast<int64_t>(seg) * kRotSeg;
+    // reversed steps u = us + i are tokens t = t_first - i (descending)
+    const int64_t t_first = L - 1 - us;
+    const int nok = pok ? static_cast<int>(L - us < kRotSeg ? (L - us > 0 ? L - us : 0) : kRotSeg) : 0;
+    // gate and unit rotation of tokens t_first + 1 - j, j = 0..kRotSeg: entry j
+    // is the coefficient of reversed step j (conjugated) and, for j >= 1, the
+    // rotation of the output of step j - 1 (whose gate is reloaded there, an
+    // L2 hit, to keep the register count down); identity where there is no token
+    cplx ev[kRotSeg + 1];
+    float rv[kRotSeg + 1];
+#pragma unroll
+    for (int j = 0; j <= kRotSeg; ++j) {
+      const int64_t tj = t_first + 1 - j;
+      const bool ok = j == 0 ? (nok > 0 && tj < L) : (j - 1 < nok);
+      ev[j] = {1.f, 0.f};
+      rv[j] = 1.f;
+      if (ok) {
+        const int64_t rowp = (row + tj) * Dp + p;
+        rv[j] = Io<T>::load(r + rowp);
+        float sn, cs;
+        sincosf(Io<T>::load(theta + rowp), &sn, &cs);
+        ev[j] = {cs, sn};
+      }
+    }
+    cplx Pv[kRotSeg], Hv[kRotSeg];
+    {
+      cplx P = {1.f, 0.f}, Gs = {0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < kRotSeg; ++i) {
+        cplx a = {1.f, 0.f}, w = {0.f, 0.f};
+        if (i < nok) {
+          a = {rv[i] * ev[i].re, -rv[i] * ev[i].im};
+          const int64_t rowu = (row + t_first - i) * D + 2 * p;
+          w = {Io<T>::load(dh + rowu), Io<T>::load(dh + rowu + 1)};
+        }
+        Gs = cfma(a, Gs, w);
+        P = cmul(a, P);
+        Pv[i] = P;
+        Hv[i] = Gs;
+      }
+      aggA[seg][pr] = P;
+      aggB[seg][pr] = Gs;
+    }
+    __syncthreads();
+
+    if (wave < kRotCP) {
+      const int c = wave;
+      cplx pa = aggA[lane][c], pb = aggB[lane][c];
+      const cplx tc = tile_carry[c];
+      cwave_incl_pair_scan(pa, pb);
+      const cplx ea = {wave_shr1(pa.re, 1.f), wave_shr1(pa.im, 0.f)};
+      const cplx eb = {wave_shr1(pb.re, 0.f), wave_shr1(pb.im, 0.f)};
+      carry_in[lane][c] = cfma(ea, tc, eb);
+      if (lane == 63) tile_carry[c] = cfma(pa, tc, pb);
+    }
+    __syncthreads();
+
+    const cplx cin = carry_in[seg][pr];
+    // element offsets of token t_first, passed through an empty asm so that the
+    // per-step addresses are formed here rather than kept live from the loads
+    // before the barrier (which spilled them)
+    int64_t offu = (row + t_first) * D + 2 * p, offp = (row + t_first) * Dp + p;
+    asm volatile("" : "+v"(offu), "+v"(offp));
+#pragma unroll
+    for (int i = 0; i < kRotSeg; ++i) {
+      if (i < nok) {
+        const int64_t t = t_first - i;
+        const cplx g = cfma(Pv[i], cin, Hv[i]);
+        cplx zp;
+        const int64_t rowu = offu - i * D;
+        const int64_t rowp = offp - i * Dp;
+        if (t > 0) {
+          const int64_t rowq = rowu - D;
+          zp = {Io<T>::load(h + rowq), Io<T>::load(h + rowq + 1)};
+        } else {
+          zp = h0 != nullptr ? cplx{h0[bi * D + 2 * p], h0[bi * D + 2 * p + 1]} : cplx{0.f, 0.f};
+        }
+        // q = g conj(e z_prev) with e = ev[i + 1] the rotation of token t
+        const cplx ez = cmul(ev[i + 1], zp);
+        const float qre = fmaf(g.re, ez.re, g.im * ez.im);
+        const float qim = fmaf(g.im, ez.re, -g.re * ez.im);
+        Io<T>::store(dr + rowp, qre);
+        Io<T>::store(dtheta + rowp, Io<T>::load(r + rowp) * qim);
+        Io<T>::store(du + rowu, g.re);
+        Io<T>::store(du + rowu + 1, g.im);
+      }
+    }
+  }
+  __syncthreads();
+  if (dh0 != nullptr && tid < kRotCP) {
+    const int64_t pp = p0 + tid;
+    if (pp < Dp) {
+      cplx g = tile_carry[tid];
+      if (L > 0) {
+        const float r0 = Io<T>::load(r + row * Dp + pp);
+        float sn, cs;
+        sincosf(Io<T>::load(theta + row * Dp + pp), &sn, &cs);
+        g = cmul({r0 * cs, -r0 * sn}, g);
+      }
+      dh0[bi * D + 2 * pp] = g.re;
+      dh0[bi * D + 2 * pp + 1] = g.im;
+    }
+  }
+}
+
+template <typename T>
+hipError_t launch_rotlru_scan_bwd(const void* r, const void* theta, const void* h,
+                                  const float* h0, const void* dh, const float* dh_last, void* dr,
+                                  void* dtheta, void* du, float* dh0, int64_t B, int64_t L,
+                                  int64_t D, hipStream_t stream) {
+  const int64_t Dp = D / 2;
+  dim3 grid(static_cast<unsigned>(B * ((Dp + kRotCP - 1) / kRotCP)));
+  hipLaunchKernelGGL(rotlru_scan_bwd_kernel<T>, grid, dim3(kRotThreads), 0, stream,
+                     static_cast<const T*>(r), static_cast<const T*>(theta),
+                     static_cast<const T*>(h), h0, static_cast<const T*>(dh), dh_last,
+                     static_cast<T*>(dr), static_cast<T*>(dtheta), static_cast<T*>(du), dh0, L,
+                     Dp);
+  return hipGetLastError();
+}
+
+template hipError_t launch_rotlru_scan_bwd<float>(const void*, const void*, const void*,
+                                                  const float*, const void*, const float*, void*,
+                                                  void*, void*, float*, int64_t, int64_t, int64_t,
+                                                  hipStream_t);
+template hipError_t launch_rotlru_scan_bwd<uint16_t>(const void*, const void*, const void*,
+                                                     const float*, const void*, const float*,
+                                                     void*, void*, void*, float*, int64_t,
+                                                     int64_t, int64_t, hipStream_t);
+
 template <typename T>
 hipError_t launch_rotlru_scan(const void* r, const void* theta, const void* u, const float* h0,
                               void* h, float* h_last, int64_t B, int64_t L, int64_t D,

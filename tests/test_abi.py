@@ -247,3 +247,16 @@ def test_rotlru_validation(L):
     assert rot(u=MIS) == ALIGN
     assert rot(h0=MIS) == ALIGN
     assert rot(B=0, r=None, th=None, u=None, h=None) == OK
+
+
+def test_rotlru_bwd_validation(L):
+    rb = lambda io=0, B=1, D=8, r=P, th=P, h=P, dh=P, dr=P, dth=P, du=P, dh0=None: \
+        L.lr_rotlru_scan_bwd(io, B, 16, D, r, th, h, None, dh, None, dr, dth, du, dh0, None)
+    assert rb(io=2) == DTYPE
+    assert rb(D=7) == SHAPE
+    assert rb(D=0) == SHAPE
+    assert rb(dth=None) == NULL
+    assert rb(du=None) == NULL
+    assert rb(h=MIS) == ALIGN
+    assert rb(dh0=MIS) == ALIGN
+    assert rb(B=0, r=None, th=None, h=None, dh=None, dr=None, dth=None, du=None) == OK

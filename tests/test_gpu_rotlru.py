@@ -38,3 +38,50 @@ def test_rotlru_empty_and_determinism():
     r2, _ = lr.lr_rotlru_scan(*args)
     torch.cuda.synchronize()
     assert torch.equal(r1, r2)
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("B,L,D", [(1, 1024, 256), (2, 1500, 38), (1, 1, 2), (3, 513, 64),
+                                   (1, 4097, 40), (2, 512, 34)])
+def test_rotlru_bwd_parity(io, B, L, D):
+    print(f"rotlru bwd io={io} B={B} L={L} D={D}", flush=True)
+    g = lrgen.make(6, io=io, B=B, L=L, D=D, grads=True)
+    h0 = lrgen.state_normal((B, D), 6)
+    dhl = lrgen.state_normal((B, D), 6, tensor_id=21)
+    r, th = dev(g.t("r")), dev(g.t("theta"))
+    h, _ = lr.lr_rotlru_scan(r, th, dev(g.t("u")), h0=dev(h0))
+    # the oracle differentiates at the states the GPU forward produced (as
+    # rounded to io), exactly what the backward consumes
+    hh = h.float().cpu().numpy()
+    dr, dth, du, dh0 = lr.lr_rotlru_scan_bwd(r, th, h, dev(g.t("dh")), h0=dev(h0),
+                                             dh_last=dev(dhl), want_dh0=True)
+    torch.cuda.synchronize()
+    rdr, rdth, rdu, rdh0 = oracle.rotlru_scan_bwd(g["r"], g["theta"], hh, g["dh"], h0, dhl)
+    check("dr", dr, rdr, TOL[io])
+    check("dtheta", dth, rdth, TOL[io])
+    check("du", du, rdu, TOL[io])
+    check("dh0", dh0, rdh0, TOL["f32"] if io == "f32" else TOL["bf16"])
+
+
+def test_rotlru_bwd_no_state_and_determinism():
+    # no h0 / dh_last: z_{-1} = 0, so dr and dtheta of token 0 vanish
+    g = lrgen.make(6, B=2, L=700, D=20, grads=True)
+    r, th, dh = dev(g.t("r")), dev(g.t("theta")), dev(g.t("dh"))
+    h, _ = lr.lr_rotlru_scan(r, th, dev(g.t("u")))
+    r1 = lr.lr_rotlru_scan_bwd(r, th, h, dh, want_dh0=True)
+    r2 = lr.lr_rotlru_scan_bwd(r, th, h, dh, want_dh0=True)
+    torch.cuda.synchronize()
+    for x1, x2 in zip(r1, r2):
+        assert torch.equal(x1, x2)
+    assert torch.count_nonzero(r1[0][:, 0]) == 0 and torch.count_nonzero(r1[1][:, 0]) == 0
+    ref = oracle.rotlru_scan_bwd(g["r"], g["theta"], h.cpu().numpy(), g["dh"])
+    for name, x, e in zip(("dr", "dtheta", "du", "dh0"), r1, ref):
+        check(name, x, e, TOL["f32"])
+    # empty sequence: dh0 = dh_last
+    dhl = torch.randn(2, 6, device="cuda")
+    z = torch.empty(2, 0, 3, device="cuda")
+    _, _, _, dh0 = lr.lr_rotlru_scan_bwd(z, z, torch.empty(2, 0, 6, device="cuda"),
+                                         torch.empty(2, 0, 6, device="cuda"), dh_last=dhl,
+                                         want_dh0=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dh0, dhl)
