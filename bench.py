@@ -460,6 +460,20 @@ def main():
     log(f"[bench] headline: {ms_step:.3f} ms/step wall, kernel {kern_ms.mean() * 1e3:.1f} us "
         f"(min {kern_ms.min() * 1e3:.1f}, max {kern_ms.max() * 1e3:.1f})")
 
+    # repeated-experiment protocol of the lrnnx benchmarks: 10 warm-ups, then
+    # 90 timed launches, 5 experiments; mean and std of the experiment means
+    exp_means, all_ms = [], []
+    for _ in range(5):
+        _, ms = time_launches(fn, sets, 10, 90)
+        exp_means.append(ms.mean())
+        all_ms.append(ms)
+    all_ms = np.concatenate(all_ms)
+    protocol = {"experiments": 5, "warmup": 10, "launches": 90,
+                "mean_us": float(np.mean(exp_means) * 1e3),
+                "std_us": float(np.std(exp_means) * 1e3),
+                "median_us": float(np.median(all_ms) * 1e3)}
+    log(f"[bench] protocol: {protocol}")
+
     kt = kern_ms.mean() / 1e3
     nbytes = selective_bytes(p)
     ops = sel_valu_ops(p)
@@ -479,6 +493,7 @@ def main():
         "config": {"workload": lrgen.NAMES[2], "B": p["B"], "L": p["L"], "D": p["D"],
                    "N": p["N"], "io": "bf16", "state": "f32", "disc": "zoh"},
         "kernel_us": kern_ms.mean() * 1e3,
+        "kernel_protocol": protocol,
         "roofline": roofline,
     }
     del sets
