@@ -182,7 +182,8 @@ def test_ssd_full_size_sampled():
 
 # -------------------------------------------------------------------- GLA
 @pytest.mark.parametrize("B,L,H,K,V", [(1, 1, 1, 128, 128), (2, 64, 2, 64, 64), (1, 100, 2, 128, 128),
-                                       (2, 130, 1, 128, 64), (1, 257, 3, 64, 128)])
+                                       (2, 130, 1, 128, 64), (1, 257, 3, 64, 128),
+                                       (1, 300, 2, 128, 256), (2, 70, 1, 64, 384)])
 def test_gla_parity(B, L, H, K, V):
     print(f"gla B={B} L={L} H={H} K={K} V={V}", flush=True)
     g = lrgen.make(4, B=B, L=L, H=H, K=K, V=V)
