@@ -405,8 +405,10 @@ SECONDARY = {"diag": measure_diag, "ssd": measure_ssd, "gla": measure_gla,
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the first few dozen launches run 5-10 % slow while the clocks ramp up;
+    # 50 warm-up steps (20 ms) reach the steady state
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--headline-only", action="store_true",
                     help="time only the headline workload (for profiler runs)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
