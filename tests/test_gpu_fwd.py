@@ -102,6 +102,23 @@ def test_selective_full_size_sampled():
         check(f"h_last[b={b}]", host(hl[b:b + 1, dsel]), rl, TOL["bf16"])
 
 
+
+def test_selective_max_channels_sampled():
+    """The largest channel count the entry point accepts (D = 2^24, 524288
+    workgroups of the paired kernel) with a ragged 5-token sequence; sampled
+    channels at both ends and in the middle against the oracle."""
+    D = 1 << 24
+    print(f"selective max D={D} B=1 L=5 N=16 bf16", flush=True)
+    g = lrgen.make(2, B=1, L=5, D=D)
+    y, hl = lr.lr_selective_scan(dev(g.t("x")), dev(g.t("dt")), dev(g.t("A")), dev(g.t("B")),
+                                 dev(g.t("C")), dev(g.t("Dskip")), want_last=True)
+    _sync()
+    dsel = np.r_[0:40, D // 2 - 20:D // 2 + 20, D - 40:D]
+    ry, rl = oracle.selective_scan(g["x"][:, :, dsel], g["dt"][:, :, dsel], g["A"][dsel], g["B"],
+                                   g["C"], g["Dskip"][dsel])
+    check("y", host(y[:, :, dsel]), ry, TOL["bf16"])
+    check("h_last", host(hl[:, dsel]), rl, TOL["bf16"])
+
 # -------------------------------------------------------------------- SSD
 def _ssd(g, disc="zoh", h0=None, seg=0, chunk=64):
     return lr.lr_ssd_scan(dev(g.t("x")), dev(g.t("dt")), dev(g.t("A")), dev(g.t("B")),
