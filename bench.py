@@ -261,10 +261,26 @@ def measure_selective_bwd(warmup, iters):
                                                              seg=seg, workspace=ws),
                           [None], warmup, iters)
     bwd_bytes = 5 * B * L * D * 2 + 4 * B * L * N * 2 + ckpt.numel() * 4
-    return dict(workload=lrgen.NAMES[2] + "_fwd_bwd_seg256", fwd_us=tf * 1e6, bwd_us=tb * 1e6,
-                fwd_bwd_tokens_per_s=B * L / (tf + tb), bwd_GBs=bwd_bytes / tb / 1e9,
-                ckpt_bytes=ckpt.numel() * 4, full_state_bytes=L * B * D * N * 4,
-                bwd_workspace_bytes=ws.numel())
+    out = dict(workload=lrgen.NAMES[2] + "_fwd_bwd_seg256", fwd_us=tf * 1e6, bwd_us=tb * 1e6,
+               fwd_bwd_tokens_per_s=B * L / (tf + tb), bwd_GBs=bwd_bytes / tb / 1e9,
+               ckpt_bytes=ckpt.numel() * 4, full_state_bytes=L * B * D * N * 4,
+               bwd_workspace_bytes=ws.numel())
+    # the other end of the memory/compute trade: a checkpoint every 32 tokens
+    # (8x the checkpoint memory) spares the backward its segment forward pass
+    del ckpt, ws
+    s32 = 32
+    ck32 = torch.empty((L + s32 - 1) // s32, B, D, N, device="cuda", dtype=torch.float32)
+    tf32, _ = time_launches(lambda s: lr.lr_selective_scan(x, dt, A, Bm, Cm, Dk, seg=s32, y=y,
+                                                           ckpt=ck32), [None], warmup, iters)
+    ws32 = torch.empty(max(lr.lr_selective_scan_bwd_workspace_bytes(B, L, D, N, s32), 16),
+                       device="cuda", dtype=torch.uint8)
+    tb32, _ = time_launches(lambda s: lr.lr_selective_scan_bwd(x, dt, A, Bm, Cm, Dk, ck32, dy,
+                                                               seg=s32, workspace=ws32),
+                            [None], warmup, iters)
+    out["seg32"] = dict(fwd_us=tf32 * 1e6, bwd_us=tb32 * 1e6,
+                        fwd_bwd_tokens_per_s=B * L / (tf32 + tb32), ckpt_bytes=ck32.numel() * 4,
+                        bwd_workspace_bytes=ws32.numel())
+    return out
 
 
 def measure_gla_bwd(warmup, iters):
