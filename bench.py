@@ -231,6 +231,33 @@ def measure_rotlru(warmup, iters):
     return out
 
 
+
+def measure_scaled(warmup, iters):
+    """Labelled scaled sweep of the two elementwise scans (diagonal and
+    rotational LRU), whose small workloads are launch bound: B=16, L=8192,
+    D=4096, fp32, seeded uniform/normal inputs of the small workloads'
+    distributions.  Reports the algorithmic HBM bandwidth of each kernel."""
+    B, L, D = 16, 8192, 4096
+    gen = torch.Generator(device="cuda").manual_seed(2026)
+    a = torch.empty(B, L, D, device="cuda").uniform_(0.90, 0.999, generator=gen)
+    b = torch.randn(B, L, D, device="cuda", generator=gen)
+    h = torch.empty_like(a)
+    t, _ = time_launches(lambda s: lr.lr_diag_scan(a, b, h=h), [None], warmup, iters)
+    nb = 3 * B * L * D * 4
+    out = {"diag": dict(shape=f"B{B}_L{L}_D{D}_fp32", us=t * 1e6, alg_bytes=nb, GBs=nb / t / 1e9,
+                        hbm_frac=nb / t / 1e9 / HBM_PEAK_GBS)}
+    t, _ = time_launches(lambda s: lr.lr_diag_scan_bwd(a, h, b), [None], warmup, iters)
+    nb = 5 * B * L * D * 4     # read a, h, dh; write da, db
+    out["diag_bwd"] = dict(shape=f"B{B}_L{L}_D{D}_fp32", us=t * 1e6, alg_bytes=nb,
+                           GBs=nb / t / 1e9, hbm_frac=nb / t / 1e9 / HBM_PEAK_GBS)
+    th = torch.empty(B, L, D // 2, device="cuda").uniform_(-np.pi, np.pi, generator=gen)
+    r = a[:, :, :D // 2].contiguous()
+    t, _ = time_launches(lambda s: lr.lr_rotlru_scan(r, th, b, h=h), [None], warmup, iters)
+    nb = 2 * B * L * D * 4 + 2 * B * L * (D // 2) * 4
+    out["rotlru"] = dict(shape=f"B{B}_L{L}_D{D}_fp32", us=t * 1e6, alg_bytes=nb,
+                         GBs=nb / t / 1e9, hbm_frac=nb / t / 1e9 / HBM_PEAK_GBS)
+    return out
+
 def measure_diag_bwd(warmup, iters):
     g = lrgen.make(1, grads=True)
     a, b, dh = dev(g.t("a")), dev(g.t("b")), dev(g.t("dh"))
@@ -415,7 +442,7 @@ def load_traffic():
 SECONDARY = {"diag": measure_diag, "ssd": measure_ssd, "gla": measure_gla,
              "ssd_fwd_bwd": measure_ssd_bwd, "diag_bwd": measure_diag_bwd,
              "selective_fwd_bwd": measure_selective_bwd, "gla_fwd_bwd": measure_gla_bwd,
-             "decode": measure_decode, "rotlru": measure_rotlru}
+             "decode": measure_decode, "rotlru": measure_rotlru, "scaled": measure_scaled}
 
 
 def main():

@@ -4,14 +4,17 @@
 // "K-Search for MLX", section "A 20x faster prefill: the Mamba SSM kernel":
 // recurrence, associative combine and the O(log N)-depth parallel scan.)
 //
-// One workgroup owns CT = 16 channels of one batch row and walks the sequence
-// in tiles of 512 steps.  Inside a tile the 1024 threads split time:
-// lane = 16 * (segment within wave) + channel, so each of the 64 time
-// segments of 8 steps is scanned sequentially in registers (loads of 16
-// consecutive channels are 64-byte coalesced).  The 64 segment aggregates of
-// each channel are then combined by one wave with a DPP (a, b)-pair scan, the
+// One workgroup owns 16 channel groups of one batch row (a group is CPL = 1,
+// 2 or 4 adjacent channels, read and written as one vector) and walks the
+// sequence in tiles of 512 steps.  Inside a tile the 1024 threads split time:
+// lane = 16 * (segment within wave) + group, so each of the 64 time segments
+// of 8 steps is scanned sequentially in registers (a 16-lane row reads 64,
+// 128 or 256 contiguous bytes of a token).  The 64 segment aggregates of each
+// channel are then combined by one wave with a DPP (a, b)-pair scan, the
 // carry entering the tile is folded in, and every lane finishes its segment.
 // The carry between tiles lives in LDS, so any L runs in the same launch.
+// CPL = 1 keeps more workgroups for small problems; wider groups are used
+// once they still fill the chip.
 #include "common.hpp"
 
 namespace lr {
@@ -22,65 +25,121 @@ constexpr int kDiagThreads = 1024;   // 16 waves, 4 segments per wave
 constexpr int kDiagSegs = kDiagThreads / kDiagCT;  // 64 segments per tile
 constexpr int kDiagTile = kDiagSegs * kDiagSeg;    // 512 steps per tile
 
-template <typename T>
+// CPL consecutive channels per lane, read and written as one CPL-wide vector
+// access (a 16-lane row of a wave then covers 16 * CPL channels of a token).
+template <typename T, int CPL>
+__device__ __forceinline__ void vload(const T* p, float (&v)[CPL]) {
+  if constexpr (CPL == 1) {
+    v[0] = Io<T>::load(p);
+  } else if constexpr (sizeof(T) == 4) {
+    if constexpr (CPL == 2) {
+      const float2 x = *reinterpret_cast<const float2*>(p);
+      v[0] = x.x; v[1] = x.y;
+    } else {
+      const float4 x = *reinterpret_cast<const float4*>(p);
+      v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+    }
+  } else {
+    if constexpr (CPL == 2) {
+      const uint32_t x = *reinterpret_cast<const uint32_t*>(p);
+      v[0] = bf2f(static_cast<uint16_t>(x)); v[1] = bf2f(static_cast<uint16_t>(x >> 16));
+    } else {
+      const uint2 x = *reinterpret_cast<const uint2*>(p);
+      v[0] = bf2f(static_cast<uint16_t>(x.x)); v[1] = bf2f(static_cast<uint16_t>(x.x >> 16));
+      v[2] = bf2f(static_cast<uint16_t>(x.y)); v[3] = bf2f(static_cast<uint16_t>(x.y >> 16));
+    }
+  }
+}
+template <typename T, int CPL>
+__device__ __forceinline__ void vstore(T* p, const float (&v)[CPL]) {
+  if constexpr (CPL == 1) {
+    Io<T>::store(p, v[0]);
+  } else if constexpr (sizeof(T) == 4) {
+    if constexpr (CPL == 2) *reinterpret_cast<float2*>(p) = float2{v[0], v[1]};
+    else *reinterpret_cast<float4*>(p) = float4{v[0], v[1], v[2], v[3]};
+  } else {
+    if constexpr (CPL == 2) {
+      *reinterpret_cast<uint32_t*>(p) = f2bf(v[0]) | (static_cast<uint32_t>(f2bf(v[1])) << 16);
+    } else {
+      *reinterpret_cast<uint2*>(p) =
+          uint2{f2bf(v[0]) | (static_cast<uint32_t>(f2bf(v[1])) << 16),
+                f2bf(v[2]) | (static_cast<uint32_t>(f2bf(v[3])) << 16)};
+    }
+  }
+}
+
+// CPL = 1: 16 channels per workgroup (small problems: more workgroups);
+// CPL = 2, 4: 32 or 64 channels per workgroup with 8- or 16-byte accesses
+// (large problems, where the 64-byte row pieces of CPL = 1 cost bandwidth).
+// Vector widths need D % CPL == 0.
+template <typename T, int CPL>
 __global__ __launch_bounds__(kDiagThreads) void diag_scan_kernel(
     const T* __restrict__ a, const T* __restrict__ b, const float* __restrict__ h0,
     T* __restrict__ h, float* __restrict__ h_last, int64_t L, int64_t D) {
-  __shared__ float aggA[kDiagSegs][kDiagCT];
-  __shared__ float aggB[kDiagSegs][kDiagCT];
-  __shared__ float carry_in[kDiagSegs][kDiagCT];
-  __shared__ float tile_carry[kDiagCT];
+  constexpr int CT = kDiagCT * CPL;   // channels per workgroup
+  __shared__ float aggA[kDiagSegs][CT];
+  __shared__ float aggB[kDiagSegs][CT];
+  __shared__ float carry_in[kDiagSegs][CT];
+  __shared__ float tile_carry[CT];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  const int ch = lane & (kDiagCT - 1);
+  const int ch = (lane & (kDiagCT - 1)) * CPL;   // first of this lane's CPL channels
   const int seg = wave * 4 + (lane >> 4);
-  const int64_t ntile = (D + kDiagCT - 1) / kDiagCT;
+  const int64_t ntile = (D + CT - 1) / CT;
   const int64_t bi = blockIdx.x / ntile;
-  const int64_t d0 = (blockIdx.x % ntile) * kDiagCT;
+  const int64_t d0 = (blockIdx.x % ntile) * CT;
   const int64_t d = d0 + ch;
-  const bool dok = d < D;
+  const bool dok = d < D;   // D % CPL == 0: all CPL channels exist
 
-  if (tid < kDiagCT) {
-    const int64_t dd = d0 + tid;
-    tile_carry[tid] = (h0 != nullptr && dd < D) ? h0[bi * D + dd] : 0.f;
+  for (int c = tid; c < CT; c += kDiagThreads) {
+    const int64_t dd = d0 + c;
+    tile_carry[c] = (h0 != nullptr && dd < D) ? h0[bi * D + dd] : 0.f;
   }
   __syncthreads();
 
   const int64_t row = bi * L;  // token offset of this batch row
   for (int64_t t0 = 0; t0 < L; t0 += kDiagTile) {
     const int64_t ts = t0 + static_cast<int64_t>(seg) * kDiagSeg;
-    float av[kDiagSeg], bv[kDiagSeg];
+    const int nok = dok ? static_cast<int>(L - ts < kDiagSeg ? (L - ts > 0 ? L - ts : 0) : kDiagSeg) : 0;
+    float av[kDiagSeg][CPL], bv[kDiagSeg][CPL];
     {
       const int64_t off0 = (row + ts) * D + d;
       const T* pa = a + off0;
       const T* pb = b + off0;
-      const int nok = dok ? static_cast<int>(L - ts < kDiagSeg ? (L - ts > 0 ? L - ts : 0) : kDiagSeg) : 0;
 #pragma unroll
       for (int i = 0; i < kDiagSeg; ++i) {
-        const bool ok = i < nok;
-        av[i] = ok ? Io<T>::load(pa) : 1.f;
-        bv[i] = ok ? Io<T>::load(pb) : 0.f;
+        if (i < nok) {
+          vload<T, CPL>(pa, av[i]);
+          vload<T, CPL>(pb, bv[i]);
+        } else {
+#pragma unroll
+          for (int k = 0; k < CPL; ++k) { av[i][k] = 1.f; bv[i][k] = 0.f; }
+        }
         pa += D;
         pb += D;
       }
     }
     // sequential scan of the segment from a zero state
-    float P = 1.f, Hs = 0.f;
 #pragma unroll
-    for (int i = 0; i < kDiagSeg; ++i) {
-      Hs = fmaf(av[i], Hs, bv[i]);
-      P *= av[i];
-      av[i] = P;   // running product  a_i ... a_first
-      bv[i] = Hs;  // running state from zero
+    for (int k = 0; k < CPL; ++k) {
+      float P = 1.f, Hs = 0.f;
+#pragma unroll
+      for (int i = 0; i < kDiagSeg; ++i) {
+        Hs = fmaf(av[i][k], Hs, bv[i][k]);
+        P *= av[i][k];
+        av[i][k] = P;   // running product  a_i ... a_first
+        bv[i][k] = Hs;  // running state from zero
+      }
+      aggA[seg][ch + k] = P;
+      aggB[seg][ch + k] = Hs;
     }
-    aggA[seg][ch] = P;
-    aggB[seg][ch] = Hs;
     __syncthreads();
 
-    if (wave < kDiagCT) {
-      // one wave per channel: lane = segment index
-      const int c = wave;
+    // one wave per channel (CPL channels per wave): lane = segment index
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) {
+      const int c = wave + kDiagCT * k;
       float pa = aggA[lane][c], pb = aggB[lane][c];
       const float tc = tile_carry[c];
       wave_incl_pair_scan(pa, pb);
@@ -91,21 +150,32 @@ __global__ __launch_bounds__(kDiagThreads) void diag_scan_kernel(
     }
     __syncthreads();
 
-    const float cin = carry_in[seg][ch];
+    float cin[CPL];
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) cin[k] = carry_in[seg][ch + k];
     {
-      T* ph = h + (row + ts) * D + d;
-      const int nok = dok ? static_cast<int>(L - ts < kDiagSeg ? (L - ts > 0 ? L - ts : 0) : kDiagSeg) : 0;
+      // offset formed after the barrier (see the backward kernel)
+      int64_t offs = (row + ts) * D + d;
+      asm volatile("" : "+v"(offs));
+      T* ph = h + offs;
 #pragma unroll
       for (int i = 0; i < kDiagSeg; ++i) {
-        if (i < nok) Io<T>::store(ph, fmaf(av[i], cin, bv[i]));
+        if (i < nok) {
+          float o[CPL];
+#pragma unroll
+          for (int k = 0; k < CPL; ++k) o[k] = fmaf(av[i][k], cin[k], bv[i][k]);
+          vstore<T, CPL>(ph, o);
+        }
         ph += D;
       }
     }
   }
   __syncthreads();
-  if (h_last != nullptr && tid < kDiagCT) {
-    const int64_t dd = d0 + tid;
-    if (dd < D) h_last[bi * D + dd] = tile_carry[tid];
+  if (h_last != nullptr) {
+    for (int c = tid; c < CT; c += kDiagThreads) {
+      const int64_t dd = d0 + c;
+      if (dd < D) h_last[bi * D + dd] = tile_carry[c];
+    }
   }
 }
 
@@ -117,29 +187,30 @@ __global__ __launch_bounds__(kDiagThreads) void diag_scan_kernel(
 // with al_0 = 1, al_u = a_{t+1} and initial state dh_last.  The gradients
 // follow per step: db_t = g_t, da_t = g_t h_{t-1} (h_{-1} = h0), and
 // dh0 = a_0 g_0.  Same work split as the forward kernel, with u in place of t.
-template <typename T>
+template <typename T, int CPL>
 __global__ __launch_bounds__(kDiagThreads) void diag_scan_bwd_kernel(
     const T* __restrict__ a, const T* __restrict__ h, const float* __restrict__ h0,
     const T* __restrict__ dh, const float* __restrict__ dh_last, T* __restrict__ da,
     T* __restrict__ db, float* __restrict__ dh0, int64_t L, int64_t D) {
-  __shared__ float aggA[kDiagSegs][kDiagCT];
-  __shared__ float aggB[kDiagSegs][kDiagCT];
-  __shared__ float carry_in[kDiagSegs][kDiagCT];
-  __shared__ float tile_carry[kDiagCT];
+  constexpr int CT = kDiagCT * CPL;   // channels per workgroup
+  __shared__ float aggA[kDiagSegs][CT];
+  __shared__ float aggB[kDiagSegs][CT];
+  __shared__ float carry_in[kDiagSegs][CT];
+  __shared__ float tile_carry[CT];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  const int ch = lane & (kDiagCT - 1);
+  const int ch = (lane & (kDiagCT - 1)) * CPL;
   const int seg = wave * 4 + (lane >> 4);
-  const int64_t ntile = (D + kDiagCT - 1) / kDiagCT;
+  const int64_t ntile = (D + CT - 1) / CT;
   const int64_t bi = blockIdx.x / ntile;
-  const int64_t d0 = (blockIdx.x % ntile) * kDiagCT;
+  const int64_t d0 = (blockIdx.x % ntile) * CT;
   const int64_t d = d0 + ch;
   const bool dok = d < D;
 
-  if (tid < kDiagCT) {
-    const int64_t dd = d0 + tid;
-    tile_carry[tid] = (dh_last != nullptr && dd < D) ? dh_last[bi * D + dd] : 0.f;
+  for (int c = tid; c < CT; c += kDiagThreads) {
+    const int64_t dd = d0 + c;
+    tile_carry[c] = (dh_last != nullptr && dd < D) ? dh_last[bi * D + dd] : 0.f;
   }
   __syncthreads();
 
@@ -148,31 +219,43 @@ __global__ __launch_bounds__(kDiagThreads) void diag_scan_bwd_kernel(
     const int64_t us = u0 + static_cast<int64_t>(seg) * kDiagSeg;
     // steps u = us + i, i.e. tokens t = L - 1 - us - i (descending)
     const int nok = dok ? static_cast<int>(L - us < kDiagSeg ? (L - us > 0 ? L - us : 0) : kDiagSeg) : 0;
-    float av[kDiagSeg], bv[kDiagSeg];
-    {
-      const int64_t t_first = L - 1 - us;
-#pragma unroll
-      for (int i = 0; i < kDiagSeg; ++i) {
-        const int64_t t = t_first - i;
-        const bool ok = i < nok;
-        av[i] = (ok && t + 1 < L) ? Io<T>::load(a + (row + t + 1) * D + d) : 1.f;
-        bv[i] = ok ? Io<T>::load(dh + (row + t) * D + d) : 0.f;
-      }
-    }
-    float P = 1.f, Gs = 0.f;
+    const int64_t t_first = L - 1 - us;
+    float av[kDiagSeg][CPL], bv[kDiagSeg][CPL];
 #pragma unroll
     for (int i = 0; i < kDiagSeg; ++i) {
-      Gs = fmaf(av[i], Gs, bv[i]);
-      P *= av[i];
-      av[i] = P;
-      bv[i] = Gs;
+      const int64_t t = t_first - i;
+      const bool ok = i < nok;
+      if (ok && t + 1 < L) {
+        vload<T, CPL>(a + (row + t + 1) * D + d, av[i]);
+      } else {
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) av[i][k] = 1.f;
+      }
+      if (ok) {
+        vload<T, CPL>(dh + (row + t) * D + d, bv[i]);
+      } else {
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) bv[i][k] = 0.f;
+      }
     }
-    aggA[seg][ch] = P;
-    aggB[seg][ch] = Gs;
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) {
+      float P = 1.f, Gs = 0.f;
+#pragma unroll
+      for (int i = 0; i < kDiagSeg; ++i) {
+        Gs = fmaf(av[i][k], Gs, bv[i][k]);
+        P *= av[i][k];
+        av[i][k] = P;
+        bv[i][k] = Gs;
+      }
+      aggA[seg][ch + k] = P;
+      aggB[seg][ch + k] = Gs;
+    }
     __syncthreads();
 
-    if (wave < kDiagCT) {
-      const int c = wave;
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) {
+      const int c = wave + kDiagCT * k;
       float pa = aggA[lane][c], pb = aggB[lane][c];
       const float tc = tile_carry[c];
       wave_incl_pair_scan(pa, pb);
@@ -182,39 +265,67 @@ __global__ __launch_bounds__(kDiagThreads) void diag_scan_bwd_kernel(
     }
     __syncthreads();
 
-    const float cin = carry_in[seg][ch];
-    {
-      const int64_t t_first = L - 1 - us;
+    float cin[CPL];
 #pragma unroll
-      for (int i = 0; i < kDiagSeg; ++i) {
-        if (i < nok) {
-          const int64_t t = t_first - i;
-          const float gt = fmaf(av[i], cin, bv[i]);
-          const float hp = t > 0 ? Io<T>::load(h + (row + t - 1) * D + d)
-                                 : (h0 != nullptr ? h0[bi * D + d] : 0.f);
-          Io<T>::store(db + (row + t) * D + d, gt);
-          Io<T>::store(da + (row + t) * D + d, gt * hp);
+    for (int k = 0; k < CPL; ++k) cin[k] = carry_in[seg][ch + k];
+    // element offset of token t_first, passed through an empty asm so that the
+    // per-step addresses are formed here rather than kept live from the loads
+    // before the barriers (which spilled them at CPL = 4)
+    int64_t offt = (row + t_first) * D + d;
+    asm volatile("" : "+v"(offt));
+#pragma unroll
+    for (int i = 0; i < kDiagSeg; ++i) {
+      if (i < nok) {
+        const int64_t t = t_first - i;
+        const int64_t off = offt - i * D;
+        float gt[CPL], hp[CPL], dv[CPL];
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) gt[k] = fmaf(av[i][k], cin[k], bv[i][k]);
+        if (t > 0) {
+          vload<T, CPL>(h + off - D, hp);
+        } else {
+#pragma unroll
+          for (int k = 0; k < CPL; ++k) hp[k] = h0 != nullptr ? h0[bi * D + d + k] : 0.f;
         }
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) dv[k] = gt[k] * hp[k];
+        vstore<T, CPL>(db + off, gt);
+        vstore<T, CPL>(da + off, dv);
       }
     }
   }
   __syncthreads();
-  if (dh0 != nullptr && tid < kDiagCT) {
-    const int64_t dd = d0 + tid;
-    if (dd < D) dh0[bi * D + dd] = L > 0 ? Io<T>::load(a + row * D + dd) * tile_carry[tid] : tile_carry[tid];
+  if (dh0 != nullptr) {
+    for (int c = tid; c < CT; c += kDiagThreads) {
+      const int64_t dd = d0 + c;
+      if (dd < D) dh0[bi * D + dd] = L > 0 ? Io<T>::load(a + row * D + dd) * tile_carry[c] : tile_carry[c];
+    }
   }
+}
+
+template <typename T, int CPL>
+static hipError_t launch_diag_bwd_cpl(const void* a, const void* h, const float* h0,
+                                      const void* dh, const float* dh_last, void* da, void* db,
+                                      float* dh0, int64_t B, int64_t L, int64_t D,
+                                      hipStream_t stream) {
+  const int64_t ct = kDiagCT * CPL;
+  dim3 grid(static_cast<unsigned>(B * ((D + ct - 1) / ct)));
+  hipLaunchKernelGGL((diag_scan_bwd_kernel<T, CPL>), grid, dim3(kDiagThreads), 0, stream,
+                     static_cast<const T*>(a), static_cast<const T*>(h), h0,
+                     static_cast<const T*>(dh), dh_last, static_cast<T*>(da),
+                     static_cast<T*>(db), dh0, L, D);
+  return hipGetLastError();
 }
 
 template <typename T>
 hipError_t launch_diag_scan_bwd(const void* a, const void* h, const float* h0, const void* dh,
                                 const float* dh_last, void* da, void* db, float* dh0, int64_t B,
                                 int64_t L, int64_t D, hipStream_t stream) {
-  dim3 grid(static_cast<unsigned>(B * ((D + kDiagCT - 1) / kDiagCT)));
-  hipLaunchKernelGGL(diag_scan_bwd_kernel<T>, grid, dim3(kDiagThreads), 0, stream,
-                     static_cast<const T*>(a), static_cast<const T*>(h), h0,
-                     static_cast<const T*>(dh), dh_last, static_cast<T*>(da),
-                     static_cast<T*>(db), dh0, L, D);
-  return hipGetLastError();
+  if (D % 4 == 0 && B * (D / 64) >= 512)
+    return launch_diag_bwd_cpl<T, 4>(a, h, h0, dh, dh_last, da, db, dh0, B, L, D, stream);
+  if (D % 2 == 0 && B * (D / 32) >= 512)
+    return launch_diag_bwd_cpl<T, 2>(a, h, h0, dh, dh_last, da, db, dh0, B, L, D, stream);
+  return launch_diag_bwd_cpl<T, 1>(a, h, h0, dh, dh_last, da, db, dh0, B, L, D, stream);
 }
 
 template hipError_t launch_diag_scan_bwd<float>(const void*, const void*, const float*, const void*,
@@ -224,15 +335,29 @@ template hipError_t launch_diag_scan_bwd<uint16_t>(const void*, const void*, con
                                                    const void*, const float*, void*, void*,
                                                    float*, int64_t, int64_t, int64_t, hipStream_t);
 
+template <typename T, int CPL>
+static hipError_t launch_diag_cpl(const void* a, const void* b, const float* h0, void* h,
+                                  float* h_last, int64_t B, int64_t L, int64_t D,
+                                  hipStream_t stream) {
+  const int64_t ct = kDiagCT * CPL;
+  dim3 grid(static_cast<unsigned>(B * ((D + ct - 1) / ct)));
+  hipLaunchKernelGGL((diag_scan_kernel<T, CPL>), grid, dim3(kDiagThreads), 0, stream,
+                     static_cast<const T*>(a), static_cast<const T*>(b), h0,
+                     static_cast<T*>(h), h_last, L, D);
+  return hipGetLastError();
+}
+
+// Wider channel tiles once they still give at least two workgroups per CU
+// (512 on 256 CUs); the vector accesses need D to be a multiple of the width.
 template <typename T>
 hipError_t launch_diag_scan(const void* a, const void* b, const float* h0, void* h,
                             float* h_last, int64_t B, int64_t L, int64_t D,
                             hipStream_t stream) {
-  dim3 grid(static_cast<unsigned>(B * ((D + kDiagCT - 1) / kDiagCT)));
-  hipLaunchKernelGGL(diag_scan_kernel<T>, grid, dim3(kDiagThreads), 0, stream,
-                     static_cast<const T*>(a), static_cast<const T*>(b), h0,
-                     static_cast<T*>(h), h_last, L, D);
-  return hipGetLastError();
+  if (D % 4 == 0 && B * (D / 64) >= 512)
+    return launch_diag_cpl<T, 4>(a, b, h0, h, h_last, B, L, D, stream);
+  if (D % 2 == 0 && B * (D / 32) >= 512)
+    return launch_diag_cpl<T, 2>(a, b, h0, h, h_last, B, L, D, stream);
+  return launch_diag_cpl<T, 1>(a, b, h0, h, h_last, B, L, D, stream);
 }
 
 template hipError_t launch_diag_scan<float>(const void*, const void*, const float*, void*, float*,

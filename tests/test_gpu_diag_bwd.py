@@ -13,7 +13,9 @@ pytestmark = pytest.mark.gpu
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 @pytest.mark.parametrize("B,L,D", [(1, 1024, 256), (2, 1500, 37), (1, 1, 5), (3, 513, 16),
-                                   (1, 4097, 20)])
+                                   (1, 4097, 20),
+                                   # wide channel tiles: 4 and 2 channels per lane
+                                   (64, 600, 512), (33, 130, 514)])
 def test_diag_bwd_parity(io, B, L, D):
     print(f"diag bwd io={io} B={B} L={L} D={D}", flush=True)
     g = lrgen.make(1, io=io, B=B, L=L, D=D, grads=True)

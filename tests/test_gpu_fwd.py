@@ -23,7 +23,9 @@ def _sync():
 # ------------------------------------------------------------------ diag
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 @pytest.mark.parametrize("B,L,D", [(1, 1, 1), (2, 65, 17), (1, 513, 5), (3, 1000, 33),
-                                   (1, 2049, 16), (1, 1024, 256)])
+                                   (1, 2049, 16), (1, 1024, 256),
+                                   # wide channel tiles: 4 and 2 channels per lane
+                                   (64, 600, 512), (33, 130, 514), (40, 70, 1000)])
 def test_diag_parity(io, B, L, D):
     print(f"diag io={io} B={B} L={L} D={D}", flush=True)
     g = lrgen.make(1, io=io, B=B, L=L, D=D)
