@@ -256,6 +256,10 @@ def measure_scaled(warmup, iters):
     nb = 2 * B * L * D * 4 + 2 * B * L * (D // 2) * 4
     out["rotlru"] = dict(shape=f"B{B}_L{L}_D{D}_fp32", us=t * 1e6, alg_bytes=nb,
                          GBs=nb / t / 1e9, hbm_frac=nb / t / 1e9 / HBM_PEAK_GBS)
+    t, _ = time_launches(lambda s: lr.lr_rotlru_scan_bwd(r, th, h, b), [None], warmup, iters)
+    nb = 3 * B * L * D * 4 + 4 * B * L * (D // 2) * 4   # read r, theta, h, dh; write dr, dtheta, du
+    out["rotlru_bwd"] = dict(shape=f"B{B}_L{L}_D{D}_fp32", us=t * 1e6, alg_bytes=nb,
+                             GBs=nb / t / 1e9, hbm_frac=nb / t / 1e9 / HBM_PEAK_GBS)
     return out
 
 def measure_diag_bwd(warmup, iters):

@@ -144,6 +144,173 @@ __global__ __launch_bounds__(kRotThreads) void rotlru_scan_kernel(
   }
 }
 
+// Wide variant for problems that still fill the chip with 32 pairs per
+// workgroup: PPL = 2 adjacent pairs per lane, so the u and h accesses are 16
+// bytes (8 for bf16) and r, theta 8 bytes.  Segments hold 4 steps (tiles of
+// 256), so a lane keeps as many running products and states as the narrow
+// kernel above (which stays faster for small, latency-bound problems).
+template <typename T, int N>
+__device__ __forceinline__ void rvload(const T* p, float (&v)[N]) {
+  if constexpr (N == 1) {
+    v[0] = Io<T>::load(p);
+  } else if constexpr (sizeof(T) == 4) {
+    if constexpr (N == 2) {
+      const float2 x = *reinterpret_cast<const float2*>(p);
+      v[0] = x.x; v[1] = x.y;
+    } else {
+      const float4 x = *reinterpret_cast<const float4*>(p);
+      v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+    }
+  } else {
+    if constexpr (N == 2) {
+      const uint32_t x = *reinterpret_cast<const uint32_t*>(p);
+      v[0] = bf2f(static_cast<uint16_t>(x)); v[1] = bf2f(static_cast<uint16_t>(x >> 16));
+    } else {
+      const uint2 x = *reinterpret_cast<const uint2*>(p);
+      v[0] = bf2f(static_cast<uint16_t>(x.x)); v[1] = bf2f(static_cast<uint16_t>(x.x >> 16));
+      v[2] = bf2f(static_cast<uint16_t>(x.y)); v[3] = bf2f(static_cast<uint16_t>(x.y >> 16));
+    }
+  }
+}
+template <typename T, int N>
+__device__ __forceinline__ void rvstore(T* p, const float (&v)[N]) {
+  if constexpr (sizeof(T) == 4) {
+    if constexpr (N == 2) *reinterpret_cast<float2*>(p) = float2{v[0], v[1]};
+    else *reinterpret_cast<float4*>(p) = float4{v[0], v[1], v[2], v[3]};
+  } else {
+    if constexpr (N == 2) {
+      *reinterpret_cast<uint32_t*>(p) = f2bf(v[0]) | (static_cast<uint32_t>(f2bf(v[1])) << 16);
+    } else {
+      *reinterpret_cast<uint2*>(p) =
+          uint2{f2bf(v[0]) | (static_cast<uint32_t>(f2bf(v[1])) << 16),
+                f2bf(v[2]) | (static_cast<uint32_t>(f2bf(v[3])) << 16)};
+    }
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kRotThreads) void rotlru_scan_wide_kernel(
+    const T* __restrict__ r, const T* __restrict__ theta, const T* __restrict__ u,
+    const float* __restrict__ h0, T* __restrict__ h, float* __restrict__ h_last, int64_t L,
+    int64_t Dp) {
+  constexpr int PPL = 2;             // pairs per lane
+  constexpr int CP = kRotCP * PPL;   // pairs per workgroup
+  constexpr int SEG = kRotSeg / PPL;  // steps per lane segment (same registers)
+  constexpr int TILE = kRotSegs * SEG;
+  __shared__ cplx aggA[kRotSegs][CP];
+  __shared__ cplx aggB[kRotSegs][CP];
+  __shared__ cplx carry_in[kRotSegs][CP];
+  __shared__ cplx tile_carry[CP];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int pr = (lane & (kRotCP - 1)) * PPL;   // first of this lane's pairs
+  const int seg = wave * 4 + (lane >> 4);
+  const int64_t ntile = (Dp + CP - 1) / CP;
+  const int64_t bi = blockIdx.x / ntile;
+  const int64_t p0 = (blockIdx.x % ntile) * CP;
+  const int64_t p = p0 + pr;
+  const bool pok = p < Dp;   // Dp % PPL == 0: all PPL pairs exist
+  const int64_t D = 2 * Dp;
+
+  for (int c = tid; c < CP; c += kRotThreads) {
+    const int64_t pp = p0 + c;
+    tile_carry[c] = (h0 != nullptr && pp < Dp) ? cplx{h0[bi * D + 2 * pp], h0[bi * D + 2 * pp + 1]}
+                                               : cplx{0.f, 0.f};
+  }
+  __syncthreads();
+
+  for (int64_t t0 = 0; t0 < L; t0 += TILE) {
+    const int64_t ts = t0 + static_cast<int64_t>(seg) * SEG;
+    const int nok = pok ? static_cast<int>(L - ts < SEG ? (L - ts > 0 ? L - ts : 0) : SEG) : 0;
+    cplx Pv[SEG][PPL], Hv[SEG][PPL];
+    {
+      cplx P[PPL], Hs[PPL];
+#pragma unroll
+      for (int k = 0; k < PPL; ++k) { P[k] = {1.f, 0.f}; Hs[k] = {0.f, 0.f}; }
+      // loads are unconditional, from a clamped token and pair (always in
+      // bounds, L > 0 here), and steps past the end take the identity: no
+      // branch around a load, so all of a segment's loads are in flight at once
+      const int64_t pc = pok ? p : Dp - PPL;
+#pragma unroll
+      for (int i = 0; i < SEG; ++i) {
+        float rv[PPL], tv[PPL], uv[2 * PPL];
+        {
+          const int64_t tc = ts + i < L ? ts + i : L - 1;
+          const int64_t rowp = (bi * L + tc) * Dp + pc;
+          rvload<T, PPL>(r + rowp, rv);
+          rvload<T, PPL>(theta + rowp, tv);
+          rvload<T, 2 * PPL>(u + 2 * rowp, uv);
+        }
+        const bool ok = i < nok;
+#pragma unroll
+        for (int k = 0; k < PPL; ++k) {
+          float sn, cs;
+          sincosf(tv[k], &sn, &cs);
+          const cplx a = ok ? cplx{rv[k] * cs, rv[k] * sn} : cplx{1.f, 0.f};
+          const cplx w = ok ? cplx{uv[2 * k], uv[2 * k + 1]} : cplx{0.f, 0.f};
+          Hs[k] = cfma(a, Hs[k], w);
+          P[k] = cmul(a, P[k]);
+          Pv[i][k] = P[k];
+          Hv[i][k] = Hs[k];
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < PPL; ++k) {
+        aggA[seg][pr + k] = P[k];
+        aggB[seg][pr + k] = Hs[k];
+      }
+    }
+    __syncthreads();
+
+    // one wave per pair (PPL pairs per wave): lane = segment index
+#pragma unroll
+    for (int k = 0; k < PPL; ++k) {
+      const int c = wave + kRotCP * k;
+      cplx pa = aggA[lane][c], pb = aggB[lane][c];
+      const cplx tc = tile_carry[c];
+      cwave_incl_pair_scan(pa, pb);
+      // exclusive prefix: the previous lane's pair (identity at lane 0)
+      const cplx ea = {wave_shr1(pa.re, 1.f), wave_shr1(pa.im, 0.f)};
+      const cplx eb = {wave_shr1(pb.re, 0.f), wave_shr1(pb.im, 0.f)};
+      carry_in[lane][c] = cfma(ea, tc, eb);
+      if (lane == 63) tile_carry[c] = cfma(pa, tc, pb);
+    }
+    __syncthreads();
+
+    cplx cin[PPL];
+#pragma unroll
+    for (int k = 0; k < PPL; ++k) cin[k] = carry_in[seg][pr + k];
+    // element offset of this lane's first output, formed after the barrier
+    // so that per-step addresses are not kept live across it
+    int64_t offu = (bi * L + ts) * D + 2 * p;
+    asm volatile("" : "+v"(offu));
+#pragma unroll
+    for (int i = 0; i < SEG; ++i) {
+      if (i < nok) {
+        float o[2 * PPL];
+#pragma unroll
+        for (int k = 0; k < PPL; ++k) {
+          const cplx z = cfma(Pv[i][k], cin[k], Hv[i][k]);
+          o[2 * k] = z.re;
+          o[2 * k + 1] = z.im;
+        }
+        rvstore<T, 2 * PPL>(h + offu + i * D, o);
+      }
+    }
+  }
+  __syncthreads();
+  if (h_last != nullptr) {
+    for (int c = tid; c < CP; c += kRotThreads) {
+      const int64_t pp = p0 + c;
+      if (pp < Dp) {
+        h_last[bi * D + 2 * pp] = tile_carry[c].re;
+        h_last[bi * D + 2 * pp + 1] = tile_carry[c].im;
+      }
+    }
+  }
+}
+
 // Backward of the rotational LRU for the loss sum_t <dh_t, h_t> + <dh_last, h_last>
 // (real inner products over the interleaved pairs).  In complex form, with
 // G_t the gradient of the loss with respect to z_t (real part + i imaginary
@@ -321,10 +488,17 @@ hipError_t launch_rotlru_scan(const void* r, const void* theta, const void* u, c
                               void* h, float* h_last, int64_t B, int64_t L, int64_t D,
                               hipStream_t stream) {
   const int64_t Dp = D / 2;
-  dim3 grid(static_cast<unsigned>(B * ((Dp + kRotCP - 1) / kRotCP)));
-  hipLaunchKernelGGL(rotlru_scan_kernel<T>, grid, dim3(kRotThreads), 0, stream,
-                     static_cast<const T*>(r), static_cast<const T*>(theta),
-                     static_cast<const T*>(u), h0, static_cast<T*>(h), h_last, L, Dp);
+  if (Dp % 2 == 0 && B * (Dp / 32) >= 512) {
+    dim3 grid(static_cast<unsigned>(B * ((Dp + 2 * kRotCP - 1) / (2 * kRotCP))));
+    hipLaunchKernelGGL(rotlru_scan_wide_kernel<T>, grid, dim3(kRotThreads), 0, stream,
+                       static_cast<const T*>(r), static_cast<const T*>(theta),
+                       static_cast<const T*>(u), h0, static_cast<T*>(h), h_last, L, Dp);
+  } else {
+    dim3 grid(static_cast<unsigned>(B * ((Dp + kRotCP - 1) / kRotCP)));
+    hipLaunchKernelGGL(rotlru_scan_kernel<T>, grid, dim3(kRotThreads), 0, stream,
+                       static_cast<const T*>(r), static_cast<const T*>(theta),
+                       static_cast<const T*>(u), h0, static_cast<T*>(h), h_last, L, Dp);
+  }
   return hipGetLastError();
 }
 
