@@ -459,12 +459,182 @@ __global__ __launch_bounds__(kRotThreads) void rotlru_scan_bwd_kernel(
   }
 }
 
+// Wide backward for the problems the wide forward serves: 2 adjacent pairs
+// per lane (vector accesses), 4 reversed steps per segment.
+template <typename T>
+__global__ __launch_bounds__(kRotThreads) void rotlru_scan_bwd_wide_kernel(
+    const T* __restrict__ r, const T* __restrict__ theta, const T* __restrict__ h,
+    const float* __restrict__ h0, const T* __restrict__ dh, const float* __restrict__ dh_last,
+    T* __restrict__ dr, T* __restrict__ dtheta, T* __restrict__ du, float* __restrict__ dh0,
+    int64_t L, int64_t Dp) {
+  constexpr int PPL = 2;
+  constexpr int CP = kRotCP * PPL;
+  constexpr int SEG = kRotSeg / PPL;
+  constexpr int TILE = kRotSegs * SEG;
+  __shared__ cplx aggA[kRotSegs][CP];
+  __shared__ cplx aggB[kRotSegs][CP];
+  __shared__ cplx carry_in[kRotSegs][CP];
+  __shared__ cplx tile_carry[CP];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int pr = (lane & (kRotCP - 1)) * PPL;
+  const int seg = wave * 4 + (lane >> 4);
+  const int64_t ntile = (Dp + CP - 1) / CP;
+  const int64_t bi = blockIdx.x / ntile;
+  const int64_t p0 = (blockIdx.x % ntile) * CP;
+  const int64_t p = p0 + pr;
+  const bool pok = p < Dp;   // Dp % 2 == 0: both pairs exist
+  const int64_t D = 2 * Dp;
+
+  for (int c = tid; c < CP; c += kRotThreads) {
+    const int64_t pp = p0 + c;
+    tile_carry[c] = (dh_last != nullptr && pp < Dp)
+                        ? cplx{dh_last[bi * D + 2 * pp], dh_last[bi * D + 2 * pp + 1]}
+                        : cplx{0.f, 0.f};
+  }
+  __syncthreads();
+
+  const int64_t row = bi * L;
+  for (int64_t u0 = 0; u0 < L; u0 += TILE) {
+    const int64_t us = u0 + static_cast<int64_t>(seg) * SEG;
+    const int64_t t_first = L - 1 - us;
+    const int nok = pok ? static_cast<int>(L - us < SEG ? (L - us > 0 ? L - us : 0) : SEG) : 0;
+    // as the narrow kernel: entry j is token t_first + 1 - j
+    cplx ev[SEG + 1][PPL];
+    float rv[SEG + 1][PPL];
+#pragma unroll
+    for (int j = 0; j <= SEG; ++j) {
+      const int64_t tj = t_first + 1 - j;
+      const bool ok = j == 0 ? (nok > 0 && tj < L) : (j - 1 < nok);
+#pragma unroll
+      for (int k = 0; k < PPL; ++k) { ev[j][k] = {1.f, 0.f}; rv[j][k] = 1.f; }
+      if (ok) {
+        const int64_t rowp = (row + tj) * Dp + p;
+        float tv[PPL];
+        rvload<T, PPL>(r + rowp, rv[j]);
+        rvload<T, PPL>(theta + rowp, tv);
+#pragma unroll
+        for (int k = 0; k < PPL; ++k) {
+          float sn, cs;
+          sincosf(tv[k], &sn, &cs);
+          ev[j][k] = {cs, sn};
+        }
+      }
+    }
+    cplx Pv[SEG][PPL], Hv[SEG][PPL];
+    {
+      cplx P[PPL], Gs[PPL];
+#pragma unroll
+      for (int k = 0; k < PPL; ++k) { P[k] = {1.f, 0.f}; Gs[k] = {0.f, 0.f}; }
+#pragma unroll
+      for (int i = 0; i < SEG; ++i) {
+        float wv[2 * PPL];
+        if (i < nok) {
+          rvload<T, 2 * PPL>(dh + (row + t_first - i) * D + 2 * p, wv);
+        }
+#pragma unroll
+        for (int k = 0; k < PPL; ++k) {
+          cplx a = {1.f, 0.f}, w = {0.f, 0.f};
+          if (i < nok) {
+            a = {rv[i][k] * ev[i][k].re, -rv[i][k] * ev[i][k].im};
+            w = {wv[2 * k], wv[2 * k + 1]};
+          }
+          Gs[k] = cfma(a, Gs[k], w);
+          P[k] = cmul(a, P[k]);
+          Pv[i][k] = P[k];
+          Hv[i][k] = Gs[k];
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < PPL; ++k) {
+        aggA[seg][pr + k] = P[k];
+        aggB[seg][pr + k] = Gs[k];
+      }
+    }
+    __syncthreads();
+
+#pragma unroll
+    for (int k = 0; k < PPL; ++k) {
+      const int c = wave + kRotCP * k;
+      cplx pa = aggA[lane][c], pb = aggB[lane][c];
+      const cplx tc = tile_carry[c];
+      cwave_incl_pair_scan(pa, pb);
+      const cplx ea = {wave_shr1(pa.re, 1.f), wave_shr1(pa.im, 0.f)};
+      const cplx eb = {wave_shr1(pb.re, 0.f), wave_shr1(pb.im, 0.f)};
+      carry_in[lane][c] = cfma(ea, tc, eb);
+      if (lane == 63) tile_carry[c] = cfma(pa, tc, pb);
+    }
+    __syncthreads();
+
+    cplx cin[PPL];
+#pragma unroll
+    for (int k = 0; k < PPL; ++k) cin[k] = carry_in[seg][pr + k];
+    int64_t offu = (row + t_first) * D + 2 * p, offp = (row + t_first) * Dp + p;
+    asm volatile("" : "+v"(offu), "+v"(offp));
+#pragma unroll
+    for (int i = 0; i < SEG; ++i) {
+      if (i < nok) {
+        const int64_t t = t_first - i;
+        const int64_t rowu = offu - i * D;
+        const int64_t rowp = offp - i * Dp;
+        float zv[2 * PPL];
+        if (t > 0) {
+          rvload<T, 2 * PPL>(h + rowu - D, zv);
+        } else {
+#pragma unroll
+          for (int k = 0; k < 2 * PPL; ++k) zv[k] = h0 != nullptr ? h0[bi * D + 2 * p + k] : 0.f;
+        }
+        float gv[2 * PPL], qr[PPL], qi[PPL];
+#pragma unroll
+        for (int k = 0; k < PPL; ++k) {
+          const cplx g = cfma(Pv[i][k], cin[k], Hv[i][k]);
+          const cplx ez = cmul(ev[i + 1][k], cplx{zv[2 * k], zv[2 * k + 1]});
+          qr[k] = fmaf(g.re, ez.re, g.im * ez.im);
+          qi[k] = fmaf(g.im, ez.re, -g.re * ez.im) * rv[i + 1][k];
+          gv[2 * k] = g.re;
+          gv[2 * k + 1] = g.im;
+        }
+        rvstore<T, PPL>(dr + rowp, qr);
+        rvstore<T, PPL>(dtheta + rowp, qi);
+        rvstore<T, 2 * PPL>(du + rowu, gv);
+      }
+    }
+  }
+  __syncthreads();
+  if (dh0 != nullptr) {
+    for (int c = tid; c < CP; c += kRotThreads) {
+      const int64_t pp = p0 + c;
+      if (pp < Dp) {
+        cplx g = tile_carry[c];
+        if (L > 0) {
+          const float r0 = Io<T>::load(r + row * Dp + pp);
+          float sn, cs;
+          sincosf(Io<T>::load(theta + row * Dp + pp), &sn, &cs);
+          g = cmul({r0 * cs, -r0 * sn}, g);
+        }
+        dh0[bi * D + 2 * pp] = g.re;
+        dh0[bi * D + 2 * pp + 1] = g.im;
+      }
+    }
+  }
+}
+
 template <typename T>
 hipError_t launch_rotlru_scan_bwd(const void* r, const void* theta, const void* h,
                                   const float* h0, const void* dh, const float* dh_last, void* dr,
                                   void* dtheta, void* du, float* dh0, int64_t B, int64_t L,
                                   int64_t D, hipStream_t stream) {
   const int64_t Dp = D / 2;
+  if (Dp % 2 == 0 && B * (Dp / 32) >= 512) {
+    dim3 grid(static_cast<unsigned>(B * ((Dp + 2 * kRotCP - 1) / (2 * kRotCP))));
+    hipLaunchKernelGGL(rotlru_scan_bwd_wide_kernel<T>, grid, dim3(kRotThreads), 0, stream,
+                       static_cast<const T*>(r), static_cast<const T*>(theta),
+                       static_cast<const T*>(h), h0, static_cast<const T*>(dh), dh_last,
+                       static_cast<T*>(dr), static_cast<T*>(dtheta), static_cast<T*>(du), dh0, L,
+                       Dp);
+    return hipGetLastError();
+  }
   dim3 grid(static_cast<unsigned>(B * ((Dp + kRotCP - 1) / kRotCP)));
   hipLaunchKernelGGL(rotlru_scan_bwd_kernel<T>, grid, dim3(kRotThreads), 0, stream,
                      static_cast<const T*>(r), static_cast<const T*>(theta),

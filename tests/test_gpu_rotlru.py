@@ -44,7 +44,9 @@ def test_rotlru_empty_and_determinism():
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 @pytest.mark.parametrize("B,L,D", [(1, 1024, 256), (2, 1500, 38), (1, 1, 2), (3, 513, 64),
-                                   (1, 4097, 40), (2, 512, 34)])
+                                   (1, 4097, 40), (2, 512, 34),
+                                   # two pairs per lane, 256-step tiles
+                                   (64, 300, 512), (40, 70, 836)])
 def test_rotlru_bwd_parity(io, B, L, D):
     print(f"rotlru bwd io={io} B={B} L={L} D={D}", flush=True)
     g = lrgen.make(6, io=io, B=B, L=L, D=D, grads=True)
