@@ -52,6 +52,19 @@ def test_diag_empty_and_determinism():
     assert torch.equal(r1, r2)
 
 
+@pytest.mark.parametrize("D", [512, 514])
+def test_diag_empty_sequence_wide_tiles(D):
+    """L = 0 through the 4- and 2-channel-per-lane kernels (B * D large enough
+    to select them): h_last is h0 for every channel, forward and backward."""
+    B = 64
+    h0 = torch.randn(B, D, device="cuda")
+    z = torch.empty(B, 0, D, device="cuda")
+    _, hl = lr.lr_diag_scan(z, z, h0=h0, want_last=True)
+    _, _, dh0 = lr.lr_diag_scan_bwd(z, z, z, dh_last=h0, want_dh0=True)
+    _sync()
+    assert torch.equal(hl, h0) and torch.equal(dh0, h0)
+
+
 # ------------------------------------------------------------- selective
 def _sel_case(io, disc, B, L, D, N, zero_A=False, seed_cfg=2):
     g = lrgen.make(seed_cfg, io=io, B=B, L=L, D=D, N=N, disc=disc)

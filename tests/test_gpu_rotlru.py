@@ -67,9 +67,11 @@ def test_rotlru_bwd_parity(io, B, L, D):
     check("dh0", dh0, rdh0, TOL["f32"] if io == "f32" else TOL["bf16"])
 
 
-def test_rotlru_bwd_no_state_and_determinism():
+@pytest.mark.parametrize("B,L,D", [(2, 700, 20), (64, 100, 512)])
+def test_rotlru_bwd_no_state_and_determinism(B, L, D):
     # no h0 / dh_last: z_{-1} = 0, so dr and dtheta of token 0 vanish
-    g = lrgen.make(6, B=2, L=700, D=20, grads=True)
+    print(f"rotlru bwd no state B={B} L={L} D={D}", flush=True)
+    g = lrgen.make(6, B=B, L=L, D=D, grads=True)
     r, th, dh = dev(g.t("r")), dev(g.t("theta")), dev(g.t("dh"))
     h, _ = lr.lr_rotlru_scan(r, th, dev(g.t("u")))
     r1 = lr.lr_rotlru_scan_bwd(r, th, h, dh, want_dh0=True)
@@ -81,11 +83,11 @@ def test_rotlru_bwd_no_state_and_determinism():
     ref = oracle.rotlru_scan_bwd(g["r"], g["theta"], h.cpu().numpy(), g["dh"])
     for name, x, e in zip(("dr", "dtheta", "du", "dh0"), r1, ref):
         check(name, x, e, TOL["f32"])
-    # empty sequence: dh0 = dh_last
-    dhl = torch.randn(2, 6, device="cuda")
-    z = torch.empty(2, 0, 3, device="cuda")
-    _, _, _, dh0 = lr.lr_rotlru_scan_bwd(z, z, torch.empty(2, 0, 6, device="cuda"),
-                                         torch.empty(2, 0, 6, device="cuda"), dh_last=dhl,
-                                         want_dh0=True)
+    # empty sequence: dh0 = dh_last, h_last = h0
+    dhl = torch.randn(B, D, device="cuda")
+    z = torch.empty(B, 0, D // 2, device="cuda")
+    zz = torch.empty(B, 0, D, device="cuda")
+    _, _, _, dh0 = lr.lr_rotlru_scan_bwd(z, z, zz, zz, dh_last=dhl, want_dh0=True)
+    _, hl = lr.lr_rotlru_scan(z, z, zz, h0=dhl, want_last=True)
     torch.cuda.synchronize()
-    assert torch.equal(dh0, dhl)
+    assert torch.equal(dh0, dhl) and torch.equal(hl, dhl)
