@@ -218,3 +218,11 @@ def state_normal(shape, cfg_id: int, tensor_id: int = 20, seed: int = SEED,
     """A seeded float32 tensor for optional fp32 state inputs (h0, S0,
     dh_last) used by parity cases."""
     return _Stream(seed, cfg_id, tensor_id).normal(shape, 0.0, std)
+
+
+def softplus_normal(shape, cfg_id: int, mean: float, std: float = 1.0, tensor_id: int = 30,
+                    seed: int = SEED, io: str = "f32") -> np.ndarray:
+    """A seeded step tensor softplus(N(mean, std)) rounded to ``io``, for
+    parity cases whose steps are far from the workloads' (e.g. mean = -9:
+    steps near 1e-4)."""
+    return _io_round(_Stream(seed, cfg_id, tensor_id).softplus_normal(shape, mean, std), io)

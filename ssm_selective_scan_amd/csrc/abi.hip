@@ -56,7 +56,8 @@ bool ssd_bwd_supported(int64_t P, int64_t N, int64_t seg);
 hipError_t launch_ssd_bwd_empty(float* dA, float* dD, float* dh0, const float* dh_last, int64_t H,
                                 int64_t nstate, hipStream_t stream);
 hipError_t launch_ssd_bwd(int disc, const void* x, const void* dt, const float* A, const void* Bm,
-                          const void* Cm, const float* Dskip, const float* ckpt, const void* dy,
+                          const void* Cm, const float* Dskip, const float* h0, const float* ckpt,
+                          const void* dy,
                           const float* dh_last, void* dx, void* ddt, float* dA, void* dBm,
                           void* dCm, float* dD, float* dh0, void* ws, int64_t B, int64_t L,
                           int64_t H, int64_t P, int64_t G, int64_t N, int64_t seg,
@@ -89,6 +90,10 @@ namespace {
 constexpr int64_t kMaxElems = int64_t(1) << 46;   // per tensor; keeps every index in int64
 constexpr int64_t kMaxGrid = std::numeric_limits<int32_t>::max();
 constexpr int64_t kMaxSelD = int64_t(1) << 24;   // channels of lr_selective_scan
+// elements between consecutive tokens of a chunked-scan input (G*N, H*P; GLA
+// H*K, H*V): the kernels address up to 64 token rows of one block with
+// unsigned 32-bit byte offsets (126 * 2^25 + a row < 2^32)
+constexpr int64_t kMaxChunkRow = int64_t(1) << 25;
 
 // Checked product of non-negative sizes; false on overflow.
 bool mul_ok(int64_t& acc, int64_t v) {
@@ -103,6 +108,12 @@ bool elems_ok(std::initializer_list<int64_t> dims) {
   for (int64_t d : dims)
     if (!mul_ok(n, d)) return false;
   return n <= kMaxElems;
+}
+
+// A token row of n1 * n2 elements that the chunked kernels can address.
+bool row_ok(int64_t n1, int64_t n2) {
+  int64_t n = 1;
+  return mul_ok(n, n1) && mul_ok(n, n2) && n <= kMaxChunkRow;
 }
 
 bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -135,8 +146,10 @@ lr_status check_ssd_sizes(int io, int disc, int64_t B, int64_t L, int64_t H, int
   if (io != LR_BF16) return LR_E_UNSUPPORTED;
   if (P % 64 != 0 || (N != 64 && N != 128) || chunk % 64 != 0 || seg % 64 != 0)
     return LR_E_UNSUPPORTED;
+  if (seg > 0 && seg % chunk != 0) return LR_E_SHAPE;   // segments are whole chunks
   if (!elems_ok({B, L, H, P}) || !elems_ok({B, L, G, N}) || !elems_ok({B, H, P, N}))
     return LR_E_OVERFLOW;
+  if (!row_ok(G, N) || !row_ok(H, P)) return LR_E_UNSUPPORTED;
   int64_t nwg = 1;
   if (!mul_ok(nwg, B) || !mul_ok(nwg, H) || !mul_ok(nwg, P / 64) || nwg > kMaxGrid)
     return LR_E_OVERFLOW;
@@ -318,11 +331,10 @@ lr_status lr_ssd_scan_bwd(lr_dtype io, lr_disc disc, int64_t B, int64_t L, int64
     return LR_E_ALIGN;
   const size_t need = lr::ssd_bwd_workspace(B, L, H, P, G, N, seg);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LR_E_WORKSPACE;
-  (void)h0;  // the entering state is ckpt[0]
   if (B * L == 0)
     return hip_status(lr::launch_ssd_bwd_empty(dA, dD, dh0, dh_last, H, B * H * P * N,
                                                static_cast<hipStream_t>(stream)));
-  return hip_status(lr::launch_ssd_bwd(disc, x, dt, A, Bm, Cm, Dskip, ckpt, dy, dh_last, dx, ddt,
+  return hip_status(lr::launch_ssd_bwd(disc, x, dt, A, Bm, Cm, Dskip, h0, ckpt, dy, dh_last, dx, ddt,
                                        dA, dBm, dCm, dD, dh0, workspace, B, L, H, P, G, N, seg,
                                        static_cast<hipStream_t>(stream)));
 }
@@ -334,8 +346,10 @@ static lr_status check_gla_sizes(int io, int64_t B, int64_t L, int64_t H, int64_
   if (B < 0 || L < 0 || H < 1 || K < 1 || V < 1 || chunk < 1 || seg < 0) return LR_E_SHAPE;
   if (io != LR_BF16 || (K != 64 && K != 128) || V % 64 != 0 || chunk % 64 != 0 || seg % 64 != 0)
     return LR_E_UNSUPPORTED;
+  if (seg > 0 && seg % chunk != 0) return LR_E_SHAPE;   // segments are whole chunks
   if (!elems_ok({B, L, H, K}) || !elems_ok({B, L, H, V}) || !elems_ok({B, H, K, V}))
     return LR_E_OVERFLOW;
+  if (!row_ok(H, K) || !row_ok(H, V)) return LR_E_UNSUPPORTED;
   int64_t nwg = 1;
   if (!mul_ok(nwg, B) || !mul_ok(nwg, H) || !mul_ok(nwg, V / 64) || nwg > kMaxGrid)
     return LR_E_OVERFLOW;

@@ -52,6 +52,7 @@ enum { kBwdZoh = 0, kBwdEuler = 1, kBwdGla = 2, kBwdDirac = 3, kBwdBilinear = 4 
 struct BwdArgs {
   const uint16_t* x; const uint16_t* dt; const float* A; const uint16_t* Bm; const uint16_t* Cm;
   const float* Dskip; const float* ckpt; const uint16_t* dy; const float* dh_last;
+  const float* h0;                // SSD: [B][H][P][N] or null; replaces ckpt[0] when given
   uint16_t* dx; uint16_t* ddt; float* dA; uint16_t* dBm; uint16_t* dCm; float* dD; float* dh0;
   uint16_t* dBpart; uint16_t* dCpart;   // [H][B][L][N] bf16 per-head partials
   float* gseg;                    // [nseg][B][H][P][N]: Gamma_loc, then Gamma_out
@@ -342,7 +343,9 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
   bf16x8 hsb[NBS][NK];
   f32x4 hacc[NT];
   {
-    const float* cp = a.ckpt + ((sg * a.B + b) * a.H + h) * kBP * NS;
+    const float* cp = (sg == 0 && a.h0 != nullptr)
+                          ? a.h0 + (b * a.H + h) * kBP * NS
+                          : a.ckpt + ((sg * a.B + b) * a.H + h) * kBP * NS;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) hacc[nt] = *reinterpret_cast<const f32x4*>(cp + p * NS + 16 * nt + 4 * g4);
   }
@@ -917,7 +920,8 @@ static hipError_t launch_bwd(BwdArgs a, void* ws, hipStream_t stream) {
 }
 
 hipError_t launch_ssd_bwd(int disc, const void* x, const void* dt, const float* A, const void* Bm,
-                          const void* Cm, const float* Dskip, const float* ckpt, const void* dy,
+                          const void* Cm, const float* Dskip, const float* h0, const float* ckpt,
+                          const void* dy,
                           const float* dh_last, void* dx, void* ddt, float* dA, void* dBm,
                           void* dCm, float* dD, float* dh0, void* ws, int64_t B, int64_t L,
                           int64_t H, int64_t P, int64_t G, int64_t N, int64_t seg,
@@ -928,6 +932,7 @@ hipError_t launch_ssd_bwd(int disc, const void* x, const void* dt, const float* 
   a.x = static_cast<const uint16_t*>(x); a.dt = static_cast<const uint16_t*>(dt); a.A = A;
   a.Bm = static_cast<const uint16_t*>(Bm); a.Cm = static_cast<const uint16_t*>(Cm);
   a.Dskip = Dskip; a.ckpt = ckpt; a.dy = static_cast<const uint16_t*>(dy); a.dh_last = dh_last;
+  a.h0 = h0;
   a.dx = static_cast<uint16_t*>(dx); a.ddt = static_cast<uint16_t*>(ddt); a.dA = dA;
   a.dBm = static_cast<uint16_t*>(dBm); a.dCm = static_cast<uint16_t*>(dCm); a.dD = dD; a.dh0 = dh0;
   a.B = B; a.L = L; a.H = H; a.G = G; a.N = N; a.seg = seg;

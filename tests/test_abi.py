@@ -132,6 +132,20 @@ def test_ssd_validation(L):
     assert ssd(L, x=None) == NULL
     assert ssd(L, x=MIS) == ALIGN
     assert ssd(L, B=0, x=None) == OK
+    # segments must be whole chunks
+    assert ssd(L, chunk=256, seg=128, ck=P) == SHAPE
+    assert ssd(L, chunk=128, seg=256, ck=P, x=None) == NULL
+
+
+def test_ssd_row_width_limit(L):
+    # 64 token rows of x (H*P elements) and of B/C (G*N) must stay within
+    # 32-bit byte offsets: up to 2^25 elements per row.  At the limit the
+    # sizes pass and the call stops at the missing pointer.
+    assert ssd(L, H=1 << 19, x=None) == NULL            # H*P = 2^25
+    assert ssd(L, H=(1 << 19) + 1, x=None) == UNSUP     # H*P = 2^25 + 64
+    assert ssd(L, H=1 << 18, G=1 << 18, x=None) == NULL   # G*N = 2^25
+    assert ssd(L, H=(1 << 18) + 1, G=(1 << 18) + 1, x=None) == UNSUP
+    assert L.lr_ssd_scan_bwd_workspace_bytes(1, 64, (1 << 19) + 1, 64, 1, 128, 64, 64) == 0
 
 
 def test_ssd_fwd_workspace(L):
@@ -184,6 +198,17 @@ def test_gla_validation(L):
     assert gla(seg=64, ck=MIS) == ALIGN
     need = L.lr_gla_scan_workspace_bytes(1, 4096, 2, 128, 128, 64)
     assert gla(Lq=4096, ws=P, wsb=need - 1) == WS
+    assert gla(chunk=256, seg=128, ck=P) == SHAPE       # segments are whole chunks
+
+
+def test_gla_row_width_limit(L):
+    def gla(H, K, V, q=None):
+        return L.lr_gla_scan(1, 1, 64, H, K, V, 64, 0, q, P, P, P, None, P, None, None, None, 0,
+                             None)
+    assert gla(1 << 18, 128, 64) == NULL                # H*K = 2^25
+    assert gla((1 << 18) + 1, 128, 64) == UNSUP
+    assert gla(1 << 18, 64, 128) == NULL                # H*V = 2^25
+    assert gla(1 << 18, 64, 192) == UNSUP
 
 
 def test_gla_bwd_validation(L):

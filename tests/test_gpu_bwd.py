@@ -96,3 +96,42 @@ def test_ssd_fwd_bwd_full_size_sampled():
                             g["Dskip"], hpre, g["dy"][sfx])
     for k in ("dB", "dC", "dx", "ddt"):
         check(f"{k}[b=0, last 256]", host(gr[k][sfx]), r[k], TOL["bf16"])
+
+
+def _inner(a, b):
+    return float((a.double() * b.double()).sum())
+
+
+def _noise_floor(a, b):
+    # size of sum(a*b) if its terms had random signs: the scale against which
+    # per-element rounding of a or b shows in the sum
+    return float(((a.double() * b.double()) ** 2).sum().sqrt())
+
+
+def test_ssd_fwd_bwd_full_size_linearity():
+    """Whole tensors at B=4, L=8192, H=32, P=64, N=128, seg=256.  y is linear
+    in x, so <dy, y(x=v)> = <dx, v> for any v (Dskip included); with h0 = 0,
+    y - Dskip x is linear in B and in C, so <dy, y(B=w) - Dskip x> = <dB, w>
+    and <dy, y(C=w) - Dskip x> = <dC, w>.  The gradients come from the
+    backward at the workload's inputs, the left sides from forwards at v, w."""
+    print("ssd fwd+bwd full size, linearity identities", flush=True)
+    g = lrgen.make(5)
+    p = g.params
+    B, L, H, P, G, N, seg = p["B"], p["L"], p["H"], p["P"], p["G"], p["N"], p["seg"]
+    _, _, gr = _fwd_bwd(g, seg)
+    T = {k: dev(g.t(k)) for k in ("x", "dt", "A", "B", "C", "Dskip", "dy")}
+    v = dev(lrgen.round_bf16(lrgen.state_normal((B, L, H, P), 5, tensor_id=31)), "bf16")
+    w = dev(lrgen.round_bf16(lrgen.state_normal((B, L, G, N), 5, tensor_id=32)), "bf16")
+    Dx = T["Dskip"].double()[None, None, :, None] * T["x"].double()
+    fwd = lambda x, Bm, Cm: lr.lr_ssd_scan(x, T["dt"], T["A"], Bm, Cm, T["Dskip"],
+                                           chunk=p["chunk"])[0]
+    cases = [("x", fwd(v, T["B"], T["C"]).double(), gr["dx"], v),
+             ("B", fwd(T["x"], w, T["C"]).double() - Dx, gr["dB"], w),
+             ("C", fwd(T["x"], T["B"], w).double() - Dx, gr["dC"], w)]
+    torch.cuda.synchronize()
+    for name, yv, grad, probe in cases:
+        lhs, rhs = _inner(T["dy"], yv), _inner(grad, probe)
+        err = abs(lhs - rhs) / _noise_floor(T["dy"], yv)
+        print(f"<dy, y({name}=probe)> = {lhs:.6e}, <d{name}, probe> = {rhs:.6e}, "
+              f"|diff| / noise floor = {err:.3e}", flush=True)
+        assert err <= TOL["bf16"], name

@@ -1,5 +1,6 @@
 """GPU parity of lr_rotlru_scan (complex-diagonal recurrence over channel
 pairs) against the fp64 oracle, through the C ABI."""
+import numpy as np
 import pytest
 import torch
 
@@ -9,6 +10,10 @@ import ssm_selective_scan_amd as lr
 from gpu_util import TOL, check, dev
 
 pytestmark = pytest.mark.gpu
+
+
+def _round_io(x, io):
+    return lrgen.round_bf16(x) if io == "bf16" else lrgen.round_f32(x)
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
@@ -53,11 +58,10 @@ def test_rotlru_bwd_parity(io, B, L, D):
     h0 = lrgen.state_normal((B, D), 6)
     dhl = lrgen.state_normal((B, D), 6, tensor_id=21)
     r, th = dev(g.t("r")), dev(g.t("theta"))
-    h, _ = lr.lr_rotlru_scan(r, th, dev(g.t("u")), h0=dev(h0))
-    # the oracle differentiates at the states the GPU forward produced (as
-    # rounded to io), exactly what the backward consumes
-    hh = h.float().cpu().numpy()
-    dr, dth, du, dh0 = lr.lr_rotlru_scan_bwd(r, th, h, dev(g.t("dh")), h0=dev(h0),
+    # both sides differentiate at the oracle's own forward states, rounded to
+    # io as a forward output would be (the forward is checked on its own)
+    hh = _round_io(oracle.rotlru_scan(g["r"], g["theta"], g["u"], h0)[0], io)
+    dr, dth, du, dh0 = lr.lr_rotlru_scan_bwd(r, th, dev(hh, io), dev(g.t("dh")), h0=dev(h0),
                                              dh_last=dev(dhl), want_dh0=True)
     torch.cuda.synchronize()
     rdr, rdth, rdu, rdh0 = oracle.rotlru_scan_bwd(g["r"], g["theta"], hh, g["dh"], h0, dhl)
@@ -73,14 +77,15 @@ def test_rotlru_bwd_no_state_and_determinism(B, L, D):
     print(f"rotlru bwd no state B={B} L={L} D={D}", flush=True)
     g = lrgen.make(6, B=B, L=L, D=D, grads=True)
     r, th, dh = dev(g.t("r")), dev(g.t("theta")), dev(g.t("dh"))
-    h, _ = lr.lr_rotlru_scan(r, th, dev(g.t("u")))
+    hh = oracle.rotlru_scan(g["r"], g["theta"], g["u"])[0].astype(np.float32)
+    h = dev(hh, "f32")
     r1 = lr.lr_rotlru_scan_bwd(r, th, h, dh, want_dh0=True)
     r2 = lr.lr_rotlru_scan_bwd(r, th, h, dh, want_dh0=True)
     torch.cuda.synchronize()
     for x1, x2 in zip(r1, r2):
         assert torch.equal(x1, x2)
     assert torch.count_nonzero(r1[0][:, 0]) == 0 and torch.count_nonzero(r1[1][:, 0]) == 0
-    ref = oracle.rotlru_scan_bwd(g["r"], g["theta"], h.cpu().numpy(), g["dh"])
+    ref = oracle.rotlru_scan_bwd(g["r"], g["theta"], hh, g["dh"])
     for name, x, e in zip(("dr", "dtheta", "du", "dh0"), r1, ref):
         check(name, x, e, TOL["f32"])
     # empty sequence: dh0 = dh_last, h_last = h0
