@@ -5,7 +5,7 @@ import math
 import numpy as np
 import pytest
 
-from oracle import max_rel_err, rel_err_p999
+from oracle import max_rel_err, rel_err_p99, rel_err_p999, rel_err_pct
 
 
 def test_exact_match_is_zero():
@@ -94,3 +94,14 @@ def test_inputs_are_compared_in_float64():
     ref = np.array([1.0, 1.0], dtype=np.float64)
     out = np.array([1.0, 1.0 + 1e-12])
     assert max_rel_err(out, ref) == pytest.approx(1e-12, rel=1e-3)
+
+
+def test_p99_position_and_general_percentile():
+    ref = np.ones(10000)
+    out = ref.copy()
+    out[:50] += 1.0           # 0.5 %: below the 99th percentile, above the 99.9th
+    assert rel_err_p99(out, ref) == 0.0
+    assert rel_err_p999(out, ref) == pytest.approx(1.0 / 1.001, rel=1e-12)
+    out[:200] += 1.0          # 2 %: both see it
+    assert rel_err_p99(out, ref) > 0.9
+    assert rel_err_pct(out, ref, 50.0) == 0.0
