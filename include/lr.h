@@ -20,15 +20,17 @@
  *     gradient.  A, Dskip, states (h0, h_last, ckpt, S0, S_last) and the
  *     parameter gradients (dA, dD, dh0) are always float32.
  *   - Ownership: the caller owns every buffer.  The library allocates no
- *     memory and keeps no per-call state; scratch memory of the backward is a
- *     caller-provided workspace whose size comes from a query function.
+ *     memory and keeps no per-call state; scratch memory is a caller-provided
+ *     workspace whose size comes from a query function.  The one exception,
+ *     lr_ssd_scan_noalloc, uses a static device array of the library instead.
  *   - Sizes: B and L may be 0 (empty input: nothing is computed; outputs that
  *     carry a state receive the initial state).  Feature sizes must be > 0.
  *   - Errors: each call validates all arguments BEFORE touching the device.
  *     On failure it returns a non-zero lr_status and writes nothing.  Launch
  *     failures map to LR_E_HIP.  Faults inside a kernel surface at the
  *     caller's next synchronisation.  No C++ exception crosses the ABI.  The
- *     library is thread-safe (it has no mutable global state).
+ *     library is thread-safe: its only global state is the per-device address
+ *     of lr_ssd_scan_noalloc's static array, set once per device.
  *   - Determinism: results are bitwise identical across runs for a fixed
  *     build, shape and input (no floating-point atomics anywhere).
  */
@@ -231,6 +233,29 @@ lr_status lr_ssd_scan(lr_dtype io, lr_disc disc, int64_t B, int64_t L,
  * The caller owns the workspace; its contents are scratch. */
 size_t lr_ssd_scan_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t P,
                                    int64_t G, int64_t N, int64_t chunk);
+
+/* ---------------------------------------------------------------------------
+ * lr_ssd_scan for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation and kernels as lr_ssd_scan with an "auto" workspace, but
+ * the sequence split's scratch (the parts' end states and decay products)
+ * lives in a static 16 MiB device array of the library, one per GPU, held
+ * until the process ends.  No workspace argument; the call allocates
+ * nothing and issues no memset.  Arguments, layouts and errors as
+ * lr_ssd_scan; LR_E_WORKSPACE if a split would need more than the static
+ * array (for N <= 128 the split needs at most ~16.7 MB, so every accepted
+ * size fits).  Nothing in the array has to start at zero: each call writes
+ * the scratch it reads.  Every call on one GPU shares that GPU's array, so
+ * calls that overlap in time on one GPU (other streams, other threads) race
+ * on it: order them on one stream.
+ * ------------------------------------------------------------------------- */
+lr_status lr_ssd_scan_noalloc(lr_dtype io, lr_disc disc, int64_t B, int64_t L,
+                              int64_t H, int64_t P, int64_t G, int64_t N,
+                              int64_t chunk, int64_t seg, const void* x,
+                              const void* dt, const float* A, const void* Bm,
+                              const void* Cm, const float* Dskip,
+                              const float* h0, void* y, float* h_last,
+                              float* ckpt, void* stream);
 
 /* Workspace bytes needed by lr_ssd_scan_bwd for these sizes (0 on invalid
  * sizes).  The workspace holds per-head partial sums of dB and dC (bf16),

@@ -16,7 +16,7 @@ from ._lib import (LR_BF16, LR_DISC_BILINEAR, LR_DISC_DIRAC, LR_DISC_EULER,  # n
                    LR_DISC_ZOH, LR_F32, LrError, check, lib)
 
 __all__ = ["lr_diag_scan", "lr_diag_scan_bwd", "lr_rotlru_scan", "lr_rotlru_scan_bwd", "lr_selective_scan", "lr_selective_scan_bwd",
-           "lr_selective_scan_bwd_workspace_bytes", "lr_ssd_scan", "lr_ssd_scan_bwd",
+           "lr_selective_scan_bwd_workspace_bytes", "lr_ssd_scan", "lr_ssd_scan_noalloc", "lr_ssd_scan_bwd",
            "lr_ssd_scan_bwd_workspace_bytes", "lr_gla_scan", "lr_gla_scan_bwd",
            "lr_gla_scan_bwd_workspace_bytes", "lr_diag_step", "lr_selective_step", "lr_ssd_step",
            "lr_gla_step", "lr_version", "LrError"]
@@ -311,6 +311,28 @@ def lr_ssd_scan(x, dt, A, Bm, Cm, Dskip=None, h0=None, disc="zoh", chunk=64, seg
         _ptr(Bm), _ptr(Cm), _ptr(Dskip), _ptr(h0), _ptr(y), _ptr(h_last),
         _ptr(ckpt if seg > 0 else None), _ptr(ws), ws.numel() if ws is not None else 0,
         _stream(x)))
+    return y, h_last, (ckpt if seg > 0 else None)
+
+
+def lr_ssd_scan_noalloc(x, dt, A, Bm, Cm, Dskip=None, h0=None, disc="zoh", chunk=64, seg=0,
+                        y=None, h_last=None, ckpt=None):
+    """lr_ssd_scan whose sequence-split scratch is the library's static
+    device array: the C call allocates nothing (pass y, h_last and ckpt to
+    keep this wrapper from allocating them).  Returns (y, h_last, ckpt)."""
+    B, L, H, P, G, N, io = _ssd_check(x, dt, A, Bm, Cm, Dskip, h0)
+    seg = _seg(seg)
+    _expect(x, "y", y, (B, L, H, P), io)
+    _expect(x, "h_last", h_last, (B, H, P, N), F32)
+    if seg > 0:
+        _expect(x, "ckpt", ckpt, (_nseg(L, seg), B, H, P, N), F32)
+    if y is None:
+        y = torch.empty_like(x)
+    if seg > 0 and ckpt is None:
+        ckpt = torch.empty(_nseg(L, seg), B, H, P, N, device=x.device, dtype=F32)
+    check("lr_ssd_scan_noalloc", lib().lr_ssd_scan_noalloc(
+        _io(x), _disc(disc), B, L, H, P, G, N, chunk, seg, _ptr(x), _ptr(dt), _ptr(A),
+        _ptr(Bm), _ptr(Cm), _ptr(Dskip), _ptr(h0), _ptr(y), _ptr(h_last),
+        _ptr(ckpt if seg > 0 else None), _stream(x)))
     return y, h_last, (ckpt if seg > 0 else None)
 
 

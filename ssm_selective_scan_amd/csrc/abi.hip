@@ -44,6 +44,8 @@ hipError_t launch_gla_fwd(const void* q, const void* k, const void* v, const voi
                           int64_t L, int64_t H, int64_t K, int64_t V, int64_t seg, void* ws,
                           size_t ws_bytes, hipStream_t stream);
 size_t ssd_fwd_workspace(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N);
+size_t ssd_noalloc_scratch_bytes();
+hipError_t ssd_noalloc_scratch(void** out);
 size_t gla_fwd_workspace(int64_t B, int64_t L, int64_t H, int64_t K, int64_t V);
 size_t gla_bwd_workspace(int64_t B, int64_t L, int64_t H, int64_t K, int64_t V, int64_t seg);
 hipError_t launch_gla_bwd(const void* q, const void* k, const void* v, const void* g,
@@ -296,6 +298,30 @@ lr_status lr_ssd_scan(lr_dtype io, lr_disc disc, int64_t B, int64_t L, int64_t H
   if (B == 0) return LR_OK;
   return hip_status(lr::launch_ssd_fwd(disc, x, dt, A, Bm, Cm, Dskip, h0, y, h_last, ckpt, B, L,
                                        H, P, G, N, seg, workspace, workspace_bytes,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+lr_status lr_ssd_scan_noalloc(lr_dtype io, lr_disc disc, int64_t B, int64_t L, int64_t H,
+                              int64_t P, int64_t G, int64_t N, int64_t chunk, int64_t seg,
+                              const void* x, const void* dt, const float* A, const void* Bm,
+                              const void* Cm, const float* Dskip, const float* h0, void* y,
+                              float* h_last, float* ckpt, void* stream) {
+  lr_status st = check_ssd_sizes(io, disc, B, L, H, P, G, N, chunk, seg);
+  if (st != LR_OK) return st;
+  const size_t need = lr::ssd_fwd_workspace(B, L, H, P, N);
+  if (need > lr::ssd_noalloc_scratch_bytes()) return LR_E_WORKSPACE;
+  if (A == nullptr) return LR_E_NULLPTR;
+  if (B * L > 0 && any_null({x, dt, Bm, Cm, y})) return LR_E_NULLPTR;
+  if (seg > 0 && B * L > 0 && ckpt == nullptr) return LR_E_NULLPTR;
+  if (!all_aligned({x, dt, A, Bm, Cm, Dskip, h0, y, h_last, ckpt})) return LR_E_ALIGN;
+  if (B == 0) return LR_OK;
+  void* ws = nullptr;
+  if (need > 0) {
+    const hipError_t e = lr::ssd_noalloc_scratch(&ws);
+    if (e != hipSuccess) return LR_E_HIP;
+  }
+  return hip_status(lr::launch_ssd_fwd(disc, x, dt, A, Bm, Cm, Dskip, h0, y, h_last, ckpt, B, L,
+                                       H, P, G, N, seg, ws, ws != nullptr ? need : 0,
                                        static_cast<hipStream_t>(stream)));
 }
 

@@ -39,6 +39,8 @@
 // of the parts before it into its entering state with the combine
 // (a2, b2) o (a1, b1) = (a2 a1, a2 b1 + b2) ("K-Search for MLX" blog,
 // section "A 20x faster prefill", combine equation), applied to whole parts.
+#include <atomic>
+
 #include "common.hpp"
 
 namespace lr {
@@ -517,6 +519,43 @@ hipError_t launch_ssd_fwd(int disc, const void* x, const void* dt, const float* 
     case 3: return launch_chunk<kModeSsdDirac, 64>(a, ws, ws_bytes, stream);
     default: return launch_chunk<kModeSsdZoh, 64>(a, ws, ws_bytes, stream);
   }
+}
+
+// ---------------------------------------------------------------------------
+// Static scratch of lr_ssd_scan_noalloc: the sequence split's part states and
+// decay products live in this file-scope device array instead of a caller
+// workspace, so the call allocates nothing.  Each GPU the library runs on
+// holds its own copy (16 MiB) until the process ends.  For N <= 128 the
+// split never needs more: its parts times workgroups stay below 512, so the
+// part states take at most 511 * 64 * 128 * 4 bytes plus 511 decays.
+// Host code reaches the array only through the address hipGetSymbolAddress
+// returns for the current device (the array's name is a host-side stand-in).
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch[kMaxScratchDevices];
+}  // namespace
+
+size_t ssd_noalloc_scratch_bytes() { return kNoAllocScratchBytes; }
+
+// Device address of `scratch` on the current device, looked up once per
+// device (two threads racing on the first call store the same address).
+hipError_t ssd_noalloc_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return hipSuccess;
 }
 
 hipError_t launch_gla_fwd(const void* q, const void* k, const void* v, const void* gate,
