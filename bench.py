@@ -11,11 +11,18 @@ taken with HIP events recorded on the launch stream.  Input/output buffer
 sets are rotated so that the 256 MB Infinity Cache cannot hold a step's
 working set from the previous step.
 
+Before the warm-ups, the headline kernel runs back to back for --settle-ms
+of GPU time (reported as clock_settle), so the timed steps see steady
+clocks rather than the first launches' ramp.
+
 The same run also measures the other four workloads (diagonal scan, SSD
-forward, GLA forward, SSD forward + backward with segment checkpoints) and a
-plain device copy for the achievable-bandwidth reference, and times the fp64
-CPU oracle on a bounded sample of the headline workload (cpu_baseline).
-One JSON line is printed.
+forward, GLA forward, SSD forward + backward with segment checkpoints), the
+backward and decode paths, and a plain device copy for the achievable
+bandwidth; records which kernels each call dispatched (dispatch, from the
+torch profiler's HIP activity trace); and, before touching the GPU, times
+the fp64 CPU oracle on a bounded sample of every workload on the host's
+cores (cpu_baseline: the headline's figure, with per_workload for all five
+and the GPU-over-oracle ratios).  One JSON line is printed.
 """
 from __future__ import annotations
 
@@ -55,10 +62,13 @@ def rotations(nbytes, floor=3):
     return max(floor, int(np.ceil(768e6 / max(nbytes, 1))) + 1)
 
 
-def time_launches(fn, sets, warmup, iters):
+def time_launches(fn, sets, warmup, iters, settle_ms=30.0):
     """Average duration (s) of fn(set) measured with events on the launch
-    stream, cycling through the buffer sets."""
+    stream, cycling through the buffer sets, after `settle_ms` of untimed
+    back-to-back launches and `warmup` more."""
     stream = torch.cuda.current_stream()
+    if settle_ms > 0:
+        settle_clocks(fn, sets, settle_ms)
     for i in range(warmup):
         fn(sets[i % len(sets)])
     torch.cuda.synchronize()
@@ -106,10 +116,11 @@ def measure_diag(warmup, iters):
     g = lrgen.make(1)
     a, b = dev(g.t("a")), dev(g.t("b"))
     sets = [dict(a=a, b=b, h=torch.empty_like(a))]
-    t, _ = time_launches(lambda s: lr.lr_diag_scan(s["a"], s["b"], h=s["h"]), sets, warmup, iters)
+    call = lambda s: lr.lr_diag_scan(s["a"], s["b"], h=s["h"])
+    t, _ = time_launches(call, sets, warmup, iters)
     p = g.params
     nb = 3 * p["B"] * p["L"] * p["D"] * 4
-    return dict(workload=lrgen.NAMES[1], kernel="diag_scan_kernel", us=t * 1e6,
+    return dict(workload=lrgen.NAMES[1], kernels=fingerprint(lambda: call(sets[0])), us=t * 1e6,
                 tokens_per_s=p["B"] * p["L"] / t, elems_per_s=p["B"] * p["L"] * p["D"] / t,
                 alg_bytes=nb, GBs=nb / t / 1e9, hbm_frac=nb / t / 1e9 / HBM_PEAK_GBS,
                 note="3 MB working set: launch/latency bound")
@@ -127,12 +138,12 @@ def measure_ssd(warmup, iters):
     B, L, H, P, N = p["B"], p["L"], p["H"], p["P"], p["N"]
     wsb = lr.lr_ssd_scan_workspace_bytes(B, L, H, P, p["G"], N, p["chunk"])
     ws = torch.empty(wsb, device="cuda", dtype=torch.uint8) if wsb else None
-    t, _ = time_launches(lambda s: lr.lr_ssd_scan(s["x"], s["dt"], A, s["Bm"], s["Cm"], Dk,
-                                                  chunk=p["chunk"], y=s["y"], workspace=ws),
-                         sets, warmup, iters)
+    call = lambda s: lr.lr_ssd_scan(s["x"], s["dt"], A, s["Bm"], s["Cm"], Dk, chunk=p["chunk"],
+                                    y=s["y"], workspace=ws)
+    t, _ = time_launches(call, sets, warmup, iters)
     nb = 2 * B * L * H * P * 2 + B * L * H * 2 + 2 * B * L * N * 2 + 2 * H * 4
     fl = ssd_mfma_flops(B, L, H, P, N)
-    return dict(workload=lrgen.NAMES[3], kernel="chunk_fwd_kernel<SSD> (state pre-pass + main)",
+    return dict(workload=lrgen.NAMES[3], kernels=fingerprint(lambda: call(sets[0])),
                 fwd_workspace_bytes=wsb, us=t * 1e6,
                 tokens_per_s=B * L / t, elems_per_s=B * L * H * P / t, alg_bytes=nb,
                 GBs=nb / t / 1e9, hbm_frac=nb / t / 1e9 / HBM_PEAK_GBS,
@@ -157,12 +168,12 @@ def measure_gla(warmup, iters):
     B, L, H, K, V = p["B"], p["L"], p["H"], p["K"], p["V"]
     wsb = lr.lr_gla_scan_workspace_bytes(B, L, H, K, V, p["chunk"])
     ws = torch.empty(wsb, device="cuda", dtype=torch.uint8) if wsb else None
-    t, _ = time_launches(lambda s: lr.lr_gla_scan(s["q"], s["k"], s["v"], s["g"],
-                                                  chunk=p["chunk"], o=s["o"], workspace=ws),
-                         sets, warmup, iters)
+    call = lambda s: lr.lr_gla_scan(s["q"], s["k"], s["v"], s["g"], chunk=p["chunk"], o=s["o"],
+                                    workspace=ws)
+    t, _ = time_launches(call, sets, warmup, iters)
     nb = 2 * B * L * H * K * 2 + 2 * B * L * H * V * 2 + B * L * H * 2
     fl = (V // 64) * ssd_mfma_flops(B, L, H, 64, K)
-    return dict(workload=lrgen.NAMES[4], kernel="chunk_fwd_kernel<GLA> (state pre-pass + main)",
+    return dict(workload=lrgen.NAMES[4], kernels=fingerprint(lambda: call(sets[0])),
                 fwd_workspace_bytes=wsb, us=t * 1e6,
                 tokens_per_s=B * L / t, elems_per_s=B * L * H * V / t, alg_bytes=nb,
                 GBs=nb / t / 1e9, hbm_frac=nb / t / 1e9 / HBM_PEAK_GBS,
@@ -183,9 +194,9 @@ def measure_ssd_bwd(warmup, iters):
     torch.cuda.reset_peak_memory_stats()
     fwsb = lr.lr_ssd_scan_workspace_bytes(B, L, H, P, G, N, p["chunk"])
     fws = torch.empty(fwsb, device="cuda", dtype=torch.uint8) if fwsb else None
-    tf, _ = time_launches(lambda s: lr.lr_ssd_scan(x, dt, A, Bm, Cm, Dk, chunk=p["chunk"],
-                                                   seg=seg, y=y, ckpt=ckpt, workspace=fws),
-                          [None], warmup, iters)
+    fcall = lambda s: lr.lr_ssd_scan(x, dt, A, Bm, Cm, Dk, chunk=p["chunk"], seg=seg, y=y,
+                                     ckpt=ckpt, workspace=fws)
+    tf, _ = time_launches(fcall, [None], warmup, iters)
     ws_bytes = lr.lr_ssd_scan_bwd_workspace_bytes(B, L, H, P, G, N, p["chunk"], seg)
     # state-related memory: checkpoints, the forward's part states, the backward's workspace
     out = dict(workload=lrgen.NAMES[5], fwd_us=tf * 1e6,
@@ -197,13 +208,13 @@ def measure_ssd_bwd(warmup, iters):
     out["fwd_GBs"] = fwd_bytes / tf / 1e9
     try:
         ws = torch.empty(max(ws_bytes, 16), device="cuda", dtype=torch.uint8)
-        tb, _ = time_launches(lambda s: lr.lr_ssd_scan_bwd(x, dt, A, Bm, Cm, Dk, None, ckpt, dy,
-                                                           chunk=p["chunk"], seg=seg,
-                                                           workspace=ws),
-                              [None], warmup, iters)
+        bcall = lambda s: lr.lr_ssd_scan_bwd(x, dt, A, Bm, Cm, Dk, None, ckpt, dy,
+                                             chunk=p["chunk"], seg=seg, workspace=ws)
+        tb, _ = time_launches(bcall, [None], warmup, iters)
         bwd_bytes = (3 * B * L * H * P * 2 + 2 * B * L * H * 2 + 4 * B * L * N * 2
                      + ckpt.numel() * 4)
-        out.update(bwd_us=tb * 1e6, bwd_GBs=bwd_bytes / tb / 1e9,
+        out.update(kernels=fingerprint(lambda: (fcall(None), bcall(None))),
+                   bwd_us=tb * 1e6, bwd_GBs=bwd_bytes / tb / 1e9,
                    fwd_bwd_tokens_per_s=B * L / (tf + tb),
                    peak_alloc_delta_bytes=torch.cuda.max_memory_allocated() - base)
     except lr.LrError as e:
@@ -406,41 +417,159 @@ def copy_bandwidth(nbytes=1 << 30, iters=10):
 
 
 # --------------------------------------------------------------------------
-# CPU oracle baseline (bounded sample of the headline workload)
+# CPU oracle baselines: every workload, on the host's cores
 # --------------------------------------------------------------------------
-def cpu_baseline(g, rows):
+# Each worker process generates one sample unit of a workload (the recipe of
+# lrgen at the unit's shape: a batch row of channels, or one (batch, head)),
+# waits at a barrier, runs the fp64 oracle on it with one BLAS thread and
+# reports its start and end.  The wall time of the parallel section, scaled
+# by (units in the workload) / (units run), is the oracle's time for the
+# whole workload on those cores.
+#   workload id: (unit shape overrides, units in the workload, what is timed)
+CPU_UNITS = {
+    1: (dict(), 1, "diag scan, the whole workload"),
+    2: (dict(B=1, D=512), 8 * 2048 // 512, "selective scan, one batch row x 512 channels"),
+    3: (dict(B=1, H=8), 8 * 32 // 8, "SSD scan, one batch row x 8 heads"),
+    4: (dict(B=1, H=4), 8 * 16 // 4, "GLA scan, one batch row x 4 heads"),
+    5: (dict(B=1, H=1), 4 * 32, "SSD forward with checkpoints + backward, one (batch, head)"),
+}
+
+
+def _oracle_unit(cfg_id):
     import oracle  # the oracle is test infrastructure; only this leg uses it
-    t0 = time.perf_counter()
-    oracle.selective_scan(g["x"][:rows], g["dt"][:rows], g["A"], g["B"][:rows], g["C"][:rows],
-                          g["Dskip"])
-    dt = time.perf_counter() - t0
-    toks = rows * g.params["L"]
-    return dict(value=toks / dt, unit="tokens/s", cores=1, kind="oracle",
-                sample=f"selective scan, {rows} of {g.params['B']} batch rows x full "
-                       f"L={g.params['L']}, D={g.params['D']}, N={g.params['N']}, fp64 numpy, "
-                       f"one thread, {dt:.1f} s")
+    over = CPU_UNITS[cfg_id][0]
+    g = lrgen.make(cfg_id, **over)
+    if cfg_id == 1:
+        return lambda: oracle.diag_scan(g["a"], g["b"])
+    if cfg_id == 2:
+        return lambda: oracle.selective_scan(g["x"], g["dt"], g["A"], g["B"], g["C"], g["Dskip"])
+    if cfg_id == 3:
+        return lambda: oracle.ssd_scan(g["x"], g["dt"], g["A"], g["B"], g["C"], g["Dskip"])
+    if cfg_id == 4:
+        return lambda: oracle.gla_scan(g["q"], g["k"], g["v"], g["g"])
+
+    def fwd_bwd():
+        oracle.ssd_scan(g["x"], g["dt"], g["A"], g["B"], g["C"], g["Dskip"], seg=g.params["seg"])
+        oracle.ssd_scan_bwd(g["x"], g["dt"], g["A"], g["B"], g["C"], g["Dskip"], None, g["dy"])
+    return fwd_bwd
+
+
+_BARRIER = None
+
+
+def _cpu_worker(cfg_id):
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(1):
+        run = _oracle_unit(cfg_id)
+        _BARRIER.wait()
+        t0 = time.perf_counter()
+        run()
+        return t0, time.perf_counter()
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baselines(workers):
+    """Oracle tokens/s of every workload on `workers` processes (one unit
+    each; the diagonal workload, a few milliseconds, on one)."""
+    import multiprocessing as mp
+    global _BARRIER
+    out = {}
+    ctx = mp.get_context("fork")
+    for cfg_id, (_, units, what) in CPU_UNITS.items():
+        P = 1 if units == 1 else min(workers, units)
+        _BARRIER = ctx.Barrier(P)
+        with ctx.Pool(P) as pool:
+            spans = pool.map(_cpu_worker, [cfg_id] * P, chunksize=1)
+        wall = max(e for _, e in spans) - min(s for s, _ in spans)
+        p = lrgen.CONFIGS[cfg_id]
+        full_s = wall * units / P
+        tokens = p["B"] * p["L"]
+        out[lrgen.NAMES[cfg_id]] = dict(
+            value=tokens / full_s, unit="tokens/s", cores=P, kind="oracle",
+            oracle_s_full_workload=full_s, wall_s=wall,
+            sample=f"{P} of {units} units ({what}), full L={p['L']}, fp64 numpy, "
+                   f"one process and one BLAS thread per core; time scaled by {units}/{P}")
+        log(f"[bench] oracle {lrgen.NAMES[cfg_id]}: {P} units in {wall:.2f} s on {P} cores "
+            f"-> {tokens / full_s:.4g} tokens/s for the whole workload")
+    return out
 
 
 def load_traffic():
     """HBM traffic of the selective kernel from the committed rocprofv3 PMC
     summary, if it was taken on the current kernel source."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", "selective_scan_mamba1_B8_L4096_D2048_N16_traffic.txt")
-    csrc = os.path.join(ROOT, "ssm_selective_scan_amd", "csrc")
     if not os.path.exists(path):
         return None
+    kv = read_kv(path)
+    if kv.get("kernel_src_sha256_16") != src_hash(("selective_scan.hip", "common.hpp")):
+        return None
+    return float(kv["traffic_bytes_per_launch"])
+
+
+SECONDARY_WARMUP, SECONDARY_ITERS = 10, 20
+
+
+def fingerprint(fn):
+    return dispatch_fingerprint({"call": fn})["call"]
+
+
+# rocprofv3 counter summaries per workload: profiles/<file> holds key = value
+# lines; they are attached to the workload only while their source hash
+# matches the current sources of the kernels involved
+COUNTER_PROFILES = {
+    "ssd": ("ssd_fwd_B8_H32_P64_N128_L2048_counters.txt", ("chunk_scan.hip", "common.hpp")),
+    "gla": ("gla_fwd_B8_H16_K128_V128_L4096_counters.txt", ("chunk_scan.hip", "common.hpp")),
+    "ssd_fwd_bwd": ("ssd_fwd_bwd_B4_H32_P64_N128_L8192_seg256_counters.txt",
+                    ("chunk_scan.hip", "ssd_bwd.hip", "common.hpp")),
+    "diag": ("diag_B1_L1024_D256_counters.txt", ("diag_scan.hip", "common.hpp")),
+}
+
+
+def src_hash(files):
+    import hashlib
+    csrc = os.path.join(ROOT, "ssm_selective_scan_amd", "csrc")
+    data = b"".join(open(os.path.join(csrc, f), "rb").read() for f in files)
+    return hashlib.sha256(data).hexdigest()[:16]
+
+
+def read_kv(path):
     kv = {}
     with open(path) as f:
         for line in f:
-            if "=" in line and not line.startswith("#"):
+            if "=" in line and not line.lstrip().startswith("#"):
                 k, v = line.split("=", 1)
                 kv[k.strip()] = v.strip()
-    src = b"".join(open(os.path.join(csrc, f), "rb").read()
-                   for f in ("selective_scan.hip", "common.hpp"))
-    sha = hashlib.sha256(src).hexdigest()[:16]
-    if kv.get("kernel_src_sha256_16") != sha:
-        return None
-    return float(kv["traffic_bytes_per_launch"])
+    return kv
+
+
+def attach_profiles(extra):
+    for key, (fname, files) in COUNTER_PROFILES.items():
+        path = os.path.join(ROOT, "profiles", fname)
+        if key not in extra or not os.path.exists(path):
+            continue
+        kv = read_kv(path)
+        if kv.get("kernel_src_sha256_16") != src_hash(files):
+            extra[key]["counters"] = f"profiles/{fname}: stale (kernel sources changed since)"
+            continue
+        vals = {}
+        for k, v in kv.items():
+            if k == "kernel_src_sha256_16":
+                continue
+            try:
+                vals[k] = float(v)
+            except ValueError:
+                vals[k] = v
+        extra[key]["counters"] = dict(vals, source=f"profiles/{fname}")
 
 
 SECONDARY = {"diag": measure_diag, "ssd": measure_ssd, "gla": measure_gla,
@@ -449,17 +578,55 @@ SECONDARY = {"diag": measure_diag, "ssd": measure_ssd, "gla": measure_gla,
              "decode": measure_decode, "rotlru": measure_rotlru, "scaled": measure_scaled}
 
 
+def settle_clocks(fn, sets, ms):
+    """Run fn back to back for about `ms` milliseconds of GPU time (untimed)
+    so the clocks have left their idle state before the warm-up steps."""
+    t0 = time.perf_counter()
+    i = 0
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(8):
+            fn(sets[i % len(sets)])
+            i += 1
+        torch.cuda.synchronize()
+    return i
+
+
+def dispatch_fingerprint(calls):
+    """Names of the GPU kernels each call dispatches, recorded in-process by
+    the torch profiler (HIP activity tracing): the kernels that ran, not the
+    ones the code meant to run."""
+    from torch.profiler import ProfilerActivity, profile
+    out = {}
+    for name, fn in calls.items():
+        torch.cuda.synchronize()
+        with profile(activities=[ProfilerActivity.CUDA]) as prof:
+            fn()
+            torch.cuda.synchronize()
+        names = []
+        for ev in prof.events():
+            if ev.device_type != torch.autograd.DeviceType.CUDA:
+                continue
+            nm = ev.name.split("(")[0].replace("void ", "")   # template, no argument list
+            if nm not in names:
+                names.append(nm)
+        out[name] = names
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # the first few dozen launches run 5-10 % slow while the clocks ramp up;
-    # 50 warm-up steps (20 ms) reach the steady state
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=50)
+    # the first few dozen launches of a process run 5-10 % slow while the
+    # clocks ramp up; this much back-to-back GPU work precedes the warm-ups
+    ap.add_argument("--settle-ms", type=float, default=300.0)
     ap.add_argument("--headline-only", action="store_true",
                     help="time only the headline workload (for profiler runs)")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-rows", type=int, default=8)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baselines")
+    ap.add_argument("--cpu-workers", type=int, default=0,
+                    help="oracle worker processes (0: the cores this process may run on, "
+                         "at most 16, the host share of one GPU)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--only", choices=sorted(SECONDARY),
@@ -470,6 +637,15 @@ def main():
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
               "the scans shard by batch/head with no exchange, see DESIGN.md", file=sys.stderr)
         sys.exit(2)
+
+    # the oracle leg runs first: its worker processes are forked before this
+    # process starts the GPU runtime
+    cpu = None
+    if not (args.no_cpu or args.copy_probe or args.only or args.headline_only):
+        workers = args.cpu_workers or min(len(os.sched_getaffinity(0)), 16)
+        log(f"[bench] CPU oracle baselines on {workers} worker processes ({cpu_model()})")
+        cpu = cpu_baselines(workers)
+
     if not torch.cuda.is_available():
         print("bench.py: no GPU available", file=sys.stderr)
         sys.exit(1)
@@ -489,6 +665,7 @@ def main():
     fn, sets = selective_setup(g)
     log(f"[bench] headline {lrgen.NAMES[2]}: {len(sets)} rotating buffer sets")
 
+    settle = settle_clocks(fn, sets, args.settle_ms)
     for i in range(args.warmup):
         fn(sets[i % len(sets)])
     torch.cuda.synchronize()
@@ -523,6 +700,11 @@ def main():
                 "median_us": float(np.median(all_ms) * 1e3)}
     log(f"[bench] protocol: {protocol}")
 
+    fp = {}
+    if not args.headline_only:
+        fp = dispatch_fingerprint({"headline": lambda: fn(sets[0])})
+        log(f"[bench] headline dispatches: {fp['headline']}")
+
     kt = kern_ms.mean() / 1e3
     nbytes = selective_bytes(p)
     ops = sel_valu_ops(p)
@@ -530,7 +712,8 @@ def main():
     roofline = {"bound": "alu", "achieved": ops / kt / 1e12, "peak": VALU_PEAK_TOPS,
                 "unit": "Tops/s (fp32 VALU lane-ops)",
                 "frac": ops / kt / 1e12 / VALU_PEAK_TOPS, "traffic": traffic,
-                "kernel": "selective_pair_kernel<bf16, ZOH>",
+                "kernel": fp["headline"][0] if fp.get("headline") else
+                          "lr::selective_pair_kernel (not fingerprinted in this run)",
                 "alg_ops_per_launch": ops, "alg_bytes_per_launch": nbytes,
                 "hbm_GBs": nbytes / kt / 1e9, "hbm_frac": nbytes / kt / 1e9 / HBM_PEAK_GBS}
 
@@ -543,6 +726,7 @@ def main():
                    "N": p["N"], "io": "bf16", "state": "f32", "disc": "zoh"},
         "kernel_us": kern_ms.mean() * 1e3,
         "kernel_protocol": protocol,
+        "clock_settle": {"ms": args.settle_ms, "launches": settle},
         "roofline": roofline,
     }
     del sets
@@ -553,16 +737,29 @@ def main():
         for name, f in SECONDARY.items():
             log(f"[bench] measuring {name}")
             try:
-                extra[name] = f(3, 20)
+                extra[name] = f(SECONDARY_WARMUP, SECONDARY_ITERS)
             except Exception as e:  # report, keep the headline line
                 extra[name] = {"error": repr(e)}
             torch.cuda.empty_cache()
         extra["copy_GBs"] = copy_bandwidth()
+        attach_profiles(extra)
         result["workloads"] = extra
+        result["dispatch"] = dict(fp, **{k: v["kernels"] for k, v in extra.items()
+                                         if isinstance(v, dict) and "kernels" in v})
 
-    if not args.no_cpu:
-        log("[bench] cpu_baseline (fp64 oracle)")
-        result["cpu_baseline"] = cpu_baseline(g, args.cpu_rows)
+    if cpu is not None:
+        head = cpu[lrgen.NAMES[2]]
+        result["cpu_baseline"] = dict(head, cpu_model=cpu_model(), per_workload=cpu)
+        gpu_tps = {lrgen.NAMES[2]: result["value"]}
+        wl = result.get("workloads", {})
+        for key, name in (("diag", 1), ("ssd", 3), ("gla", 4)):
+            if "tokens_per_s" in wl.get(key, {}):
+                gpu_tps[lrgen.NAMES[name]] = wl[key]["tokens_per_s"]
+        if "fwd_bwd_tokens_per_s" in wl.get("ssd_fwd_bwd", {}):
+            gpu_tps[lrgen.NAMES[5]] = wl["ssd_fwd_bwd"]["fwd_bwd_tokens_per_s"]
+        for name, v in cpu.items():
+            if name in gpu_tps:
+                v["gpu_over_oracle"] = gpu_tps[name] / v["value"]
     print(json.dumps(result))
 
 
