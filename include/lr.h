@@ -44,8 +44,14 @@
 extern "C" {
 #endif
 
-/* Element type of per-token tensors. */
-typedef enum { LR_F32 = 0, LR_BF16 = 1 } lr_dtype;
+/* Element type of per-token tensors.  The LR_*_RANGE_* enumerators are not
+ * valid arguments: they make every int32 value a value of the type, so an
+ * out-of-range code from the caller is rejected (LR_E_DTYPE) with defined
+ * behaviour in the C++ implementation. */
+typedef enum {
+  LR_F32 = 0, LR_BF16 = 1,
+  LR_DTYPE_RANGE_MIN = INT32_MIN, LR_DTYPE_RANGE_MAX = INT32_MAX
+} lr_dtype;
 
 /* Discretisation of a continuous-time decay A over a step dt ("lrnnx: A
  * library for Linear RNNs", Key Contributions 2-3, which name ZOH, bilinear
@@ -57,7 +63,8 @@ typedef enum { LR_F32 = 0, LR_BF16 = 1 } lr_dtype;
  *   LR_DISC_DIRAC:    abar = exp(l),                bbar = B  (the input is an
  *                     impulse of area x at the sample: no dt factor)           */
 typedef enum {
-  LR_DISC_ZOH = 0, LR_DISC_EULER = 1, LR_DISC_BILINEAR = 2, LR_DISC_DIRAC = 3
+  LR_DISC_ZOH = 0, LR_DISC_EULER = 1, LR_DISC_BILINEAR = 2, LR_DISC_DIRAC = 3,
+  LR_DISC_RANGE_MIN = INT32_MIN, LR_DISC_RANGE_MAX = INT32_MAX   /* not valid arguments */
 } lr_disc;
 
 typedef enum {
@@ -210,8 +217,15 @@ lr_status lr_selective_scan_bwd(lr_dtype io, lr_disc disc, int64_t B,
  *   seg:   0, or a multiple of 64: then ckpt[s] receives the state ENTERING
  *          token s*seg (ckpt[0] = h0 or 0) for s = 0 .. ceil(L/seg)-1 —
  *          the segment checkpoints consumed by lr_ssd_scan_bwd.
- *   ckpt:  [ceil(L/seg), B, H, P, N] fp32; required iff seg > 0.
- * Supported: io = LR_BF16; P % 64 == 0; N in {64, 128}; H % G == 0.
+ *   ckpt:  [ceil(L/seg), B, H, P, N] fp32; required iff seg > 0.  seg must
+ *          be a multiple of chunk (segments are whole chunks): LR_E_SHAPE.
+ *   workspace: optional, see lr_ssd_scan_workspace_bytes (NULL: one pass).
+ * Supported: io = LR_BF16 only (the contractions run on bf16 MFMA; fp32 I/O
+ * returns LR_E_UNSUPPORTED); P % 64 == 0; N in {64, 128}; H % G == 0;
+ * G*N and H*P at most 2^25 (the kernels address 64 token rows with 32-bit
+ * byte offsets; LR_E_UNSUPPORTED beyond).
+ * Deliberate additions to the plain scan signature: seg/ckpt (the segment
+ * checkpoints of the training path) and the optional workspace.
  * ------------------------------------------------------------------------- */
 lr_status lr_ssd_scan(lr_dtype io, lr_disc disc, int64_t B, int64_t L,
                       int64_t H, int64_t P, int64_t G, int64_t N,
@@ -272,6 +286,9 @@ size_t lr_ssd_scan_bwd_workspace_bytes(int64_t B, int64_t L, int64_t H,
  * Gradients of  loss = sum(dy * y) + <dh_last, h_last>  with respect to
  * x, dt, A, Bm, Cm, Dskip and h0.
  *   ckpt:    the checkpoints written by lr_ssd_scan with the same seg.
+ *   h0:      [B, H, P, N] fp32 or NULL: the forward's initial state; when
+ *            given, segment 0 starts from it instead of ckpt[0] (the two are
+ *            equal for checkpoints written by lr_ssd_scan with this h0).
  *   dy:      [B, L, H, P] io      dh_last: [B, H, P, N] fp32 or NULL (= 0)
  *   dx:      [B, L, H, P] io      ddt: [B, L, H] io
  *   dBm, dCm: [B, L, G, N] io (summed over the heads of each group)
@@ -301,11 +318,17 @@ lr_status lr_ssd_scan_bwd(lr_dtype io, lr_disc disc, int64_t B, int64_t L,
  *   q, k: [B, L, H, K] io    v, o: [B, L, H, V] io    g: [B, L, H] io, in (0, 1]
  *   S0, S_last: [B, H, K, V] fp32 or NULL
  *   chunk: any multiple of 64 (same meaning as in lr_ssd_scan).
- *   seg:   0, or a multiple of 64: then ckpt[s] receives the state entering
- *          token s*seg, TRANSPOSED: ckpt is [ceil(L/seg), B, H, V, K] fp32
- *          (required iff seg > 0; consumed by lr_gla_scan_bwd).
+ *   seg:   0, or a multiple of 64 and of chunk: then ckpt[s] receives the
+ *          state entering token s*seg, TRANSPOSED: ckpt is
+ *          [ceil(L/seg), B, H, V, K] fp32 (required iff seg > 0; consumed by
+ *          lr_gla_scan_bwd).  The transposed layout is the kernel's own
+ *          register order of the state (value columns outermost), which the
+ *          backward reads back directly; S0 and S_last keep [B, H, K, V].
+ *   workspace: optional, as in lr_ssd_scan (see lr_gla_scan_workspace_bytes).
  * No extra scaling of q is applied.
- * Supported: io = LR_BF16; K in {64, 128}; V % 64 == 0.
+ * Supported: io = LR_BF16 only (bf16 MFMA; fp32 I/O returns
+ * LR_E_UNSUPPORTED); K in {64, 128}; V % 64 == 0; H*K and H*V at most 2^25
+ * (32-bit row offsets, as in lr_ssd_scan).
  * ------------------------------------------------------------------------- */
 lr_status lr_gla_scan(lr_dtype io, int64_t B, int64_t L, int64_t H, int64_t K,
                       int64_t V, int64_t chunk, int64_t seg, const void* q,

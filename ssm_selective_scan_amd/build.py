@@ -64,5 +64,45 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# A build whose host code carries AddressSanitizer and UBSan (the device
+# code is compiled as usual, without them), for the CPU tests of the C ABI's
+# argument validation.
+HOSTCHECK = os.path.join(BUILD, "hostcheck")
+HOSTCHECK_LIB = os.path.join(HOSTCHECK, "liblr_hostcheck.so")
+SAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+       "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def asan_runtime() -> str:
+    """The clang ASan runtime matching hipcc, to preload into the process
+    that loads the sanitized library."""
+    import glob
+    hits = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not hits:
+        raise RuntimeError("no libclang_rt.asan-x86_64.so under /opt/rocm/llvm")
+    return hits[-1]
+
+
+def build_hostcheck() -> str:
+    os.makedirs(HOSTCHECK, exist_ok=True)
+    objs, jobs = [], []
+    with cf.ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+        for s in SOURCES:
+            obj = os.path.join(HOSTCHECK, s.replace(".hip", ".o"))
+            objs.append(obj)
+            jobs.append(ex.submit(_run, [HIPCC, *FLAGS, *SAN, "-c", os.path.join(CSRC, s),
+                                         "-o", obj]))
+        for j in jobs:
+            j.result()
+    tmp = HOSTCHECK_LIB + ".tmp"
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *SAN, "-Xarch_host",
+          "-shared-libasan", "-o", tmp, *objs])
+    os.replace(tmp, HOSTCHECK_LIB)
+    return HOSTCHECK_LIB
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "hostcheck" in sys.argv:
+        print(build_hostcheck())
+    else:
+        print(build(verbose="-v" in sys.argv))

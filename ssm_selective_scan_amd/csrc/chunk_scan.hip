@@ -42,6 +42,7 @@
 #include <atomic>
 
 #include "common.hpp"
+#include "launch.hpp"
 
 namespace lr {
 

@@ -16,6 +16,7 @@
 // CPL = 1 keeps more workgroups for small problems; wider groups are used
 // once they still fill the chip.
 #include "common.hpp"
+#include "launch.hpp"
 
 namespace lr {
 

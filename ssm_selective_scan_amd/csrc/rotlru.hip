@@ -17,6 +17,7 @@
 // per pair combines the 64 segment aggregates with a DPP complex pair scan,
 // and the carry between tiles stays in LDS.
 #include "common.hpp"
+#include "launch.hpp"
 
 namespace lr {
 

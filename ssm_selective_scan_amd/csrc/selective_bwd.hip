@@ -30,6 +30,7 @@
 #include <type_traits>
 
 #include "common.hpp"
+#include "launch.hpp"
 
 namespace lr {
 

@@ -34,6 +34,7 @@
 #include <utility>
 
 #include "common.hpp"
+#include "launch.hpp"
 
 namespace lr {
 

@@ -36,6 +36,7 @@
 //   reduce:   fixed-order fp32 sums of the partials over heads (and batch
 //             and segments for dA, dD), so results are deterministic.
 #include "common.hpp"
+#include "launch.hpp"
 
 namespace lr {
 

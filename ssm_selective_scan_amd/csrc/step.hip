@@ -12,6 +12,7 @@
 // allocates, synchronises or issues memset, so a loop of steps can be
 // captured into a HIP graph and replayed.
 #include "common.hpp"
+#include "launch.hpp"
 
 namespace lr {
 
