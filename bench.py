@@ -83,6 +83,34 @@ def time_launches(fn, sets, warmup, iters, settle_ms=30.0):
     return ms.mean() / 1e3, ms
 
 
+def graph_launch_time(fn, k=50, reps=20):
+    """Per-launch time (s) of fn when k launches run back to back from one
+    captured HIP graph (replayed `reps` times): the GPU-side cost of a launch
+    without host enqueue gaps, which dominate event timings of single
+    launches of a few microseconds."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(k):
+            fn()
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del graph
+    return e0.elapsed_time(e1) / 1e3 / (k * reps)
+
+
 # --------------------------------------------------------------------------
 # workloads
 # --------------------------------------------------------------------------
@@ -117,13 +145,25 @@ def measure_diag(warmup, iters):
     a, b = dev(g.t("a")), dev(g.t("b"))
     sets = [dict(a=a, b=b, h=torch.empty_like(a))]
     call = lambda s: lr.lr_diag_scan(s["a"], s["b"], h=s["h"])
-    t, _ = time_launches(call, sets, warmup, iters)
+    te, _ = time_launches(call, sets, warmup, iters)
+    t = graph_launch_time(lambda: call(sets[0]))
     p = g.params
     nb = 3 * p["B"] * p["L"] * p["D"] * 4
     return dict(workload=lrgen.NAMES[1], kernels=fingerprint(lambda: call(sets[0])), us=t * 1e6,
+                us_event_single_launch=te * 1e6, trivial_kernel_us=trivial_kernel_times(),
                 tokens_per_s=p["B"] * p["L"] / t, elems_per_s=p["B"] * p["L"] * p["D"] / t,
                 alg_bytes=nb, GBs=nb / t / 1e9, hbm_frac=nb / t / 1e9 / HBM_PEAK_GBS,
-                note="3 MB working set: launch/latency bound")
+                note="3 MB working set: launch/latency bound; us is the per-launch time of 50 "
+                     "launches back to back in one graph, us_event_single_launch brackets one "
+                     "launch with events (includes host enqueue gaps)")
+
+
+def trivial_kernel_times():
+    """The same two timings of a one-element torch kernel: the floor of each
+    method on this machine."""
+    z = torch.zeros(1, device="cuda")
+    te, _ = time_launches(lambda s: z.add_(1.0), [None], 50, 200, settle_ms=0)
+    return dict(us=graph_launch_time(lambda: z.add_(1.0)) * 1e6, us_event_single_launch=te * 1e6)
 
 
 def measure_ssd(warmup, iters):
@@ -226,19 +266,24 @@ def measure_rotlru(warmup, iters):
     g = lrgen.make(6)
     r, th, u = dev(g.t("r")), dev(g.t("theta")), dev(g.t("u"))
     h = torch.empty_like(u)
-    t, _ = time_launches(lambda s: lr.lr_rotlru_scan(r, th, u, h=h), [None], warmup, iters)
+    fcall = lambda: lr.lr_rotlru_scan(r, th, u, h=h)
+    te, _ = time_launches(lambda s: fcall(), [None], warmup, iters)
+    t = graph_launch_time(fcall)
     p = g.params
     nb = 2 * p["B"] * p["L"] * p["D"] * 4 + 2 * p["B"] * p["L"] * (p["D"] // 2) * 4
-    out = dict(workload=lrgen.NAMES[6], kernel="rotlru_scan_kernel", us=t * 1e6,
+    out = dict(workload=lrgen.NAMES[6], kernels=fingerprint(fcall), us=t * 1e6,
+               us_event_single_launch=te * 1e6,
                tokens_per_s=p["B"] * p["L"] / t, elems_per_s=p["B"] * p["L"] * p["D"] / t,
                alg_bytes=nb, GBs=nb / t / 1e9, hbm_frac=nb / t / 1e9 / HBM_PEAK_GBS,
                note="3 MB working set: launch/latency bound")
     dh = dev(lrgen.make(6, grads=True).t("dh"))
-    tb, _ = time_launches(lambda s: lr.lr_rotlru_scan_bwd(r, th, h, dh), [None], warmup, iters)
+    bcall = lambda: lr.lr_rotlru_scan_bwd(r, th, h, dh)
+    tbe, _ = time_launches(lambda s: bcall(), [None], warmup, iters)
+    tb = graph_launch_time(bcall)
     # read r, theta, h, dh; write dr, dtheta, du
     nbb = 3 * p["B"] * p["L"] * p["D"] * 4 + 4 * p["B"] * p["L"] * (p["D"] // 2) * 4
-    out.update(bwd_kernel="rotlru_scan_bwd_kernel", bwd_us=tb * 1e6, bwd_alg_bytes=nbb,
-               bwd_GBs=nbb / tb / 1e9)
+    out.update(bwd_kernels=fingerprint(bcall), bwd_us=tb * 1e6,
+               bwd_us_event_single_launch=tbe * 1e6, bwd_alg_bytes=nbb, bwd_GBs=nbb / tb / 1e9)
     return out
 
 
@@ -277,12 +322,16 @@ def measure_diag_bwd(warmup, iters):
     g = lrgen.make(1, grads=True)
     a, b, dh = dev(g.t("a")), dev(g.t("b")), dev(g.t("dh"))
     h, _ = lr.lr_diag_scan(a, b)
-    t, _ = time_launches(lambda s: lr.lr_diag_scan_bwd(a, h, dh), [None], warmup, iters)
+    call = lambda: lr.lr_diag_scan_bwd(a, h, dh)
+    te, _ = time_launches(lambda s: call(), [None], warmup, iters)
+    t = graph_launch_time(call)
     p = g.params
     nb = 5 * p["B"] * p["L"] * p["D"] * 4     # read a, h, dh; write da, db
-    return dict(workload=lrgen.NAMES[1] + "_bwd", kernel="diag_scan_bwd_kernel", us=t * 1e6,
+    return dict(workload=lrgen.NAMES[1] + "_bwd", kernels=fingerprint(call), us=t * 1e6,
+                us_event_single_launch=te * 1e6,
                 tokens_per_s=p["B"] * p["L"] / t, alg_bytes=nb, GBs=nb / t / 1e9,
-                hbm_frac=nb / t / 1e9 / HBM_PEAK_GBS, note="5 MB working set: launch/latency bound")
+                hbm_frac=nb / t / 1e9 / HBM_PEAK_GBS,
+                note="5 MB working set: launch/latency bound; timings as for diag")
 
 
 def measure_selective_bwd(warmup, iters):

@@ -25,6 +25,8 @@ constexpr int kDiagSeg = 8;          // steps per lane segment
 constexpr int kDiagThreads = 1024;   // 16 waves, 4 segments per wave
 constexpr int kDiagSegs = kDiagThreads / kDiagCT;  // 64 segments per tile
 constexpr int kDiagTile = kDiagSegs * kDiagSeg;    // 512 steps per tile
+// narrow tiles (few chains): channels and threads per workgroup
+constexpr int kDiagNarrowCT = 8, kDiagNarrowNT = 512;
 
 // CPL consecutive channels per lane, read and written as one CPL-wide vector
 // access (a 16-lane row of a wave then covers 16 * CPL channels of a token).
@@ -181,6 +183,108 @@ __global__ __launch_bounds__(kDiagThreads) void diag_scan_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Narrow tiles for problems with few chains (B * D small): CT = 2, 4 or 8
+// channels per workgroup instead of 16, so the grid has 2-8x more
+// workgroups, and 1024-step tiles (NT threads: NSEG = NT / CT lane segments
+// of SEG = 1024 / NSEG steps), so a sequence of up to 1024 tokens is one
+// pass of one load, two barriers and one store.  Lane = CT * segment + channel: the CT
+// channels of a token are adjacent lanes.  The segments of channel c are
+// joined by wave c: lane l folds its NSEG / 64 consecutive segments, then the
+// 64 lane totals go through the DPP (a, b)-pair scan.
+// ---------------------------------------------------------------------------
+template <typename T, int CT, int NT>
+__global__ __launch_bounds__(NT) void diag_scan_narrow_kernel(
+    const T* __restrict__ a, const T* __restrict__ b, const float* __restrict__ h0,
+    T* __restrict__ h, float* __restrict__ h_last, int64_t L, int64_t D) {
+  constexpr int NSEG = NT / CT;             // lane segments per tile
+  constexpr int SEG = 1024 / NSEG;          // steps per lane segment
+  constexpr int TL = NSEG * SEG;            // 1024 steps per tile
+  constexpr int SPL = NSEG / 64;            // segments per lane in the join
+  static_assert(CT >= 2 && CT <= 8 && TL == 1024 && SPL >= 1 && CT <= NT / 64, "narrow tile shape");
+  __shared__ float aggA[NSEG][CT];
+  __shared__ float aggB[NSEG][CT];
+  __shared__ float carry_in[NSEG][CT];
+  __shared__ float tile_carry[CT];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int ch = tid % CT;
+  const int seg = tid / CT;
+  const int64_t ntile = (D + CT - 1) / CT;
+  const int64_t bi = blockIdx.x / ntile;
+  const int64_t d0 = (blockIdx.x % ntile) * CT;
+  const int64_t d = d0 + ch;
+  const bool dok = d < D;
+
+  if (tid < CT) tile_carry[tid] = (h0 != nullptr && d0 + tid < D) ? h0[bi * D + d0 + tid] : 0.f;
+  __syncthreads();
+
+  const int64_t row = bi * L;
+  for (int64_t t0 = 0; t0 < L; t0 += TL) {
+    const int64_t ts = t0 + static_cast<int64_t>(seg) * SEG;
+    const int nok = dok ? static_cast<int>(L - ts < SEG ? (L - ts > 0 ? L - ts : 0) : SEG) : 0;
+    float av[SEG], bv[SEG];
+    {
+      const int64_t off0 = (row + ts) * D + d;
+#pragma unroll
+      for (int i = 0; i < SEG; ++i) {
+        av[i] = i < nok ? Io<T>::load(a + off0 + i * D) : 1.f;
+        bv[i] = i < nok ? Io<T>::load(b + off0 + i * D) : 0.f;
+      }
+    }
+    float P = 1.f, Hs = 0.f;
+#pragma unroll
+    for (int i = 0; i < SEG; ++i) {
+      Hs = fmaf(av[i], Hs, bv[i]);
+      P *= av[i];
+      av[i] = P;    // product of the segment's decays up to step i
+      bv[i] = Hs;   // state at step i from a zero start
+    }
+    aggA[seg][ch] = P;
+    aggB[seg][ch] = Hs;
+    __syncthreads();
+
+    if (wave < CT) {
+      const int c = wave;
+      float pa[SPL], pb[SPL];
+#pragma unroll
+      for (int j = 0; j < SPL; ++j) {
+        pa[j] = aggA[SPL * lane + j][c];
+        pb[j] = aggB[SPL * lane + j][c];
+      }
+      // the lane's segments folded in order, then the scan across lanes
+      float ta = pa[0], tb = pb[0];
+#pragma unroll
+      for (int j = 1; j < SPL; ++j) {
+        tb = fmaf(pa[j], tb, pb[j]);
+        ta *= pa[j];
+      }
+      float ia = ta, ib = tb;
+      wave_incl_pair_scan(ia, ib);
+      const float tc = tile_carry[c];
+      // state entering the lane's first segment, then each following one
+      float cin = fmaf(wave_shr1(ia, 1.f), tc, wave_shr1(ib, 0.f));
+#pragma unroll
+      for (int j = 0; j < SPL; ++j) {
+        carry_in[SPL * lane + j][c] = cin;
+        cin = fmaf(pa[j], cin, pb[j]);
+      }
+      if (lane == 63) tile_carry[c] = fmaf(ia, tc, ib);
+    }
+    __syncthreads();
+
+    const float cin = carry_in[seg][ch];
+    int64_t offs = (row + ts) * D + d;
+    asm volatile("" : "+v"(offs));
+#pragma unroll
+    for (int i = 0; i < SEG; ++i)
+      if (i < nok) Io<T>::store(h + offs + i * D, fmaf(av[i], cin, bv[i]));
+  }
+  __syncthreads();
+  if (h_last != nullptr && tid < CT && d0 + tid < D) h_last[bi * D + d0 + tid] = tile_carry[tid];
+}
+
+// ---------------------------------------------------------------------------
 // Backward.  For the loss sum_t <dh_t, h_t> + <dh_last, h_{L-1}> the adjoint
 // g_t = dl/dh_t obeys the same recurrence run backwards in time,
 //     g_{L-1} = dh_{L-1} + dh_last,   g_t = a_{t+1} g_{t+1} + dh_t,
@@ -304,6 +408,109 @@ __global__ __launch_bounds__(kDiagThreads) void diag_scan_bwd_kernel(
   }
 }
 
+// Backward with narrow tiles (see diag_scan_narrow_kernel): step u = L-1-t
+// of the reversed-time scan, 1024 steps per tile.
+template <typename T, int CT, int NT>
+__global__ __launch_bounds__(NT) void diag_scan_bwd_narrow_kernel(
+    const T* __restrict__ a, const T* __restrict__ h, const float* __restrict__ h0,
+    const T* __restrict__ dh, const float* __restrict__ dh_last, T* __restrict__ da,
+    T* __restrict__ db, float* __restrict__ dh0, int64_t L, int64_t D) {
+  constexpr int NSEG = NT / CT;
+  constexpr int SEG = 1024 / NSEG;
+  constexpr int TL = NSEG * SEG;
+  constexpr int SPL = NSEG / 64;
+  static_assert(CT >= 2 && CT <= 8 && TL == 1024 && SPL >= 1 && CT <= NT / 64, "narrow tile shape");
+  __shared__ float aggA[NSEG][CT];
+  __shared__ float aggB[NSEG][CT];
+  __shared__ float carry_in[NSEG][CT];
+  __shared__ float tile_carry[CT];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int ch = tid % CT;
+  const int seg = tid / CT;
+  const int64_t ntile = (D + CT - 1) / CT;
+  const int64_t bi = blockIdx.x / ntile;
+  const int64_t d0 = (blockIdx.x % ntile) * CT;
+  const int64_t d = d0 + ch;
+  const bool dok = d < D;
+
+  if (tid < CT) tile_carry[tid] = (dh_last != nullptr && d0 + tid < D) ? dh_last[bi * D + d0 + tid] : 0.f;
+  __syncthreads();
+
+  const int64_t row = bi * L;
+  for (int64_t u0 = 0; u0 < L; u0 += TL) {
+    const int64_t us = u0 + static_cast<int64_t>(seg) * SEG;
+    const int nok = dok ? static_cast<int>(L - us < SEG ? (L - us > 0 ? L - us : 0) : SEG) : 0;
+    const int64_t t_first = L - 1 - us;   // step i is token t_first - i
+    float av[SEG], bv[SEG];
+#pragma unroll
+    for (int i = 0; i < SEG; ++i) {
+      const int64_t t = t_first - i;
+      av[i] = (i < nok && t + 1 < L) ? Io<T>::load(a + (row + t + 1) * D + d) : 1.f;
+      bv[i] = i < nok ? Io<T>::load(dh + (row + t) * D + d) : 0.f;
+    }
+    float P = 1.f, Gs = 0.f;
+#pragma unroll
+    for (int i = 0; i < SEG; ++i) {
+      Gs = fmaf(av[i], Gs, bv[i]);
+      P *= av[i];
+      av[i] = P;
+      bv[i] = Gs;
+    }
+    aggA[seg][ch] = P;
+    aggB[seg][ch] = Gs;
+    __syncthreads();
+
+    if (wave < CT) {
+      const int c = wave;
+      float pa[SPL], pb[SPL];
+#pragma unroll
+      for (int j = 0; j < SPL; ++j) {
+        pa[j] = aggA[SPL * lane + j][c];
+        pb[j] = aggB[SPL * lane + j][c];
+      }
+      float ta = pa[0], tb = pb[0];
+#pragma unroll
+      for (int j = 1; j < SPL; ++j) {
+        tb = fmaf(pa[j], tb, pb[j]);
+        ta *= pa[j];
+      }
+      float ia = ta, ib = tb;
+      wave_incl_pair_scan(ia, ib);
+      const float tc = tile_carry[c];
+      float cin = fmaf(wave_shr1(ia, 1.f), tc, wave_shr1(ib, 0.f));
+#pragma unroll
+      for (int j = 0; j < SPL; ++j) {
+        carry_in[SPL * lane + j][c] = cin;
+        cin = fmaf(pa[j], cin, pb[j]);
+      }
+      if (lane == 63) tile_carry[c] = fmaf(ia, tc, ib);
+    }
+    __syncthreads();
+
+    const float cin = carry_in[seg][ch];
+    int64_t offt = (row + t_first) * D + d;
+    asm volatile("" : "+v"(offt));
+#pragma unroll
+    for (int i = 0; i < SEG; ++i) {
+      if (i < nok) {
+        const int64_t t = t_first - i;
+        const int64_t off = offt - i * D;
+        const float gt = fmaf(av[i], cin, bv[i]);
+        const float hp = t > 0 ? Io<T>::load(h + off - D) : (h0 != nullptr ? h0[bi * D + d] : 0.f);
+        Io<T>::store(db + off, gt);
+        Io<T>::store(da + off, gt * hp);
+      }
+    }
+  }
+  __syncthreads();
+  if (dh0 != nullptr && tid < CT && d0 + tid < D) {
+    const int64_t dd = d0 + tid;
+    dh0[bi * D + dd] = L > 0 ? Io<T>::load(a + row * D + dd) * tile_carry[tid] : tile_carry[tid];
+  }
+}
+
 template <typename T, int CPL>
 static hipError_t launch_diag_bwd_cpl(const void* a, const void* h, const float* h0,
                                       const void* dh, const float* dh_last, void* da, void* db,
@@ -322,6 +529,15 @@ template <typename T>
 hipError_t launch_diag_scan_bwd(const void* a, const void* h, const float* h0, const void* dh,
                                 const float* dh_last, void* da, void* db, float* dh0, int64_t B,
                                 int64_t L, int64_t D, hipStream_t stream) {
+  if (B * ((D + kDiagCT - 1) / kDiagCT) < 64) {   // few chains: narrow tiles
+    constexpr int CT = kDiagNarrowCT, NT = kDiagNarrowNT;
+    dim3 grid(static_cast<unsigned>(B * ((D + CT - 1) / CT)));
+    hipLaunchKernelGGL((diag_scan_bwd_narrow_kernel<T, CT, NT>), grid, dim3(NT), 0, stream,
+                       static_cast<const T*>(a), static_cast<const T*>(h), h0,
+                       static_cast<const T*>(dh), dh_last, static_cast<T*>(da),
+                       static_cast<T*>(db), dh0, L, D);
+    return hipGetLastError();
+  }
   if (D % 4 == 0 && B * (D / 64) >= 512)
     return launch_diag_bwd_cpl<T, 4>(a, h, h0, dh, dh_last, da, db, dh0, B, L, D, stream);
   if (D % 2 == 0 && B * (D / 32) >= 512)
@@ -348,12 +564,28 @@ static hipError_t launch_diag_cpl(const void* a, const void* b, const float* h0,
   return hipGetLastError();
 }
 
-// Wider channel tiles once they still give at least two workgroups per CU
-// (512 on 256 CUs); the vector accesses need D to be a multiple of the width.
+template <typename T, int CT, int NT>
+static hipError_t launch_diag_narrow(const void* a, const void* b, const float* h0, void* h,
+                                     float* h_last, int64_t B, int64_t L, int64_t D,
+                                     hipStream_t stream) {
+  dim3 grid(static_cast<unsigned>(B * ((D + CT - 1) / CT)));
+  hipLaunchKernelGGL((diag_scan_narrow_kernel<T, CT, NT>), grid, dim3(NT), 0, stream,
+                     static_cast<const T*>(a), static_cast<const T*>(b), h0,
+                     static_cast<T*>(h), h_last, L, D);
+  return hipGetLastError();
+}
+
+// Few chains (fewer than 64 workgroups of 16 channels): narrow tiles of
+// kDiagNarrowCT channels.  Otherwise 16 channel groups per workgroup, with
+// wider groups once they still give at least two workgroups per CU (512 on
+// 256 CUs); the vector accesses need D to be a multiple of the width.
 template <typename T>
 hipError_t launch_diag_scan(const void* a, const void* b, const float* h0, void* h,
                             float* h_last, int64_t B, int64_t L, int64_t D,
                             hipStream_t stream) {
+  if (B * ((D + kDiagCT - 1) / kDiagCT) < 64)
+    return launch_diag_narrow<T, kDiagNarrowCT, kDiagNarrowNT>(a, b, h0, h, h_last, B, L, D,
+                                                               stream);
   if (D % 4 == 0 && B * (D / 64) >= 512)
     return launch_diag_cpl<T, 4>(a, b, h0, h, h_last, B, L, D, stream);
   if (D % 2 == 0 && B * (D / 32) >= 512)

@@ -28,7 +28,7 @@ def kernels(fn):
 def test_dispatch_of_each_workload():
     g = lrgen.make(1)
     a, b = dev(g.t("a")), dev(g.t("b"))
-    assert kernels(lambda: lr.lr_diag_scan(a, b)) == ["lr::diag_scan_kernel<float, 1>"]
+    assert kernels(lambda: lr.lr_diag_scan(a, b)) == ["lr::diag_scan_narrow_kernel<float, 8, 512>"]
 
     g = lrgen.make(2, L=256)    # the headline's channels and batch; L does not pick the kernel
     T = {k: dev(g.t(k)) for k in ("x", "dt", "A", "B", "C", "Dskip")}
