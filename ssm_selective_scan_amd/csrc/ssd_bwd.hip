@@ -55,11 +55,13 @@ struct BwdArgs {
   const float* Dskip; const float* ckpt; const uint16_t* dy; const float* dh_last;
   const float* h0;                // SSD: [B][H][P][N] or null; replaces ckpt[0] when given
   uint16_t* dx; uint16_t* ddt; float* dA; uint16_t* dBm; uint16_t* dCm; float* dD; float* dh0;
-  uint16_t* dBpart; uint16_t* dCpart;   // [H][B][L][N] bf16 per-head partials
+  uint16_t* dBpart; uint16_t* dCpart;   // [B][L][H][N] bf16 per-head partials (heads
+                                        // innermost: the heads running together write
+                                        // one contiguous run per token)
   float* gseg;                    // [nseg][B][H][P][N]: Gamma_loc, then Gamma_out
   float* lam;                     // [nseg][B][H]
   float* dApart; float* dDpart;   // [B][H][nseg]
-  float* dgpart;                  // GLA: [H][B][L] log-gate gradient per 64-column slice
+  float* dgpart;                  // GLA: [B][L][H] log-gate gradient per 64-column slice
   uint16_t* dg;                   // GLA: [B][L][G] gate gradient
   int64_t B, L, H, G, N, seg, nseg;
 };
@@ -180,9 +182,12 @@ __global__ __launch_bounds__(256) void ssd_bwd_gloc_kernel(BwdArgs a) {
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int g4 = lane >> 4, c16 = lane & 15;
   const int64_t wid = xcd_remap(blockIdx.x, gridDim.x);
-  const int64_t sg = wid % a.nseg;
-  const int64_t bh = wid / a.nseg;
-  const int64_t h = bh % a.H, b = bh / a.H;
+  // heads vary fastest: the workgroups that run together on an XCD are the
+  // heads of one (batch row, segment), which read the same B and C rows
+  // (groups shared by heads), so those come from the XCD's L2
+  const int64_t h = wid % a.H;
+  const int64_t sg = (wid / a.H) % a.nseg;
+  const int64_t b = wid / (a.H * a.nseg);
   const int64_t grp = h / (a.H / a.G);
   const float Ah = MODE == kBwdGla ? 0.f : a.A[h];
   const int64_t ts0 = sg * a.seg;
@@ -323,9 +328,12 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int g4 = lane >> 4, c16 = lane & 15;
   const int64_t wid = xcd_remap(blockIdx.x, gridDim.x);
-  const int64_t sg = wid % a.nseg;
-  const int64_t bh = wid / a.nseg;
-  const int64_t h = bh % a.H, b = bh / a.H;
+  // heads vary fastest: the workgroups that run together on an XCD are the
+  // heads of one (batch row, segment), which read the same B and C rows
+  // (groups shared by heads), so those come from the XCD's L2
+  const int64_t h = wid % a.H;
+  const int64_t sg = (wid / a.H) % a.nseg;
+  const int64_t b = wid / (a.H * a.nseg);
   const int64_t grp = h / (a.H / a.G);
   const float Ah = DISC == kBwdGla ? 0.f : a.A[h];
   const float Dh = a.Dskip != nullptr ? a.Dskip[h] : 0.f;
@@ -633,7 +641,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
           f32x4 v;
 #pragma unroll
           for (int r = 0; r < 4; ++r) v[r] = ph * fmaf(se, d2[r], d1[r]);
-          *reinterpret_cast<u16x4*>(a.dBpart + ((h * a.B + b) * a.L + t0 + t) * NS + 16 * nt + 4 * g4) =
+          *reinterpret_cast<u16x4*>(a.dBpart + ((b * a.L + t0 + t) * a.H + h) * NS + 16 * nt + 4 * g4) =
               u16x4{f2bf(v[0]), f2bf(v[1]), f2bf(v[2]), f2bf(v[3])};
         }
       }
@@ -682,7 +690,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
           f32x4 v;
 #pragma unroll
           for (int r = 0; r < 4; ++r) v[r] = fmaf(e, d2[r], d1[r]);
-          *reinterpret_cast<u16x4*>(a.dCpart + ((h * a.B + b) * a.L + t0 + u) * NS + 16 * nt + 4 * g4) =
+          *reinterpret_cast<u16x4*>(a.dCpart + ((b * a.L + t0 + u) * a.H + h) * NS + 16 * nt + 4 * g4) =
               u16x4{f2bf(v[0]), f2bf(v[1]), f2bf(v[2]), f2bf(v[3])};
         }
       }
@@ -713,7 +721,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
       float ddt = 0.f, dAk = 0.f;
       if (DISC == kBwdGla) {
         // phi is constant: the log-gate gradient goes out per 64-column slice
-        if (k < nv) a.dgpart[(h * a.B + b) * a.L + t0 + k] = dlam;
+        if (k < nv) a.dgpart[(b * a.L + t0 + k) * a.H + h] = dlam;
       } else if (DISC == kBwdDirac) {   // phi = 1: no input-factor term
         ddt = dlam * Ah;
         dAk = dlam * dtv;
@@ -769,9 +777,9 @@ __global__ __launch_bounds__(256) void ssd_bwd_reduce_kernel(BwdArgs a, int64_t 
     const int64_t c8 = idx % n8;
     const int64_t g = (idx / n8) % a.G;
     const int64_t bt = idx / (n8 * a.G);     // b * L + t
-    const int64_t hstride = a.B * a.L * a.N;
-    const uint16_t* pb = a.dBpart + (g * hpg * a.B * a.L + bt) * a.N + 8 * c8;
-    const uint16_t* pc = a.dCpart + (g * hpg * a.B * a.L + bt) * a.N + 8 * c8;
+    const int64_t hstride = a.N;   // heads innermost
+    const uint16_t* pb = a.dBpart + (bt * a.H + g * hpg) * a.N + 8 * c8;
+    const uint16_t* pc = a.dCpart + (bt * a.H + g * hpg) * a.N + 8 * c8;
     float sb[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, sc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
     for (int64_t k = 0; k < hpg; ++k) {
@@ -819,7 +827,7 @@ __global__ __launch_bounds__(256) void gla_bwd_dg_kernel(BwdArgs a) {
   const int64_t grp = idx % a.G, bt = idx / a.G;
   const int64_t hpg = a.H / a.G;
   float s = 0.f;
-  for (int64_t hh = grp * hpg; hh < (grp + 1) * hpg; ++hh) s += a.dgpart[hh * a.B * a.L + bt];
+  for (int64_t hh = grp * hpg; hh < (grp + 1) * hpg; ++hh) s += a.dgpart[bt * a.H + hh];
   a.dg[idx] = f2bf(s / bf2f(a.dt[idx]));
 }
 
