@@ -73,6 +73,14 @@ __device__ __forceinline__ float gate_at(const BwdArgs& a, int64_t b, int64_t t,
   return MODE == kBwdGla ? bf2f(a.dt[(b * a.L + t) * a.G + grp]) : bf2f(a.dt[(b * a.L + t) * a.H + h]);
 }
 
+// The same gate as its raw bf16 bits: a prefetch keeps these, so that no
+// conversion next to the load makes the wave wait for it.
+template <int MODE>
+__device__ __forceinline__ uint16_t gate_raw(const BwdArgs& a, int64_t b, int64_t t, int64_t h,
+                                             int64_t grp) {
+  return MODE == kBwdGla ? a.dt[(b * a.L + t) * a.G + grp] : a.dt[(b * a.L + t) * a.H + h];
+}
+
 // Offset of state element idx = ((b H + h) P + p) N + n of the internal
 // [B][H][P][N] order in the caller's dh_last / dh0 layout: the same for SSD,
 // [B][G][N][V] (V = 64 H / G) for GLA.
@@ -313,6 +321,7 @@ struct MainLds {
   float rowTp[12][16], colTp[12][16];
   float toffp[4][kBQ], dphip[4][kBQ], up[4][kBQ];
   float uprevp[4];
+  float ddp[4];                // per-wave dD sums
 };
 
 // the 12 (u-tile j, t-tile i) tiles of a block: the 10 causal ones plus (0,1)
@@ -363,7 +372,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
   // (lane = token) so B is scaled to B_w while it is written to LDS
   constexpr int kRB = kBQ * (NS / 8) / 256, kRX = kBQ * (kBP / 8) / 256;
   u16x8 rb[kRB], rx[kRX];
-  float rg = 0.f;
+  uint16_t rg = 0;
   auto rfetch = [&](int j) {
     const int64_t t0 = ts0 + static_cast<int64_t>(j) * kBQ;
     const int nv = static_cast<int>((tse - t0) < kBQ ? (tse - t0) : kBQ);
@@ -379,7 +388,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
       rx[k] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
       if (r < nv) rx[k] = *reinterpret_cast<const u16x8*>(a.x + (b * a.L + t0 + r) * xrow + xoff + 8 * c);
     }
-    rg = lane < nv ? gate_at<DISC>(a, b, t0 + lane, h, grp) : 0.f;
+    rg = lane < nv ? gate_raw<DISC>(a, b, t0 + lane, h, grp) : uint16_t(0);
   };
   if (nb > 1) rfetch(0);
 #pragma unroll
@@ -390,7 +399,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
       const int64_t t0 = ts0 + static_cast<int64_t>(j) * kBQ;
       const int nv = static_cast<int>((tse - t0) < kBQ ? (tse - t0) : kBQ);
       float l2, ph, ek;
-      block_scalars<DISC>(rg, lane < nv, Ah, l2, ph, ek);
+      block_scalars<DISC>(bf2f(rg), lane < nv, Ah, l2, ph, ek);
       float sgc, sge;
       sign_scan<DISC>(ek, sgc, sge);
       const float c = wave_incl_sum(l2);
@@ -434,6 +443,39 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
   }
   float dA_acc = 0.f, dD_acc = 0.f;
 
+  // C, B, x, dy and the gate of one block of the backward sweep, loaded into
+  // registers one block ahead.  Lane = token; wave w takes 16-byte column
+  // chunks w, w + 4, ...
+  constexpr int kSB = kBQ * (NS / 8) / 256, kSX = kBQ * (kBP / 8) / 256;
+  u16x8 sc[kSB], sb[kSB], sx[kSX], sd[kSX];
+  uint16_t sgr = 0;
+  auto sfetch = [&](int j) {
+    const int64_t t0 = ts0 + static_cast<int64_t>(j) * kBQ;
+    const bool ok = lane < ((tse - t0) < kBQ ? (tse - t0) : kBQ);
+    sgr = ok ? gate_raw<DISC>(a, b, t0 + lane, h, grp) : uint16_t(0);
+    const int64_t bco = (b * a.L + t0 + lane) * bcrow + bcoff;
+    const int64_t xo = (b * a.L + t0 + lane) * xrow + xoff;
+#pragma unroll
+    for (int k = 0; k < kSB; ++k) {
+      sc[k] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      sb[k] = sc[k];
+      if (ok) {
+        sc[k] = *reinterpret_cast<const u16x8*>(a.Cm + bco + 8 * (w + 4 * k));
+        sb[k] = *reinterpret_cast<const u16x8*>(a.Bm + bco + 8 * (w + 4 * k));
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kSX; ++k) {
+      sx[k] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      sd[k] = sx[k];
+      if (ok) {
+        sx[k] = *reinterpret_cast<const u16x8*>(a.x + xo + 8 * (w + 4 * k));
+        sd[k] = *reinterpret_cast<const u16x8*>(a.dy + xo + 8 * (w + 4 * k));
+      }
+    }
+  };
+  sfetch(nb - 1);
+
 #pragma unroll 1
   for (int j = nb - 1; j >= 0; --j) {
     // the stash entry of this block (uniform switch keeps register indices static)
@@ -447,13 +489,13 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
     const int64_t t0 = ts0 + static_cast<int64_t>(j) * kBQ;
     const int nv = static_cast<int>((tse - t0) < kBQ ? (tse - t0) : kBQ);
 
-    // ---- stage the block.  Every staged row below is token `lane` of the
-    // block, so each wave computes the per-token scalars itself and scales B
-    // (by phi) and dy (by E) as they are written; wave 0 also keeps the
-    // scalars in LDS for the later phases.
+    // ---- stage the block from the registers sfetch filled.  Every staged
+    // row is token `lane` of the block, so each wave computes the per-token
+    // scalars itself and scales B (by phi) and dy (by E) as they are written;
+    // wave 0 also keeps the scalars in LDS for the later phases.
     {
       const bool ok = lane < nv;
-      const float dtv = ok ? gate_at<DISC>(a, b, t0 + lane, h, grp) : 0.f;
+      const float dtv = bf2f(sgr);   // 0 for masked tokens
       float l2, ph, ek;
       block_scalars<DISC>(dtv, ok, Ah, l2, ph, ek);
       ph = ok ? ph : 0.f;
@@ -471,37 +513,29 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
         sm.dtv[lane] = dtv;
         sm.ek[lane] = ek;
       }
-      for (int idx = tid; idx < kBQ * (NS / 8); idx += 256) {
-        const int r = idx & 63, cc = idx >> 6;   // r == lane
-        u16x8 vc = {0, 0, 0, 0, 0, 0, 0, 0}, vb = vc;
-        if (r < nv) {
-          const int64_t off = (b * a.L + t0 + r) * bcrow + bcoff + 8 * cc;
-          vc = *reinterpret_cast<const u16x8*>(a.Cm + off);
-          vb = *reinterpret_cast<const u16x8*>(a.Bm + off);
-        }
-        *reinterpret_cast<u16x8*>(sm.Cs + r * kLdN + 8 * cc) = vc;
-        *reinterpret_cast<u16x8*>(sm.Bs + r * kLdN + 8 * cc) = vb;
+#pragma unroll
+      for (int k = 0; k < kSB; ++k) {
+        const int cc = w + 4 * k;
+        *reinterpret_cast<u16x8*>(sm.Cs + lane * kLdN + 8 * cc) = sc[k];
+        *reinterpret_cast<u16x8*>(sm.Bs + lane * kLdN + 8 * cc) = sb[k];
         u16x8 pb;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) pb[i] = f2bf(bf2f(vb[i]) * ph);
-        *reinterpret_cast<u16x8*>(sm.pB + r * kLdN + 8 * cc) = pb;
+        for (int i = 0; i < 8; ++i) pb[i] = f2bf(bf2f(sb[k][i]) * ph);
+        *reinterpret_cast<u16x8*>(sm.pB + lane * kLdN + 8 * cc) = pb;
       }
-      for (int idx = tid; idx < kBQ * (kBP / 8); idx += 256) {
-        const int r = idx & 63, cc = idx >> 6;   // r == lane
-        u16x8 vx = {0, 0, 0, 0, 0, 0, 0, 0}, vd = vx;
-        if (r < nv) {
-          const int64_t off = (b * a.L + t0 + r) * xrow + xoff + 8 * cc;
-          vx = *reinterpret_cast<const u16x8*>(a.x + off);
-          vd = *reinterpret_cast<const u16x8*>(a.dy + off);
-        }
-        *reinterpret_cast<u16x8*>(sm.xs + r * kBLd + 8 * cc) = vx;
-        *reinterpret_cast<u16x8*>(sm.dys + r * kBLd + 8 * cc) = vd;
+#pragma unroll
+      for (int k = 0; k < kSX; ++k) {
+        const int cc = w + 4 * k;
+        *reinterpret_cast<u16x8*>(sm.xs + lane * kBLd + 8 * cc) = sx[k];
+        *reinterpret_cast<u16x8*>(sm.dys + lane * kBLd + 8 * cc) = sd[k];
         u16x8 de;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) de[i] = f2bf(bf2f(vd[i]) * el);
-        *reinterpret_cast<u16x8*>(sm.dyE + r * kBLd + 8 * cc) = de;
+        for (int i = 0; i < 8; ++i) de[i] = f2bf(bf2f(sd[k][i]) * el);
+        *reinterpret_cast<u16x8*>(sm.dyE + lane * kBLd + 8 * cc) = de;
       }
     }
+    // the next block's loads are in flight during this block's phases
+    if (j > 0) sfetch(j - 1);
     __syncthreads();
 
     // ---- decayed masks and the T sums
@@ -550,7 +584,10 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
     }
     __syncthreads();
 
-    // ---- recomputed C h_prev (for the c-gradient), dx, dphi, U, dD, U_prev
+    // ---- recomputed C h_prev (for the c-gradient), dx, dphi, U, dD, U_prev.
+    // The three products are formed transposed, [p][t] (lane: token
+    // 16 ti + c16, p rows 16 w + 4 g4 .. + 3), so that the sums over p are
+    // register adds plus one col4_sum, and x, dy and dx move 4 p at a time.
     {
       f32x4 yo[4], dxa[4], dxb[4];
 #pragma unroll
@@ -565,40 +602,48 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
         const bf16x8 gb = pack_dd(gacc[2 * kk], gacc[2 * kk + 1]);
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti) {
-          yo[ti] = mfma16x16x32(lds_tile_perm(sm.Cs, kLdN, 16 * ti, 32 * kk, lane), hb, yo[ti]);
-          dxb[ti] = mfma16x16x32(lds_tile_perm(sm.Bs, kLdN, 16 * ti, 32 * kk, lane), gb, dxb[ti]);
+          yo[ti] = mfma16x16x32(hb, lds_tile_perm(sm.Cs, kLdN, 16 * ti, 32 * kk, lane), yo[ti]);
+          dxb[ti] = mfma16x16x32(gb, lds_tile_perm(sm.Bs, kLdN, 16 * ti, 32 * kk, lane), dxb[ti]);
         }
       }
 #pragma unroll
       for (int ti = 0; ti < 4; ++ti) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          if (ks == 0 && ti >= 2) continue;
-          dxa[ti] = mfma16x16x32(lds_tile(sm.Mt, kBLd, 16 * ti, 32 * ks, lane),
-                                 lds_tile_tr(sm.dys, kBLd, 32 * ks, 16 * w, lane), dxa[ti]);
+          if (ks == 0 && ti >= 2) continue;   // Mp[u][t] = 0 for u < t
+          dxa[ti] = mfma16x16x32(lds_tile_tr(sm.dys, kBLd, 32 * ks, 16 * w, lane),
+                                 lds_tile(sm.Mt, kBLd, 16 * ti, 32 * ks, lane), dxa[ti]);
         }
       }
       float ddsum = 0.f;
+      const int pr = 16 * w + 4 * g4;   // this lane's 4 p rows
 #pragma unroll
       for (int ti = 0; ti < 4; ++ti) {
+        const int t = 16 * ti + c16;    // this lane's token
+        const u16x4 xv4 = *reinterpret_cast<const u16x4*>(sm.xs + t * kBLd + pr);
+        const u16x4 dy4 = *reinterpret_cast<const u16x4*>(sm.dys + t * kBLd + pr);
+        const float se = sm.sE[t], ph = sm.phi[t];
+        float toff = 0.f, dph = 0.f, uu = 0.f;
+        u16x4 o;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int t = 16 * ti + 4 * g4 + r;
-          const float xv = bf2f(sm.xs[t * kBLd + p]);
-          const float dyv = bf2f(sm.dys[t * kBLd + p]);
-          const float xb = dxb[ti][r] * sm.sE[t];
+          const float xv = bf2f(xv4[r]), dyv = bf2f(dy4[r]);
+          const float xb = dxb[ti][r] * se;
           const float gB = dxa[ti][r] + xb;
-          const float ph = sm.phi[t];
-          if (t < nv) a.dx[(b * a.L + t0 + t) * xrow + xoff + p] = f2bf(fmaf(ph, gB, Dh * dyv));
-          const float toff = row16_sum_last(sm.E[t] * yo[ti][r] * dyv);
-          const float dph = row16_sum_last(xv * gB);
-          const float uu = row16_sum_last(ph * xv * xb);
-          if (c16 == 15) {
-            sm.toffp[w][t] = toff;
-            sm.dphip[w][t] = dph;
-            sm.up[w][t] = uu;
-          }
-          ddsum += dyv * xv;
+          o[r] = f2bf(fmaf(ph, gB, Dh * dyv));
+          toff = fmaf(yo[ti][r], dyv, toff);
+          dph = fmaf(xv, gB, dph);
+          uu = fmaf(xv, xb, uu);
+          ddsum = fmaf(dyv, xv, ddsum);
+        }
+        if (t < nv) *reinterpret_cast<u16x4*>(a.dx + (b * a.L + t0 + t) * xrow + xoff + pr) = o;
+        toff = col4_sum(toff) * sm.E[t];
+        dph = col4_sum(dph);
+        uu = col4_sum(uu) * ph;
+        if (g4 == 0) {
+          sm.toffp[w][t] = toff;
+          sm.dphip[w][t] = dph;
+          sm.up[w][t] = uu;
         }
       }
       dD_acc += wave_sum(ddsum);
@@ -696,6 +741,12 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
       }
     }
 
+    // Every LDS tile of the block has been read once all waves are here; the
+    // phase below reads only per-token scalars and partial sums, which no
+    // other wave writes before the next block's dx phase, so waves 1-3 go on
+    // to stage the next block meanwhile.
+    __syncthreads();
+
     // ---- log-decay gradient -> ddt, dA (wave 0, lane = token)
     if (w == 0) {
       const int k = lane;
@@ -710,13 +761,14 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
       const float uu = sm.up[0][k] + sm.up[1][k] + sm.up[2][k] + sm.up[3][k];
       const float uprev = fast_exp2(sm.cum[kBQ - 1]) * (DISC == kBwdBilinear ? sm.sg[kBQ - 1] : 1.f) *
                           (sm.uprevp[0] + sm.uprevp[1] + sm.uprevp[2] + sm.uprevp[3]);
+      // reverse inclusive prefix sum dlam_k = sum_{j >= k} dcum_j, where the
+      // last token's dcum also carries uprev + sum(uu): that term enters every
+      // dlam_k, so it is added after the scan, and the two scans run side by side
+      const float dcum = rowT - colT + toff - uu;
       const float usum = wave_sum(uu);
-      float dcum = rowT - colT + toff - uu;
-      if (k == kBQ - 1) dcum += uprev + usum;
-      // reverse inclusive prefix sum: dlam_k = sum_{j >= k} dcum_j
       const float incl = wave_incl_sum(dcum);
       const float total = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(incl), 63));
-      const float dlam = total - incl + dcum;
+      const float dlam = (total - incl + dcum) + (uprev + usum);
       const float dtv = sm.dtv[k], ek = sm.ek[k], ph = sm.phi[k];
       float ddt = 0.f, dAk = 0.f;
       if (DISC == kBwdGla) {
@@ -747,16 +799,16 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
       }
       if (DISC != kBwdGla) {
         if (k < nv) a.ddt[(b * a.L + t0 + k) * a.H + h] = f2bf(ddt);
-        dA_acc += wave_sum(k < nv ? dAk : 0.f);
+        dA_acc += k < nv ? dAk : 0.f;   // per token; summed over the wave at the end
       }
     }
-    __syncthreads();
   }
+  dA_acc = wave_sum(dA_acc);
   if (tid == 0) a.dApart[(b * a.H + h) * a.nseg + sg] = dA_acc;
-  if (lane == 0) sm.uprevp[w] = dD_acc;
+  // own slots: wave 0 may still be reading uprevp in the last block's decay phase
+  if (lane == 0) sm.ddp[w] = dD_acc;
   __syncthreads();
-  if (tid == 0)
-    a.dDpart[(b * a.H + h) * a.nseg + sg] = sm.uprevp[0] + sm.uprevp[1] + sm.uprevp[2] + sm.uprevp[3];
+  if (tid == 0) a.dDpart[(b * a.H + h) * a.nseg + sg] = sm.ddp[0] + sm.ddp[1] + sm.ddp[2] + sm.ddp[3];
 }
 
 // ---------------------------------------------------------------------------
