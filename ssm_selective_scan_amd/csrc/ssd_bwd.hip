@@ -302,23 +302,24 @@ __global__ __launch_bounds__(256) void ssd_bwd_gcombine_kernel(BwdArgs a, int64_
 // main
 // ---------------------------------------------------------------------------
 template <int NS>
-struct MainLds {
+struct alignas(16) MainLds {
   static constexpr int kLdN = NS + 8;
   uint16_t Cs[kBQ * kLdN];     // C[u][n]
-  uint16_t Bs[kBQ * kLdN];     // B[t][n]
+  uint16_t Bs[kBQ * kLdN];     // B[t][n]                     (recompute: B_w[s][n])
   uint16_t xs[kBQ * kBLd];     // x[t][p]
   uint16_t dys[kBQ * kBLd];    // dy[u][p]
   uint16_t dyE[kBQ * kBLd];    // E_u dy[u][p]
-  uint16_t pB[kBQ * kLdN];     // phi_t B[t][n]               (recompute: B_w[s][n])
   uint16_t Mt[kBQ * kBLd];     // Mp[u][t] as [t][u]
-  uint16_t Wt[kBQ * kBLd];     // W[u][t] as [t][u]
+  uint16_t Wt[kBQ * kBLd];     // phi_t W[u][t] as [t][u]
   uint16_t Gs[kBP * kLdN];     // Gamma[p][n], then h_prev[p][n]
   // Operands that contract over tokens (or over p) are read from these
   // row-major tiles with the transposing LDS read (lds_tile_tr), so every
   // tile is written with 8- or 16-byte stores.
   float cum[kBQ], E[kBQ], sE[kBQ], phi[kBQ], dtv[kBQ], ek[kBQ];
   float sg[kBQ];               // sign of the decay product from the block start (bilinear)
-  float rowTp[12][16], colTp[12][16];
+  // T sums of the (u-tile j, t-tile i) tiles: rowT4[j][i][u % 16] over t,
+  // colT4[i][j][t % 16] over u; slots of tiles never formed stay zero
+  float rowT4[4][4][16], colT4[4][4][16];
   float toffp[4][kBQ], dphip[4][kBQ], up[4][kBQ];
   float uprevp[4];
   float ddp[4];                // per-wave dD sums
@@ -345,6 +346,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
   const int64_t b = wid / (a.H * a.nseg);
   const int64_t grp = h / (a.H / a.G);
   const float Ah = DISC == kBwdGla ? 0.f : a.A[h];
+  const float invA = DISC == kBwdZoh ? 1.f / Ah : 0.f;   // unused (series branch) when A = 0
   const float Dh = a.Dskip != nullptr ? a.Dskip[h] : 0.f;
   const int64_t ts0 = sg * a.seg;
   const int64_t tse = (ts0 + a.seg < a.L) ? ts0 + a.seg : a.L;
@@ -354,6 +356,41 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
   const int64_t bcrow = a.G * NS;
   const int64_t bcoff = grp * NS;
   const int p = 16 * w + c16;                  // this lane's p column
+  (&sm.rowT4[0][0][0])[tid] = 0.f;
+  (&sm.colT4[0][0][0])[tid] = 0.f;
+
+  // C, B, x, dy and the gate of one block of the backward sweep, loaded into
+  // registers one block ahead.  Lane = token; wave w takes 16-byte column
+  // chunks w, w + 4, ...
+  constexpr int kSB = kBQ * (NS / 8) / 256, kSX = kBQ * (kBP / 8) / 256;
+  u16x8 sc[kSB], sb[kSB], sx[kSX], sd[kSX];
+  uint16_t sgr = 0;
+  auto sfetch = [&](int j) {
+    const int64_t t0 = ts0 + static_cast<int64_t>(j) * kBQ;
+    const bool ok = lane < ((tse - t0) < kBQ ? (tse - t0) : kBQ);
+    sgr = ok ? gate_raw<DISC>(a, b, t0 + lane, h, grp) : uint16_t(0);
+    const int64_t bco = (b * a.L + t0 + lane) * bcrow + bcoff;
+    const int64_t xo = (b * a.L + t0 + lane) * xrow + xoff;
+#pragma unroll
+    for (int k = 0; k < kSB; ++k) {
+      sc[k] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      sb[k] = sc[k];
+      if (ok) {
+        sc[k] = *reinterpret_cast<const u16x8*>(a.Cm + bco + 8 * (w + 4 * k));
+        sb[k] = *reinterpret_cast<const u16x8*>(a.Bm + bco + 8 * (w + 4 * k));
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kSX; ++k) {
+      sx[k] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      sd[k] = sx[k];
+      if (ok) {
+        sx[k] = *reinterpret_cast<const u16x8*>(a.x + xo + 8 * (w + 4 * k));
+        sd[k] = *reinterpret_cast<const u16x8*>(a.dy + xo + 8 * (w + 4 * k));
+      }
+    }
+  };
+  sfetch(nb - 1);   // in flight during the recompute
 
   // ---- forward recompute of the block-entry states of this segment; they
   // are kept in registers as packed bf16 MFMA operands (hsb[j][kk] holds
@@ -412,7 +449,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
         u16x8 o;
 #pragma unroll
         for (int i = 0; i < 8; ++i) o[i] = f2bf(bf2f(rb[k][i]) * ws);
-        *reinterpret_cast<u16x8*>(sm.pB + r * kLdN + 8 * cc) = o;   // B_w
+        *reinterpret_cast<u16x8*>(sm.Bs + r * kLdN + 8 * cc) = o;   // B_w
       }
 #pragma unroll
       for (int k = 0; k < kRX; ++k) {
@@ -427,7 +464,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
         hacc[nt] *= dec;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
-          hacc[nt] = mfma16x16x32(lds_tile_tr(sm.pB, kLdN, 32 * ks, 16 * nt, lane),
+          hacc[nt] = mfma16x16x32(lds_tile_tr(sm.Bs, kLdN, 32 * ks, 16 * nt, lane),
                                   lds_tile_tr(sm.xs, kBLd, 32 * ks, 16 * w, lane), hacc[nt]);
       }
       __syncthreads();
@@ -443,38 +480,6 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
   }
   float dA_acc = 0.f, dD_acc = 0.f;
 
-  // C, B, x, dy and the gate of one block of the backward sweep, loaded into
-  // registers one block ahead.  Lane = token; wave w takes 16-byte column
-  // chunks w, w + 4, ...
-  constexpr int kSB = kBQ * (NS / 8) / 256, kSX = kBQ * (kBP / 8) / 256;
-  u16x8 sc[kSB], sb[kSB], sx[kSX], sd[kSX];
-  uint16_t sgr = 0;
-  auto sfetch = [&](int j) {
-    const int64_t t0 = ts0 + static_cast<int64_t>(j) * kBQ;
-    const bool ok = lane < ((tse - t0) < kBQ ? (tse - t0) : kBQ);
-    sgr = ok ? gate_raw<DISC>(a, b, t0 + lane, h, grp) : uint16_t(0);
-    const int64_t bco = (b * a.L + t0 + lane) * bcrow + bcoff;
-    const int64_t xo = (b * a.L + t0 + lane) * xrow + xoff;
-#pragma unroll
-    for (int k = 0; k < kSB; ++k) {
-      sc[k] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      sb[k] = sc[k];
-      if (ok) {
-        sc[k] = *reinterpret_cast<const u16x8*>(a.Cm + bco + 8 * (w + 4 * k));
-        sb[k] = *reinterpret_cast<const u16x8*>(a.Bm + bco + 8 * (w + 4 * k));
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < kSX; ++k) {
-      sx[k] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      sd[k] = sx[k];
-      if (ok) {
-        sx[k] = *reinterpret_cast<const u16x8*>(a.x + xo + 8 * (w + 4 * k));
-        sd[k] = *reinterpret_cast<const u16x8*>(a.dy + xo + 8 * (w + 4 * k));
-      }
-    }
-  };
-  sfetch(nb - 1);
 
 #pragma unroll 1
   for (int j = nb - 1; j >= 0; --j) {
@@ -491,8 +496,8 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
 
     // ---- stage the block from the registers sfetch filled.  Every staged
     // row is token `lane` of the block, so each wave computes the per-token
-    // scalars itself and scales B (by phi) and dy (by E) as they are written;
-    // wave 0 also keeps the scalars in LDS for the later phases.
+    // scalars itself and scales dy (by E) as it is written; wave 0 also keeps
+    // the scalars in LDS for the later phases.
     {
       const bool ok = lane < nv;
       const float dtv = bf2f(sgr);   // 0 for masked tokens
@@ -518,10 +523,6 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
         const int cc = w + 4 * k;
         *reinterpret_cast<u16x8*>(sm.Cs + lane * kLdN + 8 * cc) = sc[k];
         *reinterpret_cast<u16x8*>(sm.Bs + lane * kLdN + 8 * cc) = sb[k];
-        u16x8 pb;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) pb[i] = f2bf(bf2f(sb[k][i]) * ph);
-        *reinterpret_cast<u16x8*>(sm.pB + lane * kLdN + 8 * cc) = pb;
       }
 #pragma unroll
       for (int k = 0; k < kSX; ++k) {
@@ -564,7 +565,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
           const int u = u0 + r;
           float m = (u >= t) ? fast_exp2(sm.cum[u] - ct) : 0.f;
           if (DISC == kBwdBilinear) m *= st * sm.sg[u];
-          const float mp = s[r] * m, wv = rr[r] * m;
+          const float mp = s[r] * m, wv = rr[r] * m * pt;
           const float tv = mp * pt * rr[r];
           om[r] = f2bf(mp);
           ow[r] = f2bf(wv);
@@ -577,10 +578,10 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float rs = row16_sum_last(rsum[r]);
-        if (c16 == 15) sm.rowTp[tile][4 * g4 + r] = rs;
+        if (c16 == 15) sm.rowT4[tj][ti][4 * g4 + r] = rs;
       }
       const float cs = col4_sum(csum);
-      if (g4 == 0) sm.colTp[tile][c16] = cs;
+      if (g4 == 0) sm.colT4[ti][tj][c16] = cs;
     }
     __syncthreads();
 
@@ -658,7 +659,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
       if (lane == 0) sm.uprevp[w] = up;
     }
 
-    // ---- dB: Gamma to LDS, then phi_t (W^T C + sE_t x Gamma)
+    // ---- dB: Gamma to LDS, then (phi W)^T C + phi_t sE_t x Gamma
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
       *reinterpret_cast<u16x4*>(sm.Gs + p * kLdN + 16 * nt + 4 * g4) =
@@ -685,7 +686,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
           const float ph = sm.phi[t], se = sm.sE[t];
           f32x4 v;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = ph * fmaf(se, d2[r], d1[r]);
+          for (int r = 0; r < 4; ++r) v[r] = fmaf(ph * se, d2[r], d1[r]);
           *reinterpret_cast<u16x4*>(a.dBpart + ((b * a.L + t0 + t) * a.H + h) * NS + 16 * nt + 4 * g4) =
               u16x4{f2bf(v[0]), f2bf(v[1]), f2bf(v[2]), f2bf(v[3])};
         }
@@ -705,7 +706,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
     }
     __syncthreads();
 
-    // ---- dC: h_prev to LDS, then W (phi B) + E_u dy h_prev
+    // ---- dC: h_prev to LDS, then (phi W) B + E_u dy h_prev
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const u16x8 hv = __builtin_bit_cast(u16x8, hcur[nt >> 1]);
@@ -722,7 +723,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           if (ks == 1 && tj < 2) continue;
-          d1 = mfma16x16x32(lds_tile_tr(sm.pB, kLdN, 32 * ks, 16 * nt, lane),
+          d1 = mfma16x16x32(lds_tile_tr(sm.Bs, kLdN, 32 * ks, 16 * nt, lane),
                             lds_tile_tr(sm.Wt, kBLd, 32 * ks, 16 * tj, lane), d1);
         }
 #pragma unroll
@@ -752,9 +753,9 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
       const int k = lane;
       float rowT = 0.f, colT = 0.f;
 #pragma unroll
-      for (int tile = 0; tile < 12; ++tile) {
-        if (kTileJ[tile] == (k >> 4)) rowT += sm.rowTp[tile][k & 15];
-        if (kTileI[tile] == (k >> 4)) colT += sm.colTp[tile][k & 15];
+      for (int i = 0; i < 4; ++i) {
+        rowT += sm.rowT4[k >> 4][i][k & 15];
+        colT += sm.colT4[k >> 4][i][k & 15];
       }
       const float toff = sm.toffp[0][k] + sm.toffp[1][k] + sm.toffp[2][k] + sm.toffp[3][k];
       const float dph = sm.dphip[0][k] + sm.dphip[1][k] + sm.dphip[2][k] + sm.dphip[3][k];
@@ -793,7 +794,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
         const float lam = dtv * Ah;
         const float dphidA = fabsf(lam) < 1e-3f
                                  ? dtv * dtv * fmaf(lam, fmaf(lam, 1.f / 8.f, 1.f / 3.f), 0.5f)
-                                 : (dtv * ek - ph) / Ah;
+                                 : (dtv * ek - ph) * invA;
         ddt = fmaf(dlam, Ah, dph * ek);
         dAk = fmaf(dlam, dtv, dph * dphidA);
       }
