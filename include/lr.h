@@ -272,9 +272,11 @@ lr_status lr_ssd_scan_noalloc(lr_dtype io, lr_disc disc, int64_t B, int64_t L,
                               float* ckpt, void* stream);
 
 /* Workspace bytes needed by lr_ssd_scan_bwd for these sizes (0 on invalid
- * sizes).  The workspace holds per-head partial sums of dB and dC (bf16),
- * the adjoint state at segment boundaries and per-segment partials of dA,
- * dD (fp32). */
+ * sizes).  The workspace holds per-head partial sums of dB and dC (bf16)
+ * and the adjoint state at segment boundaries (fp32) for one slice of batch
+ * rows (the backward runs slice by slice; a slice holds the smallest number
+ * of rows that gives 1024 (head, segment) work items, or the whole batch),
+ * plus per-segment partials of dA, dD (fp32) for the whole batch. */
 size_t lr_ssd_scan_bwd_workspace_bytes(int64_t B, int64_t L, int64_t H,
                                        int64_t P, int64_t G, int64_t N,
                                        int64_t chunk, int64_t seg);
@@ -293,7 +295,12 @@ size_t lr_ssd_scan_bwd_workspace_bytes(int64_t B, int64_t L, int64_t H,
  *   dx:      [B, L, H, P] io      ddt: [B, L, H] io
  *   dBm, dCm: [B, L, G, N] io (summed over the heads of each group)
  *   dA: [H] fp32    dD: [H] fp32 or NULL    dh0: [B, H, P, N] fp32 or NULL
- *   workspace: device memory of at least lr_ssd_scan_bwd_workspace_bytes().
+ *   workspace: device memory of lr_ssd_scan_bwd_workspace_bytes() bytes;
+ *            a smaller one makes the backward run in smaller batch slices
+ *            (same results), down to one row per slice, for which
+ *            lr_ssd_scan_bwd_workspace_bytes(1, L, ...)
+ *            + 8 (B - 1) H ceil(L / seg) + 512 bytes suffice; below the
+ *            one-row size: LR_E_WORKSPACE.
  * Supported: as lr_ssd_scan, with P == 64 and seg in {64, 128, 192, 256};
  * every disc, bilinear with negative decays included (their signs are
  * tracked as in the forward).
@@ -340,9 +347,10 @@ lr_status lr_gla_scan(lr_dtype io, int64_t B, int64_t L, int64_t H, int64_t K,
 size_t lr_gla_scan_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t K,
                                    int64_t V, int64_t chunk);
 
-/* Workspace bytes needed by lr_gla_scan_bwd (0 on invalid sizes): fp32
- * partial sums of dk, dq and of the log-gate gradient per 64 columns of v,
- * and the adjoint state at segment boundaries. */
+/* Workspace bytes needed by lr_gla_scan_bwd (0 on invalid sizes): partial
+ * sums of dk, dq (bf16) and of the log-gate gradient (fp32) per 64 columns
+ * of v, and the adjoint state at segment boundaries (fp32), for one slice of
+ * batch rows as in lr_ssd_scan_bwd_workspace_bytes. */
 size_t lr_gla_scan_bwd_workspace_bytes(int64_t B, int64_t L, int64_t H,
                                        int64_t K, int64_t V, int64_t chunk,
                                        int64_t seg);
@@ -356,7 +364,10 @@ size_t lr_gla_scan_bwd_workspace_bytes(int64_t B, int64_t L, int64_t H,
  *   dout:  [B, L, H, V] io      dS_last: [B, H, K, V] fp32 or NULL (= 0)
  *   dq, dk: [B, L, H, K] io     dv: [B, L, H, V] io     dg: [B, L, H] io
  *   dS0:   [B, H, K, V] fp32 or NULL
- *   workspace: device memory of at least lr_gla_scan_bwd_workspace_bytes().
+ *   workspace: device memory of lr_gla_scan_bwd_workspace_bytes() bytes;
+ *            smaller down to one-row batch slices as in lr_ssd_scan_bwd
+ *            (lr_gla_scan_bwd_workspace_bytes(1, L, ...)
+ *            + 8 (B - 1) H (V / 64) ceil(L / seg) + 512 bytes suffice).
  * Supported: as lr_gla_scan, with seg in {64, 128, 192, 256}.
  * ------------------------------------------------------------------------- */
 lr_status lr_gla_scan_bwd(lr_dtype io, int64_t B, int64_t L, int64_t H,

@@ -283,14 +283,15 @@ lr_status lr_ssd_scan_bwd(lr_dtype io, lr_disc disc, int64_t B, int64_t L, int64
   if (!all_aligned({x, dt, A, Bm, Cm, Dskip, h0, ckpt, dy, dh_last, dx, ddt, dA, dBm, dCm, dD,
                     dh0, workspace}))
     return LR_E_ALIGN;
-  const size_t need = lr::ssd_bwd_workspace(B, L, H, P, G, N, seg);
+  // below the default size the backward runs in smaller batch slices
+  const size_t need = lr::ssd_bwd_workspace(B, L, H, P, G, N, seg, true);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LR_E_WORKSPACE;
   if (B * L == 0)
     return hip_status(lr::launch_ssd_bwd_empty(dA, dD, dh0, dh_last, H, B * H * P * N,
                                                static_cast<hipStream_t>(stream)));
   return hip_status(lr::launch_ssd_bwd(disc, x, dt, A, Bm, Cm, Dskip, h0, ckpt, dy, dh_last, dx, ddt,
-                                       dA, dBm, dCm, dD, dh0, workspace, B, L, H, P, G, N, seg,
-                                       static_cast<hipStream_t>(stream)));
+                                       dA, dBm, dCm, dD, dh0, workspace, workspace_bytes, B, L, H,
+                                       P, G, N, seg, static_cast<hipStream_t>(stream)));
 }
 
 // Checks shared by the GLA forward and backward.
@@ -357,7 +358,7 @@ lr_status lr_gla_scan_bwd(lr_dtype io, int64_t B, int64_t L, int64_t H, int64_t 
   if (B * L > 0 && any_null({q, k, v, g, ckpt, dout, dq, dk, dv, dg})) return LR_E_NULLPTR;
   if (!all_aligned({q, k, v, g, ckpt, dout, dS_last, dq, dk, dv, dg, dS0, workspace}))
     return LR_E_ALIGN;
-  const size_t need = lr::gla_bwd_workspace(B, L, H, K, V, seg);
+  const size_t need = lr::gla_bwd_workspace(B, L, H, K, V, seg, true);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LR_E_WORKSPACE;
   if (B * L == 0) {
     if (dS0 == nullptr || B == 0) return LR_OK;
@@ -365,7 +366,7 @@ lr_status lr_gla_scan_bwd(lr_dtype io, int64_t B, int64_t L, int64_t H, int64_t 
                                                static_cast<hipStream_t>(stream)));
   }
   return hip_status(lr::launch_gla_bwd(q, k, v, g, ckpt, dout, dS_last, dq, dk, dv, dg, dS0,
-                                       workspace, B, L, H, K, V, seg,
+                                       workspace, workspace_bytes, B, L, H, K, V, seg,
                                        static_cast<hipStream_t>(stream)));
 }
 

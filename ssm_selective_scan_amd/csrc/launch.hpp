@@ -43,13 +43,17 @@ size_t ssd_fwd_workspace(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N);
 size_t ssd_noalloc_scratch_bytes();
 hipError_t ssd_noalloc_scratch(void** out);
 size_t gla_fwd_workspace(int64_t B, int64_t L, int64_t H, int64_t K, int64_t V);
-size_t gla_bwd_workspace(int64_t B, int64_t L, int64_t H, int64_t K, int64_t V, int64_t seg);
+// Backward workspaces: the default size, or (smallest) the one for slices of
+// one batch row, below which the backward cannot run.
+size_t gla_bwd_workspace(int64_t B, int64_t L, int64_t H, int64_t K, int64_t V, int64_t seg,
+                         bool smallest = false);
 hipError_t launch_gla_bwd(const void* q, const void* k, const void* v, const void* g,
                           const float* ckpt, const void* dout, const float* dS_last, void* dq,
-                          void* dk, void* dv, void* dg, float* dS0, void* ws, int64_t B, int64_t L,
-                          int64_t H, int64_t K, int64_t V, int64_t seg, hipStream_t stream);
+                          void* dk, void* dv, void* dg, float* dS0, void* ws, size_t ws_bytes,
+                          int64_t B, int64_t L, int64_t H, int64_t K, int64_t V, int64_t seg,
+                          hipStream_t stream);
 size_t ssd_bwd_workspace(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N,
-                         int64_t seg);
+                         int64_t seg, bool smallest = false);
 bool ssd_bwd_supported(int64_t P, int64_t N, int64_t seg);
 hipError_t launch_ssd_bwd_empty(float* dA, float* dD, float* dh0, const float* dh_last, int64_t H,
                                 int64_t nstate, hipStream_t stream);
@@ -57,9 +61,9 @@ hipError_t launch_ssd_bwd(int disc, const void* x, const void* dt, const float* 
                           const void* Cm, const float* Dskip, const float* h0, const float* ckpt,
                           const void* dy,
                           const float* dh_last, void* dx, void* ddt, float* dA, void* dBm,
-                          void* dCm, float* dD, float* dh0, void* ws, int64_t B, int64_t L,
-                          int64_t H, int64_t P, int64_t G, int64_t N, int64_t seg,
-                          hipStream_t stream);
+                          void* dCm, float* dD, float* dh0, void* ws, size_t ws_bytes,
+                          int64_t B, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N,
+                          int64_t seg, hipStream_t stream);
 template <typename T>
 hipError_t launch_rotlru_scan(const void* r, const void* theta, const void* u, const float* h0,
                               void* h, float* h_last, int64_t B, int64_t L, int64_t D,

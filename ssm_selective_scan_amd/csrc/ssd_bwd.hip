@@ -64,17 +64,13 @@ struct BwdArgs {
   float* dgpart;                  // GLA: [B][L][H] log-gate gradient per 64-column slice
   uint16_t* dg;                   // GLA: [B][L][G] gate gradient
   int64_t B, L, H, G, N, seg, nseg;
+  int64_t ckB;                    // batch size of ckpt ([nseg][ckB][H][P][N]), the whole
+                                  // batch when the launches cover a slice of it
 };
 
-// Gate (SSD dt, GLA g) of token t of head h in group grp.
-template <int MODE>
-__device__ __forceinline__ float gate_at(const BwdArgs& a, int64_t b, int64_t t, int64_t h,
-                                         int64_t grp) {
-  return MODE == kBwdGla ? bf2f(a.dt[(b * a.L + t) * a.G + grp]) : bf2f(a.dt[(b * a.L + t) * a.H + h]);
-}
-
-// The same gate as its raw bf16 bits: a prefetch keeps these, so that no
-// conversion next to the load makes the wave wait for it.
+// Gate (SSD dt, GLA g) of token t of head h in group grp, as its raw bf16
+// bits: the prefetches keep these, so that no conversion next to the load
+// makes the wave wait for it.
 template <int MODE>
 __device__ __forceinline__ uint16_t gate_raw(const BwdArgs& a, int64_t b, int64_t t, int64_t h,
                                              int64_t grp) {
@@ -203,7 +199,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_gloc_kernel(BwdArgs a) {
   const int nb = static_cast<int>((tse - ts0 + kBQ - 1) / kBQ);
 
   u16x8 creg[kCC], dreg[kDC];
-  float gv = 0.f;   // gate of token `lane` of the block
+  uint16_t gv = 0;   // gate of token `lane` of the block (raw bf16: no wait at the load)
   auto fetch = [&](int j) {
     const int64_t t0 = ts0 + static_cast<int64_t>(j) * kBQ;
     const int nv = static_cast<int>((tse - t0) < kBQ ? (tse - t0) : kBQ);
@@ -219,7 +215,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_gloc_kernel(BwdArgs a) {
       dreg[k] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
       if (u < nv) dreg[k] = *reinterpret_cast<const u16x8*>(a.dy + ((b * a.L + t0 + u) * a.H + h) * kBP + 8 * c);
     }
-    gv = lane < nv ? gate_at<MODE>(a, b, t0 + lane, h, grp) : 0.f;
+    gv = lane < nv ? gate_raw<MODE>(a, b, t0 + lane, h, grp) : uint16_t(0);
   };
 
   f32x4 gacc[NT];
@@ -233,7 +229,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_gloc_kernel(BwdArgs a) {
     const int64_t t0 = ts0 + static_cast<int64_t>(j) * kBQ;
     const int nv = static_cast<int>((tse - t0) < kBQ ? (tse - t0) : kBQ);
     float l2, ph, ek;
-    block_scalars<MODE>(gv, lane < nv, Ah, l2, ph, ek);
+    block_scalars<MODE>(bf2f(gv), lane < nv, Ah, l2, ph, ek);
     float sgc, sge;
     sign_scan<MODE>(ek, sgc, sge);
     const float c = wave_incl_sum(l2);
@@ -400,64 +396,54 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
   {
     const float* cp = (sg == 0 && a.h0 != nullptr)
                           ? a.h0 + (b * a.H + h) * kBP * NS
-                          : a.ckpt + ((sg * a.B + b) * a.H + h) * kBP * NS;
+                          : a.ckpt + ((sg * a.ckB + b) * a.H + h) * kBP * NS;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) hacc[nt] = *reinterpret_cast<const f32x4*>(cp + p * NS + 16 * nt + 4 * g4);
   }
-  // B, x and the gate of the next recompute block, loaded into registers
-  // during the current block's MFMA; every wave scans the block's gates
-  // (lane = token) so B is scaled to B_w while it is written to LDS
-  constexpr int kRB = kBQ * (NS / 8) / 256, kRX = kBQ * (kBP / 8) / 256;
-  u16x8 rb[kRB], rx[kRX];
-  uint16_t rg = 0;
-  auto rfetch = [&](int j) {
-    const int64_t t0 = ts0 + static_cast<int64_t>(j) * kBQ;
-    const int nv = static_cast<int>((tse - t0) < kBQ ? (tse - t0) : kBQ);
+  // B, x and the gate of every recompute block, all loaded up front so that
+  // their latencies overlap.  Blocks before the last are full, and as in
+  // sfetch lane = token and wave w takes 16-byte column chunks w, w + 4, ...;
+  // every wave scans the block's gates itself, so B is scaled to B_w while
+  // it is written to LDS.
+  constexpr int kRJ = NBS > 1 ? NBS - 1 : 1;
+  u16x8 rb[kRJ][kSB], rx[kRJ][kSX];
+  uint16_t rg[kRJ];
 #pragma unroll
-    for (int k = 0; k < kRB; ++k) {
-      const int idx = tid + 256 * k, r = idx / (NS / 8), c = idx % (NS / 8);
-      rb[k] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      if (r < nv) rb[k] = *reinterpret_cast<const u16x8*>(a.Bm + (b * a.L + t0 + r) * bcrow + bcoff + 8 * c);
-    }
+  for (int j = 0; j + 1 < NBS; ++j) {
+    if (j + 1 < nb) {
+      const int64_t t = ts0 + static_cast<int64_t>(j) * kBQ + lane, tok = b * a.L + t;
+      rg[j] = gate_raw<DISC>(a, b, t, h, grp);
 #pragma unroll
-    for (int k = 0; k < kRX; ++k) {
-      const int idx = tid + 256 * k, r = idx >> 3, c = idx & 7;
-      rx[k] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      if (r < nv) rx[k] = *reinterpret_cast<const u16x8*>(a.x + (b * a.L + t0 + r) * xrow + xoff + 8 * c);
+      for (int k = 0; k < kSB; ++k)
+        rb[j][k] = *reinterpret_cast<const u16x8*>(a.Bm + tok * bcrow + bcoff + 8 * (w + 4 * k));
+#pragma unroll
+      for (int k = 0; k < kSX; ++k)
+        rx[j][k] = *reinterpret_cast<const u16x8*>(a.x + tok * xrow + xoff + 8 * (w + 4 * k));
     }
-    rg = lane < nv ? gate_raw<DISC>(a, b, t0 + lane, h, grp) : uint16_t(0);
-  };
-  if (nb > 1) rfetch(0);
+  }
 #pragma unroll
   for (int j = 0; j < NBS; ++j) {
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) hsb[j][kk] = pack_dd(hacc[2 * kk], hacc[2 * kk + 1]);
     if (j + 1 < nb) {
-      const int64_t t0 = ts0 + static_cast<int64_t>(j) * kBQ;
-      const int nv = static_cast<int>((tse - t0) < kBQ ? (tse - t0) : kBQ);
       float l2, ph, ek;
-      block_scalars<DISC>(bf2f(rg), lane < nv, Ah, l2, ph, ek);
+      block_scalars<DISC>(bf2f(rg[j]), true, Ah, l2, ph, ek);
       float sgc, sge;
       sign_scan<DISC>(ek, sgc, sge);
       const float c = wave_incl_sum(l2);
       const float cend = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), 63));
-      const float wsl = fast_exp2(cend - c) * (sge * sgc) * (lane < nv ? ph : 0.f);
+      const float ws = fast_exp2(cend - c) * (sge * sgc) * ph;
 #pragma unroll
-      for (int k = 0; k < kRB; ++k) {
-        const int idx = tid + 256 * k, r = idx / (NS / 8), cc = idx % (NS / 8);
-        const float ws = __shfl(wsl, r);
+      for (int k = 0; k < kSB; ++k) {
         u16x8 o;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) o[i] = f2bf(bf2f(rb[k][i]) * ws);
-        *reinterpret_cast<u16x8*>(sm.Bs + r * kLdN + 8 * cc) = o;   // B_w
+        for (int i = 0; i < 8; ++i) o[i] = f2bf(bf2f(rb[j][k][i]) * ws);
+        *reinterpret_cast<u16x8*>(sm.Bs + lane * kLdN + 8 * (w + 4 * k)) = o;   // B_w
       }
 #pragma unroll
-      for (int k = 0; k < kRX; ++k) {
-        const int idx = tid + 256 * k, r = idx >> 3, cc = idx & 7;
-        *reinterpret_cast<u16x8*>(sm.xs + r * kBLd + 8 * cc) = rx[k];
-      }
+      for (int k = 0; k < kSX; ++k)
+        *reinterpret_cast<u16x8*>(sm.xs + lane * kBLd + 8 * (w + 4 * k)) = rx[j][k];
       __syncthreads();
-      if (j + 2 < nb) rfetch(j + 1);
       const float dec = fast_exp2(cend) * sge;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
@@ -911,32 +897,57 @@ struct WsLayout {
   int64_t dB, dC, g, lam, dA, dD, dg, total;
 };
 
-// H: heads of 64 columns (for GLA, H * V / 64)
-static WsLayout ws_layout(int64_t B, int64_t L, int64_t H, int64_t N, int64_t seg, bool gla) {
+// The launches run over slices of bs batch rows: the per-token and per-state
+// partials in the workspace are sized for one slice, so the workspace stays
+// bounded as B grows.  By default a slice holds at least 1024 workgroups of
+// the main kernel (four per CU), or the whole batch.
+static int64_t bwd_slice(int64_t B, int64_t L, int64_t H, int64_t seg) {
+  const int64_t per_row = H * ((L + seg - 1) / seg);
+  const int64_t bs = (1024 + per_row - 1) / per_row;
+  return bs < B ? bs : B;
+}
+
+// H: heads of 64 columns (for GLA, H * V / 64).  dA and dD partials cover
+// the whole batch; everything else one slice of bs rows.
+static WsLayout ws_layout(int64_t B, int64_t L, int64_t H, int64_t N, int64_t seg, bool gla,
+                          int64_t bs) {
   const int64_t nseg = (L + seg - 1) / seg;
   WsLayout w;
   int64_t o = 0;
-  w.dB = o; o = align256(o + H * B * L * N * 2);
-  w.dC = o; o = align256(o + H * B * L * N * 2);
-  w.g = o; o = align256(o + nseg * B * H * kBP * N * 4);
-  w.lam = o; o = align256(o + nseg * B * H * 4);
+  w.dB = o; o = align256(o + H * bs * L * N * 2);
+  w.dC = o; o = align256(o + H * bs * L * N * 2);
+  w.g = o; o = align256(o + nseg * bs * H * kBP * N * 4);
+  w.lam = o; o = align256(o + nseg * bs * H * 4);
   w.dA = o; o = align256(o + B * H * nseg * 4);
   w.dD = o; o = align256(o + B * H * nseg * 4);
-  w.dg = o; o = align256(o + (gla ? H * B * L * 4 : 0));
+  w.dg = o; o = align256(o + (gla ? H * bs * L * 4 : 0));
   w.total = o;
   return w;
 }
 
-size_t ssd_bwd_workspace(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N,
-                         int64_t seg) {
-  (void)G;
-  if (P != kBP || seg > 256 || B * L == 0) return 0;
-  return static_cast<size_t>(ws_layout(B, L, H, N, seg, false).total);
+// The largest slice (at most the default one) whose layout fits in ws_bytes;
+// 0 when not even one row fits.
+static int64_t bwd_slice_fit(int64_t B, int64_t L, int64_t H, int64_t N, int64_t seg, bool gla,
+                             size_t ws_bytes) {
+  for (int64_t bs = bwd_slice(B, L, H, seg); bs >= 1; --bs)
+    if (static_cast<size_t>(ws_layout(B, L, H, N, seg, gla, bs).total) <= ws_bytes) return bs;
+  return 0;
 }
 
-size_t gla_bwd_workspace(int64_t B, int64_t L, int64_t H, int64_t K, int64_t V, int64_t seg) {
+size_t ssd_bwd_workspace(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N,
+                         int64_t seg, bool smallest) {
+  (void)G;
+  if (P != kBP || seg > 256 || B * L == 0) return 0;
+  const int64_t bs = smallest ? 1 : bwd_slice(B, L, H, seg);
+  return static_cast<size_t>(ws_layout(B, L, H, N, seg, false, bs).total);
+}
+
+size_t gla_bwd_workspace(int64_t B, int64_t L, int64_t H, int64_t K, int64_t V, int64_t seg,
+                         bool smallest) {
   if (V % kBP != 0 || seg > 256 || B * L == 0) return 0;
-  return static_cast<size_t>(ws_layout(B, L, H * (V / kBP), K, seg, true).total);
+  const int64_t Hs = H * (V / kBP);
+  const int64_t bs = smallest ? 1 : bwd_slice(B, L, Hs, seg);
+  return static_cast<size_t>(ws_layout(B, L, Hs, K, seg, true, bs).total);
 }
 
 bool ssd_bwd_supported(int64_t P, int64_t N, int64_t seg) {
@@ -950,10 +961,14 @@ static void launch_main(const BwdArgs& a, int64_t nwg, int nbs, hipStream_t s) {
   else hipLaunchKernelGGL((ssd_bwd_main_kernel<MODE, NS, 4>), dim3(nwg), dim3(256), 0, s, a);
 }
 
-// The four launches (plus the gate reduction for GLA) on filled-in args.
+// The launches on filled-in args: per slice of batch rows gloc, gcombine,
+// main and the dB/dC reduction (plus the gate reduction for GLA), each on
+// pointers advanced to the slice's first row; then dA, dD over the batch.
 template <int MODE>
-static hipError_t launch_bwd(BwdArgs a, void* ws, hipStream_t stream) {
-  const WsLayout lay = ws_layout(a.B, a.L, a.H, a.N, a.seg, MODE == kBwdGla);
+static hipError_t launch_bwd(BwdArgs a, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const int64_t bs = bwd_slice_fit(a.B, a.L, a.H, a.N, a.seg, MODE == kBwdGla, ws_bytes);
+  if (bs < 1) return hipErrorInvalidValue;   // the entry points check the size first
+  const WsLayout lay = ws_layout(a.B, a.L, a.H, a.N, a.seg, MODE == kBwdGla, bs);
   char* base = static_cast<char*>(ws);
   a.dBpart = reinterpret_cast<uint16_t*>(base + lay.dB);
   a.dCpart = reinterpret_cast<uint16_t*>(base + lay.dC);
@@ -963,21 +978,43 @@ static hipError_t launch_bwd(BwdArgs a, void* ws, hipStream_t stream) {
   a.dDpart = reinterpret_cast<float*>(base + lay.dD);
   a.dgpart = reinterpret_cast<float*>(base + lay.dg);
   a.nseg = (a.L + a.seg - 1) / a.seg;
-  const int64_t nwg = a.B * a.H * a.nseg;
-  if (a.N == 128) hipLaunchKernelGGL((ssd_bwd_gloc_kernel<MODE, 128>), dim3(nwg), dim3(256), 0, stream, a);
-  else hipLaunchKernelGGL((ssd_bwd_gloc_kernel<MODE, 64>), dim3(nwg), dim3(256), 0, stream, a);
+  a.ckB = a.B;
   const int64_t PN = kBP * a.N;
-  hipLaunchKernelGGL(ssd_bwd_gcombine_kernel<MODE>, dim3((a.B * a.H * PN + 255) / 256), dim3(256), 0,
-                     stream, a, PN);
   const int nbs = static_cast<int>(a.seg / kBQ);
-  if (a.N == 128) launch_main<MODE, 128>(a, nwg, nbs, stream);
-  else launch_main<MODE, 64>(a, nwg, nbs, stream);
-  const int64_t red = (a.B * a.L * a.G * (a.N / 8) + 255) / 256;
-  hipLaunchKernelGGL(ssd_bwd_reduce_kernel, dim3(red + (a.H + 3) / 4), dim3(256), 0, stream, a, red);
-  if (MODE == kBwdGla) {
-    const int64_t nd = (a.B * a.L * a.G + 255) / 256;
-    hipLaunchKernelGGL(gla_bwd_dg_kernel, dim3(nd), dim3(256), 0, stream, a);
+  for (int64_t b0 = 0; b0 < a.B; b0 += bs) {
+    BwdArgs s = a;
+    s.B = (a.B - b0) < bs ? (a.B - b0) : bs;
+    const int64_t xr = b0 * a.L * a.H * kBP;   // x, dy, dx rows of the slice
+    const int64_t gr = b0 * a.L;               // tokens before the slice
+    const int64_t st = b0 * a.H * PN;          // state elements before the slice
+    s.x += xr; s.dy += xr; s.dx += xr;
+    s.dt += gr * (MODE == kBwdGla ? a.G : a.H);
+    if (s.ddt != nullptr) s.ddt += gr * a.H;
+    s.Bm += gr * a.G * a.N; s.Cm += gr * a.G * a.N;
+    s.dBm += gr * a.G * a.N; s.dCm += gr * a.G * a.N;
+    if (s.dg != nullptr) s.dg += gr * a.G;
+    s.ckpt += st;
+    if (s.h0 != nullptr) s.h0 += st;
+    if (s.dh_last != nullptr) s.dh_last += st;
+    if (s.dh0 != nullptr) s.dh0 += st;
+    s.dApart += b0 * a.H * a.nseg;
+    s.dDpart += b0 * a.H * a.nseg;
+    const int64_t nwg = s.B * s.H * s.nseg;
+    if (s.N == 128) hipLaunchKernelGGL((ssd_bwd_gloc_kernel<MODE, 128>), dim3(nwg), dim3(256), 0, stream, s);
+    else hipLaunchKernelGGL((ssd_bwd_gloc_kernel<MODE, 64>), dim3(nwg), dim3(256), 0, stream, s);
+    hipLaunchKernelGGL(ssd_bwd_gcombine_kernel<MODE>, dim3((s.B * s.H * PN + 255) / 256), dim3(256), 0,
+                       stream, s, PN);
+    if (s.N == 128) launch_main<MODE, 128>(s, nwg, nbs, stream);
+    else launch_main<MODE, 64>(s, nwg, nbs, stream);
+    const int64_t red = (s.B * s.L * s.G * (s.N / 8) + 255) / 256;
+    hipLaunchKernelGGL(ssd_bwd_reduce_kernel, dim3(red), dim3(256), 0, stream, s, red);
+    if (MODE == kBwdGla) {
+      const int64_t nd = (s.B * s.L * s.G + 255) / 256;
+      hipLaunchKernelGGL(gla_bwd_dg_kernel, dim3(nd), dim3(256), 0, stream, s);
+    }
   }
+  if (a.dA != nullptr)
+    hipLaunchKernelGGL(ssd_bwd_reduce_kernel, dim3((a.H + 3) / 4), dim3(256), 0, stream, a, int64_t(0));
   return hipGetLastError();
 }
 
@@ -985,9 +1022,9 @@ hipError_t launch_ssd_bwd(int disc, const void* x, const void* dt, const float* 
                           const void* Cm, const float* Dskip, const float* h0, const float* ckpt,
                           const void* dy,
                           const float* dh_last, void* dx, void* ddt, float* dA, void* dBm,
-                          void* dCm, float* dD, float* dh0, void* ws, int64_t B, int64_t L,
-                          int64_t H, int64_t P, int64_t G, int64_t N, int64_t seg,
-                          hipStream_t stream) {
+                          void* dCm, float* dD, float* dh0, void* ws, size_t ws_bytes,
+                          int64_t B, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N,
+                          int64_t seg, hipStream_t stream) {
   (void)P;
   if (B * L == 0) return hipSuccess;
   BwdArgs a = {};
@@ -999,16 +1036,17 @@ hipError_t launch_ssd_bwd(int disc, const void* x, const void* dt, const float* 
   a.dBm = static_cast<uint16_t*>(dBm); a.dCm = static_cast<uint16_t*>(dCm); a.dD = dD; a.dh0 = dh0;
   a.B = B; a.L = L; a.H = H; a.G = G; a.N = N; a.seg = seg;
   // disc holds the public discretisation code (ZOH 0, Euler 1, bilinear 2, dirac 3)
-  if (disc == kBwdEuler) return launch_bwd<kBwdEuler>(a, ws, stream);
-  if (disc == kBwdDirac) return launch_bwd<kBwdDirac>(a, ws, stream);
-  if (disc == 2) return launch_bwd<kBwdBilinear>(a, ws, stream);
-  return launch_bwd<kBwdZoh>(a, ws, stream);
+  if (disc == kBwdEuler) return launch_bwd<kBwdEuler>(a, ws, ws_bytes, stream);
+  if (disc == kBwdDirac) return launch_bwd<kBwdDirac>(a, ws, ws_bytes, stream);
+  if (disc == 2) return launch_bwd<kBwdBilinear>(a, ws, ws_bytes, stream);
+  return launch_bwd<kBwdZoh>(a, ws, ws_bytes, stream);
 }
 
 hipError_t launch_gla_bwd(const void* q, const void* k, const void* v, const void* g,
                           const float* ckpt, const void* dout, const float* dS_last, void* dq,
-                          void* dk, void* dv, void* dg, float* dS0, void* ws, int64_t B, int64_t L,
-                          int64_t H, int64_t K, int64_t V, int64_t seg, hipStream_t stream) {
+                          void* dk, void* dv, void* dg, float* dS0, void* ws, size_t ws_bytes,
+                          int64_t B, int64_t L, int64_t H, int64_t K, int64_t V, int64_t seg,
+                          hipStream_t stream) {
   if (B * L == 0) return hipSuccess;
   BwdArgs a = {};
   a.x = static_cast<const uint16_t*>(v); a.dt = static_cast<const uint16_t*>(g); a.A = nullptr;
@@ -1018,7 +1056,7 @@ hipError_t launch_gla_bwd(const void* q, const void* k, const void* v, const voi
   a.dBm = static_cast<uint16_t*>(dk); a.dCm = static_cast<uint16_t*>(dq); a.dD = nullptr; a.dh0 = dS0;
   a.dg = static_cast<uint16_t*>(dg);
   a.B = B; a.L = L; a.H = H * (V / kBP); a.G = H; a.N = K; a.seg = seg;
-  return launch_bwd<kBwdGla>(a, ws, stream);
+  return launch_bwd<kBwdGla>(a, ws, ws_bytes, stream);
 }
 
 }  // namespace lr

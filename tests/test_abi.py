@@ -285,3 +285,24 @@ def test_rotlru_bwd_validation(L):
     assert rb(h=MIS) == ALIGN
     assert rb(dh0=MIS) == ALIGN
     assert rb(B=0, r=None, th=None, h=None, dh=None, dr=None, dth=None, du=None) == OK
+
+
+def test_bwd_workspace_batch_slices(L):
+    # B=4, L=8192, H=32, P=64, N=128, seg 256: 1024 (head, segment) items per
+    # batch row, so the backward runs one row at a time and its workspace holds
+    # one row's partials plus the whole batch's dA/dD partials (4 KiB per row)
+    full = L.lr_ssd_scan_bwd_workspace_bytes(4, 8192, 32, 64, 1, 128, 64, 256)
+    one = L.lr_ssd_scan_bwd_workspace_bytes(1, 8192, 32, 64, 1, 128, 64, 256)
+    assert full <= 200 * 2 ** 20
+    assert full - one == 2 * 3 * 32 * 32 * 4
+    gla = L.lr_gla_scan_bwd_workspace_bytes(8, 4096, 16, 128, 128, 64, 256)
+    assert gla == (L.lr_gla_scan_bwd_workspace_bytes(2, 4096, 16, 128, 128, 64, 256)
+                   + 2 * 6 * 32 * 16 * 4)
+    # small problems fit in one slice: the workspace grows with B
+    w1 = L.lr_ssd_scan_bwd_workspace_bytes(1, 200, 2, 64, 1, 128, 64, 64)
+    w3 = L.lr_ssd_scan_bwd_workspace_bytes(3, 200, 2, 64, 1, 128, 64, 64)
+    assert w3 > 2 * w1
+    # below the one-row size the call is refused before any launch
+    args = [1, 0, 3, 200, 2, 64, 1, 128, 64, 64, P, P, P, P, P, None, None, P, P, None,
+            P, P, P, P, P, None, None]
+    assert L.lr_ssd_scan_bwd(*args, P, w1 - 1, None) == WS

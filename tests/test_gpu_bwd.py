@@ -135,3 +135,42 @@ def test_ssd_fwd_bwd_full_size_linearity():
         print(f"<dy, y({name}=probe)> = {lhs:.6e}, <d{name}, probe> = {rhs:.6e}, "
               f"|diff| / noise floor = {err:.3e}", flush=True)
         assert err <= TOL["bf16"], name
+
+
+def _one_row_ws(B, L, H, P, G, N, seg):
+    nseg = (L + seg - 1) // seg
+    return lr.lr_ssd_scan_bwd_workspace_bytes(1, L, H, P, G, N, 64, seg) + 8 * (B - 1) * H * nseg + 512
+
+
+@pytest.mark.parametrize("disc", ["zoh", "bilinear"])
+def test_ssd_bwd_batch_slices_bit_identical(disc):
+    """A workspace for one-row batch slices runs the backward slice by slice
+    (one launch sequence per row); every gradient equals the one-pass result
+    bit for bit, and (ZOH) the one-pass result matches the oracle."""
+    B, L, H, G, N, seg = 3, 200, 2, 1, 128, 64
+    print(f"ssd bwd batch slices disc={disc} B={B} L={L} H={H}", flush=True)
+    g = lrgen.make(5, B=B, L=L, H=H, G=G, N=N, seg=seg)
+    h0 = lrgen.state_normal((B, H, 64, N), 5, tensor_id=21, std=0.3)
+    dhl = lrgen.state_normal((B, H, 64, N), 5, tensor_id=22, std=0.3)
+    T = {k: dev(g.t(k)) for k in ("x", "dt", "A", "B", "C", "Dskip", "dy")}
+    h0d, dhld = dev(h0, "f32"), dev(dhl, "f32")
+    _, _, ck = lr.lr_ssd_scan(T["x"], T["dt"], T["A"], T["B"], T["C"], T["Dskip"], h0d,
+                              disc=disc, seg=seg, want_last=True)
+    args = (T["x"], T["dt"], T["A"], T["B"], T["C"], T["Dskip"], h0d, ck, T["dy"], dhld)
+    full = lr.lr_ssd_scan_bwd(*args, disc=disc, seg=seg, want_dh0=True)
+    small = _one_row_ws(B, L, H, 64, G, N, seg)
+    assert small < lr.lr_ssd_scan_bwd_workspace_bytes(B, L, H, 64, G, N, 64, seg)
+    ws = torch.empty(small, device="cuda", dtype=torch.uint8)
+    part = lr.lr_ssd_scan_bwd(*args, disc=disc, seg=seg, workspace=ws, want_dh0=True)
+    torch.cuda.synchronize()
+    for k in ("dx", "ddt", "dA", "dB", "dC", "dD", "dh0"):
+        assert torch.equal(full[k], part[k]), k
+    if disc == "zoh":   # (bilinear parity: test_gpu_disc.py)
+        ref = oracle.ssd_scan_bwd(g["x"], g["dt"], g["A"], g["B"], g["C"], g["Dskip"], h0,
+                                  g["dy"], dhl, disc)
+        for k in ("dx", "ddt", "dA", "dB", "dC", "dD", "dh0"):
+            check(k, full[k], ref[k], TOL["bf16"])
+    one_row = lr.lr_ssd_scan_bwd_workspace_bytes(1, L, H, 64, G, N, 64, seg)
+    with pytest.raises(lr.LrError, match="LR_E_WORKSPACE"):
+        lr.lr_ssd_scan_bwd(*args, disc=disc, seg=seg, want_dh0=True,
+                           workspace=torch.empty(one_row // 2, device="cuda", dtype=torch.uint8))

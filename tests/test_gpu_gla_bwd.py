@@ -80,3 +80,25 @@ def test_gla_fwd_bwd_full_size_sampled():
     r = oracle.gla_scan_bwd(g["q"][sfx], g["k"][sfx], g["v"][sfx], g["g"][sfx], Spre, g["do"][sfx])
     for name in ("dq", "dk", "dv", "dg"):
         check(f"{name}[b=0, last 256]", host(gr[name][sfx]), r[name], TOL["bf16"])
+
+
+def test_gla_bwd_batch_slices_bit_identical():
+    """One-row batch slices (a workspace below the default size) give the
+    one-pass gradients bit for bit."""
+    B, L, H, K, V, seg = 3, 200, 2, 128, 128, 64
+    print(f"gla bwd batch slices B={B} L={L} H={H} K={K} V={V}", flush=True)
+    g = lrgen.make(4, B=B, L=L, H=H, K=K, V=V, grads=True)
+    dSl = lrgen.state_normal((B, H, K, V), 4, tensor_id=22, std=0.3)
+    T = {k: dev(g.t(k)) for k in ("q", "k", "v", "g", "do")}
+    _, _, ck = lr.lr_gla_scan(T["q"], T["k"], T["v"], T["g"], seg=seg, want_last=True)
+    args = (T["q"], T["k"], T["v"], T["g"], ck, T["do"], dev(dSl, "f32"))
+    full = lr.lr_gla_scan_bwd(*args, seg=seg, want_dS0=True)
+    nseg = (L + seg - 1) // seg
+    small = (lr.lr_gla_scan_bwd_workspace_bytes(1, L, H, K, V, 64, seg)
+             + 8 * (B - 1) * H * (V // 64) * nseg + 512)
+    assert small < lr.lr_gla_scan_bwd_workspace_bytes(B, L, H, K, V, 64, seg)
+    part = lr.lr_gla_scan_bwd(*args, seg=seg, want_dS0=True,
+                              workspace=torch.empty(small, device="cuda", dtype=torch.uint8))
+    torch.cuda.synchronize()
+    for k in ("dq", "dk", "dv", "dg", "dS0"):
+        assert torch.equal(full[k], part[k]), k
