@@ -7,10 +7,13 @@
 //    (IBM Research blog "K-Search for MLX", section "A 20x faster prefill:
 //    the Mamba SSM kernel", combine equation)
 //  * MFMA 16x16x32 bf16 operand helpers
+//  * (host) the compute-unit count of the current device
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <atomic>
 
 namespace lr {
 
@@ -150,6 +153,26 @@ __device__ __forceinline__ bf16x8 pack_dd(f32x4 lo, f32x4 hi) {
   u16x8 v = {f2bf(lo[0]), f2bf(lo[1]), f2bf(lo[2]), f2bf(lo[3]),
              f2bf(hi[0]), f2bf(hi[1]), f2bf(hi[2]), f2bf(hi[3])};
   return as_bf16x8(v);
+}
+
+// Compute units of the current device (0 if the query fails), cached per
+// device after the first call.
+inline int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      v = -1;
+    }
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v > 0 ? v : 0;
 }
 
 // blockIdx -> logical work id such that consecutive logical ids run on the

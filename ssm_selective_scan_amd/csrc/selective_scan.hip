@@ -563,7 +563,7 @@ __device__ __forceinline__ void pair_body(
     const T* __restrict__ x, const T* __restrict__ dt, const T* __restrict__ Bm,
     const T* __restrict__ Cm, T* __restrict__ y, float* __restrict__ smem, float (&h)[2],
     const float (&A2)[2], const float (&iA)[2], const float (&An)[2], int64_t bi, int64_t d0,
-    int64_t L, int64_t D, int N, float* ck, int64_t ck_step, int64_t seg) {
+    int64_t L, int64_t D, int N, float* ck, int64_t ck_step, int64_t seg, int64_t prio_t) {
   constexpr int NT = 64 * NW, NP = 4 * NW;
   constexpr int GS = 8;                    // two groups per 16-step block
   constexpr int kPairs = TT / 2;           // step pairs per tile
@@ -601,7 +601,9 @@ __device__ __forceinline__ void pair_body(
     st.load(x + row0 * D + d0, dt + row0 * D + d0, Bm + row0 * N, Cm + row0 * N, nt, dcols, N);
   }
   int64_t ck_t = 0;   // token of the next segment checkpoint
+  if (prio_t > 0) __builtin_amdgcn_s_setprio(2);
   for (int64_t t0 = 0; t0 < L; t0 += TT) {
+    if (t0 == prio_t) __builtin_amdgcn_s_setprio(0);
     st.store(xs, Bs, Cs);
     __syncthreads();
     if (t0 + TT < L) {
@@ -686,12 +688,22 @@ __device__ __forceinline__ void pair_body(
 // Workgroups are swizzled so that the two 32-channel halves of each
 // 64-channel block (one 128-byte line of x, dt and y for bf16) run on the
 // same XCD (workgroups are dealt to the 8 XCDs round-robin) and share its L2.
+//
+// prio_wg >= 0: the grid is two workgroups per CU, and workgroups from
+// prio_wg on are the second ones to arrive on their CU.  The sequencer
+// issues from the older waves first, so left alone the first workgroup of a
+// CU finishes well before its partner, which then runs its last stretch
+// with one wave per SIMD.  The second workgroup therefore holds a raised
+// wave priority (s_setprio) for the first 5/8 of its sequence; measured on
+// B=8, L=4096, D=2048, N=16 this ends both together (386 -> 346 us; the
+// switch point was swept from 1/2 to 3/4, 5/8 being the best).
 template <typename T, int DISC, int TT, int NW, bool VEC>
 __global__ __launch_bounds__(64 * NW) void selective_pair_kernel(
     const T* __restrict__ x, const T* __restrict__ dt, const float* __restrict__ A,
     const T* __restrict__ Bm, const T* __restrict__ Cm, const float* __restrict__ Dskip,
     const float* __restrict__ h0, T* __restrict__ y, float* __restrict__ h_last,
-    float* __restrict__ ckpt, int64_t L, int64_t D, int N, int64_t seg, int64_t ck_step) {
+    float* __restrict__ ckpt, int64_t L, int64_t D, int N, int64_t seg, int64_t ck_step,
+    int64_t prio_wg) {
   extern __shared__ float smem[];
   constexpr int NP = 4 * NW;
   const int tid = threadIdx.x;
@@ -729,9 +741,10 @@ __global__ __launch_bounds__(64 * NW) void selective_pair_kernel(
   const bool precise = (__syncthreads_or(small ? 1 : 0) != 0) || sizeof(T) == 4;
   float* ck = (ckpt != nullptr && dok) ? ckpt + (bi * D + d) * N + n0 : nullptr;
 
+  const int64_t prio_t = (prio_wg >= 0 && g >= prio_wg) ? (L * 5 / 8) / TT * TT : -1;
   auto body = [&](auto precise_c, auto ck_c) {
     pair_body<T, DISC, decltype(precise_c)::value, TT, NW, VEC, decltype(ck_c)::value>(
-        x, dt, Bm, Cm, y, smem, h, A2, iA, An, bi, d0, L, D, N, ck, ck_step, seg);
+        x, dt, Bm, Cm, y, smem, h, A2, iA, An, bi, d0, L, D, N, ck, ck_step, seg, prio_t);
   };
   using F = std::false_type;
   using Tr = std::true_type;
@@ -759,11 +772,13 @@ static hipError_t launch_pair(const void* x, const void* dt, const float* A, con
   const size_t lds = (2 * TT * kPairCT + 2 * TT * NP + kPairCT +
                       static_cast<size_t>(NW) * (TT / 2) * 64) * sizeof(float);
   dim3 grid(static_cast<unsigned>(B * ((D + kPairCT - 1) / kPairCT)));
+  const int cus = cu_count();
+  const int64_t prio_wg = (cus > 0 && grid.x == 2u * static_cast<unsigned>(cus)) ? cus : -1;
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, grid, dim3(64 * NW), lds, stream, static_cast<const T*>(x),
                        static_cast<const T*>(dt), A, static_cast<const T*>(Bm),
                        static_cast<const T*>(Cm), Dskip, h0, static_cast<T*>(y), h_last, ckpt, L, D,
-                       N, seg, B * D * N);
+                       N, seg, B * D * N, prio_wg);
   };
   if (D % 8 == 0) go(selective_pair_kernel<T, DISC, TT, NW, true>);
   else go(selective_pair_kernel<T, DISC, TT, NW, false>);
