@@ -343,8 +343,11 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkFwdArgs g) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int sr = s0 + r;
-            float m = (sr <= t) ? z[r] * fast_exp2(ct - cur.cum[sr]) * cur.phi[sr] : 0.f;
+            // unconditional loads, then a select (no per-lane branches
+            // around LDS reads; a non-finite value above the diagonal is discarded)
+            float m = z[r] * fast_exp2(ct - cur.cum[sr]) * cur.phi[sr];
             if (MODE == kModeSsdBilinear) m *= cur.sg[t] * cur.sg[sr];
+            m = (sr <= t) ? m : 0.f;
             if (sr == t) m += Dh;   // D x_t folded into the diagonal
             out[r] = f2bf(m);
           }

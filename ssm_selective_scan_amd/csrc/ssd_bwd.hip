@@ -549,8 +549,11 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int u = u0 + r;
-          float m = (u >= t) ? fast_exp2(sm.cum[u] - ct) : 0.f;
+          // loads and exponential unconditional, then a select: no per-lane
+          // branches around LDS reads (inf above the diagonal is discarded)
+          float m = fast_exp2(sm.cum[u] - ct);
           if (DISC == kBwdBilinear) m *= st * sm.sg[u];
+          m = (u >= t) ? m : 0.f;
           const float mp = s[r] * m, wv = rr[r] * m * pt;
           const float tv = mp * pt * rr[r];
           om[r] = f2bf(mp);
@@ -668,8 +671,8 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
           d2 = mfma16x16x32(lds_tile_tr(sm.Gs, kLdN, 32 * kp, 16 * nt, lane),
                             lds_tile(sm.xs, kBLd, 16 * ti, 32 * kp, lane), d2);
         const int t = 16 * ti + c16;
+        const float ph = sm.phi[t], se = sm.sE[t];
         if (t < nv) {
-          const float ph = sm.phi[t], se = sm.sE[t];
           f32x4 v;
 #pragma unroll
           for (int r = 0; r < 4; ++r) v[r] = fmaf(ph * se, d2[r], d1[r]);
@@ -717,8 +720,8 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
           d2 = mfma16x16x32(lds_tile_tr(sm.Gs, kLdN, 32 * kp, 16 * nt, lane),
                             lds_tile(sm.dys, kBLd, 16 * tj, 32 * kp, lane), d2);
         const int u = 16 * tj + c16;
+        const float e = sm.E[u];
         if (u < nv) {
-          const float e = sm.E[u];
           f32x4 v;
 #pragma unroll
           for (int r = 0; r < 4; ++r) v[r] = fmaf(e, d2[r], d1[r]);
