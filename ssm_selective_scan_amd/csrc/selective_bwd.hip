@@ -199,11 +199,12 @@ __device__ __forceinline__ void selective_bwd_body(const SelBwdArgs& a, SbLds<NP
   };
 
   // Staging: a chunk's inputs are loaded into registers one chunk ahead
-  // (fetch) and written to LDS when the chunk starts (put).  Missing tokens
-  // and channels are zeros: dt = 0 gives e = 1, phi = 0, so they leave the
-  // state unchanged.
+  // (fetch) and written to LDS when the chunk starts (put).  The registers
+  // keep the raw elements and put() converts them, so no conversion next to
+  // a load makes the wave wait for it.  Missing tokens and channels are
+  // zeros: dt = 0 gives e = 1, phi = 0, so they leave the state unchanged.
   constexpr int kSt = kSbTC * kSbCT / 512;   // staged x/dt/dy elements per thread
-  float rx[kSt], rdt[kSt], rdy[kSt], rb = 0.f, rc = 0.f;
+  T rx[kSt], rdt[kSt], rdy[kSt], rb = T(0), rc = T(0);
   auto fetch = [&](int64_t t0, int nv, bool with_dy) {
 #pragma unroll
     for (int k = 0; k < kSt; ++k) {
@@ -211,16 +212,16 @@ __device__ __forceinline__ void selective_bwd_body(const SelBwdArgs& a, SbLds<NP
       const int r = i >> 6, c = i & 63;
       const bool ok = r < nv && d0 + c < D;
       const int64_t off = (b * L + t0 + r) * D + d0 + c;
-      rx[k] = ok ? Io<T>::load(x + off) : 0.f;
-      rdt[k] = ok ? Io<T>::load(dt + off) : 0.f;
-      rdy[k] = (ok && with_dy) ? Io<T>::load(dy + off) : 0.f;
+      rx[k] = ok ? x[off] : T(0);
+      rdt[k] = ok ? dt[off] : T(0);
+      rdy[k] = (ok && with_dy) ? dy[off] : T(0);
     }
     if (tid < kSbTC * N) {
       const int r = tid / N, n = tid % N;
       const bool ok = r < nv;
       const int64_t off = (b * L + t0 + r) * N + n;
-      rb = ok ? Io<T>::load(Bm + off) : 0.f;
-      rc = ok ? Io<T>::load(Cm + off) : 0.f;
+      rb = ok ? Bm[off] : T(0);
+      rc = ok ? Cm[off] : T(0);
     }
   };
   auto put = [&]() {
@@ -228,14 +229,14 @@ __device__ __forceinline__ void selective_bwd_body(const SelBwdArgs& a, SbLds<NP
     for (int k = 0; k < kSt; ++k) {
       const int i = tid + 512 * k;
       const int r = i >> 6, c = i & 63;
-      sm.xs[r][c] = rx[k];
-      sm.dts[r][c] = rdt[k];
-      sm.dys[r][c] = rdy[k];
+      sm.xs[r][c] = Io<T>::cvt(rx[k]);
+      sm.dts[r][c] = Io<T>::cvt(rdt[k]);
+      sm.dys[r][c] = Io<T>::cvt(rdy[k]);
     }
     if (tid < kSbTC * N) {
       const int r = tid / N, n = tid % N;
-      sm.Bs[r][n] = rb;
-      sm.Cs[r][n] = rc;
+      sm.Bs[r][n] = Io<T>::cvt(rb);
+      sm.Cs[r][n] = Io<T>::cvt(rc);
     }
   };
   auto chunk_len = [&](int64_t t0, int64_t tse) {
