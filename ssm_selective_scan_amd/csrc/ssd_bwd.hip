@@ -627,7 +627,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
           ddsum = fmaf(dyv, xv, ddsum);
         }
         if (t < nv) *reinterpret_cast<u16x4*>(a.dx + (b * a.L + t0 + t) * xrow + xoff + pr) = o;
-        toff = col4_sum(toff) * sm.E[t];
+        toff = col4_sum(toff);   // times E_t in the decay phase
         dph = col4_sum(dph);
         uu = col4_sum(uu) * ph;
         if (g4 == 0) {
@@ -654,6 +654,15 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
       *reinterpret_cast<u16x4*>(sm.Gs + p * kLdN + 16 * nt + 4 * g4) =
           u16x4{f2bf(gacc[nt][0]), f2bf(gacc[nt][1]), f2bf(gacc[nt][2]), f2bf(gacc[nt][3])};
     __syncthreads();
+    // per-token scales of the dB and dC epilogues, read here once: the empty
+    // asm keeps the reads (and their wait) out of the ragged-tail branches
+    float psE[4], eU[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      psE[q] = sm.phi[16 * q + c16] * sm.sE[16 * q + c16];
+      eU[q] = sm.E[16 * q + c16];
+      asm volatile("" : "+v"(psE[q]), "+v"(eU[q]));
+    }
 #pragma unroll
     for (int aa = 0; aa < NT / 4; ++aa) {
       const int nt = (NT / 4) * w + aa;
@@ -671,11 +680,10 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
           d2 = mfma16x16x32(lds_tile_tr(sm.Gs, kLdN, 32 * kp, 16 * nt, lane),
                             lds_tile(sm.xs, kBLd, 16 * ti, 32 * kp, lane), d2);
         const int t = 16 * ti + c16;
-        const float ph = sm.phi[t], se = sm.sE[t];
         if (t < nv) {
           f32x4 v;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = fmaf(ph * se, d2[r], d1[r]);
+          for (int r = 0; r < 4; ++r) v[r] = fmaf(psE[ti], d2[r], d1[r]);
           *reinterpret_cast<u16x4*>(a.dBpart + ((b * a.L + t0 + t) * a.H + h) * NS + 16 * nt + 4 * g4) =
               u16x4{f2bf(v[0]), f2bf(v[1]), f2bf(v[2]), f2bf(v[3])};
         }
@@ -720,11 +728,10 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
           d2 = mfma16x16x32(lds_tile_tr(sm.Gs, kLdN, 32 * kp, 16 * nt, lane),
                             lds_tile(sm.dys, kBLd, 16 * tj, 32 * kp, lane), d2);
         const int u = 16 * tj + c16;
-        const float e = sm.E[u];
         if (u < nv) {
           f32x4 v;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = fmaf(e, d2[r], d1[r]);
+          for (int r = 0; r < 4; ++r) v[r] = fmaf(eU[tj], d2[r], d1[r]);
           *reinterpret_cast<u16x4*>(a.dCpart + ((b * a.L + t0 + u) * a.H + h) * NS + 16 * nt + 4 * g4) =
               u16x4{f2bf(v[0]), f2bf(v[1]), f2bf(v[2]), f2bf(v[3])};
         }
@@ -746,7 +753,7 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
         rowT += sm.rowT4[k >> 4][i][k & 15];
         colT += sm.colT4[k >> 4][i][k & 15];
       }
-      const float toff = sm.toffp[0][k] + sm.toffp[1][k] + sm.toffp[2][k] + sm.toffp[3][k];
+      const float toff = sm.E[k] * (sm.toffp[0][k] + sm.toffp[1][k] + sm.toffp[2][k] + sm.toffp[3][k]);
       const float dph = sm.dphip[0][k] + sm.dphip[1][k] + sm.dphip[2][k] + sm.dphip[3][k];
       const float uu = sm.up[0][k] + sm.up[1][k] + sm.up[2][k] + sm.up[3][k];
       const float uprev = fast_exp2(sm.cum[kBQ - 1]) * (DISC == kBwdBilinear ? sm.sg[kBQ - 1] : 1.f) *
