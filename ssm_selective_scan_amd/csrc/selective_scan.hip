@@ -312,6 +312,9 @@ __device__ __forceinline__ void selective_body(
       for (int k = 0; k < kRows; ++k) {
 #pragma unroll
         for (int ww = 0; ww < NW; ++ww) s[k] += part[k][ww];
+        // (the empty asm keeps the reads and sums here, ahead of the store
+        // branches, instead of each read waited on inside its branch)
+        asm volatile("" : "+v"(s[k]));
       }
       if (dd < dcols) {
 #pragma unroll
@@ -672,6 +675,9 @@ __device__ __forceinline__ void pair_body(
       for (int k = 0; k < kRows; ++k) {
 #pragma unroll
         for (int ww = 0; ww < NW; ++ww) acc[k] += part[k][ww];
+        // (the empty asm keeps the reads and sums here, ahead of the store
+        // branches, instead of each read waited on inside its branch)
+        asm volatile("" : "+v"(acc[k]));
       }
       if (ch < dcols) {
 #pragma unroll
