@@ -26,6 +26,8 @@ constexpr int kRotSeg = 8;          // steps per lane segment
 constexpr int kRotThreads = 1024;
 constexpr int kRotSegs = kRotThreads / kRotCP;   // 64
 constexpr int kRotTile = kRotSegs * kRotSeg;     // 512 steps
+// narrow tiles (few chains): pairs and threads per workgroup
+constexpr int kRotNarrowCP = 4, kRotNarrowNT = 512;
 
 struct cplx {
   float re, im;
@@ -137,6 +139,138 @@ __global__ __launch_bounds__(kRotThreads) void rotlru_scan_kernel(
   }
   __syncthreads();
   if (h_last != nullptr && tid < kRotCP) {
+    const int64_t pp = p0 + tid;
+    if (pp < Dp) {
+      h_last[bi * D + 2 * pp] = tile_carry[tid].re;
+      h_last[bi * D + 2 * pp + 1] = tile_carry[tid].im;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Narrow tiles for problems with few chains (B * Dp small), as the diagonal
+// scan's narrow kernel: CT pairs per workgroup instead of 16 and 1024-step
+// tiles (NT threads: NSEG = NT / CT lane segments of SEG = 1024 / NSEG
+// steps), so a sequence of up to 1024 tokens is one pass of one load, two
+// barriers and one store.  Lane = CT * segment + pair: the CT pairs of a
+// token are adjacent lanes.  Wave c joins the segments of pair c: lane l
+// folds its NSEG / 64 consecutive segments, then the 64 lane totals go
+// through the complex DPP pair scan.  A segment's inputs are all loaded
+// (raw) before any is converted, so the loads are in flight together.
+// ---------------------------------------------------------------------------
+template <typename T, int CT, int NT>
+__global__ __launch_bounds__(NT) void rotlru_scan_narrow_kernel(
+    const T* __restrict__ r, const T* __restrict__ theta, const T* __restrict__ u,
+    const float* __restrict__ h0, T* __restrict__ h, float* __restrict__ h_last, int64_t L,
+    int64_t Dp) {
+  constexpr int NSEG = NT / CT;          // lane segments per tile
+  constexpr int SEG = 1024 / NSEG;       // steps per lane segment
+  constexpr int TL = NSEG * SEG;         // 1024 steps per tile
+  constexpr int SPL = NSEG / 64;         // segments per lane in the join
+  static_assert(CT >= 2 && CT <= 8 && TL == 1024 && SPL >= 1 && CT <= NT / 64, "narrow tile shape");
+  __shared__ cplx aggA[NSEG][CT];
+  __shared__ cplx aggB[NSEG][CT];
+  __shared__ cplx carry_in[NSEG][CT];
+  __shared__ cplx tile_carry[CT];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int pc = tid % CT;
+  const int seg = tid / CT;
+  const int64_t ntile = (Dp + CT - 1) / CT;
+  const int64_t bi = blockIdx.x / ntile;
+  const int64_t p0 = (blockIdx.x % ntile) * CT;
+  const int64_t p = p0 + pc;
+  const bool pok = p < Dp;
+  const int64_t D = 2 * Dp;
+
+  if (tid < CT) {
+    const int64_t pp = p0 + tid;
+    tile_carry[tid] = (h0 != nullptr && pp < Dp) ? cplx{h0[bi * D + 2 * pp], h0[bi * D + 2 * pp + 1]}
+                                                 : cplx{0.f, 0.f};
+  }
+  __syncthreads();
+
+  for (int64_t t0 = 0; t0 < L; t0 += TL) {
+    const int64_t ts = t0 + static_cast<int64_t>(seg) * SEG;
+    const int nok = pok ? static_cast<int>(L - ts < SEG ? (L - ts > 0 ? L - ts : 0) : SEG) : 0;
+    T rr[SEG], tr[SEG], ur[SEG], vr[SEG];
+#pragma unroll
+    for (int i = 0; i < SEG; ++i) {
+      const bool ok = i < nok;
+      const int64_t rowp = (bi * L + ts + i) * Dp + p;
+      const int64_t rowu = (bi * L + ts + i) * D + 2 * p;
+      rr[i] = ok ? r[rowp] : T(0);
+      tr[i] = ok ? theta[rowp] : T(0);
+      ur[i] = ok ? u[rowu] : T(0);
+      vr[i] = ok ? u[rowu + 1] : T(0);
+    }
+    // the segment from a zero state; steps past L are the identity (a = 1, w = 0)
+    cplx Pv[SEG], Hv[SEG];
+    {
+      cplx P = {1.f, 0.f}, Hs = {0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < SEG; ++i) {
+        float sn, cs;
+        sincosf(Io<T>::cvt(tr[i]), &sn, &cs);
+        const float rv = Io<T>::cvt(rr[i]);
+        const bool ok = i < nok;
+        const cplx a = {ok ? rv * cs : 1.f, ok ? rv * sn : 0.f};
+        const cplx w = {Io<T>::cvt(ur[i]), Io<T>::cvt(vr[i])};
+        Hs = cfma(a, Hs, w);
+        P = cmul(a, P);
+        Pv[i] = P;
+        Hv[i] = Hs;
+      }
+      aggA[seg][pc] = P;
+      aggB[seg][pc] = Hs;
+    }
+    __syncthreads();
+
+    if (wave < CT) {
+      const int c = wave;
+      cplx pa[SPL], pb[SPL];
+#pragma unroll
+      for (int j = 0; j < SPL; ++j) {
+        pa[j] = aggA[SPL * lane + j][c];
+        pb[j] = aggB[SPL * lane + j][c];
+      }
+      // the lane's segments folded in order, then the scan across lanes
+      cplx ta = pa[0], tb = pb[0];
+#pragma unroll
+      for (int j = 1; j < SPL; ++j) {
+        tb = cfma(pa[j], tb, pb[j]);
+        ta = cmul(pa[j], ta);
+      }
+      cplx ia = ta, ib = tb;
+      cwave_incl_pair_scan(ia, ib);
+      const cplx tc = tile_carry[c];
+      // state entering the lane's first segment, then each following one
+      const cplx ea = {wave_shr1(ia.re, 1.f), wave_shr1(ia.im, 0.f)};
+      const cplx eb = {wave_shr1(ib.re, 0.f), wave_shr1(ib.im, 0.f)};
+      cplx cin = cfma(ea, tc, eb);
+#pragma unroll
+      for (int j = 0; j < SPL; ++j) {
+        carry_in[SPL * lane + j][c] = cin;
+        cin = cfma(pa[j], cin, pb[j]);
+      }
+      if (lane == 63) tile_carry[c] = cfma(ia, tc, ib);
+    }
+    __syncthreads();
+
+    const cplx cin = carry_in[seg][pc];
+#pragma unroll
+    for (int i = 0; i < SEG; ++i) {
+      if (i < nok) {
+        const cplx z = cfma(Pv[i], cin, Hv[i]);
+        const int64_t rowu = (bi * L + ts + i) * D + 2 * p;
+        Io<T>::store(h + rowu, z.re);
+        Io<T>::store(h + rowu + 1, z.im);
+      }
+    }
+  }
+  __syncthreads();
+  if (h_last != nullptr && tid < CT) {
     const int64_t pp = p0 + tid;
     if (pp < Dp) {
       h_last[bi * D + 2 * pp] = tile_carry[tid].re;
@@ -659,7 +793,13 @@ hipError_t launch_rotlru_scan(const void* r, const void* theta, const void* u, c
                               void* h, float* h_last, int64_t B, int64_t L, int64_t D,
                               hipStream_t stream) {
   const int64_t Dp = D / 2;
-  if (Dp % 2 == 0 && B * (Dp / 32) >= 512) {
+  if (B * ((Dp + kRotCP - 1) / kRotCP) < 64) {   // few chains: narrow tiles
+    dim3 grid(static_cast<unsigned>(B * ((Dp + kRotNarrowCP - 1) / kRotNarrowCP)));
+    hipLaunchKernelGGL((rotlru_scan_narrow_kernel<T, kRotNarrowCP, kRotNarrowNT>), grid,
+                       dim3(kRotNarrowNT), 0, stream, static_cast<const T*>(r),
+                       static_cast<const T*>(theta), static_cast<const T*>(u), h0,
+                       static_cast<T*>(h), h_last, L, Dp);
+  } else if (Dp % 2 == 0 && B * (Dp / 32) >= 512) {
     dim3 grid(static_cast<unsigned>(B * ((Dp + 2 * kRotCP - 1) / (2 * kRotCP))));
     hipLaunchKernelGGL(rotlru_scan_wide_kernel<T>, grid, dim3(kRotThreads), 0, stream,
                        static_cast<const T*>(r), static_cast<const T*>(theta),

@@ -17,10 +17,13 @@ def _round_io(x, io):
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
-@pytest.mark.parametrize("B,L,D", [(1, 1024, 256), (2, 1500, 38), (1, 1, 2), (3, 513, 64),
-                                   (1, 4097, 40),
-                                   # two pairs per lane, 256-step tiles
-                                   (64, 300, 512), (40, 70, 836)])
+@pytest.mark.parametrize("B,L,D", [
+    # few chains: narrow tiles (4 pairs per workgroup, 1024-step tiles), ragged pairs and tiles
+    (1, 1024, 256), (2, 1500, 38), (1, 1, 2), (3, 513, 64), (1, 4097, 40),
+    # 16 pairs per workgroup, 512-step tiles
+    (8, 300, 256),
+    # two pairs per lane, 256-step tiles
+    (64, 300, 512), (40, 70, 836)])
 def test_rotlru_parity(io, B, L, D):
     print(f"rotlru io={io} B={B} L={L} D={D}", flush=True)
     g = lrgen.make(6, io=io, B=B, L=L, D=D)
