@@ -594,6 +594,173 @@ __global__ __launch_bounds__(kRotThreads) void rotlru_scan_bwd_kernel(
   }
 }
 
+// Narrow tiles for the backward of problems with few chains, as
+// rotlru_scan_narrow_kernel: CT pairs per workgroup, 1024-step tiles of NSEG
+// lane segments of SEG reversed steps, joined per pair by one wave.
+template <typename T, int CT, int NT>
+__global__ __launch_bounds__(NT) void rotlru_scan_bwd_narrow_kernel(
+    const T* __restrict__ r, const T* __restrict__ theta, const T* __restrict__ h,
+    const float* __restrict__ h0, const T* __restrict__ dh, const float* __restrict__ dh_last,
+    T* __restrict__ dr, T* __restrict__ dtheta, T* __restrict__ du, float* __restrict__ dh0,
+    int64_t L, int64_t Dp) {
+  constexpr int NSEG = NT / CT;          // lane segments per tile
+  constexpr int SEG = 1024 / NSEG;       // reversed steps per lane segment
+  constexpr int TL = NSEG * SEG;         // 1024 steps per tile
+  constexpr int SPL = NSEG / 64;         // segments per lane in the join
+  static_assert(CT >= 2 && CT <= 8 && TL == 1024 && SPL >= 1 && CT <= NT / 64, "narrow tile shape");
+  __shared__ cplx aggA[NSEG][CT];
+  __shared__ cplx aggB[NSEG][CT];
+  __shared__ cplx carry_in[NSEG][CT];
+  __shared__ cplx tile_carry[CT];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int pr = tid % CT;
+  const int seg = tid / CT;
+  const int64_t ntile = (Dp + CT - 1) / CT;
+  const int64_t bi = blockIdx.x / ntile;
+  const int64_t p0 = (blockIdx.x % ntile) * CT;
+  const int64_t p = p0 + pr;
+  const bool pok = p < Dp;
+  const int64_t D = 2 * Dp;
+
+  if (tid < CT) {
+    const int64_t pp = p0 + tid;
+    tile_carry[tid] = (dh_last != nullptr && pp < Dp)
+                          ? cplx{dh_last[bi * D + 2 * pp], dh_last[bi * D + 2 * pp + 1]}
+                          : cplx{0.f, 0.f};
+  }
+  __syncthreads();
+
+  const int64_t row = bi * L;  // token offset of this batch row
+  for (int64_t u0 = 0; u0 < L; u0 += TL) {
+    const int64_t us = u0 + static_cast<int64_t>(seg) * SEG;
+    // reversed steps u = us + i are tokens t = t_first - i (descending)
+    const int64_t t_first = L - 1 - us;
+    const int nok = pok ? static_cast<int>(L - us < SEG ? (L - us > 0 ? L - us : 0) : SEG) : 0;
+    // gate and unit rotation of tokens t_first + 1 - j, j = 0..SEG: entry j
+    // is the coefficient of reversed step j (conjugated) and, for j >= 1, the
+    // gate and rotation of the output of step j - 1; identity where there is
+    // no token.  All loads of the segment are issued raw before any is converted.
+    T rr[SEG + 1], tr[SEG + 1], gr[SEG], gi[SEG];
+    bool okj[SEG + 1];
+#pragma unroll
+    for (int j = 0; j <= SEG; ++j) {
+      const int64_t tj = t_first + 1 - j;
+      okj[j] = j == 0 ? (nok > 0 && tj < L) : (j - 1 < nok);
+      const int64_t rowp = (row + tj) * Dp + p;
+      rr[j] = okj[j] ? r[rowp] : T(0);
+      tr[j] = okj[j] ? theta[rowp] : T(0);
+      if (j < SEG) {
+        const int64_t rowu = (row + t_first - j) * D + 2 * p;
+        gr[j] = j < nok ? dh[rowu] : T(0);
+        gi[j] = j < nok ? dh[rowu + 1] : T(0);
+      }
+    }
+    cplx ev[SEG + 1];
+    float rv[SEG + 1];
+#pragma unroll
+    for (int j = 0; j <= SEG; ++j) {
+      float sn, cs;
+      sincosf(Io<T>::cvt(tr[j]), &sn, &cs);
+      ev[j] = {okj[j] ? cs : 1.f, okj[j] ? sn : 0.f};
+      rv[j] = okj[j] ? Io<T>::cvt(rr[j]) : 1.f;
+    }
+    cplx Pv[SEG], Hv[SEG];
+    {
+      cplx P = {1.f, 0.f}, Gs = {0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < SEG; ++i) {
+        const bool ok = i < nok;
+        const cplx a = {ok ? rv[i] * ev[i].re : 1.f, ok ? -rv[i] * ev[i].im : 0.f};
+        const cplx w = {Io<T>::cvt(gr[i]), Io<T>::cvt(gi[i])};
+        Gs = cfma(a, Gs, w);
+        P = cmul(a, P);
+        Pv[i] = P;
+        Hv[i] = Gs;
+      }
+      aggA[seg][pr] = P;
+      aggB[seg][pr] = Gs;
+    }
+    __syncthreads();
+
+    if (wave < CT) {
+      const int c = wave;
+      cplx pa[SPL], pb[SPL];
+#pragma unroll
+      for (int j = 0; j < SPL; ++j) {
+        pa[j] = aggA[SPL * lane + j][c];
+        pb[j] = aggB[SPL * lane + j][c];
+      }
+      cplx ta = pa[0], tb = pb[0];
+#pragma unroll
+      for (int j = 1; j < SPL; ++j) {
+        tb = cfma(pa[j], tb, pb[j]);
+        ta = cmul(pa[j], ta);
+      }
+      cplx ia = ta, ib = tb;
+      cwave_incl_pair_scan(ia, ib);
+      const cplx tc = tile_carry[c];
+      const cplx ea = {wave_shr1(ia.re, 1.f), wave_shr1(ia.im, 0.f)};
+      const cplx eb = {wave_shr1(ib.re, 0.f), wave_shr1(ib.im, 0.f)};
+      cplx cin = cfma(ea, tc, eb);
+#pragma unroll
+      for (int j = 0; j < SPL; ++j) {
+        carry_in[SPL * lane + j][c] = cin;
+        cin = cfma(pa[j], cin, pb[j]);
+      }
+      if (lane == 63) tile_carry[c] = cfma(ia, tc, ib);
+    }
+    __syncthreads();
+
+    const cplx cin = carry_in[seg][pr];
+    // element offsets of token t_first, passed through an empty asm so that the
+    // per-step addresses are formed here rather than kept live from the loads
+    // before the barrier (which spilled them)
+    int64_t offu = (row + t_first) * D + 2 * p, offp = (row + t_first) * Dp + p;
+    asm volatile("" : "+v"(offu), "+v"(offp));
+#pragma unroll
+    for (int i = 0; i < SEG; ++i) {
+      if (i < nok) {
+        const int64_t t = t_first - i;
+        const cplx g = cfma(Pv[i], cin, Hv[i]);
+        cplx zp;
+        const int64_t rowu = offu - i * D;
+        const int64_t rowp = offp - i * Dp;
+        if (t > 0) {
+          const int64_t rowq = rowu - D;
+          zp = {Io<T>::load(h + rowq), Io<T>::load(h + rowq + 1)};
+        } else {
+          zp = h0 != nullptr ? cplx{h0[bi * D + 2 * p], h0[bi * D + 2 * p + 1]} : cplx{0.f, 0.f};
+        }
+        // q = g conj(e z_prev) with e = ev[i + 1] the rotation of token t
+        const cplx ez = cmul(ev[i + 1], zp);
+        const float qre = fmaf(g.re, ez.re, g.im * ez.im);
+        const float qim = fmaf(g.im, ez.re, -g.re * ez.im);
+        Io<T>::store(dr + rowp, qre);
+        Io<T>::store(dtheta + rowp, rv[i + 1] * qim);
+        Io<T>::store(du + rowu, g.re);
+        Io<T>::store(du + rowu + 1, g.im);
+      }
+    }
+  }
+  __syncthreads();
+  if (dh0 != nullptr && tid < CT) {
+    const int64_t pp = p0 + tid;
+    if (pp < Dp) {
+      cplx g = tile_carry[tid];
+      if (L > 0) {
+        const float r0 = Io<T>::load(r + row * Dp + pp);
+        float sn, cs;
+        sincosf(Io<T>::load(theta + row * Dp + pp), &sn, &cs);
+        g = cmul({r0 * cs, -r0 * sn}, g);
+      }
+      dh0[bi * D + 2 * pp] = g.re;
+      dh0[bi * D + 2 * pp + 1] = g.im;
+    }
+  }
+}
+
 // Wide backward for the problems the wide forward serves: 2 adjacent pairs
 // per lane (vector accesses), 4 reversed steps per segment.
 template <typename T>
@@ -761,6 +928,15 @@ hipError_t launch_rotlru_scan_bwd(const void* r, const void* theta, const void* 
                                   void* dtheta, void* du, float* dh0, int64_t B, int64_t L,
                                   int64_t D, hipStream_t stream) {
   const int64_t Dp = D / 2;
+  if (B * ((Dp + kRotCP - 1) / kRotCP) < 64) {   // few chains: narrow tiles
+    dim3 grid(static_cast<unsigned>(B * ((Dp + kRotNarrowCP - 1) / kRotNarrowCP)));
+    hipLaunchKernelGGL((rotlru_scan_bwd_narrow_kernel<T, kRotNarrowCP, kRotNarrowNT>), grid,
+                       dim3(kRotNarrowNT), 0, stream, static_cast<const T*>(r),
+                       static_cast<const T*>(theta), static_cast<const T*>(h), h0,
+                       static_cast<const T*>(dh), dh_last, static_cast<T*>(dr),
+                       static_cast<T*>(dtheta), static_cast<T*>(du), dh0, L, Dp);
+    return hipGetLastError();
+  }
   if (Dp % 2 == 0 && B * (Dp / 32) >= 512) {
     dim3 grid(static_cast<unsigned>(B * ((Dp + 2 * kRotCP - 1) / (2 * kRotCP))));
     hipLaunchKernelGGL(rotlru_scan_bwd_wide_kernel<T>, grid, dim3(kRotThreads), 0, stream,
