@@ -211,8 +211,10 @@ __global__ __launch_bounds__(NT) void diag_scan_narrow_kernel(
   const int ch = tid % CT;
   const int seg = tid / CT;
   const int64_t ntile = (D + CT - 1) / CT;
-  const int64_t bi = blockIdx.x / ntile;
-  const int64_t d0 = (blockIdx.x % ntile) * CT;
+  // consecutive tiles (channels sharing cache lines) on one XCD
+  const int64_t wid = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t bi = wid / ntile;
+  const int64_t d0 = (wid % ntile) * CT;
   const int64_t d = d0 + ch;
   const bool dok = d < D;
 
@@ -430,8 +432,10 @@ __global__ __launch_bounds__(NT) void diag_scan_bwd_narrow_kernel(
   const int ch = tid % CT;
   const int seg = tid / CT;
   const int64_t ntile = (D + CT - 1) / CT;
-  const int64_t bi = blockIdx.x / ntile;
-  const int64_t d0 = (blockIdx.x % ntile) * CT;
+  // consecutive tiles (channels sharing cache lines) on one XCD
+  const int64_t wid = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t bi = wid / ntile;
+  const int64_t d0 = (wid % ntile) * CT;
   const int64_t d = d0 + ch;
   const bool dok = d < D;
 

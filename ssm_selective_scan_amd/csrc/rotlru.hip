@@ -178,8 +178,10 @@ __global__ __launch_bounds__(NT) void rotlru_scan_narrow_kernel(
   const int pc = tid % CT;
   const int seg = tid / CT;
   const int64_t ntile = (Dp + CT - 1) / CT;
-  const int64_t bi = blockIdx.x / ntile;
-  const int64_t p0 = (blockIdx.x % ntile) * CT;
+  // consecutive tiles (channels sharing cache lines) on one XCD
+  const int64_t wid = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t bi = wid / ntile;
+  const int64_t p0 = (wid % ntile) * CT;
   const int64_t p = p0 + pc;
   const bool pok = p < Dp;
   const int64_t D = 2 * Dp;
@@ -618,8 +620,10 @@ __global__ __launch_bounds__(NT) void rotlru_scan_bwd_narrow_kernel(
   const int pr = tid % CT;
   const int seg = tid / CT;
   const int64_t ntile = (Dp + CT - 1) / CT;
-  const int64_t bi = blockIdx.x / ntile;
-  const int64_t p0 = (blockIdx.x % ntile) * CT;
+  // consecutive tiles (channels sharing cache lines) on one XCD
+  const int64_t wid = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t bi = wid / ntile;
+  const int64_t p0 = (wid % ntile) * CT;
   const int64_t p = p0 + pr;
   const bool pok = p < Dp;
   const int64_t D = 2 * Dp;
