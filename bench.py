@@ -19,10 +19,12 @@ The same run also measures the other four workloads (diagonal scan, SSD
 forward, GLA forward, SSD forward + backward with segment checkpoints), the
 backward and decode paths, and a plain device copy for the achievable
 bandwidth; records which kernels each call dispatched (dispatch, from the
-torch profiler's HIP activity trace); and, before touching the GPU, times
-the fp64 CPU oracle on a bounded sample of every workload on the host's
-cores (cpu_baseline: the headline's figure, with per_workload for all five
-and the GPU-over-oracle ratios).  One JSON line is printed.
+torch profiler's HIP activity trace); and, after the GPU work, times the
+fp64 CPU oracle on every workload on the host's cores, in worker processes
+forked before this process starts the GPU runtime (cpu_baseline: the
+headline's figure, with per_workload for all five and the GPU-over-oracle
+ratios).  Timing the oracle first slowed the headline's first timed
+launches.  One JSON line is printed.
 """
 from __future__ import annotations
 
@@ -503,16 +505,14 @@ def _oracle_unit(cfg_id):
     return fwd_bwd
 
 
-_BARRIER = None
-
-
-def _cpu_worker(cfg_id):
+def _cpu_worker(args):
+    cfg_id, reps = args
     from threadpoolctl import threadpool_limits
     with threadpool_limits(1):
         run = _oracle_unit(cfg_id)
-        _BARRIER.wait()
-        t0 = time.perf_counter()
-        run()
+        t0 = time.perf_counter()   # CLOCK_MONOTONIC: comparable across processes
+        for _ in range(reps):
+            run()
         return t0, time.perf_counter()
 
 
@@ -527,28 +527,35 @@ def cpu_model():
     return "unknown"
 
 
-def cpu_baselines(workers):
-    """Oracle tokens/s of every workload on `workers` processes (one unit
-    each; the diagonal workload, a few milliseconds, on one)."""
+def cpu_pool(workers):
+    """The oracle's worker processes, forked now (before the GPU runtime
+    starts in this process) and used at the end by cpu_baselines."""
     import multiprocessing as mp
-    global _BARRIER
+    return mp.get_context("fork").Pool(workers)
+
+
+def cpu_baselines(pool, workers):
+    """Oracle tokens/s of every workload on `workers` processes, each running
+    units // workers units of the workload one after another (all of it when
+    the units divide evenly; the diagonal workload, a few milliseconds, on one
+    process).  Wall time: first start to last end over the processes."""
     out = {}
-    ctx = mp.get_context("fork")
     for cfg_id, (_, units, what) in CPU_UNITS.items():
         P = 1 if units == 1 else min(workers, units)
-        _BARRIER = ctx.Barrier(P)
-        with ctx.Pool(P) as pool:
-            spans = pool.map(_cpu_worker, [cfg_id] * P, chunksize=1)
+        reps = max(1, units // P)
+        spans = pool.map(_cpu_worker, [(cfg_id, reps)] * P, chunksize=1)
         wall = max(e for _, e in spans) - min(s for s, _ in spans)
         p = lrgen.CONFIGS[cfg_id]
-        full_s = wall * units / P
+        done = P * reps
+        full_s = wall * units / done
         tokens = p["B"] * p["L"]
+        scaled = "" if done == units else f"; time scaled by {units}/{done}"
         out[lrgen.NAMES[cfg_id]] = dict(
             value=tokens / full_s, unit="tokens/s", cores=P, kind="oracle",
             oracle_s_full_workload=full_s, wall_s=wall,
-            sample=f"{P} of {units} units ({what}), full L={p['L']}, fp64 numpy, "
-                   f"one process and one BLAS thread per core; time scaled by {units}/{P}")
-        log(f"[bench] oracle {lrgen.NAMES[cfg_id]}: {P} units in {wall:.2f} s on {P} cores "
+            sample=f"{done} of {units} units ({what}), full L={p['L']}, fp64 numpy, "
+                   f"{P} process{'es' if P > 1 else ''} with one BLAS thread each{scaled}")
+        log(f"[bench] oracle {lrgen.NAMES[cfg_id]}: {done} units in {wall:.2f} s on {P} cores "
             f"-> {tokens / full_s:.4g} tokens/s for the whole workload")
     return out
 
@@ -687,13 +694,12 @@ def main():
               "the scans shard by batch/head with no exchange, see DESIGN.md", file=sys.stderr)
         sys.exit(2)
 
-    # the oracle leg runs first: its worker processes are forked before this
-    # process starts the GPU runtime
-    cpu = None
+    # the oracle's worker processes are forked before this process starts the
+    # GPU runtime; they run the oracle after the GPU measurements
+    pool, workers = None, 0
     if not (args.no_cpu or args.copy_probe or args.only or args.headline_only):
         workers = args.cpu_workers or min(len(os.sched_getaffinity(0)), 16)
-        log(f"[bench] CPU oracle baselines on {workers} worker processes ({cpu_model()})")
-        cpu = cpu_baselines(workers)
+        pool = cpu_pool(workers)
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU available", file=sys.stderr)
@@ -796,6 +802,12 @@ def main():
         result["dispatch"] = dict(fp, **{k: v["kernels"] for k, v in extra.items()
                                          if isinstance(v, dict) and "kernels" in v})
 
+    cpu = None
+    if pool is not None:
+        log(f"[bench] CPU oracle baselines on {workers} worker processes ({cpu_model()})")
+        cpu = cpu_baselines(pool, workers)
+        pool.close()
+        pool.join()
     if cpu is not None:
         head = cpu[lrgen.NAMES[2]]
         result["cpu_baseline"] = dict(head, cpu_model=cpu_model(), per_workload=cpu)
