@@ -47,6 +47,73 @@ template <> struct Io<uint16_t> {
   __device__ __forceinline__ static float cvt(uint16_t v) { return bf2f(v); }
 };
 
+// CPL consecutive elements of T as loaded: fp32 words, or bf16 values packed
+// in 32-bit words.  Scans keep loaded elements raw and convert them (vcvt)
+// only once every load of a segment has been issued: memory loads retire in
+// order, so a conversion next to its load would make the wave wait for that
+// load, and all earlier ones, before issuing the next.
+template <typename T, int CPL> struct VRaw { float v[CPL]; };
+template <> struct VRaw<uint16_t, 1> { uint16_t v; };
+template <> struct VRaw<uint16_t, 2> { uint32_t v; };
+template <> struct VRaw<uint16_t, 4> { uint2 v; };
+
+template <typename T, int CPL>
+__device__ __forceinline__ VRaw<T, CPL> vload_raw(const T* p) {
+  VRaw<T, CPL> r;
+  if constexpr (sizeof(T) == 4) {
+    if constexpr (CPL == 1) {
+      r.v[0] = *p;
+    } else if constexpr (CPL == 2) {
+      const float2 x = *reinterpret_cast<const float2*>(p);
+      r.v[0] = x.x; r.v[1] = x.y;
+    } else {
+      const float4 x = *reinterpret_cast<const float4*>(p);
+      r.v[0] = x.x; r.v[1] = x.y; r.v[2] = x.z; r.v[3] = x.w;
+    }
+  } else if constexpr (CPL == 1) {
+    r.v = *p;
+  } else if constexpr (CPL == 2) {
+    r.v = *reinterpret_cast<const uint32_t*>(p);
+  } else {
+    r.v = *reinterpret_cast<const uint2*>(p);
+  }
+  return r;
+}
+// x as one element of T, unconverted (exact in bf16 for the 0 and 1 used here)
+template <typename T> __device__ __forceinline__ T raw_of(float x) {
+  if constexpr (sizeof(T) == 4) return x;
+  else return static_cast<T>(f2bf(x));
+}
+// every element equal to x
+template <typename T, int CPL>
+__device__ __forceinline__ VRaw<T, CPL> vfill_raw(float x) {
+  VRaw<T, CPL> r;
+  if constexpr (sizeof(T) == 4) {
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) r.v[k] = x;
+  } else {
+    const uint32_t b = f2bf(x);
+    if constexpr (CPL == 1) r.v = static_cast<uint16_t>(b);
+    else if constexpr (CPL == 2) r.v = b | (b << 16);
+    else r.v = uint2{b | (b << 16), b | (b << 16)};
+  }
+  return r;
+}
+template <typename T, int CPL>
+__device__ __forceinline__ void vcvt(const VRaw<T, CPL>& r, float (&v)[CPL]) {
+  if constexpr (sizeof(T) == 4) {
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) v[k] = r.v[k];
+  } else if constexpr (CPL == 1) {
+    v[0] = bf2f(r.v);
+  } else if constexpr (CPL == 2) {
+    v[0] = bf2f(static_cast<uint16_t>(r.v)); v[1] = bf2f(static_cast<uint16_t>(r.v >> 16));
+  } else {
+    v[0] = bf2f(static_cast<uint16_t>(r.v.x)); v[1] = bf2f(static_cast<uint16_t>(r.v.x >> 16));
+    v[2] = bf2f(static_cast<uint16_t>(r.v.y)); v[3] = bf2f(static_cast<uint16_t>(r.v.y >> 16));
+  }
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

@@ -31,29 +31,6 @@ constexpr int kDiagNarrowCT = 8, kDiagNarrowNT = 512;
 // CPL consecutive channels per lane, read and written as one CPL-wide vector
 // access (a 16-lane row of a wave then covers 16 * CPL channels of a token).
 template <typename T, int CPL>
-__device__ __forceinline__ void vload(const T* p, float (&v)[CPL]) {
-  if constexpr (CPL == 1) {
-    v[0] = Io<T>::load(p);
-  } else if constexpr (sizeof(T) == 4) {
-    if constexpr (CPL == 2) {
-      const float2 x = *reinterpret_cast<const float2*>(p);
-      v[0] = x.x; v[1] = x.y;
-    } else {
-      const float4 x = *reinterpret_cast<const float4*>(p);
-      v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
-    }
-  } else {
-    if constexpr (CPL == 2) {
-      const uint32_t x = *reinterpret_cast<const uint32_t*>(p);
-      v[0] = bf2f(static_cast<uint16_t>(x)); v[1] = bf2f(static_cast<uint16_t>(x >> 16));
-    } else {
-      const uint2 x = *reinterpret_cast<const uint2*>(p);
-      v[0] = bf2f(static_cast<uint16_t>(x.x)); v[1] = bf2f(static_cast<uint16_t>(x.x >> 16));
-      v[2] = bf2f(static_cast<uint16_t>(x.y)); v[3] = bf2f(static_cast<uint16_t>(x.y >> 16));
-    }
-  }
-}
-template <typename T, int CPL>
 __device__ __forceinline__ void vstore(T* p, const float (&v)[CPL]) {
   if constexpr (CPL == 1) {
     Io<T>::store(p, v[0]);
@@ -110,17 +87,34 @@ __global__ __launch_bounds__(kDiagThreads) void diag_scan_kernel(
       const int64_t off0 = (row + ts) * D + d;
       const T* pa = a + off0;
       const T* pb = b + off0;
+      if constexpr (sizeof(T) == 2) {
+        // bf16: every load of the segment issued raw before any is converted
+        VRaw<T, CPL> ar[kDiagSeg], br[kDiagSeg];
 #pragma unroll
-      for (int i = 0; i < kDiagSeg; ++i) {
-        if (i < nok) {
-          vload<T, CPL>(pa, av[i]);
-          vload<T, CPL>(pb, bv[i]);
-        } else {
-#pragma unroll
-          for (int k = 0; k < CPL; ++k) { av[i][k] = 1.f; bv[i][k] = 0.f; }
+        for (int i = 0; i < kDiagSeg; ++i) {
+          ar[i] = i < nok ? vload_raw<T, CPL>(pa) : vfill_raw<T, CPL>(1.f);
+          br[i] = i < nok ? vload_raw<T, CPL>(pb) : vfill_raw<T, CPL>(0.f);
+          pa += D;
+          pb += D;
         }
-        pa += D;
-        pb += D;
+#pragma unroll
+        for (int i = 0; i < kDiagSeg; ++i) {
+          vcvt<T, CPL>(ar[i], av[i]);
+          vcvt<T, CPL>(br[i], bv[i]);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < kDiagSeg; ++i) {
+          if (i < nok) {
+            vcvt<T, CPL>(vload_raw<T, CPL>(pa), av[i]);
+            vcvt<T, CPL>(vload_raw<T, CPL>(pb), bv[i]);
+          } else {
+#pragma unroll
+            for (int k = 0; k < CPL; ++k) { av[i][k] = 1.f; bv[i][k] = 0.f; }
+          }
+          pa += D;
+          pb += D;
+        }
       }
     }
     // sequential scan of the segment from a zero state
@@ -327,22 +321,44 @@ __global__ __launch_bounds__(kDiagThreads) void diag_scan_bwd_kernel(
     // steps u = us + i, i.e. tokens t = L - 1 - us - i (descending)
     const int nok = dok ? static_cast<int>(L - us < kDiagSeg ? (L - us > 0 ? L - us : 0) : kDiagSeg) : 0;
     const int64_t t_first = L - 1 - us;
+    // at CPL = 2 (and fp32 CPL = 1) all loads of the segment, and after the
+    // barriers all of the states, are issued raw before any is converted,
+    // which measured faster there; at CPL = 4 the registers for that are not
+    // there (it spills), and each step converts its own
+    constexpr bool kPre = CPL == 2 || (CPL == 1 && sizeof(T) == 4);
     float av[kDiagSeg][CPL], bv[kDiagSeg][CPL];
+    if constexpr (kPre) {
+      VRaw<T, CPL> ar[kDiagSeg], br[kDiagSeg];
 #pragma unroll
-    for (int i = 0; i < kDiagSeg; ++i) {
-      const int64_t t = t_first - i;
-      const bool ok = i < nok;
-      if (ok && t + 1 < L) {
-        vload<T, CPL>(a + (row + t + 1) * D + d, av[i]);
-      } else {
-#pragma unroll
-        for (int k = 0; k < CPL; ++k) av[i][k] = 1.f;
+      for (int i = 0; i < kDiagSeg; ++i) {
+        const int64_t t = t_first - i;
+        const bool ok = i < nok;
+        ar[i] = (ok && t + 1 < L) ? vload_raw<T, CPL>(a + (row + t + 1) * D + d)
+                                  : vfill_raw<T, CPL>(1.f);
+        br[i] = ok ? vload_raw<T, CPL>(dh + (row + t) * D + d) : vfill_raw<T, CPL>(0.f);
       }
-      if (ok) {
-        vload<T, CPL>(dh + (row + t) * D + d, bv[i]);
-      } else {
 #pragma unroll
-        for (int k = 0; k < CPL; ++k) bv[i][k] = 0.f;
+      for (int i = 0; i < kDiagSeg; ++i) {
+        vcvt<T, CPL>(ar[i], av[i]);
+        vcvt<T, CPL>(br[i], bv[i]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kDiagSeg; ++i) {
+        const int64_t t = t_first - i;
+        const bool ok = i < nok;
+        if (ok && t + 1 < L) {
+          vcvt<T, CPL>(vload_raw<T, CPL>(a + (row + t + 1) * D + d), av[i]);
+        } else {
+#pragma unroll
+          for (int k = 0; k < CPL; ++k) av[i][k] = 1.f;
+        }
+        if (ok) {
+          vcvt<T, CPL>(vload_raw<T, CPL>(dh + (row + t) * D + d), bv[i]);
+        } else {
+#pragma unroll
+          for (int k = 0; k < CPL; ++k) bv[i][k] = 0.f;
+        }
       }
     }
 #pragma unroll
@@ -380,6 +396,14 @@ __global__ __launch_bounds__(kDiagThreads) void diag_scan_bwd_kernel(
     // before the barriers (which spilled them at CPL = 4)
     int64_t offt = (row + t_first) * D + d;
     asm volatile("" : "+v"(offt));
+    // h_{t-1} of every step (the step at t = 0 takes h0 instead)
+    VRaw<T, CPL> hr[kDiagSeg];
+    if constexpr (kPre) {
+#pragma unroll
+      for (int i = 0; i < kDiagSeg; ++i)
+        hr[i] = (i < nok && t_first - i > 0) ? vload_raw<T, CPL>(h + offt - (i + 1) * D)
+                                             : vfill_raw<T, CPL>(0.f);
+    }
 #pragma unroll
     for (int i = 0; i < kDiagSeg; ++i) {
       if (i < nok) {
@@ -388,8 +412,14 @@ __global__ __launch_bounds__(kDiagThreads) void diag_scan_bwd_kernel(
         float gt[CPL], hp[CPL], dv[CPL];
 #pragma unroll
         for (int k = 0; k < CPL; ++k) gt[k] = fmaf(av[i][k], cin[k], bv[i][k]);
-        if (t > 0) {
-          vload<T, CPL>(h + off - D, hp);
+        if constexpr (kPre) {
+          vcvt<T, CPL>(hr[i], hp);
+          if (t == 0 && h0 != nullptr) {
+#pragma unroll
+            for (int k = 0; k < CPL; ++k) hp[k] = h0[bi * D + d + k];
+          }
+        } else if (t > 0) {
+          vcvt<T, CPL>(vload_raw<T, CPL>(h + off - D), hp);
         } else {
 #pragma unroll
           for (int k = 0; k < CPL; ++k) hp[k] = h0 != nullptr ? h0[bi * D + d + k] : 0.f;

@@ -369,10 +369,29 @@ __global__ __launch_bounds__(kRotThreads) void rotlru_scan_wide_kernel(
       // bounds, L > 0 here), and steps past the end take the identity: no
       // branch around a load, so all of a segment's loads are in flight at once
       const int64_t pc = pok ? p : Dp - PPL;
+      // bf16: every load of the segment issued raw, converted afterwards
+      // (fp32 measured faster with each step's loads next to its use)
+      constexpr bool kPre = sizeof(T) == 2;
+      VRaw<T, PPL> rr[SEG], tr[SEG];
+      VRaw<T, 2 * PPL> ur[SEG];
+      if constexpr (kPre) {
+#pragma unroll
+        for (int i = 0; i < SEG; ++i) {
+          const int64_t tc = ts + i < L ? ts + i : L - 1;
+          const int64_t rowp = (bi * L + tc) * Dp + pc;
+          rr[i] = vload_raw<T, PPL>(r + rowp);
+          tr[i] = vload_raw<T, PPL>(theta + rowp);
+          ur[i] = vload_raw<T, 2 * PPL>(u + 2 * rowp);
+        }
+      }
 #pragma unroll
       for (int i = 0; i < SEG; ++i) {
         float rv[PPL], tv[PPL], uv[2 * PPL];
-        {
+        if constexpr (kPre) {
+          vcvt<T, PPL>(rr[i], rv);
+          vcvt<T, PPL>(tr[i], tv);
+          vcvt<T, 2 * PPL>(ur[i], uv);
+        } else {
           const int64_t tc = ts + i < L ? ts + i : L - 1;
           const int64_t rowp = (bi * L + tc) * Dp + pc;
           rvload<T, PPL>(r + rowp, rv);
