@@ -28,13 +28,13 @@
 // Every input tile sits in LDS exactly as it lies in memory (token rows):
 // operands whose contraction runs over tokens (x in M X, B and the
 // decay-weighted x in the state update) are read with gfx950's transposing
-// LDS read, so staging is a plain 16-byte copy.  One LDS buffer (66 KB, so
-// two workgroups share a CU): block k+1, loaded from HBM into registers
-// during block k, is written into it once block k is done.  Row pitches are
+// LDS read, so staging is a plain 16-byte copy.  One LDS buffer (66 KB):
+// block k+1, loaded from HBM into registers during block k, is written into
+// it once block k is done.  Row pitches are
 // chosen per tile for its read pattern (see ChunkBuf).
 //
-// With fewer than two workgroups per CU the sequence is cut into parts that
-// run side by side.  The parts' end states from a zero start and their decay
+// When the grid leaves CUs idle the sequence is cut into parts that run side
+// by side.  The parts' end states from a zero start and their decay
 // products come from a state-only pre-pass (SO); every part then folds those
 // of the parts before it into its entering state with the combine
 // (a2, b2) o (a1, b1) = (a2 a1, a2 b1 + b2) ("K-Search for MLX" blog,
@@ -141,7 +141,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkFwdArgs g) {
   constexpr int kCB = kCQ * kRowCB / 256;   // C, B
   constexpr int kXC = kCQ * kRowX / 256;    // x
   // One input buffer: the next block is staged after the current one is
-  // done (66 KB of LDS, so two workgroups share a CU).
+  // done (66 KB of LDS).
   __shared__ ChunkBuf<NS> sm[1];
   __shared__ uint16_t Ms[SO ? 8 : kCQ * kLdM];   // M[t][s]
 
@@ -438,16 +438,19 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkFwdArgs g) {
   }
 }
 
-// Sequence split of the forward: with fewer than two workgroups per CU
-// (512 on MI355X's 256 CUs) the sequence is cut into parts of at least 8
-// blocks, each run by its own workgroups from the state the pre-pass and
-// the fold give it.  Workspace: the parts' end states and decay products.
+// Sequence split of the forward: when the grid leaves CUs idle (fewer than
+// 256 workgroups, MI355X's CU count; the kernel's registers allow one
+// workgroup per CU) the sequence is cut into parts of at least 8 blocks, up
+// to 512 workgroups, each run by its own workgroups from the state the
+// pre-pass and the fold give it.  A grid that already fills the chip runs
+// unsplit: a split would only add the pre-pass.  Workspace: the parts' end
+// states and decay products.
 struct ChunkSplit { int64_t nblk, nparts, bpp, dec_off; size_t bytes; };
 static ChunkSplit chunk_split(int64_t B, int64_t L, int64_t H, int64_t P, int64_t NS) {
   ChunkSplit sp;
   sp.nblk = (L + kCQ - 1) / kCQ;
   const int64_t nwg = B * H * (P / kCPS);
-  int64_t want = nwg > 0 ? (512 + nwg - 1) / nwg : 1;
+  int64_t want = nwg > 0 && nwg < 256 ? (512 + nwg - 1) / nwg : 1;
   const int64_t cap = sp.nblk / 8 > 1 ? sp.nblk / 8 : 1;
   if (want > cap) want = cap;
   if (want > 16) want = 16;
