@@ -439,12 +439,12 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkFwdArgs g) {
 }
 
 // Sequence split of the forward: when the grid leaves CUs idle (fewer than
-// 256 workgroups, MI355X's CU count; the kernel's registers allow one
-// workgroup per CU) the sequence is cut into parts of at least 8 blocks, up
-// to 512 workgroups, each run by its own workgroups from the state the
-// pre-pass and the fold give it.  A grid that already fills the chip runs
-// unsplit: a split would only add the pre-pass.  Workspace: the parts' end
-// states and decay products.
+// 256 workgroups, MI355X's CU count) the sequence is cut into parts of at
+// least 8 blocks, up to 512 workgroups, each run by its own workgroups from
+// the state the pre-pass and the fold give it.  A grid with a workgroup for
+// every CU runs unsplit: a second workgroup on a CU adds only about a fifth
+// to its throughput (every phase of a block slows down), less than the
+// pre-pass costs.  Workspace: the parts' end states and decay products.
 struct ChunkSplit { int64_t nblk, nparts, bpp, dec_off; size_t bytes; };
 static ChunkSplit chunk_split(int64_t B, int64_t L, int64_t H, int64_t P, int64_t NS) {
   ChunkSplit sp;
