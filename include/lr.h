@@ -237,8 +237,9 @@ lr_status lr_ssd_scan(lr_dtype io, lr_disc disc, int64_t B, int64_t L,
 
 /* Optional workspace of lr_ssd_scan (0 when the sizes are invalid or when
  * the call does not split the sequence).  With too few (batch, head) pairs
- * to fill the GPU, the forward cuts the sequence into parts run side by
- * side: a first launch computes each part's end state from zero and its
+ * to fill the GPU (fewer than 256 workgroups of one (batch, head, 64
+ * columns of P) each, one per CU of an MI355X), the forward cuts the
+ * sequence into parts run side by side: a first launch computes each part's end state from zero and its
  * decay product into the workspace (the (a, b) combine of the "K-Search
  * for MLX" blog, section "A 20x faster prefill", applied to whole parts),
  * and the main launch folds them into the state entering every part.
