@@ -35,6 +35,10 @@
 //             partial traffic), dA, dD (fp32).
 //   reduce:   fixed-order fp32 sums of the partials over heads (and batch
 //             and segments for dA, dD), so results are deterministic.
+// The launches run per slice of batch rows (bounded workspace); from the
+// second slice on, gloc shares one launch with the previous slice's dB, dC
+// reduction (gloc_reduce), which overlaps the bandwidth-bound sums with the
+// latency-bound gloc.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -178,14 +182,13 @@ struct GlocLds {
 // every wave scans the block's gates itself (lane = token), so dy is scaled
 // by E_u while it is written to LDS, with no extra pass or barrier.
 template <int MODE, int NS>
-__global__ __launch_bounds__(256) void ssd_bwd_gloc_kernel(BwdArgs a) {
+__device__ __forceinline__ void gloc_body(const BwdArgs& a, int64_t wid) {
   constexpr int NT = NS / 16;
   constexpr int kCC = kBQ * (NS / 8) / 256;    // 16-byte C chunks per thread
   constexpr int kDC = kBQ * (kBP / 8) / 256;   // 16-byte dy chunks per thread
   __shared__ GlocLds<NS> sm;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int g4 = lane >> 4, c16 = lane & 15;
-  const int64_t wid = xcd_remap(blockIdx.x, gridDim.x);
   // heads vary fastest: the workgroups that run together on an XCD are the
   // heads of one (batch row, segment), which read the same B and C rows
   // (groups shared by heads), so those come from the XCD's L2
@@ -271,6 +274,11 @@ __global__ __launch_bounds__(256) void ssd_bwd_gloc_kernel(BwdArgs a) {
   for (int nt = 0; nt < NT; ++nt)
     *reinterpret_cast<f32x4*>(out + p * NS + 16 * nt + 4 * g4) = gacc[nt];
   if (tid == 0) a.lam[(sg * a.B + b) * a.H + h] = fast_exp2(lsum) * ssign;
+}
+
+template <int MODE, int NS>
+__global__ __launch_bounds__(256) void ssd_bwd_gloc_kernel(BwdArgs a) {
+  gloc_body<MODE, NS>(a, xcd_remap(blockIdx.x, gridDim.x));
 }
 
 // ---------------------------------------------------------------------------
@@ -816,11 +824,11 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
 // (b, t, group) row, heads summed in order.  The blocks after them: dA, dD,
 // one wave per head; lane l sums partials l, l + 64, ... in order and the
 // wave adds the 64 lane sums in a fixed pattern.
-__global__ __launch_bounds__(256) void ssd_bwd_reduce_kernel(BwdArgs a, int64_t nblk_bc) {
-  if (blockIdx.x < nblk_bc) {
+__device__ __forceinline__ void reduce_bc_block(const BwdArgs& a, int64_t blk) {
+  {
     const int64_t n8 = a.N / 8;
     const int64_t total = a.B * a.L * a.G * n8;
-    const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    const int64_t idx = blk * 256 + threadIdx.x;
     if (idx >= total) return;
     const int64_t hpg = a.H / a.G;
     const int64_t c8 = idx % n8;
@@ -849,6 +857,12 @@ __global__ __launch_bounds__(256) void ssd_bwd_reduce_kernel(BwdArgs a, int64_t 
     }
     *reinterpret_cast<u16x8*>(a.dBm + o) = ob;
     *reinterpret_cast<u16x8*>(a.dCm + o) = oc;
+  }
+}
+
+__global__ __launch_bounds__(256) void ssd_bwd_reduce_kernel(BwdArgs a, int64_t nblk_bc) {
+  if (blockIdx.x < nblk_bc) {
+    reduce_bc_block(a, blockIdx.x);
     return;
   }
   if (a.dA == nullptr) return;
@@ -870,14 +884,39 @@ __global__ __launch_bounds__(256) void ssd_bwd_reduce_kernel(BwdArgs a, int64_t 
 }
 
 // GLA: dg = (sum of the per-slice log-gate gradients) / g, fixed order.
-__global__ __launch_bounds__(256) void gla_bwd_dg_kernel(BwdArgs a) {
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;   // (b L + t) G + grp
+__device__ __forceinline__ void gla_dg_block(const BwdArgs& a, int64_t blk) {
+  const int64_t idx = blk * 256 + threadIdx.x;   // (b L + t) G + grp
   if (idx >= a.B * a.L * a.G) return;
   const int64_t grp = idx % a.G, bt = idx / a.G;
   const int64_t hpg = a.H / a.G;
   float s = 0.f;
   for (int64_t hh = grp * hpg; hh < (grp + 1) * hpg; ++hh) s += a.dgpart[bt * a.H + hh];
   a.dg[idx] = f2bf(s / bf2f(a.dt[idx]));
+}
+
+__global__ __launch_bounds__(256) void gla_bwd_dg_kernel(BwdArgs a) { gla_dg_block(a, blockIdx.x); }
+
+// One launch running two independent jobs side by side: gloc of a batch
+// slice (latency bound) and the reductions of the slice before it (bandwidth
+// bound: dB, dC over heads, and for GLA the gate gradient).  They touch
+// disjoint buffers: gloc writes the segment adjoints, the reductions read
+// the partials the previous slice's main kernel wrote.  Work ids go through
+// the XCD remap first, then the reduction blocks are spread evenly among the
+// gloc workgroups (id f is reduction block floor(f nr / total) when that
+// floor steps at f, else gloc workgroup f - floor(f nr / total)).
+template <int MODE, int NS>
+__global__ __launch_bounds__(256) void ssd_bwd_gloc_reduce_kernel(BwdArgs gl, BwdArgs rd,
+                                                                  int64_t n_red, int64_t n_dg) {
+  const int64_t total = gridDim.x;
+  const int64_t nr = n_red + n_dg;
+  const int64_t f = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t r_lo = f * nr / total, r_hi = (f + 1) * nr / total;
+  if (r_hi > r_lo) {
+    if (r_lo < n_red) reduce_bc_block(rd, r_lo);
+    else gla_dg_block(rd, r_lo - n_red);
+    return;
+  }
+  gloc_body<MODE, NS>(gl, f - r_lo);
 }
 
 // Empty input (B * L == 0): dA = dD = 0 and dh0 = dh_last (or 0).
@@ -991,6 +1030,11 @@ static hipError_t launch_bwd(BwdArgs a, void* ws, size_t ws_bytes, hipStream_t s
   a.ckB = a.B;
   const int64_t PN = kBP * a.N;
   const int nbs = static_cast<int>(a.seg / kBQ);
+  // blocks of the reductions of slice r: dB, dC over heads; GLA's gate gradient
+  auto n_red = [](const BwdArgs& r) { return (r.B * r.L * r.G * (r.N / 8) + 255) / 256; };
+  auto n_dg = [](const BwdArgs& r) { return MODE == kBwdGla ? (r.B * r.L * r.G + 255) / 256 : int64_t(0); };
+  BwdArgs prev = a;      // the slice whose reductions are still to run
+  bool pending = false;
   for (int64_t b0 = 0; b0 < a.B; b0 += bs) {
     BwdArgs s = a;
     s.B = (a.B - b0) < bs ? (a.B - b0) : bs;
@@ -1010,18 +1054,28 @@ static hipError_t launch_bwd(BwdArgs a, void* ws, size_t ws_bytes, hipStream_t s
     s.dApart += b0 * a.H * a.nseg;
     s.dDpart += b0 * a.H * a.nseg;
     const int64_t nwg = s.B * s.H * s.nseg;
-    if (s.N == 128) hipLaunchKernelGGL((ssd_bwd_gloc_kernel<MODE, 128>), dim3(nwg), dim3(256), 0, stream, s);
-    else hipLaunchKernelGGL((ssd_bwd_gloc_kernel<MODE, 64>), dim3(nwg), dim3(256), 0, stream, s);
+    if (!pending) {
+      if (s.N == 128) hipLaunchKernelGGL((ssd_bwd_gloc_kernel<MODE, 128>), dim3(nwg), dim3(256), 0, stream, s);
+      else hipLaunchKernelGGL((ssd_bwd_gloc_kernel<MODE, 64>), dim3(nwg), dim3(256), 0, stream, s);
+    } else {   // this slice's gloc beside the previous slice's reductions
+      const int64_t nr = n_red(prev), nd = n_dg(prev);
+      const dim3 grid(static_cast<unsigned>(nwg + nr + nd));
+      if (s.N == 128)
+        hipLaunchKernelGGL((ssd_bwd_gloc_reduce_kernel<MODE, 128>), grid, dim3(256), 0, stream, s, prev, nr, nd);
+      else
+        hipLaunchKernelGGL((ssd_bwd_gloc_reduce_kernel<MODE, 64>), grid, dim3(256), 0, stream, s, prev, nr, nd);
+    }
     hipLaunchKernelGGL(ssd_bwd_gcombine_kernel<MODE>, dim3((s.B * s.H * PN + 255) / 256), dim3(256), 0,
                        stream, s, PN);
     if (s.N == 128) launch_main<MODE, 128>(s, nwg, nbs, stream);
     else launch_main<MODE, 64>(s, nwg, nbs, stream);
-    const int64_t red = (s.B * s.L * s.G * (s.N / 8) + 255) / 256;
-    hipLaunchKernelGGL(ssd_bwd_reduce_kernel, dim3(red), dim3(256), 0, stream, s, red);
-    if (MODE == kBwdGla) {
-      const int64_t nd = (s.B * s.L * s.G + 255) / 256;
-      hipLaunchKernelGGL(gla_bwd_dg_kernel, dim3(nd), dim3(256), 0, stream, s);
-    }
+    prev = s;
+    pending = true;
+  }
+  if (pending) {   // the last slice's reductions
+    const int64_t nr = n_red(prev);
+    hipLaunchKernelGGL(ssd_bwd_reduce_kernel, dim3(nr), dim3(256), 0, stream, prev, nr);
+    if (MODE == kBwdGla) hipLaunchKernelGGL(gla_bwd_dg_kernel, dim3(n_dg(prev)), dim3(256), 0, stream, prev);
   }
   if (a.dA != nullptr)
     hipLaunchKernelGGL(ssd_bwd_reduce_kernel, dim3((a.H + 3) / 4), dim3(256), 0, stream, a, int64_t(0));

@@ -60,6 +60,10 @@ def test_dispatch_of_each_workload():
     assert kernels(lambda: lr.lr_ssd_scan_bwd(T["x"], T["dt"], T["A"], T["B"], T["C"],
                                               T["Dskip"], None, ck[0], T["dy"], chunk=256,
                                               seg=256)) == \
-        4 * ["lr::ssd_bwd_gloc_kernel<0, 128>", "lr::ssd_bwd_gcombine_kernel<0>",
-             "lr::ssd_bwd_main_kernel<0, 128, 4>", "lr::ssd_bwd_reduce_kernel"] + \
-        ["lr::ssd_bwd_reduce_kernel"]   # one batch row per slice, then dA, dD
+        ["lr::ssd_bwd_gloc_kernel<0, 128>", "lr::ssd_bwd_gcombine_kernel<0>",
+         "lr::ssd_bwd_main_kernel<0, 128, 4>"] + \
+        3 * ["lr::ssd_bwd_gloc_reduce_kernel<0, 128>", "lr::ssd_bwd_gcombine_kernel<0>",
+             "lr::ssd_bwd_main_kernel<0, 128, 4>"] + \
+        ["lr::ssd_bwd_reduce_kernel", "lr::ssd_bwd_reduce_kernel"]
+    # one batch row per slice; each later slice's gloc runs beside the previous
+    # slice's dB, dC reduction; the last slice's reduction, then dA, dD
