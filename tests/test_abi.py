@@ -158,6 +158,14 @@ def test_ssd_fwd_workspace(L):
     # enough workgroups already, or too short to split: no workspace
     assert L.lr_ssd_scan_workspace_bytes(8, 4096, 64, 64, 1, 128, 64) == 0
     assert L.lr_ssd_scan_workspace_bytes(1, 256, 2, 64, 1, 128, 64) == 0
+    # the split starts below 256 workgroups of (batch, head, 64 columns of P):
+    # 256 (B=8, H=32, P=64; GLA B=8, H=16, V=128) run in one pass, 255 split
+    # (into ceil(512 / 255) = 3 parts, each part's end state and decay kept)
+    assert L.lr_ssd_scan_workspace_bytes(8, 2048, 32, 64, 1, 128, 64) == 0
+    assert L.lr_gla_scan_workspace_bytes(8, 4096, 16, 128, 128, 64) == 0
+    need = L.lr_ssd_scan_workspace_bytes(5, 2048, 51, 64, 1, 128, 64)
+    assert need >= 2 * 5 * 51 * 64 * 128 * 4 + 2 * 5 * 51 * 4
+    assert L.lr_ssd_scan_workspace_bytes(1, 2048, 128, 128, 1, 128, 64) == 0   # 256 by P = 128
     # invalid sizes
     assert L.lr_ssd_scan_workspace_bytes(1, 4096, 2, 48, 1, 128, 64) == 0
     assert L.lr_gla_scan_workspace_bytes(1, 4096, 2, 128, 128, 64) > 0
