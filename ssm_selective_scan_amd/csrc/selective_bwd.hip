@@ -348,8 +348,12 @@ __device__ __forceinline__ void selective_bwd_body(const SelBwdArgs& a, SbLds<NP
           v[NPW + j] = ht * dyv;             // dC partial
           const float bx = Bv * xv;
           if constexpr (FAST) {
-            ddtp = fmaf(G[j], fmaf(Av[j], ht, bx), ddtp);
-            dAacc[j] = fmaf(G[j], fmaf(dtv, ht, (dtv - ph) * (bx * iAv[j])), dAacc[j]);
+            // ddt term G (A h + B x); the dA term G (dt h + (dt - phi) B x / A)
+            // is accumulated times A, as dt G (A h + B x) - phi G B x, which
+            // reuses both products (the 1/A is applied once, after the sweep)
+            const float u = G[j] * fmaf(Av[j], ht, bx);
+            ddtp += u;
+            dAacc[j] = fmaf(dtv, u, fmaf(-gphi, bx, dAacc[j]));
           } else {
             const float hp = i > 0 ? sm.hsl[w][i > 0 ? i - 1 : 0][j][lane] : hin[j];
             const float de = G[j] * hp;
@@ -448,9 +452,11 @@ __global__ __launch_bounds__(512) void selective_bwd_kernel(SelBwdArgs a) {
   for (int ww = 0; ww < kSbNW; ++ww) precise |= flags[ww] != 0.f;
   // the closed-form gradients lose digits in (dt - phi)/A at small |dt A|
   // (as the forward's fast form does): fp32 I/O always takes the series
-  if (DISC == kSbZoh && !precise && sizeof(T) == 2)
+  if (DISC == kSbZoh && !precise && sizeof(T) == 2) {
     selective_bwd_body<T, DISC, true, NPW>(a, sm, b, tile, Av, iAv, okj, G, dAacc, dDacc);
-  else
+#pragma unroll
+    for (int j = 0; j < NPW; ++j) dAacc[j] *= iAv[j];   // accumulated times A (see the body)
+  } else
     selective_bwd_body<T, DISC, false, NPW>(a, sm, b, tile, Av, iAv, okj, G, dAacc, dDacc);
 
 #pragma unroll
