@@ -8,6 +8,7 @@ from __future__ import annotations
 
 import concurrent.futures as cf
 import os
+import re
 import subprocess
 import sys
 
@@ -101,8 +102,65 @@ def build_hostcheck() -> str:
     return HOSTCHECK_LIB
 
 
+# Per-kernel register, scratch and LDS use, from the compiler's
+# kernel-resource-usage remarks (the device code of the normal build; the
+# objects go to _build/resources/ and are not linked).
+RESOURCES = os.path.join(BUILD, "resources")
+_REMARK_KEYS = {"VGPRs": "vgpr", "AGPRs": "agpr", "VGPRs Spill": "vgpr_spill",
+                "SGPRs Spill": "sgpr_spill", "ScratchSize [bytes/lane]": "scratch",
+                "Occupancy [waves/SIMD]": "occupancy", "LDS Size [bytes/block]": "lds"}
+
+
+def _demangle(names):
+    try:
+        p = subprocess.run(["c++filt"], input="\n".join(names), stdout=subprocess.PIPE,
+                           text=True, check=True)
+        out = p.stdout.split("\n")[:len(names)]
+    except (OSError, subprocess.CalledProcessError):
+        return list(names)
+    return [re.sub(r"^void ", "", re.sub(r"\(.*$", "", d)) for d in out]
+
+
+def resource_usage(sources=None) -> list:
+    """One dict per kernel of the given sources (default: all): name
+    (demangled, without its parameter list), source, and the integers vgpr,
+    agpr, vgpr_spill, sgpr_spill, scratch (bytes per lane), occupancy (waves
+    per SIMD) and lds (bytes per workgroup, static)."""
+    os.makedirs(RESOURCES, exist_ok=True)
+    sources = list(sources or SOURCES)
+    with cf.ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+        outs = list(ex.map(lambda s: _run([HIPCC, *FLAGS, "-Rpass-analysis=kernel-resource-usage",
+                                           "-c", os.path.join(CSRC, s), "-o",
+                                           os.path.join(RESOURCES, s.replace(".hip", ".o"))]),
+                           sources))
+    rows = []
+    for src, out in zip(sources, outs):
+        cur = None
+        for line in out.splitlines():
+            m = re.search(r"remark: Function Name: (\S+)", line)
+            if m:
+                cur = {"name": m.group(1), "source": src}
+                rows.append(cur)
+                continue
+            m = re.search(r"remark:\s+(.+?): (-?\d+) \[-Rpass-analysis", line)
+            if m and cur is not None and m.group(1).strip() in _REMARK_KEYS:
+                cur[_REMARK_KEYS[m.group(1).strip()]] = int(m.group(2))
+    for r, d in zip(rows, _demangle([r["name"] for r in rows])):
+        r["name"] = d
+    return rows
+
+
 if __name__ == "__main__":
     if "hostcheck" in sys.argv:
         print(build_hostcheck())
+    elif "resources" in sys.argv:
+        # python -m ssm_selective_scan_amd.build resources [file.hip ...]
+        srcs = [a for a in sys.argv[1:] if a.endswith(".hip")]
+        print(f"{'kernel':68s} {'VGPR':>4s} {'AGPR':>4s} {'spill':>5s} {'scratch':>7s} "
+              f"{'waves':>5s} {'LDS':>7s}")
+        for r in sorted(resource_usage(srcs or None), key=lambda r: r["name"]):
+            print(f"{r['name'][:68]:68s} {r.get('vgpr', 0):4d} {r.get('agpr', 0):4d} "
+                  f"{r.get('vgpr_spill', 0):5d} {r.get('scratch', 0):7d} "
+                  f"{r.get('occupancy', 0):5d} {r.get('lds', 0):7d}")
     else:
         print(build(verbose="-v" in sys.argv))
