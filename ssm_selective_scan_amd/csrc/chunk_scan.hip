@@ -40,6 +40,7 @@
 // (a2, b2) o (a1, b1) = (a2 a1, a2 b1 + b2) ("K-Search for MLX" blog,
 // section "A 20x faster prefill", combine equation), applied to whole parts.
 #include <atomic>
+#include <type_traits>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -325,35 +326,60 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkFwdArgs g) {
     //      10 with s-tile <= t-tile plus the all-zero (0,1) and (2,3) that
     //      complete the 32-wide k steps of M X
     {
-      const int ti_tab[12] = {3, 3, 3, 2, 2, 2, 1, 1, 3, 0, 0, 2};
-      const int si_tab[12] = {0, 1, 2, 0, 1, 2, 0, 1, 3, 0, 1, 3};
+      // Each wave's three tiles are fixed at compile time, so a C tile that
+      // two or three of them share is read from LDS once per k step.
+      auto tiles = [&](auto ta, auto sa, auto tb, auto sb, auto tc, auto sc) {
+        constexpr int TI[3] = {decltype(ta)::value, decltype(tb)::value, decltype(tc)::value};
+        constexpr int SI[3] = {decltype(sa)::value, decltype(sb)::value, decltype(sc)::value};
+        f32x4 z[3];
 #pragma unroll
-      for (int q = 0; q < 3; ++q) {
-        const int ti = ti_tab[3 * w + q], si = si_tab[3 * w + q];
-        const int t = 16 * ti + c16;           // this lane's column of Z^T
-        const int s0 = 16 * si + 4 * g4;       // this lane's 4 rows of Z^T
-        u16x4 out = {0, 0, 0, 0};
-        if (si <= ti) {
-          f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        for (int q = 0; q < 3; ++q) z[q] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int kk = 0; kk < NK; ++kk)
-            z = mfma16x16x32(lds_tile(cur.Bs, kLdB, 16 * si, 32 * kk, lane),
-                             lds_tile(cur.Cs, kLdC, 16 * ti, 32 * kk, lane), z);
-          const float ct = cur.cum[t];
+        for (int kk = 0; kk < NK; ++kk) {
+          bf16x8 cop[3];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int sr = s0 + r;
-            // unconditional loads, then a select (no per-lane branches
-            // around LDS reads; a non-finite value above the diagonal is discarded)
-            float m = z[r] * fast_exp2(ct - cur.cum[sr]) * cur.phi[sr];
-            if (MODE == kModeSsdBilinear) m *= cur.sg[t] * cur.sg[sr];
-            m = (sr <= t) ? m : 0.f;
-            if (sr == t) m += Dh;   // D x_t folded into the diagonal
-            out[r] = f2bf(m);
+          for (int q = 0; q < 3; ++q) {
+            if (SI[q] > TI[q]) continue;
+            bool reuse = false;
+#pragma unroll
+            for (int r = 0; r < q; ++r)
+              if (!reuse && SI[r] <= TI[r] && TI[r] == TI[q]) { cop[q] = cop[r]; reuse = true; }
+            if (!reuse) cop[q] = lds_tile(cur.Cs, kLdC, 16 * TI[q], 32 * kk, lane);
+            z[q] = mfma16x16x32(lds_tile(cur.Bs, kLdB, 16 * SI[q], 32 * kk, lane), cop[q], z[q]);
           }
         }
-        *reinterpret_cast<u16x4*>(Ms + t * kLdM + s0) = out;
-      }
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+          const int ti = TI[q], si = SI[q];
+          const int t = 16 * ti + c16;           // this lane's column of Z^T
+          const int s0 = 16 * si + 4 * g4;       // this lane's 4 rows of Z^T
+          u16x4 out = {0, 0, 0, 0};
+          if (si <= ti) {
+            const float ct = cur.cum[t];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int sr = s0 + r;
+              // unconditional loads, then a select (no per-lane branches
+              // around LDS reads; a non-finite value above the diagonal is discarded)
+              float m = z[q][r] * fast_exp2(ct - cur.cum[sr]) * cur.phi[sr];
+              if (MODE == kModeSsdBilinear) m *= cur.sg[t] * cur.sg[sr];
+              m = (sr <= t) ? m : 0.f;
+              if (sr == t) m += Dh;   // D x_t folded into the diagonal
+              out[r] = f2bf(m);
+            }
+          }
+          *reinterpret_cast<u16x4*>(Ms + t * kLdM + s0) = out;
+        }
+      };
+      using I0 = std::integral_constant<int, 0>;
+      using I1 = std::integral_constant<int, 1>;
+      using I2 = std::integral_constant<int, 2>;
+      using I3 = std::integral_constant<int, 3>;
+      const int wu = __builtin_amdgcn_readfirstlane(w);   // wave-uniform branch
+      if (wu == 0) tiles(I3{}, I0{}, I3{}, I1{}, I3{}, I2{});
+      else if (wu == 1) tiles(I2{}, I0{}, I2{}, I1{}, I2{}, I2{});
+      else if (wu == 2) tiles(I1{}, I0{}, I1{}, I1{}, I3{}, I3{});
+      else tiles(I0{}, I0{}, I0{}, I1{}, I2{}, I3{});
     }
     __syncthreads();
 
