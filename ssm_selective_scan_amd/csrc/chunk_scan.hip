@@ -326,8 +326,8 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkFwdArgs g) {
     //      10 with s-tile <= t-tile plus the all-zero (0,1) and (2,3) that
     //      complete the 32-wide k steps of M X
     {
-      // Each wave's three tiles are fixed at compile time, so a C tile that
-      // two or three of them share is read from LDS once per k step.
+      // Each wave's three tiles are fixed at compile time, so a C or B tile
+      // that several of them share is read from LDS once per k step.
       auto tiles = [&](auto ta, auto sa, auto tb, auto sb, auto tc, auto sc) {
         constexpr int TI[3] = {decltype(ta)::value, decltype(tb)::value, decltype(tc)::value};
         constexpr int SI[3] = {decltype(sa)::value, decltype(sb)::value, decltype(sc)::value};
@@ -336,16 +336,20 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkFwdArgs g) {
         for (int q = 0; q < 3; ++q) z[q] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk) {
-          bf16x8 cop[3];
+          bf16x8 cop[3], bop[3];
 #pragma unroll
           for (int q = 0; q < 3; ++q) {
             if (SI[q] > TI[q]) continue;
-            bool reuse = false;
+            bool cre = false, bre = false;
 #pragma unroll
-            for (int r = 0; r < q; ++r)
-              if (!reuse && SI[r] <= TI[r] && TI[r] == TI[q]) { cop[q] = cop[r]; reuse = true; }
-            if (!reuse) cop[q] = lds_tile(cur.Cs, kLdC, 16 * TI[q], 32 * kk, lane);
-            z[q] = mfma16x16x32(lds_tile(cur.Bs, kLdB, 16 * SI[q], 32 * kk, lane), cop[q], z[q]);
+            for (int r = 0; r < q; ++r) {
+              if (SI[r] > TI[r]) continue;
+              if (!cre && TI[r] == TI[q]) { cop[q] = cop[r]; cre = true; }
+              if (!bre && SI[r] == SI[q]) { bop[q] = bop[r]; bre = true; }
+            }
+            if (!cre) cop[q] = lds_tile(cur.Cs, kLdC, 16 * TI[q], 32 * kk, lane);
+            if (!bre) bop[q] = lds_tile(cur.Bs, kLdB, 16 * SI[q], 32 * kk, lane);
+            z[q] = mfma16x16x32(bop[q], cop[q], z[q]);
           }
         }
 #pragma unroll
@@ -376,10 +380,12 @@ __global__ __launch_bounds__(256) void chunk_fwd_kernel(ChunkFwdArgs g) {
       using I2 = std::integral_constant<int, 2>;
       using I3 = std::integral_constant<int, 3>;
       const int wu = __builtin_amdgcn_readfirstlane(w);   // wave-uniform branch
+      // (t tile, s tile): 4 operand tiles per k step for waves 0-2, 2 for wave 3,
+      // which also writes the zero tiles (0,1) and (2,3)
       if (wu == 0) tiles(I3{}, I0{}, I3{}, I1{}, I3{}, I2{});
       else if (wu == 1) tiles(I2{}, I0{}, I2{}, I1{}, I2{}, I2{});
-      else if (wu == 2) tiles(I1{}, I0{}, I1{}, I1{}, I3{}, I3{});
-      else tiles(I0{}, I0{}, I0{}, I1{}, I2{}, I3{});
+      else if (wu == 2) tiles(I1{}, I0{}, I1{}, I1{}, I0{}, I0{});
+      else tiles(I3{}, I3{}, I0{}, I1{}, I2{}, I3{});
     }
     __syncthreads();
 
