@@ -674,19 +674,24 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
 #pragma unroll
     for (int aa = 0; aa < NT / 4; ++aa) {
       const int nt = (NT / 4) * w + aa;
+      // the n-tile's operands of C and Gamma serve all four token tiles
+      bf16x8 ct[2], gt[2];
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        ct[k2] = lds_tile_tr(sm.Cs, kLdN, 32 * k2, 16 * nt, lane);
+        gt[k2] = lds_tile_tr(sm.Gs, kLdN, 32 * k2, 16 * nt, lane);
+      }
 #pragma unroll
       for (int ti = 0; ti < 4; ++ti) {
         f32x4 d1 = {0.f, 0.f, 0.f, 0.f}, d2 = d1;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           if (ks == 0 && ti >= 2) continue;
-          d1 = mfma16x16x32(lds_tile_tr(sm.Cs, kLdN, 32 * ks, 16 * nt, lane),
-                            lds_tile(sm.Wt, kBLd, 16 * ti, 32 * ks, lane), d1);
+          d1 = mfma16x16x32(ct[ks], lds_tile(sm.Wt, kBLd, 16 * ti, 32 * ks, lane), d1);
         }
 #pragma unroll
         for (int kp = 0; kp < 2; ++kp)
-          d2 = mfma16x16x32(lds_tile_tr(sm.Gs, kLdN, 32 * kp, 16 * nt, lane),
-                            lds_tile(sm.xs, kBLd, 16 * ti, 32 * kp, lane), d2);
+          d2 = mfma16x16x32(gt[kp], lds_tile(sm.xs, kBLd, 16 * ti, 32 * kp, lane), d2);
         const int t = 16 * ti + c16;
         if (t < nv) {
           f32x4 v;
@@ -700,13 +705,13 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
     // ---- Gamma for the previous block: E_end Gamma + sum_u E_u dy_u (x) C_u
     {
       const float dec = fast_exp2(sm.cum[kBQ - 1]) * (DISC == kBwdBilinear ? sm.sg[kBQ - 1] : 1.f);
+      const bf16x8 de0 = lds_tile_tr(sm.dyE, kBLd, 0, 16 * w, lane);
+      const bf16x8 de1 = lds_tile_tr(sm.dyE, kBLd, 32, 16 * w, lane);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         gacc[nt] *= dec;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-          gacc[nt] = mfma16x16x32(lds_tile_tr(sm.Cs, kLdN, 32 * ks, 16 * nt, lane),
-                                  lds_tile_tr(sm.dyE, kBLd, 32 * ks, 16 * w, lane), gacc[nt]);
+        gacc[nt] = mfma16x16x32(lds_tile_tr(sm.Cs, kLdN, 0, 16 * nt, lane), de0, gacc[nt]);
+        gacc[nt] = mfma16x16x32(lds_tile_tr(sm.Cs, kLdN, 32, 16 * nt, lane), de1, gacc[nt]);
       }
     }
     __syncthreads();
@@ -722,19 +727,24 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
 #pragma unroll
     for (int aa = 0; aa < NT / 4; ++aa) {
       const int nt = (NT / 4) * w + aa;
+      // the n-tile's operands of B and h_prev serve all four token tiles
+      bf16x8 bt[2], ht[2];
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        bt[k2] = lds_tile_tr(sm.Bs, kLdN, 32 * k2, 16 * nt, lane);
+        ht[k2] = lds_tile_tr(sm.Gs, kLdN, 32 * k2, 16 * nt, lane);
+      }
 #pragma unroll
       for (int tj = 0; tj < 4; ++tj) {
         f32x4 d1 = {0.f, 0.f, 0.f, 0.f}, d2 = d1;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           if (ks == 1 && tj < 2) continue;
-          d1 = mfma16x16x32(lds_tile_tr(sm.Bs, kLdN, 32 * ks, 16 * nt, lane),
-                            lds_tile_tr(sm.Wt, kBLd, 32 * ks, 16 * tj, lane), d1);
+          d1 = mfma16x16x32(bt[ks], lds_tile_tr(sm.Wt, kBLd, 32 * ks, 16 * tj, lane), d1);
         }
 #pragma unroll
         for (int kp = 0; kp < 2; ++kp)
-          d2 = mfma16x16x32(lds_tile_tr(sm.Gs, kLdN, 32 * kp, 16 * nt, lane),
-                            lds_tile(sm.dys, kBLd, 16 * tj, 32 * kp, lane), d2);
+          d2 = mfma16x16x32(ht[kp], lds_tile(sm.dys, kBLd, 16 * tj, 32 * kp, lane), d2);
         const int u = 16 * tj + c16;
         if (u < nv) {
           f32x4 v;
