@@ -671,34 +671,45 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
       eU[q] = sm.E[16 * q + c16];
       asm volatile("" : "+v"(psE[q]), "+v"(eU[q]));
     }
+    {
+      // the wave's n-tiles' operands of C and Gamma serve all four token
+      // tiles, and each token tile's operands of W and x serve both n-tiles
+      constexpr int NA = NT / 4;
+      bf16x8 ct[NA][2], gt[NA][2];
 #pragma unroll
-    for (int aa = 0; aa < NT / 4; ++aa) {
-      const int nt = (NT / 4) * w + aa;
-      // the n-tile's operands of C and Gamma serve all four token tiles
-      bf16x8 ct[2], gt[2];
+      for (int aa = 0; aa < NA; ++aa)
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        ct[k2] = lds_tile_tr(sm.Cs, kLdN, 32 * k2, 16 * nt, lane);
-        gt[k2] = lds_tile_tr(sm.Gs, kLdN, 32 * k2, 16 * nt, lane);
-      }
-#pragma unroll
-      for (int ti = 0; ti < 4; ++ti) {
-        f32x4 d1 = {0.f, 0.f, 0.f, 0.f}, d2 = d1;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          if (ks == 0 && ti >= 2) continue;
-          d1 = mfma16x16x32(ct[ks], lds_tile(sm.Wt, kBLd, 16 * ti, 32 * ks, lane), d1);
+        for (int k2 = 0; k2 < 2; ++k2) {
+          ct[aa][k2] = lds_tile_tr(sm.Cs, kLdN, 32 * k2, 16 * (NA * w + aa), lane);
+          gt[aa][k2] = lds_tile_tr(sm.Gs, kLdN, 32 * k2, 16 * (NA * w + aa), lane);
         }
 #pragma unroll
-        for (int kp = 0; kp < 2; ++kp)
-          d2 = mfma16x16x32(gt[kp], lds_tile(sm.xs, kBLd, 16 * ti, 32 * kp, lane), d2);
-        const int t = 16 * ti + c16;
-        if (t < nv) {
-          f32x4 v;
+      for (int ti = 0; ti < 4; ++ti) {
+        bf16x8 wt[2], xt[2];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = fmaf(psE[ti], d2[r], d1[r]);
-          *reinterpret_cast<u16x4*>(a.dBpart + ((b * a.L + t0 + t) * a.H + h) * NS + 16 * nt + 4 * g4) =
-              u16x4{f2bf(v[0]), f2bf(v[1]), f2bf(v[2]), f2bf(v[3])};
+        for (int k2 = 0; k2 < 2; ++k2) {
+          if (!(k2 == 0 && ti >= 2)) wt[k2] = lds_tile(sm.Wt, kBLd, 16 * ti, 32 * k2, lane);
+          xt[k2] = lds_tile(sm.xs, kBLd, 16 * ti, 32 * k2, lane);
+        }
+        const int t = 16 * ti + c16;
+#pragma unroll
+        for (int aa = 0; aa < NA; ++aa) {
+          const int nt = NA * w + aa;
+          f32x4 d1 = {0.f, 0.f, 0.f, 0.f}, d2 = d1;
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            if (ks == 0 && ti >= 2) continue;
+            d1 = mfma16x16x32(ct[aa][ks], wt[ks], d1);
+          }
+#pragma unroll
+          for (int kp = 0; kp < 2; ++kp) d2 = mfma16x16x32(gt[aa][kp], xt[kp], d2);
+          if (t < nv) {
+            f32x4 v;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = fmaf(psE[ti], d2[r], d1[r]);
+            *reinterpret_cast<u16x4*>(a.dBpart + ((b * a.L + t0 + t) * a.H + h) * NS + 16 * nt + 4 * g4) =
+                u16x4{f2bf(v[0]), f2bf(v[1]), f2bf(v[2]), f2bf(v[3])};
+          }
         }
       }
     }
@@ -724,34 +735,45 @@ __global__ __launch_bounds__(256) void ssd_bwd_main_kernel(BwdArgs a) {
           u16x4{hv[4 * (nt & 1)], hv[4 * (nt & 1) + 1], hv[4 * (nt & 1) + 2], hv[4 * (nt & 1) + 3]};
     }
     __syncthreads();
+    {
+      // as for dB: n-tile operands of B and h_prev, token-tile operands of W
+      // and dy, each read once
+      constexpr int NA = NT / 4;
+      bf16x8 bt[NA][2], ht[NA][2];
 #pragma unroll
-    for (int aa = 0; aa < NT / 4; ++aa) {
-      const int nt = (NT / 4) * w + aa;
-      // the n-tile's operands of B and h_prev serve all four token tiles
-      bf16x8 bt[2], ht[2];
+      for (int aa = 0; aa < NA; ++aa)
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        bt[k2] = lds_tile_tr(sm.Bs, kLdN, 32 * k2, 16 * nt, lane);
-        ht[k2] = lds_tile_tr(sm.Gs, kLdN, 32 * k2, 16 * nt, lane);
-      }
-#pragma unroll
-      for (int tj = 0; tj < 4; ++tj) {
-        f32x4 d1 = {0.f, 0.f, 0.f, 0.f}, d2 = d1;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          if (ks == 1 && tj < 2) continue;
-          d1 = mfma16x16x32(bt[ks], lds_tile_tr(sm.Wt, kBLd, 32 * ks, 16 * tj, lane), d1);
+        for (int k2 = 0; k2 < 2; ++k2) {
+          bt[aa][k2] = lds_tile_tr(sm.Bs, kLdN, 32 * k2, 16 * (NA * w + aa), lane);
+          ht[aa][k2] = lds_tile_tr(sm.Gs, kLdN, 32 * k2, 16 * (NA * w + aa), lane);
         }
 #pragma unroll
-        for (int kp = 0; kp < 2; ++kp)
-          d2 = mfma16x16x32(ht[kp], lds_tile(sm.dys, kBLd, 16 * tj, 32 * kp, lane), d2);
-        const int u = 16 * tj + c16;
-        if (u < nv) {
-          f32x4 v;
+      for (int tj = 0; tj < 4; ++tj) {
+        bf16x8 wt[2], dt2[2];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = fmaf(eU[tj], d2[r], d1[r]);
-          *reinterpret_cast<u16x4*>(a.dCpart + ((b * a.L + t0 + u) * a.H + h) * NS + 16 * nt + 4 * g4) =
-              u16x4{f2bf(v[0]), f2bf(v[1]), f2bf(v[2]), f2bf(v[3])};
+        for (int k2 = 0; k2 < 2; ++k2) {
+          if (!(k2 == 1 && tj < 2)) wt[k2] = lds_tile_tr(sm.Wt, kBLd, 32 * k2, 16 * tj, lane);
+          dt2[k2] = lds_tile(sm.dys, kBLd, 16 * tj, 32 * k2, lane);
+        }
+        const int u = 16 * tj + c16;
+#pragma unroll
+        for (int aa = 0; aa < NA; ++aa) {
+          const int nt = NA * w + aa;
+          f32x4 d1 = {0.f, 0.f, 0.f, 0.f}, d2 = d1;
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            if (ks == 1 && tj < 2) continue;
+            d1 = mfma16x16x32(bt[aa][ks], wt[ks], d1);
+          }
+#pragma unroll
+          for (int kp = 0; kp < 2; ++kp) d2 = mfma16x16x32(ht[aa][kp], dt2[kp], d2);
+          if (u < nv) {
+            f32x4 v;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = fmaf(eU[tj], d2[r], d1[r]);
+            *reinterpret_cast<u16x4*>(a.dCpart + ((b * a.L + t0 + u) * a.H + h) * NS + 16 * nt + 4 * g4) =
+                u16x4{f2bf(v[0]), f2bf(v[1]), f2bf(v[2]), f2bf(v[3])};
+          }
         }
       }
     }
